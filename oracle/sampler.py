@@ -1,0 +1,149 @@
+"""Oracle sampler: temperature schedule, head statistics, commit / re-noise / stop.
+
+Pages followed ([mlqm] = mlqm.cn summary of the DiffusionGemma report):
+  * [mlqm] 四: positions are ordered by entropy from low to high and locked from
+    the most certain one on, until the running entropy total passes the
+    threshold (0.1); the positions past it are re-randomised and revised next
+    round.  The temperature starts at 0.8 and falls linearly to 0.4.  Generation
+    stops early once the mean entropy is below 0.005 and the most likely token
+    sequence is unchanged over two consecutive rounds, within a 48-round cap.
+  * [mlqm] 一: multinomial (uniform replacement) diffusion: an uncertain position
+    is replaced by any vocabulary token, and a locked token stays revisable.
+  * [chooseai] (llama.cpp support paragraph): the entropy-bounded denoising
+    sampler with linear temperature 0.8 -> 0.4 and adaptive stop.
+
+Readings where the pages leave a step open:
+  * entropy is in nats, of the tempered distribution softmax(l / T);
+  * the sort is stable: equal entropies keep position order;
+  * the position whose addition makes the running total exceed the bound is not
+    committed; a committed position takes the sampled token y (Gumbel-max draw);
+  * the schedule runs over the step budget S: T_t = T0 + (T1 - T0) * t / (S - 1);
+  * stop mode 1 is "mean entropy < tau"; mode 2 adds the pages' unchanged-argmax
+    condition; on the stopping step and on the last step every position takes y.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import philox
+
+STOP_NONE, STOP_MEAN, STOP_PAGES = 0, 1, 2
+
+
+def temperature(t: int, max_steps: int, t_start: float = 0.8, t_end: float = 0.4) -> np.float32:
+    """Linear schedule over the step budget, evaluated in fp64 from the fp32 parameters."""
+    t0 = float(np.float32(t_start))
+    t1 = float(np.float32(t_end))
+    if max_steps <= 1:
+        return np.float32(t0)
+    return np.float32(t0 + (t1 - t0) * float(t) / float(max_steps - 1))
+
+
+def inv_temperature(T: np.float32) -> np.float32:
+    return np.float32(1.0 / float(T))
+
+
+def gumbel_block(seed: int, canvas: int, step: int, pos: np.ndarray, vocab: int) -> np.ndarray:
+    """Gumbel noise g[len(pos), vocab] (fp32) of the GUMBEL stream at one step."""
+    pos = np.asarray(pos, np.int64)
+    nblk = (vocab + 3) // 4
+    ctr = np.empty((pos.size, nblk, 4), np.uint32)
+    ctr[..., 0] = np.arange(nblk, dtype=np.uint32)[None, :]
+    ctr[..., 1] = pos.astype(np.uint32)[:, None]
+    ctr[..., 2] = np.uint32(step)
+    ctr[..., 3] = np.uint32((philox.TAG_GUMBEL << 24) | (canvas & 0xFFFFFF))
+    w = philox.philox4x32_10(ctr, philox.seed_key(seed)).reshape(pos.size, nblk * 4)[:, :vocab]
+    return philox.gumbel(w)
+
+
+def head_stats(logits: np.ndarray, inv_t: np.float32, seed: int, canvas: int, step: int,
+               pos: np.ndarray, want_probs: bool = False, chunk: int = 16) -> Dict[str, np.ndarray]:
+    """Per-row statistics of the tempered distribution and the Gumbel-max draw.
+
+    logits: fp32 [n, V].  z = logits * (1/T) in fp32.  Returns
+      H      entropy of softmax(z) in nats (fp64 evaluation, fp32 result)
+      am     argmax of the logits (lowest id on ties)
+      y      argmax_v (z_v + g_v) with fp32 scores (lowest id on ties)
+      margin best minus second-best perturbed score (fp32)
+      m, logS  max of z and log of sum exp(z - m)  (fp64)
+      p      softmax(z) (fp64), only if want_probs
+    """
+    logits = np.asarray(logits, np.float32)
+    n, V = logits.shape
+    out = {k: np.empty(n, t) for k, t in
+           (("H", np.float32), ("am", np.int32), ("y", np.int32), ("margin", np.float32),
+            ("m", np.float64), ("logS", np.float64))}
+    probs = np.empty((n, V), np.float64) if want_probs else None
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        z = logits[r0:r1] * np.float32(inv_t)                         # fp32
+        z64 = z.astype(np.float64)
+        m = z64.max(axis=1, keepdims=True)
+        e = np.exp(z64 - m)
+        S = e.sum(axis=1, keepdims=True)
+        H = np.log(S[:, 0]) - (e * (z64 - m)).sum(axis=1) / S[:, 0]
+        out["H"][r0:r1] = H.astype(np.float32)
+        out["m"][r0:r1] = m[:, 0]
+        out["logS"][r0:r1] = np.log(S[:, 0])
+        out["am"][r0:r1] = np.argmax(logits[r0:r1], axis=1)
+        g = gumbel_block(seed, canvas, step, pos[r0:r1], V)
+        score = z + g                                                 # fp32
+        y = np.argmax(score, axis=1)
+        best = score[np.arange(r1 - r0), y]
+        masked = score.copy()
+        masked[np.arange(r1 - r0), y] = -np.inf
+        out["y"][r0:r1] = y
+        out["margin"][r0:r1] = best - masked.max(axis=1)
+        if want_probs:
+            probs[r0:r1] = e / S
+    if want_probs:
+        out["p"] = probs
+    return out
+
+
+def commit(H: np.ndarray, y: np.ndarray, am: np.ndarray, prev_am: Optional[np.ndarray],
+           canvas: np.ndarray, step: int, max_steps: int, entropy_bound: float,
+           stop_mode: int, stop_tau: float, seed: int, canvas_index: int, vocab: int):
+    """One request's commit / re-noise / stop decision.
+
+    Returns (new_canvas int32[n], mask uint8[n], n_committed, done).
+    """
+    H = np.asarray(H, np.float32)
+    n = H.size
+    pos = np.arange(n)
+    order = np.lexsort((pos, H))              # entropy ascending, then position
+    bound = float(np.float32(entropy_bound))
+    mask = np.zeros(n, np.uint8)
+    total = 0.0
+    for i in order:
+        total += float(H[i])
+        if total <= bound:
+            mask[i] = 1
+        else:
+            break
+    mean = 0.0
+    for i in range(n):
+        mean += float(H[i])
+    mean /= n
+    tau = float(np.float32(stop_tau))
+    stop = False
+    if stop_mode == STOP_MEAN:
+        stop = mean < tau
+    elif stop_mode == STOP_PAGES:
+        stop = (mean < tau and prev_am is not None and step > 0
+                and bool(np.all(np.asarray(am) == np.asarray(prev_am))))
+    final = stop or step >= max_steps - 1
+    if final:
+        return np.asarray(y, np.int32).copy(), np.ones(n, np.uint8), n, True
+    w = philox.words(seed, philox.TAG_RENOISE, canvas_index, step, pos, 0)
+    fresh = philox.uniform_token(w, vocab)
+    new = np.where(mask == 1, np.asarray(y, np.int32), fresh).astype(np.int32)
+    return new, mask, int(mask.sum()), False
+
+
+def init_canvas(seed: int, canvas_index: int, n: int, vocab: int) -> np.ndarray:
+    """Initial canvas: n uniformly random tokens ([mlqm] 一: the canvas starts as random words)."""
+    w = philox.words(seed, philox.TAG_INIT, canvas_index, 0, np.arange(n), 0)
+    return philox.uniform_token(w, vocab)
