@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of the denoise-step hot path on one MI355X.
+
+A step is one dg_denoise_step + dg_sample_commit over the canvas batch; at the
+end of each canvas's step budget the canvas is appended to the KV cache
+(dg_commit_canvas_to_kv, inside the timed region) and a fresh canvas starts.
+value = committed canvas tokens per second = B * 256 * canvases / seconds,
+with a partially finished canvas counted pro rata.  Inputs (weights, prompt)
+are seeded synthetic data already resident in device memory when timing
+starts; the prompt encode is timed separately.
+
+The dominant stage is picked from an all-stage timing pass during warm-up, then
+timed live with HIP events inside the library (on the launch stream) during
+the timed region; its algorithmic bytes / flops per launch give the roofline.
+The CPU baseline is the oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import dg_inputs as di  # noqa: E402
+
+METRIC = "committed canvas tok/s + denoise-step latency (ms), 1×MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
+    """Algorithmic (bytes, flops) of one launch of a stage at canvas shape."""
+    es = 2 if mc.dtype == "bf16" else 4
+    n = mc.canvas_len
+    R = B * n
+    d, F, k, V = mc.d_model, mc.ffn_hidden, mc.top_k, mc.vocab
+    hd, Hq, Hkv = mc.head_dim, mc.n_q_heads, mc.n_kv_heads
+    keys = ctx + n
+    if stage == "expert_up":
+        by = n_experts_active * 2 * F * d * es + R * d * es + R * k * F * es
+        fl = 2 * R * k * d * F * 2
+    elif stage == "expert_down":
+        by = n_experts_active * d * F * es + R * k * F * es + R * k * d * 4
+        fl = 2 * R * k * F * d
+    elif stage == "lm_head":
+        by = V * d * es + R * d * es + R * V * 4
+        fl = 2 * R * d * V
+    elif stage == "attn":
+        by = 2 * B * Hkv * keys * hd * es + 2 * R * Hq * hd * es
+        fl = 4 * R * Hq * keys * hd
+    elif stage == "sampler":
+        by = R * V * 4 + (R * V * es if mc.self_cond else 0)
+        fl = 0
+    elif stage == "selfcond":
+        by = R * V * es + V * d * es + R * d * 4
+        fl = 2 * R * V * d
+    elif stage == "qkv":
+        by = (Hq + 2 * Hkv) * hd * d * es + R * d * es + R * (Hq + 2 * Hkv) * hd * 4
+        fl = 2 * R * d * (Hq + 2 * Hkv) * hd
+    elif stage == "oproj":
+        by = Hq * hd * d * es + R * Hq * hd * es + 2 * R * d * 4
+        fl = 2 * R * Hq * hd * d
+    else:
+        return None
+    return by, fl
+
+
+def roofline(stage, ms_total, launches, mc, B, ctx, n_act):
+    w = stage_work(stage, mc, B, ctx, n_act)
+    if w is None or launches == 0:
+        return None
+    by, fl = w
+    t = ms_total / launches / 1e3
+    peak_t = MFMA_PEAK_TFLOPS[mc.dtype]
+    if fl / max(by, 1) > peak_t * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = fl / t / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_t, "unit": "TFLOP/s",
+                "frac": round(ach / peak_t, 4), "traffic": None, "kernel": stage,
+                "launch_us": round(t * 1e6, 2), "bytes_per_launch": by, "flops_per_launch": fl}
+    ach = by / t / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": stage,
+            "launch_us": round(t * 1e6, 2), "bytes_per_launch": by, "flops_per_launch": fl}
+
+
+def cpu_baseline(wl, weights, prompts, seeds, budget_s: float):
+    """Oracle on the host cores: prompt encode, then denoise steps and one canvas commit."""
+    from oracle.model import OracleModel
+    from oracle import sampler as osmp
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    mc, sp = wl.model, wl.sampler
+    B = wl.batch
+    om = OracleModel(mc, weights, B, wl.prompt_len + 2 * mc.canvas_len)
+    t0 = time.perf_counter()
+    om.encode_prompt(prompts)
+    t_enc = time.perf_counter() - t0
+    canvas = np.stack([osmp.init_canvas(int(seeds[b]), 0, mc.canvas_len, mc.vocab) for b in range(B)])
+    steps, t_steps = 0, 0.0
+    while steps < 2 or (t_steps < budget_s * 0.5 and steps < sp.max_steps):
+        t0 = time.perf_counter()
+        out = om.denoise_step(canvas, steps, sp, seeds)
+        for b in range(B):
+            canvas[b], _, _, _ = osmp.commit(out["H"][b], out["y"][b], out["am"][b], None, canvas[b], steps,
+                                             sp.max_steps, sp.entropy_bound, sp.stop_mode, sp.stop_tau,
+                                             int(seeds[b]), 0, mc.vocab)
+        t_steps += time.perf_counter() - t0
+        steps += 1
+    t0 = time.perf_counter()
+    om.commit_canvas_to_kv(canvas)
+    t_commit = time.perf_counter() - t0
+    t_step = t_steps / steps
+    tok_s = B * mc.canvas_len / (sp.max_steps * t_step + t_commit)
+    return {"value": round(tok_s, 3), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{wl.name}: prompt encode ({wl.prompt_len} tokens x {B}) {t_enc:.2f} s, "
+                       f"{steps} denoise+commit steps {t_step:.3f} s/step, canvas commit {t_commit:.2f} s; "
+                       f"tok/s = {B}*{mc.canvas_len} / ({sp.max_steps} steps * s/step + commit)"),
+            "ms_per_step": round(t_step * 1e3, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--workload", default="small", choices=sorted(di.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the multi-GPU sharding of this path "
+              "is a design note, not an implemented mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from discrete_text_diffusion_dg_amd.runtime import Engine, upload_weights
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    wl = di.workload(a.workload)
+    mc, sp = wl.model, wl.sampler
+    B, n, S = wl.batch, mc.canvas_len, sp.max_steps
+    total_steps = a.warmup + a.steps
+    canvases = (total_steps + S - 1) // S + 1
+    max_ctx = wl.prompt_len + n * (canvases + 1)
+    t0 = time.perf_counter()
+    W = di.make_weights(mc, wl.seed)
+    names = W.names()
+    dw = upload_weights(W, names, "cuda")
+    log(f"[bench] {wl.name}: weights {W.nbytes() / 1e9:.2f} GB generated+uploaded in {time.perf_counter() - t0:.1f} s")
+    eng = Engine(mc, dw, names, B, max_ctx)
+    seeds = di.request_seeds(wl.seed, B)
+    eng.set_seeds(seeds)
+    prompts = di.make_prompts(mc.vocab, B, wl.prompt_len, wl.seed)
+    pt = torch.from_numpy(prompts).cuda()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    eng.encode_prompt(pt)
+    e1.record()
+    torch.cuda.synchronize()
+    encode_ms = e0.elapsed_time(e1)
+    log(f"[bench] prompt encode {encode_ms:.2f} ms")
+
+    state = {"t": 0, "canvases_done": 0}
+    eng.init_canvas()
+
+    def one_step():
+        t = state["t"]
+        eng.denoise_step(t, sp)
+        eng.sample_commit(t, sp)
+        t += 1
+        if sp.stop_mode != 0:
+            finished = bool((eng.done != 0).all())
+        else:
+            finished = t >= S
+        if finished or t >= S:
+            eng.commit_canvas_to_kv()
+            state["canvases_done"] += 1
+            eng.init_canvas()
+            eng.done.zero_()
+            t = 0
+        state["t"] = t
+
+    # warm-up, with every stage timed to find the dominant one
+    eng.profile(["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
+                 "lm_head", "sampler", "selfcond", "commit"])
+    for _ in range(a.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    prof = eng.profile_read()
+    ctx_w = eng.ctx_len
+    dominant = max(prof, key=lambda k: prof[k][0]) if prof else "expert_up"
+    log("[bench] warm-up stage ms: " + ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in prof.items()))
+    routed = eng.route_view(B * n).cpu().numpy()
+    n_act = int(np.unique(routed).size)
+
+    # timed region: exactly K steps, only the dominant stage carries events
+    eng.profile([dominant])
+    state["canvases_done"] = 0
+    t_start_step = state["t"]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        one_step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = e0.elapsed_time(e1)
+    dom_ms, dom_n = eng.profile_read().get(dominant, (0.0, 0))
+    eng.profile([])
+    canv = a.steps / S
+    tok_s = B * n * canv / (ms / 1e3)
+    rl = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act)
+    log(f"[bench] {a.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); dominant {dominant}: "
+        f"{dom_ms / max(dom_n, 1) * 1e3:.1f} us/launch")
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(wl, W, prompts, seeds, a.cpu_budget)
+            log(f"[bench] cpu baseline {cpu['value']} tok/s ({cpu['sample']})")
+        except Exception as ex:  # reported, never fatal for the GPU number
+            cpu = {"value": None, "unit": "tok/s", "cores": os.cpu_count(), "kind": "oracle",
+                   "sample": f"failed: {ex!r}"}
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms / a.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": mc.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "canvas": n, "prompt_len": wl.prompt_len,
+                   "steps_per_canvas": S, "layers": mc.n_layers, "d_model": mc.d_model,
+                   "experts": f"{mc.top_k}/{mc.n_experts}", "vocab": mc.vocab,
+                   "self_cond": mc.self_cond, "parallelism": "none (1 GPU)"},
+        "steps_per_s": round(a.steps / (ms / 1e3), 2),
+        "encode_ms": round(encode_ms, 3),
+        "stage_ms_warmup": {k: round(v[0] / max(a.warmup, 1), 4) for k, v in prof.items()},
+        "roofline": rl,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    eng.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+// Device-side building blocks shared by the gfx950 kernels of the denoise step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// ------------------------------------------------------------------ types
+// bfloat16 is kept as raw bits in memory; arithmetic is always fp32.
+struct bf16 {
+  uint16_t bits;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Num;
+template <> struct Num<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+  __device__ __forceinline__ static float round(float v) { return v; }
+};
+template <> struct Num<bf16> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const bf16* p) { return bf16_to_f32(p->bits); }
+  __device__ __forceinline__ static void store(bf16* p, float v) { p->bits = f32_to_bf16_bits(v); }
+  __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16_bits(v)); }
+};
+
+// Pack 8 fp32 values into 16 bytes (bf16) or 32 bytes (fp32) of operand data.
+__device__ __forceinline__ uint4 pack8_bf16(const float* v) {
+  uint4 r;
+  r.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+  r.z = (uint32_t)f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
+  r.w = (uint32_t)f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+  return r;
+}
+
+// ------------------------------------------------------------------ MFMA
+// Fragment: 8 consecutive k-elements of one row (A) or one column (B) per lane.
+// Lane l supplies row/column (l & 15); its lane group g = l >> 4 supplies the
+// k-elements g*8 .. g*8+7 of a 32-wide k step.  A and B use the same mapping,
+// so the products pair up whatever order the unit sums them in.
+// Accumulator: lane l holds C[(l>>4)*4 + i][l & 15], i = 0..3.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+  uint4 v;  // 8 bf16
+};
+template <> struct Frag<float> {
+  float v[8];
+};
+
+__device__ __forceinline__ void mma16x16x32(f32x4_t& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  bf16x8_t av = __builtin_bit_cast(bf16x8_t, a.v);
+  bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b.v);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16x16x32(f32x4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// Load a fragment from shared memory: 8 consecutive elements starting at p.
+__device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void lds_frag(Frag<float>& f, const float* p) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ------------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): ten rounds of two 32x32->64 multiplies, xor with the key and the
+// odd counter words, key advanced by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t a = c.x, b = c.z;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, a), lo0 = 0xD2511F53u * a;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, b), lo1 = 0xCD9E8D57u * b;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+enum : uint32_t { kTagInit = 2, kTagGumbel = 3, kTagRenoise = 4 };
+
+// Counter layout: (j >> 2, position, step, tag << 24 | canvas), output word j & 3.
+__device__ __forceinline__ uint4 philox_block(uint64_t seed, uint32_t tag, uint32_t canvas,
+                                              uint32_t step, uint32_t pos, uint32_t jblock) {
+  uint4 c = make_uint4(jblock, pos, step, (tag << 24) | (canvas & 0xFFFFFFu));
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// Uniform in (0, 1): (2 * (x >> 9) + 1) * 2^-24, exact in fp32.
+__device__ __forceinline__ float u01(uint32_t x) {
+  return (float)(2u * (x >> 9) + 1u) * 5.9604644775390625e-08f;
+}
+__device__ __forceinline__ float gumbel_of(uint32_t x) { return -logf(-logf(u01(x))); }
+__device__ __forceinline__ int32_t token_of(uint32_t x, int32_t vocab) {
+  return (int32_t)(((uint64_t)x * (uint64_t)(uint32_t)vocab) >> 32);
+}
+
+}  // namespace dg

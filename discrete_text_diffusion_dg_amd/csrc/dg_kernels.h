@@ -1,0 +1,115 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Each returns the launch status (hipGetLastError after the launch).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dg_common.h"
+
+namespace dg {
+
+// Per-request Philox seeds travel by value in the kernel arguments, so a step
+// needs no host-to-device copy.
+constexpr int kMaxBatch = 128;
+struct SeedArg {
+  uint64_t v[kMaxBatch];
+};
+
+// One expert-routed tile: (expert, first gathered row, rows, unused).
+// Capacity of the tile list for R rows routed to k experts each, 64-row tiles.
+inline int expert_tile_capacity(int rows, int top_k, int n_experts) {
+  return (rows * top_k + 63) / 64 + n_experts;
+}
+
+// ---- matrix products (k_gemm.hip); B operands are [N, K] K-contiguous
+template <typename T>
+hipError_t gemm_store_f32(const T* A, int lda, const T* B, int ldb, float* C, int ldc, int M, int N,
+                          int K, hipStream_t s);
+template <typename T>
+hipError_t gemm_resid_add(const T* A, int lda, const T* B, int ldb, float* H, int ldh, int M, int N,
+                          int K, hipStream_t s);
+// H[r][c] = emb[tok[r]][c] + (S[r] rounded to T) . W[c]; ids clamped to [0, vocab)
+template <typename T>
+hipError_t gemm_embed_selfcond(const float* S, const T* W, const T* emb, const int32_t* tok,
+                               float* H, int M, int d, int vocab, hipStream_t s);
+// act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
+template <typename T>
+hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
+                              const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F,
+                              hipStream_t s);
+// Y[g][c] = act[g] . down_e[c]
+template <typename T>
+hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
+                            const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
+// part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of P[r][k] * Bt[c][k]
+template <typename T>
+hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, int M, int N, int K,
+                       int splits, int kchunk, hipStream_t s);
+
+// ---- attention (k_attn.hip)
+struct AttnArgs {
+  const void* q;        // [B*nq, Hq*hd] operand type, RoPE applied
+  const void* kc;       // K cache of this layer: [B][Hkv][max_ctx][hd]
+  const void* vc;       // V cache of this layer
+  void* out;            // [B*nq, Hq*hd] operand type
+  float* part_o;        // split partials [splits][B*nq*Hq][hd] (fp32, unnormalised)
+  float* part_ml;       // split partials [splits][B*nq*Hq][2] (running max, sum)
+  int B, nq, Hq, Hkv, hd, max_ctx;
+  int ctx;              // keys 0..ctx+nq-1 (the new rows sit at ctx..ctx+nq-1)
+  int causal;
+  int splits;
+  float scale;
+};
+template <typename T>
+hipError_t attention(const AttnArgs& a, hipStream_t s);
+int attention_splits(int B, int nq, int Hq, int Hkv, int keys);
+
+// ---- small kernels (k_misc.hip)
+template <typename T>
+hipError_t embed_rows(const T* emb, const int32_t* tok, float* H, int M, int d, int vocab, hipStream_t s);
+template <typename T>
+hipError_t rmsnorm_rows(const float* H, const float* g, T* out, int M, int d, float eps, hipStream_t s);
+// RoPE on q and k of the fused projection, q -> Q buffer, k and v -> cache at ctx + i
+template <typename T>
+hipError_t rope_scatter(const float* qkv, const float2* rope, T* q, T* kc, T* vc, int B, int n,
+                        int Hq, int Hkv, int hd, int max_ctx, int ctx, hipStream_t s);
+hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
+hipError_t router_topk(const float* logits, int M, int E, int k, int* idx, float* w, hipStream_t s);
+hipError_t route_bucket(const int* idx, int M, int k, int E, int* chunk_counts, int* perm, int* pos,
+                        int4* tiles, int* n_tiles, hipStream_t s);
+hipError_t moe_combine(const float* Y, const int* pos, const float* w, float* H, int M, int k, int d,
+                       hipStream_t s);
+template <typename T>
+hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
+hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab,
+                       int canvas_index, hipStream_t s);
+
+// ---- sampler (k_sampler.hip)
+struct HeadPart {       // statistics of one (row, vocab chunk)
+  float m;              // max of z = logit / T
+  float s;              // sum exp(z - m)
+  float w;              // sum exp(z - m) * (z - m)
+  float lmax;           // max logit
+  int lidx;             // its index (lowest on ties)
+  float g1;             // best Gumbel-perturbed score
+  int gidx;             // its index
+  float g2;             // second-best score
+};
+int sampler_chunks(int vocab);
+int sampler_chunk_len(int vocab, int chunks);   // a multiple of 64
+template <typename T>
+hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float inv_t,
+                           const SeedArg& seeds, int n, int canvas_index, int step,
+                           HeadPart* part, T* ptilde, hipStream_t s);
+hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
+                         float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale,
+                         hipStream_t s);
+hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks,
+                           float* S, hipStream_t s);
+hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,
+                         int32_t* prev_am, uint8_t* mask, int32_t* n_committed, uint8_t* done,
+                         const SeedArg& seeds, int B, int n, int vocab, int step, int max_steps,
+                         float bound, int stop_mode, float tau, int canvas_index, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,309 @@
+// Sampler of the denoise step ([mlqm] 四: entropy-ordered commit with a 0.1 nat
+// running bound, uniform re-randomisation of the rest, temperature 0.8 -> 0.4,
+// adaptive stop; [mlqm] 一: multinomial diffusion replaces an uncertain
+// position by any vocabulary token).
+//
+// Head statistics are computed in one read of the logits: each workgroup owns
+// one (row, vocab chunk); it keeps its z = logit / T values in registers, takes
+// the chunk max, the logit argmax and the Gumbel-max top two (Philox draws,
+// four vocabulary ids per call), then sums exp(z - m) and exp(z - m)(z - m),
+// and writes exp(z - m) rounded to the operand type for the self-conditioning
+// contraction.  A merge pass combines the chunks of a row in order.
+#include "dg_kernels.h"
+
+namespace dg {
+
+namespace {
+constexpr int kChunkMax = 4096;         // vocabulary ids per workgroup (16 per thread)
+constexpr int kPerThread = kChunkMax / 256;
+}
+
+int sampler_chunks(int vocab) {
+  int c = (vocab + kChunkMax - 1) / kChunkMax;
+  return c < 1 ? 1 : c;
+}
+// chunk length: a multiple of 64 so that split-K slices of the contraction align
+static __host__ __device__ inline int chunk_len(int vocab, int chunks) {
+  const int per = (vocab + chunks - 1) / chunks;
+  return (per + 63) / 64 * 64;
+}
+
+struct Top2 {
+  float b1; int i1; float b2;
+};
+__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
+  if (o.b1 > a.b1 || (o.b1 == a.b1 && o.i1 < a.i1)) {
+    a.b2 = fmaxf(a.b1, o.b2);
+    a.b1 = o.b1; a.i1 = o.i1;
+  } else {
+    a.b2 = fmaxf(a.b2, o.b1);
+  }
+}
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, int V, int chunks, int clen,
+                                                         float inv_t, SeedArg seeds, int n,
+                                                         int canvas_index, int step, HeadPart* part,
+                                                         T* ptilde) {
+  __shared__ float red_f[3][4];
+  __shared__ int red_i[2][4];
+  __shared__ float red_b2[4];
+  const int chunk = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = row / n, pos = row % n;
+  const int v0 = chunk * clen, v1 = min(V, v0 + clen);
+  const float* L = logits + (size_t)row * V;
+  const uint64_t seed = seeds.v[b];
+
+  float z[kPerThread];
+  float zmax = -INFINITY, lmax = -INFINITY;
+  int lidx = 0x7fffffff;
+  Top2 t2{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+  for (int it = 0; it < kPerThread / 4; ++it) {
+    const int v = v0 + (it * 256 + tid) * 4;
+    if (v < v1) {
+      const float4 l4 = *reinterpret_cast<const float4*>(L + v);
+      const uint4 x = philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
+                                   (uint32_t)(v >> 2));
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float zz = lv[j] * inv_t;
+        z[it * 4 + j] = zz;
+        zmax = fmaxf(zmax, zz);
+        argmax_merge(lmax, lidx, lv[j], v + j);
+        const float sc = zz + gumbel_of(xv[j]);
+        top2_merge(t2, Top2{sc, v + j, -INFINITY});
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[it * 4 + j] = -INFINITY;
+    }
+  }
+  // workgroup reductions (fixed order)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    zmax = fmaxf(zmax, __shfl_xor(zmax, o, 64));
+    const float ol = __shfl_xor(lmax, o, 64);
+    const int oi = __shfl_xor(lidx, o, 64);
+    argmax_merge(lmax, lidx, ol, oi);
+    Top2 ot{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)};
+    top2_merge(t2, ot);
+  }
+  if (lane == 0) {
+    red_f[0][w] = zmax; red_f[1][w] = lmax; red_f[2][w] = t2.b1;
+    red_i[0][w] = lidx; red_i[1][w] = t2.i1; red_b2[w] = t2.b2;
+  }
+  __syncthreads();
+  zmax = red_f[0][0];
+  lmax = red_f[1][0]; lidx = red_i[0][0];
+  t2 = Top2{red_f[2][0], red_i[1][0], red_b2[0]};
+  for (int q = 1; q < 4; ++q) {
+    zmax = fmaxf(zmax, red_f[0][q]);
+    argmax_merge(lmax, lidx, red_f[1][q], red_i[0][q]);
+    top2_merge(t2, Top2{red_f[2][q], red_i[1][q], red_b2[q]});
+  }
+  __syncthreads();
+
+  float s = 0.f, ws = 0.f;
+#pragma unroll
+  for (int it = 0; it < kPerThread / 4; ++it) {
+    const int v = v0 + (it * 256 + tid) * 4;
+    if (v < v1) {
+      float e4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float dz = z[it * 4 + j] - zmax;
+        const float e = expf(dz);
+        e4[j] = e;
+        s += e;
+        ws += e * dz;
+      }
+      if (ptilde != nullptr) {
+        T* dst = ptilde + (size_t)row * V + v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Num<T>::store(dst + j, e4[j]);
+      }
+    }
+  }
+  s = wave_sum(s);
+  ws = wave_sum(ws);
+  if (lane == 0) { red_f[0][w] = s; red_f[1][w] = ws; }
+  __syncthreads();
+  if (tid == 0) {
+    s = red_f[0][0] + red_f[0][1] + red_f[0][2] + red_f[0][3];
+    ws = red_f[1][0] + red_f[1][1] + red_f[1][2] + red_f[1][3];
+    HeadPart hp;
+    hp.m = zmax; hp.s = s; hp.w = ws; hp.lmax = lmax; hp.lidx = lidx;
+    hp.g1 = t2.b1; hp.gidx = t2.i1; hp.g2 = t2.b2;
+    part[(size_t)row * chunks + chunk] = hp;
+  }
+}
+
+// One thread per row: combine chunk statistics in chunk order (fp64).
+__global__ void k_sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
+                                float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= M) return;
+  const HeadPart* p = part + (size_t)r * chunks;
+  double m = -INFINITY;
+  for (int c = 0; c < chunks; ++c) m = fmax(m, (double)p[c].m);
+  double S = 0.0, W = 0.0;
+  float lmax = p[0].lmax;
+  int lidx = p[0].lidx;
+  Top2 t2{p[0].g1, p[0].gidx, p[0].g2};
+  for (int c = 0; c < chunks; ++c) {
+    const double f = exp((double)p[c].m - m);
+    S += (double)p[c].s * f;
+    W += f * ((double)p[c].w + ((double)p[c].m - m) * (double)p[c].s);
+    if (c > 0) {
+      argmax_merge(lmax, lidx, p[c].lmax, p[c].lidx);
+      top2_merge(t2, Top2{p[c].g1, p[c].gidx, p[c].g2});
+    }
+  }
+  if (chunk_scale != nullptr)
+    for (int c = 0; c < chunks; ++c) chunk_scale[(size_t)r * chunks + c] = (float)(exp((double)p[c].m - m) / S);
+  if (active != nullptr && active[r / n] == 0) return;
+  H[r] = (float)(log(S) - W / S);
+  y[r] = t2.i1;
+  am[r] = lidx;
+  margin[r] = t2.b1 - t2.b2;
+}
+
+// s[r][c] = sum over chunks of scale[r][chunk] * part[chunk][r][c], chunk order.
+__global__ void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks,
+                                  float* S) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * d) return;
+  const size_t r = i / d;
+  float acc = 0.f;
+  for (int c = 0; c < chunks; ++c) acc += chunk_scale[r * chunks + c] * part[(size_t)c * M * d + i];
+  S[i] = acc;
+}
+
+// ------------------------------------------------------------------ commit
+// One workgroup per request: bitonic sort of (H, position), fp64 running total
+// in sorted order (thread 0, sequential, so the rounding is fixed), then every
+// position takes y or a fresh uniform token.
+__global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y, const int32_t* am,
+                                                int32_t* canvas, int32_t* prev_am, uint8_t* mask,
+                                                int32_t* n_committed, uint8_t* done, SeedArg seeds, int n,
+                                                int vocab, int step, int max_steps, float bound,
+                                                int stop_mode, float tau, int canvas_index) {
+  __shared__ float sh[256];
+  __shared__ int sp[256];
+  __shared__ int rank[256];
+  __shared__ int s_cnt, s_final, s_diff;
+  const int b = blockIdx.x, t = threadIdx.x;
+  if (done[b]) return;
+  const size_t base = (size_t)b * n;
+  sh[t] = t < n ? H[base + t] : INFINITY;
+  sp[t] = t;
+  if (t == 0) s_diff = 0;
+  __syncthreads();
+  if (t < n && stop_mode == 2 && am[base + t] != prev_am[base + t]) s_diff = 1;
+  for (int k = 2; k <= 256; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = t ^ j;
+      if (o > t) {
+        const bool asc = (t & k) == 0;
+        const float ha = sh[t], hb = sh[o];
+        const int pa = sp[t], pb = sp[o];
+        const bool gt = ha > hb || (ha == hb && pa > pb);
+        if (gt == asc) { sh[t] = hb; sh[o] = ha; sp[t] = pb; sp[o] = pa; }
+      }
+      __syncthreads();
+    }
+  }
+  rank[sp[t]] = t;
+  if (t == 0) {
+    const double bnd = (double)bound;
+    double c = 0.0;
+    int cnt = 0;
+    for (int j = 0; j < n; ++j) {
+      c += (double)sh[j];
+      if (c <= bnd) ++cnt; else break;
+    }
+    double mean = 0.0;
+    for (int i = 0; i < n; ++i) mean += (double)H[base + i];
+    mean /= (double)n;
+    bool stop = false;
+    if (stop_mode == 1) stop = mean < (double)tau;
+    else if (stop_mode == 2) stop = mean < (double)tau && step > 0 && s_diff == 0;
+    const bool fin = stop || step >= max_steps - 1;
+    s_cnt = cnt;
+    s_final = fin ? 1 : 0;
+  }
+  __syncthreads();
+  if (t < n) {
+    const bool fin = s_final != 0;
+    const bool keep = fin || rank[t] < s_cnt;
+    int32_t tok = y[base + t];
+    if (!keep) {
+      const uint4 x = philox_block(seeds.v[b], kTagRenoise, (uint32_t)canvas_index, (uint32_t)step,
+                                   (uint32_t)t, 0u);
+      tok = token_of(x.x, vocab);
+    }
+    canvas[base + t] = tok;
+    mask[base + t] = keep ? 1 : 0;
+    prev_am[base + t] = am[base + t];
+  }
+  if (t == 0) {
+    n_committed[b] = s_final ? n : s_cnt;
+    done[b] = (uint8_t)s_final;
+  }
+}
+
+}  // namespace dg
+
+namespace dg {
+
+template <typename T>
+hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float inv_t, const SeedArg& seeds,
+                           int n, int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int clen = chunk_len(V, chunks);
+  if (clen > kChunkMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_sampler_partial<T>), dim3(chunks, M), dim3(256), 0, s, logits, V, chunks, clen, inv_t,
+                     seeds, n, canvas_index, step, part, ptilde);
+  return hipGetLastError();
+}
+
+hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active, float* H,
+                         int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sampler_merge, dim3((M + 127) / 128), dim3(128), 0, s, part, M, chunks, n, active, H, y,
+                     am, margin, chunk_scale);
+  return hipGetLastError();
+}
+
+hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, float* S,
+                           hipStream_t s) {
+  const size_t nel = (size_t)M * d;
+  if (nel == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s, part, chunk_scale,
+                     M, d, chunks, S);
+  return hipGetLastError();
+}
+
+hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas, int32_t* prev_am,
+                         uint8_t* mask, int32_t* n_committed, uint8_t* done, const SeedArg& seeds, int B, int n,
+                         int vocab, int step, int max_steps, float bound, int stop_mode, float tau,
+                         int canvas_index, hipStream_t s) {
+  hipLaunchKernelGGL(k_commit, dim3(B), dim3(256), 0, s, H, y, am, canvas, prev_am, mask, n_committed, done, seeds,
+                     n, vocab, step, max_steps, bound, stop_mode, tau, canvas_index);
+  return hipGetLastError();
+}
+
+int sampler_chunk_len(int vocab, int chunks) { return chunk_len(vocab, chunks); }
+
+template hipError_t sampler_partial<float>(const float*, int, int, int, float, const SeedArg&, int, int, int,
+                                           HeadPart*, float*, hipStream_t);
+template hipError_t sampler_partial<bf16>(const float*, int, int, int, float, const SeedArg&, int, int, int,
+                                          HeadPart*, bf16*, hipStream_t);
+
+}  // namespace dg

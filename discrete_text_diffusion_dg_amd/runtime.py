@@ -1,0 +1,202 @@
+"""Engine: torch-owned device buffers around the libdg.so handles.
+
+torch supplies device memory and the stream; every step of the denoise path
+runs in the library's HIP kernels.  The generate loop follows the pages'
+block-autoregressive sampling: encode the prompt, then per canvas draw random
+tokens, run denoise + commit rounds until the request stops or the budget
+ends, and append the finished canvas to the KV cache ([chooseai] multi-canvas
+paragraph; [bohu] 一; [mlqm] 四).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def config_struct(mc) -> L.DgConfig:
+    return L.DgConfig(mc.n_layers, mc.d_model, mc.n_q_heads, mc.n_kv_heads, mc.head_dim, mc.n_experts,
+                      mc.ffn_hidden, mc.top_k, mc.vocab, mc.canvas_len,
+                      L.DG_DTYPE_BF16 if mc.dtype == "bf16" else L.DG_DTYPE_F32,
+                      1 if mc.self_cond else 0, mc.rope_theta, mc.rms_eps)
+
+
+def sampler_struct(sp) -> L.DgSamplerParams:
+    return L.DgSamplerParams(sp.t_start, sp.t_end, sp.entropy_bound, sp.stop_tau, sp.max_steps,
+                             sp.stop_mode)
+
+
+def upload_weights(weights, names: Sequence[str], device) -> Dict[str, torch.Tensor]:
+    """Host arrays (float32, or uint16 bfloat16 bits) -> device tensors, same bytes."""
+    out = {}
+    for n in names:
+        a = np.ascontiguousarray(weights.get(n))
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a).to(device)
+        out[n] = t
+    return out
+
+
+class Engine:
+    """One model + one state (batch of requests sharing a context length)."""
+
+    def __init__(self, model_cfg, device_weights: Dict[str, torch.Tensor], names: Sequence[str],
+                 batch: int, max_ctx: int, device="cuda"):
+        self.lib = L.load()
+        self.cfg = model_cfg
+        self.device = torch.device(device)
+        self.B, self.n, self.max_ctx = batch, model_cfg.canvas_len, max_ctx
+        self.weights = device_weights                          # keep alive
+        self._cfg = config_struct(model_cfg)
+        ptrs = (ctypes.c_void_p * len(names))(*[device_weights[n].data_ptr() for n in names])
+        self._model = ctypes.c_void_p()
+        L.check(self.lib.dg_model_create(ctypes.byref(self._cfg), ptrs, len(names), ctypes.byref(self._model)))
+        nbytes = ctypes.c_size_t()
+        L.check(self.lib.dg_state_bytes(self._model, batch, max_ctx, ctypes.byref(nbytes)))
+        self.state_buf = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+        self._state = ctypes.c_void_p()
+        L.check(self.lib.dg_state_init(self._model, self.state_buf.data_ptr(), nbytes.value, batch, max_ctx,
+                                       ctypes.byref(self._state)))
+        B, n, dev = batch, self.n, self.device
+        self.canvas = torch.zeros(B, n, dtype=torch.int32, device=dev)
+        self.H = torch.zeros(B, n, dtype=torch.float32, device=dev)
+        self.y = torch.zeros(B, n, dtype=torch.int32, device=dev)
+        self.am = torch.zeros(B, n, dtype=torch.int32, device=dev)
+        self.margin = torch.zeros(B, n, dtype=torch.float32, device=dev)
+        self.mask = torch.zeros(B, n, dtype=torch.uint8, device=dev)
+        self.n_committed = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.done = torch.zeros(B, dtype=torch.uint8, device=dev)
+        self.seeds = np.zeros(B, np.uint64)
+
+    # ------------------------------------------------------------ lifetime
+    def close(self) -> None:
+        if getattr(self, "_state", None):
+            self.lib.dg_state_destroy(self._state)
+            self._state = None
+        if getattr(self, "_model", None):
+            self.lib.dg_model_destroy(self._model)
+            self._model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ helpers
+    def _stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def set_seeds(self, seeds: np.ndarray) -> None:
+        self.seeds = np.ascontiguousarray(seeds, dtype=np.uint64)
+        assert self.seeds.size == self.B
+
+    def _seed_ptr(self):
+        return self.seeds.ctypes.data_as(ctypes.c_void_p)
+
+    @property
+    def ctx_len(self) -> int:
+        return self.lib.dg_state_ctx_len(self._state)
+
+    @property
+    def canvas_index(self) -> int:
+        return self.lib.dg_state_canvas_index(self._state)
+
+    def view(self, which: int, dtype: torch.dtype, shape) -> torch.Tensor:
+        """A torch tensor aliasing part of the state buffer (K/V cache, self-cond, prev argmax)."""
+        p = ctypes.c_void_p()
+        nb = ctypes.c_size_t()
+        L.check(self.lib.dg_state_view(self._state, which, ctypes.byref(p), ctypes.byref(nb)))
+        off = p.value - self.state_buf.data_ptr()
+        el = torch.tensor([], dtype=dtype).element_size()
+        return self.state_buf[off:off + nb.value].view(dtype).view(*shape)
+
+    def kv_views(self):
+        c = self.cfg
+        dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        shape = (c.n_layers, self.B, c.n_kv_heads, self.max_ctx, c.head_dim)
+        return self.view(L.DG_VIEW_K_CACHE, dt, shape), self.view(L.DG_VIEW_V_CACHE, dt, shape)
+
+    def self_cond_view(self) -> torch.Tensor:
+        return self.view(L.DG_VIEW_SELF_COND, torch.float32, (self.B, self.n, self.cfg.d_model))
+
+    def route_view(self, rows: int) -> torch.Tensor:
+        t = self.view(L.DG_VIEW_ROUTE, torch.int32, (self.B * self.n, self.cfg.top_k))
+        return t[:rows]
+
+    # ------------------------------------------------------------ stage timing
+    def profile(self, stages) -> None:
+        mask = 0
+        for st in stages:
+            mask |= 1 << L.STAGES.index(st)
+        L.check(self.lib.dg_profile_enable(self._state, mask))
+
+    def profile_read(self) -> Dict[str, tuple]:
+        ms = (ctypes.c_double * len(L.STAGES))()
+        n = (ctypes.c_int64 * len(L.STAGES))()
+        L.check(self.lib.dg_profile_read(self._state, ms, n))
+        return {st: (ms[i], n[i]) for i, st in enumerate(L.STAGES) if n[i]}
+
+    # ------------------------------------------------------------ the calls
+    def init_canvas(self) -> torch.Tensor:
+        L.check(self.lib.dg_init_canvas(self._state, self.canvas.data_ptr(), self._seed_ptr(), self._stream()))
+        return self.canvas
+
+    def encode_prompt(self, ids: torch.Tensor) -> None:
+        ids = ids.to(device=self.device, dtype=torch.int32).contiguous()
+        assert ids.shape[0] == self.B
+        L.check(self.lib.dg_encode_prompt(self._state, ids.data_ptr(), ids.shape[1], self._stream()))
+
+    def denoise_step(self, step: int, sp, active: Optional[torch.Tensor] = None,
+                     logits: Optional[torch.Tensor] = None, canvas: Optional[torch.Tensor] = None) -> None:
+        prm = sampler_struct(sp)
+        cv = self.canvas if canvas is None else canvas
+        L.check(self.lib.dg_denoise_step(self._state, cv.data_ptr(), step, ctypes.byref(prm), self._seed_ptr(),
+                                         _ptr(active), self.H.data_ptr(), self.y.data_ptr(), self.am.data_ptr(),
+                                         self.margin.data_ptr(), _ptr(logits), self._stream()))
+
+    def sample_commit(self, step: int, sp, H: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      am: Optional[torch.Tensor] = None) -> None:
+        prm = sampler_struct(sp)
+        H = self.H if H is None else H
+        y = self.y if y is None else y
+        am = self.am if am is None else am
+        L.check(self.lib.dg_sample_commit(self._state, H.data_ptr(), y.data_ptr(), am.data_ptr(),
+                                          self.canvas.data_ptr(), step, ctypes.byref(prm), self._seed_ptr(),
+                                          self.mask.data_ptr(), self.n_committed.data_ptr(),
+                                          self.done.data_ptr(), self._stream()))
+
+    def commit_canvas_to_kv(self, canvas: Optional[torch.Tensor] = None) -> None:
+        cv = self.canvas if canvas is None else canvas
+        L.check(self.lib.dg_commit_canvas_to_kv(self._state, cv.data_ptr(), self._stream()))
+
+    # ------------------------------------------------------------ loop
+    def run_canvas(self, sp, steps_limit: Optional[int] = None, on_step=None) -> int:
+        """Denoise one canvas for all requests; returns the number of steps run.
+
+        The per-step host read of `done` is the loop's only synchronisation."""
+        self.init_canvas()
+        self.done.zero_()
+        S = sp.max_steps if steps_limit is None else min(sp.max_steps, steps_limit)
+        steps = 0
+        for t in range(S):
+            active = (self.done == 0).to(torch.uint8)
+            self.denoise_step(t, sp, active=active)
+            self.sample_commit(t, sp)
+            steps += 1
+            if on_step is not None:
+                on_step(t, self)
+            if sp.stop_mode != 0 or t == S - 1:
+                if bool((self.done != 0).all()):
+                    break
+        return steps

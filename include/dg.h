@@ -1,0 +1,218 @@
+/*
+ * dg.h -- C ABI of the DiffusionGemma denoise-step library for MI355X (gfx950).
+ *
+ * The library runs the hot path of a block-diffusion text generator: a causally
+ * encoded prompt KV cache, then rounds of denoising over a 256-token canvas.
+ * Pages describing the method (secondary summaries of the DiffusionGemma report):
+ *   [mlqm]     mlqm.cn/news/993655, sections 一 (multinomial diffusion), 二 (MoE,
+ *              causal prompt / bidirectional canvas attention, self-conditioning),
+ *              四 (entropy-ordered commit, re-noise, 0.8 -> 0.4 temperature,
+ *              adaptive stop), 五 (where the step's time goes)
+ *   [chooseai] chooseai.io/news/4338: encoder caches the prompt, decoder attends
+ *              bidirectionally; block-autoregressive multi-canvas sampling
+ *   [bohu]     bohuyeshan.top, section 一: a developer implements one denoise step;
+ *              a finished canvas enters the KV cache before the next one starts
+ *
+ * Conventions
+ *   - Every pointer named d_* is device memory on the current HIP device,
+ *     allocated and owned by the caller; h_* pointers are host memory.  The
+ *     library borrows them for the duration of the call (asynchronous on the
+ *     given stream: buffers must stay valid until the stream reaches the work).
+ *   - Handles (dg_model, dg_state) own only host metadata, except that a model
+ *     owns two derived weight copies in device memory (the transposed embedding
+ *     for the self-conditioning contraction and the fused QKV matrices), made
+ *     once in dg_model_create and freed by dg_model_destroy.
+ *   - The four step calls allocate nothing and never synchronise the device,
+ *     except dg_encode_prompt / dg_commit_canvas_to_kv which only enqueue work.
+ *   - Errors: a negative status is returned and a thread-local message is set
+ *     (dg_last_error).  On an argument or capacity error no work is enqueued and
+ *     the state is unchanged.  No exception or abort crosses the ABI.
+ *   - Determinism: identical inputs and seeds give bitwise identical outputs
+ *     (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dg_status;
+#define DG_OK 0
+#define DG_ERR_ARG (-1)          /* invalid argument (null pointer, bad size or config) */
+#define DG_ERR_CAPACITY (-2)     /* context would exceed max_ctx, or state buffer too small */
+#define DG_ERR_HIP (-3)          /* a HIP runtime call failed */
+#define DG_ERR_UNSUPPORTED (-4)  /* shape outside what the kernels implement */
+
+#define DG_DTYPE_F32 0
+#define DG_DTYPE_BF16 1
+
+#define DG_STOP_NONE 0    /* run the whole step budget */
+#define DG_STOP_MEAN 1    /* stop once the mean canvas entropy < stop_tau */
+#define DG_STOP_PAGES 2   /* mean entropy < stop_tau and argmax unchanged from the previous step ([mlqm] 四) */
+
+typedef struct dg_config {
+  int32_t n_layers;
+  int32_t d_model;      /* multiple of 64 */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;   /* divides n_q_heads */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t n_experts;    /* 1..128 */
+  int32_t ffn_hidden;   /* multiple of 64 */
+  int32_t top_k;        /* 1..min(8, n_experts) */
+  int32_t vocab;        /* multiple of 64 */
+  int32_t canvas_len;   /* 1..256; the pages' canvas is 256 tokens ([mlqm] 一) */
+  int32_t dtype;        /* DG_DTYPE_F32 or DG_DTYPE_BF16: weight and matmul operand type */
+  int32_t self_cond;    /* 1: add (softmax of the previous step) @ E @ W_sc^T to the embeddings */
+  float rope_theta;
+  float rms_eps;
+} dg_config;
+
+typedef struct dg_sampler_params {
+  float t_start;        /* temperature at step 0 (0.8 on the pages) */
+  float t_end;          /* temperature at step max_steps-1 (0.4) */
+  float entropy_bound;  /* commit bound on the running entropy total, nats (0.1) */
+  float stop_tau;       /* adaptive-stop threshold on the mean entropy, nats */
+  int32_t max_steps;    /* step budget S of the canvas (48 on the pages) */
+  int32_t stop_mode;    /* DG_STOP_* */
+} dg_sampler_params;
+
+typedef struct dg_model dg_model;
+typedef struct dg_state dg_state;
+typedef struct ihipStream_t* dg_stream;   /* a hipStream_t; NULL = default stream */
+
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char* dg_last_error(void);
+
+/* Number of weight pointers dg_model_create expects for a config:
+ * 2 + self_cond + 10 * n_layers. */
+int32_t dg_weight_count(const dg_config* cfg);
+
+/* Create a model over caller-owned device weights.
+ * d_weights[i] point to tensors in this order ([out, in] layout for matrices,
+ * row-major; type = cfg->dtype for matrices, float32 for norm gains):
+ *   emb [V, d]; w_sc [d, d] (only if self_cond); final_norm [d];
+ *   then per layer: attn_norm [d], wq [Hq*hd, d], wk [Hkv*hd, d], wv [Hkv*hd, d],
+ *   wo [d, Hq*hd], ffn_norm [d], w_router [E, d], w_gate [E, F, d],
+ *   w_up [E, F, d], w_down [E, d, F].
+ * The weights are borrowed (must outlive the model); the call synchronises the
+ * device once after building the derived copies.  The LM head is tied to emb. */
+dg_status dg_model_create(const dg_config* cfg, const void* const* d_weights, int32_t n_weights,
+                          dg_model** out);
+void dg_model_destroy(dg_model* model);
+
+/* Device bytes needed by a state for `batch` requests and a KV capacity of
+ * max_ctx positions per request (prompt + committed canvases + one canvas). */
+dg_status dg_state_bytes(const dg_model* model, int32_t batch, int32_t max_ctx, size_t* bytes);
+
+/* Build a state inside a caller-owned device buffer of at least dg_state_bytes.
+ * Sets context length 0 and canvas index 0, and fills the RoPE table (enqueued
+ * on the default stream, synchronised before return). */
+dg_status dg_state_init(const dg_model* model, void* d_buf, size_t bytes, int32_t batch,
+                        int32_t max_ctx, dg_state** out);
+void dg_state_destroy(dg_state* state);
+
+/* Current context length N (positions held in the KV cache) and canvas index. */
+int32_t dg_state_ctx_len(const dg_state* state);
+int32_t dg_state_canvas_index(const dg_state* state);
+
+/* Device views into the state buffer, for inspection and teacher forcing:
+ *   DG_VIEW_K_CACHE / DG_VIEW_V_CACHE: [L][B][Hkv][max_ctx][hd], cfg dtype
+ *   DG_VIEW_SELF_COND: float [B][canvas_len][d], the vector s of the last step
+ *   DG_VIEW_PREV_ARGMAX: int32 [B][canvas_len], argmax seen by the last commit
+ *   DG_VIEW_ROUTE: int32 [rows][top_k], expert ids chosen in the last layer of
+ *     the last pass (rows = B * rows per request of that pass) */
+#define DG_VIEW_K_CACHE 0
+#define DG_VIEW_V_CACHE 1
+#define DG_VIEW_SELF_COND 2
+#define DG_VIEW_PREV_ARGMAX 3
+#define DG_VIEW_ROUTE 4
+dg_status dg_state_view(dg_state* state, int32_t which, void** d_ptr, size_t* bytes);
+
+/* Initial canvas: canvas_len uniformly random tokens per request ([mlqm] 一,
+ * [chooseai]: the canvas is first filled with random placeholder tokens).
+ * d_canvas: int32 [B, canvas_len] (written).  h_seeds: uint64 [B] per-request
+ * Philox seeds.  Uses the state's current canvas index. */
+dg_status dg_init_canvas(dg_state* state, int32_t* d_canvas, const uint64_t* h_seeds,
+                         dg_stream stream);
+
+/* Causal encode of a prompt ([mlqm] 二: causal attention over the user input;
+ * [chooseai]: the encoder caches the prompt context).  d_ids: int32 [B, P] with
+ * every id in [0, V) (an id outside is clamped to that range; token ids of a
+ * canvas are treated the same way).  Appends P positions to each request's KV cache at
+ * N..N+P-1 and sets N += P.  P = 0 is a no-op.  DG_ERR_CAPACITY if
+ * N + P > max_ctx.  The prompt is encoded in chunks of canvas_len tokens. */
+dg_status dg_encode_prompt(dg_state* state, const int32_t* d_ids, int32_t P, dg_stream stream);
+
+/* One denoising round over the canvas ([mlqm] 一, 二, 四).
+ * d_canvas: int32 [B, canvas_len] current tokens (read).  step: 0-based round t
+ * of the current canvas (self-conditioning is off at t = 0; the temperature is
+ * t_start + (t_end - t_start) * t / (max_steps - 1)).  h_seeds: uint64 [B].
+ * d_active: uint8 [B] or NULL (= all active); inactive requests are computed
+ * but none of their outputs is written.
+ * Outputs, all [B, canvas_len]: d_H float entropy (nats) of softmax(logits/T);
+ * d_y int32 Gumbel-max sample of that distribution; d_argmax int32 argmax of
+ * the logits; d_margin float best minus second-best Gumbel-perturbed score.
+ * d_logits: float [B, canvas_len, V] or NULL; if given, the raw logits are
+ * written there.  Updates the state's self-conditioning vector.  The canvas's
+ * own keys and values occupy cache positions N..N+canvas_len-1 during the step
+ * (DG_ERR_CAPACITY if N + canvas_len > max_ctx). */
+dg_status dg_denoise_step(dg_state* state, const int32_t* d_canvas, int32_t step,
+                          const dg_sampler_params* params, const uint64_t* h_seeds,
+                          const uint8_t* d_active, float* d_H, int32_t* d_y, int32_t* d_argmax,
+                          float* d_margin, float* d_logits, dg_stream stream);
+
+/* Entropy-bounded commit / uniform re-noise / adaptive stop ([mlqm] 四, 一).
+ * Per request b with d_done[b] == 0: sort positions by (H, position), commit the
+ * longest prefix whose running fp64 entropy total stays <= entropy_bound; the
+ * committed positions take d_y, the others a fresh uniform token.  If the stop
+ * rule fires or step == max_steps-1, every position takes d_y and d_done[b] = 1.
+ * d_canvas int32 [B, canvas_len] is updated in place; d_commit_mask uint8
+ * [B, canvas_len] and d_n_committed int32 [B] are written (positions that took
+ * y); requests already done are left untouched.  d_argmax is remembered for
+ * DG_STOP_PAGES. */
+dg_status dg_sample_commit(dg_state* state, const float* d_H, const int32_t* d_y,
+                           const int32_t* d_argmax, int32_t* d_canvas, int32_t step,
+                           const dg_sampler_params* params, const uint64_t* h_seeds,
+                           uint8_t* d_commit_mask, int32_t* d_n_committed, uint8_t* d_done,
+                           dg_stream stream);
+
+/* Append the finished canvas to the KV cache by a causal encode at positions
+ * N..N+canvas_len-1 ([bohu] 一, [chooseai]: block-autoregressive canvases);
+ * N += canvas_len, canvas index += 1.  DG_ERR_CAPACITY if N + canvas_len >
+ * max_ctx. */
+dg_status dg_commit_canvas_to_kv(dg_state* state, const int32_t* d_canvas, dg_stream stream);
+
+/* Stage timing ([mlqm] 五 splits a step's cost into MoE, sampling and
+ * attention; these counters give the same split for this implementation).
+ * When enabled, the step calls record a HIP event pair on their stream around
+ * every launch of the stages in `stage_mask` (bit i = stage i below); events
+ * come from a fixed pool created here (4096 pairs), so the step calls still
+ * allocate nothing; recording stops silently once the pool is full.
+ * dg_profile_read synchronises on the recorded events, adds each pair's
+ * elapsed time to ms[stage] and 1 to launches[stage] (arrays of
+ * DG_NUM_STAGES, overwritten), then empties the pool. */
+#define DG_STAGE_EMBED 0       /* embedding gather, self-conditioning projection */
+#define DG_STAGE_NORM 1        /* RMSNorm */
+#define DG_STAGE_QKV 2         /* fused QKV projection + RoPE + cache write */
+#define DG_STAGE_ATTN 3        /* attention (+ split merge) */
+#define DG_STAGE_OPROJ 4       /* output projection + residual */
+#define DG_STAGE_ROUTER 5      /* router logits, top-k, bucketing */
+#define DG_STAGE_EXPERT_UP 6   /* grouped expert gate/up + SwiGLU */
+#define DG_STAGE_EXPERT_DOWN 7 /* grouped expert down projection */
+#define DG_STAGE_COMBINE 8     /* weighted combine of expert outputs */
+#define DG_STAGE_LM_HEAD 9     /* tied LM head */
+#define DG_STAGE_SAMPLER 10    /* temperature softmax, entropy, Gumbel-max (partial + merge) */
+#define DG_STAGE_SELFCOND 11   /* softmax @ E contraction (+ chunk reduce) */
+#define DG_STAGE_COMMIT 12     /* commit / re-noise / stop */
+#define DG_NUM_STAGES 13
+dg_status dg_profile_enable(dg_state* state, uint32_t stage_mask);
+dg_status dg_profile_read(dg_state* state, double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H_ */

@@ -1,0 +1,99 @@
+"""The C ABI library loads and exports what include/dg.h declares (no GPU needed).
+
+Only calls that fail argument validation before touching the device are made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dg_inputs as di
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from discrete_text_diffusion_dg_amd import _lib
+    return _lib.load()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert len(names) >= 15
+    from discrete_text_diffusion_dg_amd import _lib
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/dg.h but not exported"
+        assert n in _lib.EXPORTS, f"{n} not bound in the Python binding"
+
+
+def test_weight_count(lib):
+    from discrete_text_diffusion_dg_amd.runtime import config_struct
+    for name in ("tiny", "small", "proxy"):
+        mc = di.workload(name).model
+        c = config_struct(mc)
+        assert lib.dg_weight_count(ctypes.byref(c)) == len(di.tensor_list(mc))
+
+
+def _create(lib, **kw):
+    from discrete_text_diffusion_dg_amd import _lib
+    from discrete_text_diffusion_dg_amd.runtime import config_struct
+    mc = di.workload("tiny").model
+    c = config_struct(mc)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    n = lib.dg_weight_count(ctypes.byref(c))
+    ptrs = (ctypes.c_void_p * max(n, 1))(*([None] * max(n, 1)))
+    out = ctypes.c_void_p()
+    st = lib.dg_model_create(ctypes.byref(c), ptrs, n, ctypes.byref(out))
+    return st, lib.dg_last_error().decode(), out
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -4), ("d_model", 100, -4), ("n_kv_heads", 3, -1), ("n_experts", 200, -4),
+    ("top_k", 9, -4), ("vocab", 1000, -4), ("canvas_len", 300, -4), ("dtype", 5, -1),
+    ("ffn_hidden", 100, -4), ("n_layers", 0, -1),
+])
+def test_model_create_rejects_bad_config(lib, field, value, code):
+    st, msg, out = _create(lib, **{field: value})
+    assert st == code and msg and out.value is None
+
+
+def test_model_create_rejects_null_weights(lib):
+    st, msg, out = _create(lib)
+    assert st == -1 and "null" in msg
+
+
+def test_null_handles(lib):
+    assert lib.dg_encode_prompt(None, None, 4, None) == -1
+    assert "null" in lib.dg_last_error().decode()
+    assert lib.dg_denoise_step(None, None, 0, None, None, None, None, None, None, None, None, None) == -1
+    assert lib.dg_sample_commit(None, None, None, None, None, 0, None, None, None, None, None, None) == -1
+    assert lib.dg_commit_canvas_to_kv(None, None, None) == -1
+    assert lib.dg_state_ctx_len(None) == -1
+    sz = ctypes.c_size_t()
+    assert lib.dg_state_bytes(None, 1, 512, ctypes.byref(sz)) == -1
+
+
+def test_product_path_fails_loudly_without_library(tmp_path, monkeypatch):
+    from discrete_text_diffusion_dg_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "discrete_text_diffusion_dg_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
