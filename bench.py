@@ -206,7 +206,7 @@ def main():
     ctx_w = eng.ctx_len
     dominant = max(prof, key=lambda k: prof[k][0]) if prof else "expert_up"
     log("[bench] warm-up stage ms: " + ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in prof.items()))
-    routed = eng.route_view(B * n).cpu().numpy()
+    routed = eng.route_view(B * n)[-1].cpu().numpy()
     n_act = int(np.unique(routed).size)
 
     # timed region: exactly K steps, only the dominant stage carries events

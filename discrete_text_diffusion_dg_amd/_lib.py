@@ -22,7 +22,8 @@ DG_ERR_HIP = -3
 DG_ERR_UNSUPPORTED = -4
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
-DG_VIEW_K_CACHE, DG_VIEW_V_CACHE, DG_VIEW_SELF_COND, DG_VIEW_PREV_ARGMAX, DG_VIEW_ROUTE = 0, 1, 2, 3, 4
+(DG_VIEW_K_CACHE, DG_VIEW_V_CACHE, DG_VIEW_SELF_COND, DG_VIEW_PREV_ARGMAX, DG_VIEW_ROUTE,
+ DG_VIEW_HIDDEN, DG_VIEW_ROUTER_LOGITS, DG_VIEW_ATTN_OUT) = 0, 1, 2, 3, 4, 5, 6, 7
 STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
           "lm_head", "sampler", "selfcond", "commit"]
 

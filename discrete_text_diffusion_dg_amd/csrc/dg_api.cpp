@@ -238,8 +238,8 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.attn = L.take((size_t)R * Hq * hd * es);
   o.attn_po = L.take((size_t)o.splits * R * Hq * hd * 4);
   o.attn_pml = L.take((size_t)o.splits * R * Hq * 2 * 4);
-  o.rlog = L.take((size_t)R * E * 4);
-  o.ridx = L.take((size_t)R * k * 4);
+  o.rlog = L.take((size_t)c.n_layers * R * E * 4);      // per layer, kept for inspection
+  o.ridx = L.take((size_t)c.n_layers * R * k * 4);
   o.rw = L.take((size_t)R * k * 4);
   o.chunk_counts = L.take((size_t)((R + 255) / 256) * E * 4);
   o.perm = L.take((size_t)R * k * 4);
@@ -348,7 +348,10 @@ extern "C" dg_status dg_state_view(dg_state* s, int32_t which, void** ptr, size_
     case DG_VIEW_V_CACHE: *ptr = s->vc; *bytes = s->kv_layer_elems * c.n_layers * s->m->esz; break;
     case DG_VIEW_SELF_COND: *ptr = s->s; *bytes = (size_t)s->R * c.d_model * 4; break;
     case DG_VIEW_PREV_ARGMAX: *ptr = s->prev_am; *bytes = (size_t)s->R * 4; break;
-    case DG_VIEW_ROUTE: *ptr = s->ridx; *bytes = (size_t)s->R * c.top_k * 4; break;
+    case DG_VIEW_ROUTE: *ptr = s->ridx; *bytes = (size_t)c.n_layers * s->R * c.top_k * 4; break;
+    case DG_VIEW_HIDDEN: *ptr = s->h; *bytes = (size_t)s->R * c.d_model * 4; break;
+    case DG_VIEW_ROUTER_LOGITS: *ptr = s->rlog; *bytes = (size_t)c.n_layers * s->R * c.n_experts * 4; break;
+    case DG_VIEW_ATTN_OUT: *ptr = s->attn; *bytes = (size_t)s->R * c.n_q_heads * c.head_dim * s->m->esz; break;
     default: return fail(DG_ERR_ARG, "unknown view %d", which);
   }
   return DG_OK;
@@ -420,9 +423,11 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     }
     {
       StageTimer tm(st, DG_STAGE_ROUTER, s);
-      DG_HIP(gemm_store_f32<T>(xn, d, static_cast<const T*>(L.w_router), d, st->rlog, E, M, E, d, s));
-      DG_HIP(router_topk(st->rlog, M, E, k, st->ridx, st->rw, s));
-      DG_HIP(route_bucket(st->ridx, M, k, E, st->chunk_counts, st->perm, st->pos, st->tiles, st->n_tiles, s));
+      float* rlog = st->rlog + (size_t)l * st->R * E;
+      int* ridx = st->ridx + (size_t)l * st->R * k;
+      DG_HIP(gemm_store_f32<T>(xn, d, static_cast<const T*>(L.w_router), d, rlog, E, M, E, d, s));
+      DG_HIP(router_topk(rlog, M, E, k, ridx, st->rw, s));
+      DG_HIP(route_bucket(ridx, M, k, E, st->chunk_counts, st->perm, st->pos, st->tiles, st->n_tiles, s));
     }
     {
       StageTimer tm(st, DG_STAGE_EXPERT_UP, s);

@@ -160,32 +160,47 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float e = (p[j] == -INFINITY) ? 0.f : expf(p[j] - m_new);
-      p[j] = Num<T>::round(e);
-      lsum += p[j];
+      p[j] = e;
+      lsum += e;
     }
     l_run = l_run * alpha + lsum;
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
 
-    // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps
+    // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps.  With bf16
+    // operands the fp32 probabilities are split into a bf16 head and a bf16
+    // remainder (two MFMAs, ~16 significant bits): a single bf16 rounding of P
+    // would dominate the output error, while beyond 16 bits the fp32 summation
+    // over the keys does (a third term was measured to change nothing).
+    constexpr int NT = sizeof(T) == 2 ? 2 : 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      Frag<T> pf;
-      float pv[8];
+      Frag<T> pf[NT];
+      float rest[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = p[(2 * ks) * 4 + i];
-        pv[4 + i] = p[(2 * ks + 1) * 4 + i];
+        rest[i] = p[(2 * ks) * 4 + i];
+        rest[4 + i] = p[(2 * ks + 1) * 4 + i];
       }
-      set_p(pf, pv);
+#pragma unroll
+      for (int term = 0; term < NT; ++term) {
+        float part[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          part[j] = Num<T>::round(rest[j]);
+          rest[j] -= part[j];
+        }
+        set_p(pf[term], part);
+      }
 #pragma unroll
       for (int db = 0; db < HD / 16; ++db) {
         Frag<T> vf;
         const T* row = sVt + (db * 16 + q16) * S::LDV + ks * 32 + g4 * 4;
         lds4(vf, 0, row);
         lds4(vf, 1, row + 16);
-        mma16x16x32(o[db], vf, pf);
+#pragma unroll
+        for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
       }
     }
     __syncthreads();

@@ -132,8 +132,9 @@ __global__ void k_router_topk(const float* logits, int M, int E, int k, int* idx
     sel[j] = best;
     sid[j] = bi;
   }
+  const float mx = sel[0];   // selection order is descending, so slot 0 holds the max
   float sum = 0.f;
-  for (int j = 0; j < k; ++j) { sel[j] = expf(sel[j] - sel[0]); sum += sel[j]; }
+  for (int j = 0; j < k; ++j) { sel[j] = expf(sel[j] - mx); sum += sel[j]; }
   for (int j = 0; j < k; ++j) {
     idx[(size_t)r * k + j] = sid[j];
     w[(size_t)r * k + j] = sel[j] / sum;

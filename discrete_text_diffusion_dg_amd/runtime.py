@@ -130,9 +130,25 @@ class Engine:
     def self_cond_view(self) -> torch.Tensor:
         return self.view(L.DG_VIEW_SELF_COND, torch.float32, (self.B, self.n, self.cfg.d_model))
 
-    def route_view(self, rows: int) -> torch.Tensor:
-        t = self.view(L.DG_VIEW_ROUTE, torch.int32, (self.B * self.n, self.cfg.top_k))
+    def hidden_view(self, rows: int) -> torch.Tensor:
+        t = self.view(L.DG_VIEW_HIDDEN, torch.float32, (self.B * self.n, self.cfg.d_model))
         return t[:rows]
+
+    def router_logits_view(self, rows: int) -> torch.Tensor:
+        c = self.cfg
+        t = self.view(L.DG_VIEW_ROUTER_LOGITS, torch.float32, (c.n_layers, self.B * self.n, c.n_experts))
+        return t[:, :rows]
+
+    def attn_out_view(self, rows: int) -> torch.Tensor:
+        c = self.cfg
+        dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        t = self.view(L.DG_VIEW_ATTN_OUT, dt, (self.B * self.n, c.n_q_heads * c.head_dim))
+        return t[:rows]
+
+    def route_view(self, rows: int) -> torch.Tensor:
+        c = self.cfg
+        t = self.view(L.DG_VIEW_ROUTE, torch.int32, (c.n_layers, self.B * self.n, c.top_k))
+        return t[:, :rows]
 
     # ------------------------------------------------------------ stage timing
     def profile(self, stages) -> None:

@@ -123,13 +123,22 @@ int32_t dg_state_canvas_index(const dg_state* state);
  *   DG_VIEW_K_CACHE / DG_VIEW_V_CACHE: [L][B][Hkv][max_ctx][hd], cfg dtype
  *   DG_VIEW_SELF_COND: float [B][canvas_len][d], the vector s of the last step
  *   DG_VIEW_PREV_ARGMAX: int32 [B][canvas_len], argmax seen by the last commit
- *   DG_VIEW_ROUTE: int32 [rows][top_k], expert ids chosen in the last layer of
- *     the last pass (rows = B * rows per request of that pass) */
+ *   DG_VIEW_ROUTE: int32 [L][B * canvas_len][top_k], expert ids chosen in each
+ *     layer by the last pass (its first B * rows-per-request rows are valid)
+ *   DG_VIEW_HIDDEN: float [rows][d], residual stream after the last layer of
+ *     the last pass (before the final norm)
+ *   DG_VIEW_ROUTER_LOGITS: float [L][B * canvas_len][n_experts], router logits
+ *     of each layer of the last pass (same row convention)
+ *   DG_VIEW_ATTN_OUT: [rows][n_q_heads * head_dim], cfg dtype, attention output
+ *     (before the output projection) of the last layer of the last pass */
 #define DG_VIEW_K_CACHE 0
 #define DG_VIEW_V_CACHE 1
 #define DG_VIEW_SELF_COND 2
 #define DG_VIEW_PREV_ARGMAX 3
 #define DG_VIEW_ROUTE 4
+#define DG_VIEW_HIDDEN 5
+#define DG_VIEW_ROUTER_LOGITS 6
+#define DG_VIEW_ATTN_OUT 7
 dg_status dg_state_view(dg_state* state, int32_t which, void** d_ptr, size_t* bytes);
 
 /* Initial canvas: canvas_len uniformly random tokens per request ([mlqm] 一,

@@ -131,20 +131,22 @@ class OracleModel:
         return h
 
     # ------------------------------------------------------------ the four calls
-    def encode_prompt(self, ids: np.ndarray) -> None:
-        """Causal encode of ids [B, P] at positions ctx..ctx+P-1; K/V appended."""
+    def encode_prompt(self, ids: np.ndarray, traces: Optional[List[dict]] = None) -> None:
+        """Causal encode of ids [B, P] at positions ctx..ctx+P-1; K/V appended.
+
+        traces: optional list of B dicts that receive per-layer intermediates."""
         ids = np.asarray(ids)
         P = ids.shape[1]
         assert self.ctx + P <= self.max_ctx
         pos = self.ctx + np.arange(P)
         for b in range(self.B):
             if P:
-                self._stack(b, ids[b], pos, True, True, None, None)
+                self._stack(b, ids[b], pos, True, True, None, traces[b] if traces else None)
         self.ctx += P
 
-    def commit_canvas_to_kv(self, canvas: np.ndarray) -> None:
+    def commit_canvas_to_kv(self, canvas: np.ndarray, traces: Optional[List[dict]] = None) -> None:
         """The finished canvas is encoded causally and appended ([bohu] 一)."""
-        self.encode_prompt(canvas)
+        self.encode_prompt(canvas, traces)
         self.canvas_index += 1
 
     def denoise_step(self, canvas: np.ndarray, step: int, sp, seeds: np.ndarray,

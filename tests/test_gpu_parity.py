@@ -1,9 +1,15 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
 
-Integer outputs (canvas draws, sampled tokens, argmax, commit masks) must match
-bit-exactly, except sampled tokens whose oracle Gumbel top-2 margin is below
-1e-3; logits and entropies must match within 2e-2 relative (bf16 models) or
-1e-4 (fp32), relative meaning max|diff| / max|ref| per row.
+Integer outputs (canvas draws, sampled tokens, argmax, commit masks, routing)
+must match bit-exactly, except sampled tokens whose oracle Gumbel top-2 margin
+is below 1e-3 and rows with a router near-tie; logits and entropies must match
+within 2e-2 relative (bf16 models) or 1e-4 (fp32), relative meaning
+max|diff| / max|ref| per row.
+
+Each denoise step is compared teacher-forced: before it the GPU state gets the
+oracle's self-conditioning vector and (after their own comparison) the
+oracle's prompt K/V, so a routing flip on a near-tie row in one step cannot
+leak into the next step's inputs.
 """
 import numpy as np
 import pytest
@@ -17,6 +23,15 @@ from _util import log, make_engine, micro, rel_err_rows, replace, tol_for
 pytestmark = pytest.mark.gpu
 
 MARGIN_EXEMPT = 1e-3
+# Routing may differ from the oracle only where the oracle's k-th and (k+1)-th
+# router logits are closer than GAP_REL * max|r| of the row.  Both sides round
+# the same activations to bf16, but fp32 sums (whose error near-cancelling
+# attention outputs amplify to ~1e-5) against fp64 ones flip ~1% of those
+# roundings by one ulp, and the flips carry through the residual stream to a
+# router-logit drift of up to ~1% of the logit scale (the tests print the
+# measured drift).  2e-2 is the bf16 value tolerance; fp32 operands drift ~1e-6.
+GAP_REL = {"bf16": 2e-2, "f32": 1e-4}
+MAX_FLIP_FRAC = 0.05
 
 
 @pytest.fixture(scope="module")
@@ -27,25 +42,71 @@ def torch_cuda():
     return torch
 
 
-def _compare_step(mc, got, ref, tag, allow_route_taint=0.0):
+def router_gap(r: np.ndarray, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest router logits per row (inf if k = E)."""
+    if r.shape[1] <= k:
+        return np.full(r.shape[0], np.inf)
+    srt = -np.sort(-r.astype(np.float64), axis=1)
+    return srt[:, k - 1] - srt[:, k]
+
+
+def near_tie(r: np.ndarray, mc) -> np.ndarray:
+    return router_gap(r, mc.top_k) < GAP_REL[mc.dtype] * np.abs(r).max(axis=1)
+
+
+def check_routing(mc, eng, traces, rows_per_req, tag):
+    """Per-layer routing of the last pass against the oracle traces.
+
+    Returns the per-request rows whose routing flipped in some layer; asserts
+    every flip happened at an oracle near-tie."""
+    B = len(traces)
+    groute = eng.route_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
+    glog = eng.router_logits_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
+    flipped = np.zeros((B, rows_per_req), bool)
+    drift_max, drift_med, n_flip = 0.0, [], 0
+    for l in range(mc.n_layers):
+        for b in range(B):
+            rr = traces[b]["route_idx"][l]
+            gap = router_gap(traces[b]["router_logits"][l], mc.top_k)
+            flip = np.array([set(groute[l, b, i]) != set(rr[i]) for i in range(rows_per_req)])
+            # a row that flipped in an earlier layer carries other values from then on
+            bad = flip & ~near_tie(traces[b]["router_logits"][l], mc) & ~flipped[b]
+            assert not bad.any(), (f"{tag} layer {l}: routing differs at oracle gaps "
+                                   f"{gap[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
+            clean = ~flipped[b]
+            dr = np.abs(glog[l, b] - traces[b]["router_logits"][l]).max(axis=1)[clean]
+            if dr.size:
+                drift_max = max(drift_max, float(dr.max()))
+                drift_med.append(float(np.median(dr)))
+            n_flip += int(flip.sum())
+            flipped[b] |= flip
+    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())}), all at near-ties; router drift "
+        f"max {drift_max:.2e} median {np.median(drift_med):.2e}")
+    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: too many routing flips"
+    return flipped
+
+
+def _compare_step(mc, got, ref, tag, taint):
     tol = tol_for(mc)
     gl = got["logits"].reshape(-1, mc.vocab)
     rl = ref["logits"].reshape(-1, mc.vocab)
     e_log = rel_err_rows(gl, rl)
     e_H = np.abs(got["H"].astype(np.float64) - ref["H"]) / np.abs(ref["H"]).max()
     exempt = ref["margin"] < MARGIN_EXEMPT
+    ok = ~taint
     y_bad = (got["y"] != ref["y"]) & ~exempt
     am_bad = got["am"] != ref["am"]
-    log(f"[{tag}] logits rel err max {e_log.max():.3e} median {np.median(e_log):.3e}; "
-        f"H rel err max {e_H.max():.3e}; y mismatches {int((got['y'] != ref['y']).sum())} "
-        f"(non-exempt {int(y_bad.sum())}); argmax mismatches {int(am_bad.sum())}")
-    n_rows = gl.shape[0]
-    bad_rows = e_log > tol
-    assert bad_rows.sum() <= allow_route_taint * n_rows, f"{tag}: {int(bad_rows.sum())} rows beyond tol {tol}"
-    ok = ~bad_rows.reshape(got["y"].shape)
-    assert (e_H.reshape(got["H"].shape)[ok] <= tol).all()
+    log(f"[{tag}] logits rel err max {e_log[ok.ravel()].max():.3e} (all rows {e_log.max():.3e}) "
+        f"median {np.median(e_log):.3e}; H rel err max {e_H[ok].max():.3e}; y mismatches "
+        f"{int((got['y'] != ref['y']).sum())} (non-exempt {int((y_bad & ok).sum())}); argmax mismatches "
+        f"{int(am_bad.sum())} (non-exempt {int((am_bad & ok).sum())}); rows with a routing flip {int(taint.sum())}")
+    assert (e_log[ok.ravel()] <= tol).all(), f"{tag}: logits beyond tol {tol}"
+    assert (e_H[ok] <= tol).all(), f"{tag}: entropies beyond tol {tol}"
     assert not (y_bad & ok).any(), f"{tag}: sampled tokens differ beyond the margin exemption"
-    assert not (am_bad & ok).any() or mc.dtype == "bf16", f"{tag}: argmax differs"
+    # the logit argmax is exempt only where the top two logits are within the tolerance
+    rl2 = -np.sort(-rl, axis=1)[:, :2]
+    am_close = ((rl2[:, 0] - rl2[:, 1]) < tol * np.abs(rl).max(axis=1)).reshape(am_bad.shape)
+    assert not (am_bad & ok & ~am_close).any(), f"{tag}: argmax differs"
     return e_log
 
 
@@ -146,46 +207,57 @@ def test_commit_bit_exact_on_identical_inputs(torch_cuda):
     eng.close()
 
 
-def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, emb_scale=None, check_kv=True,
-                route_taint=0.0):
+def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=True):
     W = di.make_weights(mc, seed, gain_std=gain_std)
-    if emb_scale is not None:
-        W._store["emb"] = _scaled(W.get("emb"), mc, emb_scale)
     max_ctx = P + mc.canvas_len * 2
     eng = make_engine(mc, W, batch, max_ctx)
     om = OracleModel(mc, W, batch, max_ctx)
     prompts = di.make_prompts(mc.vocab, batch, P, seed)
     seeds = di.request_seeds(seed, batch)
     eng.set_seeds(seeds)
-    om.encode_prompt(prompts)
+    ptr = [dict() for _ in range(batch)]
+    om.encode_prompt(prompts, ptr)
     eng.encode_prompt(torch.from_numpy(prompts))
     torch.cuda.synchronize()
     assert eng.ctx_len == om.ctx == P
+    tol = tol_for(mc)
     if check_kv and P > 0:
         kc, vc = eng.kv_views()
-        tol = tol_for(mc)
+        near = np.zeros((batch, P), bool)     # near-tie in a layer before the one checked
         for l in range(mc.n_layers):
             gk = kc[l, :, :, :P].float().cpu().numpy()
             rk = om.k_cache[l][:, :, :P]
             gv = vc[l, :, :, :P].float().cpu().numpy()
             rv = om.v_cache[l][:, :, :P]
-            ek = np.abs(gk - rk).max() / np.abs(rk).max()
-            ev = np.abs(gv - rv).max() / np.abs(rv).max()
-            log(f"[{tag}] layer {l} prompt K rel {ek:.2e} V rel {ev:.2e}")
-            assert ek < tol and ev < tol
+            ek = np.abs(gk - rk).max(axis=(1, 3)) / np.abs(rk).max()      # [B, P]
+            ev = np.abs(gv - rv).max(axis=(1, 3)) / np.abs(rv).max()
+            off = (ek >= tol) | (ev >= tol)
+            log(f"[{tag}] layer {l} prompt K rel {ek[~off].max():.2e} V rel {ev[~off].max():.2e}; "
+                f"positions beyond tol {int(off.sum())}")
+            assert not (off & ~near).any(), f"{tag} layer {l}: prompt K/V differ away from router near-ties"
+            assert off.mean() <= MAX_FLIP_FRAC
+            near |= np.stack([near_tie(ptr[b]["router_logits"][l], mc) for b in range(batch)])
+            # teacher forcing: the canvas steps start from the oracle's cache
+            dt = kc.dtype
+            kc[l, :, :, :P] = torch.from_numpy(rk).to(dt).cuda()
+            vc[l, :, :, :P] = torch.from_numpy(rv).to(dt).cuda()
     sp = di.SamplerConfig(max_steps=steps, entropy_bound=0.5, stop_mode=0)
     canvas = np.stack([osmp.init_canvas(int(seeds[b]), 0, mc.canvas_len, mc.vocab) for b in range(batch)])
     eng.init_canvas()
     assert np.array_equal(eng.canvas.cpu().numpy(), canvas)
     for t in range(steps):
-        ref = om.denoise_step(canvas, t, sp, seeds, want_logits=True)
+        if mc.self_cond and t > 0:
+            eng.self_cond_view().copy_(torch.from_numpy(om.s.astype(np.float32)).cuda())
+        ref = om.denoise_step(canvas, t, sp, seeds, want_logits=True, trace_requests=list(range(batch)))
         got = _gpu_step(eng, torch, t, sp)
-        _compare_step(mc, got, ref, f"{tag} step {t}", allow_route_taint=route_taint)
+        taint = check_routing(mc, eng, [ref["traces"][b] for b in range(batch)], mc.canvas_len,
+                              f"{tag} step {t}")
+        _compare_step(mc, got, ref, f"{tag} step {t}", taint)
         if mc.self_cond:
             gs = eng.self_cond_view().cpu().numpy()
             es = rel_err_rows(gs.reshape(-1, mc.d_model), om.s.reshape(-1, mc.d_model))
-            log(f"[{tag} step {t}] self-cond rel err max {es.max():.3e}")
-            assert es.max() < tol_for(mc)
+            log(f"[{tag} step {t}] self-cond rel err max {es[~taint.ravel()].max():.3e}")
+            assert es[~taint.ravel()].max() < tol
         # commit on the oracle's entropies so both canvases stay identical
         Ht = torch.from_numpy(ref["H"]).cuda()
         yt = torch.from_numpy(ref["y"]).cuda()
@@ -200,18 +272,20 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, emb_scale=N
         torch.cuda.synchronize()
         assert np.array_equal(eng.canvas.cpu().numpy(), canvas)
     # the finished canvas enters the cache
-    om.commit_canvas_to_kv(canvas)
+    ctr = [dict() for _ in range(batch)]
+    om.commit_canvas_to_kv(canvas, ctr)
     eng.commit_canvas_to_kv()
     torch.cuda.synchronize()
     assert eng.ctx_len == om.ctx and eng.canvas_index == 1
     if check_kv:
+        cflip = check_routing(mc, eng, ctr, mc.canvas_len, f"{tag} canvas commit")
         kc, vc = eng.kv_views()
         l = mc.n_layers - 1
         gk = kc[l, :, :, P:P + mc.canvas_len].float().cpu().numpy()
         rk = om.k_cache[l][:, :, P:P + mc.canvas_len]
-        ek = np.abs(gk - rk).max() / np.abs(rk).max()
-        log(f"[{tag}] committed canvas K rel {ek:.2e}")
-        assert ek < tol_for(mc)
+        ek = np.abs(gk - rk).max(axis=(1, 3)) / np.abs(rk).max()
+        log(f"[{tag}] committed canvas K rel {ek[~cflip].max():.2e}")
+        assert ek[~cflip].max() < tol
     eng.close()
 
 
@@ -230,16 +304,22 @@ def test_tiny_workload_full_canvas(torch_cuda):
 
 def test_micro_bf16_selfcond_ragged_prompt(torch_cuda):
     mc = micro()
-    _run_parity(torch_cuda, mc, 11, 300, 2, 3, "micro-bf16", gain_std=0.1, route_taint=0.02)
+    _run_parity(torch_cuda, mc, 11, 300, 2, 3, "micro-bf16", gain_std=0.1)
 
 
 def test_micro_hd128_gqa(torch_cuda):
     mc = micro(n_layers=1, n_q_heads=4, n_kv_heads=2, head_dim=128, n_experts=16, top_k=4, ffn_hidden=128,
                vocab=2048)
-    _run_parity(torch_cuda, mc, 12, 70, 1, 2, "micro-hd128", route_taint=0.02)
+    _run_parity(torch_cuda, mc, 12, 70, 1, 2, "micro-hd128")
 
 
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
     _run_parity(torch_cuda, mc, 13, 0, 1, 2, "micro-f32-dense")
+
+
+def test_small_workload_full_size(torch_cuda):
+    # the 4-layer bf16 model at its full shape: 512-token prompt, self-conditioning, 2 steps
+    wl = di.workload("small")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 2, "small")
