@@ -70,6 +70,22 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
     elif stage == "oproj":
         by = Hq * hd * d * es + R * Hq * hd * es + 2 * R * d * 4
         fl = 2 * R * Hq * hd * d
+    elif stage == "router":      # logits GEMM + top-k + bucketing
+        E = mc.n_experts
+        by = E * d * es + R * d * es + R * E * 4 + 3 * R * k * 4
+        fl = 2 * R * d * E
+    elif stage == "embed":       # gather (+ self-conditioning projection)
+        by = R * d * es + R * d * 4 + ((d * d * es + R * d * 4) if mc.self_cond else 0)
+        fl = 2 * R * d * d if mc.self_cond else 0
+    elif stage == "norm":
+        by = R * d * 4 + R * d * es
+        fl = 0
+    elif stage == "combine":
+        by = R * k * d * 4 + 2 * R * d * 4
+        fl = 2 * R * k * d
+    elif stage == "commit":
+        by = R * 16
+        fl = 0
     else:
         return None
     return by, fl
