@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_sampler.hip", "dg_api.cpp"]
+SOURCES = ["k_gemm.hip", "k_expert.hip", "k_attn.hip", "k_misc.hip", "k_sampler.hip", "dg_api.cpp"]
 ARCH = os.environ.get("DG_OFFLOAD_ARCH", "gfx950")
 
 

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -50,6 +51,8 @@ struct LayerW {
   const void* w_up;
   const void* w_down;
   void* wqkv;   // owned slice of dg_model::qkv_buf: [(Hq + 2 Hkv) hd, d]
+  void* pgu;    // owned slice of dg_model::pack_buf: fragment-packed gate/up (or null)
+  void* pd;     // owned slice of dg_model::pack_buf: fragment-packed down (or null)
 };
 
 struct dg_model {
@@ -61,6 +64,7 @@ struct dg_model {
   std::vector<LayerW> layers;
   void* emb_t = nullptr;     // owned: [d, V] transposed embedding (self-conditioning)
   void* qkv_buf = nullptr;   // owned: fused QKV matrices of every layer
+  void* pack_buf = nullptr;  // owned: fragment-packed expert weights of every layer
 };
 
 struct dg_state {
@@ -72,10 +76,10 @@ struct dg_state {
   // persistent
   void* kc; void* vc; float2* rope; float* s; int32_t* prev_am;
   // workspace
-  float* h; void* xn; float* qkv; void* q; void* attn; float* attn_po; float* attn_pml;
-  float* rlog; int* ridx; float* rw; int* chunk_counts; int* perm; int* pos; int4* tiles;
+  float* h; void* xn; float* part; size_t part_floats; void* q; void* attn; float* attn_po; float* attn_pml;
+  float* rlog; int* ridx; float* rw; int* perm; int* pos; int4* tiles;
   int* n_tiles; void* act; float* y; float* logits; HeadPart* hp; float* chunk_scale;
-  void* ptilde; float* sc_part; int32_t* tok;
+  void* ptilde; float* sc_part; int sc_sub; int32_t* tok;
   size_t total_bytes;
   // stage timing (dg_profile_enable): event pairs from a fixed pool
   uint32_t prof_mask = 0;
@@ -106,7 +110,8 @@ struct StageTimer {
 static dg_status check_config(const dg_config* c) {
   if (!c) return fail(DG_ERR_ARG, "config is null");
   if (c->n_layers < 1) return fail(DG_ERR_ARG, "n_layers must be >= 1");
-  if (c->d_model < 64 || c->d_model % 64) return fail(DG_ERR_UNSUPPORTED, "d_model must be a positive multiple of 64");
+  if (c->d_model < 256 || c->d_model % 256 || c->d_model > kMaxModel)
+    return fail(DG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 in 256..%d", kMaxModel);
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
     return fail(DG_ERR_ARG, "n_kv_heads must divide n_q_heads");
@@ -152,6 +157,8 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
   if (e != hipSuccess) { delete m; return fail(DG_ERR_HIP, "hipMalloc(qkv): %s", hipGetErrorString(e)); }
   for (int l = 0; l < cfg->n_layers; ++l) {
     LayerW L;
+    L.pgu = nullptr;
+    L.pd = nullptr;
     L.attn_norm = static_cast<const float*>(w[i++]);
     L.wq = w[i++]; L.wk = w[i++]; L.wv = w[i++]; L.wo = w[i++];
     L.ffn_norm = static_cast<const float*>(w[i++]);
@@ -167,6 +174,29 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     }
     m->layers.push_back(L);
   }
+  // expert weights repacked in MFMA-fragment order for the weight-streaming path
+  if (expert_stream_ok(d, cfg->ffn_hidden, (int)m->esz)) {
+    const size_t per_layer = (size_t)3 * cfg->n_experts * cfg->ffn_hidden * d * m->esz;
+    e = hipMalloc(&m->pack_buf, per_layer * cfg->n_layers);
+    for (int l = 0; e == hipSuccess && l < cfg->n_layers; ++l) {
+      LayerW& L = m->layers[l];
+      char* base = static_cast<char*>(m->pack_buf) + per_layer * l;
+      L.pgu = base;
+      L.pd = base + per_layer / 3 * 2;
+      e = cfg->dtype == DG_DTYPE_BF16
+              ? pack_expert_weights<bf16>(static_cast<const bf16*>(L.w_gate), static_cast<const bf16*>(L.w_up),
+                                          static_cast<const bf16*>(L.w_down), static_cast<bf16*>(L.pgu),
+                                          static_cast<bf16*>(L.pd), cfg->n_experts, d, cfg->ffn_hidden, 0)
+              : pack_expert_weights<float>(static_cast<const float*>(L.w_gate), static_cast<const float*>(L.w_up),
+                                           static_cast<const float*>(L.w_down), static_cast<float*>(L.pgu),
+                                           static_cast<float*>(L.pd), cfg->n_experts, d, cfg->ffn_hidden, 0);
+    }
+    if (e != hipSuccess) {
+      if (m->pack_buf) hipFree(m->pack_buf);
+      hipFree(m->qkv_buf); delete m;
+      return fail(DG_ERR_HIP, "packing expert weights: %s", hipGetErrorString(e));
+    }
+  }
   if (cfg->self_cond) {
     e = hipMalloc(&m->emb_t, (size_t)cfg->vocab * d * m->esz);
     if (e == hipSuccess) {
@@ -176,6 +206,7 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     }
     if (e != hipSuccess) {
       if (m->emb_t) hipFree(m->emb_t);
+      if (m->pack_buf) hipFree(m->pack_buf);
       hipFree(m->qkv_buf); delete m;
       return fail(DG_ERR_HIP, "building transposed embedding: %s", hipGetErrorString(e));
     }
@@ -183,6 +214,7 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
   e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     if (m->emb_t) hipFree(m->emb_t);
+    if (m->pack_buf) hipFree(m->pack_buf);
     hipFree(m->qkv_buf); delete m;
     return fail(DG_ERR_HIP, "model create: %s", hipGetErrorString(e));
   }
@@ -193,6 +225,7 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
 extern "C" void dg_model_destroy(dg_model* m) {
   if (!m) return;
   if (m->emb_t) hipFree(m->emb_t);
+  if (m->pack_buf) hipFree(m->pack_buf);
   if (m->qkv_buf) hipFree(m->qkv_buf);
   delete m;
 }
@@ -209,10 +242,22 @@ struct Layout {
 };
 
 struct Offsets {
-  size_t kc, vc, rope, s, prev_am, h, xn, qkv, q, attn, attn_po, attn_pml, rlog, ridx, rw, chunk_counts, perm, pos,
+  size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos,
       tiles, n_tiles, act, y, logits, hp, chunk_scale, ptilde, sc_part, tok, total;
-  int chunks, clen, splits, cap_tiles;
+  size_t part_floats;
+  int chunks, clen, splits, cap_tiles, sc_sub;
 };
+
+// K-slices of one sampler chunk in the softmax @ E contraction: enough
+// workgroups to fill the chip, each slice at least four 128-byte K steps.
+int selfcond_sub(int R, int d, int chunks, int clen, int esz) {
+  const int bm = (R >= 128 && d >= 128) ? 128 : 64;
+  const int tiles = ((R + bm - 1) / bm) * ((d + bm - 1) / bm);
+  const int bk = 128 / esz;
+  int sub = 1;
+  while (tiles * chunks * sub < 512 && clen % (sub * 2 * bk) == 0 && clen / (sub * 2) >= 4 * bk) sub *= 2;
+  return sub;
+}
 
 Offsets layout(const dg_model* m, int B, int max_ctx) {
   const dg_config& c = m->cfg;
@@ -233,7 +278,9 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.prev_am = L.take((size_t)R * 4);
   o.h = L.take((size_t)R * d * 4);
   o.xn = L.take((size_t)R * d * es);
-  o.qkv = L.take((size_t)R * nqkv * 4);
+  const int maxN = nqkv > d ? (nqkv > E ? nqkv : E) : (d > E ? d : E);
+  o.part_floats = std::max((size_t)R * maxN * 8, (size_t)1 << 22);
+  o.part = L.take(o.part_floats * 4);
   o.q = L.take((size_t)R * Hq * hd * es);
   o.attn = L.take((size_t)R * Hq * hd * es);
   o.attn_po = L.take((size_t)o.splits * R * Hq * hd * 4);
@@ -241,7 +288,6 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.rlog = L.take((size_t)c.n_layers * R * E * 4);      // per layer, kept for inspection
   o.ridx = L.take((size_t)c.n_layers * R * k * 4);
   o.rw = L.take((size_t)R * k * 4);
-  o.chunk_counts = L.take((size_t)((R + 255) / 256) * E * 4);
   o.perm = L.take((size_t)R * k * 4);
   o.pos = L.take((size_t)R * k * 4);
   o.tiles = L.take((size_t)o.cap_tiles * sizeof(int4));
@@ -252,7 +298,8 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.hp = L.take((size_t)R * o.chunks * sizeof(HeadPart));
   o.chunk_scale = L.take((size_t)R * o.chunks * 4);
   o.ptilde = c.self_cond ? L.take((size_t)R * V * es) : 0;
-  o.sc_part = c.self_cond ? L.take((size_t)o.chunks * R * d * 4) : 0;
+  o.sc_sub = selfcond_sub(R, d, o.chunks, o.clen, (int)es);
+  o.sc_part = c.self_cond ? L.take((size_t)o.chunks * o.sc_sub * R * d * 4) : 0;
   o.tok = L.take((size_t)R * 4);
   o.total = L.off;
   return o;
@@ -284,11 +331,12 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->kv_layer_elems = (size_t)batch * m->cfg.n_kv_heads * max_ctx * m->cfg.head_dim;
   s->kc = b + o.kc; s->vc = b + o.vc; s->rope = reinterpret_cast<float2*>(b + o.rope);
   s->s = reinterpret_cast<float*>(b + o.s); s->prev_am = reinterpret_cast<int32_t*>(b + o.prev_am);
-  s->h = reinterpret_cast<float*>(b + o.h); s->xn = b + o.xn; s->qkv = reinterpret_cast<float*>(b + o.qkv);
+  s->h = reinterpret_cast<float*>(b + o.h); s->xn = b + o.xn;
+  s->part = reinterpret_cast<float*>(b + o.part); s->part_floats = o.part_floats; s->sc_sub = o.sc_sub;
   s->q = b + o.q; s->attn = b + o.attn;
   s->attn_po = reinterpret_cast<float*>(b + o.attn_po); s->attn_pml = reinterpret_cast<float*>(b + o.attn_pml);
   s->rlog = reinterpret_cast<float*>(b + o.rlog); s->ridx = reinterpret_cast<int*>(b + o.ridx);
-  s->rw = reinterpret_cast<float*>(b + o.rw); s->chunk_counts = reinterpret_cast<int*>(b + o.chunk_counts);
+  s->rw = reinterpret_cast<float*>(b + o.rw);
   s->perm = reinterpret_cast<int*>(b + o.perm); s->pos = reinterpret_cast<int*>(b + o.pos);
   s->tiles = reinterpret_cast<int4*>(b + o.tiles); s->n_tiles = reinterpret_cast<int*>(b + o.n_tiles);
   s->act = b + o.act; s->y = reinterpret_cast<float*>(b + o.y); s->logits = reinterpret_cast<float*>(b + o.logits);
@@ -367,9 +415,21 @@ SeedArg make_seeds(const uint64_t* h, int B) {
   return a;
 }
 
+// Split plan of a small-M product, reduced if the partial buffer is too small.
+SplitPlan plan(const dg_state* st, int M, int N, int K) {
+  SplitPlan p = plan_splits(M, N, K, 64, 64, (int)st->m->esz, 512);
+  const int bk = 128 / (int)st->m->esz;
+  while (p.splits > 1 && (size_t)p.splits * M * N > st->part_floats) {
+    const int s = p.splits - 1;
+    p.kchunk = ((K + s - 1) / s + bk - 1) / bk * bk;
+    p.splits = (K + p.kchunk - 1) / p.kchunk;
+  }
+  return p;
+}
+
 // Layer stack over B x nq new rows at positions ctx..ctx+nq-1 whose tokens are
-// st->tok (or `tok`), writing their K/V to the cache.  Leaves the residual
-// stream in st->h.
+// `tok`, writing their K/V to the cache.  Leaves the residual stream in st->h
+// and rnd(final RMSNorm(h)) in st->xn.
 template <typename T>
 dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool self_cond, hipStream_t s) {
   const dg_model* m = st->m;
@@ -378,31 +438,34 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   const int k = c.top_k, F = c.ffn_hidden, M = st->B * nq;
   const int nqkv = (Hq + 2 * Hkv) * hd;
   T* xn = static_cast<T*>(st->xn);
+  if ((size_t)M * std::max(nqkv, std::max(d, E)) > st->part_floats)
+    return fail(DG_ERR_CAPACITY, "partial buffer too small for %d rows", M);
   {
     StageTimer tm(st, DG_STAGE_EMBED, s);
-    if (self_cond)
-      DG_HIP(gemm_embed_selfcond<T>(st->s, static_cast<const T*>(m->w_sc), static_cast<const T*>(m->emb), tok,
-                                    st->h, M, d, c.vocab, s));
-    else
-      DG_HIP(embed_rows<T>(static_cast<const T*>(m->emb), tok, st->h, M, d, c.vocab, s));
+    int S = 0;
+    if (self_cond) {
+      const SplitPlan sp = plan(st, M, d, d);
+      DG_HIP(gemm_partials_f32a<T>(st->s, d, static_cast<const T*>(m->w_sc), d, st->part, M, d, d, sp, s));
+      S = sp.splits;
+    }
+    DG_HIP(embed_norm<T>(static_cast<const T*>(m->emb), tok, st->part, S, M, d, c.vocab, m->layers[0].attn_norm,
+                         c.rms_eps, st->h, xn, s));
   }
   const int keys = st->ctx + nq;
   int splits = attention_splits(st->B, nq, Hq, Hkv, keys);
   if (splits > st->attn_splits_max) splits = st->attn_splits_max;
   const int cap = expert_tile_capacity(M, k, E);
+  const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd), p_r = plan(st, M, E, d);
+  const bool stream_ok = m->pack_buf != nullptr;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     T* kc = static_cast<T*>(st->kc) + st->kv_layer_elems * l;
     T* vc = static_cast<T*>(st->vc) + st->kv_layer_elems * l;
     {
-      StageTimer tm(st, DG_STAGE_NORM, s);
-      DG_HIP(rmsnorm_rows<T>(st->h, L.attn_norm, xn, M, d, c.rms_eps, s));
-    }
-    {
       StageTimer tm(st, DG_STAGE_QKV, s);
-      DG_HIP(gemm_store_f32<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->qkv, nqkv, M, nqkv, d, s));
-      DG_HIP(rope_scatter<T>(st->qkv, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv, hd,
-                             st->max_ctx, st->ctx, s));
+      DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, s));
+      DG_HIP(rope_scatter<T>(st->part, p_qkv.splits, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv,
+                             hd, st->max_ctx, st->ctx, s));
     }
     {
       StageTimer tm(st, DG_STAGE_ATTN, s);
@@ -414,34 +477,46 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     }
     {
       StageTimer tm(st, DG_STAGE_OPROJ, s);
-      DG_HIP(gemm_resid_add<T>(static_cast<const T*>(st->attn), Hq * hd, static_cast<const T*>(L.wo), Hq * hd,
-                               st->h, d, M, d, Hq * hd, s));
+      DG_HIP(gemm_partials<T>(static_cast<const T*>(st->attn), Hq * hd, static_cast<const T*>(L.wo), Hq * hd,
+                              st->part, M, d, Hq * hd, p_o, s));
     }
     {
       StageTimer tm(st, DG_STAGE_NORM, s);
-      DG_HIP(rmsnorm_rows<T>(st->h, L.ffn_norm, xn, M, d, c.rms_eps, s));
+      DG_HIP(add_norm<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn, s));
     }
     {
       StageTimer tm(st, DG_STAGE_ROUTER, s);
       float* rlog = st->rlog + (size_t)l * st->R * E;
       int* ridx = st->ridx + (size_t)l * st->R * k;
-      DG_HIP(gemm_store_f32<T>(xn, d, static_cast<const T*>(L.w_router), d, rlog, E, M, E, d, s));
-      DG_HIP(router_topk(rlog, M, E, k, ridx, st->rw, s));
-      DG_HIP(route_bucket(ridx, M, k, E, st->chunk_counts, st->perm, st->pos, st->tiles, st->n_tiles, s));
+      DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.w_router), d, st->part, M, E, d, p_r, s));
+      DG_HIP(router_topk(st->part, p_r.splits, M, E, k, rlog, ridx, st->rw, s));
+      DG_HIP(route_bucket(ridx, M, k, E, st->perm, st->pos, st->tiles, st->n_tiles, s));
     }
+    // weight streaming while experts see at most ~64 routed rows on average
+    // (the batch-1 shapes); the LDS-tiled engine once they see many
+    const bool stream = stream_ok && (size_t)M * k <= (size_t)64 * E;
     {
       StageTimer tm(st, DG_STAGE_EXPERT_UP, s);
-      DG_HIP(gemm_expert_gateup<T>(xn, st->perm, static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up),
-                                   static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s));
+      if (stream)
+        DG_HIP(expert_stream_gateup<T>(xn, st->perm, static_cast<const T*>(L.pgu), static_cast<T*>(st->act),
+                                       st->tiles, st->n_tiles, cap, d, F, s));
+      else
+        DG_HIP(gemm_expert_gateup<T>(xn, st->perm, static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up),
+                                     static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s));
     }
     {
       StageTimer tm(st, DG_STAGE_EXPERT_DOWN, s);
-      DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), st->y,
-                                 st->tiles, st->n_tiles, cap, d, F, s));
+      if (stream)
+        DG_HIP(expert_stream_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.pd), st->y,
+                                     st->tiles, st->n_tiles, cap, d, F, s));
+      else
+        DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), st->y,
+                                   st->tiles, st->n_tiles, cap, d, F, s));
     }
     {
       StageTimer tm(st, DG_STAGE_COMBINE, s);
-      DG_HIP(moe_combine(st->y, st->pos, st->rw, st->h, M, k, d, s));
+      const float* g_next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
+      DG_HIP(combine_norm<T>(st->y, st->pos, st->rw, k, M, d, g_next, c.rms_eps, st->h, xn, s));
     }
   }
   return DG_OK;
@@ -478,15 +553,11 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sa
   const bool sc = c.self_cond && step > 0;
   dg_status r = run_stack<T>(st, canvas, st->n, false, sc, s);
   if (r) return r;
-  T* xn = static_cast<T*>(st->xn);
-  {
-    StageTimer tm(st, DG_STAGE_NORM, s);
-    DG_HIP(rmsnorm_rows<T>(st->h, m->final_norm, xn, R, d, c.rms_eps, s));
-  }
+  T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
   float* logits = logits_out ? logits_out : st->logits;
   {
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
-    DG_HIP(gemm_store_f32<T>(xn, d, static_cast<const T*>(m->emb), d, logits, V, R, V, d, s));
+    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, logits, R, V, d, s));
   }
   const float T_t = step_temperature(p, step);
   const float inv_t = (float)(1.0 / (double)T_t);
@@ -500,9 +571,9 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sa
   }
   if (c.self_cond) {
     StageTimer tm(st, DG_STAGE_SELFCOND, s);
-    DG_HIP(gemm_splitk<T>(pt, V, static_cast<const T*>(m->emb_t), V, st->sc_part, R, d, V, st->chunks, st->clen,
-                          s));
-    DG_HIP(selfcond_reduce(st->sc_part, st->chunk_scale, R, d, st->chunks, st->s, s));
+    DG_HIP(gemm_splitk<T>(pt, V, static_cast<const T*>(m->emb_t), V, st->sc_part, R, d, V,
+                          st->chunks * st->sc_sub, st->clen / st->sc_sub, s));
+    DG_HIP(selfcond_reduce(st->sc_part, st->chunk_scale, R, d, st->chunks, st->sc_sub, st->s, s));
   }
   return DG_OK;
 }

@@ -23,16 +23,23 @@ inline int expert_tile_capacity(int rows, int top_k, int n_experts) {
 }
 
 // ---- matrix products (k_gemm.hip); B operands are [N, K] K-contiguous
+constexpr int kMaxSplits = 16;
+constexpr int kMaxModel = 4096;           // largest d_model of the row-wise kernels
+struct SplitPlan {
+  int splits, kchunk;
+};
+SplitPlan plan_splits(int M, int N, int K, int bm, int bn, int elem_bytes, int target);
+// part[s][r][c] = sum over k in split s of A[r][k] * B[c][k]   (fp32, [splits][M][N])
 template <typename T>
-hipError_t gemm_store_f32(const T* A, int lda, const T* B, int ldb, float* C, int ldc, int M, int N,
-                          int K, hipStream_t s);
+hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
+                         SplitPlan sp, hipStream_t s);
+// same with an fp32 A rounded to the operand type on load
 template <typename T>
-hipError_t gemm_resid_add(const T* A, int lda, const T* B, int ldb, float* H, int ldh, int M, int N,
-                          int K, hipStream_t s);
-// H[r][c] = emb[tok[r]][c] + (S[r] rounded to T) . W[c]; ids clamped to [0, vocab)
+hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
+                              SplitPlan sp, hipStream_t s);
+// out[r][c] = A[r] . B[c]  (the tied LM head)
 template <typename T>
-hipError_t gemm_embed_selfcond(const float* S, const T* W, const T* emb, const int32_t* tok,
-                               float* H, int M, int d, int vocab, hipStream_t s);
+hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, float* out, int M, int N, int K, hipStream_t s);
 // act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
@@ -42,6 +49,19 @@ hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const 
 template <typename T>
 hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
                             const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
+// Weight-streaming expert products for thin routed tiles (k_expert.hip) over
+// fragment-packed weights: PGU[e][F/16][d/32][2][64][8] (gate/up) and
+// PD[e][d/16][F/32][64][8] (down), built by pack_expert_weights.
+bool expert_stream_ok(int d, int F, int elem_bytes);
+template <typename T>
+hipError_t pack_expert_weights(const T* gate, const T* up, const T* down, T* pgu, T* pd, int E, int d, int F,
+                               hipStream_t s);
+template <typename T>
+hipError_t expert_stream_gateup(const T* X, const int* perm, const T* pgu, T* act, const int4* tiles,
+                                const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
+template <typename T>
+hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* tiles, const int* n_tiles,
+                              int cap_tiles, int d, int F, hipStream_t s);
 // part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of P[r][k] * Bt[c][k]
 template <typename T>
 hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, int M, int N, int K,
@@ -65,25 +85,29 @@ template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t s);
 int attention_splits(int B, int nq, int Hq, int Hkv, int keys);
 
-// ---- small kernels (k_misc.hip)
+// ---- row-wise kernels (k_misc.hip); S = number of split partials to reduce
 template <typename T>
-hipError_t embed_rows(const T* emb, const int32_t* tok, float* H, int M, int d, int vocab, hipStream_t s);
+hipError_t embed_norm(const T* emb, const int32_t* tok, const float* part, int S, int M, int d, int vocab,
+                      const float* g, float eps, float* H, T* xn, hipStream_t s);
 template <typename T>
-hipError_t rmsnorm_rows(const float* H, const float* g, T* out, int M, int d, float eps, hipStream_t s);
-// RoPE on q and k of the fused projection, q -> Q buffer, k and v -> cache at ctx + i
+hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
+                    hipStream_t s);
 template <typename T>
-hipError_t rope_scatter(const float* qkv, const float2* rope, T* q, T* kc, T* vc, int B, int n,
-                        int Hq, int Hkv, int hd, int max_ctx, int ctx, hipStream_t s);
+hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
+                        float eps, float* H, T* xn, hipStream_t s);
+// RoPE on q and k of the fused projection (sum of S partials), q -> Q buffer, k and v -> cache at ctx + i
+template <typename T>
+hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
+                        int Hkv, int hd, int max_ctx, int ctx, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
-hipError_t router_topk(const float* logits, int M, int E, int k, int* idx, float* w, hipStream_t s);
-hipError_t route_bucket(const int* idx, int M, int k, int E, int* chunk_counts, int* perm, int* pos,
-                        int4* tiles, int* n_tiles, hipStream_t s);
-hipError_t moe_combine(const float* Y, const int* pos, const float* w, float* H, int M, int k, int d,
+hipError_t router_topk(const float* part, int S, int M, int E, int k, float* rlog, int* idx, float* w,
                        hipStream_t s);
+hipError_t route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
+                        hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
-hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab,
-                       int canvas_index, hipStream_t s);
+hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,
+                       hipStream_t s);
 
 // ---- sampler (k_sampler.hip)
 struct HeadPart {       // statistics of one (row, vocab chunk)
@@ -105,7 +129,8 @@ hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float 
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
                          float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale,
                          hipStream_t s);
-hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks,
+// S[r][c] = sum over splits of chunk_scale[r][split / sub] * part[split][r][c]
+hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub,
                            float* S, hipStream_t s);
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,
                          int32_t* prev_am, uint8_t* mask, int32_t* n_committed, uint8_t* done,

@@ -1,14 +1,18 @@
 // MFMA tile engine for the matrix products of the denoise step (gfx950).
 //
-// One workgroup = 4 wave64s computes a 64 x 64 fp32 tile of C = A * B^T with
-// A [rows, K] and B [cols, K] both K-contiguous.  K is walked in 128-byte
-// slices (64 bf16 or 32 fp32 elements) staged through LDS with two buffers:
-// the next slice is fetched into registers while the current one feeds the
-// matrix cores, then written to the other buffer, one barrier per slice.
-// Waves are arranged 2 x 2; each owns a 32 x 32 sub-tile = 2 x 2 MFMA blocks
-// of 16 x 16 (v_mfma_f32_16x16x32_bf16, or 8 x v_mfma_f32_16x16x4_f32).
+// One workgroup = 4 wave64s computes a BM x BN fp32 tile of C = A * B^T with
+// A [rows, K] and B [cols, K] both K-contiguous (BM, BN in {64, 128}).  Waves
+// are arranged 2 x 2; each owns a (BM/2) x (BN/2) sub-tile made of 16 x 16
+// MFMA blocks (v_mfma_f32_16x16x32_bf16, or 8 x v_mfma_f32_16x16x4_f32).
 //
-// Schedulers map a workgroup id to a tile (dense, grouped by expert, or split
+// K is walked in 128-byte slices (64 bf16 / 32 fp32 per row).  Global loads
+// run STAGES-1 slices ahead of the matrix cores: each thread keeps STAGES-1
+// slices in registers, and the slice about to be used is written to one of two
+// LDS buffers, one barrier per slice.  With little arithmetic per slice (the
+// batch-1 products stream weights), the number of slices in flight is what
+// sets the achieved bandwidth.
+//
+// Schedulers map a workgroup id to a tile (dense, grouped by expert, split
 // along K); loaders produce 16 bytes of operand data for (tile row, k); an
 // epilogue consumes the accumulators.
 #pragma once
@@ -18,46 +22,54 @@ namespace dg {
 
 struct TileCtx {
   int m0, n0;        // first row / column of the tile in C
-  int rows, cols;    // valid rows / columns (<= 64)
+  int rows, cols;    // valid rows / columns of the tile
   int k0, k1;        // K range handled by this workgroup
-  int group;         // expert id (grouped GEMMs), split index (split-K)
-  int row_base;      // first gathered row of the tile (grouped GEMMs)
+  int group;         // expert id (grouped products), split index (split-K)
+  int row_base;      // first output row of the tile (gathered rows for grouped products)
 };
 
-template <typename T>
-struct TileShape {
-  static constexpr int BM = 64, BN = 64;
+template <typename T, int BM_, int BN_, int STAGES_ = 3>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
   static constexpr int EPC = 16 / (int)sizeof(T);      // elements per 16-byte chunk
   static constexpr int BK = 128 / (int)sizeof(T);      // K elements per slice
   static constexpr int LDK = BK + EPC;                 // padded LDS row stride (elements)
   static constexpr int KSTEPS = BK / 32;
-  static constexpr int kSmemBytes = 2 * 2 * BM * LDK * (int)sizeof(T);
+  static constexpr int WM = BM / 2, WN = BN / 2;       // per-wave sub-tile
+  static constexpr int FM = WM / 16, FN = WN / 16;     // MFMA blocks per wave
+  static constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;   // 16 B chunks per thread per slice
+  static constexpr int kSmemBytes = 2 * (BM + BN) * LDK * (int)sizeof(T);
 };
 
 // ------------------------------------------------------------------ schedulers
 // Dense tiles, column-tile major so that the row tiles sharing a weight tile are
 // consecutive; when the tile count is a multiple of 8, consecutive logical tiles
 // are placed on the same XCD (workgroups are dealt round-robin over 8 XCDs).
+// Optional split-K: the split index varies slowest.
+template <int BM, int BN>
 struct SchedDense {
-  int M, N, K, mt, nt;
+  int M, N, K, mt, nt, splits, kchunk;
   __device__ bool get(int bid, TileCtx& t) const {
-    const int total = mt * nt;
+    const int per = mt * nt, total = per * splits;
     if (bid >= total) return false;
     int idx = bid;
     if ((total & 7) == 0) idx = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int tm = idx % mt, tn = idx / mt;
-    t.m0 = tm * 64; t.n0 = tn * 64;
-    t.rows = min(64, M - t.m0); t.cols = min(64, N - t.n0);
-    t.k0 = 0; t.k1 = K; t.group = 0; t.row_base = t.m0;
+    const int s = idx / per, r = idx % per;
+    const int tm = r % mt, tn = r / mt;
+    t.m0 = tm * BM; t.n0 = tn * BN;
+    t.rows = min(BM, M - t.m0); t.cols = min(BN, N - t.n0);
+    t.k0 = s * kchunk; t.k1 = min(K, t.k0 + kchunk);
+    t.group = s; t.row_base = t.m0;
     return true;
   }
 };
 
 // Expert-grouped tiles: a device list of (expert, first gathered row, rows).
+template <int BM, int BN>
 struct SchedGroup {
   const int4* tiles;
   const int* n_tiles;
-  int nt, N, K, bn;      // bn: output columns per tile (64, or 32 for gate/up)
+  int nt, N, K, bn;      // bn: output columns per tile
   __device__ bool get(int bid, TileCtx& t) const {
     const int ti = bid / nt, tn = bid % nt;
     if (ti >= *n_tiles) return false;
@@ -69,68 +81,68 @@ struct SchedGroup {
   }
 };
 
-// Split-K over equal K chunks; the split index goes to t.group.
-struct SchedSplitK {
-  int M, N, K, mt, nt, splits, kchunk;
-  __device__ bool get(int bid, TileCtx& t) const {
-    const int per = mt * nt;
-    if (bid >= per * splits) return false;
-    const int s = bid / per, r = bid % per;
-    const int tn = r / mt, tm = r % mt;
-    t.m0 = tm * 64; t.n0 = tn * 64;
-    t.rows = min(64, M - t.m0); t.cols = min(64, N - t.n0);
-    t.k0 = s * kchunk; t.k1 = min(K, t.k0 + kchunk);
-    t.group = s; t.row_base = t.m0;
-    return true;
-  }
-};
-
 // ------------------------------------------------------------------ loaders
+// A loader resolves, once per tile, the row a thread copies (row()); every
+// K-slice then reads 16 bytes at an offset of that row (ld()).  Rows past the
+// tile's valid range are clamped to a valid row and their data zeroed after the
+// load, so every thread issues the same loads and the memory-wait counts stay
+// exact for the pipeline.
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0, 0, 0, 0); }
+
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const void* rowp, int k) {
+  return *reinterpret_cast<const uint4*>(static_cast<const T*>(rowp) + k);
+}
 
 template <typename T>
 struct ALPlain {            // A rows m0 + r of a K-contiguous matrix
   const T* p; int lda;
-  __device__ uint4 load(const TileCtx& t, int r, int k) const {
-    if (r >= t.rows) return zero16();
-    return *reinterpret_cast<const uint4*>(p + (size_t)(t.m0 + r) * lda + k);
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)(t.m0 + (valid ? r : 0)) * lda;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
 template <typename T>
 struct ALRows {             // A rows row_base + r (grouped, contiguous per tile)
   const T* p; int lda;
-  __device__ uint4 load(const TileCtx& t, int r, int k) const {
-    if (r >= t.rows) return zero16();
-    return *reinterpret_cast<const uint4*>(p + (size_t)(t.row_base + r) * lda + k);
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)(t.row_base + (valid ? r : 0)) * lda;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
 template <typename T>
 struct ALGather {           // A rows perm[row_base + r] (tokens routed to one expert)
   const T* p; int lda; const int* perm;
-  __device__ uint4 load(const TileCtx& t, int r, int k) const {
-    if (r >= t.rows) return zero16();
-    const int src = perm[t.row_base + r];
-    return *reinterpret_cast<const uint4*>(p + (size_t)src * lda + k);
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)perm[t.row_base + (valid ? r : 0)] * lda;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
 template <typename T> struct ALF32;   // fp32 source converted to the operand type
 template <>
 struct ALF32<float> {
   const float* p; int lda;
-  __device__ uint4 load(const TileCtx& t, int r, int k) const {
-    if (r >= t.rows) return zero16();
-    return *reinterpret_cast<const uint4*>(p + (size_t)(t.m0 + r) * lda + k);
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)(t.m0 + (valid ? r : 0)) * lda;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<float>(rp, k); }
 };
 template <>
 struct ALF32<bf16> {
   const float* p; int lda;
-  __device__ uint4 load(const TileCtx& t, int r, int k) const {
-    if (r >= t.rows) return zero16();
-    const float4* s = reinterpret_cast<const float4*>(p + (size_t)(t.m0 + r) * lda + k);
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)(t.m0 + (valid ? r : 0)) * lda;
+  }
+  __device__ uint4 ld(const void* rp, int k) const {
+    const float4* s = reinterpret_cast<const float4*>(static_cast<const float*>(rp) + k);
     const float4 a = s[0], b = s[1];
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     return pack8_bf16(v);
@@ -140,120 +152,150 @@ struct ALF32<bf16> {
 template <typename T>
 struct BLPlain {            // B rows n0 + n of a [N, K] matrix
   const T* p; int ldb;
-  __device__ uint4 load(const TileCtx& t, int n, int k) const {
-    if (n >= t.cols) return zero16();
-    return *reinterpret_cast<const uint4*>(p + (size_t)(t.n0 + n) * ldb + k);
+  __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
+    valid = n < t.cols;
+    return p + (size_t)(t.n0 + (valid ? n : 0)) * ldb;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
 template <typename T>
 struct BLExpert {           // B rows of expert `group`: base + group * stride
   const T* p; size_t stride; int ldb;
-  __device__ uint4 load(const TileCtx& t, int n, int k) const {
-    if (n >= t.cols) return zero16();
-    return *reinterpret_cast<const uint4*>(p + (size_t)t.group * stride + (size_t)(t.n0 + n) * ldb + k);
+  __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
+    valid = n < t.cols;
+    return p + (size_t)t.group * stride + (size_t)(t.n0 + (valid ? n : 0)) * ldb;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
+// Gate and up rows interleaved in blocks of 16: tile rows [32j, 32j+16) are
+// gate rows n0 + 16j.., rows [32j+16, 32j+32) the up rows of the same features,
+// so each wave's accumulator holds gate and up of the same 16 features side by side.
 template <typename T>
-struct BLGateUp {           // tile rows 0..31: gate rows n0.., rows 32..63: up rows n0..
+struct BLGateUp {
   const T* gate; const T* up; size_t stride; int ldb;
-  __device__ uint4 load(const TileCtx& t, int n, int k) const {
-    const int nn = n & 31;
-    if (nn >= t.cols) return zero16();
-    const T* base = (n < 32 ? gate : up) + (size_t)t.group * stride;
-    return *reinterpret_cast<const uint4*>(base + (size_t)(t.n0 + nn) * ldb + k);
+  __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
+    const int f = (n >> 5) * 16 + (n & 15);     // feature within the tile
+    valid = f < t.cols;
+    const T* base = ((n & 16) ? up : gate) + (size_t)t.group * stride;
+    return base + (size_t)(t.n0 + (valid ? f : 0)) * ldb;
   }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
 // ------------------------------------------------------------------ the tile loop
-// acc[tm][tn][i] holds C[wm*32 + tm*16 + (lane>>4)*4 + i][wn*32 + tn*16 + (lane&15)].
-template <typename T, class AL, class BL>
+// acc[a][b][i] holds C[wm*WM + a*16 + (lane>>4)*4 + i][wn*WN + b*16 + (lane&15)].
+template <class C, typename T, class AL, class BL>
 __device__ __forceinline__ void tile_mma(const TileCtx& t, const AL& al, const BL& bl, char* smem,
-                                         f32x4_t (&acc)[2][2]) {
-  using S = TileShape<T>;
+                                         f32x4_t (&acc)[C::FM][C::FN]) {
   T* sA = reinterpret_cast<T*>(smem);
-  T* sB = sA + 2 * S::BM * S::LDK;
+  T* sB = sA + 2 * C::BM * C::LDK;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < C::FM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (t.k1 - t.k0) / S::BK;
+  const int nk = (t.k1 - t.k0) / C::BK;
   if (nk <= 0) return;
-  uint4 ra[2], rb[2];
-  int rr[2], cc[2];
+  constexpr int P = C::STAGES - 1;       // slices held in registers
+  uint4 ra[P][C::ACH], rb[P][C::BCH];
+  const void* arow[C::ACH];
+  const void* brow[C::BCH];
+  bool aval[C::ACH], bval[C::BCH];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    rr[i] = c >> 3;
-    cc[i] = (c & 7) * S::EPC;
-  }
-  auto gload = [&](int k) {
+  for (int i = 0; i < C::ACH; ++i) arow[i] = al.row(t, (tid + 256 * i) >> 3, aval[i]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = al.load(t, rr[i], k + cc[i]);
-      rb[i] = bl.load(t, rr[i], k + cc[i]);
+  for (int i = 0; i < C::BCH; ++i) brow[i] = bl.row(t, (tid + 256 * i) >> 3, bval[i]);
+  const int kc = (tid & 7) * C::EPC;     // this thread's 16-byte column within a slice
+  auto gload = [&](int slot, int kt) {
+    if (kt >= nk) return;
+    const int k = t.k0 + kt * C::BK + kc;
+#pragma unroll
+    for (int i = 0; i < C::ACH; ++i) {
+      const uint4 v = al.ld(arow[i], k);
+      ra[slot][i] = aval[i] ? v : zero16();
+    }
+#pragma unroll
+    for (int i = 0; i < C::BCH; ++i) {
+      const uint4 v = bl.ld(brow[i], k);
+      rb[slot][i] = bval[i] ? v : zero16();
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int slot, int buf) {
+    T* a0 = sA + buf * C::BM * C::LDK;
+    T* b0 = sB + buf * C::BN * C::LDK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(sA + buf * S::BM * S::LDK + rr[i] * S::LDK + cc[i]) = ra[i];
-      *reinterpret_cast<uint4*>(sB + buf * S::BM * S::LDK + rr[i] * S::LDK + cc[i]) = rb[i];
+    for (int i = 0; i < C::ACH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(a0 + (c >> 3) * C::LDK + (c & 7) * C::EPC) = ra[slot][i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::BCH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(b0 + (c >> 3) * C::LDK + (c & 7) * C::EPC) = rb[slot][i];
     }
   };
-  gload(t.k0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(t.k0 + (kt + 1) * S::BK);
-    const T* a0 = sA + cur * S::BM * S::LDK;
-    const T* b0 = sB + cur * S::BM * S::LDK;
+  auto compute = [&](int buf) {
+    const T* a0 = sA + buf * C::BM * C::LDK;
+    const T* b0 = sB + buf * C::BN * C::LDK;
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; ++s) {
-      Frag<T> fa[2], fb[2];
+    for (int s = 0; s < C::KSTEPS; ++s) {
       const int kk = s * 32 + (lane >> 4) * 8;
+      Frag<T> fa[C::FM], fb[C::FN];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        lds_frag(fa[q], a0 + (wm * 32 + q * 16 + (lane & 15)) * S::LDK + kk);
-        lds_frag(fb[q], b0 + (wn * 32 + q * 16 + (lane & 15)) * S::LDK + kk);
-      }
+      for (int a = 0; a < C::FM; ++a) lds_frag(fa[a], a0 + (wm * C::WM + a * 16 + (lane & 15)) * C::LDK + kk);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < C::FN; ++b) lds_frag(fb[b], b0 + (wn * C::WN + b * 16 + (lane & 15)) * C::LDK + kk);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) mma16x16x32(acc[a][b], fa[a], fb[b]);
+      for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b) mma16x16x32(acc[a][b], fa[a], fb[b]);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  };
+
+#pragma unroll
+  for (int p = 0; p < P; ++p) gload(p, p);
+  // slice kt sits in register slot kt % P; unrolled by P so every slot index is static
+  for (int kt0 = 0; kt0 < nk; kt0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nk) {
+        sstore(u, kt & 1);
+        gload(u, kt + P);
+        __syncthreads();
+        compute(kt & 1);
+      }
+    }
   }
+  __syncthreads();   // the epilogue may reuse the shared memory
 }
 
-// Visit every accumulator element with its tile-relative (row, col).
-template <class F>
-__device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[2][2], F&& f) {
+// Visit every accumulator element with its tile-relative (row, col) and block indices.
+template <class C, class F>
+__device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[C::FM][C::FN], F&& f) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < C::FM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::FN; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        f(wm * 32 + a * 16 + (lane >> 4) * 4 + i, wn * 32 + b * 16 + (lane & 15), acc[a][b][i]);
+        f(wm * C::WM + a * 16 + (lane >> 4) * 4 + i, wn * C::WN + b * 16 + (lane & 15), acc[a][b][i]);
 }
 
-template <typename T, class SCHED, class AL, class BL, class EP>
+template <class C, typename T, class SCHED, class AL, class BL, class EP>
 __global__ __launch_bounds__(256) void k_gemm(SCHED sc, AL al, BL bl, EP ep) {
-  __shared__ __attribute__((aligned(16))) char smem[TileShape<T>::kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
   TileCtx t;
   if (!sc.get(blockIdx.x, t)) return;
-  f32x4_t acc[2][2];
-  tile_mma<T>(t, al, bl, smem, acc);
-  ep(t, acc, smem);
+  f32x4_t acc[C::FM][C::FN];
+  tile_mma<C, T>(t, al, bl, smem, acc);
+  ep.template apply<C>(t, acc);
 }
 
 }  // namespace dg

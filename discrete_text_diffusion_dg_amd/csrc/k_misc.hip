@@ -1,55 +1,146 @@
-// Row-wise kernels of the denoise step: embedding gather, RMSNorm, RoPE with
-// the KV-cache write, the MoE router (top-k, lowest expert id on ties, softmax
-// over the k selected logits), a stable counting sort of the routed rows by
-// expert, the fixed-order combine of expert outputs, and canvas initialisation.
+// Row-wise kernels of the denoise step.  Each reduces, in a fixed split order,
+// the fp32 partials of the split-K product before it and fuses the next
+// element-wise step: embedding gather (+ self-conditioning projection) with
+// the first RMSNorm, the attention output residual with the MoE RMSNorm, the
+// expert combine with the next layer's (or the final) RMSNorm, RoPE with the
+// KV-cache write, and the router logits with top-k (lowest expert id on
+// ties) and the softmax over the k selected logits.  Routed rows are bucketed
+// per expert by a stable counting sort; canvas initialisation draws Philox.
 #include "dg_kernels.h"
 
 namespace dg {
 
-// ------------------------------------------------------------------ embedding
+namespace {
+// One workgroup per row, TPR = min(256, d / 4) threads, each owning up to
+// kRowChunks float4 chunks of the row (d <= kMaxModel).
+constexpr int kRowChunks = kMaxModel / 1024;
+
+inline int row_threads(int d) { return d / 4 < 256 ? d / 4 : 256; }
+
+// Stores the updated residual row v and y = rnd(v * g / sqrt(mean(v^2) + eps)).
 template <typename T>
-__global__ void k_embed(const T* emb, const int32_t* tok, float* H, int d, int vocab) {
-  const int r = blockIdx.x;
-  const int id = min(max(tok[r], 0), vocab - 1);   // out-of-range ids are clamped, never read past E
-  const T* src = emb + (size_t)id * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) H[(size_t)r * d + c] = Num<T>::load(src + c);
-}
-template <typename T>
-hipError_t embed_rows(const T* emb, const int32_t* tok, float* H, int M, int d, int vocab, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_embed<T>), dim3(M), dim3(256), 0, s, emb, tok, H, d, vocab);
-  return hipGetLastError();
+__device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int d, const float* g, float eps,
+                                           float* hrow, T* xrow) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = (blockDim.x + 63) >> 6;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  ss = red[0];
+  for (int q = 1; q < nw; ++q) ss += red[q];
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + tid) * 4;
+      *reinterpret_cast<float4*>(hrow + c) = v[j];
+      const float4 gg = *reinterpret_cast<const float4*>(g + c);
+      Num<T>::store(xrow + c + 0, v[j].x * inv * gg.x);
+      Num<T>::store(xrow + c + 1, v[j].y * inv * gg.y);
+      Num<T>::store(xrow + c + 2, v[j].z * inv * gg.z);
+      Num<T>::store(xrow + c + 3, v[j].w * inv * gg.w);
+    }
 }
 
-// ------------------------------------------------------------------ RMSNorm
-// y = x * g / sqrt(mean(x^2) + eps), rounded to the operand type; one wave per row.
+__device__ __forceinline__ void add4(float4& a, const float4 b) {
+  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+}  // namespace
+
+// h = emb[tok] (+ sum_s part[s]); xn = rnd(rmsnorm(h) * g)
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* H, const float* g, T* out, int M, int d,
-                                                 float eps) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= M) return;
-  const float* x = H + (size_t)r * d;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  T* o = out + (size_t)r * d;
-  for (int c = lane * 4; c < d; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const float4 gg = *reinterpret_cast<const float4*>(g + c);
-    Num<T>::store(o + c + 0, v.x * inv * gg.x);
-    Num<T>::store(o + c + 1, v.y * inv * gg.y);
-    Num<T>::store(o + c + 2, v.z * inv * gg.z);
-    Num<T>::store(o + c + 3, v.w * inv * gg.w);
-  }
+__global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t* tok, const float* part, int S,
+                                                    int M, int d, int vocab, const float* g, float eps, float* H,
+                                                    T* xn) {
+  const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  const int id = min(max(tok[r], 0), vocab - 1);   // out-of-range ids are clamped, never read past E
+  float4 v[kRowChunks];
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + threadIdx.x) * 4;
+      const T* e = emb + (size_t)id * d + c;
+      float4 x = make_float4(Num<T>::load(e), Num<T>::load(e + 1), Num<T>::load(e + 2), Num<T>::load(e + 3));
+      float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < S; ++s) add4(p, *reinterpret_cast<const float4*>(part + ((size_t)s * M + r) * d + c));
+      add4(x, p);
+      v[j] = x;
+    }
+  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
+}
+
+// h += sum_s part[s]; xn = rnd(rmsnorm(h) * g)
+template <typename T>
+__global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int M, int d, const float* g, float eps,
+                                                  float* H, T* xn) {
+  const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  float4 v[kRowChunks];
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + threadIdx.x) * 4;
+      float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < S; ++s) add4(p, *reinterpret_cast<const float4*>(part + ((size_t)s * M + r) * d + c));
+      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
+      add4(x, p);
+      v[j] = x;
+    }
+  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
+}
+
+// h += sum_j w[j] * Y[pos[j]] (slots in selection order); xn = rnd(rmsnorm(h) * g)
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int* pos, const float* w, int k, int M,
+                                                      int d, const float* g, float eps, float* H, T* xn) {
+  const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  int ps[8];
+  float ws[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    if (s < k) { ps[s] = pos[(size_t)r * k + s]; ws[s] = w[(size_t)r * k + s]; }
+  float4 v[kRowChunks];
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + threadIdx.x) * 4;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s < k) {
+          const float4 y = *reinterpret_cast<const float4*>(Y + (size_t)ps[s] * d + c);
+          acc.x += ws[s] * y.x; acc.y += ws[s] * y.y; acc.z += ws[s] * y.z; acc.w += ws[s] * y.w;
+        }
+      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
+      add4(x, acc);
+      v[j] = x;
+    }
+  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
+}
+
+template <typename T>
+hipError_t embed_norm(const T* emb, const int32_t* tok, const float* part, int S, int M, int d, int vocab,
+                      const float* g, float eps, float* H, T* xn, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_embed_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, emb, tok, part, S, M, d, vocab, g, eps,
+                     H, xn);
+  return hipGetLastError();
 }
 template <typename T>
-hipError_t rmsnorm_rows(const float* H, const float* g, T* out, int M, int d, float eps, hipStream_t s) {
+hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
+                    hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_rmsnorm<T>), dim3((M + 3) / 4), dim3(256), 0, s, H, g, out, M, d, eps);
+  hipLaunchKernelGGL((k_add_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
+                        float eps, float* H, T* xn, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_combine_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, Y, pos, w, k, M, d, g, eps, H, xn);
   return hipGetLastError();
 }
 
@@ -71,18 +162,24 @@ hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t
   return hipGetLastError();
 }
 
-// Rotate-half RoPE on the fused projection output (fp32), then round: q to the
-// query buffer, k and v to the cache at position ctx + i.
+// Sum the split partials of the fused projection, apply rotate-half RoPE to q
+// and k (fp32), then round: q to the query buffer, k and v to the cache at
+// position ctx + i.
 template <typename T>
-__global__ void k_rope_scatter(const float* qkv, const float2* rope, T* q, T* kc, T* vc, int n, int Hq,
-                               int Hkv, int hd, int max_ctx, int ctx) {
+__global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int M, int n,
+                               int Hq, int Hkv, int hd, int max_ctx, int ctx) {
   const int r = blockIdx.x, b = r / n, i = r % n, pos = ctx + i, half = hd / 2;
   const int ncol = (Hq + 2 * Hkv) * hd;
-  const float* x = qkv + (size_t)r * ncol;
+  const size_t sstride = (size_t)M * ncol;
+  const float* x = part + (size_t)r * ncol;
   const float2* cs = rope + (size_t)pos * half;
   for (int u = threadIdx.x; u < (Hq + Hkv) * half; u += blockDim.x) {
     const int head = u / half, j = u % half;
-    const float a = x[head * hd + j], bb = x[head * hd + j + half];
+    float a = 0.f, bb = 0.f;
+    for (int s = 0; s < S; ++s) {
+      a += x[s * sstride + head * hd + j];
+      bb += x[s * sstride + head * hd + j + half];
+    }
     const float2 t = cs[j];
     const float o1 = a * t.x - bb * t.y, o2 = bb * t.x + a * t.y;
     if (head < Hq) {
@@ -98,152 +195,134 @@ __global__ void k_rope_scatter(const float* qkv, const float2* rope, T* q, T* kc
   }
   for (int u = threadIdx.x; u < Hkv * hd; u += blockDim.x) {
     const int kh = u / hd, c = u % hd;
-    Num<T>::store(vc + (((size_t)b * Hkv + kh) * max_ctx + pos) * hd + c, x[(Hq + Hkv) * hd + u]);
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += x[s * sstride + (Hq + Hkv) * hd + u];
+    Num<T>::store(vc + (((size_t)b * Hkv + kh) * max_ctx + pos) * hd + c, v);
   }
 }
 template <typename T>
-hipError_t rope_scatter(const float* qkv, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
+hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
                         int Hkv, int hd, int max_ctx, int ctx, hipStream_t s) {
   if (B * n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_rope_scatter<T>), dim3(B * n), dim3(256), 0, s, qkv, rope, q, kc, vc, n, Hq, Hkv,
-                     hd, max_ctx, ctx);
+  hipLaunchKernelGGL((k_rope_scatter<T>), dim3(B * n), dim3(256), 0, s, part, S, rope, q, kc, vc, B * n, n, Hq,
+                     Hkv, hd, max_ctx, ctx);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ router
-// One thread per row: k passes of an arg-max over the E logits (strict > keeps
-// the lowest id among equal values), then softmax over the selected logits.
-__global__ void k_router_topk(const float* logits, int M, int E, int k, int* idx, float* w) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row: the router logits (sum of split partials) sit two per
+// lane; k rounds of a wave arg-max (ties to the lower expert id) pick the
+// experts in descending order, then softmax over the selected logits.
+__global__ __launch_bounds__(256) void k_router_topk(const float* part, int S, int M, int E, int k, float* rlog,
+                                                     int* idx, float* w) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= M) return;
-  const float* x = logits + (size_t)r * E;
-  uint32_t used[4] = {0u, 0u, 0u, 0u};
+  float v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = lane + 64 * h;
+    float x = -INFINITY;
+    if (e < E) {
+      x = 0.f;
+      for (int s = 0; s < S; ++s) x += part[((size_t)s * M + r) * E + e];
+      rlog[(size_t)r * E + e] = x;
+    }
+    v[h] = x;
+  }
+  bool used0 = lane >= E, used1 = lane + 64 >= E;
   float sel[8];
   int sid[8];
-  for (int j = 0; j < k; ++j) {
-    float best = -INFINITY;
-    int bi = -1;
-    for (int e = 0; e < E; ++e) {
-      if ((used[e >> 5] >> (e & 31)) & 1u) continue;
-      const float v = x[e];
-      if (bi < 0 || v > best) { best = v; bi = e; }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv;
+    int bi;
+    if (!used0 && (used1 || v[0] >= v[1])) { bv = v[0]; bi = lane; }
+    else if (!used1) { bv = v[1]; bi = lane + 64; }
+    else { bv = -INFINITY; bi = 0x7fffffff; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    used[bi >> 5] |= 1u << (bi & 31);
-    sel[j] = best;
+    if (bi == lane) used0 = true;
+    if (bi == lane + 64) used1 = true;
+    sel[j] = bv;
     sid[j] = bi;
   }
-  const float mx = sel[0];   // selection order is descending, so slot 0 holds the max
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) { sel[j] = expf(sel[j] - mx); sum += sel[j]; }
-  for (int j = 0; j < k; ++j) {
-    idx[(size_t)r * k + j] = sid[j];
-    w[(size_t)r * k + j] = sel[j] / sum;
+  if (lane == 0) {
+    const float mx = sel[0];   // selection order is descending, so slot 0 holds the max
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) if (j < k) { sel[j] = expf(sel[j] - mx); sum += sel[j]; }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) {
+        idx[(size_t)r * k + j] = sid[j];
+        w[(size_t)r * k + j] = sel[j] / sum;
+      }
   }
 }
-hipError_t router_topk(const float* logits, int M, int E, int k, int* idx, float* w, hipStream_t s) {
+hipError_t router_topk(const float* part, int S, int M, int E, int k, float* rlog, int* idx, float* w,
+                       hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_router_topk, dim3((M + 127) / 128), dim3(128), 0, s, logits, M, E, k, idx, w);
+  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, part, S, M, E, k, rlog, idx, w);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ bucketing
-// Stable counting sort of (row, slot) entries by expert, rows in chunks of 256:
-// (1) per-chunk expert counts, (2) one workgroup scans them into per-chunk
-// bases and writes the 64-row tile list, (3) each entry's rank among the
-// chunk's earlier rows for the same expert comes from an LDS bitmask.
-__global__ __launch_bounds__(256) void k_route_count(const int* idx, int M, int k, int E, int* cc) {
-  __shared__ int cnt[128];
-  const int chunk = blockIdx.x, r = chunk * 256 + threadIdx.x;
-  if (threadIdx.x < E) cnt[threadIdx.x] = 0;
+// One workgroup: per-expert counts, the 64-row tile list, then a stable
+// scatter of (row, slot) entries by expert, rows in chunks of 256 whose ranks
+// within an expert come from an LDS bitmask.
+__global__ __launch_bounds__(256) void k_route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos,
+                                                      int4* tiles, int* n_tiles) {
+  __shared__ int cnt[128], base[128];
+  __shared__ uint32_t bits[128][8];
+  const int t = threadIdx.x;
+  if (t < 128) cnt[t] = 0;
   __syncthreads();
-  if (r < M)
+  for (int r = t; r < M; r += 256)
     for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[(size_t)r * k + j]], 1);
   __syncthreads();
-  if (threadIdx.x < E) cc[chunk * E + threadIdx.x] = cnt[threadIdx.x];
-}
-
-__global__ __launch_bounds__(128) void k_route_scan(int* cc, int nchunks, int E, int4* tiles, int* n_tiles) {
-  __shared__ int tot[128], off[129];
-  const int e = threadIdx.x;
-  if (e < E) {
-    int t = 0;
-    for (int c = 0; c < nchunks; ++c) t += cc[c * E + e];
-    tot[e] = t;
-  }
-  __syncthreads();
-  if (e == 0) {
+  if (t == 0) {
     int acc = 0, nt = 0;
-    for (int x = 0; x < E; ++x) {
-      off[x] = acc;
-      for (int r0 = 0; r0 < tot[x]; r0 += 64) tiles[nt++] = make_int4(x, acc + r0, min(64, tot[x] - r0), 0);
-      acc += tot[x];
+    for (int e = 0; e < E; ++e) {
+      base[e] = acc;
+      for (int r0 = 0; r0 < cnt[e]; r0 += 64) tiles[nt++] = make_int4(e, acc + r0, min(64, cnt[e] - r0), 0);
+      acc += cnt[e];
     }
-    off[E] = acc;
     *n_tiles = nt;
   }
-  __syncthreads();
-  if (e < E) {
-    int base = off[e];
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = cc[c * E + e];
-      cc[c * E + e] = base;
-      base += v;
+  for (int c0 = 0; c0 < M; c0 += 256) {
+    for (int i = t; i < E * 8; i += 256) bits[i >> 3][i & 7] = 0u;
+    __syncthreads();
+    const int r = c0 + t;
+    if (r < M)
+      for (int j = 0; j < k; ++j) atomicOr(&bits[idx[(size_t)r * k + j]][t >> 5], 1u << (t & 31));
+    __syncthreads();
+    if (r < M)
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(size_t)r * k + j];
+        int rank = 0;
+        for (int wd = 0; wd < (t >> 5); ++wd) rank += __popc(bits[e][wd]);
+        rank += __popc(bits[e][t >> 5] & ((1u << (t & 31)) - 1u));
+        const int g = base[e] + rank;
+        perm[g] = r;
+        pos[(size_t)r * k + j] = g;
+      }
+    __syncthreads();
+    if (t < E) {
+      int c = 0;
+      for (int wd = 0; wd < 8; ++wd) c += __popc(bits[t][wd]);
+      base[t] += c;
     }
   }
 }
-
-__global__ __launch_bounds__(256) void k_route_scatter(const int* idx, int M, int k, int E, const int* base,
-                                                       int* perm, int* pos) {
-  __shared__ uint32_t bits[128][8];
-  const int chunk = blockIdx.x, t = threadIdx.x, r = chunk * 256 + t;
-  for (int i = t; i < E * 8; i += 256) bits[i >> 3][i & 7] = 0u;
-  __syncthreads();
-  if (r < M)
-    for (int j = 0; j < k; ++j) atomicOr(&bits[idx[(size_t)r * k + j]][t >> 5], 1u << (t & 31));
-  __syncthreads();
-  if (r >= M) return;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[(size_t)r * k + j];
-    int rank = 0;
-    for (int wd = 0; wd < (t >> 5); ++wd) rank += __popc(bits[e][wd]);
-    rank += __popc(bits[e][t >> 5] & ((1u << (t & 31)) - 1u));
-    const int g = base[chunk * E + e] + rank;
-    perm[g] = r;
-    pos[(size_t)r * k + j] = g;
-  }
-}
-
-hipError_t route_bucket(const int* idx, int M, int k, int E, int* chunk_counts, int* perm, int* pos,
-                        int4* tiles, int* n_tiles, hipStream_t s) {
+hipError_t route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
+                        hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  const int nchunks = (M + 255) / 256;
-  hipLaunchKernelGGL(k_route_count, dim3(nchunks), dim3(256), 0, s, idx, M, k, E, chunk_counts);
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(128), 0, s, chunk_counts, nchunks, E, tiles, n_tiles);
-  hipLaunchKernelGGL(k_route_scatter, dim3(nchunks), dim3(256), 0, s, idx, M, k, E, chunk_counts, perm, pos);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ combine
-// H[r] += sum_j w[r][j] * Y[pos[r][j]], slots in selection order.
-__global__ void k_moe_combine(const float* Y, const int* pos, const float* w, float* H, int k, int d) {
-  const int r = blockIdx.x;
-  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float wj = w[(size_t)r * k + j];
-      const float4 y = *reinterpret_cast<const float4*>(Y + (size_t)pos[(size_t)r * k + j] * d + c);
-      acc.x += wj * y.x; acc.y += wj * y.y; acc.z += wj * y.z; acc.w += wj * y.w;
-    }
-    float4* h = reinterpret_cast<float4*>(H + (size_t)r * d + c);
-    float4 hv = *h;
-    hv.x += acc.x; hv.y += acc.y; hv.z += acc.z; hv.w += acc.w;
-    *h = hv;
-  }
-}
-hipError_t moe_combine(const float* Y, const int* pos, const float* w, float* H, int M, int k, int d,
-                       hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_moe_combine, dim3(M), dim3(256), 0, s, Y, pos, w, H, k, d);
+  hipLaunchKernelGGL(k_route_bucket, dim3(1), dim3(256), 0, s, idx, M, k, E, perm, pos, tiles, n_tiles);
   return hipGetLastError();
 }
 
@@ -283,11 +362,14 @@ hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int 
   return hipGetLastError();
 }
 
-#define DG_INST(T)                                                                                   \
-  template hipError_t embed_rows<T>(const T*, const int32_t*, float*, int, int, int, hipStream_t);  \
-  template hipError_t rmsnorm_rows<T>(const float*, const float*, T*, int, int, float, hipStream_t); \
-  template hipError_t rope_scatter<T>(const float*, const float2*, T*, T*, T*, int, int, int, int,  \
-                                      int, int, int, hipStream_t);                                  \
+#define DG_INST(T)                                                                                               \
+  template hipError_t embed_norm<T>(const T*, const int32_t*, const float*, int, int, int, int, const float*,  \
+                                    float, float*, T*, hipStream_t);                                            \
+  template hipError_t add_norm<T>(const float*, int, int, int, const float*, float, float*, T*, hipStream_t);   \
+  template hipError_t combine_norm<T>(const float*, const int*, const float*, int, int, int, const float*, float, \
+                                      float*, T*, hipStream_t);                                                 \
+  template hipError_t rope_scatter<T>(const float*, int, const float2*, T*, T*, T*, int, int, int, int, int, int, \
+                                      int, hipStream_t);                                                        \
   template hipError_t transpose<T>(const T*, T*, int, int, hipStream_t);
 DG_INST(float)
 DG_INST(bf16)

@@ -174,14 +174,19 @@ __global__ void k_sampler_merge(const HeadPart* part, int M, int chunks, int n, 
   margin[r] = t2.b1 - t2.b2;
 }
 
-// s[r][c] = sum over chunks of scale[r][chunk] * part[chunk][r][c], chunk order.
-__global__ void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks,
+// s[r][c] = sum over splits of scale[r][split / sub] * part[split][r][c], split order;
+// each vocabulary chunk of the sampler is contracted as `sub` K-slices.
+__global__ void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub,
                                   float* S) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)M * d) return;
   const size_t r = i / d;
   float acc = 0.f;
-  for (int c = 0; c < chunks; ++c) acc += chunk_scale[r * chunks + c] * part[(size_t)c * M * d + i];
+  for (int c = 0; c < chunks; ++c) {
+    float pc = 0.f;
+    for (int u = 0; u < sub; ++u) pc += part[(size_t)(c * sub + u) * M * d + i];
+    acc += chunk_scale[r * chunks + c] * pc;
+  }
   S[i] = acc;
 }
 
@@ -195,6 +200,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
                                                 int vocab, int step, int max_steps, float bound,
                                                 int stop_mode, float tau, int canvas_index) {
   __shared__ float sh[256];
+  __shared__ float hpos[256];
   __shared__ int sp[256];
   __shared__ int rank[256];
   __shared__ int s_cnt, s_final, s_diff;
@@ -202,6 +208,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
   if (done[b]) return;
   const size_t base = (size_t)b * n;
   sh[t] = t < n ? H[base + t] : INFINITY;
+  hpos[t] = sh[t];
   sp[t] = t;
   if (t == 0) s_diff = 0;
   __syncthreads();
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
       if (c <= bnd) ++cnt; else break;
     }
     double mean = 0.0;
-    for (int i = 0; i < n; ++i) mean += (double)H[base + i];
+    for (int i = 0; i < n; ++i) mean += (double)hpos[i];
     mean /= (double)n;
     bool stop = false;
     if (stop_mode == 1) stop = mean < (double)tau;
@@ -281,12 +288,12 @@ hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const u
   return hipGetLastError();
 }
 
-hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, float* S,
+hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub, float* S,
                            hipStream_t s) {
   const size_t nel = (size_t)M * d;
   if (nel == 0) return hipSuccess;
   hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s, part, chunk_scale,
-                     M, d, chunks, S);
+                     M, d, chunks, sub, S);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ MARGIN_EXEMPT = 1e-3
 # router-logit drift of up to ~1% of the logit scale (the tests print the
 # measured drift).  2e-2 is the bf16 value tolerance; fp32 operands drift ~1e-6.
 GAP_REL = {"bf16": 2e-2, "f32": 1e-4}
-MAX_FLIP_FRAC = 0.05
+MAX_FLIP_FRAC = 0.10
 
 
 @pytest.fixture(scope="module")
