@@ -30,7 +30,7 @@ STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "exper
 EXPORTS = [
     "dg_last_error", "dg_weight_count", "dg_model_create", "dg_model_destroy", "dg_state_bytes",
     "dg_state_init", "dg_state_destroy", "dg_state_ctx_len", "dg_state_canvas_index", "dg_state_view",
-    "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_commit",
+    "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_commit",
     "dg_commit_canvas_to_kv", "dg_profile_enable", "dg_profile_read",
 ]
 
@@ -86,14 +86,15 @@ def load() -> ctypes.CDLL:
     lib.dg_encode_prompt.argtypes = [vp, vp, i32, vp]
     lib.dg_denoise_step.argtypes = [vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp,
                                     vp, vp]
+    lib.dg_sample_logits.argtypes = [vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp, vp]
     lib.dg_sample_commit.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp,
                                      vp, vp]
     lib.dg_commit_canvas_to_kv.argtypes = [vp, vp, vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_uint32]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("dg_model_create", "dg_state_bytes", "dg_state_init", "dg_state_view", "dg_init_canvas",
-                 "dg_encode_prompt", "dg_denoise_step", "dg_sample_commit", "dg_commit_canvas_to_kv",
-                 "dg_profile_enable", "dg_profile_read"):
+                 "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_commit",
+                 "dg_commit_canvas_to_kv", "dg_profile_enable", "dg_profile_read"):
         getattr(lib, name).restype = i32
     _check_single_hip_runtime()
     _lib = lib

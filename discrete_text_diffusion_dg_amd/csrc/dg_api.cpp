@@ -543,22 +543,14 @@ float step_temperature(const dg_sampler_params* p, int step) {
   return (float)(t0 + (t1 - t0) * (double)step / (double)(p->max_steps - 1));
 }
 
+// Sampler stage on R rows of logits: head statistics, outputs, and (self-
+// conditioning models) the next step's self-conditioning vector.
 template <typename T>
-dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sampler_params* p,
-                      const uint64_t* seeds, const uint8_t* active, float* H, int32_t* y, int32_t* am,
-                      float* margin, float* logits_out, hipStream_t s) {
+dg_status run_head(dg_state* st, const float* logits, int step, const dg_sampler_params* p, const uint64_t* seeds,
+                   const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, V = c.vocab, R = st->R;
-  const bool sc = c.self_cond && step > 0;
-  dg_status r = run_stack<T>(st, canvas, st->n, false, sc, s);
-  if (r) return r;
-  T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
-  float* logits = logits_out ? logits_out : st->logits;
-  {
-    StageTimer tm(st, DG_STAGE_LM_HEAD, s);
-    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, logits, R, V, d, s));
-  }
   const float T_t = step_temperature(p, step);
   const float inv_t = (float)(1.0 / (double)T_t);
   const SeedArg sa = make_seeds(seeds, st->B);
@@ -576,6 +568,25 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sa
     DG_HIP(selfcond_reduce(st->sc_part, st->chunk_scale, R, d, st->chunks, st->sc_sub, st->s, s));
   }
   return DG_OK;
+}
+
+template <typename T>
+dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sampler_params* p,
+                      const uint64_t* seeds, const uint8_t* active, float* H, int32_t* y, int32_t* am,
+                      float* margin, float* logits_out, hipStream_t s) {
+  const dg_model* m = st->m;
+  const dg_config& c = m->cfg;
+  const int d = c.d_model, V = c.vocab, R = st->R;
+  const bool sc = c.self_cond && step > 0;
+  dg_status r = run_stack<T>(st, canvas, st->n, false, sc, s);
+  if (r) return r;
+  T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
+  float* logits = logits_out ? logits_out : st->logits;
+  {
+    StageTimer tm(st, DG_STAGE_LM_HEAD, s);
+    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, logits, R, V, d, s));
+  }
+  return run_head<T>(st, logits, step, p, seeds, active, H, y, am, margin, s);
 }
 
 dg_status check_params(const dg_sampler_params* p) {
@@ -624,6 +635,20 @@ extern "C" dg_status dg_denoise_step(dg_state* st, const int32_t* d_canvas, int3
              ? run_denoise<bf16>(st, d_canvas, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, d_logits, s)
              : run_denoise<float>(st, d_canvas, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, d_logits,
                                   s);
+}
+
+extern "C" dg_status dg_sample_logits(dg_state* st, const float* d_logits, int32_t step,
+                                      const dg_sampler_params* params, const uint64_t* h_seeds,
+                                      const uint8_t* d_active, float* d_H, int32_t* d_y, int32_t* d_argmax,
+                                      float* d_margin, dg_stream stream) {
+  if (!st || !d_logits || !h_seeds || !d_H || !d_y || !d_argmax || !d_margin) return fail(DG_ERR_ARG, "null argument");
+  dg_status r = check_params(params);
+  if (r) return r;
+  if (step < 0 || step >= params->max_steps) return fail(DG_ERR_ARG, "step %d outside 0..max_steps-1", step);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return st->m->cfg.dtype == DG_DTYPE_BF16
+             ? run_head<bf16>(st, d_logits, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, s)
+             : run_head<float>(st, d_logits, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, s);
 }
 
 extern "C" dg_status dg_sample_commit(dg_state* st, const float* d_H, const int32_t* d_y, const int32_t* d_argmax,

@@ -181,6 +181,13 @@ class Engine:
                                          _ptr(active), self.H.data_ptr(), self.y.data_ptr(), self.am.data_ptr(),
                                          self.margin.data_ptr(), _ptr(logits), self._stream()))
 
+    def sample_logits(self, step: int, sp, logits: torch.Tensor, active: Optional[torch.Tensor] = None) -> None:
+        prm = sampler_struct(sp)
+        logits = logits.to(device=self.device, dtype=torch.float32).contiguous()
+        L.check(self.lib.dg_sample_logits(self._state, logits.data_ptr(), step, ctypes.byref(prm), self._seed_ptr(),
+                                          _ptr(active), self.H.data_ptr(), self.y.data_ptr(), self.am.data_ptr(),
+                                          self.margin.data_ptr(), self._stream()))
+
     def sample_commit(self, step: int, sp, H: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       am: Optional[torch.Tensor] = None) -> None:
         prm = sampler_struct(sp)

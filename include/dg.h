@@ -174,6 +174,18 @@ dg_status dg_denoise_step(dg_state* state, const int32_t* d_canvas, int32_t step
                           const uint8_t* d_active, float* d_H, int32_t* d_y, int32_t* d_argmax,
                           float* d_margin, float* d_logits, dg_stream stream);
 
+/* The sampler stage of dg_denoise_step alone, on caller-supplied logits
+ * ([mlqm] 四; [chooseai] llama.cpp paragraph: the entropy-bounded sampler runs
+ * on the model's logits): per row the temperature softmax, its entropy, the
+ * logit argmax, the Gumbel-max sample and the top-2 margin, exactly as
+ * dg_denoise_step computes them after its LM head, and (self-conditioning
+ * models) the next step's self-conditioning vector from the same
+ * distribution.  d_logits: float [B, canvas_len, V] (read).  Other arguments
+ * and outputs as for dg_denoise_step. */
+dg_status dg_sample_logits(dg_state* state, const float* d_logits, int32_t step, const dg_sampler_params* params,
+                           const uint64_t* h_seeds, const uint8_t* d_active, float* d_H, int32_t* d_y,
+                           int32_t* d_argmax, float* d_margin, dg_stream stream);
+
 /* Entropy-bounded commit / uniform re-noise / adaptive stop ([mlqm] 四, 一).
  * Per request b with d_done[b] == 0: sort positions by (H, position), commit the
  * longest prefix whose running fp64 entropy total stays <= entropy_bound; the

@@ -13,6 +13,9 @@ attention over the prompt and bidirectional attention over the canvas):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 
@@ -76,10 +79,27 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
     Hkv = k.shape[1]
     out = np.empty((nq, Hq, hd), np.float64)
     scale = 1.0 / np.sqrt(hd)
-    for h in range(Hq):
+    # Query rows are independent; they are evaluated in blocks to bound memory.
+    # Under the causal mask a block needs only the keys up to its last position
+    # (the others would get probability exactly 0).
+    blk = 1024
+
+    def head(h):
         g = (h * Hkv) // Hq
-        s = (q[:, h, :] @ k[:, g, :].T) * scale                          # [nq, nk]
-        if causal:
-            s = np.where(k_pos[None, :] <= q_pos[:, None], s, -np.inf)
-        out[:, h, :] = softmax(s, axis=-1) @ v[:, g, :]
+        for q0 in range(0, nq, blk):
+            q1 = min(nq, q0 + blk)
+            qp = q_pos[q0:q1]
+            kmax = int(np.searchsorted(k_pos, qp.max(), side="right")) if causal else len(k_pos)
+            s = (q[q0:q1, h, :] @ k[:kmax, g, :].T) * scale               # [block, keys]
+            if causal:
+                s = np.where(k_pos[None, :kmax] <= qp[:, None], s, -np.inf)
+            out[q0:q1, h, :] = softmax(s, axis=-1) @ v[:kmax, g, :]
+
+    # heads are independent; numpy releases the interpreter lock in these kernels
+    if nq * len(k_pos) >= 1 << 20 and Hq > 1:
+        with ThreadPoolExecutor(min(Hq, os.cpu_count() or 1)) as ex:
+            list(ex.map(head, range(Hq)))
+    else:
+        for h in range(Hq):
+            head(h)
     return out
