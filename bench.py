@@ -212,18 +212,25 @@ def main():
             t = 0
         state["t"] = t
 
-    # warm-up, with every stage timed to find the dominant one
+    # warm-up; every stage is timed after the first step (first launches pay
+    # one-off costs) to find the dominant one
+    n_first = 1 if a.warmup > 1 else 0
+    for _ in range(n_first):
+        one_step()
     eng.profile(["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
                  "lm_head", "sampler", "selfcond", "commit"])
-    for _ in range(a.warmup):
+    for _ in range(a.warmup - n_first):
         one_step()
     torch.cuda.synchronize()
     prof = eng.profile_read()
     ctx_w = eng.ctx_len
     dominant = max(prof, key=lambda k: prof[k][0]) if prof else "expert_up"
     log("[bench] warm-up stage ms: " + ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in prof.items()))
-    routed = eng.route_view(B * n)[-1].cpu().numpy()
-    n_act = int(np.unique(routed).size)
+    # experts that receive rows, averaged over the layers (one expert launch per layer)
+    routed = eng.route_view(B * n).cpu().numpy()
+    act_per_layer = [int(np.unique(r).size) for r in routed]
+    n_act = float(np.mean(act_per_layer))
+    log(f"[bench] active experts per layer: {act_per_layer}")
 
     # timed region: exactly K steps, only the dominant stage carries events
     eng.profile([dominant])
@@ -265,8 +272,9 @@ def main():
                    "self_cond": mc.self_cond, "parallelism": "none (1 GPU)"},
         "steps_per_s": round(a.steps / (ms / 1e3), 2),
         "encode_ms": round(encode_ms, 3),
-        "stage_ms_warmup": {k: round(v[0] / max(a.warmup, 1), 4) for k, v in prof.items()},
+        "stage_ms_warmup": {k: round(v[0] / max(a.warmup - n_first, 1), 4) for k, v in prof.items()},
         "roofline": rl,
+        "active_experts_per_layer": act_per_layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

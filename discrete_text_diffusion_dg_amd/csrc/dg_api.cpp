@@ -77,7 +77,7 @@ struct dg_state {
   void* kc; void* vc; float2* rope; float* s; int32_t* prev_am;
   // workspace
   float* h; void* xn; float* part; size_t part_floats; void* q; void* attn; float* attn_po; float* attn_pml;
-  float* rlog; int* ridx; float* rw; int* perm; int* pos; int4* tiles;
+  float* rlog; int* ridx; float* rw; int* perm; int* pos; int4* tiles; int* rcnt;
   int* n_tiles; void* act; float* y; float* logits; HeadPart* hp; float* chunk_scale;
   void* ptilde; float* sc_part; int sc_sub; int32_t* tok;
   size_t total_bytes;
@@ -242,7 +242,7 @@ struct Layout {
 };
 
 struct Offsets {
-  size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos,
+  size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos, rcnt,
       tiles, n_tiles, act, y, logits, hp, chunk_scale, ptilde, sc_part, tok, total;
   size_t part_floats;
   int chunks, clen, splits, cap_tiles, sc_sub;
@@ -292,6 +292,7 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.pos = L.take((size_t)R * k * 4);
   o.tiles = L.take((size_t)o.cap_tiles * sizeof(int4));
   o.n_tiles = L.take(4);
+  o.rcnt = L.take((size_t)E * ((R + 15) / 16) * 4);     // router count table
   o.act = L.take((size_t)R * k * F * es);
   o.y = L.take((size_t)R * k * d * 4);
   o.logits = L.take((size_t)R * V * 4);
@@ -339,6 +340,7 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->rw = reinterpret_cast<float*>(b + o.rw);
   s->perm = reinterpret_cast<int*>(b + o.perm); s->pos = reinterpret_cast<int*>(b + o.pos);
   s->tiles = reinterpret_cast<int4*>(b + o.tiles); s->n_tiles = reinterpret_cast<int*>(b + o.n_tiles);
+  s->rcnt = reinterpret_cast<int*>(b + o.rcnt);
   s->act = b + o.act; s->y = reinterpret_cast<float*>(b + o.y); s->logits = reinterpret_cast<float*>(b + o.logits);
   s->hp = reinterpret_cast<HeadPart*>(b + o.hp); s->chunk_scale = reinterpret_cast<float*>(b + o.chunk_scale);
   s->ptilde = m->cfg.self_cond ? b + o.ptilde : nullptr;
@@ -455,7 +457,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   int splits = attention_splits(st->B, nq, Hq, Hkv, keys);
   if (splits > st->attn_splits_max) splits = st->attn_splits_max;
   const int cap = expert_tile_capacity(M, k, E);
-  const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd), p_r = plan(st, M, E, d);
+  const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd);
   const bool stream_ok = m->pack_buf != nullptr;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
@@ -488,9 +490,8 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       StageTimer tm(st, DG_STAGE_ROUTER, s);
       float* rlog = st->rlog + (size_t)l * st->R * E;
       int* ridx = st->ridx + (size_t)l * st->R * k;
-      DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.w_router), d, st->part, M, E, d, p_r, s));
-      DG_HIP(router_topk(st->part, p_r.splits, M, E, k, rlog, ridx, st->rw, s));
-      DG_HIP(route_bucket(ridx, M, k, E, st->perm, st->pos, st->tiles, st->n_tiles, s));
+      DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
+                       st->tiles, st->n_tiles, st->rcnt, s));
     }
     // weight streaming while experts see at most ~64 routed rows on average
     // (the batch-1 shapes); the LDS-tiled engine once they see many

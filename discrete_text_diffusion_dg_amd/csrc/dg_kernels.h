@@ -100,10 +100,11 @@ template <typename T>
 hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
                         int Hkv, int hd, int max_ctx, int ctx, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
-hipError_t router_topk(const float* part, int S, int M, int E, int k, float* rlog, int* idx, float* w,
-                       hipStream_t s);
-hipError_t route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
-                        hipStream_t s);
+// Router of one layer: logits, top-k + softmax weights, and the expert-sorted
+// order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / 16) ints.
+template <typename T>
+hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
+                  int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
 hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,

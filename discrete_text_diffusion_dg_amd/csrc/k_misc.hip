@@ -210,121 +210,215 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
 }
 
 // ------------------------------------------------------------------ router
-// One wave per row: the router logits (sum of split partials) sit two per
-// lane; k rounds of a wave arg-max (ties to the lower expert id) pick the
-// experts in descending order, then softmax over the selected logits.
-__global__ __launch_bounds__(256) void k_router_topk(const float* part, int S, int M, int E, int k, float* rlog,
-                                                     int* idx, float* w) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= M) return;
-  float v[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = lane + 64 * h;
-    float x = -INFINITY;
-    if (e < E) {
-      x = 0.f;
-      for (int s = 0; s < S; ++s) x += part[((size_t)s * M + r) * E + e];
-      rlog[(size_t)r * E + e] = x;
-    }
-    v[h] = x;
-  }
-  bool used0 = lane >= E, used1 = lane + 64 >= E;
-  float sel[8];
-  int sid[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    float bv;
-    int bi;
-    if (!used0 && (used1 || v[0] >= v[1])) { bv = v[0]; bi = lane; }
-    else if (!used1) { bv = v[1]; bi = lane + 64; }
-    else { bv = -INFINITY; bi = 0x7fffffff; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (bi == lane) used0 = true;
-    if (bi == lane + 64) used1 = true;
-    sel[j] = bv;
-    sid[j] = bi;
-  }
-  if (lane == 0) {
-    const float mx = sel[0];   // selection order is descending, so slot 0 holds the max
-    float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) if (j < k) { sel[j] = expf(sel[j] - mx); sum += sel[j]; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) {
-        idx[(size_t)r * k + j] = sid[j];
-        w[(size_t)r * k + j] = sel[j] / sum;
-      }
-  }
+// Two launches per layer, no atomics.  k_router: a workgroup owns 16 rows --
+//  1. their router logits on MFMA, the four waves splitting K and adding their
+//     partial sums through LDS in a fixed order;
+//  2. per row, the top k logits by rank -- the number of logits beating one,
+//     ties going to the lower expert id -- then softmax over the selected;
+//  3. per expert, the count of the block's (row, slot) entries -> cnt[e][blk],
+//     and per entry its rank among the block's entries of that expert, in
+//     (row, slot) order -> pos.
+// k_route_finish (one workgroup) turns the count table into per-block
+// exclusive prefixes (per expert, in place), the expert totals into offsets,
+// writes the 64-row tile list, and the final position of every entry in the
+// expert-sorted order, offset + block prefix + rank, into pos and perm: rows
+// of an expert stay in ascending row order.
+template <typename T>
+__device__ __forceinline__ void router_frag(Frag<T>& f, const T* p);
+template <>
+__device__ __forceinline__ void router_frag(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const uint4*>(p);
 }
-hipError_t router_topk(const float* part, int S, int M, int E, int k, float* rlog, int* idx, float* w,
-                       hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, part, S, M, E, k, rlog, idx, w);
-  return hipGetLastError();
+template <>
+__device__ __forceinline__ void router_frag(Frag<float>& f, const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
-// ------------------------------------------------------------------ bucketing
-// One workgroup: per-expert counts, the 64-row tile list, then a stable
-// scatter of (row, slot) entries by expert, rows in chunks of 256 whose ranks
-// within an expert come from an LDS bitmask.
-__global__ __launch_bounds__(256) void k_route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos,
-                                                      int4* tiles, int* n_tiles) {
-  __shared__ int cnt[128], base[128];
-  __shared__ uint32_t bits[128][8];
-  const int t = threadIdx.x;
-  if (t < 128) cnt[t] = 0;
+// NCB = ceil(E / 16) column blocks of logits (a template parameter, so every
+// operand load is unconditional).
+template <typename T, int NCB>
+__global__ __launch_bounds__(256) void k_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog,
+                                                int* idx, float* w, int* pos, int* cnt) {
+  __shared__ float red[3][NCB * 4][64];
+  __shared__ float lg[16][129];
+  __shared__ int sel_e[16][8];
+  __shared__ float sel_v[16][8];
+  __shared__ int ent_e[16 * 8];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g4 = lane >> 4, c16 = lane & 15;
+  const int r0 = blockIdx.x * 16;
+  const int KS = d / 32, ks0 = wv * KS / 4, ks1 = (wv + 1) * KS / 4;
+  const T* ap = xn + (size_t)min(r0 + c16, M - 1) * d + g4 * 8;
+  const T* bp[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) bp[cb] = wr + (size_t)min(cb * 16 + c16, E - 1) * d + g4 * 8;
+  f32x4_t acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // d is a multiple of 256, so each wave's K range (a quarter) is a multiple
+  // of 2 steps: pairs of steps, the loads of a pair issued together
+  for (int ks = ks0; ks < ks1; ks += 2) {
+    Frag<T> a[2], b[2][NCB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      router_frag(a[u], ap + (ks + u) * 32);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) router_frag(b[u][cb], bp[cb] + (ks + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) mma16x16x32(acc[cb], a[u], b[u][cb]);
+  }
+  if (wv > 0)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wv - 1][cb * 4 + i][lane] = acc[cb][i];
   __syncthreads();
-  for (int r = t; r < M; r += 256)
-    for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[(size_t)r * k + j]], 1);
+  if (wv == 0)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lg[g4 * 4 + i][cb * 16 + c16] =
+              ((acc[cb][i] + red[0][cb * 4 + i][lane]) + red[1][cb * 4 + i][lane]) + red[2][cb * 4 + i][lane];
+  __syncthreads();
+
+  // top-k by rank: the rank of expert e in its row is the number of logits that
+  // beat it (greater, or equal with a lower id); ranks 0..k-1 are the slots
+  const int nrow = min(16, M - r0);
+  for (int pr = t; pr < nrow * E; pr += 256) {
+    const int rl = pr / E, e = pr - rl * E;
+    const float v = lg[rl][e];
+    int rank = 0;
+    for (int x = 0; x < E; ++x) {
+      const float o = lg[rl][x];
+      rank += (o > v) || (o == v && x < e);
+    }
+    rlog[(size_t)(r0 + rl) * E + e] = v;
+    if (rank < k) {
+      sel_e[rl][rank] = e;
+      sel_v[rl][rank] = v;
+    }
+  }
+  __syncthreads();
+  // softmax over the selected logits, slots summed in order; entry q = (row q / k, slot q % k)
+  const int nent = nrow * k;
+  int* se = &ent_e[0];
+  if (t < nent) {
+    const int rl = t / k, j = t - rl * k;
+    const float mx = sel_v[rl][0];
+    float sum = 0.f;
+    for (int u = 0; u < k; ++u) sum += expf(sel_v[rl][u] - mx);
+    const int e = sel_e[rl][j];
+    idx[(size_t)r0 * k + t] = e;
+    w[(size_t)r0 * k + t] = expf(sel_v[rl][j] - mx) / sum;
+    se[t] = e;
+  }
+  __syncthreads();
+  // rank of each entry among the block's entries of its expert, in entry order
+  if (t < nent) {
+    const int e = se[t];
+    int rank = 0;
+    for (int u = 0; u < t; ++u) rank += se[u] == e;
+    pos[(size_t)r0 * k + t] = rank;
+  }
+  const int nblk = gridDim.x;
+  for (int e = t; e < E; e += 256) {
+    int c = 0;
+    for (int u = 0; u < nent; ++u) c += se[u] == e;
+    cnt[(size_t)e * nblk + blockIdx.x] = c;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int k, int E, int nblk, int* cnt,
+                                                      int* perm, int* pos, int4* tiles, int* n_tiles) {
+  __shared__ int seg[256];
+  __shared__ int offs[128];
+  const int t = threadIdx.x;
+  int ep = 1;
+  while (ep < E) ep <<= 1;
+  const int tpe = 256 / ep;                       // threads per expert (>= 2)
+  const int e = t / tpe, sg = t % tpe;
+  const int per = (nblk + tpe - 1) / tpe, b0 = min(nblk, sg * per), b1 = min(nblk, b0 + per);
+  int* row = cnt + (size_t)(e < E ? e : 0) * nblk;
+  int ssum = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) ssum += row[b];
+  seg[t] = ssum;
+  __syncthreads();
+  if (e < E) {
+    int run = 0;
+    for (int j = 0; j < sg; ++j) run += seg[e * tpe + j];
+    for (int b = b0; b < b1; ++b) {
+      const int c = row[b];
+      row[b] = run;
+      run += c;
+    }
+    if (sg == 0) {
+      int tot = 0;
+      for (int j = 0; j < tpe; ++j) tot += seg[e * tpe + j];
+      offs[e] = tot;
+    }
+  }
   __syncthreads();
   if (t == 0) {
-    int acc = 0, nt = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = acc;
-      for (int r0 = 0; r0 < cnt[e]; r0 += 64) tiles[nt++] = make_int4(e, acc + r0, min(64, cnt[e] - r0), 0);
-      acc += cnt[e];
+    int acc_rows = 0, nt = 0;
+    for (int x = 0; x < E; ++x) {
+      const int c = offs[x];
+      offs[x] = acc_rows;
+      for (int q0 = 0; q0 < c; q0 += 64) tiles[nt++] = make_int4(x, acc_rows + q0, min(64, c - q0), 0);
+      acc_rows += c;
     }
     *n_tiles = nt;
   }
-  for (int c0 = 0; c0 < M; c0 += 256) {
-    for (int i = t; i < E * 8; i += 256) bits[i >> 3][i & 7] = 0u;
-    __syncthreads();
-    const int r = c0 + t;
-    if (r < M)
-      for (int j = 0; j < k; ++j) atomicOr(&bits[idx[(size_t)r * k + j]][t >> 5], 1u << (t & 31));
-    __syncthreads();
-    if (r < M)
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[(size_t)r * k + j];
-        int rank = 0;
-        for (int wd = 0; wd < (t >> 5); ++wd) rank += __popc(bits[e][wd]);
-        rank += __popc(bits[e][t >> 5] & ((1u << (t & 31)) - 1u));
-        const int g = base[e] + rank;
-        perm[g] = r;
-        pos[(size_t)r * k + j] = g;
+  __syncthreads();
+  const int MK = M * k;
+  for (int i0 = t; i0 < MK; i0 += 4 * 256) {     // four independent entries in flight per thread
+    int ex[4], rk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      ex[u] = i < MK ? idx[i] : 0;
+      rk[u] = i < MK ? pos[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      if (i < MK) {
+        const int p = offs[ex[u]] + cnt[(size_t)ex[u] * nblk + i / (16 * k)] + rk[u];
+        pos[i] = p;
+        perm[p] = i / k;
       }
-    __syncthreads();
-    if (t < E) {
-      int c = 0;
-      for (int wd = 0; wd < 8; ++wd) c += __popc(bits[t][wd]);
-      base[t] += c;
     }
   }
 }
-hipError_t route_bucket(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
-                        hipStream_t s) {
+
+template <typename T>
+hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
+                  int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route_bucket, dim3(1), dim3(256), 0, s, idx, M, k, E, perm, pos, tiles, n_tiles);
+  const int nblk = (M + 15) / 16;
+  const dim3 grid(nblk), block(256);
+  switch ((E + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_router<T, 1>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
+    case 2: hipLaunchKernelGGL((k_router<T, 2>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
+    case 3: case 4:
+      hipLaunchKernelGGL((k_router<T, 4>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
+    default:
+      hipLaunchKernelGGL((k_router<T, 8>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(256), 0, s, idx, M, k, E, nblk, cnt, perm, pos, tiles, n_tiles);
   return hipGetLastError();
 }
+template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,
+                                  int4*, int*, int*, hipStream_t);
+template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, float*, int*, float*, int*, int*,
+                                 int4*, int*, int*, hipStream_t);
 
 // ------------------------------------------------------------------ transpose
 template <typename T>
