@@ -72,7 +72,8 @@ struct dg_state {
   int B, max_ctx, n, R;  // R = B * n rows per pass
   int ctx = 0, canvas_index = 0;
   int chunks, clen, attn_splits_max, cap_tiles;
-  size_t kv_layer_elems;  // B * Hkv * max_ctx * hd
+  int ctx_pad;            // max_ctx rounded up to the 64-key attention tile: K/V row stride
+  size_t kv_layer_elems;  // B * Hkv * ctx_pad * hd
   // persistent
   void* kc; void* vc; float2* rope; float* s; int32_t* prev_am;
   // workspace
@@ -119,7 +120,8 @@ static dg_status check_config(const dg_config* c) {
   if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
     return fail(DG_ERR_UNSUPPORTED, "top_k must be in 1..min(8, n_experts)");
   if (c->ffn_hidden < 64 || c->ffn_hidden % 64) return fail(DG_ERR_UNSUPPORTED, "ffn_hidden must be a multiple of 64");
-  if (c->vocab < 64 || c->vocab % 64) return fail(DG_ERR_UNSUPPORTED, "vocab must be a positive multiple of 64");
+  if (c->vocab < 64 || c->vocab % 64 || c->vocab > 262144)
+    return fail(DG_ERR_UNSUPPORTED, "vocab must be a multiple of 64 in 64..262144");
   if (c->canvas_len < 1 || c->canvas_len > 256) return fail(DG_ERR_UNSUPPORTED, "canvas_len must be in 1..256");
   if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16) return fail(DG_ERR_ARG, "dtype must be F32 or BF16");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(DG_ERR_ARG, "rope_theta > 0 and rms_eps >= 0 required");
@@ -270,7 +272,8 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.splits = 16;
   o.cap_tiles = expert_tile_capacity(R, k, E);
   Layout L;
-  const size_t kv = (size_t)c.n_layers * B * Hkv * max_ctx * hd * es;
+  const int ctx_pad = (max_ctx + 63) / 64 * 64;
+  const size_t kv = (size_t)c.n_layers * B * Hkv * ctx_pad * hd * es;
   o.kc = L.take(kv);
   o.vc = L.take(kv);
   o.rope = L.take((size_t)max_ctx * (hd / 2) * sizeof(float2));
@@ -329,7 +332,8 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   char* b = static_cast<char*>(buf);
   s->m = m; s->B = batch; s->max_ctx = max_ctx; s->n = m->cfg.canvas_len; s->R = batch * s->n;
   s->chunks = o.chunks; s->clen = o.clen; s->attn_splits_max = o.splits; s->cap_tiles = o.cap_tiles;
-  s->kv_layer_elems = (size_t)batch * m->cfg.n_kv_heads * max_ctx * m->cfg.head_dim;
+  s->ctx_pad = (max_ctx + 63) / 64 * 64;
+  s->kv_layer_elems = (size_t)batch * m->cfg.n_kv_heads * s->ctx_pad * m->cfg.head_dim;
   s->kc = b + o.kc; s->vc = b + o.vc; s->rope = reinterpret_cast<float2*>(b + o.rope);
   s->s = reinterpret_cast<float*>(b + o.s); s->prev_am = reinterpret_cast<int32_t*>(b + o.prev_am);
   s->h = reinterpret_cast<float*>(b + o.h); s->xn = b + o.xn;
@@ -350,6 +354,9 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   hipError_t e = rope_table(s->rope, max_ctx, m->cfg.head_dim, m->cfg.rope_theta, 0);
   if (e == hipSuccess) e = hipMemsetAsync(s->s, 0, (size_t)s->R * m->cfg.d_model * 4, 0);
   if (e == hipSuccess) e = hipMemsetAsync(s->prev_am, 0, (size_t)s->R * 4, 0);
+  // attention tiles read whole 64-key rows of V^T past the context: keep them finite
+  if (e == hipSuccess) e = hipMemsetAsync(s->kc, 0, s->kv_layer_elems * m->cfg.n_layers * m->esz, 0);
+  if (e == hipSuccess) e = hipMemsetAsync(s->vc, 0, s->kv_layer_elems * m->cfg.n_layers * m->esz, 0);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) { delete s; return fail(DG_ERR_HIP, "state init: %s", hipGetErrorString(e)); }
   *out = s;
@@ -467,13 +474,13 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       StageTimer tm(st, DG_STAGE_QKV, s);
       DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, s));
       DG_HIP(rope_scatter<T>(st->part, p_qkv.splits, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv,
-                             hd, st->max_ctx, st->ctx, s));
+                             hd, st->ctx_pad, st->ctx, s));
     }
     {
       StageTimer tm(st, DG_STAGE_ATTN, s);
       AttnArgs a;
       a.q = st->q; a.kc = kc; a.vc = vc; a.out = st->attn; a.part_o = st->attn_po; a.part_ml = st->attn_pml;
-      a.B = st->B; a.nq = nq; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.max_ctx = st->max_ctx; a.ctx = st->ctx;
+      a.B = st->B; a.nq = nq; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.kv_stride = st->ctx_pad; a.ctx = st->ctx;
       a.causal = causal ? 1 : 0; a.splits = splits; a.scale = (float)(1.0 / std::sqrt((double)hd));
       DG_HIP(attention<T>(a, s));
     }

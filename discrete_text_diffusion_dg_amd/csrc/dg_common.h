@@ -12,16 +12,19 @@ struct bf16 {
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round to nearest, ties to even: the gfx950 packed converter (v_cvt_pk_bf16_f32,
+// rounding per the default mode, nearest-even), two values per instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.f); }
 
 template <typename T> struct Num;
 template <> struct Num<float> {
@@ -40,10 +43,10 @@ template <> struct Num<bf16> {
 // Pack 8 fp32 values into 16 bytes (bf16) or 32 bytes (fp32) of operand data.
 __device__ __forceinline__ uint4 pack8_bf16(const float* v) {
   uint4 r;
-  r.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-  r.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-  r.z = (uint32_t)f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
-  r.w = (uint32_t)f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+  r.x = f32x2_to_bf16x2(v[0], v[1]);
+  r.y = f32x2_to_bf16x2(v[2], v[3]);
+  r.z = f32x2_to_bf16x2(v[4], v[5]);
+  r.w = f32x2_to_bf16x2(v[6], v[7]);
   return r;
 }
 
@@ -82,6 +85,9 @@ __device__ __forceinline__ void lds_frag(Frag<float>& f, const float* p) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
+// e^x through the hardware base-2 exponential (about 1 ulp; x <= 0 here).
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -101,10 +107,9 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t a = c.x, b = c.z;
-    const uint32_t hi0 = __umulhi(0xD2511F53u, a), lo0 = 0xD2511F53u * a;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, b), lo1 = 0xCD9E8D57u * b;
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    // each 32x32 -> 64-bit product is one multiply-add on the vector unit
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

@@ -70,12 +70,12 @@ hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, i
 // ---- attention (k_attn.hip)
 struct AttnArgs {
   const void* q;        // [B*nq, Hq*hd] operand type, RoPE applied
-  const void* kc;       // K cache of this layer: [B][Hkv][max_ctx][hd]
-  const void* vc;       // V cache of this layer
+  const void* kc;       // K cache of this layer: [B][Hkv][kv_stride][hd]
+  const void* vc;       // V cache of this layer, transposed: [B][Hkv][hd][kv_stride]
   void* out;            // [B*nq, Hq*hd] operand type
   float* part_o;        // split partials [splits][B*nq*Hq][hd] (fp32, unnormalised)
   float* part_ml;       // split partials [splits][B*nq*Hq][2] (running max, sum)
-  int B, nq, Hq, Hkv, hd, max_ctx;
+  int B, nq, Hq, Hkv, hd, kv_stride;   // kv_stride: context capacity rounded up to 64
   int ctx;              // keys 0..ctx+nq-1 (the new rows sit at ctx..ctx+nq-1)
   int causal;
   int splits;
@@ -96,9 +96,10 @@ template <typename T>
 hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
                         float eps, float* H, T* xn, hipStream_t s);
 // RoPE on q and k of the fused projection (sum of S partials), q -> Q buffer, k and v -> cache at ctx + i
+// (K rows [B][Hkv][stride][hd], V transposed [B][Hkv][hd][stride])
 template <typename T>
 hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
-                        int Hkv, int hd, int max_ctx, int ctx, hipStream_t s);
+                        int Hkv, int hd, int stride, int ctx, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
 // Router of one layer: logits, top-k + softmax weights, and the expert-sorted
 // order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / 16) ints.

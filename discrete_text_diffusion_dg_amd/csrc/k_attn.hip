@@ -6,20 +6,42 @@
 // attention over the 256-token canvas).  New rows' keys and values are already
 // in the cache at ctx..ctx+nq-1, so one loop covers keys 0..ctx+nq-1.
 //
-// Layout: a workgroup owns 64 query rows of one (request, kv head); the rows
-// are the (query head in the group, position) pairs, head-major, so all query
-// heads sharing a kv head reuse one K/V tile in LDS.  Each wave owns 16 rows.
-// Per 64-key tile: S^T = K Q^T on MFMA (keys on the M side, so each lane holds
-// 16 scores of a single query), online softmax in registers, then
-// O^T += V^T P on MFMA with V staged transposed in LDS; the accumulator layout
-// again gives each lane one query, so rescaling needs no lane exchange.
-// Long key ranges are split across workgroups; partial (O, max, sum) are merged
-// in a fixed order by a second kernel.
+// Cache layout: K rows [key][d], V transposed [d][key] (row stride: the context
+// capacity rounded up to the 64-key tile).  Query rows of a (request, kv head)
+// are the (query head in the group, position) pairs, head-major, so every
+// query head sharing a kv head reads the same K/V.  Per 64-key tile:
+// S^T = K Q^T on MFMA (keys on the M side, each lane holding 16 scores of one
+// query), online softmax in registers, O^T += V^T P on MFMA (again one query
+// per lane, so rescaling needs no lane exchange).  Both MFMA operands come as
+// fragments: K rows give the A operand of S^T directly, V^T rows that of O^T.
+//
+// Two launch shapes:
+//  * spread (few query blocks, the batch-1 shapes): a workgroup owns 16 * QB
+//    query rows; its NW waves take the key tiles round-robin, streaming K and
+//    V^T fragments straight from memory one tile ahead, and merge their
+//    partial (O, max, sum) through LDS in wave order at the end -- many short
+//    chains instead of a few long ones;
+//  * tiled (many query blocks): a workgroup owns 64 query rows, one wave per
+//    16, and the four waves share each K / V^T tile staged in LDS, prefetched
+//    kPre tiles ahead.
+// Long key ranges are further split across workgroups; partial (O, max, sum)
+// are merged in a fixed order by a second kernel.
 #include "dg_kernels.h"
 
 namespace dg {
 
 namespace {
+
+constexpr int kPre = 2;                                // K/V tiles in flight ahead of the MFMAs
+
+// Key order inside a 64-key tile.  Row r of score block kb (S^T = K Q^T, 16
+// keys on the M side) holds key (kb / 2) * 32 + (r / 4) * 8 + (kb % 2) * 4 + r % 4,
+// so the accumulator rows a lane group g owns (g*4 .. g*4+3 of blocks 2s and
+// 2s+1) are the 8 consecutive keys s*32 + g*8 .. +7 -- exactly the k-elements
+// that group supplies to O^T += V^T P for that 32-key step.  The V^T fragment
+// is then one contiguous 16-byte read; the sum over keys does not depend on
+// their order.
+__device__ __forceinline__ int tile_key(int kb, int r) { return (kb >> 1) * 32 + (r >> 2) * 8 + (kb & 1) * 4 + (r & 3); }
 
 template <typename T, int HD>
 struct AttnShape {
@@ -45,6 +67,21 @@ __device__ __forceinline__ void set_p(Frag<float>& f, const float* p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) f.v[j] = p[j];
 }
+// P operand of O^T += V^T P.  bf16: head = rnd(p), remainder = rnd(p - head)
+// (two MFMAs, ~16 significant bits); a pair of values per conversion.
+__device__ __forceinline__ void split_p(Frag<bf16> (&f)[2], float* r) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[j] = f32x2_to_bf16x2(r[2 * j], r[2 * j + 1]);
+    r[2 * j] -= __uint_as_float(w[j] << 16);
+    r[2 * j + 1] -= __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+  f[0].v = make_uint4(w[0], w[1], w[2], w[3]);
+  f[1].v = make_uint4(f32x2_to_bf16x2(r[0], r[1]), f32x2_to_bf16x2(r[2], r[3]), f32x2_to_bf16x2(r[4], r[5]),
+                      f32x2_to_bf16x2(r[6], r[7]));
+}
+__device__ __forceinline__ void split_p(Frag<float> (&f)[1], float* r) { set_p(f[0], r); }
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v) {
 #pragma unroll
@@ -52,7 +89,7 @@ __device__ __forceinline__ void store4(T* dst, const float* v) {
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_tiled(AttnArgs a) {
   using S = AttnShape<T, HD>;
   __shared__ __attribute__((aligned(16))) char smem[S::kSmem];
   T* sK = reinterpret_cast<T*>(smem);
@@ -100,8 +137,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     }
   }
 
-  const T* Kc = reinterpret_cast<const T*>(a.kc) + ((size_t)b * a.Hkv + kvh) * a.max_ctx * HD;
-  const T* Vc = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * a.max_ctx * HD;
+  const T* Kc = reinterpret_cast<const T*>(a.kc) + ((size_t)b * a.Hkv + kvh) * a.kv_stride * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * HD * a.kv_stride;
 
   f32x4_t o[HD / 16];
 #pragma unroll
@@ -109,23 +146,47 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CH_PER_KEY = HD / EPC;                  // 16-byte chunks per key row
-  constexpr int CHUNKS = S::KT * CH_PER_KEY;
-
-  for (int k0 = kbeg; k0 < kend; k0 += S::KT) {
-    // stage K [key][d] and V^T [d][key]; keys past kend are zero
-    for (int c = tid; c < CHUNKS; c += 256) {
-      const int key = c / CH_PER_KEY, dc = (c % CH_PER_KEY) * EPC;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (k0 + key < kend) {
-        kv = *reinterpret_cast<const uint4*>(Kc + (size_t)(k0 + key) * HD + dc);
-        vv = *reinterpret_cast<const uint4*>(Vc + (size_t)(k0 + key) * HD + dc);
-      }
-      *reinterpret_cast<uint4*>(sK + key * S::LDK + dc) = kv;
-      const T* ve = reinterpret_cast<const T*>(&vv);
+  constexpr int CH_PER_KEY = HD / EPC;                  // 16-byte chunks per K row
+  constexpr int KCH = S::KT * CH_PER_KEY / 256;         // K chunks per thread per tile
+  constexpr int VCH = HD * (S::KT / EPC) / 256;         // V^T chunks per thread per tile
+  static_assert(KCH >= 1 && VCH >= 1, "tile shape");
+  const int ntiles = kend > kbeg ? (kend - kbeg + S::KT - 1) / S::KT : 0;
+  uint4 kr0[KCH], vr0[VCH], kr1[KCH], vr1[VCH];     // two register slots (tiles t and t + 1)
+  auto gload = [&](uint4 (&kr)[KCH], uint4 (&vr)[VCH], int t) __attribute__((always_inline)) {
+    const int k0 = kbeg + min(t, ntiles - 1) * S::KT;       // past the end: reload the last tile
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) sVt[(dc + j) * S::LDV + key] = ve[j];
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, key = min(k0 + c / CH_PER_KEY, kend - 1);
+      kr[i] = *reinterpret_cast<const uint4*>(Kc + (size_t)key * HD + (c % CH_PER_KEY) * EPC);
     }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {        // V^T rows are padded to whole tiles (finite past the context)
+      const int c = tid + 256 * i, d = c / (S::KT / EPC), kc = (c % (S::KT / EPC)) * EPC;
+      vr[i] = *reinterpret_cast<const uint4*>(Vt + (size_t)d * a.kv_stride + k0 + kc);
+    }
+  };
+  auto sstore = [&](const uint4 (&kr)[KCH], const uint4 (&vr)[VCH]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(sK + (c / CH_PER_KEY) * S::LDK + (c % CH_PER_KEY) * EPC) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(sVt + (c / (S::KT / EPC)) * S::LDV + (c % (S::KT / EPC)) * EPC) = vr[i];
+    }
+  };
+  if (ntiles > 0) {
+    gload(kr0, vr0, 0);
+    gload(kr1, vr1, 1);
+  }
+
+  // one tile: store the slot holding tile t, refill it with tile t + 2
+  auto tile = [&](uint4 (&kr)[KCH], uint4 (&vr)[VCH], int t) __attribute__((always_inline)) {
+    const int k0 = kbeg + t * S::KT;
+    sstore(kr, vr);
+    gload(kr, vr, t + kPre);
     __syncthreads();
 
     // scores S^T[key][query] for the 64 keys of the tile
@@ -136,7 +197,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
 #pragma unroll
       for (int s = 0; s < HD / 32; ++s) {
         Frag<T> kf;
-        lds_frag(kf, sK + (kb * 16 + q16) * S::LDK + s * 32 + g4 * 8);
+        lds_frag(kf, sK + tile_key(kb, q16) * S::LDK + s * 32 + g4 * 8);
         mma16x16x32(sc[kb], kf, qf[s]);
       }
     }
@@ -146,7 +207,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kpos = k0 + kb * 16 + g4 * 4 + i;
+        const int kpos = k0 + tile_key(kb, g4 * 4 + i);
         float v = sc[kb][i] * a.scale;
         if (kpos >= kend || (a.causal && kpos > qpos)) v = -INFINITY;
         p[kb * 4 + i] = v;
@@ -155,11 +216,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run - m_new);
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float e = (p[j] == -INFINITY) ? 0.f : expf(p[j] - m_new);
+      const float e = (p[j] == -INFINITY) ? 0.f : exp_fast(p[j] - m_new);
       p[j] = e;
       lsum += e;
     }
@@ -183,27 +244,21 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
         rest[i] = p[(2 * ks) * 4 + i];
         rest[4 + i] = p[(2 * ks + 1) * 4 + i];
       }
-#pragma unroll
-      for (int term = 0; term < NT; ++term) {
-        float part[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          part[j] = Num<T>::round(rest[j]);
-          rest[j] -= part[j];
-        }
-        set_p(pf[term], part);
-      }
+      split_p(pf, rest);
 #pragma unroll
       for (int db = 0; db < HD / 16; ++db) {
         Frag<T> vf;
-        const T* row = sVt + (db * 16 + q16) * S::LDV + ks * 32 + g4 * 4;
-        lds4(vf, 0, row);
-        lds4(vf, 1, row + 16);
+        lds_frag(vf, sVt + (db * 16 + q16) * S::LDV + ks * 32 + g4 * 8);
 #pragma unroll
         for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
       }
     }
     __syncthreads();
+  };
+  static_assert(kPre == 2, "two register slots");
+  for (int t0 = 0; t0 < ntiles; t0 += kPre) {
+    tile(kr0, vr0, t0);
+    if (t0 + 1 < ntiles) tile(kr1, vr1, t0 + 1);
   }
 
   // full row sum across the four lane groups holding the same query
@@ -228,6 +283,206 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs a) {
       float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
       pm[0] = m_run;
       pm[1] = l_run;
+    }
+  }
+}
+
+// ---- spread: 16 * QB query rows per workgroup, NW waves taking key tiles round-robin
+template <typename T, int HD, int NW, int QB>
+__global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
+  constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
+  constexpr int NT = sizeof(T) == 2 ? 2 : 1;
+  __shared__ float sm_o[NW][QB][HD][16];
+  __shared__ float sm_m[NW][QB][16], sm_l[NW][QB][16], sm_tot[2][QB][16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4, q16 = lane & 15;
+  const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
+  const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv, split = blockIdx.z;
+  const int rho0 = blockIdx.x * 16 * QB;           // < rows_total (grid.x is exact)
+
+  bool qv[QB];
+  int qpos[QB];
+  Frag<T> qf[QB][NS];
+  const T* Q = reinterpret_cast<const T*>(a.q);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rho = rho0 + qb * 16 + q16;
+    qv[qb] = rho < rows_total;
+    const int hh = qv[qb] ? rho / a.nq : 0, qi = qv[qb] ? rho % a.nq : 0;
+    qpos[qb] = a.ctx + qi;
+    const size_t qrow = ((size_t)(b * a.nq + qi) * a.Hq + kvh * G + hh) * HD;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (qv[qb]) {
+        lds_frag(qf[qb][s], Q + qrow + s * 32 + g4 * 8);
+      } else {
+        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        set_p(qf[qb][s], z);
+      }
+    }
+  }
+
+  // key range of this workgroup (one split)
+  const int total = a.ctx + a.nq;
+  int klimit = total;
+  if (a.causal) {
+    const int last = min(rho0 + 16 * QB - 1, rows_total - 1);
+    const int imax = (rho0 / a.nq == last / a.nq) ? last % a.nq : a.nq - 1;
+    klimit = a.ctx + imax + 1;
+  }
+  const int per = ((total + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+  const int kbeg = split * per, kend = min(klimit, kbeg + per);
+  const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+
+  const T* Kc = reinterpret_cast<const T*>(a.kc) + ((size_t)b * a.Hkv + kvh) * a.kv_stride * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * HD * a.kv_stride;
+
+  f32x4_t o[QB][NDB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) o[qb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // fragments of one tile: K rows (A of S^T, rows in tile_key order) and V^T
+  // rows (A of O^T: keys ks*32 + g4*8 .. +7, matching P's layout)
+  Frag<T> kf[2][4][NS], vf[2][2][NDB];
+  auto load = [&](int buf, int t) {
+    const int k0 = kbeg + t * KT;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(k0 + tile_key(kb, q16), kend - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) lds_frag(kf[buf][kb][s], Kc + (size_t)key * HD + s * 32 + g4 * 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        lds_frag(vf[buf][ks][db], Vt + (size_t)(db * 16 + q16) * a.kv_stride + k0 + ks * 32 + g4 * 8);
+  };
+  auto compute = [&](int buf, int t) {
+    const int k0 = kbeg + t * KT;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4_t sc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) mma16x16x32(sc[kb], kf[buf][kb][s], qf[qb][s]);
+      }
+      float p[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kpos = k0 + tile_key(kb, g4 * 4 + i);
+          float v = sc[kb][i] * a.scale;
+          if (kpos >= kend || (a.causal && kpos > qpos[qb])) v = -INFINITY;
+          p[kb * 4 + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run[qb], tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run[qb] - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = (p[j] == -INFINITY) ? 0.f : exp_fast(p[j] - m_new);
+        p[j] = e;
+        lsum += e;
+      }
+      l_run[qb] = l_run[qb] * alpha + lsum;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) o[qb][j] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> pf[NT];
+        float rest[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rest[i] = p[(2 * ks) * 4 + i];
+          rest[4 + i] = p[(2 * ks + 1) * 4 + i];
+        }
+        split_p(pf, rest);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int term = 0; term < NT; ++term) mma16x16x32(o[qb][db], vf[buf][ks][db], pf[term]);
+      }
+    }
+  };
+  // the wave's tiles w, w + NW, ...: the next one is loaded (unconditionally,
+  // clamped to the last tile) while the current one is computed
+  if (w < ntiles) load(0, w);
+  for (int t0 = w; t0 < ntiles; t0 += 2 * NW) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + u * NW;
+      if (t >= ntiles) break;
+      load(u ^ 1, min(t + NW, ntiles - 1));
+      compute(u, t);
+    }
+  }
+
+  // merge the waves' partials in wave order
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    l_run[qb] += __shfl_xor(l_run[qb], 16, 64);
+    l_run[qb] += __shfl_xor(l_run[qb], 32, 64);
+    if (g4 == 0) {
+      sm_m[w][qb][q16] = m_run[qb];
+      sm_l[w][qb][q16] = l_run[qb];
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[w][qb][db * 16 + g4 * 4 + i][q16] = o[qb][db][i];
+  }
+  __syncthreads();
+  // per (query, wave): rescale factor exp(m_w - M) and the total 1 / sum (or M, sum for a split)
+  if (threadIdx.x < QB * 16) {
+    const int qb = threadIdx.x / 16, q = threadIdx.x % 16;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm_m[v][qb][q]);
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float mv = sm_m[v][qb][q];
+      const float f = mv == -INFINITY ? 0.f : expf(mv - M);
+      L += f * sm_l[v][qb][q];
+      sm_m[v][qb][q] = f;                       // the slot now holds the wave's factor
+    }
+    sm_tot[0][qb][q] = M;
+    sm_tot[1][qb][q] = L;
+  }
+  __syncthreads();
+  const size_t nrows = (size_t)a.B * a.nq * a.Hq;
+  for (int e = threadIdx.x; e < QB * 16 * HD; e += 64 * NW) {
+    const int d = e % HD, q = (e / HD) % 16, qb = e / (16 * HD);
+    const int rho = rho0 + qb * 16 + q;
+    if (rho >= rows_total) continue;
+    float O = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) O += sm_m[v][qb][q] * sm_o[v][qb][d][q];
+    const float M = sm_tot[0][qb][q], L = sm_tot[1][qb][q];
+    const int hh = rho / a.nq, qi = rho % a.nq;
+    const size_t rowid = (size_t)(b * a.nq + qi) * a.Hq + kvh * G + hh;
+    if (a.splits == 1) {
+      Num<T>::store(reinterpret_cast<T*>(a.out) + rowid * HD + d, O / L);
+    } else {
+      a.part_o[((size_t)split * nrows + rowid) * HD + d] = O;
+      if (d == 0) {
+        a.part_ml[((size_t)split * nrows + rowid) * 2] = M;
+        a.part_ml[((size_t)split * nrows + rowid) * 2 + 1] = L;
+      }
     }
   }
 }
@@ -259,11 +514,23 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   store4(out, v);
 }
 
+// Launch shape: spread while the 64-row query blocks cannot fill the chip.
+constexpr int kSpreadNW = 4, kSpreadQB = 1;
+inline bool use_spread(int B, int nq, int Hq, int Hkv) {
+  return ((Hq / Hkv) * nq + 63) / 64 * B * Hkv < 128;
+}
+
 template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  dim3 grid((G * a.nq + 63) / 64, a.B * a.Hkv, a.splits);
-  hipLaunchKernelGGL((k_attention<T, HD>), grid, dim3(256), 0, s, a);
+  if (use_spread(a.B, a.nq, a.Hq, a.Hkv)) {
+    constexpr int NW = kSpreadNW, QB = kSpreadQB;
+    dim3 grid((G * a.nq + 16 * QB - 1) / (16 * QB), a.B * a.Hkv, a.splits);
+    hipLaunchKernelGGL((k_attn_spread<T, HD, NW, QB>), grid, dim3(64 * NW), 0, s, a);
+  } else {
+    dim3 grid((G * a.nq + 63) / 64, a.B * a.Hkv, a.splits);
+    hipLaunchKernelGGL((k_attn_tiled<T, HD>), grid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const size_t threads = (size_t)a.B * a.nq * a.Hq * (HD / 4);
@@ -273,11 +540,20 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Key splits (and the merge launch they need): spread -- at most 8 tiles per
+// wave; tiled -- only where a workgroup would walk more than 16 tiles, and only
+// as far as filling the chip asks.
 int attention_splits(int B, int nq, int Hq, int Hkv, int keys) {
-  const int wg = ((Hq / Hkv) * nq + 63) / 64 * B * Hkv;
-  int splits = (512 + wg - 1) / wg;
-  const int max_by_keys = (keys + 255) / 256;
-  if (splits > max_by_keys) splits = max_by_keys;
+  const int tiles = (keys + 63) / 64;
+  int splits;
+  if (use_spread(B, nq, Hq, Hkv)) {
+    splits = (tiles + 8 * kSpreadNW - 1) / (8 * kSpreadNW);
+  } else {
+    const int wg = ((Hq / Hkv) * nq + 63) / 64 * B * Hkv;
+    splits = (256 + wg - 1) / wg;
+    const int max_by_keys = (tiles + 15) / 16;
+    if (splits > max_by_keys) splits = max_by_keys;
+  }
   if (splits > 16) splits = 16;
   if (splits < 1) splits = 1;
   return splits;

@@ -167,7 +167,7 @@ hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t
 // position ctx + i.
 template <typename T>
 __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int M, int n,
-                               int Hq, int Hkv, int hd, int max_ctx, int ctx) {
+                               int Hq, int Hkv, int hd, int stride, int ctx) {
   const int r = blockIdx.x, b = r / n, i = r % n, pos = ctx + i, half = hd / 2;
   const int ncol = (Hq + 2 * Hkv) * hd;
   const size_t sstride = (size_t)M * ncol;
@@ -188,7 +188,7 @@ __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* 
       Num<T>::store(dst + j + half, o2);
     } else {
       const int kh = head - Hq;
-      T* dst = kc + (((size_t)b * Hkv + kh) * max_ctx + pos) * hd;
+      T* dst = kc + (((size_t)b * Hkv + kh) * stride + pos) * hd;
       Num<T>::store(dst + j, o1);
       Num<T>::store(dst + j + half, o2);
     }
@@ -197,15 +197,15 @@ __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* 
     const int kh = u / hd, c = u % hd;
     float v = 0.f;
     for (int s = 0; s < S; ++s) v += x[s * sstride + (Hq + Hkv) * hd + u];
-    Num<T>::store(vc + (((size_t)b * Hkv + kh) * max_ctx + pos) * hd + c, v);
+    Num<T>::store(vc + (((size_t)b * Hkv + kh) * hd + c) * stride + pos, v);   // V^T
   }
 }
 template <typename T>
 hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
-                        int Hkv, int hd, int max_ctx, int ctx, hipStream_t s) {
+                        int Hkv, int hd, int stride, int ctx, hipStream_t s) {
   if (B * n <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_rope_scatter<T>), dim3(B * n), dim3(256), 0, s, part, S, rope, q, kc, vc, B * n, n, Hq,
-                     Hkv, hd, max_ctx, ctx);
+                     Hkv, hd, stride, ctx);
   return hipGetLastError();
 }
 

@@ -43,6 +43,17 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
   if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
 }
 
+// Four consecutive values in one store (8 bytes bf16, 16 bytes fp32).
+__device__ __forceinline__ void store4(bf16* p, const float* e) {
+  uint2 u;
+  u.x = f32x2_to_bf16x2(e[0], e[1]);
+  u.y = f32x2_to_bf16x2(e[2], e[3]);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+__device__ __forceinline__ void store4(float* p, const float* e) {
+  *reinterpret_cast<float4*>(p) = make_float4(e[0], e[1], e[2], e[3]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, int V, int chunks, int clen,
                                                          float inv_t, SeedArg seeds, int n,
@@ -61,28 +72,63 @@ __global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, in
   float zmax = -INFINITY, lmax = -INFINITY;
   int lidx = 0x7fffffff;
   Top2 t2{-INFINITY, 0x7fffffff, -INFINITY};
+  // every load is issued unconditionally (addresses clamped into the chunk, the
+  // values past its end masked) so that all of them are in flight together
+  float4 l4[kPerThread / 4];
+#pragma unroll
+  for (int it = 0; it < kPerThread / 4; ++it) {
+    const int v = min(v0 + (it * 256 + tid) * 4, v1 - 4);
+    l4[it] = *reinterpret_cast<const float4*>(L + v);
+  }
+  // logit arg-max and the max of z over all of the thread's values
 #pragma unroll
   for (int it = 0; it < kPerThread / 4; ++it) {
     const int v = v0 + (it * 256 + tid) * 4;
-    if (v < v1) {
-      const float4 l4 = *reinterpret_cast<const float4*>(L + v);
-      const uint4 x = philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
-                                   (uint32_t)(v >> 2));
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+    const bool ok = v < v1;
+    const float lv[4] = {l4[it].x, l4[it].y, l4[it].z, l4[it].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float zz = lv[j] * inv_t;
-        z[it * 4 + j] = zz;
-        zmax = fmaxf(zmax, zz);
-        argmax_merge(lmax, lidx, lv[j], v + j);
-        const float sc = zz + gumbel_of(xv[j]);
-        top2_merge(t2, Top2{sc, v + j, -INFINITY});
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[it * 4 + j] = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const float zz = ok ? lv[j] * inv_t : -INFINITY;
+      z[it * 4 + j] = zz;
+      zmax = fmaxf(zmax, zz);
+      if (ok) argmax_merge(lmax, lidx, lv[j], v + j);
     }
+  }
+  // Gumbel-max top two.  The first four values of every lane are scored
+  // exactly; the wave's second-best score b2 and largest z then bound the rest:
+  // a value can enter the chunk's top two only if its Gumbel noise exceeds
+  // b2 - max z, i.e. only if its uniform exceeds exp(-exp(-(b2 - max z))) -- a
+  // threshold on the raw Philox word (lowered by a 1e-3 margin on the score,
+  // far above fp32 rounding).  Values under it cannot change the top two, so
+  // they skip the two logarithms.
+  auto score = [&](int it, const uint4& x, uint32_t qmin) {
+    const int v = v0 + (it * 256 + tid) * 4;
+    if (v >= v1) return;
+    const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((xv[j] >> 9) >= qmin) top2_merge(t2, Top2{z[it * 4 + j] + gumbel_of(xv[j]), v + j, -INFINITY});
+  };
+  score(0, philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
+                        (uint32_t)((v0 + tid * 4) >> 2)), 0u);
+  uint32_t qmin = 0;
+  {
+    Top2 tw = t2;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      top2_merge(tw, Top2{__shfl_xor(tw.b1, o, 64), __shfl_xor(tw.i1, o, 64), __shfl_xor(tw.b2, o, 64)});
+    const float delta = tw.b2 - wave_max(zmax) - 1e-3f;
+    if (delta > -INFINITY) {
+      const float uthr = expf(-expf(-delta));                 // prune when u < uthr
+      const float q = floorf(uthr * 8388608.f - 0.5f) - 1.f;  // u = (2q + 1) 2^-24 < uthr for q < qmin
+      qmin = q > 0.f ? (uint32_t)q : 0u;
+    }
+  }
+#pragma unroll
+  for (int it = 1; it < kPerThread / 4; ++it) {
+    const int v = v0 + (it * 256 + tid) * 4;
+    score(it, philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
+                           (uint32_t)(v >> 2)), qmin);
   }
   // workgroup reductions (fixed order)
 #pragma unroll
@@ -123,11 +169,7 @@ __global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, in
         s += e;
         ws += e * dz;
       }
-      if (ptilde != nullptr) {
-        T* dst = ptilde + (size_t)row * V + v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Num<T>::store(dst + j, e4[j]);
-      }
+      if (ptilde != nullptr) store4(ptilde + (size_t)row * V + v, e4);
     }
   }
   s = wave_sum(s);
@@ -144,50 +186,72 @@ __global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, in
   }
 }
 
-// One thread per row: combine chunk statistics in chunk order (fp64).
-__global__ void k_sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
-                                float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per row, lane c holding chunk c (chunks <= 64): the chunk statistics
+// combine in fp64 through a fixed butterfly, so the result does not depend on
+// scheduling; arg-max and Gumbel top-two merges are order-free.
+__global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int M, int chunks, int n,
+                                                       const uint8_t* active, float* H, int32_t* y, int32_t* am,
+                                                       float* margin, float* chunk_scale) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= M) return;
-  const HeadPart* p = part + (size_t)r * chunks;
-  double m = -INFINITY;
-  for (int c = 0; c < chunks; ++c) m = fmax(m, (double)p[c].m);
-  double S = 0.0, W = 0.0;
-  float lmax = p[0].lmax;
-  int lidx = p[0].lidx;
-  Top2 t2{p[0].g1, p[0].gidx, p[0].g2};
-  for (int c = 0; c < chunks; ++c) {
-    const double f = exp((double)p[c].m - m);
-    S += (double)p[c].s * f;
-    W += f * ((double)p[c].w + ((double)p[c].m - m) * (double)p[c].s);
-    if (c > 0) {
-      argmax_merge(lmax, lidx, p[c].lmax, p[c].lidx);
-      top2_merge(t2, Top2{p[c].g1, p[c].gidx, p[c].g2});
-    }
+  const bool has = lane < chunks;
+  HeadPart p;
+  if (has) p = part[(size_t)r * chunks + lane];
+  else { p.m = -INFINITY; p.s = 0.f; p.w = 0.f; p.lmax = -INFINITY; p.lidx = 0x7fffffff;
+         p.g1 = -INFINITY; p.gidx = 0x7fffffff; p.g2 = -INFINITY; }
+  const float mf = wave_max(p.m);
+  const double m = (double)mf;
+  const double f = has ? exp((double)p.m - m) : 0.0;
+  double S = (double)p.s * f;
+  double W = has ? f * ((double)p.w + ((double)p.m - m) * (double)p.s) : 0.0;
+  float lmax = p.lmax;
+  int lidx = p.lidx;
+  Top2 t2{p.g1, p.gidx, p.g2};
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    S += __shfl_xor(S, o, 64);
+    W += __shfl_xor(W, o, 64);
+    argmax_merge(lmax, lidx, __shfl_xor(lmax, o, 64), __shfl_xor(lidx, o, 64));
+    top2_merge(t2, Top2{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)});
   }
-  if (chunk_scale != nullptr)
-    for (int c = 0; c < chunks; ++c) chunk_scale[(size_t)r * chunks + c] = (float)(exp((double)p[c].m - m) / S);
-  if (active != nullptr && active[r / n] == 0) return;
+  if (chunk_scale != nullptr && has) chunk_scale[(size_t)r * chunks + lane] = (float)(f / S);
+  if (lane != 0 || (active != nullptr && active[r / n] == 0)) return;
   H[r] = (float)(log(S) - W / S);
   y[r] = t2.i1;
   am[r] = lidx;
   margin[r] = t2.b1 - t2.b2;
 }
 
-// s[r][c] = sum over splits of scale[r][split / sub] * part[split][r][c], split order;
-// each vocabulary chunk of the sampler is contracted as `sub` K-slices.
-__global__ void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub,
-                                  float* S) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)M * d) return;
-  const size_t r = i / d;
-  float acc = 0.f;
-  for (int c = 0; c < chunks; ++c) {
-    float pc = 0.f;
-    for (int u = 0; u < sub; ++u) pc += part[(size_t)(c * sub + u) * M * d + i];
-    acc += chunk_scale[r * chunks + c] * pc;
+// s[r][c] = sum over chunks of scale[r][chunk] * (sum of the chunk's `sub` K-slice
+// partials, slice order).  Four columns per thread; the partial loads of up to
+// four chunks are issued together.
+__global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d,
+                                                         int chunks, int sub, float* S) {
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;      // float4 index
+  const size_t nq = (size_t)M * d / 4;
+  if (q >= nq) return;
+  const size_t r = q * 4 / d;
+  const float4* p4 = reinterpret_cast<const float4*>(part);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < chunks; c0 += 4) {
+    float4 pc[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      pc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + cc < chunks)
+        for (int u = 0; u < sub; ++u) {
+          const float4 v = p4[(size_t)((c0 + cc) * sub + u) * nq + q];
+          pc[cc].x += v.x; pc[cc].y += v.y; pc[cc].z += v.z; pc[cc].w += v.w;
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      if (c0 + cc < chunks) {
+        const float sc = chunk_scale[r * chunks + c0 + cc];
+        acc.x += sc * pc[cc].x; acc.y += sc * pc[cc].y; acc.z += sc * pc[cc].z; acc.w += sc * pc[cc].w;
+      }
   }
-  S[i] = acc;
+  reinterpret_cast<float4*>(S)[q] = acc;
 }
 
 // ------------------------------------------------------------------ commit
@@ -283,16 +347,16 @@ hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float 
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active, float* H,
                          int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sampler_merge, dim3((M + 127) / 128), dim3(128), 0, s, part, M, chunks, n, active, H, y,
+  hipLaunchKernelGGL(k_sampler_merge, dim3((M + 3) / 4), dim3(256), 0, s, part, M, chunks, n, active, H, y,
                      am, margin, chunk_scale);
   return hipGetLastError();
 }
 
 hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub, float* S,
                            hipStream_t s) {
-  const size_t nel = (size_t)M * d;
-  if (nel == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s, part, chunk_scale,
+  const size_t nq = (size_t)M * d / 4;      // d is a multiple of 256
+  if (nq == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, part, chunk_scale,
                      M, d, chunks, sub, S);
   return hipGetLastError();
 }

@@ -122,10 +122,17 @@ class Engine:
         return self.state_buf[off:off + nb.value].view(dtype).view(*shape)
 
     def kv_views(self):
+        """K and V caches as [L][B][Hkv][max_ctx][hd] tensors aliasing the state.
+
+        K is stored row-major per key, V transposed ([hd][ctx] per kv head), each
+        with the context capacity rounded up to 64; the V view is a transposed
+        (strided) view, so writes through it land in the library's layout."""
         c = self.cfg
         dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
-        shape = (c.n_layers, self.B, c.n_kv_heads, self.max_ctx, c.head_dim)
-        return self.view(L.DG_VIEW_K_CACHE, dt, shape), self.view(L.DG_VIEW_V_CACHE, dt, shape)
+        ctx_pad = (self.max_ctx + 63) // 64 * 64
+        k = self.view(L.DG_VIEW_K_CACHE, dt, (c.n_layers, self.B, c.n_kv_heads, ctx_pad, c.head_dim))
+        v = self.view(L.DG_VIEW_V_CACHE, dt, (c.n_layers, self.B, c.n_kv_heads, c.head_dim, ctx_pad))
+        return k[:, :, :, :self.max_ctx, :], v.transpose(-1, -2)[:, :, :, :self.max_ctx, :]
 
     def self_cond_view(self) -> torch.Tensor:
         return self.view(L.DG_VIEW_SELF_COND, torch.float32, (self.B, self.n, self.cfg.d_model))

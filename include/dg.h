@@ -63,7 +63,7 @@ typedef struct dg_config {
   int32_t n_experts;    /* 1..128 */
   int32_t ffn_hidden;   /* multiple of 64 */
   int32_t top_k;        /* 1..min(8, n_experts) */
-  int32_t vocab;        /* multiple of 64 */
+  int32_t vocab;        /* multiple of 64, at most 262144 */
   int32_t canvas_len;   /* 1..256; the pages' canvas is 256 tokens ([mlqm] 一) */
   int32_t dtype;        /* DG_DTYPE_F32 or DG_DTYPE_BF16: weight and matmul operand type */
   int32_t self_cond;    /* 1: add (softmax of the previous step) @ E @ W_sc^T to the embeddings */
@@ -120,7 +120,9 @@ int32_t dg_state_ctx_len(const dg_state* state);
 int32_t dg_state_canvas_index(const dg_state* state);
 
 /* Device views into the state buffer, for inspection and teacher forcing:
- *   DG_VIEW_K_CACHE / DG_VIEW_V_CACHE: [L][B][Hkv][max_ctx][hd], cfg dtype
+ *   DG_VIEW_K_CACHE: [L][B][Hkv][ctx_pad][hd], cfg dtype, ctx_pad = max_ctx rounded up to 64
+ *   DG_VIEW_V_CACHE: [L][B][Hkv][hd][ctx_pad], cfg dtype (V transposed: each kv head's values
+ *                    stored dimension-major, so attention reads V^T rows directly)
  *   DG_VIEW_SELF_COND: float [B][canvas_len][d], the vector s of the last step
  *   DG_VIEW_PREV_ARGMAX: int32 [B][canvas_len], argmax seen by the last commit
  *   DG_VIEW_ROUTE: int32 [L][B * canvas_len][top_k], expert ids chosen in each
