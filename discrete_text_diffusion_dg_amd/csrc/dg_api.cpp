@@ -295,7 +295,7 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.pos = L.take((size_t)R * k * 4);
   o.tiles = L.take((size_t)o.cap_tiles * sizeof(int4));
   o.n_tiles = L.take(4);
-  o.rcnt = L.take((size_t)E * ((R + 15) / 16) * 4);     // router count table
+  o.rcnt = L.take((size_t)E * ((R + router_rows_per_block(E) - 1) / router_rows_per_block(E)) * 4);  // router counts
   o.act = L.take((size_t)R * k * F * es);
   o.y = L.take((size_t)R * k * d * 4);
   o.logits = L.take((size_t)R * V * 4);

@@ -102,7 +102,8 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
                         int Hkv, int hd, int stride, int ctx, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
 // Router of one layer: logits, top-k + softmax weights, and the expert-sorted
-// order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / 16) ints.
+// order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / router_rows_per_block(E)) ints.
+int router_rows_per_block(int E);
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
                   int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s);

@@ -210,11 +210,12 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
 }
 
 // ------------------------------------------------------------------ router
-// Two launches per layer, no atomics.  k_router: a workgroup owns 16 rows --
+// Two launches per layer, no atomics.  k_router: a workgroup owns RPB rows --
 //  1. their router logits on MFMA, the four waves splitting K and adding their
 //     partial sums through LDS in a fixed order;
-//  2. per row, the top k logits by rank -- the number of logits beating one,
-//     ties going to the lower expert id -- then softmax over the selected;
+//  2. per row, the top k logits -- ties going to the lower expert id -- by
+//     rank counting (E <= 32) or by bisection on unique keys (larger E), then
+//     softmax over the selected;
 //  3. per expert, the count of the block's (row, slot) entries -> cnt[e][blk],
 //     and per entry its rank among the block's entries of that expert, in
 //     (row, slot) order -> pos.
@@ -238,38 +239,83 @@ __device__ __forceinline__ void router_frag(Frag<float>& f, const float* p) {
 
 // NCB = ceil(E / 16) column blocks of logits (a template parameter, so every
 // operand load is unconditional).
-template <typename T, int NCB>
-__global__ __launch_bounds__(256) void k_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog,
+// Top k of one row (E <= 128 logits in LDS) by one wave: keys (order-preserving
+// bits of the logit, then 127 - expert) are unique, so the k-th largest key T
+// is found bit by bit (39 steps, a wave ballot count each) and exactly k keys
+// are >= T; the slot of each is the number of keys above it.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 7) | (uint64_t)(127 - e);
+}
+__device__ __forceinline__ void topk_bisect(const float* row, int E, int k, int lane, int* sel_e, float* sel_v) {
+  const bool h0 = lane < E, h1 = lane + 64 < E;
+  const float v0 = h0 ? row[lane] : 0.f, v1 = h1 ? row[lane + 64] : 0.f;
+  const uint64_t k0 = h0 ? route_key(v0, lane) : 0ull, k1 = h1 ? route_key(v1, lane + 64) : 0ull;
+  uint64_t T = 0;
+  for (int bit = 38; bit >= 0; --bit) {
+    const uint64_t c = T | (1ull << bit);
+    const int n = __popcll(__ballot(k0 >= c)) + __popcll(__ballot(k1 >= c));
+    if (n >= k) T = c;
+  }
+  uint64_t m0 = __ballot(h0 && k0 >= T), m1 = __ballot(h1 && k1 >= T);
+  while (m0 | m1) {
+    const bool hi = m0 == 0;
+    const int l = __ffsll((unsigned long long)(hi ? m1 : m0)) - 1;
+    if (hi) m1 &= m1 - 1; else m0 &= m0 - 1;
+    const uint64_t ks = __shfl(hi ? k1 : k0, l, 64);
+    const int slot = __popcll(__ballot(k0 > ks)) + __popcll(__ballot(k1 > ks));
+    if (lane == 0) {
+      sel_e[slot] = hi ? l + 64 : l;
+      sel_v[slot] = row[hi ? l + 64 : l];
+    }
+  }
+}
+
+template <typename T, int NCB, int RPB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog,
                                                 int* idx, float* w, int* pos, int* cnt) {
-  __shared__ float red[3][NCB * 4][64];
+  __shared__ float red[NW - 1][NCB * 4][64];
   __shared__ float lg[16][129];
-  __shared__ int sel_e[16][8];
-  __shared__ float sel_v[16][8];
-  __shared__ int ent_e[16 * 8];
+  __shared__ int sel_e[RPB][8];
+  __shared__ float sel_v[RPB][8];
+  __shared__ int ent_e[RPB * 8];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g4 = lane >> 4, c16 = lane & 15;
-  const int r0 = blockIdx.x * 16;
-  const int KS = d / 32, ks0 = wv * KS / 4, ks1 = (wv + 1) * KS / 4;
-  const T* ap = xn + (size_t)min(r0 + c16, M - 1) * d + g4 * 8;
+  const int r0 = blockIdx.x * RPB;
+  const int KS = d / 32, ks0 = wv * KS / NW, ks1 = (wv + 1) * KS / NW;
+  // MFMA rows c16 >= RPB repeat a valid row; their logits are never read
+  const T* ap = xn + (size_t)min(r0 + min(c16, RPB - 1), M - 1) * d + g4 * 8;
   const T* bp[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) bp[cb] = wr + (size_t)min(cb * 16 + c16, E - 1) * d + g4 * 8;
   f32x4_t acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // d is a multiple of 256, so each wave's K range (a quarter) is a multiple
-  // of 2 steps: pairs of steps, the loads of a pair issued together
-  for (int ks = ks0; ks < ks1; ks += 2) {
-    Frag<T> a[2], b[2][NCB];
+  // d is a multiple of 256 split over 4 waves, or of 512 split over 8, so each
+  // wave's K range is a multiple of 2 steps: pairs of steps, the next pair's loads in flight while the
+  // current pair is multiplied (clamped to the last pair at the end)
+  Frag<T> a2[2][2], b2[2][2][NCB];
+  auto ld_pair = [&](int buf, int ks) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      router_frag(a[u], ap + (ks + u) * 32);
+      router_frag(a2[buf][u], ap + (ks + u) * 32);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) router_frag(b[u][cb], bp[cb] + (ks + u) * 32);
+      for (int cb = 0; cb < NCB; ++cb) router_frag(b2[buf][u][cb], bp[cb] + (ks + u) * 32);
     }
+  };
+  auto mm_pair = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) mma16x16x32(acc[cb], a[u], b[u][cb]);
+      for (int cb = 0; cb < NCB; ++cb) mma16x16x32(acc[cb], a2[buf][u], b2[buf][u][cb]);
+  };
+  ld_pair(0, ks0);
+  for (int ks = ks0; ks < ks1; ks += 4) {
+    ld_pair(1, min(ks + 2, ks1 - 2));
+    mm_pair(0);
+    if (ks + 2 >= ks1) break;
+    ld_pair(0, min(ks + 4, ks1 - 2));
+    mm_pair(1);
   }
   if (wv > 0)
 #pragma unroll
@@ -282,25 +328,37 @@ __global__ __launch_bounds__(256) void k_router(const T* xn, const T* wr, int M,
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          lg[g4 * 4 + i][cb * 16 + c16] =
-              ((acc[cb][i] + red[0][cb * 4 + i][lane]) + red[1][cb * 4 + i][lane]) + red[2][cb * 4 + i][lane];
+        {
+          float v = acc[cb][i];
+#pragma unroll
+          for (int q = 0; q < NW - 1; ++q) v += red[q][cb * 4 + i][lane];
+          lg[g4 * 4 + i][cb * 16 + c16] = v;
+        }
   __syncthreads();
 
-  // top-k by rank: the rank of expert e in its row is the number of logits that
-  // beat it (greater, or equal with a lower id); ranks 0..k-1 are the slots
-  const int nrow = min(16, M - r0);
-  for (int pr = t; pr < nrow * E; pr += 256) {
+  const int nrow = min(RPB, M - r0);
+  for (int pr = t; pr < nrow * E; pr += 64 * NW) {
     const int rl = pr / E, e = pr - rl * E;
-    const float v = lg[rl][e];
-    int rank = 0;
-    for (int x = 0; x < E; ++x) {
-      const float o = lg[rl][x];
-      rank += (o > v) || (o == v && x < e);
-    }
-    rlog[(size_t)(r0 + rl) * E + e] = v;
-    if (rank < k) {
-      sel_e[rl][rank] = e;
-      sel_v[rl][rank] = v;
+    rlog[(size_t)(r0 + rl) * E + e] = lg[rl][e];
+  }
+  if (E > 32) {
+    // top-k by bisection, one row per wave
+    for (int rl = wv; rl < nrow; rl += NW) topk_bisect(lg[rl], E, k, lane, sel_e[rl], sel_v[rl]);
+  } else {
+    // top-k by rank: the rank of expert e in its row is the number of logits
+    // that beat it (greater, or equal with a lower id); ranks 0..k-1 are slots
+    for (int pr = t; pr < nrow * E; pr += 64 * NW) {
+      const int rl = pr / E, e = pr - rl * E;
+      const float v = lg[rl][e];
+      int rank = 0;
+      for (int x = 0; x < E; ++x) {
+        const float o = lg[rl][x];
+        rank += (o > v) || (o == v && x < e);
+      }
+      if (rank < k) {
+        sel_e[rl][rank] = e;
+        sel_v[rl][rank] = v;
+      }
     }
   }
   __syncthreads();
@@ -326,24 +384,35 @@ __global__ __launch_bounds__(256) void k_router(const T* xn, const T* wr, int M,
     pos[(size_t)r0 * k + t] = rank;
   }
   const int nblk = gridDim.x;
-  for (int e = t; e < E; e += 256) {
+  for (int e = t; e < E; e += 64 * NW) {
     int c = 0;
     for (int u = 0; u < nent; ++u) c += se[u] == e;
     cnt[(size_t)e * nblk + blockIdx.x] = c;
   }
 }
 
-__global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int k, int E, int nblk, int* cnt,
-                                                      int* perm, int* pos, int4* tiles, int* n_tiles) {
+constexpr int kFinishLds = 16384;     // count-table entries kept in LDS by the finish kernel
+
+__global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int k, int E, int nblk, int rpb,
+                                                      int* cnt, int* perm, int* pos, int4* tiles, int* n_tiles) {
   __shared__ int seg[256];
-  __shared__ int offs[128];
+  __shared__ int offs[128], toff[129];
+  __shared__ int tab[kFinishLds];
   const int t = threadIdx.x;
+  // the count table [E][nblk]: in LDS when it fits (one coalesced read), else in place in memory
+  const bool in_lds = E * nblk <= kFinishLds;
+  int* ct = in_lds ? tab : cnt;
+  if (in_lds) {
+#pragma unroll 8
+    for (int i = t; i < E * nblk; i += 256) tab[i] = cnt[i];
+    __syncthreads();
+  }
   int ep = 1;
   while (ep < E) ep <<= 1;
   const int tpe = 256 / ep;                       // threads per expert (>= 2)
   const int e = t / tpe, sg = t % tpe;
   const int per = (nblk + tpe - 1) / tpe, b0 = min(nblk, sg * per), b1 = min(nblk, b0 + per);
-  int* row = cnt + (size_t)(e < E ? e : 0) * nblk;
+  int* row = ct + (size_t)(e < E ? e : 0) * nblk;
   int ssum = 0;
   if (e < E)
     for (int b = b0; b < b1; ++b) ssum += row[b];
@@ -364,17 +433,25 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
     }
   }
   __syncthreads();
+  // exclusive prefixes over experts of the row counts and of the 64-row tile counts
   if (t == 0) {
-    int acc_rows = 0, nt = 0;
+    int acc_rows = 0, acc_tiles = 0;
     for (int x = 0; x < E; ++x) {
       const int c = offs[x];
       offs[x] = acc_rows;
-      for (int q0 = 0; q0 < c; q0 += 64) tiles[nt++] = make_int4(x, acc_rows + q0, min(64, c - q0), 0);
+      toff[x] = acc_tiles;
       acc_rows += c;
+      acc_tiles += (c + 63) / 64;
     }
-    *n_tiles = nt;
+    toff[E] = acc_tiles;
+    *n_tiles = acc_tiles;
   }
   __syncthreads();
+  for (int x = t; x < E; x += 256) {
+    const int c = (x + 1 < E ? offs[x + 1] : M * k) - offs[x];
+    for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
+      tiles[toff[x] + q] = make_int4(x, offs[x] + q * 64, min(64, c - q * 64), 0);
+  }
   const int MK = M * k;
   for (int i0 = t; i0 < MK; i0 += 4 * 256) {     // four independent entries in flight per thread
     int ex[4], rk[4];
@@ -388,7 +465,7 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * 256;
       if (i < MK) {
-        const int p = offs[ex[u]] + cnt[(size_t)ex[u] * nblk + i / (16 * k)] + rk[u];
+        const int p = offs[ex[u]] + ct[(size_t)ex[u] * nblk + i / (rpb * k)] + rk[u];
         pos[i] = p;
         perm[p] = i / k;
       }
@@ -396,23 +473,39 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
   }
 }
 
+template <typename T, int NW>
+hipError_t launch_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w,
+                         int* pos, int* cnt, hipStream_t s) {
+  constexpr int RPB = 16;
+  const dim3 grid((M + RPB - 1) / RPB), block(64 * NW);
+  switch ((E + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_router<T, 1, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos,
+                               cnt); break;
+    case 2: hipLaunchKernelGGL((k_router<T, 2, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos,
+                               cnt); break;
+    case 3: case 4:
+      hipLaunchKernelGGL((k_router<T, 4, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt);
+      break;
+    default:
+      hipLaunchKernelGGL((k_router<T, 8, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt);
+      break;
+  }
+  return hipGetLastError();
+}
+
+int router_rows_per_block(int) { return 16; }
+
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
                   int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int nblk = (M + 15) / 16;
-  const dim3 grid(nblk), block(256);
-  switch ((E + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_router<T, 1>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
-    case 2: hipLaunchKernelGGL((k_router<T, 2>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
-    case 3: case 4:
-      hipLaunchKernelGGL((k_router<T, 4>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
-    default:
-      hipLaunchKernelGGL((k_router<T, 8>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt); break;
-  }
-  hipError_t e = hipGetLastError();
+  // eight waves split K for wide models whose K steps divide into whole pairs per wave
+  hipError_t e = d % 512 == 0 ? launch_router<T, 8>(xn, wr, M, d, E, k, rlog, idx, w, pos, cnt, s)
+                          : launch_router<T, 4>(xn, wr, M, d, E, k, rlog, idx, w, pos, cnt, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(256), 0, s, idx, M, k, E, nblk, cnt, perm, pos, tiles, n_tiles);
+  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(256), 0, s, idx, M, k, E, nblk, 16, cnt, perm, pos, tiles,
+                     n_tiles);
   return hipGetLastError();
 }
 template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,

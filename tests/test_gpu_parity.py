@@ -368,6 +368,12 @@ def test_micro_hd128_gqa(torch_cuda):
     _run_parity(torch_cuda, mc, 12, 70, 1, 2, "micro-hd128")
 
 
+def test_micro_many_experts_top8(torch_cuda):
+    # 128 experts, top-8 (the proxy's router shape: 4-row router blocks, 8 logit column blocks)
+    mc = micro(n_layers=2, n_experts=128, top_k=8, ffn_hidden=128, vocab=2048)
+    _run_parity(torch_cuda, mc, 14, 200, 2, 2, "micro-e128", gain_std=0.1)
+
+
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
