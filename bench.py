@@ -31,6 +31,17 @@ import dg_inputs as di  # noqa: E402
 
 METRIC = "committed canvas tok/s + denoise-step latency (ms), 1×MI355X"
 HBM_PEAK_GBS = 8000.0
+
+# HBM traffic per launch of a stage's kernel from two rocprofv3 --pmc passes over
+# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the
+# stage's dispatches of the timed steps), each scaled by what the counter reads
+# for a plain 256 MiB copy (--calibrate-copy): FETCH_SIZE x2.0, WRITE_SIZE x1.0.
+# Keyed by (workload, stage); valid only for the kernel source it was taken on
+# (sha1 of the file), reported as null otherwise.
+MEASURED_TRAFFIC = {
+    # gate/up expert streaming, small workload: FETCH 43262.0 KiB x2.0 + WRITE 2048.0 KiB x1.0
+    ("small", "expert_up"): {"bytes_per_launch": 90697759, "sha1": "017e734451c722918850bda128d1cc22a1ebe928"},
+}
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
@@ -91,7 +102,25 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
     return by, fl
 
 
-def roofline(stage, ms_total, launches, mc, B, ctx, n_act):
+STAGE_SOURCE = {"expert_up": "k_expert.hip", "expert_down": "k_expert.hip", "attn": "k_attn.hip",
+                "router": "k_misc.hip", "sampler": "k_sampler.hip", "lm_head": "k_gemm.hip", "qkv": "k_gemm.hip"}
+
+
+def measured_traffic(workload: str, stage: str):
+    """Counter-derived HBM bytes per launch, or None if absent or taken on another kernel source."""
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((workload, stage))
+    src = STAGE_SOURCE.get(stage)
+    if rec is None or src is None:
+        return None
+    path = os.path.join(ROOT, "discrete_text_diffusion_dg_amd", "csrc", src)
+    with open(path, "rb") as f:
+        if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
+            return None
+    return rec["bytes_per_launch"]
+
+
+def roofline(stage, ms_total, launches, mc, B, ctx, n_act, traffic=None):
     w = stage_work(stage, mc, B, ctx, n_act)
     if w is None or launches == 0:
         return None
@@ -101,11 +130,11 @@ def roofline(stage, ms_total, launches, mc, B, ctx, n_act):
     if fl / max(by, 1) > peak_t * 1e12 / (HBM_PEAK_GBS * 1e9):
         ach = fl / t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_t, "unit": "TFLOP/s",
-                "frac": round(ach / peak_t, 4), "traffic": None, "kernel": stage,
+                "frac": round(ach / peak_t, 4), "traffic": traffic, "kernel": stage,
                 "launch_us": round(t * 1e6, 2), "bytes_per_launch": by, "flops_per_launch": fl}
     ach = by / t / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": stage,
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": stage,
             "launch_us": round(t * 1e6, 2), "bytes_per_launch": by, "flops_per_launch": fl}
 
 
@@ -155,7 +184,18 @@ def main():
     ap.add_argument("--workload", default="small", choices=sorted(di.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 256 MiB three times (the reference kernel for the HBM counters)")
     a = ap.parse_args()
+    if a.calibrate_copy:
+        import torch
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 256 MiB three times")
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the multi-GPU sharding of this path "
               "is a design note, not an implemented mode", file=sys.stderr)
@@ -256,7 +296,7 @@ def main():
     eng.profile([])
     canv = a.steps / S
     tok_s = B * n * canv / (ms / 1e3)
-    rl = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act)
+    rl = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act, measured_traffic(wl.name, dominant))
     log(f"[bench] {a.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); dominant {dominant}: "
         f"{dom_ms / max(dom_n, 1) * 1e3:.1f} us/launch")
 
