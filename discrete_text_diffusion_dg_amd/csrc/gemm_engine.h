@@ -14,7 +14,8 @@
 //
 // Schedulers map a workgroup id to a tile (dense, grouped by expert, split
 // along K); loaders produce 16 bytes of operand data for (tile row, k); an
-// epilogue consumes the accumulators.
+// epilogue consumes the accumulators (and may reuse the tile's shared memory,
+// free once the K loop has ended).
 #pragma once
 #include "dg_common.h"
 
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(256) void k_gemm(SCHED sc, AL al, BL bl, EP ep) {
   if (!sc.get(blockIdx.x, t)) return;
   f32x4_t acc[C::FM][C::FN];
   tile_mma<C, T>(t, al, bl, smem, acc);
-  ep.template apply<C>(t, acc);
+  ep.template apply<C>(t, acc, smem);
 }
 
 }  // namespace dg

@@ -13,7 +13,7 @@ namespace dg {
 struct EpStoreF32 {        // out[group * split_stride + (row_base + r) * ldo + n0 + c] = v
   float* out; int ldo; size_t split_stride;
   template <class C>
-  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN]) const {
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
     float* base = out + (size_t)t.group * split_stride;
     for_each_acc<C>(acc, [&](int r, int c, float v) {
       if (r < t.rows && c < t.cols) base[(size_t)(t.row_base + r) * ldo + t.n0 + c] = v;
@@ -25,7 +25,7 @@ template <typename T>
 struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the same 16 features
   T* act; int F;
   template <class C>
-  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN]) const {
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
     for (int a = 0; a < C::FM; ++a)
@@ -67,10 +67,15 @@ SplitPlan plan_splits(int M, int N, int K, int bm, int bn, int elem_bytes, int t
   return SplitPlan{s, kchunk};
 }
 
+// Split-K slices hold at least four 128-byte K steps; the prefetch depth of the
+// small-M products (4 slices in registers) puts a whole slice's loads in flight
+// at once instead of walking it in two round trips.
+constexpr int kSplitStages = 5;
+
 template <typename T>
 hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
                          SplitPlan sp, hipStream_t s) {
-  using C = TileCfg<T, 64, 64>;
+  using C = TileCfg<T, 64, 64, kSplitStages>;
   SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
   return launch<C, T>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
                       EpStoreF32{part, N, (size_t)M * N}, s);
@@ -79,7 +84,7 @@ hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, 
 template <typename T>
 hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
                               SplitPlan sp, hipStream_t s) {
-  using C = TileCfg<T, 64, 64>;
+  using C = TileCfg<T, 64, 64, kSplitStages>;
   SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
   return launch<C, T>(sc.mt * sc.nt * sp.splits, sc, ALF32<T>{A, lda}, BLPlain<T>{B, ldb},
                       EpStoreF32{part, N, (size_t)M * N}, s);

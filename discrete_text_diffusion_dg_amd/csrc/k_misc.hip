@@ -17,6 +17,45 @@ constexpr int kRowChunks = kMaxModel / 1024;
 
 inline int row_threads(int d) { return d / 4 < 256 ? d / 4 : 256; }
 
+__device__ __forceinline__ void add4(float4& a, const float4 b) {
+  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+
+// Sum over the S split partials of one float4 (part + s * stride + off), in
+// split order; the loads of up to 8 splits are issued together (indices past S
+// re-read the last split and are not added).
+__device__ __forceinline__ float4 sum_splits4(const float* part, int S, size_t stride, size_t off) {
+  float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(part + (size_t)min(s0 + u, S - 1) * stride + off);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) add4(p, v[u]);
+  }
+  return p;
+}
+__device__ __forceinline__ float sum_splits1(const float* part, int S, size_t stride, size_t off) {
+  float p = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(size_t)min(s0 + u, S - 1) * stride + off];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) p += v[u];
+  }
+  return p;
+}
+
+// Four consecutive values in one store (8 bytes bf16, 16 bytes fp32).
+__device__ __forceinline__ void store_row4(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f32x2_to_bf16x2(a, b), f32x2_to_bf16x2(c, d));
+}
+__device__ __forceinline__ void store_row4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
 // Stores the updated residual row v and y = rnd(v * g / sqrt(mean(v^2) + eps)).
 template <typename T>
 __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int d, const float* g, float eps,
@@ -39,16 +78,11 @@ __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int 
       const int c = (j * blockDim.x + tid) * 4;
       *reinterpret_cast<float4*>(hrow + c) = v[j];
       const float4 gg = *reinterpret_cast<const float4*>(g + c);
-      Num<T>::store(xrow + c + 0, v[j].x * inv * gg.x);
-      Num<T>::store(xrow + c + 1, v[j].y * inv * gg.y);
-      Num<T>::store(xrow + c + 2, v[j].z * inv * gg.z);
-      Num<T>::store(xrow + c + 3, v[j].w * inv * gg.w);
+      store_row4(xrow + c, v[j].x * inv * gg.x, v[j].y * inv * gg.y, v[j].z * inv * gg.z, v[j].w * inv * gg.w);
     }
 }
 
-__device__ __forceinline__ void add4(float4& a, const float4 b) {
-  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-}
+
 }  // namespace
 
 // h = emb[tok] (+ sum_s part[s]); xn = rnd(rmsnorm(h) * g)
@@ -65,9 +99,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t*
       const int c = (j * blockDim.x + threadIdx.x) * 4;
       const T* e = emb + (size_t)id * d + c;
       float4 x = make_float4(Num<T>::load(e), Num<T>::load(e + 1), Num<T>::load(e + 2), Num<T>::load(e + 3));
-      float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < S; ++s) add4(p, *reinterpret_cast<const float4*>(part + ((size_t)s * M + r) * d + c));
-      add4(x, p);
+      add4(x, S > 0 ? sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c) : make_float4(0.f, 0.f, 0.f, 0.f));
       v[j] = x;
     }
   norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
@@ -83,8 +115,7 @@ __global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int 
   for (int j = 0; j < kRowChunks; ++j)
     if (j < nj) {
       const int c = (j * blockDim.x + threadIdx.x) * 4;
-      float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < S; ++s) add4(p, *reinterpret_cast<const float4*>(part + ((size_t)s * M + r) * d + c));
+      const float4 p = sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c);
       float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
       add4(x, p);
       v[j] = x;
@@ -175,11 +206,8 @@ __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* 
   const float2* cs = rope + (size_t)pos * half;
   for (int u = threadIdx.x; u < (Hq + Hkv) * half; u += blockDim.x) {
     const int head = u / half, j = u % half;
-    float a = 0.f, bb = 0.f;
-    for (int s = 0; s < S; ++s) {
-      a += x[s * sstride + head * hd + j];
-      bb += x[s * sstride + head * hd + j + half];
-    }
+    const float a = sum_splits1(x, S, sstride, head * hd + j);
+    const float bb = sum_splits1(x, S, sstride, head * hd + j + half);
     const float2 t = cs[j];
     const float o1 = a * t.x - bb * t.y, o2 = bb * t.x + a * t.y;
     if (head < Hq) {
@@ -195,8 +223,7 @@ __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* 
   }
   for (int u = threadIdx.x; u < Hkv * hd; u += blockDim.x) {
     const int kh = u / hd, c = u % hd;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += x[s * sstride + (Hq + Hkv) * hd + u];
+    const float v = sum_splits1(x, S, sstride, (Hq + Hkv) * hd + u);
     Num<T>::store(vc + (((size_t)b * Hkv + kh) * hd + c) * stride + pos, v);   // V^T
   }
 }
