@@ -188,6 +188,11 @@ class OracleModel:
                 out["logits"][b] = logits
             if cfg.self_cond:
                 s_next[b] = st["p"] @ self.W("emb")
+                if want_logits:
+                    # spread of that sum under independent relative perturbations of its terms (tests):
+                    # sqrt(sum_v p_v^2 E_v^2)
+                    E = self.W("emb")
+                    out.setdefault("s_rms", np.zeros((self.B, n, cfg.d_model)))[b] = np.sqrt((st["p"] ** 2) @ (E * E))
             if trace is not None:
                 trace["m"], trace["logS"] = st["m"], st["logS"]
                 out["traces"][b] = trace

@@ -32,7 +32,8 @@ MARGIN_EXEMPT = 1e-3
 # router-logit drift of up to ~1% of the logit scale (the tests print the
 # measured drift).  2e-2 is the bf16 value tolerance; fp32 operands drift ~1e-6.
 GAP_REL = {"bf16": 2e-2, "f32": 1e-4}
-MAX_FLIP_FRAC = 0.10
+MAX_FLIP_FRAC = 0.25     # sanity bound on rows with an (explained) routing flip
+MAX_KV_OFF_FRAC = 0.10   # cached K/V positions beyond the value tolerance (all at router near-ties)
 
 
 @pytest.fixture(scope="module")
@@ -55,36 +56,46 @@ def near_tie(r: np.ndarray, mc) -> np.ndarray:
     return router_gap(r, mc.top_k) < GAP_REL[mc.dtype] * np.abs(r).max(axis=1)
 
 
-def check_routing(mc, eng, traces, rows_per_req, tag):
-    """Per-layer routing of the last pass against the oracle traces.
+def _routing_core(mc, groute, glog, traces, tag):
+    """Routing of one pass (groute / glog: [L][requests][rows][...]) against the oracle traces.
 
-    Returns the per-request rows whose routing flipped in some layer; asserts
-    every flip happened at an oracle near-tie."""
+    A row's expert set may differ from the oracle's only where the oracle's gap
+    between its k-th and (k+1)-th router logits is at most twice the row's
+    measured logit discrepancy (the largest |GPU - oracle| over its experts):
+    an expert swap needs the two logits to move past each other, and each moved
+    by at most that much.  A row that flipped in an earlier layer carries other
+    values from then on and is not checked again.  Returns the flipped rows."""
+    nreq, n = groute.shape[1], groute.shape[2]
+    flipped = np.zeros((nreq, n), bool)
+    drift_max, drift_med, n_flip = 0.0, [], 0
+    for l in range(mc.n_layers):
+        for j in range(nreq):
+            r = traces[j]["router_logits"][l]
+            rr = traces[j]["route_idx"][l]
+            gap = router_gap(r, mc.top_k)
+            drift_row = np.abs(glog[l, j].astype(np.float64) - r).max(axis=1)
+            flip = np.array([set(groute[l, j, i]) != set(rr[i]) for i in range(n)])
+            bad = flip & (gap > 2.0 * drift_row * (1 + 1e-6)) & ~flipped[j]
+            assert not bad.any(), (f"{tag} layer {l}: routing differs where the oracle gap {gap[bad][:5]} exceeds "
+                                   f"twice the measured drift {drift_row[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
+            clean = ~flipped[j] & ~flip
+            if clean.any():
+                drift_max = max(drift_max, float(drift_row[clean].max()))
+                drift_med.append(float(np.median(drift_row[clean])))
+            n_flip += int(flip.sum())
+            flipped[j] |= flip
+    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())}), each within twice its row's measured "
+        f"drift; router drift max {drift_max:.2e} median {np.median(drift_med):.2e}")
+    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: too many routing flips"
+    return flipped
+
+
+def check_routing(mc, eng, traces, rows_per_req, tag):
+    """Per-layer routing of the last pass against the oracle traces (see _routing_core)."""
     B = len(traces)
     groute = eng.route_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
     glog = eng.router_logits_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
-    flipped = np.zeros((B, rows_per_req), bool)
-    drift_max, drift_med, n_flip = 0.0, [], 0
-    for l in range(mc.n_layers):
-        for b in range(B):
-            rr = traces[b]["route_idx"][l]
-            gap = router_gap(traces[b]["router_logits"][l], mc.top_k)
-            flip = np.array([set(groute[l, b, i]) != set(rr[i]) for i in range(rows_per_req)])
-            # a row that flipped in an earlier layer carries other values from then on
-            bad = flip & ~near_tie(traces[b]["router_logits"][l], mc) & ~flipped[b]
-            assert not bad.any(), (f"{tag} layer {l}: routing differs at oracle gaps "
-                                   f"{gap[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
-            clean = ~flipped[b]
-            dr = np.abs(glog[l, b] - traces[b]["router_logits"][l]).max(axis=1)[clean]
-            if dr.size:
-                drift_max = max(drift_max, float(dr.max()))
-                drift_med.append(float(np.median(dr)))
-            n_flip += int(flip.sum())
-            flipped[b] |= flip
-    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())}), all at near-ties; router drift "
-        f"max {drift_max:.2e} median {np.median(drift_med):.2e}")
-    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: too many routing flips"
-    return flipped
+    return _routing_core(mc, groute, glog, traces, tag)
 
 
 def _compare_step(mc, got, ref, tag, taint):
@@ -254,7 +265,7 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
             log(f"[{tag}] {what} layer {l} K rel {ek[~off].max():.2e} V rel {ev[~off].max():.2e}; "
                 f"positions beyond tol {int(off.sum())}")
             assert not (off & ~near).any(), f"{tag} {what} layer {l}: K/V differ away from router near-ties"
-            assert off.mean() <= MAX_FLIP_FRAC
+            assert off.mean() <= MAX_KV_OFF_FRAC
             near |= np.stack([near_tie(traces[b]["router_logits"][l], mc) for b in range(nb)])
             if teacher:   # later passes start from the oracle's cache
                 dt = kc.dtype
@@ -286,10 +297,19 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
             taint = check_routing_subset(mc, eng, traces, reqs, batch, f"{tag} canvas {c} step {t}")
             _compare_step(mc, got, ref, f"{tag} canvas {c} step {t}", taint)
             if mc.self_cond:
-                gs = eng.self_cond_view()[ridx].cpu().numpy()
-                es = rel_err_rows(gs.reshape(-1, mc.d_model), om.s.reshape(-1, mc.d_model))
-                log(f"[{tag} canvas {c} step {t}] self-cond rel err max {es[~taint.ravel()].max():.3e}")
-                assert es[~taint.ravel()].max() < tol
+                # s = sum_v p_v E_v.  A logit discrepancy dz (max over the row, z units) perturbs the terms by
+                # relative amounts up to ~dz; summed with cancellation that moves s by about dz * sqrt(sum_v p_v^2 E_v^2)
+                # per element, which exceeds tol * |s| where p is near uniform (s then cancels to ~1/sqrt(V) of its
+                # terms).  Bound: tol * max|s_row| + 4 dz * sqrt(p^2 @ E^2).
+                gs = eng.self_cond_view()[ridx].cpu().numpy().astype(np.float64).reshape(-1, mc.d_model)
+                rs = om.s.reshape(-1, mc.d_model)
+                dz = (np.abs(got["logits"].astype(np.float64) - ref["logits"]) * float(ref["inv_t"])).max(axis=2)
+                bound = tol * np.abs(rs).max(axis=1, keepdims=True) + 4.0 * dz.reshape(-1, 1) * ref["s_rms"].reshape(-1, mc.d_model)
+                ratio = (np.abs(gs - rs) / bound).max(axis=1)
+                es = rel_err_rows(gs, rs)
+                log(f"[{tag} canvas {c} step {t}] self-cond: max |ds| / bound {ratio[~taint.ravel()].max():.3f}; "
+                    f"rel err max {es[~taint.ravel()].max():.3e}")
+                assert ratio[~taint.ravel()].max() <= 1.0
             # commit on the oracle's entropies (GPU's own for requests the oracle does not run)
             Hf, yf, amf = eng.H.clone(), eng.y.clone(), eng.am.clone()
             Hf[ridx] = torch.from_numpy(ref["H"]).cuda()
@@ -322,26 +342,7 @@ def check_routing_subset(mc, eng, traces, reqs, batch, tag):
     n = mc.canvas_len
     groute = eng.route_view(batch * n).cpu().numpy().reshape(mc.n_layers, batch, n, -1)[:, reqs]
     glog = eng.router_logits_view(batch * n).cpu().numpy().reshape(mc.n_layers, batch, n, -1)[:, reqs]
-    flipped = np.zeros((len(reqs), n), bool)
-    drift_max, drift_med, n_flip = 0.0, [], 0
-    for l in range(mc.n_layers):
-        for j in range(len(reqs)):
-            rr = traces[j]["route_idx"][l]
-            gap = router_gap(traces[j]["router_logits"][l], mc.top_k)
-            flip = np.array([set(groute[l, j, i]) != set(rr[i]) for i in range(n)])
-            bad = flip & ~near_tie(traces[j]["router_logits"][l], mc) & ~flipped[j]
-            assert not bad.any(), (f"{tag} layer {l}: routing differs at oracle gaps "
-                                   f"{gap[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
-            dr = np.abs(glog[l, j] - traces[j]["router_logits"][l]).max(axis=1)[~flipped[j]]
-            if dr.size:
-                drift_max = max(drift_max, float(dr.max()))
-                drift_med.append(float(np.median(dr)))
-            n_flip += int(flip.sum())
-            flipped[j] |= flip
-    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())}), all at near-ties; router drift "
-        f"max {drift_max:.2e} median {np.median(drift_med):.2e}")
-    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: too many routing flips"
-    return flipped
+    return _routing_core(mc, groute, glog, traces, tag)
 
 
 def _scaled(arr, mc, s):
@@ -378,6 +379,13 @@ def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
     _run_parity(torch_cuda, mc, 13, 0, 1, 2, "micro-f32-dense")
+
+
+def test_proxy_shapes_two_layers(torch_cuda):
+    # the 26B-scale proxy's layer, head, expert and vocabulary shapes (d 2048, 16/8 heads x 128, 128 experts
+    # top-8, F 768, vocab 262144: 64 sampler chunks) with 2 of its 30 layers and a 256-token prompt
+    mc = replace(di.workload("proxy").model, n_layers=2)
+    _run_parity(torch_cuda, mc, 2, 256, 1, 2, "proxy-2L")
 
 
 def test_small_workload_full_size(torch_cuda):
