@@ -1,5 +1,6 @@
 // Expert SwiGLU products for thin routed tiles (at most 64 rows, the batch-1
-// shapes): weight streaming from a fragment-packed layout, no LDS tiles.
+// shapes): weights streamed from a fragment-packed layout, the tile's
+// activation rows staged through LDS.
 //
 // Packed layout (built once by dg_model_create): a weight matrix W[N][K] of
 // one expert is stored as blocks P[N/16][K/32][64 lanes][8 elements], where
@@ -9,14 +10,20 @@
 // Gate and up of the same 16 features are interleaved per K step
 // (PGU[F/16][d/32][2][64][8]) so silu(g) * u is formed lane-locally.
 //
-// A wave owns FB feature blocks (of 16 outputs), all row blocks of the tile and
-// 1/KW of the K range (KW > 1: the waves of a block group add their partial
-// sums through LDS once, at the end); the tile's activation rows are read with
-// plain row loads (small, shared through the caches).  K steps are processed in groups of U; the loads of the
-// next group are issued before the MFMAs of the current one.  The number of
-// row blocks (1..4) is a template parameter chosen per tile at run time, so
-// every load of a path is unconditional and the memory-wait counts stay exact.
+// A workgroup of NW waves owns NW feature blocks (of 16 outputs) of one tile;
+// each wave streams the weights of its block over the whole K range.  The
+// tile's activation rows are read once per workgroup, as whole cache lines,
+// in chunks of KC K steps that are double-buffered in LDS (padded rows: the
+// fragment reads of 8 lanes cover distinct banks), so the weight stream keeps
+// the CU's memory requests to itself; the activations in registers would be
+// re-read by every wave, in half-line pieces.  Chunks are handed over with an
+// LDS-only barrier, so the weight loads in flight are not drained at the
+// hand-over.  The number of row blocks (1..4) is a template parameter chosen
+// per tile at run time, so every load of a path is unconditional and the
+// memory-wait counts stay exact.
 #include "dg_kernels.h"
+
+#include <type_traits>
 
 namespace dg {
 
@@ -35,30 +42,24 @@ __device__ __forceinline__ void frag_ld(Frag<float>& f, const float* p) {
   f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
-template <typename T>
-__device__ __forceinline__ void frag_keep(Frag<T>& f, bool keep);
-template <>
-__device__ __forceinline__ void frag_keep(Frag<bf16>& f, bool keep) {
-  if (!keep) f.v = make_uint4(0, 0, 0, 0);
-}
-template <>
-__device__ __forceinline__ void frag_keep(Frag<float>& f, bool keep) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f.v[j] = keep ? f.v[j] : 0.f;
-}
 
+// K steps per group (the weight loads of the next group are issued before the
+// MFMAs of the current one) and per staged activation chunk, per element type.
+// Measured on the batch-1 tile lists (9..32 active experts of 32, d = F = 1024):
+// one feature block per wave and four waves per workgroup (two workgroups per
+// CU) beat wider blocks, eight or sixteen waves, and 128-row tiles.
 template <typename T> struct StreamCfg;
-template <> struct StreamCfg<bf16> { static constexpr int U = 2; };
-template <> struct StreamCfg<float> { static constexpr int U = 1; };
-// Blocking of the two products: FB output blocks (of 16) per wave, and KW waves
-// of a workgroup splitting the K range of the same blocks (4 / KW block groups
-// per 4-wave workgroup).  These products are bound by the weight loads each CU
-// keeps in flight; every wave also re-reads its tile's activation rows, so the
-// split pays only where it adds streaming waves without multiplying those
-// re-reads: measured on skewed routings (9..31 of 32 experts active), the
-// down product gains 20-28% from a 4-way split, gate/up gains nothing.
-constexpr int kFbUp = 2, kKwUp = 1;
-constexpr int kFbDown = 2, kKwDown = 4;
+template <> struct StreamCfg<bf16> { static constexpr int U = 2, KC = 4; };
+template <> struct StreamCfg<float> { static constexpr int U = 1, KC = 2; };
+constexpr int kStreamWaves = 4;
+
+// Orders this wave's LDS writes before the barrier and the other waves' LDS
+// reads after it, without waiting for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---- packing
 // Gate/up of expert e: PGU[e][F/16][d/32][2][64][8] from gate/up [e][F][d].
@@ -103,155 +104,143 @@ __global__ void k_pack_down(const T* down, T* out, int d, int F) {
 // ---- streaming products
 // GATEUP: out = act [rows][F] (T), B = PGU, A rows gathered through perm.
 // else:   out = Y   [rows][d] (fp32), B = PD, A rows row_base + r of act.
-// The wave covers K steps [kb, kb + KSw); with KW > 1 the KW waves of a block
-// group add their accumulators through `red` (LDS) and the first one stores.
-template <typename T, bool GATEUP, int RB, int FB, int U, int KW>
+// LDS: two stages of [64 rows][KC*32 + pad] elements; a stage holds K steps
+// [c*KC, (c+1)*KC) of the tile's rows.
+template <typename T, bool GATEUP, int RB, int NW, int U, int KC>
 __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T* Wp, void* out, int e,
-                                            int row_base, int rows, int K, int N, int nb0, int wk, float* red) {
-  const int lane = threadIdx.x & 63, g4 = lane >> 4, c16 = lane & 15;
-  constexpr int NF = GATEUP ? 2 * FB : FB;           // fragments of B per K step
-  const int KS = K / 32, KSw = KS / KW, kb = wk * KSw;
-  const T* arow[RB];
-  bool aval[RB];
+                                            int row_base, int rows, int K, int N, int nb, T* lds) {
+  constexpr int EPR = KC * 32;              // elements of a row per chunk
+  constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int LROW = EPR + VEC;           // padded LDS row (elements)
+  constexpr int SEGS = EPR / VEC;           // pieces per row per chunk
+  constexpr int NT = 64 * NW;
+  constexpr int PIECES = RB * 16 * SEGS;
+  static_assert(NT % SEGS == 0, "a thread's pieces share one column");
+  constexpr int PPT = (PIECES + NT - 1) / NT;
+  constexpr int RSTEP = NT / SEGS;          // rows between a thread's pieces
+  constexpr int STAGE = 64 * LROW;          // elements per LDS stage
+  constexpr int NF = GATEUP ? 2 : 1;        // B fragments per K step
+  constexpr int GPC = KC / U;               // groups per chunk
+  static_assert(GPC % 2 == 0, "the double buffer alternates within a chunk");
+
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
+  const int KS = K / 32, NC = KS / KC;
+  // staging: this thread moves pieces (row r0 + j * RSTEP, column seg) of every chunk
+  const int seg = tid % SEGS, r0 = tid / SEGS;
+  const T* aptr[PPT];
+  bool pok[PPT];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = rb * 16 + c16;
-    aval[rb] = r < rows;
-    const int rr = aval[rb] ? r : 0;
+  for (int j = 0; j < PPT; ++j) {
+    const int r = r0 + j * RSTEP;
+    pok[j] = PIECES % NT == 0 || r < RB * 16;
+    // rows past the tile repeat a real row (their outputs are not stored), so
+    // every staging load is issued
+    const int rr = r < rows ? r : rows - 1;
     const int src = GATEUP ? perm[row_base + rr] : row_base + rr;
-    arow[rb] = X + (size_t)src * K + kb * 32 + g4 * 8;
+    aptr[j] = X + (size_t)src * K + seg * VEC;
   }
-  // per block: base pointer of its packed column of K steps
-  constexpr int blk = (GATEUP ? 2 : 1) * 512;   // elements per (block, K step)
-  const T* bp[FB];
-  bool bval[FB];
+  uint4 st[PPT];
+  auto stage_load = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-  for (int f = 0; f < FB; ++f) {
-    const int nb = nb0 + f;
-    bval[f] = nb * 16 < N;
-    const int nbc = bval[f] ? nb : 0;
-    bp[f] = Wp + (size_t)e * (GATEUP ? 2 : 1) * N * K + ((size_t)nbc * KS + kb) * blk + lane * 8;
-  }
+    for (int j = 0; j < PPT; ++j) st[j] = *reinterpret_cast<const uint4*>(aptr[j] + (size_t)c * EPR);
+  };
+  auto stage_store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+      if (pok[j]) *reinterpret_cast<uint4*>(lds + buf * STAGE + (r0 + j * RSTEP) * LROW + seg * VEC) = st[j];
+  };
+
+  constexpr int blk = NF * 512;             // elements per (block, K step)
+  const T* bp = Wp + (size_t)e * NF * N * K + (size_t)nb * KS * blk + lane * 8;
   f32x4_t acc[RB][NF];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[rb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  Frag<T> a[2][U][RB], b[2][U][NF];
-  auto load = [&](int buf, int ks0) {
+  Frag<T> b[2][U][NF];
+  auto load_b = [&](int buf, int ks0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NF; ++j) frag_ld(b[buf][u][j], bp + (size_t)(ks0 + u) * blk + j * 512);
+  };
+  // K steps kk .. kk+U-1 of the chunk in LDS stage abuf
+  auto comp = [&](int buf, int abuf, int kk) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ks = ks0 + u;
+      Frag<T> a[RB];
 #pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        if (GATEUP) {
-          frag_ld(b[buf][u][2 * f], bp[f] + (size_t)ks * blk);
-          frag_ld(b[buf][u][2 * f + 1], bp[f] + (size_t)ks * blk + 512);
-        } else {
-          frag_ld(b[buf][u][f], bp[f] + (size_t)ks * blk);
-        }
-      }
+      for (int rb = 0; rb < RB; ++rb)
+        lds_frag(a[rb], lds + abuf * STAGE + (rb * 16 + c16) * LROW + (kk + u) * 32 + g4 * 8);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) frag_ld(a[buf][u][rb], arow[rb] + ks * 32);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) mma16x16x32(acc[rb][j], a[rb], b[buf][u][j]);
     }
   };
-  auto comp = [&](int buf) {
+  // one chunk: stage the next one while its K steps stream; the last chunk
+  // stages nothing and prefetches no weights past the end
+  auto chunk = [&](int c, auto last) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last)::value;
+    if (!LAST) stage_load(c + 1);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) frag_keep(a[buf][u][rb], aval[rb]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int j = 0; j < NF; ++j) mma16x16x32(acc[rb][j], a[buf][u][rb], b[buf][u][j]);
+    for (int g = 0; g < GPC; ++g) {
+      if (!LAST || g + 1 < GPC) load_b((g + 1) & 1, c * KC + (g + 1) * U);
+      comp(g & 1, c & 1, g * U);
     }
+    if (!LAST) stage_store((c + 1) & 1);
+    lds_barrier();
   };
-  // KSw is a multiple of U; groups of U steps, double-buffered
-  load(0, 0);
-  int ks0 = 0;
-  for (; ks0 + U < KSw; ks0 += 2 * U) {
-    load(1, ks0 + U);
-    comp(0);
-    if (ks0 + 2 * U < KSw) load(0, ks0 + 2 * U);
-    comp(1);
-  }
-  if (ks0 < KSw) comp(0);
+  stage_load(0);
+  load_b(0, 0);
+  stage_store(0);
+  lds_barrier();
+  int c = 0;
+  for (; c + 1 < NC; ++c) chunk(c, std::false_type{});
+  chunk(c, std::true_type{});
 
-  if constexpr (KW > 1) {
-    // lane-major slots: entry j of wave wk lives at red[((wk - 1) * NA + j) * 64 + lane]
-    constexpr int NA = RB * NF * 4;
-    if (wk > 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int j = 0; j < NF; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[((wk - 1) * NA + (rb * NF + j) * 4 + i) * 64 + lane] = acc[rb][j][i];
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int v = 1; v < KW; ++v)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int j = 0; j < NF; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][j][i] += red[((v - 1) * NA + (rb * NF + j) * 4 + i) * 64 + lane];
-  }
-
-  // epilogue: the lane holds rows rb*16 + g4*4 + i, column c16 of each block
+  // epilogue: the lane holds rows rb*16 + g4*4 + i, column c16 of the block
+  const int col = nb * 16 + c16;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rb * 16 + g4 * 4 + i;
       if (r >= rows) continue;
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        if (!bval[f]) continue;
-        const int col = (nb0 + f) * 16 + c16;
-        if (GATEUP) {
-          const float g = acc[rb][2 * f][i], u = acc[rb][2 * f + 1][i];
-          Num<T>::store(static_cast<T*>(out) + (size_t)(row_base + r) * N + col, g / (1.0f + expf(-g)) * u);
-        } else {
-          static_cast<float*>(out)[(size_t)(row_base + r) * N + col] = acc[rb][f][i];
-        }
+      if (GATEUP) {
+        const float g = acc[rb][0][i], u = acc[rb][1][i];
+        Num<T>::store(static_cast<T*>(out) + (size_t)(row_base + r) * N + col, g / (1.0f + expf(-g)) * u);
+      } else {
+        static_cast<float*>(out)[(size_t)(row_base + r) * N + col] = acc[rb][0][i];
       }
     }
 }
 
-// Grid: x = N / (16 * FB * 4 / KW) block groups (exact, so every exit below is
-// uniform over the workgroup and all of its waves reach the reduction barrier),
-// y = tile capacity (tiles past n_tiles exit).
-template <typename T, bool GATEUP, int FB, int KW, int U>
-__global__ __launch_bounds__(256) void k_expert_stream(const T* X, const int* perm, const T* Wp, void* out,
-                                                       const int4* tiles, const int* n_tiles, int K, int N) {
-  constexpr int NF = GATEUP ? 2 * FB : FB;
-  constexpr int GW = 4 / KW;                          // block groups per workgroup
-  __shared__ float red[KW > 1 ? GW * (KW - 1) * 4 * NF * 4 * 64 : 1];
+// Grid: x = N / (16 * NW) feature-block groups (exact), y = tile capacity
+// (tiles past n_tiles exit; the exit is uniform over the workgroup, so every
+// wave reaches the same barriers).
+template <typename T, bool GATEUP, int NW, int U, int KC>
+__global__ __launch_bounds__(64 * NW, 2) void k_expert_stream(const T* X, const int* perm, const T* Wp, void* out,
+                                                              const int4* tiles, const int* n_tiles, int K, int N) {
+  __shared__ __attribute__((aligned(16))) T lds[2 * 64 * (KC * 32 + 16 / sizeof(T))];
   const int ti = blockIdx.y;
   if (ti >= *n_tiles) return;
   const int4 td = tiles[ti];
-  const int w = threadIdx.x >> 6, wf = w / KW, wk = w % KW;
-  const int nb0 = (blockIdx.x * GW + wf) * FB;
-  float* r = red + (KW > 1 ? wf * (KW - 1) * 4 * NF * 4 * 64 : 0);
+  const int nb = blockIdx.x * NW + (int)(threadIdx.x >> 6);
   switch ((td.z + 15) >> 4) {
-    case 1: stream_body<T, GATEUP, 1, FB, U, KW>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb0, wk, r); break;
-    case 2: stream_body<T, GATEUP, 2, FB, U, KW>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb0, wk, r); break;
-    case 3: stream_body<T, GATEUP, 3, FB, U, KW>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb0, wk, r); break;
-    default: stream_body<T, GATEUP, 4, FB, U, KW>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb0, wk, r); break;
+    case 1: stream_body<T, GATEUP, 1, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    case 2: stream_body<T, GATEUP, 2, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    case 3: stream_body<T, GATEUP, 3, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    default: stream_body<T, GATEUP, 4, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
   }
 }
 
 }  // namespace
 
 bool expert_stream_ok(int d, int F, int elem_bytes) {
-  const int U = elem_bytes == 2 ? StreamCfg<bf16>::U : StreamCfg<float>::U;
-  // K steps split evenly over the waves in groups of U; whole block groups along N
-  return d % (32 * U * kKwUp) == 0 && F % (32 * U * kKwDown) == 0 && F % (16 * kFbUp * 4 / kKwUp) == 0 &&
-         d % (16 * kFbDown * 4 / kKwDown) == 0;
+  const int KC = elem_bytes == 2 ? StreamCfg<bf16>::KC : StreamCfg<float>::KC;
+  // whole staged chunks along K, whole workgroups of feature blocks along N
+  return d % (32 * KC) == 0 && F % (32 * KC) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamWaves) == 0;
 }
 
 template <typename T>
@@ -269,20 +258,18 @@ hipError_t pack_expert_weights(const T* gate, const T* up, const T* down, T* pgu
 template <typename T>
 hipError_t expert_stream_gateup(const T* X, const int* perm, const T* pgu, T* act, const int4* tiles,
                                 const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
-  const int per_wg = 16 * kFbUp * 4 / kKwUp;
-  dim3 grid(F / per_wg, cap_tiles);
-  hipLaunchKernelGGL((k_expert_stream<T, true, kFbUp, kKwUp, StreamCfg<T>::U>), grid, dim3(256), 0, s, X, perm, pgu, (void*)act, tiles,
-                     n_tiles, d, F);
+  constexpr int NW = kStreamWaves;
+  hipLaunchKernelGGL((k_expert_stream<T, true, NW, StreamCfg<T>::U, StreamCfg<T>::KC>), dim3(F / (16 * NW), cap_tiles),
+                     dim3(64 * NW), 0, s, X, perm, pgu, (void*)act, tiles, n_tiles, d, F);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* tiles, const int* n_tiles,
                               int cap_tiles, int d, int F, hipStream_t s) {
-  const int per_wg = 16 * kFbDown * 4 / kKwDown;
-  dim3 grid(d / per_wg, cap_tiles);
-  hipLaunchKernelGGL((k_expert_stream<T, false, kFbDown, kKwDown, StreamCfg<T>::U>), grid, dim3(256), 0, s, act, (const int*)nullptr, pd,
-                     (void*)Y, tiles, n_tiles, F, d);
+  constexpr int NW = kStreamWaves;
+  hipLaunchKernelGGL((k_expert_stream<T, false, NW, StreamCfg<T>::U, StreamCfg<T>::KC>), dim3(d / (16 * NW), cap_tiles),
+                     dim3(64 * NW), 0, s, act, (const int*)nullptr, pd, (void*)Y, tiles, n_tiles, F, d);
   return hipGetLastError();
 }
 
