@@ -100,6 +100,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS hand-overs: orders this wave's LDS writes before
+// the barrier and the other waves' LDS reads after it (s_waitcnt lgkmcnt(0);
+// s_barrier), without waiting for the wave's outstanding global loads, which
+// __syncthreads() would drain.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
 // (SC'11): ten rounds of two 32x32->64 multiplies, xor with the key and the

@@ -16,23 +16,27 @@
 // fragments: K rows give the A operand of S^T directly, V^T rows that of O^T.
 //
 // Two launch shapes:
-//  * spread (few query blocks, the batch-1 shapes): a workgroup owns 16 * QB
-//    query rows; its NW waves take the key tiles round-robin, streaming K and
-//    V^T fragments straight from memory one tile ahead, and merge their
-//    partial (O, max, sum) through LDS in wave order at the end -- many short
-//    chains instead of a few long ones;
-//  * tiled (many query blocks): a workgroup owns 64 query rows, one wave per
-//    16, and the four waves share each K / V^T tile staged in LDS, prefetched
-//    kPre tiles ahead.
+//  * spread (few query rows per kv head and short contexts, the small batch-1
+//    shape): a workgroup owns 16 * QB query rows; its NW waves take the key
+//    tiles round-robin, streaming K and V^T fragments straight from memory one
+//    tile ahead, and merge their partial (O, max, sum) through LDS in wave
+//    order at the end -- many short chains instead of a few long ones;
+//  * wide (everything else): a workgroup owns 16 * NWQ query rows, one wave
+//    per 16, and the waves share each K / V^T tile staged in LDS (two stages,
+//    the global loads of a tile issued two tiles ahead, one LDS-only barrier
+//    per tile).  Every workgroup of a kv head reads the head's whole key range
+//    (or its split of it), so the K/V bytes a launch moves scale with the
+//    number of query blocks per kv head: 16-row blocks re-read a long context
+//    too often, which is what decides between the two shapes.
 // Long key ranges are further split across workgroups; partial (O, max, sum)
 // are merged in a fixed order by a second kernel.
 #include "dg_kernels.h"
 
+#include <type_traits>
+
 namespace dg {
 
 namespace {
-
-constexpr int kPre = 2;                                // K/V tiles in flight ahead of the MFMAs
 
 // Key order inside a 64-key tile.  Row r of score block kb (S^T = K Q^T, 16
 // keys on the M side) holds key (kb / 2) * 32 + (r / 4) * 8 + (kb % 2) * 4 + r % 4,
@@ -42,14 +46,6 @@ constexpr int kPre = 2;                                // K/V tiles in flight ah
 // is then one contiguous 16-byte read; the sum over keys does not depend on
 // their order.
 __device__ __forceinline__ int tile_key(int kb, int r) { return (kb >> 1) * 32 + (r >> 2) * 8 + (kb & 1) * 4 + (r & 3); }
-
-template <typename T, int HD>
-struct AttnShape {
-  static constexpr int KT = 64;                         // keys per tile
-  static constexpr int LDK = HD + 16 / (int)sizeof(T);  // sK row stride
-  static constexpr int LDV = KT + 16 / (int)sizeof(T);  // sVt row stride
-  static constexpr int kSmem = (KT * LDK + HD * LDV) * (int)sizeof(T);
-};
 
 // Four consecutive operand elements from LDS into fragment slots [off, off+4).
 __device__ __forceinline__ void lds4(Frag<bf16>& f, int half, const bf16* p) {
@@ -88,116 +84,105 @@ __device__ __forceinline__ void store4(T* dst, const float* v) {
   for (int j = 0; j < 4; ++j) Num<T>::store(dst + j, v[j]);
 }
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void k_attn_tiled(AttnArgs a) {
-  using S = AttnShape<T, HD>;
-  __shared__ __attribute__((aligned(16))) char smem[S::kSmem];
-  T* sK = reinterpret_cast<T*>(smem);
-  T* sVt = sK + S::KT * S::LDK;
+// ---- wide: 16 * NWQ query rows per workgroup sharing LDS-staged K / V^T tiles
+template <typename T, int HD, int NWQ>
+__global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
+  constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
+  constexpr int NT = sizeof(T) == 2 ? 2 : 1;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int LDK = HD + EPC, LDV = KT + EPC;
+  constexpr int KBUF = KT * LDK, VBUF = HD * LDV;     // elements per stage
+  constexpr int NTH = 64 * NWQ;
+  constexpr int CH_PER_KEY = HD / EPC;
+  constexpr int KCH = KT * CH_PER_KEY / NTH, VCH = HD * (KT / EPC) / NTH;
+  static_assert(KCH >= 1 && VCH >= 1 && KT * CH_PER_KEY % NTH == 0 && HD * (KT / EPC) % NTH == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) T smem[2 * (KBUF + VBUF)];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
-  const int G = a.Hq / a.Hkv;
-  const int rows_total = G * a.nq;
-  const int bk = blockIdx.y;                  // request * Hkv + kv head
-  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
-  const int split = blockIdx.z;
-  const int rho0 = blockIdx.x * 64;
-  if (rho0 >= rows_total) return;
-
-  // this lane's query row
+  const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
+  const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv, split = blockIdx.z;
+  const int rho0 = blockIdx.x * 16 * NWQ;
   const int rho = rho0 + w * 16 + q16;
   const bool qvalid = rho < rows_total;
   const int hh = qvalid ? rho / a.nq : 0, qi = qvalid ? rho % a.nq : 0;
-  const int head = kvh * G + hh;
-  const int qpos = a.ctx + qi;
-
-  // key range of this workgroup
+  const int head = kvh * G + hh, qpos = a.ctx + qi;
   const int total = a.ctx + a.nq;
   int klimit = total;
   if (a.causal) {
-    const int last = min(rho0 + 63, rows_total - 1);
+    const int last = min(rho0 + 16 * NWQ - 1, rows_total - 1);
     const int imax = (rho0 / a.nq == last / a.nq) ? last % a.nq : a.nq - 1;
     klimit = a.ctx + imax + 1;
   }
-  const int per = ((total + a.splits - 1) / a.splits + S::KT - 1) / S::KT * S::KT;
-  const int kbeg = split * per;
-  const int kend = min(klimit, kbeg + per);
+  const int per = ((total + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+  const int kbeg = split * per, kend = min(klimit, kbeg + per);
+  const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
 
   const T* Q = reinterpret_cast<const T*>(a.q);
-  const size_t qstride = (size_t)a.Hq * HD;
-  const size_t qrow = (size_t)(b * a.nq + qi) * qstride + (size_t)head * HD;
-  Frag<T> qf[HD / 32];
+  const size_t qrow = (size_t)(b * a.nq + qi) * a.Hq * HD + (size_t)head * HD;
+  Frag<T> qf[NS];
 #pragma unroll
-  for (int s = 0; s < HD / 32; ++s) {
+  for (int s = 0; s < NS; ++s) {
     if (qvalid) {
-      lds_frag(qf[s], Q + qrow + s * 32 + g4 * 8);   // global read, same shape as an LDS fragment
+      lds_frag(qf[s], Q + qrow + s * 32 + g4 * 8);
     } else {
       float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       set_p(qf[s], z);
     }
   }
-
   const T* Kc = reinterpret_cast<const T*>(a.kc) + ((size_t)b * a.Hkv + kvh) * a.kv_stride * HD;
   const T* Vt = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * HD * a.kv_stride;
-
-  f32x4_t o[HD / 16];
+  f32x4_t o[NDB];
 #pragma unroll
-  for (int j = 0; j < HD / 16; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NDB; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CH_PER_KEY = HD / EPC;                  // 16-byte chunks per K row
-  constexpr int KCH = S::KT * CH_PER_KEY / 256;         // K chunks per thread per tile
-  constexpr int VCH = HD * (S::KT / EPC) / 256;         // V^T chunks per thread per tile
-  static_assert(KCH >= 1 && VCH >= 1, "tile shape");
-  const int ntiles = kend > kbeg ? (kend - kbeg + S::KT - 1) / S::KT : 0;
-  uint4 kr0[KCH], vr0[VCH], kr1[KCH], vr1[VCH];     // two register slots (tiles t and t + 1)
-  auto gload = [&](uint4 (&kr)[KCH], uint4 (&vr)[VCH], int t) __attribute__((always_inline)) {
-    const int k0 = kbeg + min(t, ntiles - 1) * S::KT;       // past the end: reload the last tile
+  uint4 kr0[KCH], vr0[VCH], kr1[KCH], vr1[VCH];
+  // K rows past the range are clamped to its last key; V^T rows are padded to
+  // whole tiles (finite past the context), so every load is in bounds
+  auto gload = [&](auto slot, int t) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    const int k0 = kbeg + t * KT;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, key = min(k0 + c / CH_PER_KEY, kend - 1);
-      kr[i] = *reinterpret_cast<const uint4*>(Kc + (size_t)key * HD + (c % CH_PER_KEY) * EPC);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {        // V^T rows are padded to whole tiles (finite past the context)
-      const int c = tid + 256 * i, d = c / (S::KT / EPC), kc = (c % (S::KT / EPC)) * EPC;
-      vr[i] = *reinterpret_cast<const uint4*>(Vt + (size_t)d * a.kv_stride + k0 + kc);
-    }
-  };
-  auto sstore = [&](const uint4 (&kr)[KCH], const uint4 (&vr)[VCH]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sK + (c / CH_PER_KEY) * S::LDK + (c % CH_PER_KEY) * EPC) = kr[i];
+      const int c = tid + NTH * i, key = min(k0 + c / CH_PER_KEY, kend - 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(Kc + (size_t)key * HD + (c % CH_PER_KEY) * EPC);
+      if constexpr (SL == 0) kr0[i] = v; else kr1[i] = v;
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sVt + (c / (S::KT / EPC)) * S::LDV + (c % (S::KT / EPC)) * EPC) = vr[i];
+      const int c = tid + NTH * i, d = c / (KT / EPC), kc = (c % (KT / EPC)) * EPC;
+      const uint4 v = *reinterpret_cast<const uint4*>(Vt + (size_t)d * a.kv_stride + k0 + kc);
+      if constexpr (SL == 0) vr0[i] = v; else vr1[i] = v;
     }
   };
-  if (ntiles > 0) {
-    gload(kr0, vr0, 0);
-    gload(kr1, vr1, 1);
-  }
-
-  // one tile: store the slot holding tile t, refill it with tile t + 2
-  auto tile = [&](uint4 (&kr)[KCH], uint4 (&vr)[VCH], int t) __attribute__((always_inline)) {
-    const int k0 = kbeg + t * S::KT;
-    sstore(kr, vr);
-    gload(kr, vr, t + kPre);
-    __syncthreads();
-
+  auto sstore = [&](auto slot, int buf) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    T* sK = smem + buf * (KBUF + VBUF);
+    T* sV = sK + KBUF;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + NTH * i;
+      *reinterpret_cast<uint4*>(sK + (c / CH_PER_KEY) * LDK + (c % CH_PER_KEY) * EPC) = SL == 0 ? kr0[i] : kr1[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + NTH * i;
+      *reinterpret_cast<uint4*>(sV + (c / (KT / EPC)) * LDV + (c % (KT / EPC)) * EPC) = SL == 0 ? vr0[i] : vr1[i];
+    }
+  };
+  auto compute = [&](int buf, int t) __attribute__((always_inline)) {
+    const T* sK = smem + buf * (KBUF + VBUF);
+    const T* sV = sK + KBUF;
+    const int k0 = kbeg + t * KT;
     // scores S^T[key][query] for the 64 keys of the tile
     f32x4_t sc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < HD / 32; ++s) {
+      for (int s = 0; s < NS; ++s) {
         Frag<T> kf;
-        lds_frag(kf, sK + tile_key(kb, q16) * S::LDK + s * 32 + g4 * 8);
+        lds_frag(kf, sK + tile_key(kb, q16) * LDK + s * 32 + g4 * 8);
         mma16x16x32(sc[kb], kf, qf[s]);
       }
     }
@@ -227,14 +212,12 @@ __global__ __launch_bounds__(256) void k_attn_tiled(AttnArgs a) {
     l_run = l_run * alpha + lsum;
     m_run = m_new;
 #pragma unroll
-    for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
-
+    for (int j = 0; j < NDB; ++j) o[j] *= alpha;
     // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps.  With bf16
     // operands the fp32 probabilities are split into a bf16 head and a bf16
     // remainder (two MFMAs, ~16 significant bits): a single bf16 rounding of P
     // would dominate the output error, while beyond 16 bits the fp32 summation
     // over the keys does (a third term was measured to change nothing).
-    constexpr int NT = sizeof(T) == 2 ? 2 : 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       Frag<T> pf[NT];
@@ -246,20 +229,49 @@ __global__ __launch_bounds__(256) void k_attn_tiled(AttnArgs a) {
       }
       split_p(pf, rest);
 #pragma unroll
-      for (int db = 0; db < HD / 16; ++db) {
+      for (int db = 0; db < NDB; ++db) {
         Frag<T> vf;
-        lds_frag(vf, sVt + (db * 16 + q16) * S::LDV + ks * 32 + g4 * 8);
+        lds_frag(vf, sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
 #pragma unroll
         for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
       }
     }
-    __syncthreads();
   };
-  static_assert(kPre == 2, "two register slots");
-  for (int t0 = 0; t0 < ntiles; t0 += kPre) {
-    tile(kr0, vr0, t0);
-    if (t0 + 1 < ntiles) tile(kr1, vr1, t0 + 1);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // tile t: its data came through register slot t % 2 into LDS stage t % 2.
+  // Tile t + 2 is loaded into slot t % 2 while tile t is computed; tile t + 1
+  // (slot (t + 1) % 2, loaded during tile t - 1) is staged at the end.
+  if (ntiles > 0) {
+    gload(S0{}, 0);
+    gload(S1{}, min(1, ntiles - 1));
+    sstore(S0{}, 0);
+    lds_barrier();
   }
+  int t = 0;
+  for (; t + 3 < ntiles; t += 2) {          // every load here exists
+    gload(S0{}, t + 2);
+    compute(0, t);
+    sstore(S1{}, 1);
+    lds_barrier();
+    gload(S1{}, t + 3);
+    compute(1, t + 1);
+    sstore(S0{}, 0);
+    lds_barrier();
+  }
+  // at most three tiles left (t even): loads only for tiles that exist
+  if (t < ntiles) {
+    if (t + 2 < ntiles) gload(S0{}, t + 2);
+    compute(0, t);
+    if (t + 1 < ntiles) sstore(S1{}, 1);
+    lds_barrier();
+  }
+  if (t + 1 < ntiles) {
+    compute(1, t + 1);
+    if (t + 2 < ntiles) sstore(S0{}, 0);
+    lds_barrier();
+  }
+  if (t + 2 < ntiles) compute(0, t + 2);
 
   // full row sum across the four lane groups holding the same query
   l_run += __shfl_xor(l_run, 16, 64);
@@ -270,14 +282,14 @@ __global__ __launch_bounds__(256) void k_attn_tiled(AttnArgs a) {
     T* out = reinterpret_cast<T*>(a.out) + qrow;
     const float inv = 1.f / l_run;
 #pragma unroll
-    for (int db = 0; db < HD / 16; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
       store4(out + db * 16 + g4 * 4, v);
     }
   } else {
     float* po = a.part_o + ((size_t)split * a.B * a.nq * a.Hq + rowid) * HD;
 #pragma unroll
-    for (int db = 0; db < HD / 16; ++db)
+    for (int db = 0; db < NDB; ++db)
       *reinterpret_cast<float4*>(po + db * 16 + g4 * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
     if (g4 == 0) {
       float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
@@ -514,22 +526,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   store4(out, v);
 }
 
-// Launch shape: spread while the 64-row query blocks cannot fill the chip.
-constexpr int kSpreadNW = 4, kSpreadQB = 1;
-inline bool use_spread(int B, int nq, int Hq, int Hkv) {
-  return ((Hq / Hkv) * nq + 63) / 64 * B * Hkv < 128;
+// Launch shape.  Spread while the K/V bytes its 16-row query blocks re-read
+// stay small (measured on MI355X: 768 keys, 16/4 heads x 64, 50 MB: spread
+// 10.4 us against 13.1 us wide); wide otherwise (2304 keys, 16/8 x 128:
+// 51.8 -> 29.1 us; 9216 keys, 16/4 x 64: 80.8 -> 44.5 us; 32 requests x 4352
+// keys: 842 -> 414 us).
+constexpr int kSpreadNW = 4, kSpreadQB = 1, kWideNWQ = 8;
+constexpr double kSpreadMaxBytes = 128.0 * (1 << 20);
+inline bool use_spread(int B, int nq, int Hq, int Hkv, int hd, int keys) {
+  const double blocks = (double)(((Hq / Hkv) * nq + 15) / 16) * B * Hkv;
+  return blocks * keys * hd * 4.0 <= kSpreadMaxBytes && ((Hq / Hkv) * nq + 63) / 64 * B * Hkv < 128;
 }
 
 template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  if (use_spread(a.B, a.nq, a.Hq, a.Hkv)) {
+  if (use_spread(a.B, a.nq, a.Hq, a.Hkv, HD, a.ctx + a.nq)) {
     constexpr int NW = kSpreadNW, QB = kSpreadQB;
     dim3 grid((G * a.nq + 16 * QB - 1) / (16 * QB), a.B * a.Hkv, a.splits);
     hipLaunchKernelGGL((k_attn_spread<T, HD, NW, QB>), grid, dim3(64 * NW), 0, s, a);
   } else {
-    dim3 grid((G * a.nq + 63) / 64, a.B * a.Hkv, a.splits);
-    hipLaunchKernelGGL((k_attn_tiled<T, HD>), grid, dim3(256), 0, s, a);
+    constexpr int NWQ = kWideNWQ;
+    dim3 grid((G * a.nq + 16 * NWQ - 1) / (16 * NWQ), a.B * a.Hkv, a.splits);
+    hipLaunchKernelGGL((k_attn_wide<T, HD, NWQ>), grid, dim3(64 * NWQ), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
@@ -541,17 +560,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 // Key splits (and the merge launch they need): spread -- at most 8 tiles per
-// wave; tiled -- only where a workgroup would walk more than 16 tiles, and only
-// as far as filling the chip asks.
-int attention_splits(int B, int nq, int Hq, int Hkv, int keys) {
+// wave; wide -- only as many as filling the chip (~256 workgroups) asks, with
+// at least four tiles per split.
+int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys) {
   const int tiles = (keys + 63) / 64;
   int splits;
-  if (use_spread(B, nq, Hq, Hkv)) {
+  if (use_spread(B, nq, Hq, Hkv, hd, keys)) {
     splits = (tiles + 8 * kSpreadNW - 1) / (8 * kSpreadNW);
   } else {
-    const int wg = ((Hq / Hkv) * nq + 63) / 64 * B * Hkv;
+    const int wg = ((Hq / Hkv) * nq + 16 * kWideNWQ - 1) / (16 * kWideNWQ) * B * Hkv;
     splits = (256 + wg - 1) / wg;
-    const int max_by_keys = (tiles + 15) / 16;
+    const int max_by_keys = tiles / 4;
     if (splits > max_by_keys) splits = max_by_keys;
   }
   if (splits > 16) splits = 16;

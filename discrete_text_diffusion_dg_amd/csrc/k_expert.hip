@@ -53,14 +53,6 @@ template <> struct StreamCfg<bf16> { static constexpr int U = 2, KC = 4; };
 template <> struct StreamCfg<float> { static constexpr int U = 1, KC = 2; };
 constexpr int kStreamWaves = 4;
 
-// Orders this wave's LDS writes before the barrier and the other waves' LDS
-// reads after it, without waiting for outstanding global loads.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---- packing
 // Gate/up of expert e: PGU[e][F/16][d/32][2][64][8] from gate/up [e][F][d].
 template <typename T>
