@@ -447,7 +447,8 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   const int k = c.top_k, F = c.ffn_hidden, M = st->B * nq;
   const int nqkv = (Hq + 2 * Hkv) * hd;
   T* xn = static_cast<T*>(st->xn);
-  if ((size_t)M * std::max(nqkv, std::max(d, E)) > st->part_floats)
+  if ((size_t)M * std::max(nqkv, std::max(d, E)) > st->part_floats ||
+      (size_t)router_ksplits(M, d, E) * M * E > st->part_floats)
     return fail(DG_ERR_CAPACITY, "partial buffer too small for %d rows", M);
   {
     StageTimer tm(st, DG_STAGE_EMBED, s);
@@ -497,8 +498,10 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       StageTimer tm(st, DG_STAGE_ROUTER, s);
       float* rlog = st->rlog + (size_t)l * st->R * E;
       int* ridx = st->ridx + (size_t)l * st->R * k;
+      // the split-K partial buffer is free here (the output projection's
+      // partials were consumed by add_norm); it holds the router's partial logits
       DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
-                       st->tiles, st->n_tiles, st->rcnt, s));
+                       st->tiles, st->n_tiles, st->rcnt, st->part, s));
     }
     // weight streaming while experts see at most ~64 routed rows on average
     // (the batch-1 shapes); the LDS-tiled engine once they see many

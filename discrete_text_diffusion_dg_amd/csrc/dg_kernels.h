@@ -102,11 +102,15 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
                         int Hkv, int hd, int stride, int ctx, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
 // Router of one layer: logits, top-k + softmax weights, and the expert-sorted
-// order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / router_rows_per_block(E)) ints.
+// order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / router_rows_per_block(E)) ints;
+// part: scratch of router_ksplits(M, d, E) * M * E floats (K-split partial logits).
+// Requires d % (32 * kRouterWaves) == 0, E <= 128, k <= 8.
+constexpr int kRouterWaves = 4, kRouterMaxSplits = 8;
 int router_rows_per_block(int E);
+int router_ksplits(int M, int d, int E);
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s);
+                  int* pos, int4* tiles, int* n_tiles, int* cnt, float* part, hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
 hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,

@@ -237,20 +237,25 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
 }
 
 // ------------------------------------------------------------------ router
-// Two launches per layer, no atomics.  k_router: a workgroup owns RPB rows --
-//  1. their router logits on MFMA, the four waves splitting K and adding their
-//     partial sums through LDS in a fixed order;
-//  2. per row, the top k logits -- ties going to the lower expert id -- by
-//     rank counting (E <= 32) or by bisection on unique keys (larger E), then
-//     softmax over the selected;
-//  3. per expert, the count of the block's (row, slot) entries -> cnt[e][blk],
-//     and per entry its rank among the block's entries of that expert, in
-//     (row, slot) order -> pos.
-// k_route_finish (one workgroup) turns the count table into per-block
-// exclusive prefixes (per expert, in place), the expert totals into offsets,
-// writes the 64-row tile list, and the final position of every entry in the
-// expert-sorted order, offset + block prefix + rank, into pos and perm: rows
-// of an expert stay in ascending row order.
+// Three launches per layer, no atomics.
+//  k_router_logits: a workgroup owns 16 rows x 16 experts x one K split; its
+//    waves split that K range, add their MFMA partial sums through LDS in wave
+//    order and store fp32 partial logits.  Spreading the router matrix over
+//    rows x expert blocks x K splits keeps every workgroup's reads small (one
+//    workgroup per 16 rows would stream the whole matrix per CU).
+//  k_router_select: a workgroup owns RPB rows --
+//    1. their logits, the K-split partials added in split order;
+//    2. per row, the top k logits -- ties going to the lower expert id -- by
+//       rank counting (E <= 32) or by bisection on unique keys (larger E),
+//       then softmax over the selected;
+//    3. per expert, the count of the block's (row, slot) entries -> cnt[e][blk],
+//       and per entry its rank among the block's entries of that expert, in
+//       (row, slot) order -> pos.
+//  k_route_finish (one workgroup) turns the count table into per-block
+//    exclusive prefixes (per expert, in place), the expert totals into
+//    offsets, writes the 64-row tile list, and the final position of every
+//    entry in the expert-sorted order, offset + block prefix + rank, into pos
+//    and perm: rows of an expert stay in ascending row order.
 template <typename T>
 __device__ __forceinline__ void router_frag(Frag<T>& f, const T* p);
 template <>
@@ -264,113 +269,120 @@ __device__ __forceinline__ void router_frag(Frag<float>& f, const float* p) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
-// NCB = ceil(E / 16) column blocks of logits (a template parameter, so every
-// operand load is unconditional).
 // Top k of one row (E <= 128 logits in LDS) by one wave: keys (order-preserving
-// bits of the logit, then 127 - expert) are unique, so the k-th largest key T
-// is found bit by bit (39 steps, a wave ballot count each) and exactly k keys
-// are >= T; the slot of each is the number of keys above it.
+// bits of the logit, then 127 - expert) are unique, so k rounds of a wave-wide
+// maximum pick the slots in order -- largest logit first, ties to the lower
+// expert id.  A lane holds experts lane and lane + 64.
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
   const uint32_t u = __float_as_uint(v);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)o << 7) | (uint64_t)(127 - e);
 }
-__device__ __forceinline__ void topk_bisect(const float* row, int E, int k, int lane, int* sel_e, float* sel_v) {
-  const bool h0 = lane < E, h1 = lane + 64 < E;
-  const float v0 = h0 ? row[lane] : 0.f, v1 = h1 ? row[lane + 64] : 0.f;
-  const uint64_t k0 = h0 ? route_key(v0, lane) : 0ull, k1 = h1 ? route_key(v1, lane + 64) : 0ull;
-  uint64_t T = 0;
-  for (int bit = 38; bit >= 0; --bit) {
-    const uint64_t c = T | (1ull << bit);
-    const int n = __popcll(__ballot(k0 >= c)) + __popcll(__ballot(k1 >= c));
-    if (n >= k) T = c;
-  }
-  uint64_t m0 = __ballot(h0 && k0 >= T), m1 = __ballot(h1 && k1 >= T);
-  while (m0 | m1) {
-    const bool hi = m0 == 0;
-    const int l = __ffsll((unsigned long long)(hi ? m1 : m0)) - 1;
-    if (hi) m1 &= m1 - 1; else m0 &= m0 - 1;
-    const uint64_t ks = __shfl(hi ? k1 : k0, l, 64);
-    const int slot = __popcll(__ballot(k0 > ks)) + __popcll(__ballot(k1 > ks));
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void topk_rounds(const float* row, int E, int k, int lane, int* sel_e, float* sel_v) {
+  bool a0 = lane < E, a1 = lane + 64 < E;
+  const uint64_t k0 = a0 ? route_key(row[lane], lane) : 0ull, k1 = a1 ? route_key(row[lane + 64], lane + 64) : 0ull;
+  for (int slot = 0; slot < k; ++slot) {
+    // remaining keys only; an exhausted lane offers 0, below every remaining key
+    // of another lane unless that key is 0 too, and then the winner check below
+    // still finds the one remaining owner
+    uint64_t m = a0 ? k0 : 0ull;
+    if (a1 && (!a0 || k1 > k0)) m = k1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t x = shfl_xor_u64(m, o);
+      m = x > m ? x : m;
+    }
+    const int e = 127 - (int)(m & 127u);
+    if (a0 && k0 == m) a0 = false;
+    if (a1 && k1 == m) a1 = false;
     if (lane == 0) {
-      sel_e[slot] = hi ? l + 64 : l;
-      sel_v[slot] = row[hi ? l + 64 : l];
+      sel_e[slot] = e;
+      sel_v[slot] = row[e];
     }
   }
 }
 
-template <typename T, int NCB, int RPB, int NW>
-__global__ __launch_bounds__(64 * NW) void k_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog,
-                                                int* idx, float* w, int* pos, int* cnt) {
-  __shared__ float red[NW - 1][NCB * 4][64];
-  __shared__ float lg[16][129];
-  __shared__ int sel_e[RPB][8];
-  __shared__ float sel_v[RPB][8];
-  __shared__ int ent_e[RPB * 8];
+template <typename T, int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_logits(const T* xn, const T* wr, int M, int d, int E, float* part) {
+  __shared__ float red[NW - 1][4][64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, g4 = lane >> 4, c16 = lane & 15;
-  const int r0 = blockIdx.x * RPB;
-  const int KS = d / 32, ks0 = wv * KS / NW, ks1 = (wv + 1) * KS / NW;
-  // MFMA rows c16 >= RPB repeat a valid row; their logits are never read
-  const T* ap = xn + (size_t)min(r0 + min(c16, RPB - 1), M - 1) * d + g4 * 8;
-  const T* bp[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) bp[cb] = wr + (size_t)min(cb * 16 + c16, E - 1) * d + g4 * 8;
-  f32x4_t acc[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // d is a multiple of 256 split over 4 waves, or of 512 split over 8, so each
-  // wave's K range is a multiple of 2 steps: pairs of steps, the next pair's loads in flight while the
-  // current pair is multiplied (clamped to the last pair at the end)
-  Frag<T> a2[2][2], b2[2][2][NCB];
-  auto ld_pair = [&](int buf, int ks) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      router_frag(a2[buf][u], ap + (ks + u) * 32);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) router_frag(b2[buf][u][cb], bp[cb] + (ks + u) * 32);
-    }
-  };
-  auto mm_pair = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) mma16x16x32(acc[cb], a2[buf][u], b2[buf][u][cb]);
-  };
-  ld_pair(0, ks0);
+  const int r0 = blockIdx.x * 16, e0 = blockIdx.y * 16, z = blockIdx.z, ksp = gridDim.z;
+  const int KS = d / 32, KSW = KS / (ksp * NW), ks0 = (z * NW + wv) * KSW, ks1 = ks0 + KSW;
+  // rows past M and experts past E repeat a valid one; their results are not stored
+  const T* ap = xn + (size_t)min(r0 + c16, M - 1) * d + g4 * 8;
+  const T* bp = wr + (size_t)min(e0 + c16, E - 1) * d + g4 * 8;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int ks = ks0; ks < ks1; ks += 4) {
-    ld_pair(1, min(ks + 2, ks1 - 2));
-    mm_pair(0);
-    if (ks + 2 >= ks1) break;
-    ld_pair(0, min(ks + 4, ks1 - 2));
-    mm_pair(1);
+    Frag<T> a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ks + u < ks1) {
+        router_frag(a[u], ap + (ks + u) * 32);
+        router_frag(b[u], bp + (ks + u) * 32);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ks + u < ks1) mma16x16x32(acc, a[u], b[u]);
   }
   if (wv > 0)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wv - 1][cb * 4 + i][lane] = acc[cb][i];
+    for (int i = 0; i < 4; ++i) red[wv - 1][i][lane] = acc[i];
   __syncthreads();
-  if (wv == 0)
+  if (wv != 0) return;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+  for (int i = 0; i < 4; ++i) {
+    float v = acc[i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-        {
-          float v = acc[cb][i];
-#pragma unroll
-          for (int q = 0; q < NW - 1; ++q) v += red[q][cb * 4 + i][lane];
-          lg[g4 * 4 + i][cb * 16 + c16] = v;
-        }
-  __syncthreads();
-
-  const int nrow = min(RPB, M - r0);
-  for (int pr = t; pr < nrow * E; pr += 64 * NW) {
-    const int rl = pr / E, e = pr - rl * E;
-    rlog[(size_t)(r0 + rl) * E + e] = lg[rl][e];
+    for (int q = 0; q < NW - 1; ++q) v += red[q][i][lane];
+    const int r = r0 + g4 * 4 + i, e = e0 + c16;
+    if (r < M && e < E) part[((size_t)z * M + r) * E + e] = v;
   }
+}
+
+template <int RPB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_select(const float* part, int ksp, int M, int E, int k, float* rlog,
+                                                          int* idx, float* w, int* pos, int* cnt) {
+  __shared__ float lg[RPB][129];
+  __shared__ int sel_e[RPB][8];
+  __shared__ float sel_v[RPB][8];
+  __shared__ int ent_e[RPB * 8];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int r0 = blockIdx.x * RPB;
+  const int nrow = min(RPB, M - r0);
+  // every partial of this thread's (row, expert) entries is loaded before any
+  // is added (one round trip), then the splits are summed in order
+  constexpr int EPT = RPB * 128 / (64 * NW);       // entries per thread, at most
+  float pv[EPT][kRouterMaxSplits];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int pr = t + j * 64 * NW;
+    const int rl = pr / E, e = pr - rl * E;
+    const size_t o = (size_t)(r0 + rl) * E + e;
+#pragma unroll
+    for (int z = 0; z < kRouterMaxSplits; ++z)
+      if (pr < nrow * E && z < ksp) pv[j][z] = part[(size_t)z * M * E + o];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int pr = t + j * 64 * NW;
+    if (pr < nrow * E) {
+      const int rl = pr / E, e = pr - rl * E;
+      float v = pv[j][0];
+#pragma unroll
+      for (int z = 1; z < kRouterMaxSplits; ++z)
+        if (z < ksp) v += pv[j][z];
+      lg[rl][e] = v;
+      rlog[(size_t)(r0 + rl) * E + e] = v;
+    }
+  }
+  __syncthreads();
   if (E > 32) {
-    // top-k by bisection, one row per wave
-    for (int rl = wv; rl < nrow; rl += NW) topk_bisect(lg[rl], E, k, lane, sel_e[rl], sel_v[rl]);
+    // top-k by rounds of a wave maximum, one row per wave
+    for (int rl = wv; rl < nrow; rl += NW) topk_rounds(lg[rl], E, k, lane, sel_e[rl], sel_v[rl]);
   } else {
     // top-k by rank: the rank of expert e in its row is the number of logits
     // that beat it (greater, or equal with a lower id); ranks 0..k-1 are slots
@@ -403,26 +415,38 @@ __global__ __launch_bounds__(64 * NW) void k_router(const T* xn, const T* wr, in
     se[t] = e;
   }
   __syncthreads();
-  // rank of each entry among the block's entries of its expert, in entry order
-  if (t < nent) {
-    const int e = se[t];
-    int rank = 0;
-    for (int u = 0; u < t; ++u) rank += se[u] == e;
-    pos[(size_t)r0 * k + t] = rank;
+  // rank of each entry among the block's entries of its expert, in entry order,
+  // and the block's count per expert: eight consecutive lanes share an entry
+  // (an expert), each scanning one sixteenth of the entries, added by shuffles
+  static_assert(64 * NW >= 8 * RPB * 8 && 64 * NW >= 8 * 128, "eight lanes per entry and per expert");
+  const int q = t >> 3, sl = t & 7, u0 = sl * (RPB * 8 / 8), u1 = u0 + RPB * 8 / 8;
+  {
+    const int e = q < nent ? se[q] : -1;
+    int r = 0;
+    for (int u = u0; u < u1 && u < q; ++u) r += se[u] == e;
+    r += __shfl_xor(r, 1, 64);
+    r += __shfl_xor(r, 2, 64);
+    r += __shfl_xor(r, 4, 64);
+    if (q < nent && sl == 0) pos[(size_t)r0 * k + q] = r;
   }
-  const int nblk = gridDim.x;
-  for (int e = t; e < E; e += 64 * NW) {
+  {
     int c = 0;
-    for (int u = 0; u < nent; ++u) c += se[u] == e;
-    cnt[(size_t)e * nblk + blockIdx.x] = c;
+    for (int u = u0; u < u1 && u < nent; ++u) c += se[u] == q;
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    c += __shfl_xor(c, 4, 64);
+    if (q < E && sl == 0) cnt[(size_t)q * gridDim.x + blockIdx.x] = c;
   }
 }
 
 constexpr int kFinishLds = 16384;     // count-table entries kept in LDS by the finish kernel
+constexpr int kFinishThreads = 1024;
 
-__global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int k, int E, int nblk, int rpb,
-                                                      int* cnt, int* perm, int* pos, int4* tiles, int* n_tiles) {
-  __shared__ int seg[256];
+__global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx, int M, int k, int E, int nblk,
+                                                                 int rpb, int* cnt, int* perm, int* pos, int4* tiles,
+                                                                 int* n_tiles) {
+  constexpr int NT = kFinishThreads;
+  __shared__ int seg[NT];
   __shared__ int offs[128], toff[129];
   __shared__ int tab[kFinishLds];
   const int t = threadIdx.x;
@@ -430,13 +454,15 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
   const bool in_lds = E * nblk <= kFinishLds;
   int* ct = in_lds ? tab : cnt;
   if (in_lds) {
-#pragma unroll 8
-    for (int i = t; i < E * nblk; i += 256) tab[i] = cnt[i];
+#pragma unroll 4
+    for (int i = t; i < E * nblk; i += NT) tab[i] = cnt[i];
     __syncthreads();
   }
+  // per expert: tpe threads each sum a run of blocks, then turn their run into
+  // exclusive per-block prefixes
   int ep = 1;
   while (ep < E) ep <<= 1;
-  const int tpe = 256 / ep;                       // threads per expert (>= 2)
+  const int tpe = NT / ep;                        // threads per expert (>= 8)
   const int e = t / tpe, sg = t % tpe;
   const int per = (nblk + tpe - 1) / tpe, b0 = min(nblk, sg * per), b1 = min(nblk, b0 + per);
   int* row = ct + (size_t)(e < E ? e : 0) * nblk;
@@ -453,44 +479,44 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
       row[b] = run;
       run += c;
     }
-    if (sg == 0) {
-      int tot = 0;
-      for (int j = 0; j < tpe; ++j) tot += seg[e * tpe + j];
-      offs[e] = tot;
-    }
+    if (sg == tpe - 1) offs[e] = run;             // the expert's total
   }
   __syncthreads();
-  // exclusive prefixes over experts of the row counts and of the 64-row tile counts
-  if (t == 0) {
-    int acc_rows = 0, acc_tiles = 0;
-    for (int x = 0; x < E; ++x) {
-      const int c = offs[x];
-      offs[x] = acc_rows;
-      toff[x] = acc_tiles;
-      acc_rows += c;
-      acc_tiles += (c + 63) / 64;
+  // exclusive prefixes over experts of the row counts and of the 64-row tile
+  // counts: one wave, two experts per lane, a shuffle scan
+  if (t < 64) {
+    const int x0 = 2 * t, x1 = 2 * t + 1;
+    const int c0 = x0 < E ? offs[x0] : 0, c1 = x1 < E ? offs[x1] : 0;
+    const int n0 = (c0 + 63) / 64, n1 = (c1 + 63) / 64;
+    int rs = c0 + c1, ts = n0 + n1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ro = __shfl_up(rs, o, 64), to = __shfl_up(ts, o, 64);
+      if (t >= o) { rs += ro; ts += to; }
     }
-    toff[E] = acc_tiles;
-    *n_tiles = acc_tiles;
+    const int rx = rs - c0 - c1, tx = ts - n0 - n1;   // exclusive
+    if (x0 < E) { offs[x0] = rx; toff[x0] = tx; }
+    if (x1 < E) { offs[x1] = rx + c0; toff[x1] = tx + n0; }
+    if (t == 63) { toff[E] = ts; *n_tiles = ts; }
   }
   __syncthreads();
-  for (int x = t; x < E; x += 256) {
+  for (int x = t; x < E; x += NT) {
     const int c = (x + 1 < E ? offs[x + 1] : M * k) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
       tiles[toff[x] + q] = make_int4(x, offs[x] + q * 64, min(64, c - q * 64), 0);
   }
   const int MK = M * k;
-  for (int i0 = t; i0 < MK; i0 += 4 * 256) {     // four independent entries in flight per thread
+  for (int i0 = t; i0 < MK; i0 += 4 * NT) {      // four independent entries in flight per thread
     int ex[4], rk[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256;
+      const int i = i0 + u * NT;
       ex[u] = i < MK ? idx[i] : 0;
       rk[u] = i < MK ? pos[i] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256;
+      const int i = i0 + u * NT;
       if (i < MK) {
         const int p = offs[ex[u]] + ct[(size_t)ex[u] * nblk + i / (rpb * k)] + rk[u];
         pos[i] = p;
@@ -500,45 +526,40 @@ __global__ __launch_bounds__(256) void k_route_finish(const int* idx, int M, int
   }
 }
 
-template <typename T, int NW>
-hipError_t launch_router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w,
-                         int* pos, int* cnt, hipStream_t s) {
-  constexpr int RPB = 16;
-  const dim3 grid((M + RPB - 1) / RPB), block(64 * NW);
-  switch ((E + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_router<T, 1, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos,
-                               cnt); break;
-    case 2: hipLaunchKernelGGL((k_router<T, 2, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos,
-                               cnt); break;
-    case 3: case 4:
-      hipLaunchKernelGGL((k_router<T, 4, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt);
-      break;
-    default:
-      hipLaunchKernelGGL((k_router<T, 8, RPB, NW>), grid, block, 0, s, xn, wr, M, d, E, k, rlog, idx, w, pos, cnt);
-      break;
-  }
-  return hipGetLastError();
-}
-
 int router_rows_per_block(int) { return 16; }
+
+// K splits of the logits: enough workgroups to spread the router matrix over
+// the chip (~256), each wave keeping at least one whole K step.
+int router_ksplits(int M, int d, int E) {
+  const int blocks = ((M + 15) / 16) * ((E + 15) / 16);
+  int ksp = 1;
+  while (blocks * ksp < 256 && 2 * ksp <= kRouterMaxSplits && d % (32 * 2 * ksp * kRouterWaves) == 0) ksp *= 2;
+  return ksp;
+}
 
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int* cnt, hipStream_t s) {
+                  int* pos, int4* tiles, int* n_tiles, int* cnt, float* part, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  const int nblk = (M + 15) / 16;
-  // eight waves split K for wide models whose K steps divide into whole pairs per wave
-  hipError_t e = d % 512 == 0 ? launch_router<T, 8>(xn, wr, M, d, E, k, rlog, idx, w, pos, cnt, s)
-                          : launch_router<T, 4>(xn, wr, M, d, E, k, rlog, idx, w, pos, cnt, s);
+  if (d % (32 * kRouterWaves) != 0 || E > 128 || k > 8) return hipErrorInvalidValue;
+  constexpr int RPB = 16;
+  const int nblk = (M + RPB - 1) / RPB, ksp = router_ksplits(M, d, E);
+  hipLaunchKernelGGL((k_router_logits<T, kRouterWaves>), dim3(nblk, (E + 15) / 16, ksp), dim3(64 * kRouterWaves), 0, s,
+                     xn, wr, M, d, E, part);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(256), 0, s, idx, M, k, E, nblk, 16, cnt, perm, pos, tiles,
-                     n_tiles);
+  hipLaunchKernelGGL((k_router_select<RPB, 16>), dim3(nblk), dim3(1024), 0, s, part, ksp, M, E, k, rlog, idx, w, pos,
+                     cnt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), 0, s, idx, M, k, E, nblk, RPB, cnt, perm, pos,
+                     tiles, n_tiles);
   return hipGetLastError();
 }
 template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,
-                                  int4*, int*, int*, hipStream_t);
+                                  int4*, int*, int*, float*, hipStream_t);
 template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, float*, int*, float*, int*, int*,
-                                 int4*, int*, int*, hipStream_t);
+                                 int4*, int*, int*, float*, hipStream_t);
 
 // ------------------------------------------------------------------ transpose
 template <typename T>
