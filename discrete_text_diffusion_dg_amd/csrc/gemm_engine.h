@@ -290,7 +290,7 @@ __device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[C::FM][C::FN],
 }
 
 template <class C, typename T, class SCHED, class AL, class BL, class EP>
-__global__ __launch_bounds__(256) void k_gemm(SCHED sc, AL al, BL bl, EP ep) {
+__global__ __launch_bounds__(256, 2) void k_gemm(SCHED sc, AL al, BL bl, EP ep) {
   __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
   TileCtx t;
   if (!sc.get(blockIdx.x, t)) return;
