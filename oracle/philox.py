@@ -11,8 +11,10 @@ Stream layout (a choice of this project; the pages only say randomness drives
 the initial canvas, the sampled tokens and the re-noising, [mlqm] sections 一, 四):
   key     = (low 32 bits of the request seed, high 32 bits of the request seed)
   counter = (j >> 2, position, step, tag << 24 | canvas index), output word j & 3
-  tags: INIT (initial canvas, j = 0, step 0), GUMBEL (j = vocabulary id),
-        RENOISE (j = 0)
+  tags: INIT (initial canvas, j = 0, step 0), RENOISE (j = 0), GUMBEL (one
+        word per vocabulary id v, laid out per aligned group of 64 ids: counter
+        word 0 = 16 * (v >> 6) + (v & 15), output word (v >> 4) & 3 -- see
+        sampler.gumbel_call_of)
 """
 from __future__ import annotations
 

@@ -45,17 +45,29 @@ def inv_temperature(T: np.float32) -> np.float32:
     return np.float32(1.0 / float(T))
 
 
+def gumbel_call_of(v: np.ndarray):
+    """(counter word 0, output word) of vocabulary id v in the GUMBEL stream.
+
+    Each aligned group of 64 ids is served by 16 Philox calls: id v takes output
+    word (v >> 4) & 3 of the call whose first counter word is 16 * (v >> 6) + (v & 15),
+    so ids c, c + 16, c + 32, c + 48 of a group share one call.
+    """
+    v = np.asarray(v, np.int64)
+    return (((v >> 6) << 4) | (v & 15)), ((v >> 4) & 3)
+
+
 def gumbel_block(seed: int, canvas: int, step: int, pos: np.ndarray, vocab: int) -> np.ndarray:
     """Gumbel noise g[len(pos), vocab] (fp32) of the GUMBEL stream at one step."""
     pos = np.asarray(pos, np.int64)
-    nblk = (vocab + 3) // 4
-    ctr = np.empty((pos.size, nblk, 4), np.uint32)
-    ctr[..., 0] = np.arange(nblk, dtype=np.uint32)[None, :]
+    call, word = gumbel_call_of(np.arange(vocab))
+    ncall = int(call.max()) + 1
+    ctr = np.empty((pos.size, ncall, 4), np.uint32)
+    ctr[..., 0] = np.arange(ncall, dtype=np.uint32)[None, :]
     ctr[..., 1] = pos.astype(np.uint32)[:, None]
     ctr[..., 2] = np.uint32(step)
     ctr[..., 3] = np.uint32((philox.TAG_GUMBEL << 24) | (canvas & 0xFFFFFF))
-    w = philox.philox4x32_10(ctr, philox.seed_key(seed)).reshape(pos.size, nblk * 4)[:, :vocab]
-    return philox.gumbel(w)
+    out = philox.philox4x32_10(ctr, philox.seed_key(seed))          # [pos, call, 4]
+    return philox.gumbel(out[:, call, word])
 
 
 def head_stats(logits: np.ndarray, inv_t: np.float32, seed: int, canvas: int, step: int,

@@ -53,8 +53,22 @@ def test_stream_layout_words():
     key = np.array([5, 7], np.uint32)
     ref = np.concatenate([philox.philox4x32_10(ctr0, key), philox.philox4x32_10(ctr1, key)])
     assert np.array_equal(w, ref)
-    g = smp.gumbel_block(seed, 3, 9, np.array([11]), 8)[0]
-    assert np.array_equal(g, philox.gumbel(ref))
+
+
+def test_gumbel_stream_layout():
+    # hand-listed (vocabulary id -> counter word 0, output word) of the GUMBEL stream
+    cases = {0: (0, 0), 5: (5, 0), 16: (0, 1), 33: (1, 2), 63: (15, 3), 64: (16, 0), 80: (16, 1),
+             127: (31, 3), 200: (56, 0), 4095: (1023, 3)}
+    seed, canvas, step, pos = (7 << 32) | 5, 3, 9, 11
+    key = np.array([5, 7], np.uint32)
+    g = smp.gumbel_block(seed, canvas, step, np.array([pos]), 4096)[0]
+    for v, (c0, word) in cases.items():
+        ctr = np.array([c0, pos, step, (philox.TAG_GUMBEL << 24) | canvas], np.uint32)
+        assert g[v] == philox.gumbel(philox.philox4x32_10(ctr, key)[word:word + 1])[0], v
+    # every id of a 4096-id range draws its own word: (call, word) pairs are all distinct
+    call, word = smp.gumbel_call_of(np.arange(4096))
+    assert len(set(zip(call.tolist(), word.tolist()))) == 4096
+    assert call.max() == 1023
 
 
 def test_uniform01_range_and_exactness():
