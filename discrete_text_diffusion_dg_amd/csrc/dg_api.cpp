@@ -71,7 +71,7 @@ struct dg_state {
   const dg_model* m;
   int B, max_ctx, n, R;  // R = B * n rows per pass
   int ctx = 0, canvas_index = 0;
-  int chunks, clen, attn_splits_max, cap_tiles;
+  int chunks, attn_splits_max, cap_tiles;   // chunks: 128-id vocabulary chunks of the head statistics
   int ctx_pad;            // max_ctx rounded up to the 64-key attention tile: K/V row stride
   size_t kv_layer_elems;  // B * Hkv * ctx_pad * hd
   // persistent
@@ -79,8 +79,8 @@ struct dg_state {
   // workspace
   float* h; void* xn; float* part; size_t part_floats; void* q; void* attn; float* attn_po; float* attn_pml;
   float* rlog; int* ridx; float* rw; int* perm; int* pos; int4* tiles; int* rcnt;
-  int* n_tiles; void* act; float* y; float* logits; HeadPart* hp; float* chunk_scale;
-  void* ptilde; float* sc_part; int sc_sub; int32_t* tok;
+  int* n_tiles; void* act; float* y; HeadPart* hp; float* chunk_scale;
+  void* ptilde; float* sc_part; int sc_splits, sc_kchunk; int32_t* tok;
   size_t total_bytes;
   // stage timing (dg_profile_enable): event pairs from a fixed pool
   uint32_t prof_mask = 0;
@@ -245,20 +245,26 @@ struct Layout {
 
 struct Offsets {
   size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos, rcnt,
-      tiles, n_tiles, act, y, logits, hp, chunk_scale, ptilde, sc_part, tok, total;
+      tiles, n_tiles, act, y, hp, chunk_scale, ptilde, sc_part, tok, total;
   size_t part_floats;
-  int chunks, clen, splits, cap_tiles, sc_sub;
+  int chunks, splits, cap_tiles, sc_splits, sc_kchunk;
 };
 
-// K-slices of one sampler chunk in the softmax @ E contraction: enough
-// workgroups to fill the chip, each slice at least four 128-byte K steps.
-int selfcond_sub(int R, int d, int chunks, int clen, int esz) {
+// K splits of the softmax @ E contraction (K = vocabulary): enough workgroups
+// to fill the chip (~512), each split at least four 128-byte K steps.  The
+// chunk scales are applied in the operand loader, so splits need not follow
+// the 128-id chunks.
+void selfcond_plan(int R, int d, int V, int esz, int* splits, int* kchunk) {
   const int bm = (R >= 128 && d >= 128) ? 128 : 64;
   const int tiles = ((R + bm - 1) / bm) * ((d + bm - 1) / bm);
   const int bk = 128 / esz;
-  int sub = 1;
-  while (tiles * chunks * sub < 512 && clen % (sub * 2 * bk) == 0 && clen / (sub * 2) >= 4 * bk) sub *= 2;
-  return sub;
+  int sp = (512 + tiles - 1) / tiles;
+  const int max_sp = V / (4 * bk);
+  if (sp > max_sp) sp = max_sp;
+  if (sp < 1) sp = 1;
+  const int kc = ((V + sp - 1) / sp + bk - 1) / bk * bk;
+  *kchunk = kc;
+  *splits = (V + kc - 1) / kc;
 }
 
 Offsets layout(const dg_model* m, int B, int max_ctx) {
@@ -267,8 +273,8 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   const int n = c.canvas_len, R = B * n, d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int nqkv = (Hq + 2 * Hkv) * hd, k = c.top_k, E = c.n_experts, F = c.ffn_hidden, V = c.vocab;
   Offsets o;
-  o.chunks = sampler_chunks(V);
-  o.clen = sampler_chunk_len(V, o.chunks);
+  o.chunks = head_chunks(V);
+  selfcond_plan(R, d, V, (int)es, &o.sc_splits, &o.sc_kchunk);
   o.splits = 16;
   o.cap_tiles = expert_tile_capacity(R, k, E);
   Layout L;
@@ -298,12 +304,10 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.rcnt = L.take((size_t)E * ((R + router_rows_per_block(E) - 1) / router_rows_per_block(E)) * 4);  // router counts
   o.act = L.take((size_t)R * k * F * es);
   o.y = L.take((size_t)R * k * d * 4);
-  o.logits = L.take((size_t)R * V * 4);
   o.hp = L.take((size_t)R * o.chunks * sizeof(HeadPart));
   o.chunk_scale = L.take((size_t)R * o.chunks * 4);
   o.ptilde = c.self_cond ? L.take((size_t)R * V * es) : 0;
-  o.sc_sub = selfcond_sub(R, d, o.chunks, o.clen, (int)es);
-  o.sc_part = c.self_cond ? L.take((size_t)o.chunks * o.sc_sub * R * d * 4) : 0;
+  o.sc_part = c.self_cond ? L.take((size_t)o.sc_splits * R * d * 4) : 0;
   o.tok = L.take((size_t)R * 4);
   o.total = L.off;
   return o;
@@ -331,13 +335,14 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   dg_state* s = new dg_state();
   char* b = static_cast<char*>(buf);
   s->m = m; s->B = batch; s->max_ctx = max_ctx; s->n = m->cfg.canvas_len; s->R = batch * s->n;
-  s->chunks = o.chunks; s->clen = o.clen; s->attn_splits_max = o.splits; s->cap_tiles = o.cap_tiles;
+  s->chunks = o.chunks; s->attn_splits_max = o.splits; s->cap_tiles = o.cap_tiles;
   s->ctx_pad = (max_ctx + 63) / 64 * 64;
   s->kv_layer_elems = (size_t)batch * m->cfg.n_kv_heads * s->ctx_pad * m->cfg.head_dim;
   s->kc = b + o.kc; s->vc = b + o.vc; s->rope = reinterpret_cast<float2*>(b + o.rope);
   s->s = reinterpret_cast<float*>(b + o.s); s->prev_am = reinterpret_cast<int32_t*>(b + o.prev_am);
   s->h = reinterpret_cast<float*>(b + o.h); s->xn = b + o.xn;
-  s->part = reinterpret_cast<float*>(b + o.part); s->part_floats = o.part_floats; s->sc_sub = o.sc_sub;
+  s->part = reinterpret_cast<float*>(b + o.part); s->part_floats = o.part_floats;
+  s->sc_splits = o.sc_splits; s->sc_kchunk = o.sc_kchunk;
   s->q = b + o.q; s->attn = b + o.attn;
   s->attn_po = reinterpret_cast<float*>(b + o.attn_po); s->attn_pml = reinterpret_cast<float*>(b + o.attn_pml);
   s->rlog = reinterpret_cast<float*>(b + o.rlog); s->ridx = reinterpret_cast<int*>(b + o.ridx);
@@ -345,7 +350,7 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->perm = reinterpret_cast<int*>(b + o.perm); s->pos = reinterpret_cast<int*>(b + o.pos);
   s->tiles = reinterpret_cast<int4*>(b + o.tiles); s->n_tiles = reinterpret_cast<int*>(b + o.n_tiles);
   s->rcnt = reinterpret_cast<int*>(b + o.rcnt);
-  s->act = b + o.act; s->y = reinterpret_cast<float*>(b + o.y); s->logits = reinterpret_cast<float*>(b + o.logits);
+  s->act = b + o.act; s->y = reinterpret_cast<float*>(b + o.y);
   s->hp = reinterpret_cast<HeadPart*>(b + o.hp); s->chunk_scale = reinterpret_cast<float*>(b + o.chunk_scale);
   s->ptilde = m->cfg.self_cond ? b + o.ptilde : nullptr;
   s->sc_part = m->cfg.self_cond ? reinterpret_cast<float*>(b + o.sc_part) : nullptr;
@@ -554,31 +559,45 @@ float step_temperature(const dg_sampler_params* p, int step) {
   return (float)(t0 + (t1 - t0) * (double)step / (double)(p->max_steps - 1));
 }
 
-// Sampler stage on R rows of logits: head statistics, outputs, and (self-
-// conditioning models) the next step's self-conditioning vector.
+// Sampler stage after the head statistics: the per-row merge (entropy, sample,
+// arg-max, margin) and, for self-conditioning models, the next step's
+// self-conditioning vector softmax(z) @ E.
 template <typename T>
-dg_status run_head(dg_state* st, const float* logits, int step, const dg_sampler_params* p, const uint64_t* seeds,
-                   const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
+dg_status run_merge(dg_state* st, const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin,
+                    hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, V = c.vocab, R = st->R;
-  const float T_t = step_temperature(p, step);
-  const float inv_t = (float)(1.0 / (double)T_t);
-  const SeedArg sa = make_seeds(seeds, st->B);
-  T* pt = c.self_cond ? static_cast<T*>(st->ptilde) : nullptr;
   {
     StageTimer tm(st, DG_STAGE_SAMPLER, s);
-    DG_HIP(sampler_partial<T>(logits, R, V, st->chunks, inv_t, sa, st->n, st->canvas_index, step, st->hp, pt, s));
     DG_HIP(sampler_merge(st->hp, R, st->chunks, st->n, active, H, y, am, margin,
                          c.self_cond ? st->chunk_scale : nullptr, s));
   }
   if (c.self_cond) {
     StageTimer tm(st, DG_STAGE_SELFCOND, s);
-    DG_HIP(gemm_splitk<T>(pt, V, static_cast<const T*>(m->emb_t), V, st->sc_part, R, d, V,
-                          st->chunks * st->sc_sub, st->clen / st->sc_sub, s));
-    DG_HIP(selfcond_reduce(st->sc_part, st->chunk_scale, R, d, st->chunks, st->sc_sub, st->s, s));
+    DG_HIP(gemm_selfcond<T>(static_cast<const T*>(st->ptilde), st->chunk_scale, st->chunks,
+                            static_cast<const T*>(m->emb_t), st->sc_part, R, d, V, st->sc_splits, st->sc_kchunk, s));
+    DG_HIP(selfcond_reduce(st->sc_part, R, d, st->sc_splits, st->s, s));
   }
   return DG_OK;
+}
+
+float step_inv_temperature(const dg_sampler_params* p, int step) {
+  return (float)(1.0 / (double)step_temperature(p, step));
+}
+
+// Sampler stage on supplied logits [R][V].
+template <typename T>
+dg_status run_head(dg_state* st, const float* logits, int step, const dg_sampler_params* p, const uint64_t* seeds,
+                   const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
+  const dg_config& c = st->m->cfg;
+  {
+    StageTimer tm(st, DG_STAGE_SAMPLER, s);
+    DG_HIP(head_from_logits<T>(logits, st->R, c.vocab, step_inv_temperature(p, step), make_seeds(seeds, st->B),
+                               st->n, st->canvas_index, step, st->hp,
+                               c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, s));
+  }
+  return run_merge<T>(st, active, H, y, am, margin, s);
 }
 
 template <typename T>
@@ -592,12 +611,14 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sa
   dg_status r = run_stack<T>(st, canvas, st->n, false, sc, s);
   if (r) return r;
   T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
-  float* logits = logits_out ? logits_out : st->logits;
   {
+    // the LM head with the head statistics in its epilogue (logits stored only when asked for)
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
-    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, logits, R, V, d, s));
+    const HeadArgs<T> h{step_inv_temperature(p, step), make_seeds(seeds, st->B), st->n, st->canvas_index, step,
+                        st->hp, c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, logits_out};
+    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
   }
-  return run_head<T>(st, logits, step, p, seeds, active, H, y, am, margin, s);
+  return run_merge<T>(st, active, H, y, am, margin, s);
 }
 
 dg_status check_params(const dg_sampler_params* p) {

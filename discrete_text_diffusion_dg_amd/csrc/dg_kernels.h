@@ -16,6 +16,27 @@ struct SeedArg {
   uint64_t v[kMaxBatch];
 };
 
+// Statistics of one (row, 128-id vocabulary chunk), written by the LM-head
+// epilogue (or by head_from_logits) and combined per row by sampler_merge.
+struct HeadPart {       // statistics of one (row, vocab chunk)
+  float m;              // max of z = logit / T
+  float s;              // sum exp(z - m)
+  float w;              // sum exp(z - m) * (z - m)
+  float lmax;           // max logit
+  int lidx;             // its index (lowest on ties)
+  float g1;             // best Gumbel-perturbed score
+  int gidx;             // its index
+  float g2;             // second-best score
+};
+
+// Sampler inputs of the LM-head epilogue; ptilde (exp(z - chunk max), operand
+// type) and logits (fp32) are written when non-null.
+template <typename T>
+struct HeadArgs {
+  float inv_t; SeedArg seeds; int n, canvas_index, step;
+  HeadPart* part; T* ptilde; float* logits;
+};
+
 // One expert-routed tile: (expert, first gathered row, rows, unused).
 // Capacity of the tile list for R rows routed to k experts each, 64-row tiles.
 inline int expert_tile_capacity(int rows, int top_k, int n_experts) {
@@ -37,9 +58,12 @@ hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, 
 template <typename T>
 hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
                               SplitPlan sp, hipStream_t s);
-// out[r][c] = A[r] . B[c]  (the tied LM head)
+// The tied LM head, logits[r][v] = A[r] . B[v], in 128 x 128 tiles whose epilogue
+// writes the head statistics of each (row, 128-id chunk) -- part[r][v / 128] --
+// and, as asked, exp(z - chunk max) and the logits.  V must be a multiple of 64.
 template <typename T>
-hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, float* out, int M, int N, int K, hipStream_t s);
+hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
+                        hipStream_t s);
 // act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
@@ -62,10 +86,11 @@ hipError_t expert_stream_gateup(const T* X, const int* perm, const T* pgu, T* ac
 template <typename T>
 hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* tiles, const int* n_tiles,
                               int cap_tiles, int d, int F, hipStream_t s);
-// part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of P[r][k] * Bt[c][k]
+// part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of
+// rnd(P[r][k] * scale[r][k / 128]) * Bt[c][k]   (P: [M][K], scale: [M][nchunk], Bt: [N][K])
 template <typename T>
-hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, int M, int N, int K,
-                       int splits, int kchunk, hipStream_t s);
+hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt, float* part, int M, int N, int K,
+                         int splits, int kchunk, hipStream_t s);
 
 // ---- attention (k_attn.hip)
 struct AttnArgs {
@@ -117,28 +142,16 @@ hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int 
                        hipStream_t s);
 
 // ---- sampler (k_sampler.hip)
-struct HeadPart {       // statistics of one (row, vocab chunk)
-  float m;              // max of z = logit / T
-  float s;              // sum exp(z - m)
-  float w;              // sum exp(z - m) * (z - m)
-  float lmax;           // max logit
-  int lidx;             // its index (lowest on ties)
-  float g1;             // best Gumbel-perturbed score
-  int gidx;             // its index
-  float g2;             // second-best score
-};
-int sampler_chunks(int vocab);
-int sampler_chunk_len(int vocab, int chunks);   // a multiple of 64
+int head_chunks(int vocab);     // 128-id chunks of the vocabulary
+// head statistics of supplied fp32 logits [M][V] (V a multiple of 64)
 template <typename T>
-hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float inv_t,
-                           const SeedArg& seeds, int n, int canvas_index, int step,
-                           HeadPart* part, T* ptilde, hipStream_t s);
+hipError_t head_from_logits(const float* logits, int M, int V, float inv_t, const SeedArg& seeds, int n,
+                            int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s);
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
                          float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale,
                          hipStream_t s);
-// S[r][c] = sum over splits of chunk_scale[r][split / sub] * part[split][r][c]
-hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub,
-                           float* S, hipStream_t s);
+// S[r][c] = sum over splits (in order) of part[split][r][c]
+hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, hipStream_t s);
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,
                          int32_t* prev_am, uint8_t* mask, int32_t* n_committed, uint8_t* done,
                          const SeedArg& seeds, int B, int n, int vocab, int step, int max_steps,

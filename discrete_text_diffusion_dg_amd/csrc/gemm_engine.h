@@ -83,8 +83,9 @@ struct SchedGroup {
 };
 
 // ------------------------------------------------------------------ loaders
-// A loader resolves, once per tile, the row a thread copies (row()); every
-// K-slice then reads 16 bytes at an offset of that row (ld()).  Rows past the
+// A loader resolves, once per tile, the row a thread copies (row(), returning
+// the loader's Row: a row pointer, or more per-row state); every K-slice then
+// reads 16 bytes at an offset of that row (ld()).  Rows past the
 // tile's valid range are clamped to a valid row and their data zeroed after the
 // load, so every thread issues the same loads and the memory-wait counts stay
 // exact for the pipeline.
@@ -97,6 +98,7 @@ __device__ __forceinline__ uint4 ld16(const void* rowp, int k) {
 
 template <typename T>
 struct ALPlain {            // A rows m0 + r of a K-contiguous matrix
+  using Row = const void*;
   const T* p; int lda;
   __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
     valid = r < t.rows;
@@ -107,6 +109,7 @@ struct ALPlain {            // A rows m0 + r of a K-contiguous matrix
 
 template <typename T>
 struct ALRows {             // A rows row_base + r (grouped, contiguous per tile)
+  using Row = const void*;
   const T* p; int lda;
   __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
     valid = r < t.rows;
@@ -117,6 +120,7 @@ struct ALRows {             // A rows row_base + r (grouped, contiguous per tile
 
 template <typename T>
 struct ALGather {           // A rows perm[row_base + r] (tokens routed to one expert)
+  using Row = const void*;
   const T* p; int lda; const int* perm;
   __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
     valid = r < t.rows;
@@ -128,6 +132,7 @@ struct ALGather {           // A rows perm[row_base + r] (tokens routed to one e
 template <typename T> struct ALF32;   // fp32 source converted to the operand type
 template <>
 struct ALF32<float> {
+  using Row = const void*;
   const float* p; int lda;
   __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
     valid = r < t.rows;
@@ -137,6 +142,7 @@ struct ALF32<float> {
 };
 template <>
 struct ALF32<bf16> {
+  using Row = const void*;
   const float* p; int lda;
   __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
     valid = r < t.rows;
@@ -152,6 +158,7 @@ struct ALF32<bf16> {
 
 template <typename T>
 struct BLPlain {            // B rows n0 + n of a [N, K] matrix
+  using Row = const void*;
   const T* p; int ldb;
   __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
     valid = n < t.cols;
@@ -162,6 +169,7 @@ struct BLPlain {            // B rows n0 + n of a [N, K] matrix
 
 template <typename T>
 struct BLExpert {           // B rows of expert `group`: base + group * stride
+  using Row = const void*;
   const T* p; size_t stride; int ldb;
   __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
     valid = n < t.cols;
@@ -175,6 +183,7 @@ struct BLExpert {           // B rows of expert `group`: base + group * stride
 // so each wave's accumulator holds gate and up of the same 16 features side by side.
 template <typename T>
 struct BLGateUp {
+  using Row = const void*;
   const T* gate; const T* up; size_t stride; int ldb;
   __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
     const int f = (n >> 5) * 16 + (n & 15);     // feature within the tile
@@ -203,8 +212,8 @@ __device__ __forceinline__ void tile_mma(const TileCtx& t, const AL& al, const B
   if (nk <= 0) return;
   constexpr int P = C::STAGES - 1;       // slices held in registers
   uint4 ra[P][C::ACH], rb[P][C::BCH];
-  const void* arow[C::ACH];
-  const void* brow[C::BCH];
+  typename AL::Row arow[C::ACH];
+  typename BL::Row brow[C::BCH];
   bool aval[C::ACH], bval[C::BCH];
 #pragma unroll
   for (int i = 0; i < C::ACH; ++i) arow[i] = al.row(t, (tid + 256 * i) >> 3, aval[i]);

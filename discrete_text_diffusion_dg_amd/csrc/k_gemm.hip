@@ -1,10 +1,11 @@
 // Matrix products of the denoise step on the MFMA tile engine:
-// the fused QKV / output / router / self-conditioning projections (dense,
-// split along K; the fp32 partials are reduced in a fixed order by the
-// row-wise kernel that consumes them), the tied LM head, the expert SwiGLU
-// pair and down projection (grouped by expert), and the split-K contraction
-// of the sampled distribution with the embedding (self-conditioning vector).
-#include "dg_kernels.h"
+// the fused QKV / output / self-conditioning projections (dense, split along
+// K; the fp32 partials are reduced in a fixed order by the row-wise kernel
+// that consumes them), the tied LM head with the head statistics in its
+// epilogue, the expert SwiGLU pair and down projection (grouped by expert),
+// and the split-K contraction of the sampled distribution with the embedding
+// (self-conditioning vector).
+#include "dg_head.h"
 #include "gemm_engine.h"
 
 namespace dg {
@@ -40,6 +41,60 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
             Num<T>::store(act + (size_t)(t.row_base + r) * F + t.n0 + f, g / (1.0f + expf(-g)) * u);
           }
         }
+  }
+};
+
+// LM-head tile -> head statistics of its 128 rows x 128 vocabulary ids (and,
+// when asked for, the fp32 logits).  The accumulators go through the tile's
+// shared memory, free once the K loop has ended.
+template <typename T>
+struct EpHead {
+  float inv_t; SeedArg seeds; int n, canvas_index, step, V, nchunk;
+  HeadPart* part; T* ptilde; float* logits;
+  template <class C>
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
+    static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk && C::kSmemBytes >= kHeadTileBytes, "head tiles");
+    float* tile = reinterpret_cast<float*>(smem);
+    for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kHeadLd + c] = v; });
+    if (logits != nullptr)
+      for_each_acc<C>(acc, [&](int r, int c, float v) {
+        if (r < t.rows && c < t.cols) logits[(size_t)(t.m0 + r) * V + t.n0 + c] = v;
+      });
+    __syncthreads();
+    head_tile_stats<T>(tile, t.m0, t.rows, t.n0, t.cols, V, inv_t, seeds, n, canvas_index, step, part, nchunk,
+                       ptilde);
+  }
+};
+
+// A rows of exp(z - m_c) (128-id chunks c) times the chunk's probability scale
+// scale[row][c], in fp32, rounded to the operand type: the softmax @ E operand.
+template <typename T>
+struct ALScaled {
+  const T* p; int lda; const float* scale; int nchunk;
+  struct Row {
+    const T* p; const float* sc;
+  };
+  __device__ Row row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    const size_t rr = (size_t)t.m0 + (valid ? r : 0);
+    return Row{p + rr * lda, scale + rr * nchunk};
+  }
+  __device__ uint4 ld(const Row& rp, int k) const {
+    const uint4 raw = *reinterpret_cast<const uint4*>(rp.p + k);
+    const float sc = rp.sc[k / kHeadChunk];           // the 16 bytes lie in one chunk
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16) * sc;
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * sc;
+      }
+      return pack8_bf16(v);
+    } else {
+      return make_uint4(__float_as_uint(__uint_as_float(raw.x) * sc), __float_as_uint(__uint_as_float(raw.y) * sc),
+                        __float_as_uint(__uint_as_float(raw.z) * sc), __float_as_uint(__uint_as_float(raw.w) * sc));
+    }
   }
 };
 
@@ -91,15 +146,13 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
 }
 
 template <typename T>
-hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, float* out, int M, int N, int K, hipStream_t s) {
-  if (M >= 128) {
-    using C = TileCfg<T, 128, 128>;
-    SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K};
-    return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{out, N, 0}, s);
-  }
-  using C = TileCfg<T, 64, 64>;
-  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), 1, K};
-  return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{out, N, 0}, s);
+hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
+                        hipStream_t s) {
+  if (V % 64) return hipErrorInvalidValue;
+  using C = TileCfg<T, kHeadChunk, kHeadChunk>;
+  SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K};
+  EpHead<T> ep{h.inv_t, h.seeds, h.n, h.canvas_index, h.step, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits};
+  return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, ep, s);
 }
 
 template <typename T>
@@ -122,18 +175,17 @@ hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* t
 }
 
 template <typename T>
-hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, int M, int N, int K,
-                       int splits, int kchunk, hipStream_t s) {
+hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt, float* part, int M, int N, int K,
+                         int splits, int kchunk, hipStream_t s) {
+  const ALScaled<T> al{P, K, scale, nchunk};
   if (M >= 128 && N >= 128) {
     using C = TileCfg<T, 128, 128>;
     SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk};
-    return launch<C, T>(sc.mt * sc.nt * splits, sc, ALPlain<T>{P, ldp}, BLPlain<T>{Bt, ldb},
-                        EpStoreF32{part, N, (size_t)M * N}, s);
+    return launch<C, T>(sc.mt * sc.nt * splits, sc, al, BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
   }
   using C = TileCfg<T, 64, 64>;
   SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), splits, kchunk};
-  return launch<C, T>(sc.mt * sc.nt * splits, sc, ALPlain<T>{P, ldp}, BLPlain<T>{Bt, ldb},
-                      EpStoreF32{part, N, (size_t)M * N}, s);
+  return launch<C, T>(sc.mt * sc.nt * splits, sc, al, BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
 #define DG_INST(T)                                                                                       \
@@ -141,13 +193,14 @@ hipError_t gemm_splitk(const T* P, int ldp, const T* Bt, int ldb, float* part, i
                                        hipStream_t);                                                    \
   template hipError_t gemm_partials_f32a<T>(const float*, int, const T*, int, float*, int, int, int,      \
                                             SplitPlan, hipStream_t);                                    \
-  template hipError_t gemm_lm_head<T>(const T*, int, const T*, int, float*, int, int, int, hipStream_t);  \
+  template hipError_t gemm_lm_head<T>(const T*, int, const T*, int, int, int, int, const HeadArgs<T>&,      \
+                                      hipStream_t);                                                     \
   template hipError_t gemm_expert_gateup<T>(const T*, const int*, const T*, const T*, T*, const int4*,    \
                                             const int*, int, int, int, hipStream_t);                    \
   template hipError_t gemm_expert_down<T>(const T*, const T*, float*, const int4*, const int*, int, int,  \
                                           int, hipStream_t);                                            \
-  template hipError_t gemm_splitk<T>(const T*, int, const T*, int, float*, int, int, int, int, int,       \
-                                     hipStream_t);
+  template hipError_t gemm_selfcond<T>(const T*, const float*, int, const T*, float*, int, int, int, int, \
+                                       int, hipStream_t);
 DG_INST(float)
 DG_INST(bf16)
 #undef DG_INST

@@ -3,253 +3,139 @@
 // adaptive stop; [mlqm] 一: multinomial diffusion replaces an uncertain
 // position by any vocabulary token).
 //
-// Head statistics are computed in one read of the logits: each workgroup owns
-// one (row, vocab chunk); it keeps its z = logit / T values in registers, takes
-// the chunk max, the logit argmax and the Gumbel-max top two (Philox draws,
-// four vocabulary ids per call), then sums exp(z - m) and exp(z - m)(z - m),
-// and writes exp(z - m) rounded to the operand type for the self-conditioning
-// contraction.  A merge pass combines the chunks of a row in order.
-#include "dg_kernels.h"
+// Head statistics per (row, 128-id chunk) come from the LM-head epilogue; for
+// supplied logits, k_head_logits stages the same 128 x 128 tiles through LDS
+// and runs the same code (dg_head.h).  A merge pass combines the chunks of a
+// row in order; the self-conditioning contraction scales each chunk's
+// exp(z - m) in its operand loader, so its split partials add plainly.
+#include "dg_head.h"
 
 namespace dg {
 
-namespace {
-constexpr int kChunkMax = 4096;         // vocabulary ids per workgroup (16 per thread)
-constexpr int kPerThread = kChunkMax / 256;
-}
+int head_chunks(int vocab) { return (vocab + kHeadChunk - 1) / kHeadChunk; }
 
-int sampler_chunks(int vocab) {
-  int c = (vocab + kChunkMax - 1) / kChunkMax;
-  return c < 1 ? 1 : c;
-}
-// chunk length: a multiple of 64 so that split-K slices of the contraction align
-static __host__ __device__ inline int chunk_len(int vocab, int chunks) {
-  const int per = (vocab + chunks - 1) / chunks;
-  return (per + 63) / 64 * 64;
-}
-
-struct Top2 {
-  float b1; int i1; float b2;
-};
-__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
-  if (o.b1 > a.b1 || (o.b1 == a.b1 && o.i1 < a.i1)) {
-    a.b2 = fmaxf(a.b1, o.b2);
-    a.b1 = o.b1; a.i1 = o.i1;
-  } else {
-    a.b2 = fmaxf(a.b2, o.b1);
-  }
-}
-__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-}
-
-// Four consecutive values in one store (8 bytes bf16, 16 bytes fp32).
-__device__ __forceinline__ void store4(bf16* p, const float* e) {
-  uint2 u;
-  u.x = f32x2_to_bf16x2(e[0], e[1]);
-  u.y = f32x2_to_bf16x2(e[2], e[3]);
-  *reinterpret_cast<uint2*>(p) = u;
-}
-__device__ __forceinline__ void store4(float* p, const float* e) {
-  *reinterpret_cast<float4*>(p) = make_float4(e[0], e[1], e[2], e[3]);
-}
-
+// One workgroup per 128 x 128 tile of supplied fp32 logits [M][V].
 template <typename T>
-__global__ __launch_bounds__(256) void k_sampler_partial(const float* logits, int V, int chunks, int clen,
-                                                         float inv_t, SeedArg seeds, int n,
-                                                         int canvas_index, int step, HeadPart* part,
-                                                         T* ptilde) {
-  __shared__ float red_f[3][4];
-  __shared__ int red_i[2][4];
-  __shared__ float red_b2[4];
-  const int chunk = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = row / n, pos = row % n;
-  const int v0 = chunk * clen, v1 = min(V, v0 + clen);
-  const float* L = logits + (size_t)row * V;
-  const uint64_t seed = seeds.v[b];
+__global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M, int V, float inv_t, SeedArg seeds,
+                                                     int n, int canvas_index, int step, HeadPart* part, int nchunk,
+                                                     T* ptilde) {
+  __shared__ __attribute__((aligned(16))) float tile[kHeadChunk * kHeadLd];
+  const int n0 = blockIdx.x * kHeadChunk, m0 = blockIdx.y * kHeadChunk;
+  const int rows = min(kHeadChunk, M - m0), cols = min(kHeadChunk, V - n0);
+  // 32 float4 per tile row: all loads issued together, rows / ids past the end read as 0
+  float4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int q = threadIdx.x + 256 * i, r = q >> 5, c = (q & 31) * 4;
+    v[i] = r < rows && c < cols ? *reinterpret_cast<const float4*>(logits + (size_t)(m0 + r) * V + n0 + c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int q = threadIdx.x + 256 * i, r = q >> 5, c = (q & 31) * 4;
+    *reinterpret_cast<float4*>(tile + r * kHeadLd + c) = v[i];
+  }
+  __syncthreads();
+  head_tile_stats<T>(tile, m0, rows, n0, cols, V, inv_t, seeds, n, canvas_index, step, part, nchunk, ptilde);
+}
 
-  float z[kPerThread];
-  float zmax = -INFINITY, lmax = -INFINITY;
+// One workgroup per row; thread t holds chunks t, t + 256, ... (CPT of them) in
+// registers: first the row max of the chunk maxima (and the order-free arg-max
+// and Gumbel top-two merges), then its chunks' sums in fp64 in chunk order,
+// combined by a fixed butterfly per wave and the four waves in wave order -- the
+// result does not depend on scheduling -- and last the per-chunk scales
+// exp(m_c - M) / S that turn each chunk's exp(z - m_c) into probabilities.
+template <int CPT>
+__global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int chunks, int n, const uint8_t* active,
+                                                       float* H, int32_t* y, int32_t* am, float* margin,
+                                                       float* chunk_scale) {
+  __shared__ float sm_m[4], sm_l[4], sm_g1[4], sm_g2[4];
+  __shared__ int sm_li[4], sm_gi[4];
+  __shared__ double sm_S[4], sm_W[4];
+  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const HeadPart* pr = part + (size_t)r * chunks;
+  HeadPart p[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = t + 256 * j;
+    if (c < chunks) p[j] = pr[c];
+    else { p[j].m = -INFINITY; p[j].s = 0.f; p[j].w = 0.f; p[j].lmax = -INFINITY; p[j].lidx = 0x7fffffff;
+           p[j].g1 = -INFINITY; p[j].gidx = 0x7fffffff; p[j].g2 = -INFINITY; }
+  }
+  float mloc = -INFINITY, lmax = -INFINITY;
   int lidx = 0x7fffffff;
   Top2 t2{-INFINITY, 0x7fffffff, -INFINITY};
-  // every load is issued unconditionally (addresses clamped into the chunk, the
-  // values past its end masked) so that all of them are in flight together
-  float4 l4[kPerThread / 4];
 #pragma unroll
-  for (int it = 0; it < kPerThread / 4; ++it) {
-    const int v = min(v0 + (it * 256 + tid) * 4, v1 - 4);
-    l4[it] = *reinterpret_cast<const float4*>(L + v);
+  for (int j = 0; j < CPT; ++j) {
+    mloc = fmaxf(mloc, p[j].m);
+    argmax_merge(lmax, lidx, p[j].lmax, p[j].lidx);
+    top2_merge(t2, Top2{p[j].g1, p[j].gidx, p[j].g2});
   }
-  // logit arg-max and the max of z over all of the thread's values
-#pragma unroll
-  for (int it = 0; it < kPerThread / 4; ++it) {
-    const int v = v0 + (it * 256 + tid) * 4;
-    const bool ok = v < v1;
-    const float lv[4] = {l4[it].x, l4[it].y, l4[it].z, l4[it].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float zz = ok ? lv[j] * inv_t : -INFINITY;
-      z[it * 4 + j] = zz;
-      zmax = fmaxf(zmax, zz);
-      if (ok) argmax_merge(lmax, lidx, lv[j], v + j);
-    }
-  }
-  // Gumbel-max top two.  The first four values of every lane are scored
-  // exactly; the wave's second-best score b2 and largest z then bound the rest:
-  // a value can enter the chunk's top two only if its Gumbel noise exceeds
-  // b2 - max z, i.e. only if its uniform exceeds exp(-exp(-(b2 - max z))) -- a
-  // threshold on the raw Philox word (lowered by a 1e-3 margin on the score,
-  // far above fp32 rounding).  Values under it cannot change the top two, so
-  // they skip the two logarithms.
-  auto score = [&](int it, const uint4& x, uint32_t qmin) {
-    const int v = v0 + (it * 256 + tid) * 4;
-    if (v >= v1) return;
-    const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((xv[j] >> 9) >= qmin) top2_merge(t2, Top2{z[it * 4 + j] + gumbel_of(xv[j]), v + j, -INFINITY});
-  };
-  score(0, philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
-                        (uint32_t)((v0 + tid * 4) >> 2)), 0u);
-  uint32_t qmin = 0;
-  {
-    Top2 tw = t2;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      top2_merge(tw, Top2{__shfl_xor(tw.b1, o, 64), __shfl_xor(tw.i1, o, 64), __shfl_xor(tw.b2, o, 64)});
-    const float delta = tw.b2 - wave_max(zmax) - 1e-3f;
-    if (delta > -INFINITY) {
-      const float uthr = expf(-expf(-delta));                 // prune when u < uthr
-      const float q = floorf(uthr * 8388608.f - 0.5f) - 1.f;  // u = (2q + 1) 2^-24 < uthr for q < qmin
-      qmin = q > 0.f ? (uint32_t)q : 0u;
-    }
-  }
-#pragma unroll
-  for (int it = 1; it < kPerThread / 4; ++it) {
-    const int v = v0 + (it * 256 + tid) * 4;
-    score(it, philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos,
-                           (uint32_t)(v >> 2)), qmin);
-  }
-  // workgroup reductions (fixed order)
+  mloc = wave_max(mloc);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    zmax = fmaxf(zmax, __shfl_xor(zmax, o, 64));
-    const float ol = __shfl_xor(lmax, o, 64);
-    const int oi = __shfl_xor(lidx, o, 64);
-    argmax_merge(lmax, lidx, ol, oi);
-    Top2 ot{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)};
-    top2_merge(t2, ot);
+    argmax_merge(lmax, lidx, __shfl_xor(lmax, o, 64), __shfl_xor(lidx, o, 64));
+    top2_merge(t2, Top2{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)});
   }
   if (lane == 0) {
-    red_f[0][w] = zmax; red_f[1][w] = lmax; red_f[2][w] = t2.b1;
-    red_i[0][w] = lidx; red_i[1][w] = t2.i1; red_b2[w] = t2.b2;
+    sm_m[wv] = mloc; sm_l[wv] = lmax; sm_li[wv] = lidx; sm_g1[wv] = t2.b1; sm_gi[wv] = t2.i1; sm_g2[wv] = t2.b2;
   }
   __syncthreads();
-  zmax = red_f[0][0];
-  lmax = red_f[1][0]; lidx = red_i[0][0];
-  t2 = Top2{red_f[2][0], red_i[1][0], red_b2[0]};
-  for (int q = 1; q < 4; ++q) {
-    zmax = fmaxf(zmax, red_f[0][q]);
-    argmax_merge(lmax, lidx, red_f[1][q], red_i[0][q]);
-    top2_merge(t2, Top2{red_f[2][q], red_i[1][q], red_b2[q]});
-  }
-  __syncthreads();
-
-  float s = 0.f, ws = 0.f;
+  const double m = (double)fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  double S = 0.0, W = 0.0;
 #pragma unroll
-  for (int it = 0; it < kPerThread / 4; ++it) {
-    const int v = v0 + (it * 256 + tid) * 4;
-    if (v < v1) {
-      float e4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float dz = z[it * 4 + j] - zmax;
-        const float e = expf(dz);
-        e4[j] = e;
-        s += e;
-        ws += e * dz;
-      }
-      if (ptilde != nullptr) store4(ptilde + (size_t)row * V + v, e4);
-    }
+  for (int j = 0; j < CPT; ++j) {
+    if (p[j].m == -INFINITY) continue;
+    const double f = exp((double)p[j].m - m);
+    S += (double)p[j].s * f;
+    W += f * ((double)p[j].w + ((double)p[j].m - m) * (double)p[j].s);
   }
-  s = wave_sum(s);
-  ws = wave_sum(ws);
-  if (lane == 0) { red_f[0][w] = s; red_f[1][w] = ws; }
-  __syncthreads();
-  if (tid == 0) {
-    s = red_f[0][0] + red_f[0][1] + red_f[0][2] + red_f[0][3];
-    ws = red_f[1][0] + red_f[1][1] + red_f[1][2] + red_f[1][3];
-    HeadPart hp;
-    hp.m = zmax; hp.s = s; hp.w = ws; hp.lmax = lmax; hp.lidx = lidx;
-    hp.g1 = t2.b1; hp.gidx = t2.i1; hp.g2 = t2.b2;
-    part[(size_t)row * chunks + chunk] = hp;
-  }
-}
-
-// One wave per row, lane c holding chunk c (chunks <= 64): the chunk statistics
-// combine in fp64 through a fixed butterfly, so the result does not depend on
-// scheduling; arg-max and Gumbel top-two merges are order-free.
-__global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int M, int chunks, int n,
-                                                       const uint8_t* active, float* H, int32_t* y, int32_t* am,
-                                                       float* margin, float* chunk_scale) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= M) return;
-  const bool has = lane < chunks;
-  HeadPart p;
-  if (has) p = part[(size_t)r * chunks + lane];
-  else { p.m = -INFINITY; p.s = 0.f; p.w = 0.f; p.lmax = -INFINITY; p.lidx = 0x7fffffff;
-         p.g1 = -INFINITY; p.gidx = 0x7fffffff; p.g2 = -INFINITY; }
-  const float mf = wave_max(p.m);
-  const double m = (double)mf;
-  const double f = has ? exp((double)p.m - m) : 0.0;
-  double S = (double)p.s * f;
-  double W = has ? f * ((double)p.w + ((double)p.m - m) * (double)p.s) : 0.0;
-  float lmax = p.lmax;
-  int lidx = p.lidx;
-  Top2 t2{p.g1, p.gidx, p.g2};
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     S += __shfl_xor(S, o, 64);
     W += __shfl_xor(W, o, 64);
-    argmax_merge(lmax, lidx, __shfl_xor(lmax, o, 64), __shfl_xor(lidx, o, 64));
-    top2_merge(t2, Top2{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)});
   }
-  if (chunk_scale != nullptr && has) chunk_scale[(size_t)r * chunks + lane] = (float)(f / S);
-  if (lane != 0 || (active != nullptr && active[r / n] == 0)) return;
+  if (lane == 0) { sm_S[wv] = S; sm_W[wv] = W; }
+  __syncthreads();
+  S = ((sm_S[0] + sm_S[1]) + sm_S[2]) + sm_S[3];
+  W = ((sm_W[0] + sm_W[1]) + sm_W[2]) + sm_W[3];
+  if (chunk_scale != nullptr) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = t + 256 * j;
+      if (c < chunks)
+        chunk_scale[(size_t)r * chunks + c] = p[j].m == -INFINITY ? 0.f : (float)(exp((double)p[j].m - m) / S);
+    }
+  }
+  if (t != 0 || (active != nullptr && active[r / n] == 0)) return;
+  lmax = sm_l[0]; lidx = sm_li[0];
+  t2 = Top2{sm_g1[0], sm_gi[0], sm_g2[0]};
+  for (int q = 1; q < 4; ++q) {
+    argmax_merge(lmax, lidx, sm_l[q], sm_li[q]);
+    top2_merge(t2, Top2{sm_g1[q], sm_gi[q], sm_g2[q]});
+  }
   H[r] = (float)(log(S) - W / S);
   y[r] = t2.i1;
   am[r] = lidx;
   margin[r] = t2.b1 - t2.b2;
 }
 
-// s[r][c] = sum over chunks of scale[r][chunk] * (sum of the chunk's `sub` K-slice
-// partials, slice order).  Four columns per thread; the partial loads of up to
-// four chunks are issued together.
-__global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, const float* chunk_scale, int M, int d,
-                                                         int chunks, int sub, float* S) {
+// s[r][c] = sum of the split partials in split order, four columns per thread,
+// the loads of up to eight splits issued together.
+__global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, int M, int d, int splits, float* S) {
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;      // float4 index
   const size_t nq = (size_t)M * d / 4;
   if (q >= nq) return;
-  const size_t r = q * 4 / d;
   const float4* p4 = reinterpret_cast<const float4*>(part);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < chunks; c0 += 4) {
-    float4 pc[4];
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float4 pc[8];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      pc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + cc < chunks)
-        for (int u = 0; u < sub; ++u) {
-          const float4 v = p4[(size_t)((c0 + cc) * sub + u) * nq + q];
-          pc[cc].x += v.x; pc[cc].y += v.y; pc[cc].z += v.z; pc[cc].w += v.w;
-        }
-    }
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < splits) pc[u] = p4[(size_t)(s0 + u) * nq + q];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      if (c0 + cc < chunks) {
-        const float sc = chunk_scale[r * chunks + c0 + cc];
-        acc.x += sc * pc[cc].x; acc.y += sc * pc[cc].y; acc.z += sc * pc[cc].z; acc.w += sc * pc[cc].w;
-      }
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < splits) { acc.x += pc[u].x; acc.y += pc[u].y; acc.z += pc[u].z; acc.w += pc[u].w; }
   }
   reinterpret_cast<float4*>(S)[q] = acc;
 }
@@ -334,30 +220,37 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
 namespace dg {
 
 template <typename T>
-hipError_t sampler_partial(const float* logits, int M, int V, int chunks, float inv_t, const SeedArg& seeds,
-                           int n, int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s) {
+hipError_t head_from_logits(const float* logits, int M, int V, float inv_t, const SeedArg& seeds, int n,
+                            int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  const int clen = chunk_len(V, chunks);
-  if (clen > kChunkMax) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_sampler_partial<T>), dim3(chunks, M), dim3(256), 0, s, logits, V, chunks, clen, inv_t,
-                     seeds, n, canvas_index, step, part, ptilde);
+  if (V % 64) return hipErrorInvalidValue;
+  const dim3 grid(head_chunks(V), (M + kHeadChunk - 1) / kHeadChunk);
+  hipLaunchKernelGGL((k_head_logits<T>), grid, dim3(256), 0, s, logits, M, V, inv_t, seeds, n, canvas_index, step,
+                     part, head_chunks(V), ptilde);
   return hipGetLastError();
 }
 
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active, float* H,
                          int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sampler_merge, dim3((M + 3) / 4), dim3(256), 0, s, part, M, chunks, n, active, H, y,
-                     am, margin, chunk_scale);
+  const dim3 grid(M), block(256);
+  if (chunks <= 256)
+    hipLaunchKernelGGL((k_sampler_merge<1>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+  else if (chunks <= 512)
+    hipLaunchKernelGGL((k_sampler_merge<2>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+  else if (chunks <= 1024)
+    hipLaunchKernelGGL((k_sampler_merge<4>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+  else if (chunks <= 2048)
+    hipLaunchKernelGGL((k_sampler_merge<8>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t selfcond_reduce(const float* part, const float* chunk_scale, int M, int d, int chunks, int sub, float* S,
-                           hipStream_t s) {
+hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, hipStream_t s) {
   const size_t nq = (size_t)M * d / 4;      // d is a multiple of 256
   if (nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, part, chunk_scale,
-                     M, d, chunks, sub, S);
+  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, part, M, d, splits, S);
   return hipGetLastError();
 }
 
@@ -370,11 +263,9 @@ hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, in
   return hipGetLastError();
 }
 
-int sampler_chunk_len(int vocab, int chunks) { return chunk_len(vocab, chunks); }
-
-template hipError_t sampler_partial<float>(const float*, int, int, int, float, const SeedArg&, int, int, int,
-                                           HeadPart*, float*, hipStream_t);
-template hipError_t sampler_partial<bf16>(const float*, int, int, int, float, const SeedArg&, int, int, int,
-                                          HeadPart*, bf16*, hipStream_t);
+template hipError_t head_from_logits<float>(const float*, int, int, float, const SeedArg&, int, int, int,
+                                            HeadPart*, float*, hipStream_t);
+template hipError_t head_from_logits<bf16>(const float*, int, int, float, const SeedArg&, int, int, int,
+                                           HeadPart*, bf16*, hipStream_t);
 
 }  // namespace dg
