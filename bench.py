@@ -63,14 +63,14 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
     elif stage == "expert_down":
         by = n_experts_active * d * F * es + R * k * F * es + R * k * d * 4
         fl = 2 * R * k * F * d
-    elif stage == "lm_head":
-        by = V * d * es + R * d * es + R * V * 4
+    elif stage == "lm_head":     # with the head statistics in its epilogue: writes P~ and the chunk records
+        by = V * d * es + R * d * es + (R * V * es if mc.self_cond else 0) + R * ((V + 127) // 128) * 32
         fl = 2 * R * d * V
     elif stage == "attn":
         by = 2 * B * Hkv * keys * hd * es + 2 * R * Hq * hd * es
         fl = 4 * R * Hq * keys * hd
-    elif stage == "sampler":
-        by = R * V * 4 + (R * V * es if mc.self_cond else 0)
+    elif stage == "sampler":     # per-row merge of the 128-id chunk records
+        by = R * ((V + 127) // 128) * 32 + (R * ((V + 127) // 128) * 4 if mc.self_cond else 0)
         fl = 0
     elif stage == "selfcond":
         by = R * V * es + V * d * es + R * d * 4
