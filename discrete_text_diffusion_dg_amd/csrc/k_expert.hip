@@ -11,19 +11,23 @@
 // (PGU[F/16][d/32][2][64][8]) so silu(g) * u is formed lane-locally.
 //
 // A workgroup of NW waves owns NW feature blocks (of 16 outputs) of one tile;
-// each wave streams the weights of its block over the whole K range.  The
-// tile's activation rows are read once per workgroup, as whole cache lines,
-// in chunks of KC K steps that are double-buffered in LDS (padded rows: the
-// fragment reads of 8 lanes cover distinct banks), so the weight stream keeps
-// the CU's memory requests to itself; the activations in registers would be
-// re-read by every wave, in half-line pieces.  Chunks are handed over with an
-// LDS-only barrier, so the weight loads in flight are not drained at the
-// hand-over.  The number of row blocks (1..4) is a template parameter chosen
-// per tile at run time, so every load of a path is unconditional and the
-// memory-wait counts stay exact.
+// each wave streams the weights of its block over the whole K range through a
+// ring of PD K steps of fragments: the load of step s + PD is issued as soon as
+// step s has been multiplied, so PD steps of weights stay in flight.  The
+// tile's activation rows are read once per workgroup, as whole cache lines, in
+// chunks of KC K steps that are double-buffered in LDS (padded rows: the
+// fragment reads of 8 lanes cover distinct banks), and the staging registers
+// are double-buffered too: the rows of chunk c + 2 are requested when chunk c
+// starts and written to LDS when chunk c + 1 ends, so a staging load is never
+// waited on in the chunk that issued it (the memory counter completes in
+// order: waiting on it would also drain the weight ring).  Chunks are handed
+// over with an LDS-only barrier.  The number of row blocks (1..4) is a
+// template parameter chosen per tile at run time, so every load of a path is
+// unconditional and the memory-wait counts stay exact.
 #include "dg_kernels.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace dg {
 
@@ -43,14 +47,14 @@ __device__ __forceinline__ void frag_ld(Frag<float>& f, const float* p) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
-// K steps per group (the weight loads of the next group are issued before the
-// MFMAs of the current one) and per staged activation chunk, per element type.
-// Measured on the batch-1 tile lists (9..32 active experts of 32, d = F = 1024):
-// one feature block per wave and four waves per workgroup (two workgroups per
-// CU) beat wider blocks, eight or sixteen waves, and 128-row tiles.
-template <typename T> struct StreamCfg;
-template <> struct StreamCfg<bf16> { static constexpr int U = 2, KC = 4; };
-template <> struct StreamCfg<float> { static constexpr int U = 1, KC = 2; };
+// Weight ring depth PD and activation chunk KC (K steps), per element type and
+// product.  Measured on batch-1 tile lists (11..32 active experts of 32,
+// d = F = 1024, bf16): gate/up gains 10-25% from an 8-step ring on the skewed
+// lists; the down product, with half the bytes per step, is flat from 2 to 8.
+template <typename T, bool GATEUP> struct StreamCfg;
+template <> struct StreamCfg<bf16, true> { static constexpr int PD = 8, KC = 4; };
+template <> struct StreamCfg<bf16, false> { static constexpr int PD = 4, KC = 4; };
+template <bool G> struct StreamCfg<float, G> { static constexpr int PD = 2, KC = 2; };
 constexpr int kStreamWaves = 4;
 
 // ---- packing
@@ -94,13 +98,21 @@ __global__ void k_pack_down(const T* down, T* out, int d, int F) {
 }
 
 // ---- streaming products
+template <int... U, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, U...>, F&& f) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+
 // GATEUP: out = act [rows][F] (T), B = PGU, A rows gathered through perm.
 // else:   out = Y   [rows][d] (fp32), B = PD, A rows row_base + r of act.
 // LDS: two stages of [64 rows][KC*32 + pad] elements; a stage holds K steps
-// [c*KC, (c+1)*KC) of the tile's rows.
-template <typename T, bool GATEUP, int RB, int NW, int U, int KC>
+// [c*KC, (c+1)*KC) of the tile's rows.  The K loop runs in super steps of SS
+// K steps (an even number of chunks, a multiple of the ring depth), unrolled so
+// that every ring slot and staging set is a compile-time index.
+template <typename T, bool GATEUP, int RB, int NW, int PD, int KC>
 __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T* Wp, void* out, int e,
                                             int row_base, int rows, int K, int N, int nb, T* lds) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   constexpr int EPR = KC * 32;              // elements of a row per chunk
   constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte piece
   constexpr int LROW = EPR + VEC;           // padded LDS row (elements)
@@ -112,11 +124,13 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T
   constexpr int RSTEP = NT / SEGS;          // rows between a thread's pieces
   constexpr int STAGE = 64 * LROW;          // elements per LDS stage
   constexpr int NF = GATEUP ? 2 : 1;        // B fragments per K step
-  constexpr int GPC = KC / U;               // groups per chunk
-  static_assert(GPC % 2 == 0, "the double buffer alternates within a chunk");
+  constexpr int SS = PD > 2 * KC ? PD : 2 * KC;
+  constexpr int CPS = SS / KC;              // chunks per super step (even)
+  static_assert(SS % PD == 0 && SS % KC == 0 && CPS % 2 == 0, "ring and chunk sizes are powers of two");
+  constexpr bool PIN = KC > 2;              // keep the issue order of the loads as written
 
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, c16 = lane & 15;
-  const int KS = K / 32, NC = KS / KC;
+  const int KS = K / 32, NSS = KS / SS;
   // staging: this thread moves pieces (row r0 + j * RSTEP, column seg) of every chunk
   const int seg = tid % SEGS, r0 = tid / SEGS;
   const T* aptr[PPT];
@@ -131,15 +145,15 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T
     const int src = GATEUP ? perm[row_base + rr] : row_base + rr;
     aptr[j] = X + (size_t)src * K + seg * VEC;
   }
-  uint4 st[PPT];
-  auto stage_load = [&](int c) __attribute__((always_inline)) {
+  u32x4 st[2][PPT];
+  auto stage_load = [&](int set, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) st[j] = *reinterpret_cast<const uint4*>(aptr[j] + (size_t)c * EPR);
+    for (int j = 0; j < PPT; ++j) st[set][j] = *reinterpret_cast<const u32x4*>(aptr[j] + (size_t)c * EPR);
   };
-  auto stage_store = [&](int buf) __attribute__((always_inline)) {
+  auto stage_store = [&](int set, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      if (pok[j]) *reinterpret_cast<uint4*>(lds + buf * STAGE + (r0 + j * RSTEP) * LROW + seg * VEC) = st[j];
+      if (pok[j]) *reinterpret_cast<u32x4*>(lds + buf * STAGE + (r0 + j * RSTEP) * LROW + seg * VEC) = st[set][j];
   };
 
   constexpr int blk = NF * 512;             // elements per (block, K step)
@@ -149,47 +163,50 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[rb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  Frag<T> b[2][U][NF];
-  auto load_b = [&](int buf, int ks0) __attribute__((always_inline)) {
+  Frag<T> b[PD][NF];
+  auto load_b = [&](int slot, int ks) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < NF; ++j) frag_ld(b[buf][u][j], bp + (size_t)(ks0 + u) * blk + j * 512);
+    for (int j = 0; j < NF; ++j) frag_ld(b[slot][j], bp + (size_t)ks * blk + j * 512);
   };
-  // K steps kk .. kk+U-1 of the chunk in LDS stage abuf
-  auto comp = [&](int buf, int abuf, int kk) __attribute__((always_inline)) {
+  // K step kk of the chunk in LDS stage abuf, weights from ring slot `slot`
+  auto comp = [&](int slot, int abuf, int kk) __attribute__((always_inline)) {
+    Frag<T> a[RB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Frag<T> a[RB];
+    for (int rb = 0; rb < RB; ++rb)
+      lds_frag(a[rb], lds + abuf * STAGE + (rb * 16 + c16) * LROW + kk * 32 + g4 * 8);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        lds_frag(a[rb], lds + abuf * STAGE + (rb * 16 + c16) * LROW + (kk + u) * 32 + g4 * 8);
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int j = 0; j < NF; ++j) mma16x16x32(acc[rb][j], a[rb], b[buf][u][j]);
-    }
+      for (int j = 0; j < NF; ++j) mma16x16x32(acc[rb][j], a[rb], b[slot][j]);
   };
-  // one chunk: stage the next one while its K steps stream; the last chunk
-  // stages nothing and prefetches no weights past the end
-  auto chunk = [&](int c, auto last) __attribute__((always_inline)) {
+  // K step u of super step g; the last super step stages and prefetches
+  // nothing past the end
+  auto kstep = [&](int g, auto last, auto uc) __attribute__((always_inline)) {
     constexpr bool LAST = decltype(last)::value;
-    if (!LAST) stage_load(c + 1);
-#pragma unroll
-    for (int g = 0; g < GPC; ++g) {
-      if (!LAST || g + 1 < GPC) load_b((g + 1) & 1, c * KC + (g + 1) * U);
-      comp(g & 1, c & 1, g * U);
+    constexpr int u = decltype(uc)::value;
+    constexpr int cl = u / KC;                // chunk within the super step; its parity is the chunk's
+    if constexpr (u % KC == 0 && (!LAST || cl + 2 < CPS)) stage_load(cl & 1, g * CPS + cl + 2);
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+    comp(u % PD, cl & 1, u % KC);
+    if constexpr (!LAST || u + PD < SS) load_b(u % PD, g * SS + u + PD);
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (u % KC == KC - 1) {
+      if constexpr (!LAST || cl + 1 < CPS) stage_store((cl + 1) & 1, (cl + 1) & 1);
+      lds_barrier();
     }
-    if (!LAST) stage_store((c + 1) & 1);
-    lds_barrier();
   };
-  stage_load(0);
-  load_b(0, 0);
-  stage_store(0);
+  auto superstep = [&](int g, auto last) __attribute__((always_inline)) {
+    static_for(std::make_integer_sequence<int, SS>{}, [&](auto uc) __attribute__((always_inline)) { kstep(g, last, uc); });
+  };
+#pragma unroll
+  for (int s = 0; s < PD; ++s) load_b(s, s);
+  stage_load(0, 0);
+  stage_load(1, 1);
+  stage_store(0, 0);
   lds_barrier();
-  int c = 0;
-  for (; c + 1 < NC; ++c) chunk(c, std::false_type{});
-  chunk(c, std::true_type{});
+  int g = 0;
+  for (; g + 1 < NSS; ++g) superstep(g, std::false_type{});
+  superstep(g, std::true_type{});
 
   // epilogue: the lane holds rows rb*16 + g4*4 + i, column c16 of the block
   const int col = nb * 16 + c16;
@@ -211,7 +228,7 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T
 // Grid: x = N / (16 * NW) feature-block groups (exact), y = tile capacity
 // (tiles past n_tiles exit; the exit is uniform over the workgroup, so every
 // wave reaches the same barriers).
-template <typename T, bool GATEUP, int NW, int U, int KC>
+template <typename T, bool GATEUP, int NW, int PD, int KC>
 __global__ __launch_bounds__(64 * NW, 2) void k_expert_stream(const T* X, const int* perm, const T* Wp, void* out,
                                                               const int4* tiles, const int* n_tiles, int K, int N) {
   __shared__ __attribute__((aligned(16))) T lds[2 * 64 * (KC * 32 + 16 / sizeof(T))];
@@ -220,19 +237,26 @@ __global__ __launch_bounds__(64 * NW, 2) void k_expert_stream(const T* X, const 
   const int4 td = tiles[ti];
   const int nb = blockIdx.x * NW + (int)(threadIdx.x >> 6);
   switch ((td.z + 15) >> 4) {
-    case 1: stream_body<T, GATEUP, 1, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
-    case 2: stream_body<T, GATEUP, 2, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
-    case 3: stream_body<T, GATEUP, 3, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
-    default: stream_body<T, GATEUP, 4, NW, U, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    case 1: stream_body<T, GATEUP, 1, NW, PD, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    case 2: stream_body<T, GATEUP, 2, NW, PD, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    case 3: stream_body<T, GATEUP, 3, NW, PD, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
+    default: stream_body<T, GATEUP, 4, NW, PD, KC>(X, perm, Wp, out, td.x, td.y, td.z, K, N, nb, lds); break;
   }
 }
 
 }  // namespace
 
+// K steps per super step of a configuration
+template <typename C>
+constexpr int stream_ss() {
+  return C::PD > 2 * C::KC ? C::PD : 2 * C::KC;
+}
+
 bool expert_stream_ok(int d, int F, int elem_bytes) {
-  const int KC = elem_bytes == 2 ? StreamCfg<bf16>::KC : StreamCfg<float>::KC;
-  // whole staged chunks along K, whole workgroups of feature blocks along N
-  return d % (32 * KC) == 0 && F % (32 * KC) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamWaves) == 0;
+  const int ssg = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, true>>() : stream_ss<StreamCfg<float, true>>();
+  const int ssd = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, false>>() : stream_ss<StreamCfg<float, false>>();
+  // whole super steps along K, whole workgroups of feature blocks along N
+  return d % (32 * ssg) == 0 && F % (32 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamWaves) == 0;
 }
 
 template <typename T>
@@ -251,7 +275,8 @@ template <typename T>
 hipError_t expert_stream_gateup(const T* X, const int* perm, const T* pgu, T* act, const int4* tiles,
                                 const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
   constexpr int NW = kStreamWaves;
-  hipLaunchKernelGGL((k_expert_stream<T, true, NW, StreamCfg<T>::U, StreamCfg<T>::KC>), dim3(F / (16 * NW), cap_tiles),
+  using C = StreamCfg<T, true>;
+  hipLaunchKernelGGL((k_expert_stream<T, true, NW, C::PD, C::KC>), dim3(F / (16 * NW), cap_tiles),
                      dim3(64 * NW), 0, s, X, perm, pgu, (void*)act, tiles, n_tiles, d, F);
   return hipGetLastError();
 }
@@ -260,7 +285,8 @@ template <typename T>
 hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* tiles, const int* n_tiles,
                               int cap_tiles, int d, int F, hipStream_t s) {
   constexpr int NW = kStreamWaves;
-  hipLaunchKernelGGL((k_expert_stream<T, false, NW, StreamCfg<T>::U, StreamCfg<T>::KC>), dim3(d / (16 * NW), cap_tiles),
+  using C = StreamCfg<T, false>;
+  hipLaunchKernelGGL((k_expert_stream<T, false, NW, C::PD, C::KC>), dim3(d / (16 * NW), cap_tiles),
                      dim3(64 * NW), 0, s, act, (const int*)nullptr, pd, (void*)Y, tiles, n_tiles, F, d);
   return hipGetLastError();
 }
