@@ -16,8 +16,21 @@
 // along K); loaders produce 16 bytes of operand data for (tile row, k); an
 // epilogue consumes the accumulators (and may reuse the tile's shared memory,
 // free once the K loop has ended).
+//
+// bf16 products whose loaders only locate rows (plain, grouped, gathered) use
+// a second tile loop, tile_mma_dma: operand rows go from global memory
+// straight into LDS (16 bytes per lane, no register staging) through an
+// S-stage ring, S-1 slices ahead of the matrix cores.  A slice row (128 bytes)
+// keeps its eight 16-byte pieces in a rotated order, piece q of tile row r at
+// position q ^ ((r >> 1) & 7), so every row is still fetched as one whole
+// cache line and each 16-lane phase of a fragment read touches 16 distinct
+// bank groups.  Each wave waits for its own slice loads with an explicit
+// memory-counter wait and the slice is handed over with an LDS-only barrier,
+// so the later slices' loads stay in flight.
 #pragma once
 #include "dg_common.h"
+
+#include <type_traits>
 
 namespace dg {
 
@@ -284,6 +297,108 @@ __device__ __forceinline__ void tile_mma(const TileCtx& t, const AL& al, const B
   __syncthreads();   // the epilogue may reuse the shared memory
 }
 
+// ------------------------------------------------------------------ the DMA tile loop (bf16)
+// Same tile and accumulator layout as TileCfg<bf16, BM, BN> (4 waves, 2 x 2),
+// S slices of 64 K-elements in LDS.
+template <int BM_, int BN_, int S_>
+struct TileCfgD {
+  static constexpr int BM = BM_, BN = BN_, STAGES = S_;
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int ROWB = 128;                          // bytes of a slice row (64 bf16)
+  static constexpr int STAGE = (BM + BN) * ROWB;            // bytes of one slice of the tile
+  static constexpr int NI = (BM + BN) / 8 / 4;              // 8-row load groups per wave per slice
+  static_assert((BM + BN) % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
+  static constexpr int kSmemBytes = S_ * STAGE;
+};
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds_addr + 16 * i (lds_addr wave-uniform).  Issued from asm so that the
+// compiler's wait insertion, which cannot tell these LDS writes from the
+// fragment reads of other slices, does not drain them before every LDS read;
+// the tile loop waits for them itself.  M0 is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
+  uint32_t m0save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(m0save)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(g)
+               : "memory");
+}
+
+template <class C, class AL, class BL>
+__device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, const BL& bl, char* smem,
+                                             f32x4_t (&acc)[C::FM][C::FN]) {
+  static_assert(std::is_same<typename AL::Row, const void*>::value && std::is_same<typename BL::Row, const void*>::value,
+                "row-locating loaders only");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+    for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = (t.k1 - t.k0) / 64;
+  if (nk <= 0) return;
+  // load group j of this wave: tile rows 8 * (w + 4 j) .. + 7 (A rows, then B
+  // rows); lane (row rr = lane >> 3, position p = lane & 7) fetches piece
+  // p ^ ((r >> 1) & 7) of its row.  Rows past the tile repeat a valid row;
+  // their products are never stored.
+  const char* src[C::NI];
+  uint32_t dst[C::NI];
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j) {
+    const int gi = w + 4 * j;
+    const int row = gi * 8 + (lane >> 3);
+    const bool isA = row < C::BM;
+    const int r = isA ? row : row - C::BM;
+    bool valid;
+    const void* rp = isA ? al.row(t, r, valid) : bl.row(t, r, valid);
+    const int q = (lane & 7) ^ ((r >> 1) & 7);
+    src[j] = static_cast<const char*>(rp) + (size_t)t.k0 * 2 + q * 16;
+    dst[j] = (uint32_t)(gi * 8 * C::ROWB);
+  }
+  const uint32_t lbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t sb = lbase + (uint32_t)((kt % C::STAGES) * C::STAGE);
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) lds_dma16(src[j] + (size_t)kt * 128, sb + dst[j]);
+  };
+  const int c16 = lane & 15, g4 = lane >> 4, sw = (c16 >> 1) & 7;
+  const int aoff = (wm * C::WM + c16) * C::ROWB, boff = (C::BM + wn * C::WN + c16) * C::ROWB;
+  auto kstep = [&](const char* sb, int kk) __attribute__((always_inline)) {
+    const int ch = ((kk * 4 + g4) ^ sw) * 16;
+    Frag<bf16> fa[C::FM], fb[C::FN];
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a) fa[a].v = *reinterpret_cast<const uint4*>(sb + aoff + a * 16 * C::ROWB + ch);
+#pragma unroll
+    for (int b = 0; b < C::FN; ++b) fb[b].v = *reinterpret_cast<const uint4*>(sb + boff + b * 16 * C::ROWB + ch);
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::FN; ++b) mma16x16x32(acc[a][b], fa[a], fb[b]);
+  };
+#pragma unroll
+  for (int p = 0; p < C::STAGES - 1; ++p)
+    if (p < nk) issue(p);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of slice kt are done once at most the next S-2 slices' are outstanding
+    if (kt + C::STAGES - 2 < nk) wait_vmcnt<(C::STAGES - 2) * C::NI>();
+    else wait_vmcnt<0>();
+    lds_barrier();            // slice kt is in LDS for every wave; slice kt-1 is no longer read
+    if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1);
+    const char* sb = smem + (kt % C::STAGES) * C::STAGE;
+    kstep(sb, 0);
+    kstep(sb, 1);
+  }
+  __syncthreads();   // the epilogue may reuse the shared memory
+}
+
 // Visit every accumulator element with its tile-relative (row, col) and block indices.
 template <class C, class F>
 __device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[C::FM][C::FN], F&& f) {
@@ -300,11 +415,24 @@ __device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[C::FM][C::FN],
 
 template <class C, typename T, class SCHED, class AL, class BL, class EP>
 __global__ __launch_bounds__(256, 2) void k_gemm(SCHED sc, AL al, BL bl, EP ep) {
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
+  constexpr int kBytes = C::kSmemBytes > EP::kSmemBytes ? C::kSmemBytes : EP::kSmemBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
   TileCtx t;
   if (!sc.get(blockIdx.x, t)) return;
   f32x4_t acc[C::FM][C::FN];
   tile_mma<C, T>(t, al, bl, smem, acc);
+  ep.template apply<C>(t, acc, smem);
+}
+
+// LDS: the slice ring, or what the epilogue needs if that is more
+template <class C, class SCHED, class AL, class BL, class EP>
+__global__ __launch_bounds__(256, 2) void k_gemm_dma(SCHED sc, AL al, BL bl, EP ep) {
+  constexpr int kBytes = C::kSmemBytes > EP::kSmemBytes ? C::kSmemBytes : EP::kSmemBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kBytes];
+  TileCtx t;
+  if (!sc.get(blockIdx.x, t)) return;
+  f32x4_t acc[C::FM][C::FN];
+  tile_mma_dma<C>(t, al, bl, smem, acc);
   ep.template apply<C>(t, acc, smem);
 }
 

@@ -12,6 +12,7 @@ namespace dg {
 
 // ------------------------------------------------------------------ epilogues
 struct EpStoreF32 {        // out[group * split_stride + (row_base + r) * ldo + n0 + c] = v
+  static constexpr int kSmemBytes = 0;
   float* out; int ldo; size_t split_stride;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
@@ -24,6 +25,7 @@ struct EpStoreF32 {        // out[group * split_stride + (row_base + r) * ldo + 
 
 template <typename T>
 struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the same 16 features
+  static constexpr int kSmemBytes = 0;
   T* act; int F;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
@@ -49,11 +51,12 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
 // shared memory, free once the K loop has ended.
 template <typename T>
 struct EpHead {
+  static constexpr int kSmemBytes = kHeadTileBytes;
   float inv_t; SeedArg seeds; int n, canvas_index, step, V, nchunk;
   HeadPart* part; T* ptilde; float* logits;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
-    static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk && C::kSmemBytes >= kHeadTileBytes, "head tiles");
+    static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk, "head tiles");
     float* tile = reinterpret_cast<float*>(smem);
     for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kHeadLd + c] = v; });
     if (logits != nullptr)
@@ -107,6 +110,13 @@ static hipError_t launch(int grid, const SCHED& sc, const AL& al, const BL& bl, 
   return hipGetLastError();
 }
 
+template <class C, class SCHED, class AL, class BL, class EP>
+static hipError_t launch_dma(int grid, const SCHED& sc, const AL& al, const BL& bl, const EP& ep, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_dma<C, SCHED, AL, BL, EP>), dim3(grid), dim3(256), 0, s, sc, al, bl, ep);
+  return hipGetLastError();
+}
+
 // Split count for a small-M product: enough workgroups to fill the chip, at
 // least four 128-byte K slices per workgroup.
 SplitPlan plan_splits(int M, int N, int K, int bm, int bn, int elem_bytes, int target) {
@@ -126,10 +136,20 @@ SplitPlan plan_splits(int M, int N, int K, int bm, int bn, int elem_bytes, int t
 // small-M products (4 slices in registers) puts a whole slice's loads in flight
 // at once instead of walking it in two round trips.
 constexpr int kSplitStages = 5;
+// rows from which an unsplit product takes 128 x 128 DMA tiles
+constexpr int kDmaMinRows = 512;
 
 template <typename T>
 hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
                          SplitPlan sp, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // many rows, no split: 128 x 128 tiles through the DMA loop
+    if (sp.splits == 1 && M >= kDmaMinRows && K % 64 == 0) {
+      using C = TileCfgD<128, 128, 2>;
+      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K};
+      return launch_dma<C>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{part, N, 0}, s);
+    }
+  }
   using C = TileCfg<T, 64, 64, kSplitStages>;
   SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
   return launch<C, T>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
@@ -149,9 +169,14 @@ template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s) {
   if (V % 64) return hipErrorInvalidValue;
-  using C = TileCfg<T, kHeadChunk, kHeadChunk>;
   SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K};
   EpHead<T> ep{h.inv_t, h.seeds, h.n, h.canvas_index, h.step, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits};
+  if constexpr (sizeof(T) == 2) {
+    if (K % 64 == 0)
+      return launch_dma<TileCfgD<kHeadChunk, kHeadChunk, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
+                                                              ep, s);
+  }
+  using C = TileCfg<T, kHeadChunk, kHeadChunk>;
   return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, ep, s);
 }
 
@@ -159,6 +184,14 @@ template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
                               const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F,
                               hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (d % 64 == 0) {
+      // 64 rows x 64 features (gate and up interleaved: 128 B rows) per tile
+      SchedGroup<64, 128> sc{tiles, n_tiles, cdiv(F, 64), F, d, 64};
+      return launch_dma<TileCfgD<64, 128, 3>>(cap_tiles * sc.nt, sc, ALGather<T>{X, d, perm},
+                                              BLGateUp<T>{gate, up, (size_t)F * d, d}, EpSwiGLU<T>{act, F}, s);
+    }
+  }
   using C = TileCfg<T, 64, 64>;
   SchedGroup<64, 64> sc{tiles, n_tiles, cdiv(F, 32), F, d, 32};
   return launch<C, T>(cap_tiles * sc.nt, sc, ALGather<T>{X, d, perm}, BLGateUp<T>{gate, up, (size_t)F * d, d},
@@ -168,6 +201,13 @@ hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const 
 template <typename T>
 hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
                             const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (F % 64 == 0) {
+      SchedGroup<64, 128> sc{tiles, n_tiles, cdiv(d, 128), d, F, 128};
+      return launch_dma<TileCfgD<64, 128, 3>>(cap_tiles * sc.nt, sc, ALRows<T>{act, F},
+                                              BLExpert<T>{down, (size_t)d * F, F}, EpStoreF32{Y, d, 0}, s);
+    }
+  }
   using C = TileCfg<T, 64, 64>;
   SchedGroup<64, 64> sc{tiles, n_tiles, cdiv(d, 64), d, F, 64};
   return launch<C, T>(cap_tiles * sc.nt, sc, ALRows<T>{act, F}, BLExpert<T>{down, (size_t)d * F, F},
