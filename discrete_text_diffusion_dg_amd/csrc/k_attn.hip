@@ -85,6 +85,27 @@ __device__ __forceinline__ void store4(T* dst, const float* v) {
 }
 
 // ---- wide: 16 * NWQ query rows per workgroup sharing LDS-staged K / V^T tiles
+// bf16 V^T pieces are staged as fp16 (exact for |v| in [2^-14, 65504]) so that
+// the probabilities enter O^T += V^T P as one fp16 operand (11 significant
+// bits) instead of a two-term bf16 split.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = f32x2_to_f16x2(__uint_as_float(w[j] << 16), __uint_as_float(w[j] & 0xFFFF0000u));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ void mma16x16x32_f16(f32x4_t& acc, uint4 a, uint4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc, 0,
+                                               0, 0);
+}
+
 template <typename T, int HD, int NWQ>
 __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
@@ -134,7 +155,8 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   f32x4_t o[NDB];
 #pragma unroll
   for (int j = 0; j < NDB; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // bf16 path: m_run in base-2 units (score * cs)
+  const float cs = a.scale * 1.4426950408889634f;
 
   uint4 kr0[KCH], vr0[VCH], kr1[KCH], vr1[VCH];
   // K rows past the range are clamped to its last key; V^T rows are padded to
@@ -167,7 +189,9 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       const int c = tid + NTH * i;
-      *reinterpret_cast<uint4*>(sV + (c / (KT / EPC)) * LDV + (c % (KT / EPC)) * EPC) = SL == 0 ? vr0[i] : vr1[i];
+      uint4 v = SL == 0 ? vr0[i] : vr1[i];
+      if constexpr (sizeof(T) == 2) v = bf16x8_to_f16x8(v);
+      *reinterpret_cast<uint4*>(sV + (c / (KT / EPC)) * LDV + (c % (KT / EPC)) * EPC) = v;
     }
   };
   auto compute = [&](int buf, int t) __attribute__((always_inline)) {
@@ -186,57 +210,108 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
         mma16x16x32(sc[kb], kf, qf[s]);
       }
     }
-    float p[16];
-    float tmax = -INFINITY;
+    if constexpr (sizeof(T) == 2) {
+      // masks only where a tile crosses the end of the range or the causal diagonal
+      if (k0 + KT > kend || a.causal) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kpos = k0 + tile_key(kb, g4 * 4 + i);
-        float v = sc[kb][i] * a.scale;
-        if (kpos >= kend || (a.causal && kpos > qpos)) v = -INFINITY;
-        p[kb * 4 + i] = v;
-        tmax = fmaxf(tmax, v);
+          for (int i = 0; i < 4; ++i) {
+            const int kpos = k0 + tile_key(kb, g4 * 4 + i);
+            if (kpos >= kend || (a.causal && kpos > qpos)) sc[kb][i] = -INFINITY;
+          }
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run - m_new);
-    float lsum = 0.f;
+      // online softmax in base-2 units: z = score * scale * log2(e)
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float e = (p[j] == -INFINITY) ? 0.f : exp_fast(p[j] - m_new);
-      p[j] = e;
-      lsum += e;
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) o[j] *= alpha;
-    // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps.  With bf16
-    // operands the fp32 probabilities are split into a bf16 head and a bf16
-    // remainder (two MFMAs, ~16 significant bits): a single bf16 rounding of P
-    // would dominate the output error, while beyond 16 bits the fp32 summation
-    // over the keys does (a third term was measured to change nothing).
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax * cs);
+      const float mo = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: every term is 0
+      if (__ballot(m_new != m_run) != 0) {                 // rescale only when some running max moved
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mo);
+        l_run *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      Frag<T> pf[NT];
-      float rest[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rest[i] = p[(2 * ks) * 4 + i];
-        rest[4 + i] = p[(2 * ks + 1) * 4 + i];
+        for (int j = 0; j < NDB; ++j) o[j] *= alpha;
       }
-      split_p(pf, rest);
+      m_run = m_new;
+      uint32_t ph[8];                                      // fp16 pairs of exp2(z - m), keys in tile order
+      float lsum = 0.f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        Frag<T> vf;
-        lds_frag(vf, sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
+      for (int kb = 0; kb < 4; ++kb) {
+        float e[4];
 #pragma unroll
-        for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
+        for (int i = 0; i < 4; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], cs, -mo));
+          lsum += e[i];
+        }
+        ph[kb * 2] = f32x2_to_f16x2(e[0], e[1]);
+        ph[kb * 2 + 1] = f32x2_to_f16x2(e[2], e[3]);
+      }
+      l_run += lsum;
+      // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps of fp16 operands
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 pf = make_uint4(ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint4 vf = *reinterpret_cast<const uint4*>(sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
+          mma16x16x32_f16(o[db], vf, pf);
+        }
+      }
+    } else {
+      float p[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kpos = k0 + tile_key(kb, g4 * 4 + i);
+          float v = sc[kb][i] * a.scale;
+          if (kpos >= kend || (a.causal && kpos > qpos)) v = -INFINITY;
+          p[kb * 4 + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = (p[j] == -INFINITY) ? 0.f : exp_fast(p[j] - m_new);
+        p[j] = e;
+        lsum += e;
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+      // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps (fp32 operands)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag<T> pf[NT];
+        float rest[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rest[i] = p[(2 * ks) * 4 + i];
+          rest[4 + i] = p[(2 * ks + 1) * 4 + i];
+        }
+        split_p(pf, rest);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          Frag<T> vf;
+          lds_frag(vf, sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
+#pragma unroll
+          for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
+        }
       }
     }
   };
+
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   // tile t: its data came through register slot t % 2 into LDS stage t % 2.
@@ -293,7 +368,7 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
       *reinterpret_cast<float4*>(po + db * 16 + g4 * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
     if (g4 == 0) {
       float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
-      pm[0] = m_run;
+      pm[0] = sizeof(T) == 2 ? m_run * 0.6931471805599453f : m_run;   // the merge takes natural units
       pm[1] = l_run;
     }
   }
