@@ -254,6 +254,7 @@ struct Offsets {
 // to fill the chip (~512), each split at least four 128-byte K steps.  The
 // chunk scales are applied in the operand loader, so splits need not follow
 // the 128-id chunks.
+constexpr int kHeadChunkIds = 128;   // vocabulary ids per head chunk (the sampler's unit)
 void selfcond_plan(int R, int d, int V, int esz, int* splits, int* kchunk) {
   const int bm = (R >= 128 && d >= 128) ? 128 : 64;
   const int tiles = ((R + bm - 1) / bm) * ((d + bm - 1) / bm);
@@ -262,7 +263,8 @@ void selfcond_plan(int R, int d, int V, int esz, int* splits, int* kchunk) {
   const int max_sp = V / (4 * bk);
   if (sp > max_sp) sp = max_sp;
   if (sp < 1) sp = 1;
-  const int kc = ((V + sp - 1) / sp + bk - 1) / bk * bk;
+  // whole 128-id chunks per split: each split applies its chunks' probability scales
+  const int kc = ((V + sp - 1) / sp + kHeadChunkIds - 1) / kHeadChunkIds * kHeadChunkIds;
   *kchunk = kc;
   *splits = (V + kc - 1) / kc;
 }

@@ -309,7 +309,7 @@ struct TileCfgD {
   static constexpr int STAGE = (BM + BN) * ROWB;            // bytes of one slice of the tile
   static constexpr int NI = (BM + BN) / 8 / 4;              // 8-row load groups per wave per slice
   static_assert((BM + BN) % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
-  static constexpr int kSmemBytes = S_ * STAGE;
+  static constexpr int kSmemBytes = S_ * STAGE + S_ * BM * 4;   // slices, then per-slice row scales (scaled loaders)
 };
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
@@ -331,6 +331,24 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
                : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(g)
                : "memory");
 }
+
+// 4 bytes per lane: lane i writes lds_addr + 4 * i.
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_addr) {
+  uint32_t m0save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(m0save)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(g)
+               : "memory");
+}
+
+// Loader traits: a loader that defines kChunkScale = true also supplies a
+// per-row scale for every 128-element K chunk (scale_ptr(t, r, chunk)); the
+// loop then sums each chunk's products apart and adds them in times the row's
+// scale, in fp32.
+template <class AL, class = void>
+struct chunk_scaled : std::false_type {};
+template <class AL>
+struct chunk_scaled<AL, std::void_t<decltype(AL::kChunkScale)>> : std::integral_constant<bool, AL::kChunkScale> {};
 
 template <class C, class AL, class BL>
 __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, const BL& bl, char* smem,
@@ -364,13 +382,38 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     dst[j] = (uint32_t)(gi * 8 * C::ROWB);
   }
   const uint32_t lbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
+  constexpr bool SCALED = chunk_scaled<AL>::value;
+  static_assert(!SCALED || (C::STAGES == 2 && C::BM == 128), "chunk scales: two stages, 128 rows");
+  // chunk scales: wave 0 brings the 128 rows' scales of a slice's chunk with the slice
+  const char* ssrc[2] = {nullptr, nullptr};
+  if constexpr (SCALED) {
+    if (w == 0) {
+      bool valid;
+      ssrc[0] = static_cast<const char*>(al.scale_ptr(t, lane, t.k0 / 128, valid));
+      ssrc[1] = static_cast<const char*>(al.scale_ptr(t, 64 + lane, t.k0 / 128, valid));
+    }
+  }
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const uint32_t sb = lbase + (uint32_t)((kt % C::STAGES) * C::STAGE);
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) lds_dma16(src[j] + (size_t)kt * 128, sb + dst[j]);
+    if constexpr (SCALED) {
+      if (w == 0) {
+        const uint32_t slot = lbase + (uint32_t)(C::STAGES * C::STAGE + (kt % C::STAGES) * C::BM * 4);
+        lds_dma4(ssrc[0] + (size_t)(kt >> 1) * 4, slot);
+        lds_dma4(ssrc[1] + (size_t)(kt >> 1) * 4, slot + 256);
+      }
+    }
   };
   const int c16 = lane & 15, g4 = lane >> 4, sw = (c16 >> 1) & 7;
   const int aoff = (wm * C::WM + c16) * C::ROWB, boff = (C::BM + wn * C::WN + c16) * C::ROWB;
+  f32x4_t accc[SCALED ? C::FM : 1][SCALED ? C::FN : 1];   // the current chunk's products (scaled loaders)
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::FN; ++b) accc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   auto kstep = [&](const char* sb, int kk) __attribute__((always_inline)) {
     const int ch = ((kk * 4 + g4) ^ sw) * 16;
     Frag<bf16> fa[C::FM], fb[C::FN];
@@ -381,7 +424,10 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
 #pragma unroll
     for (int a = 0; a < C::FM; ++a)
 #pragma unroll
-      for (int b = 0; b < C::FN; ++b) mma16x16x32(acc[a][b], fa[a], fb[b]);
+      for (int b = 0; b < C::FN; ++b) {
+        if constexpr (SCALED) mma16x16x32(accc[a][b], fa[a], fb[b]);
+        else mma16x16x32(acc[a][b], fa[a], fb[b]);
+      }
   };
 #pragma unroll
   for (int p = 0; p < C::STAGES - 1; ++p)
@@ -395,6 +441,23 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     const char* sb = smem + (kt % C::STAGES) * C::STAGE;
     kstep(sb, 0);
     kstep(sb, 1);
+    if constexpr (SCALED) {
+      if ((kt & 1) || kt == nk - 1) {   // a 128-element chunk (or the range) ends: acc += scale(row) * chunk products
+        const float* sc = reinterpret_cast<const float*>(smem + C::STAGES * C::STAGE + (kt % C::STAGES) * C::BM * 4);
+#pragma unroll
+        for (int a = 0; a < C::FM; ++a) {
+          const float4 s4 = *reinterpret_cast<const float4*>(sc + wm * C::WM + a * 16 + g4 * 4);
+          const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[a][b][i] = __builtin_fmaf(sv[i], accc[a][b][i], acc[a][b][i]);
+              accc[a][b][i] = 0.f;
+            }
+        }
+      }
+    }
   }
   __syncthreads();   // the epilogue may reuse the shared memory
 }

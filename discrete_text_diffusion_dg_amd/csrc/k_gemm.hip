@@ -139,6 +139,24 @@ constexpr int kSplitStages = 5;
 // rows from which an unsplit product takes 128 x 128 DMA tiles
 constexpr int kDmaMinRows = 512;
 
+// exp(z - m_c) rows (row-locating) with the probability scale of each 128-id
+// chunk: scale[row][c] multiplies the chunk's fp32 partial products.
+template <typename T>
+struct ALChunkScaled {
+  static constexpr bool kChunkScale = true;
+  using Row = const void*;
+  const T* p; int lda; const float* scale; int nchunk;
+  __device__ const void* row(const TileCtx& t, int r, bool& valid) const {
+    valid = r < t.rows;
+    return p + (size_t)(t.m0 + (valid ? r : 0)) * lda;
+  }
+  __device__ const void* scale_ptr(const TileCtx& t, int r, int chunk, bool& valid) const {
+    valid = r < t.rows;
+    return scale + (size_t)(t.m0 + (valid ? r : 0)) * nchunk + chunk;
+  }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
+};
+
 template <typename T>
 hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
                          SplitPlan sp, hipStream_t s) {
@@ -217,6 +235,13 @@ hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* t
 template <typename T>
 hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt, float* part, int M, int N, int K,
                          int splits, int kchunk, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (M >= 128 && N >= 128 && kchunk % 128 == 0 && K % 64 == 0) {
+      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk};
+      return launch_dma<TileCfgD<128, 128, 2>>(sc.mt * sc.nt * splits, sc, ALChunkScaled<T>{P, K, scale, nchunk},
+                                               BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
+    }
+  }
   const ALScaled<T> al{P, K, scale, nchunk};
   if (M >= 128 && N >= 128) {
     using C = TileCfg<T, 128, 128>;
