@@ -167,6 +167,13 @@ hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, 
       SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K};
       return launch_dma<C>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{part, N, 0}, s);
     }
+    // few rows, split along K: 64 x 64 tiles, a split's slices all in flight at once
+    if (sp.kchunk % 64 == 0 && K % 64 == 0) {
+      using C = TileCfgD<64, 64, kSplitStages - 1>;
+      SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
+      return launch_dma<C>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
+                           EpStoreF32{part, N, (size_t)M * N}, s);
+    }
   }
   using C = TileCfg<T, 64, 64, kSplitStages>;
   SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
