@@ -497,18 +497,32 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       DG_HIP(gemm_partials<T>(static_cast<const T*>(st->attn), Hq * hd, static_cast<const T*>(L.wo), Hq * hd,
                               st->part, M, d, Hq * hd, p_o, s));
     }
-    {
-      StageTimer tm(st, DG_STAGE_NORM, s);
-      DG_HIP(add_norm<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn, s));
-    }
-    {
-      StageTimer tm(st, DG_STAGE_ROUTER, s);
-      float* rlog = st->rlog + (size_t)l * st->R * E;
-      int* ridx = st->ridx + (size_t)l * st->R * k;
-      // the split-K partial buffer is free here (the output projection's
-      // partials were consumed by add_norm); it holds the router's partial logits
-      DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
-                       st->tiles, st->n_tiles, st->rcnt, st->part, s));
+    float* rlog = st->rlog + (size_t)l * st->R * E;
+    int* ridx = st->ridx + (size_t)l * st->R * k;
+    if (router_fused_ok(M, d, E, k)) {
+      // few routed entries: the norm's workgroups form the router logits, top-k
+      // and weights; one workgroup sorts the entries by expert
+      {
+        StageTimer tm(st, DG_STAGE_NORM, s);
+        DG_HIP(add_norm_router<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn,
+                                  static_cast<const T*>(L.w_router), E, k, rlog, ridx, st->rw, s));
+      }
+      {
+        StageTimer tm(st, DG_STAGE_ROUTER, s);
+        DG_HIP(route_sort(ridx, M, k, E, st->perm, st->pos, st->tiles, st->n_tiles, s));
+      }
+    } else {
+      {
+        StageTimer tm(st, DG_STAGE_NORM, s);
+        DG_HIP(add_norm<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn, s));
+      }
+      {
+        StageTimer tm(st, DG_STAGE_ROUTER, s);
+        // the split-K partial buffer is free here (the output projection's
+        // partials were consumed by add_norm); it holds the router's partial logits
+        DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
+                         st->tiles, st->n_tiles, st->rcnt, st->part, s));
+      }
     }
     // weight streaming while experts see at most ~64 routed rows on average
     // (the batch-1 shapes); the LDS-tiled engine once they see many

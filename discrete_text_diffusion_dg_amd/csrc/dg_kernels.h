@@ -136,6 +136,15 @@ int router_ksplits(int M, int d, int E);
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
                   int* pos, int4* tiles, int* n_tiles, int* cnt, float* part, hipStream_t s);
+// Few routed entries (M * k <= 4096, E a power of two <= 128): add_norm plus
+// the router logits, top-k and softmax of each row (rlog, idx, w), then the
+// expert-sorted order (perm, pos, tiles) in one workgroup.
+bool router_fused_ok(int M, int d, int E, int k);
+template <typename T>
+hipError_t add_norm_router(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
+                           const T* wr, int E, int k, float* rlog, int* idx, float* w, hipStream_t s);
+hipError_t route_sort(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
+                      hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
 hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,

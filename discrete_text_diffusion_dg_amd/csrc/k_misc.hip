@@ -59,7 +59,7 @@ __device__ __forceinline__ void store_row4(float* p, float a, float b, float c, 
 // Stores the updated residual row v and y = rnd(v * g / sqrt(mean(v^2) + eps)).
 template <typename T>
 __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int d, const float* g, float eps,
-                                           float* hrow, T* xrow) {
+                                           float* hrow, T* xrow, float* xs = nullptr) {
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = (blockDim.x + 63) >> 6;
   float ss = 0.f;
@@ -79,6 +79,10 @@ __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int 
       *reinterpret_cast<float4*>(hrow + c) = v[j];
       const float4 gg = *reinterpret_cast<const float4*>(g + c);
       store_row4(xrow + c, v[j].x * inv * gg.x, v[j].y * inv * gg.y, v[j].z * inv * gg.z, v[j].w * inv * gg.w);
+      if (xs != nullptr)   // the rounded row, as the products downstream see it
+        *reinterpret_cast<float4*>(xs + c) =
+            make_float4(Num<T>::round(v[j].x * inv * gg.x), Num<T>::round(v[j].y * inv * gg.y),
+                        Num<T>::round(v[j].z * inv * gg.z), Num<T>::round(v[j].w * inv * gg.w));
     }
 }
 
@@ -561,6 +565,205 @@ template hipError_t router<float>(const float*, const float*, int, int, int, int
 template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, float*, int*, float*, int*, int*,
                                  int4*, int*, int*, float*, hipStream_t);
 
+// ------------------------------------------------------------------ router for few entries
+// When the routed entries of a launch fit one workgroup (M * k <= 4096), the
+// router is two launches instead of three plus the norm:
+//  k_add_norm_router: the add-norm workgroup of a row also forms the row's E
+//    router logits from the rounded normed row (E groups of threads, each
+//    thread a fixed interleave of 8-element pieces so a group reads whole
+//    cache lines of W_r; pieces in order, then a fixed shuffle tree), its top
+//    k -- ties to the lower expert id -- and the softmax over the selected;
+//  k_route_sort (one workgroup): the expert-sorted order of all M * k
+//    entries, rows of an expert in row order: per (entry block, wave) counts
+//    and in-wave ranks by ballots, exclusive prefixes per expert, expert
+//    offsets, the 64-row tile list, pos and perm.
+constexpr int kSortThreads = 1024, kSortMaxEntries = 4096, kSortBlocks = kSortMaxEntries / kSortThreads;
+constexpr int kRouterPieces = 16;
+
+bool router_fused_ok(int M, int d, int E, int k) {
+  const int nt = row_threads(d);
+  // at most kRouterPieces 8-element pieces of W_r per thread, all loaded at once
+  return M * k <= kSortMaxEntries && E <= 128 && k <= 8 && (E & (E - 1)) == 0 && nt >= 64 && E <= nt && nt / E <= 64 &&
+         d % (8 * (nt / E)) == 0 && d <= kMaxModel && d / (8 * (nt / E)) <= kRouterPieces;
+}
+
+template <typename T>
+__device__ __forceinline__ void wr_piece(const T* p, float (&w)[8]);
+template <>
+__device__ __forceinline__ void wr_piece(const bf16* p, float (&w)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { w[2 * j] = __uint_as_float(x[j] << 16); w[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u); }
+}
+template <>
+__device__ __forceinline__ void wr_piece(const float* p, float (&w)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int S, int M, int d, const float* g,
+                                                         float eps, float* H, T* xn, const T* wr, int E, int k,
+                                                         float* rlog, int* idx, float* w) {
+  __shared__ float xs[kMaxModel];
+  __shared__ float lg[128];
+  __shared__ int sel_e[8];
+  __shared__ float sel_v[8];
+  const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
+  float4 v[kRowChunks];
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + tid) * 4;
+      const float4 p = sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c);
+      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
+      add4(x, p);
+      v[j] = x;
+    }
+  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d, xs);
+  __syncthreads();
+  // logit of expert e: tpe threads, thread sl taking pieces sl, sl + tpe, ...
+  const int tpe = blockDim.x / E, e = tid / tpe, sl = tid % tpe;
+  const T* wrow = wr + (size_t)e * d;
+  const int ppt = d / (8 * tpe);                  // pieces of this thread (<= kRouterPieces)
+  float wv[kRouterPieces][8];
+#pragma unroll
+  for (int u = 0; u < kRouterPieces; ++u)         // every load issued before any is used (pieces past ppt
+    wr_piece(wrow + (sl + min(u, ppt - 1) * tpe) * 8, wv[u]);   // repeat the last one and are not added)
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < kRouterPieces; ++u)
+    if (u < ppt) {
+      const int c = sl + u * tpe;
+      const float4 x0 = *reinterpret_cast<const float4*>(xs + c * 8), x1 = *reinterpret_cast<const float4*>(xs + c * 8 + 4);
+      acc += x0.x * wv[u][0]; acc += x0.y * wv[u][1]; acc += x0.z * wv[u][2]; acc += x0.w * wv[u][3];
+      acc += x1.x * wv[u][4]; acc += x1.y * wv[u][5]; acc += x1.z * wv[u][6]; acc += x1.w * wv[u][7];
+    }
+  for (int o = tpe >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (sl == 0) {
+    lg[e] = acc;
+    rlog[(size_t)r * E + e] = acc;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  if (E > 32) {
+    topk_rounds(lg, E, k, lane, sel_e, sel_v);
+  } else if (lane < E) {
+    // rank of expert lane: the logits that beat it (greater, or equal with a lower id)
+    const float x = lg[lane];
+    int rank = 0;
+    for (int q = 0; q < E; ++q) {
+      const float o = lg[q];
+      rank += (o > x) || (o == x && q < lane);
+    }
+    if (rank < k) { sel_e[rank] = lane; sel_v[rank] = x; }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");   // one wave: LDS writes before reads
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  if (lane < k) {
+    const float mx = sel_v[0];
+    float sum = 0.f;
+    for (int u = 0; u < k; ++u) sum += expf(sel_v[u] - mx);
+    idx[(size_t)r * k + lane] = sel_e[lane];
+    w[(size_t)r * k + lane] = expf(sel_v[lane] - mx) / sum;
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int MK, int k, int E, int* perm, int* pos,
+                                                            int4* tiles, int* n_tiles) {
+  constexpr int NW = kSortThreads / 64;
+  __shared__ int cnt[kSortBlocks][NW][128];
+  __shared__ int offs[128], toff[129];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int nb = (MK + kSortThreads - 1) / kSortThreads;
+  int ex[kSortBlocks], rk[kSortBlocks];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+#pragma unroll
+  for (int j = 0; j < kSortBlocks; ++j) {
+    ex[j] = -1; rk[j] = 0;
+    if (j < nb) {
+      const int i = j * kSortThreads + t;
+      ex[j] = i < MK ? idx[i] : -1;
+      cnt[j][wv][lane] = 0;
+      cnt[j][wv][lane + 64] = 0;
+      // entries of this wave in entry order: one ballot per distinct expert
+      uint64_t left = __ballot(ex[j] >= 0);
+      while (left) {
+        const int leader = __ffsll((unsigned long long)left) - 1;
+        const int e = __builtin_amdgcn_readlane(ex[j], leader);
+        const uint64_t m = __ballot(ex[j] == e);
+        if (ex[j] == e) rk[j] = __popcll(m & lt);
+        if (lane == 0) cnt[j][wv][e] = __popcll(m);
+        left &= ~m;
+      }
+    }
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over (block, wave) in entry order; the total
+  if (t < E) {
+    int run = 0;
+    for (int j = 0; j < nb; ++j)
+      for (int q = 0; q < NW; ++q) {
+        const int c = cnt[j][q][t];
+        cnt[j][q][t] = run;
+        run += c;
+      }
+    offs[t] = run;
+  }
+  __syncthreads();
+  // exclusive prefixes over experts of the row counts and of the 64-row tile
+  // counts: one wave, two experts per lane, a shuffle scan
+  if (t < 64) {
+    const int x0 = 2 * t, x1 = 2 * t + 1;
+    const int c0 = x0 < E ? offs[x0] : 0, c1 = x1 < E ? offs[x1] : 0;
+    const int n0 = (c0 + 63) / 64, n1 = (c1 + 63) / 64;
+    int rs = c0 + c1, ts = n0 + n1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ro = __shfl_up(rs, o, 64), to = __shfl_up(ts, o, 64);
+      if (t >= o) { rs += ro; ts += to; }
+    }
+    const int rx = rs - c0 - c1, tx = ts - n0 - n1;   // exclusive
+    if (x0 < E) { offs[x0] = rx; toff[x0] = tx; }
+    if (x1 < E) { offs[x1] = rx + c0; toff[x1] = tx + n0; }
+    if (t == 63) { toff[E] = ts; *n_tiles = ts; }
+  }
+  __syncthreads();
+  for (int x = t; x < E; x += kSortThreads) {
+    const int c = (x + 1 < E ? offs[x + 1] : MK) - offs[x];
+    for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
+      tiles[toff[x] + q] = make_int4(x, offs[x] + q * 64, min(64, c - q * 64), 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kSortBlocks; ++j) {
+    if (ex[j] < 0) continue;
+    const int i = j * kSortThreads + t;
+    const int p = offs[ex[j]] + cnt[j][wv][ex[j]] + rk[j];
+    pos[i] = p;
+    perm[p] = i / k;
+  }
+}
+
+template <typename T>
+hipError_t add_norm_router(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
+                           const T* wr, int E, int k, float* rlog, int* idx, float* w, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!router_fused_ok(M, d, E, k)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_add_norm_router<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, wr, E,
+                     k, rlog, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t route_sort(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
+                      hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (M * k > kSortMaxEntries || E > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), 0, s, idx, M * k, k, E, perm, pos, tiles, n_tiles);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ transpose
 template <typename T>
 __global__ void k_transpose(const T* src, T* dst, int rows, int cols) {
@@ -598,6 +801,8 @@ hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int 
 }
 
 #define DG_INST(T)                                                                                               \
+  template hipError_t add_norm_router<T>(const float*, int, int, int, const float*, float, float*, T*, const T*,  \
+                                         int, int, float*, int*, float*, hipStream_t);                          \
   template hipError_t embed_norm<T>(const T*, const int32_t*, const float*, int, int, int, int, const float*,  \
                                     float, float*, T*, hipStream_t);                                            \
   template hipError_t add_norm<T>(const float*, int, int, int, const float*, float, float*, T*, hipStream_t);   \
