@@ -424,7 +424,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
   const T* Vt = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * HD * a.kv_stride;
 
   f32x4_t o[QB][NDB];
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB];              // m_run in base-2 units (score * cs)
+  const float cs = a.scale * 1.4426950408889634f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
@@ -461,33 +462,44 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) mma16x16x32(sc[kb], kf[buf][kb][s], qf[qb][s]);
       }
-      float p[16];
+      // masks only where a tile crosses the end of the range or the causal diagonal
+      if (k0 + KT > kend || a.causal) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kpos = k0 + tile_key(kb, g4 * 4 + i);
+            if (kpos >= kend || (a.causal && kpos > qpos[qb])) sc[kb][i] = -INFINITY;
+          }
+      }
+      // online softmax in base-2 units: z = score * scale * log2(e)
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kpos = k0 + tile_key(kb, g4 * 4 + i);
-          float v = sc[kb][i] * a.scale;
-          if (kpos >= kend || (a.causal && kpos > qpos[qb])) v = -INFINITY;
-          p[kb * 4 + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[qb], tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run[qb] - m_new);
+      const float m_new = fmaxf(m_run[qb], tmax * cs);
+      const float mo = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: every term is 0
+      if (__ballot(m_new != m_run[qb]) != 0) {             // rescale only when some running max moved
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mo);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) o[qb][j] *= alpha;
+      }
+      m_run[qb] = m_new;
+      float p[16];
       float lsum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = (p[j] == -INFINITY) ? 0.f : exp_fast(p[j] - m_new);
-        p[j] = e;
-        lsum += e;
-      }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-      m_run[qb] = m_new;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) o[qb][j] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], cs, -mo));
+          p[kb * 4 + i] = e;
+          lsum += e;
+        }
+      l_run[qb] += lsum;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         Frag<T> pf[NT];
@@ -506,7 +518,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
     }
   };
   // the wave's tiles w, w + NW, ...: the next one is loaded (unconditionally,
-  // clamped to the last tile) while the current one is computed
+  // clamped to the last tile) while the current one is computed (a three-tile
+  // ring was measured slower on the small canvas shape: 12.7 against 11.0 us)
   if (w < ntiles) load(0, w);
   for (int t0 = w; t0 < ntiles; t0 += 2 * NW) {
 #pragma unroll
@@ -543,11 +556,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float mv = sm_m[v][qb][q];
-      const float f = mv == -INFINITY ? 0.f : expf(mv - M);
+      const float f = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
       L += f * sm_l[v][qb][q];
       sm_m[v][qb][q] = f;                       // the slot now holds the wave's factor
     }
-    sm_tot[0][qb][q] = M;
+    sm_tot[0][qb][q] = M * 0.6931471805599453f;   // natural units for the split merge
     sm_tot[1][qb][q] = L;
   }
   __syncthreads();
