@@ -480,9 +480,15 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     T* vc = static_cast<T*>(st->vc) + st->kv_layer_elems * l;
     {
       StageTimer tm(st, DG_STAGE_QKV, s);
-      DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, s));
-      DG_HIP(rope_scatter<T>(st->part, p_qkv.splits, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv,
-                             hd, st->ctx_pad, st->ctx, s));
+      if (qkv_rope_ok(d, hd, (int)m->esz)) {
+        // one head per tile, RoPE and the cache scatter in the product's epilogue
+        DG_HIP(gemm_qkv_rope<T>(xn, static_cast<const T*>(L.wqkv), M, d, hd, st->rope, static_cast<T*>(st->q), kc, vc,
+                                nq, Hq, Hkv, st->ctx_pad, st->ctx, s));
+      } else {
+        DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, s));
+        DG_HIP(rope_scatter<T>(st->part, p_qkv.splits, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv,
+                               hd, st->ctx_pad, st->ctx, s));
+      }
     }
     {
       StageTimer tm(st, DG_STAGE_ATTN, s);

@@ -64,6 +64,13 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
 template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s);
+// The fused QKV projection of rows r = b * n + i with RoPE at position ctx + i
+// applied to q and k in its epilogue: q -> q [M][Hq * hd], k -> K cache rows,
+// v -> V^T cache columns (the layouts rope_scatter writes).  One head per tile.
+bool qkv_rope_ok(int d, int hd, int elem_bytes);
+template <typename T>
+hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const float2* rope, T* q, T* kc, T* vc,
+                         int n, int Hq, int Hkv, int stride, int ctx, hipStream_t s);
 // act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,

@@ -69,6 +69,50 @@ struct EpHead {
   }
 };
 
+// Fused QKV projection tile -> RoPE and scatter: the tile covers BM rows x one
+// head (BN == hd columns of the [q heads | k heads | v heads] projection).  q
+// and k are rotated (rotate-half, table rope[pos][j] = (cos, sin)) and stored
+// to the query buffer / the K cache row pos; v goes to the transposed V cache
+// column pos.  Row r of the product is (request r / n, position ctx + r % n).
+template <typename T, int HD>
+struct EpQKV {
+  static constexpr int kLd = HD + 4;
+  static constexpr int kSmemBytes = 128 * kLd * 4;         // at most 128 rows staged
+  const float2* rope; T* q; T* kc; T* vc;
+  int n, Hq, Hkv, stride, ctx;
+  template <class C>
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
+    static_assert(C::BN == HD && C::BM <= 128, "one head per tile");
+    float* tile = reinterpret_cast<float*>(smem);
+    for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kLd + c] = v; });
+    __syncthreads();
+    constexpr int half = HD / 2;
+    const int head = t.n0 / HD;
+    if (head < Hq + Hkv) {
+      for (int u = threadIdx.x; u < C::BM * half; u += blockDim.x) {
+        const int r = u / half, j = u % half;
+        if (r >= t.rows) continue;
+        const int row = t.m0 + r, b = row / n, pos = ctx + row % n;
+        const float a = tile[r * kLd + j], bb = tile[r * kLd + j + half];
+        const float2 cs = rope[(size_t)pos * half + j];
+        const float o1 = a * cs.x - bb * cs.y, o2 = bb * cs.x + a * cs.y;
+        T* dst = head < Hq ? q + (size_t)row * Hq * HD + head * HD
+                           : kc + (((size_t)b * Hkv + (head - Hq)) * stride + pos) * HD;
+        Num<T>::store(dst + j, o1);
+        Num<T>::store(dst + j + half, o2);
+      }
+    } else {
+      const int kh = head - Hq - Hkv;
+      for (int u = threadIdx.x; u < C::BM * HD; u += blockDim.x) {
+        const int c = u / C::BM, r = u % C::BM;           // consecutive threads: consecutive positions
+        if (r >= t.rows) continue;
+        const int row = t.m0 + r, b = row / n, pos = ctx + row % n;
+        Num<T>::store(vc + (((size_t)b * Hkv + kh) * HD + c) * stride + pos, tile[r * kLd + c]);
+      }
+    }
+  }
+};
+
 // A rows of exp(z - m_c) (128-id chunks c) times the chunk's probability scale
 // scale[row][c], in fp32, rounded to the operand type: the softmax @ E operand.
 template <typename T>
@@ -190,6 +234,42 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
                       EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
+template <typename T, int HD>
+static hipError_t qkv_rope_hd(const T* xn, const T* wqkv, int M, int K, const float2* rope, T* q, T* kc, T* vc, int n,
+                              int Hq, int Hkv, int stride, int ctx, hipStream_t s) {
+  const int N = (Hq + 2 * Hkv) * HD;
+  const EpQKV<T, HD> ep{rope, q, kc, vc, n, Hq, Hkv, stride, ctx};
+  if constexpr (sizeof(T) == 2) {
+    if (M <= 512) {
+      SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K};
+      return launch_dma<TileCfgD<32, HD, 4>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
+    }
+    SchedDense<128, HD> sc{M, N, K, cdiv(M, 128), N / HD, 1, K};
+    return launch_dma<TileCfgD<128, HD, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
+  } else {
+    using C = TileCfg<T, 64, HD>;
+    SchedDense<64, HD> sc{M, N, K, cdiv(M, 64), N / HD, 1, K};
+    return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
+  }
+}
+
+bool qkv_rope_ok(int d, int hd, int elem_bytes) {
+  if (elem_bytes == 2) return (hd == 64 || hd == 128) && d % 64 == 0;
+  return hd == 64 && d % 32 == 0;
+}
+
+template <typename T>
+hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const float2* rope, T* q, T* kc, T* vc,
+                         int n, int Hq, int Hkv, int stride, int ctx, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!qkv_rope_ok(d, hd, (int)sizeof(T))) return hipErrorInvalidValue;
+  if (hd == 64) return qkv_rope_hd<T, 64>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, ctx, s);
+  if constexpr (sizeof(T) == 2) {
+    return qkv_rope_hd<T, 128>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, ctx, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s) {
@@ -267,6 +347,8 @@ hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt
                                             SplitPlan, hipStream_t);                                    \
   template hipError_t gemm_lm_head<T>(const T*, int, const T*, int, int, int, int, const HeadArgs<T>&,      \
                                       hipStream_t);                                                     \
+  template hipError_t gemm_qkv_rope<T>(const T*, const T*, int, int, int, const float2*, T*, T*, T*, int, int, \
+                                       int, int, int, hipStream_t);                                     \
   template hipError_t gemm_expert_gateup<T>(const T*, const int*, const T*, const T*, T*, const int4*,    \
                                             const int*, int, int, int, hipStream_t);                    \
   template hipError_t gemm_expert_down<T>(const T*, const T*, float*, const int4*, const int*, int, int,  \
