@@ -505,6 +505,10 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     }
     float* rlog = st->rlog + (size_t)l * st->R * E;
     int* ridx = st->ridx + (size_t)l * st->R * k;
+    // weight streaming while experts see at most ~64 routed rows on average
+    // (the batch-1 shapes); the LDS-tiled engine once they see many
+    const bool stream = stream_ok && (size_t)M * k <= (size_t)64 * E;
+    const int tile_rows = stream ? 64 : expert_group_tile_rows(d, F, m->esz);
     if (router_fused_ok(M, d, E, k)) {
       // few routed entries: the norm's workgroups form the router logits, top-k
       // and weights; one workgroup sorts the entries by expert
@@ -515,7 +519,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       }
       {
         StageTimer tm(st, DG_STAGE_ROUTER, s);
-        DG_HIP(route_sort(ridx, M, k, E, st->perm, st->pos, st->tiles, st->n_tiles, s));
+        DG_HIP(route_sort(ridx, M, k, E, tile_rows, st->perm, st->pos, st->tiles, st->n_tiles, s));
       }
     } else {
       {
@@ -527,12 +531,9 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
         // the split-K partial buffer is free here (the output projection's
         // partials were consumed by add_norm); it holds the router's partial logits
         DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
-                         st->tiles, st->n_tiles, st->rcnt, st->part, s));
+                         st->tiles, st->n_tiles, tile_rows, st->rcnt, st->part, s));
       }
     }
-    // weight streaming while experts see at most ~64 routed rows on average
-    // (the batch-1 shapes); the LDS-tiled engine once they see many
-    const bool stream = stream_ok && (size_t)M * k <= (size_t)64 * E;
     {
       StageTimer tm(st, DG_STAGE_EXPERT_UP, s);
       if (stream)

@@ -38,7 +38,8 @@ struct HeadArgs {
 };
 
 // One expert-routed tile: (expert, first gathered row, rows, unused).
-// Capacity of the tile list for R rows routed to k experts each, 64-row tiles.
+// Capacity of the tile list for R rows routed to k experts each, tiles of at
+// least 64 rows.
 inline int expert_tile_capacity(int rows, int top_k, int n_experts) {
   return (rows * top_k + 63) / 64 + n_experts;
 }
@@ -71,6 +72,10 @@ bool qkv_rope_ok(int d, int hd, int elem_bytes);
 template <typename T>
 hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const float2* rope, T* q, T* kc, T* vc,
                          int n, int Hq, int Hkv, int stride, int ctx, hipStream_t s);
+// Rows per tile of the expert-grouped products (the router writes its tile
+// list with this many rows per tile for them): 128 on the bf16 LDS-DMA tile
+// loop, else 64.
+int expert_group_tile_rows(int d, int F, size_t elem_bytes);
 // act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
@@ -142,7 +147,7 @@ int router_rows_per_block(int E);
 int router_ksplits(int M, int d, int E);
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int* cnt, float* part, hipStream_t s);
+                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, hipStream_t s);
 // Few routed entries (M * k <= 4096, E a power of two <= 128): add_norm plus
 // the router logits, top-k and softmax of each row (rlog, idx, w), then the
 // expert-sorted order (perm, pos, tiles) in one workgroup.
@@ -150,8 +155,8 @@ bool router_fused_ok(int M, int d, int E, int k);
 template <typename T>
 hipError_t add_norm_router(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
                            const T* wr, int E, int k, float* rlog, int* idx, float* w, hipStream_t s);
-hipError_t route_sort(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
-                      hipStream_t s);
+hipError_t route_sort(const int* idx, int M, int k, int E, int tile_rows, int* perm, int* pos, int4* tiles,
+                      int* n_tiles, hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
 hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,

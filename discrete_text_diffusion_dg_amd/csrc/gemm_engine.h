@@ -85,8 +85,16 @@ struct SchedGroup {
   const int* n_tiles;
   int nt, N, K, bn;      // bn: output columns per tile
   __device__ bool get(int bid, TileCtx& t) const {
-    const int ti = bid / nt, tn = bid % nt;
-    if (ti >= *n_tiles) return false;
+    // The grid is sized for the list's capacity; the first n_tiles * nt
+    // workgroups take a tile each.  Workgroup bid runs on XCD bid % 8: XCD x
+    // takes a contiguous run of (row tile, column tile) pairs, column tiles
+    // fastest, so the workgroups sharing a row tile (and the tiles of one
+    // expert) meet in one L2.
+    const int total = *n_tiles * nt;
+    if (bid >= total) return false;
+    const int q = total >> 3, r = total & 7, x = bid & 7;
+    const int idx = x * q + min(x, r) + (bid >> 3);
+    const int ti = idx / nt, tn = idx % nt;
     const int4 d = tiles[ti];
     t.group = d.x; t.row_base = d.y; t.rows = d.z;
     t.m0 = 0; t.n0 = tn * bn; t.cols = min(bn, N - t.n0);

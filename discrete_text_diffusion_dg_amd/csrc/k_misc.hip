@@ -257,7 +257,8 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
 //       (row, slot) order -> pos.
 //  k_route_finish (one workgroup) turns the count table into per-block
 //    exclusive prefixes (per expert, in place), the expert totals into
-//    offsets, writes the 64-row tile list, and the final position of every
+//    offsets, writes the tile list (runs of at most tile_rows rows of one
+//    expert), and the final position of every
 //    entry in the expert-sorted order, offset + block prefix + rank, into pos
 //    and perm: rows of an expert stay in ascending row order.
 template <typename T>
@@ -447,8 +448,8 @@ constexpr int kFinishLds = 16384;     // count-table entries kept in LDS by the 
 constexpr int kFinishThreads = 1024;
 
 __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx, int M, int k, int E, int nblk,
-                                                                 int rpb, int* cnt, int* perm, int* pos, int4* tiles,
-                                                                 int* n_tiles) {
+                                                                 int rpb, int tr, int* cnt, int* perm, int* pos,
+                                                                 int4* tiles, int* n_tiles) {
   constexpr int NT = kFinishThreads;
   __shared__ int seg[NT];
   __shared__ int offs[128], toff[129];
@@ -486,12 +487,12 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
     if (sg == tpe - 1) offs[e] = run;             // the expert's total
   }
   __syncthreads();
-  // exclusive prefixes over experts of the row counts and of the 64-row tile
+  // exclusive prefixes over experts of the row counts and of the tr-row tile
   // counts: one wave, two experts per lane, a shuffle scan
   if (t < 64) {
     const int x0 = 2 * t, x1 = 2 * t + 1;
     const int c0 = x0 < E ? offs[x0] : 0, c1 = x1 < E ? offs[x1] : 0;
-    const int n0 = (c0 + 63) / 64, n1 = (c1 + 63) / 64;
+    const int n0 = (c0 + tr - 1) / tr, n1 = (c1 + tr - 1) / tr;
     int rs = c0 + c1, ts = n0 + n1;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
   for (int x = t; x < E; x += NT) {
     const int c = (x + 1 < E ? offs[x + 1] : M * k) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
-      tiles[toff[x] + q] = make_int4(x, offs[x] + q * 64, min(64, c - q * 64), 0);
+      tiles[toff[x] + q] = make_int4(x, offs[x] + q * tr, min(tr, c - q * tr), 0);
   }
   const int MK = M * k;
   for (int i0 = t; i0 < MK; i0 += 4 * NT) {      // four independent entries in flight per thread
@@ -543,9 +544,9 @@ int router_ksplits(int M, int d, int E) {
 
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int* cnt, float* part, hipStream_t s) {
+                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (d % (32 * kRouterWaves) != 0 || E > 128 || k > 8) return hipErrorInvalidValue;
+  if (d % (32 * kRouterWaves) != 0 || E > 128 || k > 8 || tile_rows < 1) return hipErrorInvalidValue;
   constexpr int RPB = 16;
   const int nblk = (M + RPB - 1) / RPB, ksp = router_ksplits(M, d, E);
   hipLaunchKernelGGL((k_router_logits<T, kRouterWaves>), dim3(nblk, (E + 15) / 16, ksp), dim3(64 * kRouterWaves), 0, s,
@@ -556,14 +557,14 @@ hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* r
                      cnt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), 0, s, idx, M, k, E, nblk, RPB, cnt, perm, pos,
-                     tiles, n_tiles);
+  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), 0, s, idx, M, k, E, nblk, RPB, tile_rows, cnt,
+                     perm, pos, tiles, n_tiles);
   return hipGetLastError();
 }
 template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,
-                                  int4*, int*, int*, float*, hipStream_t);
+                                  int4*, int*, int, int*, float*, hipStream_t);
 template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, float*, int*, float*, int*, int*,
-                                 int4*, int*, int*, float*, hipStream_t);
+                                 int4*, int*, int, int*, float*, hipStream_t);
 
 // ------------------------------------------------------------------ router for few entries
 // When the routed entries of a launch fit one workgroup (M * k <= 4096), the
@@ -576,7 +577,7 @@ template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, f
 //  k_route_sort (one workgroup): the expert-sorted order of all M * k
 //    entries, rows of an expert in row order: per (entry block, wave) counts
 //    and in-wave ranks by ballots, exclusive prefixes per expert, expert
-//    offsets, the 64-row tile list, pos and perm.
+//    offsets, the tile list, pos and perm.
 constexpr int kSortThreads = 1024, kSortMaxEntries = 4096, kSortBlocks = kSortMaxEntries / kSortThreads;
 constexpr int kRouterPieces = 16;
 
@@ -671,8 +672,8 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
   }
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int MK, int k, int E, int* perm, int* pos,
-                                                            int4* tiles, int* n_tiles) {
+__global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int MK, int k, int E, int tr, int* perm,
+                                                            int* pos, int4* tiles, int* n_tiles) {
   constexpr int NW = kSortThreads / 64;
   __shared__ int cnt[kSortBlocks][NW][128];
   __shared__ int offs[128], toff[129];
@@ -713,12 +714,12 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int
     offs[t] = run;
   }
   __syncthreads();
-  // exclusive prefixes over experts of the row counts and of the 64-row tile
+  // exclusive prefixes over experts of the row counts and of the tr-row tile
   // counts: one wave, two experts per lane, a shuffle scan
   if (t < 64) {
     const int x0 = 2 * t, x1 = 2 * t + 1;
     const int c0 = x0 < E ? offs[x0] : 0, c1 = x1 < E ? offs[x1] : 0;
-    const int n0 = (c0 + 63) / 64, n1 = (c1 + 63) / 64;
+    const int n0 = (c0 + tr - 1) / tr, n1 = (c1 + tr - 1) / tr;
     int rs = c0 + c1, ts = n0 + n1;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int
   for (int x = t; x < E; x += kSortThreads) {
     const int c = (x + 1 < E ? offs[x + 1] : MK) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
-      tiles[toff[x] + q] = make_int4(x, offs[x] + q * 64, min(64, c - q * 64), 0);
+      tiles[toff[x] + q] = make_int4(x, offs[x] + q * tr, min(tr, c - q * tr), 0);
   }
 #pragma unroll
   for (int j = 0; j < kSortBlocks; ++j) {
@@ -756,11 +757,12 @@ hipError_t add_norm_router(const float* part, int S, int M, int d, const float* 
   return hipGetLastError();
 }
 
-hipError_t route_sort(const int* idx, int M, int k, int E, int* perm, int* pos, int4* tiles, int* n_tiles,
-                      hipStream_t s) {
+hipError_t route_sort(const int* idx, int M, int k, int E, int tile_rows, int* perm, int* pos, int4* tiles,
+                      int* n_tiles, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (M * k > kSortMaxEntries || E > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), 0, s, idx, M * k, k, E, perm, pos, tiles, n_tiles);
+  hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), 0, s, idx, M * k, k, E, tile_rows, perm, pos, tiles,
+                     n_tiles);
   return hipGetLastError();
 }
 

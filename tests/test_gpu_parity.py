@@ -375,6 +375,20 @@ def test_micro_many_experts_top8(torch_cuda):
     _run_parity(torch_cuda, mc, 14, 200, 2, 2, "micro-e128", gain_std=0.1)
 
 
+def test_micro_grouped_experts_fused_router(torch_cuda):
+    # 4 experts top-2: 512 routed entries over 4 experts take the grouped 128-row tile products
+    # (ragged last tiles per expert), routed by the fused norm + router and the one-workgroup sort
+    mc = micro(n_layers=2, n_experts=4, top_k=2, vocab=2048)
+    _run_parity(torch_cuda, mc, 15, 130, 1, 2, "micro-grouped-e4")
+
+
+def test_micro_grouped_experts_split_router(torch_cuda):
+    # 6 experts top-3 (not a power of two: the three-launch router) on the grouped 128-row tiles,
+    # two requests so the 512 canvas rows span several router blocks
+    mc = micro(n_layers=1, n_experts=6, top_k=3, vocab=2048)
+    _run_parity(torch_cuda, mc, 16, 70, 2, 2, "micro-grouped-e6")
+
+
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
