@@ -35,15 +35,17 @@ __device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
 }
-// Branch-free forms for one new value (selects, no divergent control flow).
-__device__ __forceinline__ void top2_insert(Top2& a, float v, int i) {
-  const bool better = (v > a.b1) | ((v == a.b1) & (i < a.i1));   // bitwise: no short-circuit branches
-  a.b2 = better ? a.b1 : fmaxf(a.b2, v);
-  a.b1 = better ? v : a.b1;
+// Branch-free insertion of one new value (selects, no divergent control flow)
+// for values visited in increasing id order: an equal value never replaces
+// the held one (its id is larger), so one comparison decides.
+__device__ __forceinline__ void top2_insert_ordered(Top2& a, float v, int i) {
+  const bool better = v > a.b1;
+  a.b2 = __builtin_amdgcn_fmed3f(a.b1, v, a.b2);   // b2 <= b1: the middle value is the new second best
+  a.b1 = fmaxf(a.b1, v);
   a.i1 = better ? i : a.i1;
 }
-__device__ __forceinline__ void argmax_insert(float& v, int& i, float ov, int oi) {
-  const bool better = (ov > v) | ((ov == v) & (oi < i));
+__device__ __forceinline__ void argmax_insert_ordered(float& v, int& i, float ov, int oi) {
+  const bool better = ov > v;
   v = better ? ov : v;
   i = better ? oi : i;
 }
@@ -71,16 +73,15 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
     const float4 t4 = reinterpret_cast<const float4*>(tr)[q];
     x[4 * q] = t4.x; x[4 * q + 1] = t4.y; x[4 * q + 2] = t4.z; x[4 * q + 3] = t4.w;
   }
-  // z max and logit arg-max (lowest id on ties)
-  float zmax = -INFINITY, lmax = -INFINITY;
+  // logit arg-max (lowest id on ties); rounding is monotone and 1 / T > 0, so
+  // the largest z = logit * (1 / T) is the largest logit times 1 / T
+  float lmax = -INFINITY;
   int lidx = 0x7fffffff;
   if (have) {
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-      zmax = fmaxf(zmax, x[k] * inv_t);
-      argmax_insert(lmax, lidx, x[k], v0 + k);
-    }
+    for (int k = 0; k < 64; ++k) argmax_insert_ordered(lmax, lidx, x[k], v0 + k);
   }
+  const float zmax = lmax * inv_t;
   // Gumbel-max top two: every value is scored (a lane owns a row of its own,
   // so pruning by a per-row threshold would leave the wave executing the
   // scoring of almost every value anyway)
@@ -88,16 +89,16 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
   const uint64_t seed = seeds.v[b];
   const uint32_t call0 = gumbel_call(v0);
   if (have) {
+    // all 16 calls first, then the 64 scores in id order (id v0 + k takes
+    // word k >> 4 of call k & 15)
+    uint32_t xs[16][4];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const uint4 xw = philox_block(seed, kTagGumbel, (uint32_t)canvas_index, (uint32_t)step, (uint32_t)pos, call0 | c);
-      const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = c + 16 * j;
-        top2_insert(t2, x[k] * inv_t + gumbel_of(xs[j]), v0 + k);
-      }
+      xs[c][0] = xw.x; xs[c][1] = xw.y; xs[c][2] = xw.z; xs[c][3] = xw.w;
     }
+#pragma unroll
+    for (int k = 0; k < 64; ++k) top2_insert_ordered(t2, x[k] * inv_t + gumbel_of(xs[k & 15][k >> 4]), v0 + k);
   }
   // the chunk's row max, then exp(z - m) and its sums (ids in order)
   const float m = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
