@@ -56,20 +56,31 @@ struct TileCfg {
 };
 
 // ------------------------------------------------------------------ schedulers
-// Dense tiles, column-tile major so that the row tiles sharing a weight tile are
-// consecutive; when the tile count is a multiple of 8, consecutive logical tiles
-// are placed on the same XCD (workgroups are dealt round-robin over 8 XCDs).
-// Optional split-K: the split index varies slowest.
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup bid runs on XCD
+// bid % 8); xcd_run gives XCD x a contiguous run of the `total` logical tiles.
+__device__ __forceinline__ int xcd_run(int bid, int total) {
+  const int q = total >> 3, r = total & 7, x = bid & 7;
+  return x * q + min(x, r) + (bid >> 3);
+}
+
+// Dense tiles in bands of kBandRows row tiles: within a band the row tiles
+// vary fastest, then the column tiles, so the workgroups resident on one XCD
+// at a time cover about 8 row tiles x 8 column tiles and both operands are
+// re-read from that XCD's L2 (column-major over all row tiles would stream
+// the whole A operand through every L2 once per column tile).  Optional
+// split-K: the split index varies slowest.
+constexpr int kBandRows = 8;
 template <int BM, int BN>
 struct SchedDense {
   int M, N, K, mt, nt, splits, kchunk;
   __device__ bool get(int bid, TileCtx& t) const {
     const int per = mt * nt, total = per * splits;
     if (bid >= total) return false;
-    int idx = bid;
-    if ((total & 7) == 0) idx = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int idx = xcd_run(bid, total);
     const int s = idx / per, r = idx % per;
-    const int tm = r % mt, tn = r / mt;
+    const int band = r / (kBandRows * nt), first = band * kBandRows;
+    const int bh = min(kBandRows, mt - first), rb = r - band * kBandRows * nt;
+    const int tm = first + rb % bh, tn = rb / bh;
     t.m0 = tm * BM; t.n0 = tn * BN;
     t.rows = min(BM, M - t.m0); t.cols = min(BN, N - t.n0);
     t.k0 = s * kchunk; t.k1 = min(K, t.k0 + kchunk);
@@ -92,8 +103,7 @@ struct SchedGroup {
     // expert) meet in one L2.
     const int total = *n_tiles * nt;
     if (bid >= total) return false;
-    const int q = total >> 3, r = total & 7, x = bid & 7;
-    const int idx = x * q + min(x, r) + (bid >> 3);
+    const int idx = xcd_run(bid, total);
     const int ti = idx / nt, tn = idx % nt;
     const int4 d = tiles[ti];
     t.group = d.x; t.row_base = d.y; t.rows = d.z;
