@@ -255,10 +255,10 @@ hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* k
 //    3. per expert, the count of the block's (row, slot) entries -> cnt[e][blk],
 //       and per entry its rank among the block's entries of that expert, in
 //       (row, slot) order -> pos.
-//  k_route_finish (one workgroup) turns the count table into per-block
-//    exclusive prefixes (per expert, in place), the expert totals into
-//    offsets, writes the tile list (runs of at most tile_rows rows of one
-//    expert), and the final position of every
+//  k_route_finish turns the count table into per-block exclusive prefixes
+//    (per expert, in place), the expert totals into offsets, writes the tile
+//    list (runs of at most tile_rows rows of one expert), and the final
+//    position of every
 //    entry in the expert-sorted order, offset + block prefix + rank, into pos
 //    and perm: rows of an expert stay in ascending row order.
 template <typename T>
@@ -455,7 +455,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
   __shared__ int offs[128], toff[129];
   __shared__ int tab[kFinishLds];
   const int t = threadIdx.x;
-  // the count table [E][nblk]: in LDS when it fits (one coalesced read), else in place in memory
+  // the count table [E][nblk]: in LDS when it fits (one coalesced read), else
+  // in place in memory.  With the table in LDS several workgroups may run:
+  // each forms the (identical) prefixes and offsets and places its own slice
+  // of the entries; workgroup 0 writes the tile list.
   const bool in_lds = E * nblk <= kFinishLds;
   int* ct = in_lds ? tab : cnt;
   if (in_lds) {
@@ -502,27 +505,31 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
     const int rx = rs - c0 - c1, tx = ts - n0 - n1;   // exclusive
     if (x0 < E) { offs[x0] = rx; toff[x0] = tx; }
     if (x1 < E) { offs[x1] = rx + c0; toff[x1] = tx + n0; }
-    if (t == 63) { toff[E] = ts; *n_tiles = ts; }
+    if (t == 63) {
+      toff[E] = ts;
+      if (blockIdx.x == 0) *n_tiles = ts;
+    }
   }
   __syncthreads();
-  for (int x = t; x < E; x += NT) {
+  for (int x = t; x < E && blockIdx.x == 0; x += NT) {
     const int c = (x + 1 < E ? offs[x + 1] : M * k) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
       tiles[toff[x] + q] = make_int4(x, offs[x] + q * tr, min(tr, c - q * tr), 0);
   }
-  const int MK = M * k;
-  for (int i0 = t; i0 < MK; i0 += 4 * NT) {      // four independent entries in flight per thread
+  const int MK = M * k, slice = (MK + gridDim.x - 1) / gridDim.x;
+  const int lo = blockIdx.x * slice, hi = min(MK, lo + slice);
+  for (int i0 = lo + t; i0 < hi; i0 += 4 * NT) {   // four independent entries in flight per thread
     int ex[4], rk[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * NT;
-      ex[u] = i < MK ? idx[i] : 0;
-      rk[u] = i < MK ? pos[i] : 0;
+      ex[u] = i < hi ? idx[i] : 0;
+      rk[u] = i < hi ? pos[i] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * NT;
-      if (i < MK) {
+      if (i < hi) {
         const int p = offs[ex[u]] + ct[(size_t)ex[u] * nblk + i / (rpb * k)] + rk[u];
         pos[i] = p;
         perm[p] = i / k;
@@ -557,8 +564,11 @@ hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* r
                      cnt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_finish, dim3(1), dim3(kFinishThreads), 0, s, idx, M, k, E, nblk, RPB, tile_rows, cnt,
-                     perm, pos, tiles, n_tiles);
+  // one workgroup per 1024 entries (up to 64) when the count table fits LDS
+  const int fin_ent = (M * k + kFinishThreads - 1) / kFinishThreads;
+  const int fin_wg = E * nblk <= kFinishLds ? (fin_ent < 64 ? fin_ent : 64) : 1;
+  hipLaunchKernelGGL(k_route_finish, dim3(fin_wg), dim3(kFinishThreads), 0, s, idx, M, k, E, nblk, RPB, tile_rows,
+                     cnt, perm, pos, tiles, n_tiles);
   return hipGetLastError();
 }
 template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,
