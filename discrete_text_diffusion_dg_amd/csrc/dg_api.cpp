@@ -469,7 +469,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
                          c.rms_eps, st->h, xn, s));
   }
   const int keys = st->ctx + nq;
-  int splits = attention_splits(st->B, nq, Hq, Hkv, hd, keys);
+  int splits = attention_splits(st->B, nq, Hq, Hkv, hd, keys, (int)st->m->esz);
   if (splits > st->attn_splits_max) splits = st->attn_splits_max;
   const int cap = expert_tile_capacity(M, k, E);
   const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd);

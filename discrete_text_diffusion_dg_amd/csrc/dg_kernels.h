@@ -120,7 +120,7 @@ struct AttnArgs {
 };
 template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t s);
-int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys);
+int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys, int elem_bytes);
 
 // ---- row-wise kernels (k_misc.hip); S = number of split partials to reduce
 template <typename T>

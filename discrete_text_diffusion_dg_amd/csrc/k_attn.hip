@@ -105,8 +105,17 @@ __device__ __forceinline__ void mma16x16x32_f16(f32x4_t& acc, uint4 a, uint4 b) 
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc, 0,
                                                0, 0);
 }
+// Maximum over the four lanes q16 + 16 g4 that hold one query's scores: the
+// gfx950 row swaps (16-lane rows, then 32-lane halves) are plain VALU moves,
+// where a shuffle goes through the LDS crossbar.
+__device__ __forceinline__ float max_over_g4(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
 
-template <typename T, int HD, int NWQ>
+template <typename T, int HD, int NWQ, int QBW>
 __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
   constexpr int NT = sizeof(T) == 2 ? 2 : 1;
@@ -116,21 +125,31 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   constexpr int NTH = 64 * NWQ;
   constexpr int CH_PER_KEY = HD / EPC;
   constexpr int KCH = KT * CH_PER_KEY / NTH, VCH = HD * (KT / EPC) / NTH;
+  constexpr int RPW = 16 * NWQ;                        // query rows per query block of the workgroup
   static_assert(KCH >= 1 && VCH >= 1 && KT * CH_PER_KEY % NTH == 0 && HD * (KT / EPC) % NTH == 0, "tile shape");
+  static_assert(QBW == 1 || sizeof(T) == 2, "several query blocks per wave: bf16 path only");
   __shared__ __attribute__((aligned(16))) T smem[2 * (KBUF + VBUF)];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
   const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
   const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv, split = blockIdx.z;
-  const int rho0 = blockIdx.x * 16 * NWQ;
-  const int rho = rho0 + w * 16 + q16;
-  const bool qvalid = rho < rows_total;
-  const int hh = qvalid ? rho / a.nq : 0, qi = qvalid ? rho % a.nq : 0;
-  const int head = kvh * G + hh, qpos = a.ctx + qi;
+  const int rho0 = blockIdx.x * RPW * QBW;
+  // query block qb of this wave: rows rho0 + qb * RPW + 16 w + (0..15)
+  bool qvalid[QBW];
+  int qi[QBW], head[QBW], qpos[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int rho = rho0 + qb * RPW + w * 16 + q16;
+    qvalid[qb] = rho < rows_total;
+    const int hh = qvalid[qb] ? rho / a.nq : 0;
+    qi[qb] = qvalid[qb] ? rho % a.nq : 0;
+    head[qb] = kvh * G + hh;
+    qpos[qb] = a.ctx + qi[qb];
+  }
   const int total = a.ctx + a.nq;
   int klimit = total;
   if (a.causal) {
-    const int last = min(rho0 + 16 * NWQ - 1, rows_total - 1);
+    const int last = min(rho0 + RPW * QBW - 1, rows_total - 1);
     const int imax = (rho0 / a.nq == last / a.nq) ? last % a.nq : a.nq - 1;
     klimit = a.ctx + imax + 1;
   }
@@ -139,24 +158,38 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   const int ntiles = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
 
   const T* Q = reinterpret_cast<const T*>(a.q);
-  const size_t qrow = (size_t)(b * a.nq + qi) * a.Hq * HD + (size_t)head * HD;
-  Frag<T> qf[NS];
+  Frag<T> qf[QBW][NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (qvalid) {
-      lds_frag(qf[s], Q + qrow + s * 32 + g4 * 8);
-    } else {
-      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      set_p(qf[s], z);
+  for (int qb = 0; qb < QBW; ++qb) {
+    const size_t qrow = (size_t)(b * a.nq + qi[qb]) * a.Hq * HD + (size_t)head[qb] * HD;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (qvalid[qb]) {
+        lds_frag(qf[qb][s], Q + qrow + s * 32 + g4 * 8);
+      } else {
+        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        set_p(qf[qb][s], z);
+      }
     }
   }
   const T* Kc = reinterpret_cast<const T*>(a.kc) + ((size_t)b * a.Hkv + kvh) * a.kv_stride * HD;
   const T* Vt = reinterpret_cast<const T*>(a.vc) + ((size_t)b * a.Hkv + kvh) * HD * a.kv_stride;
-  f32x4_t o[NDB];
+  f32x4_t o[QBW][NDB];
+  float m_run[QBW], l_run[QBW];            // bf16 path: m_run in base-2 units (score * cs)
+  // bf16 path: the row sums come from the matrix cores, as a 16-row block of
+  // ones times P (every element of osum is the query's running sum of the
+  // fp16 P it multiplied into O)
+  f32x4_t osum[QBW];
 #pragma unroll
-  for (int j = 0; j < NDB; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;   // bf16 path: m_run in base-2 units (score * cs)
+  for (int qb = 0; qb < QBW; ++qb) {
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) o[qb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    osum[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   const float cs = a.scale * 1.4426950408889634f;
+  const uint4 ones16 = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 
   uint4 kr0[KCH], vr0[VCH], kr1[KCH], vr1[VCH];
   // K rows past the range are clamped to its last key; V^T rows are padded to
@@ -198,69 +231,74 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
     const T* sK = smem + buf * (KBUF + VBUF);
     const T* sV = sK + KBUF;
     const int k0 = kbeg + t * KT;
-    // scores S^T[key][query] for the 64 keys of the tile
-    f32x4_t sc[4];
+    // scores S^T[key][query] for the 64 keys of the tile; each K fragment
+    // serves every query block of the wave
+    f32x4_t sc[QBW][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) sc[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         Frag<T> kf;
         lds_frag(kf, sK + tile_key(kb, q16) * LDK + s * 32 + g4 * 8);
-        mma16x16x32(sc[kb], kf, qf[s]);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) mma16x16x32(sc[qb][kb], kf, qf[qb][s]);
       }
     }
     if constexpr (sizeof(T) == 2) {
-      // masks only where a tile crosses the end of the range or the causal diagonal
-      if (k0 + KT > kend || a.causal) {
+      uint4 pf[QBW][2];                                    // fp16 exp2(z - m), two 32-key steps per block
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) {
+        // masks only where a tile crosses the end of the range or the causal diagonal
+        if (k0 + KT > kend || a.causal) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kpos = k0 + tile_key(kb, g4 * 4 + i);
+              if (kpos >= kend || (a.causal && kpos > qpos[qb])) sc[qb][kb][i] = -INFINITY;
+            }
+        }
+        // online softmax in base-2 units: z = score * scale * log2(e)
+        float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kpos = k0 + tile_key(kb, g4 * 4 + i);
-            if (kpos >= kend || (a.causal && kpos > qpos)) sc[kb][i] = -INFINITY;
-          }
-      }
-      // online softmax in base-2 units: z = score * scale * log2(e)
-      float tmax = -INFINITY;
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[qb][kb][i]);
+        tmax = max_over_g4(tmax);
+        const float m_new = fmaxf(m_run[qb], tmax * cs);
+        const float mo = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: every term is 0
+        if (__ballot(m_new != m_run[qb]) != 0) {             // rescale only when some running max moved
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mo);
+          osum[qb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax * cs);
-      const float mo = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: every term is 0
-      if (__ballot(m_new != m_run) != 0) {                 // rescale only when some running max moved
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mo);
-        l_run *= alpha;
-#pragma unroll
-        for (int j = 0; j < NDB; ++j) o[j] *= alpha;
-      }
-      m_run = m_new;
-      uint32_t ph[8];                                      // fp16 pairs of exp2(z - m), keys in tile order
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], cs, -mo));
-          lsum += e[i];
+          for (int j = 0; j < NDB; ++j) o[qb][j] *= alpha;
         }
-        ph[kb * 2] = f32x2_to_f16x2(e[0], e[1]);
-        ph[kb * 2 + 1] = f32x2_to_f16x2(e[2], e[3]);
+        m_run[qb] = m_new;
+        uint32_t ph[8];                                      // fp16 pairs, keys in tile order
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][kb][i], cs, -mo));
+          ph[kb * 2] = f32x2_to_f16x2(e[0], e[1]);
+          ph[kb * 2 + 1] = f32x2_to_f16x2(e[2], e[3]);
+        }
+        pf[qb][0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+        pf[qb][1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
       }
-      l_run += lsum;
-      // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps of fp16 operands
+      // O^T[d][q] += V^T[d][keys] P[keys][q]; each V^T fragment serves every query block
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint4 pf = make_uint4(ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const uint4 vf = *reinterpret_cast<const uint4*>(sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
-          mma16x16x32_f16(o[db], vf, pf);
+#pragma unroll
+          for (int qb = 0; qb < QBW; ++qb) mma16x16x32_f16(o[qb][db], vf, pf[qb][ks]);
         }
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) mma16x16x32_f16(osum[qb], ones16, pf[qb][ks]);
       }
     } else {
       float p[16];
@@ -270,15 +308,15 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kpos = k0 + tile_key(kb, g4 * 4 + i);
-          float v = sc[kb][i] * a.scale;
-          if (kpos >= kend || (a.causal && kpos > qpos)) v = -INFINITY;
+          float v = sc[0][kb][i] * a.scale;
+          if (kpos >= kend || (a.causal && kpos > qpos[0])) v = -INFINITY;
           p[kb * 4 + i] = v;
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run - m_new);
+      const float m_new = fmaxf(m_run[0], tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp_fast(m_run[0] - m_new);
       float lsum = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -286,27 +324,27 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
         p[j] = e;
         lsum += e;
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      l_run[0] = l_run[0] * alpha + lsum;
+      m_run[0] = m_new;
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) o[j] *= alpha;
+      for (int j = 0; j < NDB; ++j) o[0][j] *= alpha;
       // O^T[d][q] += V^T[d][keys] P[keys][q], two 32-key steps (fp32 operands)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        Frag<T> pf[NT];
+        Frag<T> pfr[NT];
         float rest[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           rest[i] = p[(2 * ks) * 4 + i];
           rest[4 + i] = p[(2 * ks + 1) * 4 + i];
         }
-        split_p(pf, rest);
+        split_p(pfr, rest);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           Frag<T> vf;
           lds_frag(vf, sV + (db * 16 + q16) * LDV + ks * 32 + g4 * 8);
 #pragma unroll
-          for (int term = 0; term < NT; ++term) mma16x16x32(o[db], vf, pf[term]);
+          for (int term = 0; term < NT; ++term) mma16x16x32(o[0][db], vf, pfr[term]);
         }
       }
     }
@@ -348,28 +386,38 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   }
   if (t + 2 < ntiles) compute(0, t + 2);
 
-  // full row sum across the four lane groups holding the same query
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!qvalid) return;
-  const size_t rowid = (size_t)(b * a.nq + qi) * a.Hq + head;
-  if (a.splits == 1) {
-    T* out = reinterpret_cast<T*>(a.out) + qrow;
-    const float inv = 1.f / l_run;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
-      store4(out + db * 16 + g4 * 4, v);
+  for (int qb = 0; qb < QBW; ++qb) {
+    // full row sum: the matrix-core sums (bf16), else across the four lane
+    // groups holding the same query
+    if constexpr (sizeof(T) == 2) {
+      l_run[qb] = osum[qb][0];
+    } else {
+      l_run[qb] += __shfl_xor(l_run[qb], 16, 64);
+      l_run[qb] += __shfl_xor(l_run[qb], 32, 64);
     }
-  } else {
-    float* po = a.part_o + ((size_t)split * a.B * a.nq * a.Hq + rowid) * HD;
+    if (!qvalid[qb]) continue;
+    const size_t qrow = (size_t)(b * a.nq + qi[qb]) * a.Hq * HD + (size_t)head[qb] * HD;
+    const size_t rowid = (size_t)(b * a.nq + qi[qb]) * a.Hq + head[qb];
+    if (a.splits == 1) {
+      T* out = reinterpret_cast<T*>(a.out) + qrow;
+      const float inv = 1.f / l_run[qb];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<float4*>(po + db * 16 + g4 * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-    if (g4 == 0) {
-      float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
-      pm[0] = sizeof(T) == 2 ? m_run * 0.6931471805599453f : m_run;   // the merge takes natural units
-      pm[1] = l_run;
+      for (int db = 0; db < NDB; ++db) {
+        float v[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv, o[qb][db][3] * inv};
+        store4(out + db * 16 + g4 * 4, v);
+      }
+    } else {
+      float* po = a.part_o + ((size_t)split * a.B * a.nq * a.Hq + rowid) * HD;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<float4*>(po + db * 16 + g4 * 4) =
+            make_float4(o[qb][db][0], o[qb][db][1], o[qb][db][2], o[qb][db][3]);
+      if (g4 == 0) {
+        float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
+        pm[0] = sizeof(T) == 2 ? m_run[qb] * 0.6931471805599453f : m_run[qb];   // the merge takes natural units
+        pm[1] = l_run[qb];
+      }
     }
   }
 }
@@ -478,8 +526,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_over_g4(tmax);
       const float m_new = fmaxf(m_run[qb], tmax * cs);
       const float mo = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: every term is 0
       if (__ballot(m_new != m_run[qb]) != 0) {             // rescale only when some running max moved
@@ -620,6 +667,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // 51.8 -> 29.1 us; 9216 keys, 16/4 x 64: 80.8 -> 44.5 us; 32 requests x 4352
 // keys: 842 -> 414 us).
 constexpr int kSpreadNW = 4, kSpreadQB = 1, kWideNWQ = 8;
+// Query blocks per wave of the wide kernel.  Two (256 query rows per
+// workgroup share each staged K/V tile, halving the K/V bytes re-read through
+// L2 per query) for bf16 with 64-dim heads when that still leaves ~256
+// workgroups without key splits (many requests; measured 250 -> 230 us per
+// layer at 32 x 256 rows and 4352 keys).  Else one: at batch 1 the halved
+// workgroup count asks for twice the key splits (multi-canvas, 8448 keys:
+// 34 -> 39 us), and 128-dim heads would spill.
+inline int wide_qbw(int elem_bytes, int hd, int B, int nq, int Hq, int Hkv) {
+  if (elem_bytes != 2 || hd != 64) return 1;
+  const int rows = 16 * kWideNWQ * 2;
+  return ((Hq / Hkv) * nq + rows - 1) / rows * B * Hkv >= 256 ? 2 : 1;
+}
 constexpr double kSpreadMaxBytes = 128.0 * (1 << 20);
 inline bool use_spread(int B, int nq, int Hq, int Hkv, int hd, int keys) {
   const double blocks = (double)(((Hq / Hkv) * nq + 15) / 16) * B * Hkv;
@@ -635,8 +694,15 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_attn_spread<T, HD, NW, QB>), grid, dim3(64 * NW), 0, s, a);
   } else {
     constexpr int NWQ = kWideNWQ;
-    dim3 grid((G * a.nq + 16 * NWQ - 1) / (16 * NWQ), a.B * a.Hkv, a.splits);
-    hipLaunchKernelGGL((k_attn_wide<T, HD, NWQ>), grid, dim3(64 * NWQ), 0, s, a);
+    if (wide_qbw((int)sizeof(T), HD, a.B, a.nq, a.Hq, a.Hkv) == 2) {
+      if constexpr (sizeof(T) == 2 && HD == 64) {
+        dim3 grid((G * a.nq + 32 * NWQ - 1) / (32 * NWQ), a.B * a.Hkv, a.splits);
+        hipLaunchKernelGGL((k_attn_wide<T, HD, NWQ, 2>), grid, dim3(64 * NWQ), 0, s, a);
+      }
+    } else {
+      dim3 grid((G * a.nq + 16 * NWQ - 1) / (16 * NWQ), a.B * a.Hkv, a.splits);
+      hipLaunchKernelGGL((k_attn_wide<T, HD, NWQ, 1>), grid, dim3(64 * NWQ), 0, s, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
@@ -650,13 +716,14 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 // Key splits (and the merge launch they need): spread -- at most 8 tiles per
 // wave; wide -- only as many as filling the chip (~256 workgroups) asks, with
 // at least four tiles per split.
-int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys) {
+int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys, int elem_bytes) {
   const int tiles = (keys + 63) / 64;
   int splits;
   if (use_spread(B, nq, Hq, Hkv, hd, keys)) {
     splits = (tiles + 8 * kSpreadNW - 1) / (8 * kSpreadNW);
   } else {
-    const int wg = ((Hq / Hkv) * nq + 16 * kWideNWQ - 1) / (16 * kWideNWQ) * B * Hkv;
+    const int rows = 16 * kWideNWQ * wide_qbw(elem_bytes, hd, B, nq, Hq, Hkv);
+    const int wg = ((Hq / Hkv) * nq + rows - 1) / rows * B * Hkv;
     splits = (256 + wg - 1) / wg;
     const int max_by_keys = tiles / 4;
     if (splits > max_by_keys) splits = max_by_keys;
