@@ -426,13 +426,10 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
   const int c16 = lane & 15, g4 = lane >> 4, sw = (c16 >> 1) & 7;
   const int aoff = (wm * C::WM + c16) * C::ROWB, boff = (C::BM + wn * C::WN + c16) * C::ROWB;
   f32x4_t accc[SCALED ? C::FM : 1][SCALED ? C::FN : 1];   // the current chunk's products (scaled loaders)
-  if constexpr (SCALED) {
-#pragma unroll
-    for (int a = 0; a < C::FM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::FN; ++b) accc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  auto kstep = [&](const char* sb, int kk) __attribute__((always_inline)) {
+  // fresh: the first step of a 128-element chunk (scaled loaders) starts the
+  // chunk products from zero in the matrix instruction itself
+  auto kstep = [&](const char* sb, int kk, auto fresh) __attribute__((always_inline)) {
+    constexpr bool FRESH = decltype(fresh)::value;
     const int ch = ((kk * 4 + g4) ^ sw) * 16;
     Frag<bf16> fa[C::FM], fb[C::FN];
 #pragma unroll
@@ -443,39 +440,53 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     for (int a = 0; a < C::FM; ++a)
 #pragma unroll
       for (int b = 0; b < C::FN; ++b) {
-        if constexpr (SCALED) mma16x16x32(accc[a][b], fa[a], fb[b]);
-        else mma16x16x32(acc[a][b], fa[a], fb[b]);
+        if constexpr (SCALED && FRESH) {
+          accc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          mma16x16x32(accc[a][b], fa[a], fb[b]);
+        } else if constexpr (SCALED) {
+          mma16x16x32(accc[a][b], fa[a], fb[b]);
+        } else {
+          mma16x16x32(acc[a][b], fa[a], fb[b]);
+        }
       }
   };
+  using Fresh = std::true_type;
+  using Cont = std::false_type;
 #pragma unroll
   for (int p = 0; p < C::STAGES - 1; ++p)
     if (p < nk) issue(p);
-  for (int kt = 0; kt < nk; ++kt) {
+  // one K slice: wait for this wave's loads of it, hand it over, issue the
+  // slice S-1 ahead, two K steps
+  auto slice = [&](int kt, auto fresh) __attribute__((always_inline)) {
     // this wave's loads of slice kt are done once at most the next S-2 slices' are outstanding
     if (kt + C::STAGES - 2 < nk) wait_vmcnt<(C::STAGES - 2) * C::NI>();
     else wait_vmcnt<0>();
     lds_barrier();            // slice kt is in LDS for every wave; slice kt-1 is no longer read
     if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1);
     const char* sb = smem + (kt % C::STAGES) * C::STAGE;
-    kstep(sb, 0);
-    kstep(sb, 1);
-    if constexpr (SCALED) {
-      if ((kt & 1) || kt == nk - 1) {   // a 128-element chunk (or the range) ends: acc += scale(row) * chunk products
-        const float* sc = reinterpret_cast<const float*>(smem + C::STAGES * C::STAGE + (kt % C::STAGES) * C::BM * 4);
+    kstep(sb, 0, fresh);
+    kstep(sb, 1, Cont{});
+  };
+  if constexpr (SCALED) {
+    // a 128-element chunk is two slices (chunks start at even slices); its
+    // products start from zero and end as acc += scale(row) * chunk products
+    for (int kt = 0; kt < nk; kt += 2) {
+      slice(kt, Fresh{});
+      if (kt + 1 < nk) slice(kt + 1, Cont{});
+      const int kl = kt + 1 < nk ? kt + 1 : kt;
+      const float* sc = reinterpret_cast<const float*>(smem + C::STAGES * C::STAGE + (kl % C::STAGES) * C::BM * 4);
 #pragma unroll
-        for (int a = 0; a < C::FM; ++a) {
-          const float4 s4 = *reinterpret_cast<const float4*>(sc + wm * C::WM + a * 16 + g4 * 4);
-          const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      for (int a = 0; a < C::FM; ++a) {
+        const float4 s4 = *reinterpret_cast<const float4*>(sc + wm * C::WM + a * 16 + g4 * 4);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-          for (int b = 0; b < C::FN; ++b)
+        for (int b = 0; b < C::FN; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc[a][b][i] = __builtin_fmaf(sv[i], accc[a][b][i], acc[a][b][i]);
-              accc[a][b][i] = 0.f;
-            }
-        }
+          for (int i = 0; i < 4; ++i) acc[a][b][i] = __builtin_fmaf(sv[i], accc[a][b][i], acc[a][b][i]);
       }
     }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) slice(kt, Cont{});
   }
   __syncthreads();   // the epilogue may reuse the shared memory
 }
