@@ -598,20 +598,30 @@ bool router_fused_ok(int M, int d, int E, int k) {
          d % (8 * (nt / E)) == 0 && d <= kMaxModel && d / (8 * (nt / E)) <= kRouterPieces;
 }
 
-template <typename T>
-__device__ __forceinline__ void wr_piece(const T* p, float (&w)[8]);
+// One 8-element piece of a router-matrix row, held as loaded (load) and
+// widened to fp32 where it is used (get).
+template <typename T> struct WrPiece;
 template <>
-__device__ __forceinline__ void wr_piece(const bf16* p, float (&w)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+struct WrPiece<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&w)[8]) const {
+    const uint32_t x[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { w[2 * j] = __uint_as_float(x[j] << 16); w[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u); }
-}
+    for (int j = 0; j < 4; ++j) { w[2 * j] = __uint_as_float(x[j] << 16); w[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u); }
+  }
+};
 template <>
-__device__ __forceinline__ void wr_piece(const float* p, float (&w)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-}
+struct WrPiece<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float (&w)[8]) const {
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+};
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int S, int M, int d, const float* g,
@@ -622,6 +632,15 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
   __shared__ int sel_e[8];
   __shared__ float sel_v[8];
   const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
+  // this thread's pieces of the router matrix (expert e, pieces sl, sl + tpe,
+  // ...), requested first so that they arrive while the row is added and
+  // normalised; pieces past ppt repeat the last one and are not added
+  const int tpe = blockDim.x / E, e = tid / tpe, sl = tid % tpe;
+  const T* wrow = wr + (size_t)e * d;
+  const int ppt = d / (8 * tpe);                  // pieces of this thread (<= kRouterPieces)
+  WrPiece<T> wp[kRouterPieces];
+#pragma unroll
+  for (int u = 0; u < kRouterPieces; ++u) wp[u].load(wrow + (sl + min(u, ppt - 1) * tpe) * 8);
   float4 v[kRowChunks];
 #pragma unroll
   for (int j = 0; j < kRowChunks; ++j)
@@ -635,21 +654,16 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
   norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d, xs);
   __syncthreads();
   // logit of expert e: tpe threads, thread sl taking pieces sl, sl + tpe, ...
-  const int tpe = blockDim.x / E, e = tid / tpe, sl = tid % tpe;
-  const T* wrow = wr + (size_t)e * d;
-  const int ppt = d / (8 * tpe);                  // pieces of this thread (<= kRouterPieces)
-  float wv[kRouterPieces][8];
-#pragma unroll
-  for (int u = 0; u < kRouterPieces; ++u)         // every load issued before any is used (pieces past ppt
-    wr_piece(wrow + (sl + min(u, ppt - 1) * tpe) * 8, wv[u]);   // repeat the last one and are not added)
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < kRouterPieces; ++u)
     if (u < ppt) {
       const int c = sl + u * tpe;
+      float wv[8];
+      wp[u].get(wv);
       const float4 x0 = *reinterpret_cast<const float4*>(xs + c * 8), x1 = *reinterpret_cast<const float4*>(xs + c * 8 + 4);
-      acc += x0.x * wv[u][0]; acc += x0.y * wv[u][1]; acc += x0.z * wv[u][2]; acc += x0.w * wv[u][3];
-      acc += x1.x * wv[u][4]; acc += x1.y * wv[u][5]; acc += x1.z * wv[u][6]; acc += x1.w * wv[u][7];
+      acc += x0.x * wv[0]; acc += x0.y * wv[1]; acc += x0.z * wv[2]; acc += x0.w * wv[3];
+      acc += x1.x * wv[4]; acc += x1.y * wv[5]; acc += x1.z * wv[6]; acc += x1.w * wv[7];
     }
   for (int o = tpe >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (sl == 0) {
