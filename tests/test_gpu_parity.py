@@ -389,6 +389,20 @@ def test_micro_grouped_experts_split_router(torch_cuda):
     _run_parity(torch_cuda, mc, 16, 70, 2, 2, "micro-grouped-e6")
 
 
+def test_micro_many_requests_wide_attention_bf16(torch_cuda):
+    # 16 requests x 16/8 heads x 64: the wide attention kernel with two 16-row query blocks
+    # per wave (256 workgroups without key splits); the oracle runs requests 0 and 15
+    mc = micro(n_layers=1, n_q_heads=16, n_kv_heads=8, head_dim=64, n_experts=8, top_k=2, vocab=2048)
+    _run_parity(torch_cuda, mc, 17, 40, 16, 2, "micro-wide-bf16", oracle_reqs=[0, 15])
+
+
+def test_micro_many_requests_wide_attention_f32(torch_cuda):
+    # the same shape in fp32: the wide kernel's fp32 path (one query block per wave)
+    mc = micro(n_layers=1, dtype="f32", n_q_heads=16, n_kv_heads=8, head_dim=64, n_experts=8, top_k=2,
+               vocab=2048)
+    _run_parity(torch_cuda, mc, 18, 40, 16, 2, "micro-wide-f32", oracle_reqs=[0, 15])
+
+
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
