@@ -12,6 +12,8 @@ starts; the prompt encode is timed separately.
 The dominant stage is picked from an all-stage timing pass during warm-up, then
 timed live with HIP events inside the library (on the launch stream) during
 the timed region; its algorithmic bytes / flops per launch give the roofline.
+stage_roofline_warmup gives every stage's fraction of its own roofline from
+the warm-up timings (the same event pairs, before the timed region).
 The CPU baseline is the oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -297,6 +299,14 @@ def main():
     canv = a.steps / S
     tok_s = B * n * canv / (ms / 1e3)
     rl = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act, measured_traffic(wl.name, dominant))
+    # every stage against its own roofline, from the warm-up event timings
+    # (matrix-core fraction for the products and attention, HBM fraction for
+    # the streaming stages)
+    stage_rl = {}
+    for k, (k_ms, k_n) in prof.items():
+        r = roofline(k, k_ms, k_n, mc, B, ctx_w, n_act)
+        if r is not None:
+            stage_rl[k] = {f: r[f] for f in ("bound", "achieved", "unit", "frac", "launch_us")}
     log(f"[bench] {a.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); dominant {dominant}: "
         f"{dom_ms / max(dom_n, 1) * 1e3:.1f} us/launch")
 
@@ -321,6 +331,7 @@ def main():
         "encode_ms": round(encode_ms, 3),
         "stage_ms_warmup": {k: round(v[0] / max(a.warmup - n_first, 1), 4) for k, v in prof.items()},
         "roofline": rl,
+        "stage_roofline_warmup": stage_rl,
         "active_experts_per_layer": act_per_layer,
         "cpu_baseline": cpu,
     }
