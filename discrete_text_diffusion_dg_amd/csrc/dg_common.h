@@ -87,6 +87,14 @@ __device__ __forceinline__ void lds_frag(Frag<float>& f, const float* p) {
 
 // e^x through the hardware base-2 exponential (about 1 ulp; x <= 0 here).
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// SwiGLU of one (gate, up) pair: silu(g) * u = g * u / (1 + exp(-g)), with the
+// hardware exp2 and reciprocal (about 1 ulp each, far below the operand
+// rounding the product then gets).  For g below about -88, exp(-g) is +inf and
+// the value is -0 (the limit); above, 1 + exp(-g) rounds to 1.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  const float den = 1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(den);
+}
 
 // ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {

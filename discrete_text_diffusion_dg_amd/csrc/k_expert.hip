@@ -218,7 +218,7 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const T
       if (r >= rows) continue;
       if (GATEUP) {
         const float g = acc[rb][0][i], u = acc[rb][1][i];
-        Num<T>::store(static_cast<T*>(out) + (size_t)(row_base + r) * N + col, g / (1.0f + expf(-g)) * u);
+        Num<T>::store(static_cast<T*>(out) + (size_t)(row_base + r) * N + col, swiglu(g, u));
       } else {
         static_cast<float*>(out)[(size_t)(row_base + r) * N + col] = acc[rb][0][i];
       }

@@ -40,7 +40,7 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
           const int f = (wn * C::WN / 32 + j) * 16 + (lane & 15);
           if (r < t.rows && f < t.cols) {
             const float g = acc[a][2 * j][i], u = acc[a][2 * j + 1][i];
-            Num<T>::store(act + (size_t)(t.row_base + r) * F + t.n0 + f, g / (1.0f + expf(-g)) * u);
+            Num<T>::store(act + (size_t)(t.row_base + r) * F + t.n0 + f, swiglu(g, u));
           }
         }
   }
