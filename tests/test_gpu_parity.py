@@ -403,6 +403,13 @@ def test_micro_many_requests_wide_attention_f32(torch_cuda):
     _run_parity(torch_cuda, mc, 18, 40, 16, 2, "micro-wide-f32", oracle_reqs=[0, 15])
 
 
+def test_micro_ragged_vocabulary_full_step(torch_cuda):
+    # vocabulary 4160 = 32.5 chunks of 128: the fused LM-head tiles and the chunk-scaled
+    # softmax @ E product both end on a half chunk (one 64-id slice)
+    mc = micro(n_layers=1, vocab=4160)
+    _run_parity(torch_cuda, mc, 19, 50, 1, 3, "micro-ragged-vocab")
+
+
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
