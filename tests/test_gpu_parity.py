@@ -410,6 +410,13 @@ def test_micro_ragged_vocabulary_full_step(torch_cuda):
     _run_parity(torch_cuda, mc, 19, 50, 1, 3, "micro-ragged-vocab")
 
 
+def test_micro_short_canvas_two_requests(torch_cuda):
+    # a 100-position canvas: ragged query blocks, head tiles of 100 rows per request
+    # (tiles straddling requests), positions past the canvas in the commit sort
+    mc = micro(n_layers=1, canvas_len=100, vocab=2048)
+    _run_parity(torch_cuda, mc, 20, 37, 2, 2, "micro-canvas100")
+
+
 def test_micro_f32_no_prompt_dense_moe(torch_cuda):
     # empty prompt, E = k (every expert selected): the MoE is a dense weighted sum
     mc = micro(n_layers=1, dtype="f32", n_experts=4, top_k=4, self_cond=True, vocab=1024)
