@@ -283,10 +283,39 @@ __device__ __forceinline__ uint64_t route_key(float v, int e) {
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)o << 7) | (uint64_t)(127 - e);
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
+// Wave-wide maximum of a 64-bit key, in every lane: DPP lane moves within
+// rows of 16 (pairs, quads, half rows, rows) and the gfx950 row swaps across
+// rows and halves -- plain VALU moves, where shuffles go through the LDS
+// crossbar.
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t m) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)m, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(m >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t x = ((uint64_t)hi << 32) | lo;
+  return x > m ? x : m;
 }
+__device__ __forceinline__ uint64_t max_swap_u64(uint64_t m, bool rows32) {
+  const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+  if (rows32) {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const uint64_t x = ((uint64_t)b[0] << 32) | a[0], y = ((uint64_t)b[1] << 32) | a[1];
+    return x > y ? x : y;
+  }
+  const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const uint64_t x = ((uint64_t)b[0] << 32) | a[0], y = ((uint64_t)b[1] << 32) | a[1];
+  return x > y ? x : y;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t m) {
+  m = max_dpp_u64<0xB1>(m);     // quad_perm 1,0,3,2: lane pairs
+  m = max_dpp_u64<0x4E>(m);     // quad_perm 2,3,0,1: quads
+  m = max_dpp_u64<0x141>(m);    // row_half_mirror: eight lanes
+  m = max_dpp_u64<0x140>(m);    // row_mirror: rows of 16
+  m = max_swap_u64(m, false);   // rows 0/1 and 2/3
+  return max_swap_u64(m, true); // halves
+}
+
 __device__ __forceinline__ void topk_rounds(const float* row, int E, int k, int lane, int* sel_e, float* sel_v) {
   bool a0 = lane < E, a1 = lane + 64 < E;
   const uint64_t k0 = a0 ? route_key(row[lane], lane) : 0ull, k1 = a1 ? route_key(row[lane + 64], lane + 64) : 0ull;
@@ -296,11 +325,7 @@ __device__ __forceinline__ void topk_rounds(const float* row, int E, int k, int 
     // still finds the one remaining owner
     uint64_t m = a0 ? k0 : 0ull;
     if (a1 && (!a0 || k1 > k0)) m = k1;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t x = shfl_xor_u64(m, o);
-      m = x > m ? x : m;
-    }
+    m = wave_max_u64(m);
     const int e = 127 - (int)(m & 127u);
     if (a0 && k0 == m) a0 = false;
     if (a1 && k1 == m) a1 = false;
