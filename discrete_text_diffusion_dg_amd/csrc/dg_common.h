@@ -1,5 +1,6 @@
 // Device-side building blocks shared by the gfx950 kernels of the denoise step.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -97,14 +98,53 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // ------------------------------------------------------------------ reductions
+// Wave-wide butterflies in six lane-exchange steps, all plain VALU moves (the
+// shuffles they replace go through the LDS crossbar): DPP moves inside rows
+// of 16 lanes -- pairs, quads, mirrored half rows, mirrored rows -- then the
+// gfx950 row swaps (rows 0/1 and 2/3, then the two halves).  Each step pairs
+// every lane with one partner (an involution), so after step s every lane
+// holds the combination of its 2^(s+1) lanes; with a commutative merge the
+// two lanes of a pair compute the same value.
+template <int S>
+__device__ __forceinline__ uint32_t lane_partner(uint32_t v) {
+  if constexpr (S == 0) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+  } else if constexpr (S == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);    // quad_perm 2,3,0,1
+  } else if constexpr (S == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  } else if constexpr (S == 3) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // row_mirror
+  } else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);         // rows 0/1, 2/3
+    return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);         // halves
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ float lane_partner(float v) { return __uint_as_float(lane_partner<S>(__float_as_uint(v))); }
+template <int S>
+__device__ __forceinline__ int lane_partner(int v) { return (int)lane_partner<S>((uint32_t)v); }
+template <int S>
+__device__ __forceinline__ double lane_partner(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint64_t p = ((uint64_t)lane_partner<S>((uint32_t)(u >> 32)) << 32) | lane_partner<S>((uint32_t)u);
+  return __longlong_as_double((long long)p);
+}
+// f(step) for the six steps, each with its step as a compile-time constant
+template <class F>
+__device__ __forceinline__ void butterfly_steps(F&& f) {
+  f(std::integral_constant<int, 0>{}); f(std::integral_constant<int, 1>{}); f(std::integral_constant<int, 2>{});
+  f(std::integral_constant<int, 3>{}); f(std::integral_constant<int, 4>{}); f(std::integral_constant<int, 5>{});
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  butterfly_steps([&](auto st) { v += lane_partner<decltype(st)::value>(v); });
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  butterfly_steps([&](auto st) { v = fmaxf(v, lane_partner<decltype(st)::value>(v)); });
   return v;
 }
 

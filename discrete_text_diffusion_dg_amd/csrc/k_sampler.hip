@@ -72,11 +72,11 @@ __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int
     top2_merge(t2, Top2{p[j].g1, p[j].gidx, p[j].g2});
   }
   mloc = wave_max(mloc);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    argmax_merge(lmax, lidx, __shfl_xor(lmax, o, 64), __shfl_xor(lidx, o, 64));
-    top2_merge(t2, Top2{__shfl_xor(t2.b1, o, 64), __shfl_xor(t2.i1, o, 64), __shfl_xor(t2.b2, o, 64)});
-  }
+  butterfly_steps([&](auto st) {
+    constexpr int S = decltype(st)::value;
+    argmax_merge(lmax, lidx, lane_partner<S>(lmax), lane_partner<S>(lidx));
+    top2_merge(t2, Top2{lane_partner<S>(t2.b1), lane_partner<S>(t2.i1), lane_partner<S>(t2.b2)});
+  });
   if (lane == 0) {
     sm_m[wv] = mloc; sm_l[wv] = lmax; sm_li[wv] = lidx; sm_g1[wv] = t2.b1; sm_gi[wv] = t2.i1; sm_g2[wv] = t2.b2;
   }
@@ -90,11 +90,10 @@ __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int
     S += (double)p[j].s * f;
     W += f * ((double)p[j].w + ((double)p[j].m - m) * (double)p[j].s);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    S += __shfl_xor(S, o, 64);
-    W += __shfl_xor(W, o, 64);
-  }
+  butterfly_steps([&](auto st) {
+    S += lane_partner<decltype(st)::value>(S);
+    W += lane_partner<decltype(st)::value>(W);
+  });
   if (lane == 0) { sm_S[wv] = S; sm_W[wv] = W; }
   __syncthreads();
   S = ((sm_S[0] + sm_S[1]) + sm_S[2]) + sm_S[3];
