@@ -101,7 +101,7 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
     for (int k = 0; k < 64; ++k) top2_insert_ordered(t2, x[k] * inv_t + gumbel_of(xs[k & 15][k >> 4]), v0 + k);
   }
   // the chunk's row max, then exp(z - m) and its sums (ids in order)
-  const float m = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+  const float m = fmaxf(zmax, lane_partner<5>(zmax));     // lane ^ 32: the row's other half
   float s = 0.f, ws = 0.f;
   if (have) {
 #pragma unroll
@@ -125,10 +125,10 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
     }
   }
   // the two halves of the row (lanes l and l ^ 32): sums in half order
-  const float so = __shfl_xor(s, 32, 64), wo = __shfl_xor(ws, 32, 64);
-  const float lo = __shfl_xor(lmax, 32, 64);
-  const int lio = __shfl_xor(lidx, 32, 64);
-  const Top2 to{__shfl_xor(t2.b1, 32, 64), __shfl_xor(t2.i1, 32, 64), __shfl_xor(t2.b2, 32, 64)};
+  const float so = lane_partner<5>(s), wo = lane_partner<5>(ws);
+  const float lo = lane_partner<5>(lmax);
+  const int lio = lane_partner<5>(lidx);
+  const Top2 to{lane_partner<5>(t2.b1), lane_partner<5>(t2.i1), lane_partner<5>(t2.b2)};
   if (half == 0 && rl < rows) {
     argmax_merge(lmax, lidx, lo, lio);
     top2_merge(t2, to);

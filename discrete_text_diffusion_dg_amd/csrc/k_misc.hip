@@ -454,17 +454,17 @@ __global__ __launch_bounds__(64 * NW) void k_router_select(const float* part, in
     const int e = q < nent ? se[q] : -1;
     int r = 0;
     for (int u = u0; u < u1 && u < q; ++u) r += se[u] == e;
-    r += __shfl_xor(r, 1, 64);
-    r += __shfl_xor(r, 2, 64);
-    r += __shfl_xor(r, 4, 64);
+    r += lane_partner<0>(r);      // the eight lanes of the entry: pairs, quads, half rows
+    r += lane_partner<1>(r);
+    r += lane_partner<2>(r);
     if (q < nent && sl == 0) pos[(size_t)r0 * k + q] = r;
   }
   {
     int c = 0;
     for (int u = u0; u < u1 && u < nent; ++u) c += se[u] == q;
-    c += __shfl_xor(c, 1, 64);
-    c += __shfl_xor(c, 2, 64);
-    c += __shfl_xor(c, 4, 64);
+    c += lane_partner<0>(c);
+    c += lane_partner<1>(c);
+    c += lane_partner<2>(c);
     if (q < E && sl == 0) cnt[(size_t)q * gridDim.x + blockIdx.x] = c;
   }
 }
@@ -690,7 +690,10 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
       acc += x0.x * wv[0]; acc += x0.y * wv[1]; acc += x0.z * wv[2]; acc += x0.w * wv[3];
       acc += x1.x * wv[4]; acc += x1.y * wv[5]; acc += x1.z * wv[6]; acc += x1.w * wv[7];
     }
-  for (int o = tpe >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  // the expert's tpe (aligned, a power of two <= 64) lanes: butterfly steps up to tpe
+  butterfly_steps([&](auto st) {
+    if ((2 << decltype(st)::value) <= tpe) acc += lane_partner<decltype(st)::value>(acc);
+  });
   if (sl == 0) {
     lg[e] = acc;
     rlog[(size_t)r * E + e] = acc;
