@@ -140,6 +140,22 @@ __global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, int 
 }
 
 // ------------------------------------------------------------------ commit
+// Value of lane (lane ^ J) for J < 64: quad permutes for 1 and 2, row shifts
+// for 4 and 8 (the partner lies J lanes up or down inside the row of 16), the
+// gfx950 row swaps for 16 and 32.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (J == 1 || J == 2 || J == 16 || J == 32) {
+    return lane_partner<J == 1 ? 0 : J == 2 ? 1 : J == 16 ? 4 : 5>(v);
+  } else {
+    static_assert(J == 4 || J == 8, "lane distance");
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x100 + J, 0xF, 0xF, false);   // row_shl: lane + J
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x110 + J, 0xF, 0xF, false);   // row_shr: lane - J
+    return (lane & J) ? dn : up;
+  }
+}
+
 // One workgroup per request: bitonic sort of (H, position), fp64 running total
 // in sorted order (thread 0, sequential, so the rounding is fixed), then every
 // position takes y or a fresh uniform token.
@@ -158,23 +174,49 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
   const size_t base = (size_t)b * n;
   sh[t] = t < n ? H[base + t] : INFINITY;
   hpos[t] = sh[t];
-  sp[t] = t;
   if (t == 0) s_diff = 0;
   __syncthreads();
   if (t < n && stop_mode == 2 && am[base + t] != prev_am[base + t]) s_diff = 1;
-  for (int k = 2; k <= 256; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int o = t ^ j;
-      if (o > t) {
-        const bool asc = (t & k) == 0;
-        const float ha = sh[t], hb = sh[o];
-        const int pa = sp[t], pb = sp[o];
-        const bool gt = ha > hb || (ha == hb && pa > pb);
-        if (gt == asc) { sh[t] = hb; sh[o] = ha; sp[t] = pb; sp[o] = pa; }
-      }
-      __syncthreads();
-    }
-  }
+  // bitonic sort of (H, position) over the 256 threads, ascending; thread i
+  // holds element i.  Partners within a wave (distance < 64) are exchanged by
+  // lane moves, the others through LDS.
+  float kh = sh[t];
+  int kp = t;
+  auto cmpx = [&](int k, int j, float ph, int pp) __attribute__((always_inline)) {
+    const bool asc = (t & k) == 0, lower = (t & j) == 0;
+    const bool gt = kh > ph || (kh == ph && kp > pp);      // this element orders after its partner
+    if ((lower == asc) == gt) { kh = ph; kp = pp; }        // keep the smaller (or larger) of the pair
+  };
+  auto step_lds = [&](int k, int j) __attribute__((always_inline)) {
+    sh[t] = kh; sp[t] = kp;
+    __syncthreads();
+    const float ph = sh[t ^ j];
+    const int pp = sp[t ^ j];
+    __syncthreads();
+    cmpx(k, j, ph, pp);
+  };
+  auto step_lane = [&](int k, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    const float ph = __uint_as_float(xor_lane<J>(__float_as_uint(kh)));
+    const int pp = (int)xor_lane<J>((uint32_t)kp);
+    cmpx(k, J, ph, pp);
+  };
+  auto lanes_from = [&](int k, int jtop) __attribute__((always_inline)) {   // steps j = jtop .. 1 (jtop < 64)
+    if (jtop >= 32) step_lane(k, std::integral_constant<int, 32>{});
+    if (jtop >= 16) step_lane(k, std::integral_constant<int, 16>{});
+    if (jtop >= 8) step_lane(k, std::integral_constant<int, 8>{});
+    if (jtop >= 4) step_lane(k, std::integral_constant<int, 4>{});
+    if (jtop >= 2) step_lane(k, std::integral_constant<int, 2>{});
+    step_lane(k, std::integral_constant<int, 1>{});
+  };
+  for (int k = 2; k <= 64; k <<= 1) lanes_from(k, k >> 1);
+  step_lds(128, 64);
+  lanes_from(128, 32);
+  step_lds(256, 128);
+  step_lds(256, 64);
+  lanes_from(256, 32);
+  sh[t] = kh; sp[t] = kp;
+  __syncthreads();
   rank[sp[t]] = t;
   if (t == 0) {
     const double bnd = (double)bound;
