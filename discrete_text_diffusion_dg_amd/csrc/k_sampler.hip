@@ -170,13 +170,19 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
   __shared__ int rank[256];
   __shared__ int s_cnt, s_final, s_diff;
   const int b = blockIdx.x, t = threadIdx.x;
-  if (done[b]) return;
   const size_t base = (size_t)b * n;
-  sh[t] = t < n ? H[base + t] : INFINITY;
-  hpos[t] = sh[t];
+  // every input of this position is requested at once (a finished request
+  // returns after its loads, before any barrier)
+  const uint8_t fin_before = done[b];
+  const float h_in = t < n ? H[base + t] : INFINITY;
+  const int32_t y_t = t < n ? y[base + t] : 0, am_t = t < n ? am[base + t] : 0;
+  const int32_t pam_t = t < n ? prev_am[base + t] : 0;
+  if (fin_before) return;
+  sh[t] = h_in;
+  hpos[t] = h_in;
   if (t == 0) s_diff = 0;
   __syncthreads();
-  if (t < n && stop_mode == 2 && am[base + t] != prev_am[base + t]) s_diff = 1;
+  if (t < n && stop_mode == 2 && am_t != pam_t) s_diff = 1;
   // bitonic sort of (H, position) over the 256 threads, ascending; thread i
   // holds element i.  Partners within a wave (distance < 64) are exchanged by
   // lane moves, the others through LDS.
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
   if (t < n) {
     const bool fin = s_final != 0;
     const bool keep = fin || rank[t] < s_cnt;
-    int32_t tok = y[base + t];
+    int32_t tok = y_t;
     if (!keep) {
       const uint4 x = philox_block(seeds.v[b], kTagRenoise, (uint32_t)canvas_index, (uint32_t)step,
                                    (uint32_t)t, 0u);
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
     }
     canvas[base + t] = tok;
     mask[base + t] = keep ? 1 : 0;
-    prev_am[base + t] = am[base + t];
+    prev_am[base + t] = am_t;
   }
   if (t == 0) {
     n_committed[b] = s_final ? n : s_cnt;
