@@ -102,7 +102,14 @@ __global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t*
     if (j < nj) {
       const int c = (j * blockDim.x + threadIdx.x) * 4;
       const T* e = emb + (size_t)id * d + c;
-      float4 x = make_float4(Num<T>::load(e), Num<T>::load(e + 1), Num<T>::load(e + 2), Num<T>::load(e + 3));
+      float4 x;
+      if constexpr (sizeof(T) == 2) {           // four bf16 in one 8-byte load
+        const uint2 u = *reinterpret_cast<const uint2*>(e);
+        x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+      } else {
+        x = *reinterpret_cast<const float4*>(e);
+      }
       add4(x, S > 0 ? sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c) : make_float4(0.f, 0.f, 0.f, 0.f));
       v[j] = x;
     }
