@@ -78,10 +78,15 @@ __device__ __forceinline__ void split_p(Frag<bf16> (&f)[2], float* r) {
                       f32x2_to_bf16x2(r[6], r[7]));
 }
 __device__ __forceinline__ void split_p(Frag<float> (&f)[1], float* r) { set_p(f[0], r); }
+// Four consecutive output values (dst 4-element aligned): one 8-byte store of
+// bf16 pairs, or one 16-byte store.
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const float* v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) Num<T>::store(dst + j, v[j]);
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // ---- wide: 16 * NWQ query rows per workgroup sharing LDS-staged K / V^T tiles
