@@ -78,8 +78,10 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
   float lmax = -INFINITY;
   int lidx = 0x7fffffff;
   if (have) {
+    // ids local to the half (constants of the unrolled scan), made global once
 #pragma unroll
-    for (int k = 0; k < 64; ++k) argmax_insert_ordered(lmax, lidx, x[k], v0 + k);
+    for (int k = 0; k < 64; ++k) argmax_insert_ordered(lmax, lidx, x[k], k);
+    lidx += v0;
   }
   const float zmax = lmax * inv_t;
   // Gumbel-max top two: every value is scored (a lane owns a row of its own,
@@ -98,7 +100,8 @@ __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int r
       xs[c][0] = xw.x; xs[c][1] = xw.y; xs[c][2] = xw.z; xs[c][3] = xw.w;
     }
 #pragma unroll
-    for (int k = 0; k < 64; ++k) top2_insert_ordered(t2, x[k] * inv_t + gumbel_of(xs[k & 15][k >> 4]), v0 + k);
+    for (int k = 0; k < 64; ++k) top2_insert_ordered(t2, x[k] * inv_t + gumbel_of(xs[k & 15][k >> 4]), k);
+    t2.i1 += v0;
   }
   // the chunk's row max, then exp(z - m) and its sums (ids in order)
   const float m = fmaxf(zmax, lane_partner<5>(zmax));     // lane ^ 32: the row's other half
