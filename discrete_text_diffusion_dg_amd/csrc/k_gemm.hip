@@ -88,11 +88,21 @@ struct EpQKV {
     __syncthreads();
     constexpr int half = HD / 2;
     const int head = t.n0 / HD;
+    // request and position of a row: shifts when the canvas length is a power
+    // of two (the usual 256), else a division
+    const bool pow2 = (n & (n - 1)) == 0;
+    const int nsh = __ffs(n) - 1;
+    auto split_row = [&](int row, int& b, int& pos) __attribute__((always_inline)) {
+      if (pow2) { b = row >> nsh; pos = ctx + (row & (n - 1)); }
+      else { b = row / n; pos = ctx + row % n; }
+    };
     if (head < Hq + Hkv) {
       for (int u = threadIdx.x; u < C::BM * half; u += blockDim.x) {
         const int r = u / half, j = u % half;
         if (r >= t.rows) continue;
-        const int row = t.m0 + r, b = row / n, pos = ctx + row % n;
+        const int row = t.m0 + r;
+        int b, pos;
+        split_row(row, b, pos);
         const float a = tile[r * kLd + j], bb = tile[r * kLd + j + half];
         const float2 cs = rope[(size_t)pos * half + j];
         const float o1 = a * cs.x - bb * cs.y, o2 = bb * cs.x + a * cs.y;
@@ -106,7 +116,9 @@ struct EpQKV {
       for (int u = threadIdx.x; u < C::BM * HD; u += blockDim.x) {
         const int c = u / C::BM, r = u % C::BM;           // consecutive threads: consecutive positions
         if (r >= t.rows) continue;
-        const int row = t.m0 + r, b = row / n, pos = ctx + row % n;
+        const int row = t.m0 + r;
+        int b, pos;
+        split_row(row, b, pos);
         Num<T>::store(vc + (((size_t)b * Hkv + kh) * HD + c) * stride + pos, tile[r * kLd + c]);
       }
     }
