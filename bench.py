@@ -4,10 +4,16 @@
 A step is one dg_denoise_step + dg_sample_commit over the canvas batch; at the
 end of each canvas's step budget the canvas is appended to the KV cache
 (dg_commit_canvas_to_kv, inside the timed region) and a fresh canvas starts.
-value = committed canvas tokens per second = B * 256 * canvases / seconds,
-with a partially finished canvas counted pro rata.  Inputs (weights, prompt)
-are seeded synthetic data already resident in device memory when timing
-starts; the prompt encode is timed separately.
+value = committed canvas tokens per second = B * 256 * (K / S) / seconds for
+K timed steps of an S-step canvas budget, the seconds being the timed steps
+plus the pro-rata share K / S of one canvas commit (whatever commits fall in
+the timed region are replaced by that share).  The default workload is the
+26B-A4B-scale proxy (30 layers, d 2048, 128 experts top-8, vocabulary
+262144); the small, multi-canvas and batched workloads follow in short runs
+reported under other_workloads.  Inputs (weights, prompt) are seeded
+synthetic data already resident in device memory when timing starts; the
+prompt encode is timed separately.  Per-step latencies come from one event
+per step on the launch stream (median and p90 reported).
 
 The dominant stage is picked from an all-stage timing pass during warm-up, then
 timed live with HIP events inside the library (on the launch stream) during
@@ -140,42 +146,237 @@ def roofline(stage, ms_total, launches, mc, B, ctx, n_act, traffic=None):
             "launch_us": round(t * 1e6, 2), "bytes_per_launch": by, "flops_per_launch": fl}
 
 
-def cpu_baseline(wl, weights, prompts, seeds, budget_s: float):
-    """Oracle on the host cores: prompt encode, then denoise steps and one canvas commit."""
-    from oracle.model import OracleModel
-    from oracle import sampler as osmp
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle on the host cores, on a bounded sample of the workload.
+
+    Models of up to 8 layers run whole: prompt encode, denoise + commit steps
+    until about half the budget is spent (at least 2), one canvas commit.
+    Deeper models run their first 2 layers (the same seeded weights) with the
+    full embedding, LM head and sampler; each pass's time is extrapolated to
+    all layers from the measured per-layer time (labelled as such)."""
+    import dataclasses
+    from oracle.model import OracleModel
+    from oracle import sampler as osmp
     mc, sp = wl.model, wl.sampler
     B = wl.batch
-    om = OracleModel(mc, weights, B, wl.prompt_len + 2 * mc.canvas_len)
-    t0 = time.perf_counter()
-    om.encode_prompt(prompts)
-    t_enc = time.perf_counter() - t0
-    canvas = np.stack([osmp.init_canvas(int(seeds[b]), 0, mc.canvas_len, mc.vocab) for b in range(B)])
-    steps, t_steps = 0, 0.0
-    while steps < 2 or (t_steps < budget_s * 0.5 and steps < sp.max_steps):
+    L_full = mc.n_layers
+    L_run = L_full if L_full <= 8 else 2
+    mrun = dataclasses.replace(mc, n_layers=L_run)
+    weights = di.make_weights(mrun, wl.seed)
+    prompts = di.make_prompts(mc.vocab, B, wl.prompt_len, wl.seed)
+    seeds = di.request_seeds(wl.seed, B)
+    om = OracleModel(mrun, weights, B, wl.prompt_len + 2 * mc.canvas_len)
+    om.W("emb")                        # widened once, as a resident model would hold it
+    marks = []
+    om.on_layer = lambda l: marks.append(time.perf_counter())
+
+    def timed(fn):
+        """(seconds, seconds extrapolated to L_full layers) of one pass over the requests."""
+        marks.clear()
         t0 = time.perf_counter()
-        out = om.denoise_step(canvas, steps, sp, seeds)
-        for b in range(B):
-            canvas[b], _, _, _ = osmp.commit(out["H"][b], out["y"][b], out["am"][b], None, canvas[b], steps,
-                                             sp.max_steps, sp.entropy_bound, sp.stop_mode, sp.stop_tau,
-                                             int(seeds[b]), 0, mc.vocab)
-        t_steps += time.perf_counter() - t0
+        fn()
+        t = time.perf_counter() - t0
+        if L_run == L_full:
+            return t, t
+        # marks: end of each layer, request after request; a layer's time is the gap
+        # to the previous layer's end within the same request
+        gaps = [marks[j + l] - marks[j + l - 1] for j in range(0, len(marks), L_run) for l in range(1, L_run)]
+        per_layer = float(np.mean(gaps)) if gaps else 0.0
+        return t, t + (L_full - L_run) * per_layer * (len(marks) // L_run)
+
+    t_enc, x_enc = timed(lambda: om.encode_prompt(prompts))
+    canvas = np.stack([osmp.init_canvas(int(seeds[b]), 0, mc.canvas_len, mc.vocab) for b in range(B)])
+    steps, t_steps, x_steps = 0, 0.0, 0.0
+    while steps < 2 or (t_steps < budget_s * 0.5 and steps < sp.max_steps):
+        def one():
+            out = om.denoise_step(canvas, steps, sp, seeds)
+            for b in range(B):
+                canvas[b], _, _, _ = osmp.commit(out["H"][b], out["y"][b], out["am"][b], None, canvas[b], steps,
+                                                 sp.max_steps, sp.entropy_bound, sp.stop_mode, sp.stop_tau,
+                                                 int(seeds[b]), 0, mc.vocab)
+        t, x = timed(one)
+        t_steps += t
+        x_steps += x
         steps += 1
-    t0 = time.perf_counter()
-    om.commit_canvas_to_kv(canvas)
-    t_commit = time.perf_counter() - t0
-    t_step = t_steps / steps
-    tok_s = B * mc.canvas_len / (sp.max_steps * t_step + t_commit)
-    return {"value": round(tok_s, 3), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"{wl.name}: prompt encode ({wl.prompt_len} tokens x {B}) {t_enc:.2f} s, "
-                       f"{steps} denoise+commit steps {t_step:.3f} s/step, canvas commit {t_commit:.2f} s; "
-                       f"tok/s = {B}*{mc.canvas_len} / ({sp.max_steps} steps * s/step + commit)"),
-            "ms_per_step": round(t_step * 1e3, 2)}
+    _, x_commit = timed(lambda: om.commit_canvas_to_kv(canvas))
+    x_step = x_steps / steps
+    tok_s = B * mc.canvas_len / (sp.max_steps * x_step + x_commit)
+    part = ("" if L_run == L_full else
+            f"; first {L_run} of {L_full} layers run (same weights, full embedding, LM head and sampler), "
+            f"each pass extrapolated to {L_full} layers from its measured per-layer time")
+    return {"value": round(tok_s, 4), "unit": "tok/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": (f"{wl.name}: prompt encode ({wl.prompt_len} tokens x {B}) {x_enc:.2f} s, "
+                       f"{steps} denoise+commit steps {x_step:.3f} s/step, canvas commit {x_commit:.2f} s; "
+                       f"tok/s = {B}*{mc.canvas_len} / ({sp.max_steps} steps * s/step + commit){part}"),
+            "ms_per_step": round(x_step * 1e3, 2), "extrapolated": L_run != L_full}
+
+
+class Runner:
+    """One workload on the device: weights, engine, prompt encode, the step loop."""
+
+    def __init__(self, wl, steps: int, warmup: int):
+        import torch
+        from discrete_text_diffusion_dg_amd.runtime import Engine, upload_weights
+        self.torch = torch
+        self.wl = wl
+        mc, sp = wl.model, wl.sampler
+        self.B, self.n, self.S = wl.batch, mc.canvas_len, sp.max_steps
+        total = warmup + steps + self.S          # + one accounting canvas
+        canvases = (total + self.S - 1) // self.S + 2
+        max_ctx = wl.prompt_len + self.n * (canvases + 1)
+        t0 = time.perf_counter()
+        W = di.make_weights(mc, wl.seed, cache=False)       # streamed: generated, uploaded, dropped
+        names = W.names()
+        dw, done_b, next_log = {}, 0, 4e9
+        for nm_ in names:
+            dw.update(upload_weights(W, [nm_], "cuda"))
+            done_b += dw[nm_].numel() * dw[nm_].element_size()
+            if done_b >= next_log:
+                log(f"[bench] {wl.name}: {done_b / 1e9:.1f} of {W.nbytes() / 1e9:.1f} GB of weights on the device")
+                next_log += 4e9
+        log(f"[bench] {wl.name}: weights {W.nbytes() / 1e9:.2f} GB generated+uploaded in "
+            f"{time.perf_counter() - t0:.1f} s")
+        self.eng = Engine(mc, dw, names, self.B, max_ctx)
+        self.eng.set_seeds(di.request_seeds(wl.seed, self.B))
+        prompts = torch.from_numpy(di.make_prompts(mc.vocab, self.B, wl.prompt_len, wl.seed)).cuda()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.eng.encode_prompt(prompts)
+        e1.record()
+        torch.cuda.synchronize()
+        self.encode_ms = e0.elapsed_time(e1)
+        log(f"[bench] {wl.name}: prompt encode {self.encode_ms:.2f} ms")
+        self.t = 0
+        self.canvases_done = 0
+        self.commit_ev = None
+        self.eng.init_canvas()
+
+    def step(self):
+        eng, sp = self.eng, self.wl.sampler
+        t = self.t
+        eng.denoise_step(t, sp)
+        eng.sample_commit(t, sp)
+        t += 1
+        finished = bool((eng.done != 0).all()) if sp.stop_mode != 0 else t >= self.S
+        if finished or t >= self.S:
+            if self.commit_ev is not None:
+                self.commit_ev[0].record()
+            eng.commit_canvas_to_kv()
+            if self.commit_ev is not None:
+                self.commit_ev[1].record()
+            self.canvases_done += 1
+            eng.init_canvas()
+            eng.done.zero_()
+            t = 0
+        self.t = t
+
+    def close(self):
+        self.eng.close()
+        del self.eng
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def measure(wl, steps: int, warmup: int, stage_detail: bool):
+    """Timed run of one workload; returns the bench fields (and the Runner, still open)."""
+    import torch
+    r = Runner(wl, steps, warmup)
+    eng, mc = r.eng, wl.model
+    B, n, S = r.B, r.n, r.S
+    n_first = 1 if warmup > 1 else 0
+    for _ in range(n_first):
+        r.step()
+    prof = {}
+    if stage_detail:
+        eng.profile(STAGES)
+    for _ in range(warmup - n_first):
+        r.step()
+    torch.cuda.synchronize()
+    if stage_detail:
+        prof = eng.profile_read()
+    ctx_w = eng.ctx_len
+    dominant = max(prof, key=lambda k: prof[k][0]) if prof else None
+    routed = eng.route_view(B * n).cpu().numpy()
+    act_per_layer = [int(np.unique(x).size) for x in routed]
+    n_act = float(np.mean(act_per_layer))
+    r.canvases_done = 0
+    # timed region: exactly `steps` steps; one event before each step (same stream as the
+    # library's launches) gives the per-step latencies; only the dominant stage carries
+    # the library's own event pairs
+    eng.profile([dominant] if dominant else [])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        r.step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    ms = float(ev[0].elapsed_time(ev[steps]))
+    dom_ms, dom_n = eng.profile_read().get(dominant, (0.0, 0)) if dominant else (0.0, 0)
+    eng.profile([])
+    commits_timed = r.canvases_done
+    # accounting canvas (untimed): positions committed per step over one whole canvas,
+    # and the time of one canvas commit to the KV cache
+    r.canvases_done = 0
+    r.commit_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    while r.t != 0 or r.canvases_done == 0:
+        r.step()
+    torch.cuda.synchronize()
+    commit_ms = r.commit_ev[0].elapsed_time(r.commit_ev[1])
+    r.commit_ev = None
+    ncom = []
+    for _ in range(S):
+        t_before = r.t
+        eng.denoise_step(t_before, wl.sampler)
+        eng.sample_commit(t_before, wl.sampler)
+        ncom.append(int(eng.n_committed.sum().item()))
+        r.t = t_before + 1
+        if r.t >= S or (wl.sampler.stop_mode != 0 and bool((eng.done != 0).all())):
+            break
+    # committed canvas tokens over the step + commit time they cost: the timed region's
+    # own commits are replaced by the pro-rata share of one commit (steps / S canvases)
+    canv = steps / S
+    ms_adj = ms - commits_timed * commit_ms + canv * commit_ms
+    tok_s = B * n * canv / (ms_adj / 1e3)
+    out = {"value": round(tok_s, 2), "ms_per_step": round(ms / steps, 4), "commit_ms": round(commit_ms, 3),
+           "canvases_per_timed_region": round(canv, 4), "commits_in_timed_region": commits_timed,
+           "ms_per_step_median": round(float(np.median(per)), 4),
+           "ms_per_step_p90": round(float(np.percentile(per, 90)), 4),
+           "steps_per_s": round(steps / (ms / 1e3), 2), "encode_ms": round(r.encode_ms, 3),
+           "wall_ms": round(wall * 1e3, 2), "n_committed_per_step": ncom,
+           "active_experts_per_layer": act_per_layer}
+    if stage_detail:
+        out["stage_ms_warmup"] = {k: round(v[0] / max(warmup - n_first, 1), 4) for k, v in prof.items()}
+        out["roofline"] = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act,
+                                   measured_traffic(wl.name, dominant)) if dominant else None
+        stage_rl = {}
+        for k, (k_ms, k_n) in prof.items():
+            x = roofline(k, k_ms, k_n, mc, B, ctx_w, n_act)
+            if x is not None:
+                stage_rl[k] = {f: x[f] for f in ("bound", "achieved", "unit", "frac", "launch_us")}
+        out["stage_roofline_warmup"] = stage_rl
+        log(f"[bench] {wl.name}: warm-up stage ms: " + ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in prof.items()))
+        log(f"[bench] {wl.name}: dominant {dominant}: {dom_ms / max(dom_n, 1) * 1e3:.1f} us/launch")
+    log(f"[bench] {wl.name}: {steps} steps in {ms:.2f} ms (median {np.median(per):.3f}, p90 "
+        f"{np.percentile(per, 90):.3f} ms/step; wall {wall * 1e3:.1f} ms); {tok_s:.1f} committed tok/s")
+    return out, r
+
+
+STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
+          "lm_head", "sampler", "selfcond", "commit"]
+EXTRA_WORKLOADS = ("small", "multicanvas", "batched")
 
 
 def main():
@@ -183,8 +384,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=6)
-    ap.add_argument("--workload", default="small", choices=sorted(di.WORKLOADS))
+    ap.add_argument("--workload", default="proxy", choices=sorted(di.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the short runs of the other workloads reported as extra keys")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 256 MiB three times (the reference kernel for the HBM counters)")
@@ -204,139 +407,51 @@ def main():
         sys.exit(2)
 
     import torch
-    from discrete_text_diffusion_dg_amd.runtime import Engine, upload_weights
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
     wl = di.workload(a.workload)
     mc, sp = wl.model, wl.sampler
-    B, n, S = wl.batch, mc.canvas_len, sp.max_steps
-    total_steps = a.warmup + a.steps
-    canvases = (total_steps + S - 1) // S + 1
-    max_ctx = wl.prompt_len + n * (canvases + 1)
-    t0 = time.perf_counter()
-    # host copies are kept only for the CPU baseline; large models stream to the device
-    W = di.make_weights(mc, wl.seed, cache=not a.no_cpu_baseline)
-    names = W.names()
-    dw, done_b, next_log = {}, 0, 4e9
-    for nm in names:
-        dw.update(upload_weights(W, [nm], "cuda"))
-        done_b += dw[nm].numel() * dw[nm].element_size()
-        if done_b >= next_log:
-            log(f"[bench] {wl.name}: {done_b / 1e9:.1f} of {W.nbytes() / 1e9:.1f} GB of weights on the device")
-            next_log += 4e9
-    log(f"[bench] {wl.name}: weights {W.nbytes() / 1e9:.2f} GB generated+uploaded in {time.perf_counter() - t0:.1f} s")
-    eng = Engine(mc, dw, names, B, max_ctx)
-    seeds = di.request_seeds(wl.seed, B)
-    eng.set_seeds(seeds)
-    prompts = di.make_prompts(mc.vocab, B, wl.prompt_len, wl.seed)
-    pt = torch.from_numpy(prompts).cuda()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    eng.encode_prompt(pt)
-    e1.record()
-    torch.cuda.synchronize()
-    encode_ms = e0.elapsed_time(e1)
-    log(f"[bench] prompt encode {encode_ms:.2f} ms")
-
-    state = {"t": 0, "canvases_done": 0}
-    eng.init_canvas()
-
-    def one_step():
-        t = state["t"]
-        eng.denoise_step(t, sp)
-        eng.sample_commit(t, sp)
-        t += 1
-        if sp.stop_mode != 0:
-            finished = bool((eng.done != 0).all())
-        else:
-            finished = t >= S
-        if finished or t >= S:
-            eng.commit_canvas_to_kv()
-            state["canvases_done"] += 1
-            eng.init_canvas()
-            eng.done.zero_()
-            t = 0
-        state["t"] = t
-
-    # warm-up; every stage is timed after the first step (first launches pay
-    # one-off costs) to find the dominant one
-    n_first = 1 if a.warmup > 1 else 0
-    for _ in range(n_first):
-        one_step()
-    eng.profile(["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
-                 "lm_head", "sampler", "selfcond", "commit"])
-    for _ in range(a.warmup - n_first):
-        one_step()
-    torch.cuda.synchronize()
-    prof = eng.profile_read()
-    ctx_w = eng.ctx_len
-    dominant = max(prof, key=lambda k: prof[k][0]) if prof else "expert_up"
-    log("[bench] warm-up stage ms: " + ", ".join(f"{k} {v[0]:.2f}/{v[1]}" for k, v in prof.items()))
-    # experts that receive rows, averaged over the layers (one expert launch per layer)
-    routed = eng.route_view(B * n).cpu().numpy()
-    act_per_layer = [int(np.unique(r).size) for r in routed]
-    n_act = float(np.mean(act_per_layer))
-    log(f"[bench] active experts per layer: {act_per_layer}")
-
-    # timed region: exactly K steps, only the dominant stage carries events
-    eng.profile([dominant])
-    state["canvases_done"] = 0
-    t_start_step = state["t"]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    e0.record()
-    for _ in range(a.steps):
-        one_step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms = e0.elapsed_time(e1)
-    dom_ms, dom_n = eng.profile_read().get(dominant, (0.0, 0))
-    eng.profile([])
-    canv = a.steps / S
-    tok_s = B * n * canv / (ms / 1e3)
-    rl = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act, measured_traffic(wl.name, dominant))
-    # every stage against its own roofline, from the warm-up event timings
-    # (matrix-core fraction for the products and attention, HBM fraction for
-    # the streaming stages)
-    stage_rl = {}
-    for k, (k_ms, k_n) in prof.items():
-        r = roofline(k, k_ms, k_n, mc, B, ctx_w, n_act)
-        if r is not None:
-            stage_rl[k] = {f: r[f] for f in ("bound", "achieved", "unit", "frac", "launch_us")}
-    log(f"[bench] {a.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms); dominant {dominant}: "
-        f"{dom_ms / max(dom_n, 1) * 1e3:.1f} us/launch")
-
+    res, runner = measure(wl, a.steps, a.warmup, stage_detail=True)
+    runner.close()
+    extras = {}
+    if not a.no_extras:
+        for name in EXTRA_WORKLOADS:
+            if name == wl.name:
+                continue
+            try:
+                x, r = measure(di.workload(name), 24, 3, stage_detail=False)
+                r.close()
+                extras[name] = {k: x[k] for k in ("value", "ms_per_step", "ms_per_step_median", "ms_per_step_p90",
+                                                  "steps_per_s", "encode_ms")}
+                extras[name]["steps"] = 24
+            except Exception as ex:   # reported, never fatal for the headline
+                extras[name] = {"error": repr(ex)}
     cpu = None
     if not a.no_cpu_baseline:
         try:
-            cpu = cpu_baseline(wl, W, prompts, seeds, a.cpu_budget)
+            cpu = cpu_baseline(wl, a.cpu_budget)
             log(f"[bench] cpu baseline {cpu['value']} tok/s ({cpu['sample']})")
         except Exception as ex:  # reported, never fatal for the GPU number
             cpu = {"value": None, "unit": "tok/s", "cores": os.cpu_count(), "kind": "oracle",
                    "sample": f"failed: {ex!r}"}
 
     line = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms / a.steps, 4), "higher_is_better": True,
+        "metric": METRIC, "value": res["value"], "unit": "tok/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": mc.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "canvas": n, "prompt_len": wl.prompt_len,
-                   "steps_per_canvas": S, "layers": mc.n_layers, "d_model": mc.d_model,
-                   "experts": f"{mc.top_k}/{mc.n_experts}", "vocab": mc.vocab,
-                   "self_cond": mc.self_cond, "parallelism": "none (1 GPU)"},
-        "steps_per_s": round(a.steps / (ms / 1e3), 2),
-        "encode_ms": round(encode_ms, 3),
-        "stage_ms_warmup": {k: round(v[0] / max(a.warmup - n_first, 1), 4) for k, v in prof.items()},
-        "roofline": rl,
-        "stage_roofline_warmup": stage_rl,
-        "active_experts_per_layer": act_per_layer,
-        "cpu_baseline": cpu,
+        "config": {"workload": wl.name, "batch": wl.batch, "canvas": mc.canvas_len, "prompt_len": wl.prompt_len,
+                   "steps_per_canvas": sp.max_steps, "layers": mc.n_layers, "d_model": mc.d_model,
+                   "heads": f"{mc.n_q_heads}/{mc.n_kv_heads}x{mc.head_dim}",
+                   "experts": f"{mc.top_k}/{mc.n_experts}", "ffn_hidden": mc.ffn_hidden, "vocab": mc.vocab,
+                   "self_cond": mc.self_cond, "stop": "mean H < %g" % sp.stop_tau if sp.stop_mode else "none",
+                   "parallelism": "none (1 GPU)"},
     }
+    line.update({k: v for k, v in res.items() if k not in ("value", "ms_per_step")})
+    line["cpu_baseline"] = cpu
+    line["other_workloads"] = extras
     print(json.dumps(line), flush=True)
-    eng.close()
 
 
 if __name__ == "__main__":

@@ -19,9 +19,12 @@
  *     library borrows them for the duration of the call (asynchronous on the
  *     given stream: buffers must stay valid until the stream reaches the work).
  *   - Handles (dg_model, dg_state) own only host metadata, except that a model
- *     owns two derived weight copies in device memory (the transposed embedding
- *     for the self-conditioning contraction and the fused QKV matrices), made
- *     once in dg_model_create and freed by dg_model_destroy.
+ *     owns derived weight copies in device memory, made once in dg_model_create
+ *     and freed by dg_model_destroy: the fused QKV matrices ((Hq + 2 Hkv) hd d
+ *     elements per layer), the transposed embedding for the self-conditioning
+ *     contraction (V d elements, self-conditioning models), and the expert
+ *     weights in MFMA-fragment order for the weight-streaming expert kernels
+ *     (3 E F d elements per layer: as large as the caller's expert tensors).
  *   - The four step calls allocate nothing and never synchronise the device,
  *     except dg_encode_prompt / dg_commit_canvas_to_kv which only enqueue work.
  *   - Errors: a negative status is returned and a thread-local message is set
@@ -56,7 +59,7 @@ typedef int32_t dg_status;
 
 typedef struct dg_config {
   int32_t n_layers;
-  int32_t d_model;      /* multiple of 64 */
+  int32_t d_model;      /* multiple of 256, at most 4096 */
   int32_t n_q_heads;
   int32_t n_kv_heads;   /* divides n_q_heads */
   int32_t head_dim;     /* 64 or 128 */

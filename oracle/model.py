@@ -25,6 +25,8 @@ Readings where the pages are silent (no layer formula is printed):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -46,6 +48,12 @@ class OracleModel:
             cache_f64 = cfg.n_params() < 1.2e9
         self._cache_f64 = cache_f64
         self._f64: Dict[str, np.ndarray] = {}
+        # without the fp64 cache (large models), the stored tensors of the layer
+        # in use are held so that a weight set which regenerates on every access
+        # is asked for each tensor once per pass
+        self._raw: Dict[str, np.ndarray] = {}
+        self._raw_layer = None
+        self.on_layer = None      # optional callback(layer) after each layer (progress of long runs)
         L, Hkv, hd = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
         self.k_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
         self.v_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
@@ -54,19 +62,29 @@ class OracleModel:
         self.s = np.zeros((batch, cfg.canvas_len, cfg.d_model))
 
     # ------------------------------------------------------------ weights
+    def _stored(self, name: str) -> np.ndarray:
+        layer = name.split(".", 1)[0] if name.startswith("l") and "." in name else None
+        if layer is not None and layer != self._raw_layer:
+            self._raw = {}
+            self._raw_layer = layer
+        if name not in self._raw:
+            self._raw[name] = self.w.get(name)
+        return self._raw[name]
+
     def W(self, name: str) -> np.ndarray:
         if name in self._f64:
             return self._f64[name]
-        a = nm.upcast(self.w.get(name))
-        if self._cache_f64:
+        if self._cache_f64 or name == "emb":
+            a = nm.upcast(self.w.get(name))
             self._f64[name] = a
-        return a
+            return a
+        return nm.upcast(self._stored(name))
 
     def expert(self, layer: int, kind: str, e: int) -> np.ndarray:
         name = f"l{layer}.{kind}"
         if self._cache_f64:
             return self.W(name)[e]
-        return nm.upcast(self.w.get(name)[e])
+        return nm.upcast(self._stored(name)[e])
 
     # ------------------------------------------------------------ blocks
     def _moe(self, l: int, xm: np.ndarray, trace: Optional[dict]) -> np.ndarray:
@@ -78,13 +96,26 @@ class OracleModel:
         rsel = np.take_along_axis(r, idx, axis=1).astype(np.float64)
         wts = nm.softmax(rsel, axis=1)
         contrib = np.zeros((n, k, cfg.d_model))
-        for e in np.unique(idx):
+        experts = np.unique(idx)
+        kinds = ("w_gate", "w_up", "w_down")
+        if self._cache_f64:
+            mats = {(kind, e): self.expert(l, kind, e) for kind in kinds for e in experts}
+        else:
+            # widen the selected experts' stored matrices to fp64 on several threads
+            # (plain element conversions; the products below stay in order)
+            for kind in kinds:
+                self._stored(f"l{l}.{kind}")
+            keys = [(kind, e) for kind in kinds for e in experts]
+            with ThreadPoolExecutor(min(len(keys), os.cpu_count() or 1)) as ex:
+                mats = dict(zip(keys, ex.map(lambda ke: self.expert(l, ke[0], ke[1]), keys)))
+        for e in experts:
             rows, slots = np.nonzero(idx == e)
             m = xm[rows]
-            g = m @ self.expert(l, "w_gate", e).T
-            u = m @ self.expert(l, "w_up", e).T
+            g = m @ mats[("w_gate", e)].T
+            u = m @ mats[("w_up", e)].T
             a = self.rnd(nm.silu(g) * u)
-            contrib[rows, slots] = a @ self.expert(l, "w_down", e).T
+            contrib[rows, slots] = a @ mats[("w_down", e)].T
+        del mats
         y = np.zeros((n, cfg.d_model))
         for j in range(k):                                               # fixed slot order
             y += wts[:, j:j + 1] * contrib[:, j]
@@ -128,6 +159,8 @@ class OracleModel:
             trace["h0"] = h.copy()
         for l in range(self.cfg.n_layers):
             h = self._layer(l, b, h, pos, causal, store_kv, trace)
+            if self.on_layer is not None:
+                self.on_layer(l)
         return h
 
     # ------------------------------------------------------------ the four calls

@@ -24,16 +24,31 @@ from _util import log, make_engine, micro, rel_err_rows, replace, tol_for
 pytestmark = pytest.mark.gpu
 
 MARGIN_EXEMPT = 1e-3
-# Routing may differ from the oracle only where the oracle's k-th and (k+1)-th
-# router logits are closer than GAP_REL * max|r| of the row.  Both sides round
-# the same activations to bf16, but fp32 sums (whose error near-cancelling
-# attention outputs amplify to ~1e-5) against fp64 ones flip ~1% of those
-# roundings by one ulp, and the flips carry through the residual stream to a
-# router-logit drift of up to ~1% of the logit scale (the tests print the
-# measured drift).  2e-2 is the bf16 value tolerance; fp32 operands drift ~1e-6.
+# Routing may differ from the oracle only where the oracle's gap between its
+# k-th and (k+1)-th router logits is at most twice the row's measured router
+# logit discrepancy, and that discrepancy is itself held to the value
+# tolerance on logits (2e-2 of the row's largest |logit| for bf16 operands,
+# 1e-4 for fp32): both sides round the same activations to bf16, but fp32 sums
+# against fp64 ones flip a few of those roundings by one ulp, and the flips
+# carry through the residual stream to a router-logit drift the tests print.
 GAP_REL = {"bf16": 2e-2, "f32": 1e-4}
-MAX_FLIP_FRAC = 0.25     # sanity bound on rows with an (explained) routing flip
+MAX_FLIP_FRAC = 0.10     # rows of a pass with a routing flip (each one explained by the gap rule)
 MAX_KV_OFF_FRAC = 0.10   # cached K/V positions beyond the value tolerance (all at router near-ties)
+MAX_EXEMPT_TOKEN_FRAC = 0.02   # sampled tokens that differ under the margin exemption, per step
+
+
+def progress(msg: str) -> None:
+    """A progress line on stdout and in gpurun_out/test_progress.log (long cases)."""
+    import os
+    import time
+    log(msg)
+    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    try:
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "test_progress.log"), "a") as f:
+            f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+    except OSError:
+        pass
 
 
 @pytest.fixture(scope="module")
@@ -59,34 +74,45 @@ def near_tie(r: np.ndarray, mc) -> np.ndarray:
 def _routing_core(mc, groute, glog, traces, tag):
     """Routing of one pass (groute / glog: [L][requests][rows][...]) against the oracle traces.
 
-    A row's expert set may differ from the oracle's only where the oracle's gap
-    between its k-th and (k+1)-th router logits is at most twice the row's
-    measured logit discrepancy (the largest |GPU - oracle| over its experts):
-    an expert swap needs the two logits to move past each other, and each moved
-    by at most that much.  A row that flipped in an earlier layer carries other
-    values from then on and is not checked again.  Returns the flipped rows."""
+    Router logits of every row not yet flipped must match the oracle's within the
+    value tolerance (GAP_REL of the row's largest |logit|).  A row's expert set
+    may then differ from the oracle's only where the oracle's gap between its
+    k-th and (k+1)-th router logits is at most twice the row's measured logit
+    discrepancy (the largest |GPU - oracle| over its experts, itself within that
+    tolerance): an expert swap needs the two logits to move past each other,
+    and each moved by at most that much.  A row that flipped in an earlier layer
+    carries other values from then on and is not checked again.  At most
+    MAX_FLIP_FRAC of the rows may flip.  Returns the flipped rows."""
     nreq, n = groute.shape[1], groute.shape[2]
     flipped = np.zeros((nreq, n), bool)
-    drift_max, drift_med, n_flip = 0.0, [], 0
+    drift_max, drift_rel_max, drift_med, n_flip = 0.0, 0.0, [], 0
+    tol = GAP_REL[mc.dtype]
     for l in range(mc.n_layers):
         for j in range(nreq):
             r = traces[j]["router_logits"][l]
             rr = traces[j]["route_idx"][l]
             gap = router_gap(r, mc.top_k)
             drift_row = np.abs(glog[l, j].astype(np.float64) - r).max(axis=1)
+            scale = np.maximum(np.abs(r).max(axis=1), 1e-30)
+            live = ~flipped[j]
+            rel = drift_row / scale
+            assert (rel[live] <= tol).all(), (f"{tag} layer {l}: router logits beyond {tol} of the row scale "
+                                              f"(max {rel[live].max():.3e}, rows {np.nonzero(live & (rel > tol))[0][:5]})")
             flip = np.array([set(groute[l, j, i]) != set(rr[i]) for i in range(n)])
-            bad = flip & (gap > 2.0 * drift_row * (1 + 1e-6)) & ~flipped[j]
+            bad = flip & (gap > 2.0 * drift_row * (1 + 1e-6)) & live
             assert not bad.any(), (f"{tag} layer {l}: routing differs where the oracle gap {gap[bad][:5]} exceeds "
                                    f"twice the measured drift {drift_row[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
-            clean = ~flipped[j] & ~flip
+            clean = live & ~flip
             if clean.any():
                 drift_max = max(drift_max, float(drift_row[clean].max()))
+                drift_rel_max = max(drift_rel_max, float(rel[clean].max()))
                 drift_med.append(float(np.median(drift_row[clean])))
-            n_flip += int(flip.sum())
+            n_flip += int((flip & live).sum())
             flipped[j] |= flip
-    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())}), each within twice its row's measured "
-        f"drift; router drift max {drift_max:.2e} median {np.median(drift_med):.2e}")
-    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: too many routing flips"
+    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())} of {flipped.size}, "
+        f"{flipped.mean():.3f}), each within twice its row's measured drift; router drift max {drift_max:.2e} "
+        f"({drift_rel_max:.2e} of the row scale) median {np.median(drift_med):.2e}")
+    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: {flipped.mean():.3f} of the rows flipped routing"
     return flipped
 
 
@@ -121,6 +147,8 @@ def _compare_step(mc, got, ref, tag, taint):
     assert (e_log[ok.ravel()] <= tol).all(), f"{tag}: logits beyond tol {tol}"
     assert (e_H[ok] <= tol).all(), f"{tag}: entropies beyond tol {tol}"
     assert not (y_bad & ok).any(), f"{tag}: sampled tokens differ beyond the margin exemption"
+    n_ex = int(((got["y"] != ref["y"]) & exempt & ok).sum())
+    assert n_ex <= MAX_EXEMPT_TOKEN_FRAC * max(int(ok.sum()), 1), f"{tag}: {n_ex} exempted token differences"
     # the logit argmax is exempt only where the top two logits are within twice
     # the row's measured logit discrepancy
     rl2 = -np.sort(-rl, axis=1)[:, :2]
@@ -228,22 +256,28 @@ def test_commit_bit_exact_on_identical_inputs(torch_cuda):
 
 
 def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=True, canvases=1,
-                oracle_reqs=None, sp_max_steps=None):
+                oracle_reqs=None, sp_max_steps=None, determinism=False):
     """GPU engine over `batch` requests against the oracle on `oracle_reqs` (default: all).
 
     Per canvas: initial canvas bit-exact, `steps` teacher-forced denoise steps,
-    then the canvas is appended to the KV cache (early if steps < budget)."""
+    then the canvas is appended to the KV cache (early if steps < budget).
+    determinism: before the canvas commit, the canvas's steps are run again
+    from the same inputs and every output compared bit for bit."""
     W = di.make_weights(mc, seed, gain_std=gain_std)
     reqs = list(range(batch)) if oracle_reqs is None else list(oracle_reqs)
     nb = len(reqs)
     max_ctx = P + mc.canvas_len * (canvases + 1)
+    progress(f"[{tag}] weights + engine ({mc.n_layers} layers, d {mc.d_model}, V {mc.vocab})")
     eng = make_engine(mc, W, batch, max_ctx)
     om = OracleModel(mc, W, nb, max_ctx)
+    if mc.n_layers >= 8:
+        om.on_layer = lambda l: progress(f"[{tag}] oracle layer {l} done") if l % 5 == 4 else None
     prompts = di.make_prompts(mc.vocab, batch, P, seed)
     seeds = di.request_seeds(seed, batch)
     oseeds = seeds[reqs]
     eng.set_seeds(seeds)
     ptr = [dict() for _ in range(nb)]
+    progress(f"[{tag}] oracle prompt encode ({P} tokens)")
     om.encode_prompt(prompts[reqs], ptr)
     eng.encode_prompt(torch.from_numpy(prompts))
     torch.cuda.synchronize()
@@ -282,7 +316,8 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
                            for j in range(nb)])
         eng.init_canvas()
         assert np.array_equal(eng.canvas[ridx].cpu().numpy(), canvas), f"{tag}: initial canvas {c}"
-        full_canvas = eng.canvas.clone()
+        if determinism and c == 0:
+            _check_determinism(torch, eng, sp, min(steps, 2), tag)
         for t in range(steps):
             if mc.self_cond and t > 0:
                 eng.self_cond_view()[ridx] = torch.from_numpy(om.s.astype(np.float32)).cuda()
@@ -337,6 +372,41 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
     eng.close()
 
 
+def _check_determinism(torch, eng, sp, steps, tag):
+    """Run `steps` denoise + commit steps twice from the same canvas and state;
+    every output and the state the steps write must agree bit for bit."""
+    c0 = eng.canvas.clone()
+    s0 = eng.self_cond_view().clone()
+    runs = []
+    for rep in range(2):
+        eng.canvas.copy_(c0)
+        eng.self_cond_view().copy_(s0)
+        eng.done.zero_()
+        rec = []
+        for t in range(steps):
+            logits = torch.empty(eng.B, eng.n, eng.cfg.vocab, dtype=torch.float32, device="cuda")
+            eng.denoise_step(t, sp, logits=logits)
+            out = [eng.H.clone(), eng.y.clone(), eng.am.clone(), eng.margin.clone(), logits,
+                   eng.self_cond_view().clone(), eng.route_view(eng.B * eng.n).clone(),
+                   eng.router_logits_view(eng.B * eng.n).clone()]
+            eng.sample_commit(t, sp)
+            out += [eng.canvas.clone(), eng.mask.clone(), eng.n_committed.clone(), eng.done.clone()]
+            rec.append(out)
+        torch.cuda.synchronize()
+        runs.append(rec)
+    names = ["H", "y", "argmax", "margin", "logits", "self-cond", "routing", "router logits", "canvas",
+             "commit mask", "n_committed", "done"]
+    for t in range(steps):
+        for nmx, a, b in zip(names, runs[0][t], runs[1][t]):
+            # raw bytes: bit for bit, NaN and -0 included
+            ab, bb = a.contiguous().view(-1).view(torch.uint8), b.contiguous().view(-1).view(torch.uint8)
+            assert torch.equal(ab, bb), f"{tag}: step {t} {nmx} differs between identical runs"
+    log(f"[{tag}] determinism: {steps} denoise + commit steps repeated bit for bit ({len(names)} outputs each)")
+    eng.canvas.copy_(c0)
+    eng.self_cond_view().copy_(s0)
+    eng.done.zero_()
+
+
 def check_routing_subset(mc, eng, traces, reqs, batch, tag):
     """check_routing for an oracle that runs a subset of the GPU's requests."""
     n = mc.canvas_len
@@ -379,7 +449,7 @@ def test_micro_grouped_experts_fused_router(torch_cuda):
     # 4 experts top-2: 512 routed entries over 4 experts take the grouped 128-row tile products
     # (ragged last tiles per expert), routed by the fused norm + router and the one-workgroup sort
     mc = micro(n_layers=2, n_experts=4, top_k=2, vocab=2048)
-    _run_parity(torch_cuda, mc, 15, 130, 1, 2, "micro-grouped-e4")
+    _run_parity(torch_cuda, mc, 15, 130, 1, 2, "micro-grouped-e4", determinism=True)
 
 
 def test_micro_grouped_experts_split_router(torch_cuda):
@@ -430,10 +500,22 @@ def test_proxy_shapes_two_layers(torch_cuda):
     _run_parity(torch_cuda, mc, 2, 256, 1, 2, "proxy-2L")
 
 
-def test_small_workload_full_size(torch_cuda):
-    # the 4-layer bf16 model at its full shape: 512-token prompt, self-conditioning, 2 steps
+def test_small_workload_full_canvas(torch_cuda):
+    # the 4-layer bf16 model at its full shape: 512-token prompt, self-conditioning,
+    # all 24 steps of the canvas (the last one takes y everywhere), then the commit;
+    # the first two steps are also repeated and compared bit for bit
     wl = di.workload("small")
-    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 2, "small")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, wl.sampler.max_steps, "small",
+                determinism=True)
+
+
+def test_proxy_workload_full_depth(torch_cuda):
+    # the 26B-scale proxy at its full shape: 30 layers, d 2048, 16/8 heads x 128, 128 experts
+    # top-8, F 768, vocabulary 262144, 2048-token prompt; one teacher-forced step (the
+    # routing of all 30 layers and the K/V of the whole prompt compared), repeated bit for bit
+    wl = di.workload("proxy")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 1, "proxy", check_kv=True,
+                sp_max_steps=wl.sampler.max_steps, determinism=True)
 
 
 def test_multicanvas_workload_sampled(torch_cuda):
@@ -448,7 +530,7 @@ def test_batched_workload_sampled(torch_cuda):
     # 32 concurrent requests with 4096-token prompts; the oracle runs requests 0 and 31
     wl = di.workload("batched")
     _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, wl.batch, 2, "batched", oracle_reqs=[0, 31],
-                sp_max_steps=wl.sampler.max_steps)
+                sp_max_steps=wl.sampler.max_steps, determinism=True)
 
 
 def _crafted_logits(rng, B, n, V, kind):

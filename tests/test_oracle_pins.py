@@ -243,6 +243,49 @@ def test_gumbel_max_frequencies():
     assert np.all(st["margin"] >= 0)
 
 
+def _gumbel_by_hand(seed, canvas, step, pos, ids):
+    """Gumbel draws of ids < 16 from hand-written counters: id v is word 0 of the
+    call with counter (v, pos, step, GUMBEL << 24 | canvas) under key (seed lo, seed hi)."""
+    key = np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint32)
+    out = []
+    for v in ids:
+        ctr = np.array([v, pos, step, (3 << 24) | canvas], np.uint32)
+        out.append(philox.gumbel(philox.philox4x32_10(ctr, key)[0:1])[0])
+    return np.array(out, np.float32)
+
+
+def test_margin_is_top2_gap_of_perturbed_tempered_scores():
+    # 4-id vocabulary: the top two of z + g (ids 0 and 1 here) differ from the
+    # top two of z alone (ids 0 and 2), so a margin over z, over unperturbed
+    # logits, or without the 1/T factor gives another value
+    seed, canvas, step, pos = (3 << 32) | 1, 0, 2, 5
+    g = _gumbel_by_hand(seed, canvas, step, pos, range(4))
+    lg = np.array([[2.0, 0.9, 1.9, 0.0]], np.float32)
+    inv_t = np.float32(1.25)
+    st = smp.head_stats(lg, inv_t, seed, canvas, step, np.array([pos]))
+    score = lg[0] * inv_t + g                                  # fp32, as the scores are defined
+    srt = np.sort(score)
+    assert st["y"][0] == int(np.argmax(score)) == 0
+    assert st["margin"][0] == np.float32(srt[-1] - srt[-2])
+    # the hand-computed draws: g = (1.00097, 2.13609, 0.45004, 0.14130) to 5 digits,
+    # z = (2.5, 1.125, 2.375, 0), scores (3.50097, 3.26109, 2.82504, 0.14130):
+    # margin = 3.50097 - 3.26109; over z alone it would be 0.125, and without
+    # the 1/T factor id 1 would win
+    assert abs(float(st["margin"][0]) - (3.50097 - 3.26109)) < 2e-5
+    assert int(np.argmax(lg[0] + g)) == 1
+
+
+def test_margin_zero_on_exact_tie():
+    # logits -g make the scores of ids 1 and 3 exactly 0 (x + (-x) is exact);
+    # the others sit far below: y is the lower tied id and the margin is 0
+    seed, canvas, step, pos = (9 << 32) | 4, 1, 0, 17
+    g = _gumbel_by_hand(seed, canvas, step, pos, range(4))
+    lg = np.array([[-g[0] - 10, -g[1], -g[2] - 10, -g[3]]], np.float32)
+    st = smp.head_stats(lg, np.float32(1.0), seed, canvas, step, np.array([pos]))
+    assert st["y"][0] == 1
+    assert st["margin"][0] == 0.0
+
+
 def test_ties_take_lowest_id():
     lg = np.array([[1.0, 3.0, 3.0, 2.0]], np.float32)
     st = smp.head_stats(lg, np.float32(1.0), 1, 0, 0, np.arange(1))
