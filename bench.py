@@ -220,7 +220,13 @@ def cpu_baseline(wl, budget_s: float):
 
 
 class Runner:
-    """One workload on the device: weights, engine, prompt encode, the step loop."""
+    """One workload on the device: weights, engine, prompt encode, the step loop.
+
+    Steps run through the library's device-driven loop (dg_run_canvas), one
+    step per call so that an event can follow each: the step index,
+    temperature and done flags stay on the device, a finished canvas is
+    committed to the KV cache by the same call, and the next call starts a new
+    canvas."""
 
     def __init__(self, wl, steps: int, warmup: int):
         import torch
@@ -229,7 +235,7 @@ class Runner:
         self.wl = wl
         mc, sp = wl.model, wl.sampler
         self.B, self.n, self.S = wl.batch, mc.canvas_len, sp.max_steps
-        total = warmup + steps + self.S          # + one accounting canvas
+        total = warmup + steps + 2 * self.S          # + the accounting canvas
         canvases = (total + self.S - 1) // self.S + 2
         max_ctx = wl.prompt_len + self.n * (canvases + 1)
         t0 = time.perf_counter()
@@ -257,27 +263,17 @@ class Runner:
         log(f"[bench] {wl.name}: prompt encode {self.encode_ms:.2f} ms")
         self.t = 0
         self.canvases_done = 0
-        self.commit_ev = None
-        self.eng.init_canvas()
 
-    def step(self):
-        eng, sp = self.eng, self.wl.sampler
-        t = self.t
-        eng.denoise_step(t, sp)
-        eng.sample_commit(t, sp)
-        t += 1
-        finished = bool((eng.done != 0).all()) if sp.stop_mode != 0 else t >= self.S
-        if finished or t >= self.S:
-            if self.commit_ev is not None:
-                self.commit_ev[0].record()
-            eng.commit_canvas_to_kv()
-            if self.commit_ev is not None:
-                self.commit_ev[1].record()
+    def step(self, graph: bool, commit: bool = True) -> bool:
+        """One step of the current canvas (a new canvas when t == 0); True if the canvas finished."""
+        sp = self.wl.sampler
+        issued, finished = self.eng.run_canvas_device(sp, first_step=self.t, n_steps=1, graph=graph,
+                                                      early_exit=sp.stop_mode != 0, commit_kv=commit)
+        self.t += issued
+        if finished:
             self.canvases_done += 1
-            eng.init_canvas()
-            eng.done.zero_()
-            t = 0
-        self.t = t
+            self.t = 0
+        return finished
 
     def close(self):
         self.eng.close()
@@ -286,65 +282,78 @@ class Runner:
         self.torch.cuda.empty_cache()
 
 
-def measure(wl, steps: int, warmup: int, stage_detail: bool):
+def measure(wl, steps: int, warmup: int, stage_detail: bool, graph: bool = True):
     """Timed run of one workload; returns the bench fields (and the Runner, still open)."""
     import torch
     r = Runner(wl, steps, warmup)
     eng, mc = r.eng, wl.model
     B, n, S = r.B, r.n, r.S
+    # warm-up: the first step without timers (one-off costs), then every stage's event
+    # pairs (the captured graph carries none, so these steps run uncaptured)
     n_first = 1 if warmup > 1 else 0
     for _ in range(n_first):
-        r.step()
+        r.step(graph=False)
     prof = {}
     if stage_detail:
         eng.profile(STAGES)
     for _ in range(warmup - n_first):
-        r.step()
+        r.step(graph=False)
     torch.cuda.synchronize()
     if stage_detail:
         prof = eng.profile_read()
+        eng.profile([])
     ctx_w = eng.ctx_len
     dominant = max(prof, key=lambda k: prof[k][0]) if prof else None
     routed = eng.route_view(B * n).cpu().numpy()
-    act_per_layer = [int(np.unique(x).size) for x in routed]
+    act_per_layer = [int(np.unique(x[x >= 0]).size) for x in routed]
     n_act = float(np.mean(act_per_layer))
+    if graph:
+        r.step(graph=True)       # capture outside the timed region
+        torch.cuda.synchronize()
     r.canvases_done = 0
-    # timed region: exactly `steps` steps; one event before each step (same stream as the
-    # library's launches) gives the per-step latencies; only the dominant stage carries
-    # the library's own event pairs
-    eng.profile([dominant] if dominant else [])
+    t_first = r.t
+    # timed region: exactly `steps` steps; one event after each step (same stream as the
+    # library's launches) gives the per-step latencies
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev[0].record()
     for i in range(steps):
-        r.step()
+        r.step(graph=graph)
         ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
     ms = float(ev[0].elapsed_time(ev[steps]))
-    dom_ms, dom_n = eng.profile_read().get(dominant, (0.0, 0)) if dominant else (0.0, 0)
-    eng.profile([])
     commits_timed = r.canvases_done
+    # the dominant stage's kernels timed with the library's event pairs over the same
+    # steps replayed uncaptured (same kernels and launch shapes; the graph holds no events)
+    dom_ms, dom_n = 0.0, 0
+    if dominant:
+        while r.t != t_first:
+            r.step(graph=graph)
+        eng.profile([dominant])
+        for _ in range(steps):
+            r.step(graph=False)
+        torch.cuda.synchronize()
+        dom_ms, dom_n = eng.profile_read().get(dominant, (0.0, 0))
+        eng.profile([])
     # accounting canvas (untimed): positions committed per step over one whole canvas,
-    # and the time of one canvas commit to the KV cache
-    r.canvases_done = 0
-    r.commit_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    while r.t != 0 or r.canvases_done == 0:
-        r.step()
-    torch.cuda.synchronize()
-    commit_ms = r.commit_ev[0].elapsed_time(r.commit_ev[1])
-    r.commit_ev = None
+    # then the time of one canvas commit to the KV cache
+    while r.t != 0:
+        r.step(graph=graph)
     ncom = []
-    for _ in range(S):
-        t_before = r.t
-        eng.denoise_step(t_before, wl.sampler)
-        eng.sample_commit(t_before, wl.sampler)
+    while True:
+        fin = r.step(graph=graph, commit=False)
         ncom.append(int(eng.n_committed.sum().item()))
-        r.t = t_before + 1
-        if r.t >= S or (wl.sampler.stop_mode != 0 and bool((eng.done != 0).all())):
+        if fin:
             break
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    eng.commit_canvas_to_kv()
+    c1.record()
+    torch.cuda.synchronize()
+    commit_ms = c0.elapsed_time(c1)
     # committed canvas tokens over the step + commit time they cost: the timed region's
     # own commits are replaced by the pro-rata share of one commit (steps / S canvases)
     canv = steps / S
@@ -355,8 +364,8 @@ def measure(wl, steps: int, warmup: int, stage_detail: bool):
            "ms_per_step_median": round(float(np.median(per)), 4),
            "ms_per_step_p90": round(float(np.percentile(per, 90)), 4),
            "steps_per_s": round(steps / (ms / 1e3), 2), "encode_ms": round(r.encode_ms, 3),
-           "wall_ms": round(wall * 1e3, 2), "n_committed_per_step": ncom,
-           "active_experts_per_layer": act_per_layer}
+           "wall_ms": round(wall * 1e3, 2), "loop": "device loop, captured graph" if graph else "device loop",
+           "n_committed_per_step": ncom, "active_experts_per_layer": act_per_layer}
     if stage_detail:
         out["stage_ms_warmup"] = {k: round(v[0] / max(warmup - n_first, 1), 4) for k, v in prof.items()}
         out["roofline"] = roofline(dominant, dom_ms, dom_n, mc, B, ctx_w, n_act,
@@ -389,6 +398,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the short runs of the other workloads reported as extra keys")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-graph", action="store_true", help="device loop without the captured step graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 256 MiB three times (the reference kernel for the HBM counters)")
     a = ap.parse_args()
@@ -413,7 +423,7 @@ def main():
 
     wl = di.workload(a.workload)
     mc, sp = wl.model, wl.sampler
-    res, runner = measure(wl, a.steps, a.warmup, stage_detail=True)
+    res, runner = measure(wl, a.steps, a.warmup, stage_detail=True, graph=not a.no_graph)
     runner.close()
     extras = {}
     if not a.no_extras:
@@ -421,7 +431,7 @@ def main():
             if name == wl.name:
                 continue
             try:
-                x, r = measure(di.workload(name), 24, 3, stage_detail=False)
+                x, r = measure(di.workload(name), 24, 3, stage_detail=False, graph=not a.no_graph)
                 r.close()
                 extras[name] = {k: x[k] for k in ("value", "ms_per_step", "ms_per_step_median", "ms_per_step_p90",
                                                   "steps_per_s", "encode_ms")}

@@ -23,15 +23,17 @@ DG_ERR_UNSUPPORTED = -4
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
 (DG_VIEW_K_CACHE, DG_VIEW_V_CACHE, DG_VIEW_SELF_COND, DG_VIEW_PREV_ARGMAX, DG_VIEW_ROUTE,
- DG_VIEW_HIDDEN, DG_VIEW_ROUTER_LOGITS, DG_VIEW_ATTN_OUT) = 0, 1, 2, 3, 4, 5, 6, 7
+ DG_VIEW_HIDDEN, DG_VIEW_ROUTER_LOGITS, DG_VIEW_ATTN_OUT, DG_VIEW_CTX_LENS, DG_VIEW_CANVAS_INDEX) = range(10)
+DG_RUN_GRAPH, DG_RUN_EARLY_EXIT, DG_RUN_COMMIT_KV = 1, 2, 4
 STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
           "lm_head", "sampler", "selfcond", "commit"]
 
 EXPORTS = [
     "dg_last_error", "dg_weight_count", "dg_model_create", "dg_model_destroy", "dg_state_bytes",
     "dg_state_init", "dg_state_destroy", "dg_state_ctx_len", "dg_state_canvas_index", "dg_state_view",
-    "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_commit",
-    "dg_commit_canvas_to_kv", "dg_profile_enable", "dg_profile_read",
+    "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
+    "dg_sample_commit",
+    "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_profile_enable", "dg_profile_read",
 ]
 
 
@@ -87,14 +89,19 @@ def load() -> ctypes.CDLL:
     lib.dg_denoise_step.argtypes = [vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp,
                                     vp, vp]
     lib.dg_sample_logits.argtypes = [vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp, vp]
+    lib.dg_sample_logits_static.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(DgSamplerParams), vp, vp,
+                                            vp, vp, vp, vp]
     lib.dg_sample_commit.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp,
                                      vp, vp]
-    lib.dg_commit_canvas_to_kv.argtypes = [vp, vp, vp]
+    lib.dg_commit_canvas_to_kv.argtypes = [vp, vp, vp, vp]
+    lib.dg_run_canvas.argtypes = [vp, vp, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i32, i32, ctypes.c_uint32, ctypes.POINTER(i32), vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_uint32]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("dg_model_create", "dg_state_bytes", "dg_state_init", "dg_state_view", "dg_init_canvas",
-                 "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_commit",
-                 "dg_commit_canvas_to_kv", "dg_profile_enable", "dg_profile_read"):
+                 "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
+                 "dg_sample_commit",
+                 "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_profile_enable", "dg_profile_read"):
         getattr(lib, name).restype = i32
     _check_single_hip_runtime()
     _lib = lib

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "dg_kernels.h"
@@ -67,10 +68,35 @@ struct dg_model {
   void* pack_buf = nullptr;  // owned: fragment-packed expert weights of every layer
 };
 
+// One captured denoise + commit step of the device-driven canvas loop and what
+// it was captured for (buffers, sampler parameters, seeds, attention plan).
+struct StepGraph {
+  hipGraphExec_t exec = nullptr;
+  std::vector<const void*> bufs;
+  dg_sampler_params params{};
+  std::vector<uint64_t> seeds;
+  int attn_splits = -1, attn_keys_class = -1;
+};
+
 struct dg_state {
   const dg_model* m;
   int B, max_ctx, n, R;  // R = B * n rows per pass
+  // per-request context lengths and canvas indices live in the state buffer
+  // (ctx_dev, cidx_dev); the host keeps their largest values (capacity
+  // checks, launch plans) and whether all requests still agree
   int ctx = 0, canvas_index = 0;
+  bool uniform = true;
+  int32_t* ctx_dev; int32_t* cidx_dev; float* inv_tab;
+  int32_t* step_dev;     // [0] step of the canvas, [1] every request done, [2] loop steps completed
+  volatile int32_t* progress = nullptr;      // mapped host memory: (steps completed, all done)
+  int32_t* progress_dev = nullptr;           // its device address
+  int64_t steps_launched = 0;                // loop steps enqueued since init (progress[0] counts them done)
+  int loop_step = 0;                         // next step of the loop's current canvas
+  hipStream_t cap_stream = nullptr;          // graphs are captured here (never on the null stream), launched on the caller's
+  float* inv_tab_host = nullptr;             // pinned: 1 / T per step of the loop's budget
+  dg_sampler_params tab_params{};
+  bool tab_valid = false;
+  StepGraph graph;
   int chunks, attn_splits_max, cap_tiles;   // chunks: 128-id vocabulary chunks of the head statistics
   int ctx_pad;            // max_ctx rounded up to the 64-key attention tile: K/V row stride
   size_t kv_layer_elems;  // B * Hkv * ctx_pad * hd
@@ -243,9 +269,11 @@ struct Layout {
   }
 };
 
+constexpr int kMaxLoopSteps = 4096;   // longest step budget of the device-driven loop
+
 struct Offsets {
   size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos, rcnt,
-      tiles, n_tiles, act, y, hp, chunk_scale, ptilde, sc_part, tok, total;
+      tiles, n_tiles, act, y, hp, chunk_scale, ptilde, sc_part, tok, ctxv, cidx, stepv, inv_tab, total;
   size_t part_floats;
   int chunks, splits, cap_tiles, sc_splits, sc_kchunk;
 };
@@ -311,6 +339,10 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.ptilde = c.self_cond ? L.take((size_t)R * V * es) : 0;
   o.sc_part = c.self_cond ? L.take((size_t)o.sc_splits * R * d * 4) : 0;
   o.tok = L.take((size_t)R * 4);
+  o.ctxv = L.take((size_t)B * 4);
+  o.cidx = L.take((size_t)B * 4);
+  o.stepv = L.take(4 * 4);                          // step counter, all-done flag, steps completed
+  o.inv_tab = L.take((size_t)kMaxLoopSteps * 4);
   o.total = L.off;
   return o;
 }
@@ -357,15 +389,42 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->ptilde = m->cfg.self_cond ? b + o.ptilde : nullptr;
   s->sc_part = m->cfg.self_cond ? reinterpret_cast<float*>(b + o.sc_part) : nullptr;
   s->tok = reinterpret_cast<int32_t*>(b + o.tok);
+  s->ctx_dev = reinterpret_cast<int32_t*>(b + o.ctxv);
+  s->cidx_dev = reinterpret_cast<int32_t*>(b + o.cidx);
+  s->step_dev = reinterpret_cast<int32_t*>(b + o.stepv);
+  s->inv_tab = reinterpret_cast<float*>(b + o.inv_tab);
   s->total_bytes = o.total;
-  hipError_t e = rope_table(s->rope, max_ctx, m->cfg.head_dim, m->cfg.rope_theta, 0);
+  // progress record of the device-driven loop in mapped host memory
+  void* hp = nullptr;
+  void* tabp = nullptr;
+  hipError_t e = hipHostMalloc(&tabp, (size_t)kMaxLoopSteps * 4, hipHostMallocDefault);
+  if (e == hipSuccess) s->inv_tab_host = static_cast<float*>(tabp);
+  if (e == hipSuccess) e = hipHostMalloc(&hp, 16, hipHostMallocMapped);
+  if (e == hipSuccess) {
+    s->progress = static_cast<volatile int32_t*>(hp);
+    s->progress[0] = 0; s->progress[1] = 0;
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, hp, 0);
+    s->progress_dev = static_cast<int32_t*>(dp);
+  }
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&s->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = rope_table(s->rope, max_ctx, m->cfg.head_dim, m->cfg.rope_theta, 0);
   if (e == hipSuccess) e = hipMemsetAsync(s->s, 0, (size_t)s->R * m->cfg.d_model * 4, 0);
   if (e == hipSuccess) e = hipMemsetAsync(s->prev_am, 0, (size_t)s->R * 4, 0);
+  if (e == hipSuccess) e = hipMemsetAsync(s->ctx_dev, 0, (size_t)batch * 4, 0);
+  if (e == hipSuccess) e = hipMemsetAsync(s->cidx_dev, 0, (size_t)batch * 4, 0);
+  if (e == hipSuccess) e = hipMemsetAsync(s->step_dev, 0, 16, 0);
   // attention tiles read whole 64-key rows of V^T past the context: keep them finite
   if (e == hipSuccess) e = hipMemsetAsync(s->kc, 0, s->kv_layer_elems * m->cfg.n_layers * m->esz, 0);
   if (e == hipSuccess) e = hipMemsetAsync(s->vc, 0, s->kv_layer_elems * m->cfg.n_layers * m->esz, 0);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) { delete s; return fail(DG_ERR_HIP, "state init: %s", hipGetErrorString(e)); }
+  if (e != hipSuccess) {
+    if (s->progress) hipHostFree(const_cast<int32_t*>(s->progress));
+    if (s->inv_tab_host) hipHostFree(s->inv_tab_host);
+    if (s->cap_stream) hipStreamDestroy(s->cap_stream);
+    delete s;
+    return fail(DG_ERR_HIP, "state init: %s", hipGetErrorString(e));
+  }
   *out = s;
   return DG_OK;
 }
@@ -373,6 +432,11 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
 extern "C" void dg_state_destroy(dg_state* s) {
   if (!s) return;
   for (hipEvent_t e : s->prof_ev) hipEventDestroy(e);
+  if (s->graph.exec) hipGraphExecDestroy(s->graph.exec);
+  if (s->progress || s->inv_tab_host) hipDeviceSynchronize();   // queued loop steps use both
+  if (s->progress) hipHostFree(const_cast<int32_t*>(s->progress));
+  if (s->inv_tab_host) hipHostFree(s->inv_tab_host);
+  if (s->cap_stream) hipStreamDestroy(s->cap_stream);
   delete s;
 }
 
@@ -416,6 +480,8 @@ extern "C" dg_status dg_state_view(dg_state* s, int32_t which, void** ptr, size_
     case DG_VIEW_HIDDEN: *ptr = s->h; *bytes = (size_t)s->R * c.d_model * 4; break;
     case DG_VIEW_ROUTER_LOGITS: *ptr = s->rlog; *bytes = (size_t)c.n_layers * s->R * c.n_experts * 4; break;
     case DG_VIEW_ATTN_OUT: *ptr = s->attn; *bytes = (size_t)s->R * c.n_q_heads * c.head_dim * s->m->esz; break;
+    case DG_VIEW_CTX_LENS: *ptr = s->ctx_dev; *bytes = (size_t)s->B * 4; break;
+    case DG_VIEW_CANVAS_INDEX: *ptr = s->cidx_dev; *bytes = (size_t)s->B * 4; break;
     default: return fail(DG_ERR_ARG, "unknown view %d", which);
   }
   return DG_OK;
@@ -443,11 +509,19 @@ SplitPlan plan(const dg_state* st, int M, int N, int K) {
   return p;
 }
 
-// Layer stack over B x nq new rows at positions ctx..ctx+nq-1 whose tokens are
-// `tok`, writing their K/V to the cache.  Leaves the residual stream in st->h
-// and rnd(final RMSNorm(h)) in st->xn.
+int attn_splits_for(const dg_state* st, int nq, int keys) {
+  const dg_config& c = st->m->cfg;
+  int splits = attention_splits(st->B, nq, c.n_q_heads, c.n_kv_heads, c.head_dim, keys, (int)st->m->esz);
+  return splits > st->attn_splits_max ? st->attn_splits_max : splits;
+}
+
+// Layer stack over B x nq new rows whose tokens are `tok`: request b's rows
+// sit at positions ctx[b] + pos_off + i and write their K/V to the cache there.
+// Requests the gate leaves out compute and write nothing.  Leaves the residual
+// stream in st->h and rnd(final RMSNorm(h)) in st->xn.
 template <typename T>
-dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool self_cond, hipStream_t s) {
+dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool self_cond, Gate gate, int pos_off,
+                    hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, E = c.n_experts;
@@ -457,20 +531,20 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   if ((size_t)M * std::max(nqkv, std::max(d, E)) > st->part_floats ||
       (size_t)router_ksplits(M, d, E) * M * E > st->part_floats)
     return fail(DG_ERR_CAPACITY, "partial buffer too small for %d rows", M);
+  const PosArg pa{st->ctx_dev, pos_off};
   {
     StageTimer tm(st, DG_STAGE_EMBED, s);
     int S = 0;
     if (self_cond) {
       const SplitPlan sp = plan(st, M, d, d);
-      DG_HIP(gemm_partials_f32a<T>(st->s, d, static_cast<const T*>(m->w_sc), d, st->part, M, d, d, sp, s));
+      DG_HIP(gemm_partials_f32a<T>(st->s, d, static_cast<const T*>(m->w_sc), d, st->part, M, d, d, sp, gate, nq, s));
       S = sp.splits;
     }
     DG_HIP(embed_norm<T>(static_cast<const T*>(m->emb), tok, st->part, S, M, d, c.vocab, m->layers[0].attn_norm,
-                         c.rms_eps, st->h, xn, s));
+                         c.rms_eps, st->h, xn, gate, nq, s));
   }
-  const int keys = st->ctx + nq;
-  int splits = attention_splits(st->B, nq, Hq, Hkv, hd, keys, (int)st->m->esz);
-  if (splits > st->attn_splits_max) splits = st->attn_splits_max;
+  const int keys = st->ctx + pos_off + nq;    // the largest key count over the requests
+  const int splits = attn_splits_for(st, nq, keys);
   const int cap = expert_tile_capacity(M, k, E);
   const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd);
   const bool stream_ok = m->pack_buf != nullptr;
@@ -483,25 +557,26 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       if (qkv_rope_ok(d, hd, (int)m->esz)) {
         // one head per tile, RoPE and the cache scatter in the product's epilogue
         DG_HIP(gemm_qkv_rope<T>(xn, static_cast<const T*>(L.wqkv), M, d, hd, st->rope, static_cast<T*>(st->q), kc, vc,
-                                nq, Hq, Hkv, st->ctx_pad, st->ctx, s));
+                                nq, Hq, Hkv, st->ctx_pad, pa, gate, s));
       } else {
-        DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, s));
+        DG_HIP(gemm_partials<T>(xn, d, static_cast<const T*>(L.wqkv), d, st->part, M, nqkv, d, p_qkv, gate, nq, s));
         DG_HIP(rope_scatter<T>(st->part, p_qkv.splits, st->rope, static_cast<T*>(st->q), kc, vc, st->B, nq, Hq, Hkv,
-                               hd, st->ctx_pad, st->ctx, s));
+                               hd, st->ctx_pad, pa, gate, s));
       }
     }
     {
       StageTimer tm(st, DG_STAGE_ATTN, s);
       AttnArgs a;
       a.q = st->q; a.kc = kc; a.vc = vc; a.out = st->attn; a.part_o = st->attn_po; a.part_ml = st->attn_pml;
-      a.B = st->B; a.nq = nq; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.kv_stride = st->ctx_pad; a.ctx = st->ctx;
+      a.B = st->B; a.nq = nq; a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.kv_stride = st->ctx_pad;
+      a.pos = pa; a.keys_max = keys; a.gate = gate;
       a.causal = causal ? 1 : 0; a.splits = splits; a.scale = (float)(1.0 / std::sqrt((double)hd));
       DG_HIP(attention<T>(a, s));
     }
     {
       StageTimer tm(st, DG_STAGE_OPROJ, s);
       DG_HIP(gemm_partials<T>(static_cast<const T*>(st->attn), Hq * hd, static_cast<const T*>(L.wo), Hq * hd,
-                              st->part, M, d, Hq * hd, p_o, s));
+                              st->part, M, d, Hq * hd, p_o, gate, nq, s));
     }
     float* rlog = st->rlog + (size_t)l * st->R * E;
     int* ridx = st->ridx + (size_t)l * st->R * k;
@@ -515,7 +590,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       {
         StageTimer tm(st, DG_STAGE_NORM, s);
         DG_HIP(add_norm_router<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn,
-                                  static_cast<const T*>(L.w_router), E, k, rlog, ridx, st->rw, s));
+                                  static_cast<const T*>(L.w_router), E, k, rlog, ridx, st->rw, gate, nq, s));
       }
       {
         StageTimer tm(st, DG_STAGE_ROUTER, s);
@@ -524,14 +599,14 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     } else {
       {
         StageTimer tm(st, DG_STAGE_NORM, s);
-        DG_HIP(add_norm<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn, s));
+        DG_HIP(add_norm<T>(st->part, p_o.splits, M, d, L.ffn_norm, c.rms_eps, st->h, xn, gate, nq, s));
       }
       {
         StageTimer tm(st, DG_STAGE_ROUTER, s);
         // the split-K partial buffer is free here (the output projection's
         // partials were consumed by add_norm); it holds the router's partial logits
         DG_HIP(router<T>(xn, static_cast<const T*>(L.w_router), M, d, E, k, rlog, ridx, st->rw, st->perm, st->pos,
-                         st->tiles, st->n_tiles, tile_rows, st->rcnt, st->part, s));
+                         st->tiles, st->n_tiles, tile_rows, st->rcnt, st->part, gate, nq, s));
       }
     }
     {
@@ -555,7 +630,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     {
       StageTimer tm(st, DG_STAGE_COMBINE, s);
       const float* g_next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
-      DG_HIP(combine_norm<T>(st->y, st->pos, st->rw, k, M, d, g_next, c.rms_eps, st->h, xn, s));
+      DG_HIP(combine_norm<T>(st->y, st->pos, st->rw, k, M, d, g_next, c.rms_eps, st->h, xn, gate, nq, s));
     }
   }
   return DG_OK;
@@ -564,15 +639,17 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
 template <typename T>
 dg_status run_encode(dg_state* st, const int32_t* ids, int P, hipStream_t s) {
   const int n = st->n;
+  const Gate all{nullptr, 0};
   for (int p0 = 0; p0 < P; p0 += n) {
     const int len = P - p0 < n ? P - p0 : n;
     // gather the chunk's tokens of every request into [B, len]
     DG_HIP(hipMemcpy2DAsync(st->tok, (size_t)len * 4, ids + p0, (size_t)P * 4, (size_t)len * 4, st->B,
                             hipMemcpyDeviceToDevice, s));
-    dg_status r = run_stack<T>(st, st->tok, len, true, false, s);
+    dg_status r = run_stack<T>(st, st->tok, len, true, false, all, p0, s);
     if (r) return r;
-    st->ctx += len;
   }
+  DG_HIP(advance_context(st->ctx_dev, st->cidx_dev, st->B, P, 0, all, s));
+  st->ctx += P;
   return DG_OK;
 }
 
@@ -582,66 +659,75 @@ float step_temperature(const dg_sampler_params* p, int step) {
   return (float)(t0 + (t1 - t0) * (double)step / (double)(p->max_steps - 1));
 }
 
+float step_inv_temperature(const dg_sampler_params* p, int step) {
+  return (float)(1.0 / (double)step_temperature(p, step));
+}
+
+// Step and temperature given by value (the explicit step calls).
+StepInfo explicit_step(const dg_state* st, const dg_sampler_params* p, int step) {
+  return StepInfo{step, step_inv_temperature(p, step), nullptr, nullptr, st->cidx_dev};
+}
+// Step and temperature read from the state (the device-driven loop).
+StepInfo loop_step(const dg_state* st) {
+  return StepInfo{0, 0.f, st->step_dev, st->inv_tab, st->cidx_dev};
+}
+
 // Sampler stage after the head statistics: the per-row merge (entropy, sample,
 // arg-max, margin) and, for self-conditioning models, the next step's
 // self-conditioning vector softmax(z) @ E.
 template <typename T>
-dg_status run_merge(dg_state* st, const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin,
-                    hipStream_t s) {
+dg_status run_merge(dg_state* st, Gate gate, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, V = c.vocab, R = st->R;
   {
     StageTimer tm(st, DG_STAGE_SAMPLER, s);
-    DG_HIP(sampler_merge(st->hp, R, st->chunks, st->n, active, H, y, am, margin,
+    DG_HIP(sampler_merge(st->hp, R, st->chunks, st->n, gate, H, y, am, margin,
                          c.self_cond ? st->chunk_scale : nullptr, s));
   }
   if (c.self_cond) {
     StageTimer tm(st, DG_STAGE_SELFCOND, s);
     DG_HIP(gemm_selfcond<T>(static_cast<const T*>(st->ptilde), st->chunk_scale, st->chunks,
-                            static_cast<const T*>(m->emb_t), st->sc_part, R, d, V, st->sc_splits, st->sc_kchunk, s));
-    DG_HIP(selfcond_reduce(st->sc_part, R, d, st->sc_splits, st->s, s));
+                            static_cast<const T*>(m->emb_t), st->sc_part, R, d, V, st->sc_splits, st->sc_kchunk,
+                            gate, st->n, s));
+    DG_HIP(selfcond_reduce(st->sc_part, R, d, st->sc_splits, st->s, gate, st->n, s));
   }
   return DG_OK;
 }
 
-float step_inv_temperature(const dg_sampler_params* p, int step) {
-  return (float)(1.0 / (double)step_temperature(p, step));
-}
-
 // Sampler stage on supplied logits [R][V].
 template <typename T>
-dg_status run_head(dg_state* st, const float* logits, int step, const dg_sampler_params* p, const uint64_t* seeds,
-                   const uint8_t* active, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
+dg_status run_head(dg_state* st, const float* logits, const StepInfo& si, const uint64_t* seeds, Gate gate,
+                   float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
   const dg_config& c = st->m->cfg;
   {
     StageTimer tm(st, DG_STAGE_SAMPLER, s);
-    DG_HIP(head_from_logits<T>(logits, st->R, c.vocab, step_inv_temperature(p, step), make_seeds(seeds, st->B),
-                               st->n, st->canvas_index, step, st->hp,
-                               c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, s));
+    DG_HIP(head_from_logits<T>(logits, st->R, c.vocab, si, make_seeds(seeds, st->B), st->n, st->hp,
+                               c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, gate, s));
   }
-  return run_merge<T>(st, active, H, y, am, margin, s);
+  return run_merge<T>(st, gate, H, y, am, margin, s);
 }
 
+// One denoising round.  sc_mode: 0 no self-conditioning term, 1 the term
+// (s of the previous step), as the explicit calls decide from the step; the
+// loop always adds it, with s cleared at the start of each canvas.
 template <typename T>
-dg_status run_denoise(dg_state* st, const int32_t* canvas, int step, const dg_sampler_params* p,
-                      const uint64_t* seeds, const uint8_t* active, float* H, int32_t* y, int32_t* am,
-                      float* margin, float* logits_out, hipStream_t s) {
+dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, bool sc, const uint64_t* seeds,
+                      Gate gate, float* H, int32_t* y, int32_t* am, float* margin, float* logits_out, hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, V = c.vocab, R = st->R;
-  const bool sc = c.self_cond && step > 0;
-  dg_status r = run_stack<T>(st, canvas, st->n, false, sc, s);
+  dg_status r = run_stack<T>(st, canvas, st->n, false, sc, gate, 0, s);
   if (r) return r;
   T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
   {
     // the LM head with the head statistics in its epilogue (logits stored only when asked for)
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
-    const HeadArgs<T> h{step_inv_temperature(p, step), make_seeds(seeds, st->B), st->n, st->canvas_index, step,
-                        st->hp, c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, logits_out};
+    const HeadArgs<T> h{si, make_seeds(seeds, st->B), st->n, st->hp,
+                        c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, logits_out, gate};
     DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
   }
-  return run_merge<T>(st, active, H, y, am, margin, s);
+  return run_merge<T>(st, gate, H, y, am, margin, s);
 }
 
 dg_status check_params(const dg_sampler_params* p) {
@@ -653,14 +739,19 @@ dg_status check_params(const dg_sampler_params* p) {
   return DG_OK;
 }
 
+dg_status check_capacity(const dg_state* st) {
+  if (st->ctx + st->n > st->max_ctx)
+    return fail(DG_ERR_CAPACITY, "context %d + canvas %d exceeds max_ctx %d", st->ctx, st->n, st->max_ctx);
+  return DG_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ the calls
 extern "C" dg_status dg_init_canvas(dg_state* st, int32_t* d_canvas, const uint64_t* h_seeds, dg_stream stream) {
   if (!st || !d_canvas || !h_seeds) return fail(DG_ERR_ARG, "null argument");
   const SeedArg sa = make_seeds(h_seeds, st->B);
-  DG_HIP(init_canvas(d_canvas, sa, st->B, st->n, st->m->cfg.vocab, st->canvas_index,
-                     reinterpret_cast<hipStream_t>(stream)));
+  DG_HIP(init_canvas(d_canvas, sa, st->B, st->n, st->m->cfg.vocab, st->cidx_dev, reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 
@@ -683,13 +774,14 @@ extern "C" dg_status dg_denoise_step(dg_state* st, const int32_t* d_canvas, int3
   dg_status r = check_params(params);
   if (r) return r;
   if (step < 0 || step >= params->max_steps) return fail(DG_ERR_ARG, "step %d outside 0..max_steps-1", step);
-  if (st->ctx + st->n > st->max_ctx)
-    return fail(DG_ERR_CAPACITY, "context %d + canvas %d exceeds max_ctx %d", st->ctx, st->n, st->max_ctx);
+  if ((r = check_capacity(st))) return r;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const StepInfo si = explicit_step(st, params, step);
+  const bool sc = st->m->cfg.self_cond && step > 0;
+  const Gate g{d_active, 0};
   return st->m->cfg.dtype == DG_DTYPE_BF16
-             ? run_denoise<bf16>(st, d_canvas, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, d_logits, s)
-             : run_denoise<float>(st, d_canvas, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, d_logits,
-                                  s);
+             ? run_denoise<bf16>(st, d_canvas, si, sc, h_seeds, g, d_H, d_y, d_argmax, d_margin, d_logits, s)
+             : run_denoise<float>(st, d_canvas, si, sc, h_seeds, g, d_H, d_y, d_argmax, d_margin, d_logits, s);
 }
 
 extern "C" dg_status dg_sample_logits(dg_state* st, const float* d_logits, int32_t step,
@@ -701,9 +793,43 @@ extern "C" dg_status dg_sample_logits(dg_state* st, const float* d_logits, int32
   if (r) return r;
   if (step < 0 || step >= params->max_steps) return fail(DG_ERR_ARG, "step %d outside 0..max_steps-1", step);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const StepInfo si = explicit_step(st, params, step);
+  const Gate g{d_active, 0};
   return st->m->cfg.dtype == DG_DTYPE_BF16
-             ? run_head<bf16>(st, d_logits, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, s)
-             : run_head<float>(st, d_logits, step, params, h_seeds, d_active, d_H, d_y, d_argmax, d_margin, s);
+             ? run_head<bf16>(st, d_logits, si, h_seeds, g, d_H, d_y, d_argmax, d_margin, s)
+             : run_head<float>(st, d_logits, si, h_seeds, g, d_H, d_y, d_argmax, d_margin, s);
+}
+
+extern "C" dg_status dg_sample_logits_static(const float* d_logits, int32_t rows, int32_t vocab, int32_t canvas_len,
+                                             int32_t canvas_index, int32_t step, const dg_sampler_params* params,
+                                             const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax,
+                                             float* d_margin, dg_stream stream) {
+  if (!d_logits || !h_seeds || !d_H || !d_y || !d_argmax || !d_margin) return fail(DG_ERR_ARG, "null argument");
+  dg_status r = check_params(params);
+  if (r) return r;
+  if (step < 0 || step >= params->max_steps) return fail(DG_ERR_ARG, "step %d outside 0..max_steps-1", step);
+  if (canvas_len < 1 || canvas_len > 256) return fail(DG_ERR_UNSUPPORTED, "canvas_len must be in 1..256");
+  if (rows < 1 || rows % canvas_len) return fail(DG_ERR_ARG, "rows must be a positive multiple of canvas_len");
+  if (rows / canvas_len > kMaxBatch) return fail(DG_ERR_UNSUPPORTED, "at most %d requests", kMaxBatch);
+  if (vocab < 64 || vocab % 64 || vocab > 262144)
+    return fail(DG_ERR_UNSUPPORTED, "vocab must be a multiple of 64 in 64..262144");
+  if (canvas_index < 0) return fail(DG_ERR_ARG, "canvas_index must be >= 0");
+  const size_t need = kStaticHeadOffset + (size_t)rows * head_chunks(vocab) * sizeof(HeadPart);
+  if (need > kStaticScratchBytes)
+    return fail(DG_ERR_CAPACITY, "rows x 128-id chunks need %zu scratch bytes, the fixed scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* base = nullptr;
+  DG_HIP(static_scratch(&base));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int B = rows / canvas_len;
+  int32_t* cidx = static_cast<int32_t*>(base);
+  HeadPart* hp = reinterpret_cast<HeadPart*>(static_cast<char*>(base) + kStaticHeadOffset);
+  DG_HIP(fill_u32(cidx, (uint32_t)canvas_index, (size_t)B, s));     // every request: this canvas index
+  const StepInfo si{step, step_inv_temperature(params, step), nullptr, nullptr, cidx};
+  const Gate all{nullptr, 0};
+  DG_HIP(head_from_logits<float>(d_logits, rows, vocab, si, make_seeds(h_seeds, B), canvas_len, hp, nullptr, all, s));
+  DG_HIP(sampler_merge(hp, rows, head_chunks(vocab), canvas_len, all, d_H, d_y, d_argmax, d_margin, nullptr, s));
+  return DG_OK;
 }
 
 extern "C" dg_status dg_sample_commit(dg_state* st, const float* d_H, const int32_t* d_y, const int32_t* d_argmax,
@@ -718,20 +844,167 @@ extern "C" dg_status dg_sample_commit(dg_state* st, const float* d_H, const int3
   const SeedArg sa = make_seeds(h_seeds, st->B);
   StageTimer tm(st, DG_STAGE_COMMIT, reinterpret_cast<hipStream_t>(stream));
   DG_HIP(commit_kernel(d_H, d_y, d_argmax, d_canvas, st->prev_am, d_commit_mask, d_n_committed, d_done, sa, st->B,
-                       st->n, st->m->cfg.vocab, step, params->max_steps, params->entropy_bound, params->stop_mode,
-                       params->stop_tau, st->canvas_index, reinterpret_cast<hipStream_t>(stream)));
+                       st->n, st->m->cfg.vocab, explicit_step(st, params, step), params->max_steps,
+                       params->entropy_bound, params->stop_mode, params->stop_tau,
+                       reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 
-extern "C" dg_status dg_commit_canvas_to_kv(dg_state* st, const int32_t* d_canvas, dg_stream stream) {
+extern "C" dg_status dg_commit_canvas_to_kv(dg_state* st, const int32_t* d_canvas, const uint8_t* d_which,
+                                            dg_stream stream) {
   if (!st || !d_canvas) return fail(DG_ERR_ARG, "null argument");
-  if (st->ctx + st->n > st->max_ctx)
-    return fail(DG_ERR_CAPACITY, "context %d + canvas %d exceeds max_ctx %d", st->ctx, st->n, st->max_ctx);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  dg_status r = st->m->cfg.dtype == DG_DTYPE_BF16 ? run_stack<bf16>(st, d_canvas, st->n, true, false, s)
-                                                  : run_stack<float>(st, d_canvas, st->n, true, false, s);
+  dg_status r = check_capacity(st);
   if (r) return r;
-  st->ctx += st->n;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Gate g{d_which, 0};
+  r = st->m->cfg.dtype == DG_DTYPE_BF16 ? run_stack<bf16>(st, d_canvas, st->n, true, false, g, 0, s)
+                                        : run_stack<float>(st, d_canvas, st->n, true, false, g, 0, s);
+  if (r) return r;
+  DG_HIP(advance_context(st->ctx_dev, st->cidx_dev, st->B, st->n, 1, g, s));
+  st->ctx += st->n;            // largest context over the requests (those left out stay behind)
   st->canvas_index += 1;
+  if (d_which != nullptr) st->uniform = false;
+  return DG_OK;
+}
+
+// ------------------------------------------------------------------ the device-driven canvas loop
+namespace {
+
+// Enqueue one loop step: the denoise round of the requests not yet done, the
+// commit, and the step end (step counter, all-done flag, progress record).
+template <typename T>
+dg_status enqueue_loop_step(dg_state* st, int32_t* canvas, const dg_sampler_params* p, const uint64_t* seeds,
+                            float* H, int32_t* y, int32_t* am, float* margin, uint8_t* mask, int32_t* ncom,
+                            uint8_t* done, hipStream_t s) {
+  const Gate g{done, 1};
+  const StepInfo si = loop_step(st);
+  dg_status r = run_denoise<T>(st, canvas, si, st->m->cfg.self_cond != 0, seeds, g, H, y, am, margin, nullptr, s);
+  if (r) return r;
+  {
+    StageTimer tm(st, DG_STAGE_COMMIT, s);
+    DG_HIP(commit_kernel(H, y, am, canvas, st->prev_am, mask, ncom, done, make_seeds(seeds, st->B), st->B, st->n,
+                         st->m->cfg.vocab, si, p->max_steps, p->entropy_bound, p->stop_mode, p->stop_tau, s));
+  }
+  DG_HIP(step_end(done, st->B, st->step_dev, st->progress_dev, s));
+  return DG_OK;
+}
+
+bool same_params(const dg_sampler_params& a, const dg_sampler_params& b) {
+  return a.t_start == b.t_start && a.t_end == b.t_end && a.entropy_bound == b.entropy_bound &&
+         a.stop_tau == b.stop_tau && a.max_steps == b.max_steps && a.stop_mode == b.stop_mode;
+}
+
+}  // namespace
+
+extern "C" dg_status dg_run_canvas(dg_state* st, int32_t* d_canvas, const dg_sampler_params* params,
+                                   const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax,
+                                   float* d_margin, uint8_t* d_commit_mask, int32_t* d_n_committed, uint8_t* d_done,
+                                   int32_t first_step, int32_t n_steps, uint32_t flags, int32_t* h_result,
+                                   dg_stream stream) {
+  if (!st || !d_canvas || !h_seeds || !d_H || !d_y || !d_argmax || !d_margin || !d_commit_mask || !d_n_committed ||
+      !d_done)
+    return fail(DG_ERR_ARG, "null argument");
+  dg_status r = check_params(params);
+  if (r) return r;
+  if (params->max_steps > kMaxLoopSteps) return fail(DG_ERR_UNSUPPORTED, "max_steps above %d", kMaxLoopSteps);
+  if (first_step < 0 || first_step >= params->max_steps)
+    return fail(DG_ERR_ARG, "first_step %d outside 0..max_steps-1", first_step);
+  if (n_steps < 1 || n_steps > params->max_steps - first_step)
+    return fail(DG_ERR_ARG, "n_steps %d outside 1..%d", n_steps, params->max_steps - first_step);
+  if (first_step > 0 && first_step != st->loop_step)
+    return fail(DG_ERR_ARG, "first_step %d does not continue the canvas (next step %d)", first_step, st->loop_step);
+  if (flags & ~(uint32_t)(DG_RUN_GRAPH | DG_RUN_EARLY_EXIT | DG_RUN_COMMIT_KV))
+    return fail(DG_ERR_ARG, "unknown flags 0x%x", flags);
+  if ((r = check_capacity(st))) return r;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = st->m->cfg.dtype == DG_DTYPE_BF16;
+  const int S = params->max_steps;
+  // the temperature table of this budget: copied from pinned host memory,
+  // rewritten only when the parameters change (after the copies still queued
+  // from it have run)
+  if (!st->tab_valid || !same_params(st->tab_params, *params)) {
+    if (st->tab_valid) DG_HIP(hipStreamSynchronize(s));
+    for (int t = 0; t < S; ++t) st->inv_tab_host[t] = step_inv_temperature(params, t);
+    st->tab_params = *params;
+    st->tab_valid = true;
+  }
+  if (first_step == 0) {
+    DG_HIP(hipMemcpyAsync(st->inv_tab, st->inv_tab_host, (size_t)S * 4, hipMemcpyHostToDevice, s));
+    // canvas set-up: tokens, cleared done flags, self-conditioning vector and step counter
+    DG_HIP(init_canvas(d_canvas, make_seeds(h_seeds, st->B), st->B, st->n, st->m->cfg.vocab, st->cidx_dev, s));
+    DG_HIP(fill_u8(d_done, 0, (size_t)st->B, s));
+    if (st->m->cfg.self_cond) DG_HIP(fill_u32(st->s, 0u, (size_t)st->R * st->m->cfg.d_model, s));
+    DG_HIP(fill_u32(st->step_dev, 0u, 2, s));      // step counter and all-done flag (not the completed count)
+    st->loop_step = 0;
+  }
+
+  const int keys = st->ctx + st->n;
+  const int splits = attn_splits_for(st, st->n, keys);
+  const int keys_class = attention_launch_class(st->B, st->n, st->m->cfg.n_q_heads, st->m->cfg.n_kv_heads,
+                                                st->m->cfg.head_dim, keys);
+  const uint32_t saved_prof = st->prof_mask;
+  if (flags & DG_RUN_GRAPH) {
+    std::vector<const void*> bufs{d_canvas, d_H, d_y, d_argmax, d_margin, d_commit_mask, d_n_committed, d_done};
+    std::vector<uint64_t> seeds(h_seeds, h_seeds + st->B);
+    StepGraph& G = st->graph;
+    const bool reuse = G.exec && G.bufs == bufs && same_params(G.params, *params) && G.seeds == seeds &&
+                       G.attn_splits == splits && G.attn_keys_class == keys_class;
+    if (!reuse) {
+      if (G.exec) { hipGraphExecDestroy(G.exec); G.exec = nullptr; }
+      st->prof_mask = 0;      // no event records inside the graph
+      hipGraph_t graph = nullptr;
+      hipStream_t cs = st->cap_stream;
+      DG_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+      r = bf ? enqueue_loop_step<bf16>(st, d_canvas, params, h_seeds, d_H, d_y, d_argmax, d_margin, d_commit_mask,
+                                       d_n_committed, d_done, cs)
+             : enqueue_loop_step<float>(st, d_canvas, params, h_seeds, d_H, d_y, d_argmax, d_margin, d_commit_mask,
+                                        d_n_committed, d_done, cs);
+      const hipError_t ec = hipStreamEndCapture(cs, &graph);
+      st->prof_mask = saved_prof;
+      if (r) { if (graph) hipGraphDestroy(graph); return r; }
+      if (ec != hipSuccess) return fail(DG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
+      const hipError_t ei = hipGraphInstantiate(&G.exec, graph, nullptr, nullptr, 0);
+      hipGraphDestroy(graph);
+      if (ei != hipSuccess) { G.exec = nullptr; return fail(DG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei)); }
+      G.bufs = bufs; G.params = *params; G.seeds = seeds; G.attn_splits = splits; G.attn_keys_class = keys_class;
+    }
+  }
+  // the steps: at most S; with DG_RUN_EARLY_EXIT the host stays at most two
+  // steps ahead of the device (reading the progress record in mapped host
+  // memory, no synchronisation) and stops issuing once every request is done
+  const int64_t base = st->steps_launched;
+  int issued = 0;
+  bool seen_done = false;
+  for (int t = first_step; t < first_step + n_steps; ++t) {
+    if (flags & DG_RUN_GRAPH) {
+      DG_HIP(hipGraphLaunch(st->graph.exec, s));
+    } else {
+      r = bf ? enqueue_loop_step<bf16>(st, d_canvas, params, h_seeds, d_H, d_y, d_argmax, d_margin, d_commit_mask,
+                                       d_n_committed, d_done, s)
+             : enqueue_loop_step<float>(st, d_canvas, params, h_seeds, d_H, d_y, d_argmax, d_margin, d_commit_mask,
+                                        d_n_committed, d_done, s);
+      if (r) return r;
+    }
+    ++issued;
+    ++st->steps_launched;
+    if (flags & DG_RUN_EARLY_EXIT) {
+      const int64_t need = st->steps_launched - 2;
+      bool all_done = false;
+      for (;;) {
+        const int64_t got = (int64_t)__atomic_load_n(const_cast<int32_t*>(&st->progress[0]), __ATOMIC_ACQUIRE);
+        if (got > base) all_done = __atomic_load_n(const_cast<int32_t*>(&st->progress[1]), __ATOMIC_RELAXED) != 0;
+        if (all_done || got >= need) break;
+        std::this_thread::yield();
+      }
+      if (all_done) { seen_done = true; break; }
+    }
+  }
+  st->loop_step = first_step + issued;
+  const bool finished = seen_done || st->loop_step == S;
+  if (h_result) { h_result[0] = issued; h_result[1] = finished ? 1 : 0; }
+  if ((flags & DG_RUN_COMMIT_KV) && finished) {
+    r = dg_commit_canvas_to_kv(st, d_canvas, nullptr, stream);
+    if (r) return r;
+  }
   return DG_OK;
 }

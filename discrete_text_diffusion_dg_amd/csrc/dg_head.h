@@ -59,13 +59,16 @@ __device__ __forceinline__ uint32_t gumbel_call(int v) { return ((uint32_t)(v >>
 // Called by all 256 threads of the workgroup.
 template <typename T>
 __device__ __forceinline__ void head_tile_stats(const float* tile, int m0, int rows, int n0, int cols, int V,
-                                                float inv_t, const SeedArg& seeds, int n, int canvas_index, int step,
-                                                HeadPart* part, int nchunk, T* ptilde) {
+                                                const StepInfo& si, const SeedArg& seeds, int n, HeadPart* part,
+                                                int nchunk, T* ptilde) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rl = w * 32 + (lane & 31), half = lane >> 5, c0 = half * 64;
   const bool have = rl < rows && c0 < cols;
   const int row = m0 + rl, v0 = n0 + c0;
   const int b = have ? row / n : 0, pos = have ? row % n : 0;
+  const int step = si.get_step();
+  const float inv_t = si.get_inv_t(step);
+  const int canvas_index = si.cidx[b];
   const float* tr = tile + rl * kHeadLd + c0;
   float x[64];
 #pragma unroll

@@ -16,6 +16,44 @@ struct SeedArg {
   uint64_t v[kMaxBatch];
 };
 
+// Requests taking part in a pass.  Request b computes iff active(b): every
+// kernel of the pass skips the rows, tiles and blocks of the others, whose
+// outputs and state are left as they were.  p == nullptr: every request.
+struct Gate {
+  const uint8_t* p;
+  int invert;          // 0: p[b] != 0 marks an active request; 1: p[b] != 0 marks a finished one
+  __device__ __forceinline__ bool active(int b) const { return p == nullptr || ((p[b] != 0) != (invert != 0)); }
+  // any request among rows r0 .. r0 + rows - 1 (n rows per request) active
+  __device__ __forceinline__ bool any_active(int r0, int rows, int n) const {
+    if (p == nullptr) return true;
+    for (int b = r0 / n; b <= (r0 + rows - 1) / n; ++b)
+      if (active(b)) return true;
+    return false;
+  }
+};
+
+// Positions of a pass: request b's new rows sit at ctx[b] + off + i (ctx: the
+// per-request context lengths held in the state).
+struct PosArg {
+  const int32_t* ctx;
+  int off;
+  __device__ __forceinline__ int base(int b) const { return ctx[b] + off; }
+};
+
+// Step of the canvas, its temperature and the canvas index of each request.
+// The explicit step calls give the step and 1 / T by value; the device-driven
+// canvas loop reads them from the state (the step counter and a per-step
+// table of 1 / T computed on the host), so one captured step serves them all.
+struct StepInfo {
+  int step;
+  float inv_t;
+  const int32_t* pstep;     // non-null: the step counter of the loop
+  const float* inv_tab;     // 1 / T of each step (loop mode)
+  const int32_t* cidx;      // canvas index of each request
+  __device__ __forceinline__ int get_step() const { return pstep != nullptr ? *pstep : step; }
+  __device__ __forceinline__ float get_inv_t(int st) const { return pstep != nullptr ? inv_tab[st] : inv_t; }
+};
+
 // Statistics of one (row, 128-id vocabulary chunk), written by the LM-head
 // epilogue (or by head_from_logits) and combined per row by sampler_merge.
 struct HeadPart {       // statistics of one (row, vocab chunk)
@@ -33,8 +71,9 @@ struct HeadPart {       // statistics of one (row, vocab chunk)
 // type) and logits (fp32) are written when non-null.
 template <typename T>
 struct HeadArgs {
-  float inv_t; SeedArg seeds; int n, canvas_index, step;
+  StepInfo si; SeedArg seeds; int n;
   HeadPart* part; T* ptilde; float* logits;
+  Gate gate;
 };
 
 // One expert-routed tile: (expert, first gathered row, rows, unused).
@@ -52,26 +91,29 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(int M, int N, int K, int bm, int bn, int elem_bytes, int target);
 // part[s][r][c] = sum over k in split s of A[r][k] * B[c][k]   (fp32, [splits][M][N])
+// Tiles whose rows (n per request) all belong to requests the gate leaves
+// out are skipped.
 template <typename T>
 hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
-                         SplitPlan sp, hipStream_t s);
+                         SplitPlan sp, Gate g, int n, hipStream_t s);
 // same with an fp32 A rounded to the operand type on load
 template <typename T>
 hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
-                              SplitPlan sp, hipStream_t s);
+                              SplitPlan sp, Gate g, int n, hipStream_t s);
 // The tied LM head, logits[r][v] = A[r] . B[v], in 128 x 128 tiles whose epilogue
 // writes the head statistics of each (row, 128-id chunk) -- part[r][v / 128] --
 // and, as asked, exp(z - chunk max) and the logits.  V must be a multiple of 64.
 template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s);
-// The fused QKV projection of rows r = b * n + i with RoPE at position ctx + i
-// applied to q and k in its epilogue: q -> q [M][Hq * hd], k -> K cache rows,
-// v -> V^T cache columns (the layouts rope_scatter writes).  One head per tile.
+// The fused QKV projection of rows r = b * n + i with RoPE at position
+// pos.base(b) + i applied to q and k in its epilogue: q -> q [M][Hq * hd],
+// k -> K cache rows, v -> V^T cache columns (the layouts rope_scatter writes).
+// One head per tile; requests the gate leaves out write nothing.
 bool qkv_rope_ok(int d, int hd, int elem_bytes);
 template <typename T>
 hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const float2* rope, T* q, T* kc, T* vc,
-                         int n, int Hq, int Hkv, int stride, int ctx, hipStream_t s);
+                         int n, int Hq, int Hkv, int stride, PosArg pos, Gate g, hipStream_t s);
 // Rows per tile of the expert-grouped products (the router writes its tile
 // list with this many rows per tile for them): 128 on the bf16 LDS-DMA tile
 // loop, else 64.
@@ -102,7 +144,7 @@ hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* t
 // rnd(P[r][k] * scale[r][k / 128]) * Bt[c][k]   (P: [M][K], scale: [M][nchunk], Bt: [N][K])
 template <typename T>
 hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt, float* part, int M, int N, int K,
-                         int splits, int kchunk, hipStream_t s);
+                         int splits, int kchunk, Gate g, int n, hipStream_t s);
 
 // ---- attention (k_attn.hip)
 struct AttnArgs {
@@ -113,7 +155,9 @@ struct AttnArgs {
   float* part_o;        // split partials [splits][B*nq*Hq][hd] (fp32, unnormalised)
   float* part_ml;       // split partials [splits][B*nq*Hq][2] (running max, sum)
   int B, nq, Hq, Hkv, hd, kv_stride;   // kv_stride: context capacity rounded up to 64
-  int ctx;              // keys 0..ctx+nq-1 (the new rows sit at ctx..ctx+nq-1)
+  PosArg pos;           // request b: keys 0..pos.base(b)+nq-1 (the new rows sit at pos.base(b)..+nq-1)
+  int keys_max;         // largest key count over the requests (launch shape only)
+  Gate gate;            // requests left out compute and write nothing
   int causal;
   int splits;
   float scale;
@@ -121,22 +165,26 @@ struct AttnArgs {
 template <typename T>
 hipError_t attention(const AttnArgs& a, hipStream_t s);
 int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys, int elem_bytes);
+// Which attention kernel a launch takes for this many keys (0 spread, 1 wide).
+int attention_launch_class(int B, int nq, int Hq, int Hkv, int hd, int keys);
 
 // ---- row-wise kernels (k_misc.hip); S = number of split partials to reduce
+// Row kernels: one workgroup per row; rows of requests the gate leaves out
+// (n rows per request) return at once.
 template <typename T>
 hipError_t embed_norm(const T* emb, const int32_t* tok, const float* part, int S, int M, int d, int vocab,
-                      const float* g, float eps, float* H, T* xn, hipStream_t s);
+                      const float* g, float eps, float* H, T* xn, Gate gt, int n, hipStream_t s);
 template <typename T>
 hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
-                    hipStream_t s);
+                    Gate gt, int n, hipStream_t s);
 template <typename T>
 hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
-                        float eps, float* H, T* xn, hipStream_t s);
-// RoPE on q and k of the fused projection (sum of S partials), q -> Q buffer, k and v -> cache at ctx + i
-// (K rows [B][Hkv][stride][hd], V transposed [B][Hkv][hd][stride])
+                        float eps, float* H, T* xn, Gate gt, int n, hipStream_t s);
+// RoPE on q and k of the fused projection (sum of S partials), q -> Q buffer, k and v -> cache at
+// pos.base(b) + i (K rows [B][Hkv][stride][hd], V transposed [B][Hkv][hd][stride])
 template <typename T>
 hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
-                        int Hkv, int hd, int stride, int ctx, hipStream_t s);
+                        int Hkv, int hd, int stride, PosArg pos, Gate gt, hipStream_t s);
 hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t s);
 // Router of one layer: logits, top-k + softmax weights, and the expert-sorted
 // order (perm, pos, 64-row tiles).  cnt: scratch of E * ceil(M / router_rows_per_block(E)) ints;
@@ -145,37 +193,61 @@ hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t
 constexpr int kRouterWaves = 4, kRouterMaxSplits = 8;
 int router_rows_per_block(int E);
 int router_ksplits(int M, int d, int E);
+// Rows of requests the gate leaves out get expert id -1 in every slot and take
+// no place in the expert-sorted order (their pos entries are not written).
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, hipStream_t s);
+                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, Gate gt, int n,
+                  hipStream_t s);
 // Few routed entries (M * k <= 4096, E a power of two <= 128): add_norm plus
 // the router logits, top-k and softmax of each row (rlog, idx, w), then the
 // expert-sorted order (perm, pos, tiles) in one workgroup.
 bool router_fused_ok(int M, int d, int E, int k);
 template <typename T>
 hipError_t add_norm_router(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
-                           const T* wr, int E, int k, float* rlog, int* idx, float* w, hipStream_t s);
+                           const T* wr, int E, int k, float* rlog, int* idx, float* w, Gate gt, int n,
+                           hipStream_t s);
 hipError_t route_sort(const int* idx, int M, int k, int E, int tile_rows, int* perm, int* pos, int4* tiles,
                       int* n_tiles, hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s);
-hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,
+// canvas_len uniform tokens per request b, Philox canvas index cidx[b]
+hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, const int32_t* cidx,
                        hipStream_t s);
+// Per-request context bookkeeping: ctx[b] += add and cidx[b] += add_canvas for
+// the requests the gate selects.
+hipError_t advance_context(int32_t* ctx, int32_t* cidx, int B, int add, int add_canvas, Gate g, hipStream_t s);
+// Fills of a device buffer (kernels, so that captured graphs hold no memset nodes).
+hipError_t fill_u32(void* p, uint32_t v, size_t count, hipStream_t s);
+hipError_t fill_u8(void* p, uint8_t v, size_t count, hipStream_t s);
+// End of a step of the device-driven loop.  step[0] (the canvas step)
+// advances, step[1] = every request done, step[2] counts the loop steps
+// completed; progress (mapped host memory, may be null) receives
+// (step[2], step[1]).
+hipError_t step_end(const uint8_t* done, int B, int32_t* step, volatile int32_t* progress, hipStream_t s);
 
 // ---- sampler (k_sampler.hip)
+// Fixed device scratch of the allocation-free sampler entry point
+// (dg_sample_logits_static): its device address on the current device, looked
+// up on the first call there.  Layout: kMaxBatch canvas indices (int32), then
+// from kStaticHeadOffset the per-(row, chunk) head statistics.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr size_t kStaticHeadOffset = 4096;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(void** ptr);
 int head_chunks(int vocab);     // 128-id chunks of the vocabulary
 // head statistics of supplied fp32 logits [M][V] (V a multiple of 64)
 template <typename T>
-hipError_t head_from_logits(const float* logits, int M, int V, float inv_t, const SeedArg& seeds, int n,
-                            int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s);
-hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active,
+hipError_t head_from_logits(const float* logits, int M, int V, const StepInfo& si, const SeedArg& seeds, int n,
+                            HeadPart* part, T* ptilde, Gate g, hipStream_t s);
+hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, Gate g,
                          float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale,
                          hipStream_t s);
-// S[r][c] = sum over splits (in order) of part[split][r][c]
-hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, hipStream_t s);
+// S[r][c] = sum over splits (in order) of part[split][r][c], rows of active requests
+hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s);
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,
                          int32_t* prev_am, uint8_t* mask, int32_t* n_committed, uint8_t* done,
-                         const SeedArg& seeds, int B, int n, int vocab, int step, int max_steps,
-                         float bound, int stop_mode, float tau, int canvas_index, hipStream_t s);
+                         const SeedArg& seeds, int B, int n, int vocab, const StepInfo& si, int max_steps,
+                         float bound, int stop_mode, float tau, hipStream_t s);
 
 }  // namespace dg

@@ -28,7 +28,7 @@
 // memory-counter wait and the slice is handed over with an LDS-only barrier,
 // so the later slices' loads stay in flight.
 #pragma once
-#include "dg_common.h"
+#include "dg_kernels.h"
 
 #include <type_traits>
 
@@ -73,6 +73,8 @@ constexpr int kBandRows = 8;
 template <int BM, int BN>
 struct SchedDense {
   int M, N, K, mt, nt, splits, kchunk;
+  Gate gate;       // tiles whose rows all belong to requests left out are skipped
+  int n;           // rows per request (with a gate)
   __device__ bool get(int bid, TileCtx& t) const {
     const int per = mt * nt, total = per * splits;
     if (bid >= total) return false;
@@ -85,7 +87,7 @@ struct SchedDense {
     t.rows = min(BM, M - t.m0); t.cols = min(BN, N - t.n0);
     t.k0 = s * kchunk; t.k1 = min(K, t.k0 + kchunk);
     t.group = s; t.row_base = t.m0;
-    return true;
+    return gate.p == nullptr || gate.any_active(t.m0, t.rows, n);
   }
 };
 

@@ -139,6 +139,8 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
   const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv, split = blockIdx.z;
   const int rho0 = blockIdx.x * RPW * QBW;
+  if (!a.gate.active(b)) return;                 // the whole workgroup, before any barrier
+  const int ctx = a.pos.base(b);
   // query block qb of this wave: rows rho0 + qb * RPW + 16 w + (0..15)
   bool qvalid[QBW];
   int qi[QBW], head[QBW], qpos[QBW];
@@ -149,14 +151,14 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
     const int hh = qvalid[qb] ? rho / a.nq : 0;
     qi[qb] = qvalid[qb] ? rho % a.nq : 0;
     head[qb] = kvh * G + hh;
-    qpos[qb] = a.ctx + qi[qb];
+    qpos[qb] = ctx + qi[qb];
   }
-  const int total = a.ctx + a.nq;
+  const int total = ctx + a.nq;
   int klimit = total;
   if (a.causal) {
     const int last = min(rho0 + RPW * QBW - 1, rows_total - 1);
     const int imax = (rho0 / a.nq == last / a.nq) ? last % a.nq : a.nq - 1;
-    klimit = a.ctx + imax + 1;
+    klimit = ctx + imax + 1;
   }
   const int per = ((total + a.splits - 1) / a.splits + KT - 1) / KT * KT;
   const int kbeg = split * per, kend = min(klimit, kbeg + per);
@@ -438,6 +440,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
   const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
   const int bk = blockIdx.y, b = bk / a.Hkv, kvh = bk % a.Hkv, split = blockIdx.z;
   const int rho0 = blockIdx.x * 16 * QB;           // < rows_total (grid.x is exact)
+  if (!a.gate.active(b)) return;                   // the whole workgroup, before any barrier
+  const int ctx = a.pos.base(b);
 
   bool qv[QB];
   int qpos[QB];
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
     const int rho = rho0 + qb * 16 + q16;
     qv[qb] = rho < rows_total;
     const int hh = qv[qb] ? rho / a.nq : 0, qi = qv[qb] ? rho % a.nq : 0;
-    qpos[qb] = a.ctx + qi;
+    qpos[qb] = ctx + qi;
     const size_t qrow = ((size_t)(b * a.nq + qi) * a.Hq + kvh * G + hh) * HD;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -462,12 +466,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
   }
 
   // key range of this workgroup (one split)
-  const int total = a.ctx + a.nq;
+  const int total = ctx + a.nq;
   int klimit = total;
   if (a.causal) {
     const int last = min(rho0 + 16 * QB - 1, rows_total - 1);
     const int imax = (rho0 / a.nq == last / a.nq) ? last % a.nq : a.nq - 1;
-    klimit = a.ctx + imax + 1;
+    klimit = ctx + imax + 1;
   }
   const int per = ((total + a.splits - 1) / a.splits + KT - 1) / KT * KT;
   const int kbeg = split * per, kend = min(klimit, kbeg + per);
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t rowid = gid / (HD / 4);
   const int d0 = (int)(gid % (HD / 4)) * 4;
-  if (rowid >= nrows) return;
+  if (rowid >= nrows || !a.gate.active((int)(rowid / a.Hq / a.nq))) return;
   float m = -INFINITY;
   for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_ml[(s * nrows + rowid) * 2]);
   float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -693,7 +697,7 @@ inline bool use_spread(int B, int nq, int Hq, int Hkv, int hd, int keys) {
 template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  if (use_spread(a.B, a.nq, a.Hq, a.Hkv, HD, a.ctx + a.nq)) {
+  if (use_spread(a.B, a.nq, a.Hq, a.Hkv, HD, a.keys_max)) {
     constexpr int NW = kSpreadNW, QB = kSpreadQB;
     dim3 grid((G * a.nq + 16 * QB - 1) / (16 * QB), a.B * a.Hkv, a.splits);
     hipLaunchKernelGGL((k_attn_spread<T, HD, NW, QB>), grid, dim3(64 * NW), 0, s, a);
@@ -736,6 +740,10 @@ int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys, int elem_
   if (splits > 16) splits = 16;
   if (splits < 1) splits = 1;
   return splits;
+}
+
+int attention_launch_class(int B, int nq, int Hq, int Hkv, int hd, int keys) {
+  return use_spread(B, nq, Hq, Hkv, hd, keys) ? 0 : 1;
 }
 
 template <typename T>

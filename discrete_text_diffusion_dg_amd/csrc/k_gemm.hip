@@ -52,7 +52,7 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
 template <typename T>
 struct EpHead {
   static constexpr int kSmemBytes = kHeadTileBytes;
-  float inv_t; SeedArg seeds; int n, canvas_index, step, V, nchunk;
+  StepInfo si; SeedArg seeds; int n, V, nchunk;
   HeadPart* part; T* ptilde; float* logits;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
@@ -64,8 +64,7 @@ struct EpHead {
         if (r < t.rows && c < t.cols) logits[(size_t)(t.m0 + r) * V + t.n0 + c] = v;
       });
     __syncthreads();
-    head_tile_stats<T>(tile, t.m0, t.rows, t.n0, t.cols, V, inv_t, seeds, n, canvas_index, step, part, nchunk,
-                       ptilde);
+    head_tile_stats<T>(tile, t.m0, t.rows, t.n0, t.cols, V, si, seeds, n, part, nchunk, ptilde);
   }
 };
 
@@ -73,13 +72,15 @@ struct EpHead {
 // head (BN == hd columns of the [q heads | k heads | v heads] projection).  q
 // and k are rotated (rotate-half, table rope[pos][j] = (cos, sin)) and stored
 // to the query buffer / the K cache row pos; v goes to the transposed V cache
-// column pos.  Row r of the product is (request r / n, position ctx + r % n).
+// column pos.  Row r of the product is (request b = r / n, position
+// pos.base(b) + r % n); rows of requests the gate leaves out are not stored.
 template <typename T, int HD>
 struct EpQKV {
   static constexpr int kLd = HD + 4;
   static constexpr int kSmemBytes = 128 * kLd * 4;         // at most 128 rows staged
   const float2* rope; T* q; T* kc; T* vc;
-  int n, Hq, Hkv, stride, ctx;
+  int n, Hq, Hkv, stride;
+  PosArg pa; Gate gate;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
     static_assert(C::BN == HD && C::BM <= 128, "one head per tile");
@@ -93,8 +94,8 @@ struct EpQKV {
     const bool pow2 = (n & (n - 1)) == 0;
     const int nsh = __ffs(n) - 1;
     auto split_row = [&](int row, int& b, int& pos) __attribute__((always_inline)) {
-      if (pow2) { b = row >> nsh; pos = ctx + (row & (n - 1)); }
-      else { b = row / n; pos = ctx + row % n; }
+      if (pow2) { b = row >> nsh; pos = pa.base(b) + (row & (n - 1)); }
+      else { b = row / n; pos = pa.base(b) + row % n; }
     };
     if (head < Hq + Hkv) {
       for (int u = threadIdx.x; u < C::BM * half; u += blockDim.x) {
@@ -103,6 +104,7 @@ struct EpQKV {
         const int row = t.m0 + r;
         int b, pos;
         split_row(row, b, pos);
+        if (!gate.active(b)) continue;
         const float a = tile[r * kLd + j], bb = tile[r * kLd + j + half];
         const float2 cs = rope[(size_t)pos * half + j];
         const float o1 = a * cs.x - bb * cs.y, o2 = bb * cs.x + a * cs.y;
@@ -119,6 +121,7 @@ struct EpQKV {
         const int row = t.m0 + r;
         int b, pos;
         split_row(row, b, pos);
+        if (!gate.active(b)) continue;
         Num<T>::store(vc + (((size_t)b * Hkv + kh) * HD + c) * stride + pos, tile[r * kLd + c]);
       }
     }
@@ -217,33 +220,33 @@ struct ALChunkScaled {
 
 template <typename T>
 hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
-                         SplitPlan sp, hipStream_t s) {
+                         SplitPlan sp, Gate g, int n, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // many rows, no split: 128 x 128 tiles through the DMA loop
     if (sp.splits == 1 && M >= kDmaMinRows && K % 64 == 0) {
       using C = TileCfgD<128, 128, 2>;
-      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K};
+      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K, g, n};
       return launch_dma<C>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{part, N, 0}, s);
     }
     // few rows, split along K: 64 x 64 tiles, a split's slices all in flight at once
     if (sp.kchunk % 64 == 0 && K % 64 == 0) {
       using C = TileCfgD<64, 64, kSplitStages - 1>;
-      SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
+      SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk, g, n};
       return launch_dma<C>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
                            EpStoreF32{part, N, (size_t)M * N}, s);
     }
   }
   using C = TileCfg<T, 64, 64, kSplitStages>;
-  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
+  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk, g, n};
   return launch<C, T>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
                       EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
 template <typename T>
 hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, float* part, int M, int N, int K,
-                              SplitPlan sp, hipStream_t s) {
+                              SplitPlan sp, Gate g, int n, hipStream_t s) {
   using C = TileCfg<T, 64, 64, kSplitStages>;
-  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk};
+  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk, g, n};
   return launch<C, T>(sc.mt * sc.nt * sp.splits, sc, ALF32<T>{A, lda}, BLPlain<T>{B, ldb},
                       EpStoreF32{part, N, (size_t)M * N}, s);
 }
@@ -254,19 +257,19 @@ template <int HD> constexpr int kQkvStages = 4;
 
 template <typename T, int HD>
 static hipError_t qkv_rope_hd(const T* xn, const T* wqkv, int M, int K, const float2* rope, T* q, T* kc, T* vc, int n,
-                              int Hq, int Hkv, int stride, int ctx, hipStream_t s) {
+                              int Hq, int Hkv, int stride, PosArg pa, Gate g, hipStream_t s) {
   const int N = (Hq + 2 * Hkv) * HD;
-  const EpQKV<T, HD> ep{rope, q, kc, vc, n, Hq, Hkv, stride, ctx};
+  const EpQKV<T, HD> ep{rope, q, kc, vc, n, Hq, Hkv, stride, pa, g};
   if constexpr (sizeof(T) == 2) {
     if (M <= 512) {
-      SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K};
+      SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K, g, n};
       return launch_dma<TileCfgD<32, HD, kQkvStages<HD>>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
     }
-    SchedDense<128, HD> sc{M, N, K, cdiv(M, 128), N / HD, 1, K};
+    SchedDense<128, HD> sc{M, N, K, cdiv(M, 128), N / HD, 1, K, g, n};
     return launch_dma<TileCfgD<128, HD, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
   } else {
     using C = TileCfg<T, 64, HD>;
-    SchedDense<64, HD> sc{M, N, K, cdiv(M, 64), N / HD, 1, K};
+    SchedDense<64, HD> sc{M, N, K, cdiv(M, 64), N / HD, 1, K, g, n};
     return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
   }
 }
@@ -278,12 +281,12 @@ bool qkv_rope_ok(int d, int hd, int elem_bytes) {
 
 template <typename T>
 hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const float2* rope, T* q, T* kc, T* vc,
-                         int n, int Hq, int Hkv, int stride, int ctx, hipStream_t s) {
+                         int n, int Hq, int Hkv, int stride, PosArg pa, Gate g, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (!qkv_rope_ok(d, hd, (int)sizeof(T))) return hipErrorInvalidValue;
-  if (hd == 64) return qkv_rope_hd<T, 64>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, ctx, s);
+  if (hd == 64) return qkv_rope_hd<T, 64>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, pa, g, s);
   if constexpr (sizeof(T) == 2) {
-    return qkv_rope_hd<T, 128>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, ctx, s);
+    return qkv_rope_hd<T, 128>(xn, wqkv, M, d, rope, q, kc, vc, n, Hq, Hkv, stride, pa, g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -292,8 +295,8 @@ template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s) {
   if (V % 64) return hipErrorInvalidValue;
-  SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K};
-  EpHead<T> ep{h.inv_t, h.seeds, h.n, h.canvas_index, h.step, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits};
+  SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K, h.gate, h.n};
+  EpHead<T> ep{h.si, h.seeds, h.n, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits};
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0)
       return launch_dma<TileCfgD<kHeadChunk, kHeadChunk, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
@@ -347,10 +350,10 @@ hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* t
 
 template <typename T>
 hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt, float* part, int M, int N, int K,
-                         int splits, int kchunk, hipStream_t s) {
+                         int splits, int kchunk, Gate g, int n, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (M >= 128 && N >= 128 && kchunk % 128 == 0 && K % 64 == 0) {
-      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk};
+      SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk, g, n};
       return launch_dma<TileCfgD<128, 128, 2>>(sc.mt * sc.nt * splits, sc, ALChunkScaled<T>{P, K, scale, nchunk},
                                                BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
     }
@@ -358,29 +361,29 @@ hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt
   const ALScaled<T> al{P, K, scale, nchunk};
   if (M >= 128 && N >= 128) {
     using C = TileCfg<T, 128, 128>;
-    SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk};
+    SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), splits, kchunk, g, n};
     return launch<C, T>(sc.mt * sc.nt * splits, sc, al, BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
   }
   using C = TileCfg<T, 64, 64>;
-  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), splits, kchunk};
+  SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), splits, kchunk, g, n};
   return launch<C, T>(sc.mt * sc.nt * splits, sc, al, BLPlain<T>{Bt, K}, EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
 #define DG_INST(T)                                                                                       \
   template hipError_t gemm_partials<T>(const T*, int, const T*, int, float*, int, int, int, SplitPlan,    \
-                                       hipStream_t);                                                    \
+                                       Gate, int, hipStream_t);                                         \
   template hipError_t gemm_partials_f32a<T>(const float*, int, const T*, int, float*, int, int, int,      \
-                                            SplitPlan, hipStream_t);                                    \
+                                            SplitPlan, Gate, int, hipStream_t);                         \
   template hipError_t gemm_lm_head<T>(const T*, int, const T*, int, int, int, int, const HeadArgs<T>&,      \
                                       hipStream_t);                                                     \
   template hipError_t gemm_qkv_rope<T>(const T*, const T*, int, int, int, const float2*, T*, T*, T*, int, int, \
-                                       int, int, int, hipStream_t);                                     \
+                                       int, int, PosArg, Gate, hipStream_t);                            \
   template hipError_t gemm_expert_gateup<T>(const T*, const int*, const T*, const T*, T*, const int4*,    \
                                             const int*, int, int, int, hipStream_t);                    \
   template hipError_t gemm_expert_down<T>(const T*, const T*, float*, const int4*, const int*, int, int,  \
                                           int, hipStream_t);                                            \
   template hipError_t gemm_selfcond<T>(const T*, const float*, int, const T*, float*, int, int, int, int, \
-                                       int, hipStream_t);
+                                       int, Gate, int, hipStream_t);
 DG_INST(float)
 DG_INST(bf16)
 #undef DG_INST

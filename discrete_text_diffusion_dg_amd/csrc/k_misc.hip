@@ -93,8 +93,9 @@ __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int 
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t* tok, const float* part, int S,
                                                     int M, int d, int vocab, const float* g, float eps, float* H,
-                                                    T* xn) {
+                                                    T* xn, Gate gt, int n) {
   const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  if (!gt.active(r / n)) return;
   const int id = min(max(tok[r], 0), vocab - 1);   // out-of-range ids are clamped, never read past E
   float4 v[kRowChunks];
 #pragma unroll
@@ -119,8 +120,9 @@ __global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t*
 // h += sum_s part[s]; xn = rnd(rmsnorm(h) * g)
 template <typename T>
 __global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int M, int d, const float* g, float eps,
-                                                  float* H, T* xn) {
+                                                  float* H, T* xn, Gate gt, int n) {
   const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  if (!gt.active(r / n)) return;
   float4 v[kRowChunks];
 #pragma unroll
   for (int j = 0; j < kRowChunks; ++j)
@@ -137,8 +139,10 @@ __global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int 
 // h += sum_j w[j] * Y[pos[j]] (slots in selection order); xn = rnd(rmsnorm(h) * g)
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int* pos, const float* w, int k, int M,
-                                                      int d, const float* g, float eps, float* H, T* xn) {
+                                                      int d, const float* g, float eps, float* H, T* xn, Gate gt,
+                                                      int n) {
   const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  if (!gt.active(r / n)) return;
   int ps[8];
   float ws[8];
 #pragma unroll
@@ -165,24 +169,25 @@ __global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int*
 
 template <typename T>
 hipError_t embed_norm(const T* emb, const int32_t* tok, const float* part, int S, int M, int d, int vocab,
-                      const float* g, float eps, float* H, T* xn, hipStream_t s) {
+                      const float* g, float eps, float* H, T* xn, Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_embed_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, emb, tok, part, S, M, d, vocab, g, eps,
-                     H, xn);
+                     H, xn, gt, n);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
-                    hipStream_t s) {
+                    Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_add_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn);
+  hipLaunchKernelGGL((k_add_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, gt, n);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
-                        float eps, float* H, T* xn, hipStream_t s) {
+                        float eps, float* H, T* xn, Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_combine_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, Y, pos, w, k, M, d, g, eps, H, xn);
+  hipLaunchKernelGGL((k_combine_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, Y, pos, w, k, M, d, g, eps, H, xn,
+                     gt, n);
   return hipGetLastError();
 }
 
@@ -209,8 +214,10 @@ hipError_t rope_table(float2* tab, int max_ctx, int hd, float theta, hipStream_t
 // position ctx + i.
 template <typename T>
 __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int M, int n,
-                               int Hq, int Hkv, int hd, int stride, int ctx) {
-  const int r = blockIdx.x, b = r / n, i = r % n, pos = ctx + i, half = hd / 2;
+                               int Hq, int Hkv, int hd, int stride, PosArg pa, Gate gt) {
+  const int r = blockIdx.x, b = r / n, i = r % n, half = hd / 2;
+  if (!gt.active(b)) return;
+  const int pos = pa.base(b) + i;
   const int ncol = (Hq + 2 * Hkv) * hd;
   const size_t sstride = (size_t)M * ncol;
   const float* x = part + (size_t)r * ncol;
@@ -240,10 +247,10 @@ __global__ void k_rope_scatter(const float* part, int S, const float2* rope, T* 
 }
 template <typename T>
 hipError_t rope_scatter(const float* part, int S, const float2* rope, T* q, T* kc, T* vc, int B, int n, int Hq,
-                        int Hkv, int hd, int stride, int ctx, hipStream_t s) {
+                        int Hkv, int hd, int stride, PosArg pa, Gate gt, hipStream_t s) {
   if (B * n <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_rope_scatter<T>), dim3(B * n), dim3(256), 0, s, part, S, rope, q, kc, vc, B * n, n, Hq,
-                     Hkv, hd, stride, ctx);
+                     Hkv, hd, stride, pa, gt);
   return hipGetLastError();
 }
 
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(64 * NW) void k_router_logits(const T* xn, const T*
 
 template <int RPB, int NW>
 __global__ __launch_bounds__(64 * NW) void k_router_select(const float* part, int ksp, int M, int E, int k, float* rlog,
-                                                          int* idx, float* w, int* pos, int* cnt) {
+                                                          int* idx, float* w, int* pos, int* cnt, Gate gt, int n) {
   __shared__ float lg[RPB][129];
   __shared__ int sel_e[RPB][8];
   __shared__ float sel_v[RPB][8];
@@ -446,9 +453,11 @@ __global__ __launch_bounds__(64 * NW) void k_router_select(const float* part, in
     const float mx = sel_v[rl][0];
     float sum = 0.f;
     for (int u = 0; u < k; ++u) sum += expf(sel_v[rl][u] - mx);
-    const int e = sel_e[rl][j];
+    // rows of requests left out: expert -1, no place in the sorted order
+    const bool live = gt.active((r0 + rl) / n);
+    const int e = live ? sel_e[rl][j] : -1;
     idx[(size_t)r0 * k + t] = e;
-    w[(size_t)r0 * k + t] = expf(sel_v[rl][j] - mx) / sum;
+    w[(size_t)r0 * k + t] = live ? expf(sel_v[rl][j] - mx) / sum : 0.f;
     se[t] = e;
   }
   __syncthreads();
@@ -484,7 +493,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
                                                                  int4* tiles, int* n_tiles) {
   constexpr int NT = kFinishThreads;
   __shared__ int seg[NT];
-  __shared__ int offs[128], toff[129];
+  __shared__ int offs[128], toff[129], routed;
   __shared__ int tab[kFinishLds];
   const int t = threadIdx.x;
   // the count table [E][nblk]: in LDS when it fits (one coalesced read), else
@@ -539,12 +548,13 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
     if (x1 < E) { offs[x1] = rx + c0; toff[x1] = tx + n0; }
     if (t == 63) {
       toff[E] = ts;
+      routed = rs;          // entries with an expert (rows left out have none)
       if (blockIdx.x == 0) *n_tiles = ts;
     }
   }
   __syncthreads();
   for (int x = t; x < E && blockIdx.x == 0; x += NT) {
-    const int c = (x + 1 < E ? offs[x + 1] : M * k) - offs[x];
+    const int c = (x + 1 < E ? offs[x + 1] : routed) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
       tiles[toff[x] + q] = make_int4(x, offs[x] + q * tr, min(tr, c - q * tr), 0);
   }
@@ -561,7 +571,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_route_finish(const int* idx,
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * NT;
-      if (i < hi) {
+      if (i < hi && ex[u] >= 0) {
         const int p = offs[ex[u]] + ct[(size_t)ex[u] * nblk + i / (rpb * k)] + rk[u];
         pos[i] = p;
         perm[p] = i / k;
@@ -583,7 +593,8 @@ int router_ksplits(int M, int d, int E) {
 
 template <typename T>
 hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* rlog, int* idx, float* w, int* perm,
-                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, hipStream_t s) {
+                  int* pos, int4* tiles, int* n_tiles, int tile_rows, int* cnt, float* part, Gate gt, int n,
+                  hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (d % (32 * kRouterWaves) != 0 || E > 128 || k > 8 || tile_rows < 1) return hipErrorInvalidValue;
   constexpr int RPB = 16;
@@ -593,7 +604,7 @@ hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* r
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_router_select<RPB, 16>), dim3(nblk), dim3(1024), 0, s, part, ksp, M, E, k, rlog, idx, w, pos,
-                     cnt);
+                     cnt, gt, n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // one workgroup per 1024 entries (up to 64) when the count table fits LDS
@@ -604,9 +615,9 @@ hipError_t router(const T* xn, const T* wr, int M, int d, int E, int k, float* r
   return hipGetLastError();
 }
 template hipError_t router<float>(const float*, const float*, int, int, int, int, float*, int*, float*, int*, int*,
-                                  int4*, int*, int, int*, float*, hipStream_t);
+                                  int4*, int*, int, int*, float*, Gate, int, hipStream_t);
 template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, float*, int*, float*, int*, int*,
-                                 int4*, int*, int, int*, float*, hipStream_t);
+                                 int4*, int*, int, int*, float*, Gate, int, hipStream_t);
 
 // ------------------------------------------------------------------ router for few entries
 // When the routed entries of a launch fit one workgroup (M * k <= 4096), the
@@ -658,12 +669,16 @@ struct WrPiece<float> {
 template <typename T>
 __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int S, int M, int d, const float* g,
                                                          float eps, float* H, T* xn, const T* wr, int E, int k,
-                                                         float* rlog, int* idx, float* w) {
+                                                         float* rlog, int* idx, float* w, Gate gt, int n) {
   __shared__ float xs[kMaxModel];
   __shared__ float lg[128];
   __shared__ int sel_e[8];
   __shared__ float sel_v[8];
   const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
+  if (!gt.active(r / n)) {            // a row of a request left out: no expert, no place in the order
+    if (tid < k) { idx[(size_t)r * k + tid] = -1; w[(size_t)r * k + tid] = 0.f; }
+    return;
+  }
   // this thread's pieces of the router matrix (expert e, pieces sl, sl + tpe,
   // ...), requested first so that they arrive while the row is added and
   // normalised; pieces past ppt repeat the last one and are not added
@@ -735,7 +750,7 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int
                                                             int* pos, int4* tiles, int* n_tiles) {
   constexpr int NW = kSortThreads / 64;
   __shared__ int cnt[kSortBlocks][NW][128];
-  __shared__ int offs[128], toff[129];
+  __shared__ int offs[128], toff[129], routed;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int nb = (MK + kSortThreads - 1) / kSortThreads;
   int ex[kSortBlocks], rk[kSortBlocks];
@@ -788,11 +803,11 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int
     const int rx = rs - c0 - c1, tx = ts - n0 - n1;   // exclusive
     if (x0 < E) { offs[x0] = rx; toff[x0] = tx; }
     if (x1 < E) { offs[x1] = rx + c0; toff[x1] = tx + n0; }
-    if (t == 63) { toff[E] = ts; *n_tiles = ts; }
+    if (t == 63) { toff[E] = ts; routed = rs; *n_tiles = ts; }
   }
   __syncthreads();
   for (int x = t; x < E; x += kSortThreads) {
-    const int c = (x + 1 < E ? offs[x + 1] : MK) - offs[x];
+    const int c = (x + 1 < E ? offs[x + 1] : routed) - offs[x];
     for (int q = 0; q < toff[x + 1] - toff[x]; ++q)
       tiles[toff[x] + q] = make_int4(x, offs[x] + q * tr, min(tr, c - q * tr), 0);
   }
@@ -808,11 +823,12 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int
 
 template <typename T>
 hipError_t add_norm_router(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
-                           const T* wr, int E, int k, float* rlog, int* idx, float* w, hipStream_t s) {
+                           const T* wr, int E, int k, float* rlog, int* idx, float* w, Gate gt, int n,
+                           hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (!router_fused_ok(M, d, E, k)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_add_norm_router<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, wr, E,
-                     k, rlog, idx, w);
+                     k, rlog, idx, w, gt, n);
   return hipGetLastError();
 }
 
@@ -848,29 +864,64 @@ hipError_t transpose(const T* src, T* dst, int rows, int cols, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ canvas init
-__global__ void k_init_canvas(int32_t* canvas, SeedArg seeds, int n, int vocab, int canvas_index) {
+__global__ void k_init_canvas(int32_t* canvas, SeedArg seeds, int n, int vocab, const int32_t* cidx) {
   const int b = blockIdx.x;
+  const uint32_t c = (uint32_t)cidx[b];
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint4 x = philox_block(seeds.v[b], kTagInit, (uint32_t)canvas_index, 0u, (uint32_t)i, 0u);
+    const uint4 x = philox_block(seeds.v[b], kTagInit, c, 0u, (uint32_t)i, 0u);
     canvas[(size_t)b * n + i] = token_of(x.x, vocab);
   }
 }
-hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, int canvas_index,
+hipError_t init_canvas(int32_t* canvas, const SeedArg& seeds, int B, int n, int vocab, const int32_t* cidx,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_init_canvas, dim3(B), dim3(256), 0, s, canvas, seeds, n, vocab, canvas_index);
+  hipLaunchKernelGGL(k_init_canvas, dim3(B), dim3(256), 0, s, canvas, seeds, n, vocab, cidx);
+  return hipGetLastError();
+}
+
+__global__ void k_advance_context(int32_t* ctx, int32_t* cidx, int B, int add, int add_canvas, Gate g) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B && g.active(b)) {
+    ctx[b] += add;
+    cidx[b] += add_canvas;
+  }
+}
+hipError_t advance_context(int32_t* ctx, int32_t* cidx, int B, int add, int add_canvas, Gate g, hipStream_t s) {
+  hipLaunchKernelGGL(k_advance_context, dim3((B + 63) / 64), dim3(64), 0, s, ctx, cidx, B, add, add_canvas, g);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t count) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+__global__ void k_fill_u8(uint8_t* p, uint8_t v, size_t count) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+hipError_t fill_u8(void* p, uint8_t v, size_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u8, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, static_cast<uint8_t*>(p), v,
+                     count);
+  return hipGetLastError();
+}
+hipError_t fill_u32(void* p, uint32_t v, size_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, static_cast<uint32_t*>(p), v,
+                     count);
   return hipGetLastError();
 }
 
 #define DG_INST(T)                                                                                               \
   template hipError_t add_norm_router<T>(const float*, int, int, int, const float*, float, float*, T*, const T*,  \
-                                         int, int, float*, int*, float*, hipStream_t);                          \
+                                         int, int, float*, int*, float*, Gate, int, hipStream_t);               \
   template hipError_t embed_norm<T>(const T*, const int32_t*, const float*, int, int, int, int, const float*,  \
-                                    float, float*, T*, hipStream_t);                                            \
-  template hipError_t add_norm<T>(const float*, int, int, int, const float*, float, float*, T*, hipStream_t);   \
+                                    float, float*, T*, Gate, int, hipStream_t);                                 \
+  template hipError_t add_norm<T>(const float*, int, int, int, const float*, float, float*, T*, Gate, int,      \
+                                  hipStream_t);                                                                 \
   template hipError_t combine_norm<T>(const float*, const int*, const float*, int, int, int, const float*, float, \
-                                      float*, T*, hipStream_t);                                                 \
+                                      float*, T*, Gate, int, hipStream_t);                                      \
   template hipError_t rope_scatter<T>(const float*, int, const float2*, T*, T*, T*, int, int, int, int, int, int, \
-                                      int, hipStream_t);                                                        \
+                                      PosArg, Gate, hipStream_t);                                               \
   template hipError_t transpose<T>(const T*, T*, int, int, hipStream_t);
 DG_INST(float)
 DG_INST(bf16)

@@ -10,18 +10,20 @@
 // exp(z - m) in its operand loader, so its split partials add plainly.
 #include "dg_head.h"
 
+#include <mutex>
+
 namespace dg {
 
 int head_chunks(int vocab) { return (vocab + kHeadChunk - 1) / kHeadChunk; }
 
 // One workgroup per 128 x 128 tile of supplied fp32 logits [M][V].
 template <typename T>
-__global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M, int V, float inv_t, SeedArg seeds,
-                                                     int n, int canvas_index, int step, HeadPart* part, int nchunk,
-                                                     T* ptilde) {
+__global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M, int V, StepInfo si, SeedArg seeds,
+                                                     int n, HeadPart* part, int nchunk, T* ptilde, Gate g) {
   __shared__ __attribute__((aligned(16))) float tile[kHeadChunk * kHeadLd];
   const int n0 = blockIdx.x * kHeadChunk, m0 = blockIdx.y * kHeadChunk;
   const int rows = min(kHeadChunk, M - m0), cols = min(kHeadChunk, V - n0);
+  if (!g.any_active(m0, rows, n)) return;
   // 32 float4 per tile row: all loads issued together, rows / ids past the end read as 0
   float4 v[16];
 #pragma unroll
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M,
     *reinterpret_cast<float4*>(tile + r * kHeadLd + c) = v[i];
   }
   __syncthreads();
-  head_tile_stats<T>(tile, m0, rows, n0, cols, V, inv_t, seeds, n, canvas_index, step, part, nchunk, ptilde);
+  head_tile_stats<T>(tile, m0, rows, n0, cols, V, si, seeds, n, part, nchunk, ptilde);
 }
 
 // One workgroup per row; thread t holds chunks t, t + 256, ... (CPT of them) in
@@ -46,13 +48,14 @@ __global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M,
 // result does not depend on scheduling -- and last the per-chunk scales
 // exp(m_c - M) / S that turn each chunk's exp(z - m_c) into probabilities.
 template <int CPT>
-__global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int chunks, int n, const uint8_t* active,
+__global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int chunks, int n, Gate g,
                                                        float* H, int32_t* y, int32_t* am, float* margin,
                                                        float* chunk_scale) {
   __shared__ float sm_m[4], sm_l[4], sm_g1[4], sm_g2[4];
   __shared__ int sm_li[4], sm_gi[4];
   __shared__ double sm_S[4], sm_W[4];
   const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  if (!g.active(r / n)) return;          // the whole workgroup: no barrier is reached
   const HeadPart* pr = part + (size_t)r * chunks;
   HeadPart p[CPT];
 #pragma unroll
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int
         chunk_scale[(size_t)r * chunks + c] = p[j].m == -INFINITY ? 0.f : (float)(exp((double)p[j].m - m) / S);
     }
   }
-  if (t != 0 || (active != nullptr && active[r / n] == 0)) return;
+  if (t != 0) return;
   lmax = sm_l[0]; lidx = sm_li[0];
   t2 = Top2{sm_g1[0], sm_gi[0], sm_g2[0]};
   for (int q = 1; q < 4; ++q) {
@@ -121,10 +124,11 @@ __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int
 
 // s[r][c] = sum of the split partials in split order, four columns per thread,
 // the loads of up to eight splits issued together.
-__global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, int M, int d, int splits, float* S) {
+__global__ __launch_bounds__(256) void k_selfcond_reduce(const float* part, int M, int d, int splits, float* S,
+                                                         Gate g, int n) {
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;      // float4 index
   const size_t nq = (size_t)M * d / 4;
-  if (q >= nq) return;
+  if (q >= nq || !g.active((int)(q / (d / 4)) / n)) return;
   const float4* p4 = reinterpret_cast<const float4*>(part);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < splits; s0 += 8) {
@@ -162,8 +166,8 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y, const int32_t* am,
                                                 int32_t* canvas, int32_t* prev_am, uint8_t* mask,
                                                 int32_t* n_committed, uint8_t* done, SeedArg seeds, int n,
-                                                int vocab, int step, int max_steps, float bound,
-                                                int stop_mode, float tau, int canvas_index) {
+                                                int vocab, StepInfo si, int max_steps, float bound,
+                                                int stop_mode, float tau) {
   __shared__ float sh[256];
   __shared__ float hpos[256];
   __shared__ int sp[256];
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
   // every input of this position is requested at once (a finished request
   // returns after its loads, before any barrier)
   const uint8_t fin_before = done[b];
+  const int step = si.get_step(), canvas_index = si.cidx[b];
   const float h_in = t < n ? H[base + t] : INFINITY;
   const int32_t y_t = t < n ? y[base + t] : 0, am_t = t < n ? am[base + t] : 0;
   const int32_t pam_t = t < n ? prev_am[base + t] : 0;
@@ -267,52 +272,105 @@ __global__ __launch_bounds__(256) void k_commit(const float* H, const int32_t* y
 namespace dg {
 
 template <typename T>
-hipError_t head_from_logits(const float* logits, int M, int V, float inv_t, const SeedArg& seeds, int n,
-                            int canvas_index, int step, HeadPart* part, T* ptilde, hipStream_t s) {
+hipError_t head_from_logits(const float* logits, int M, int V, const StepInfo& si, const SeedArg& seeds, int n,
+                            HeadPart* part, T* ptilde, Gate g, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (V % 64) return hipErrorInvalidValue;
   const dim3 grid(head_chunks(V), (M + kHeadChunk - 1) / kHeadChunk);
-  hipLaunchKernelGGL((k_head_logits<T>), grid, dim3(256), 0, s, logits, M, V, inv_t, seeds, n, canvas_index, step,
-                     part, head_chunks(V), ptilde);
+  hipLaunchKernelGGL((k_head_logits<T>), grid, dim3(256), 0, s, logits, M, V, si, seeds, n, part, head_chunks(V),
+                     ptilde, g);
   return hipGetLastError();
 }
 
-hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, const uint8_t* active, float* H,
+hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, Gate g, float* H,
                          int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(M), block(256);
   if (chunks <= 256)
-    hipLaunchKernelGGL((k_sampler_merge<1>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<1>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
   else if (chunks <= 512)
-    hipLaunchKernelGGL((k_sampler_merge<2>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<2>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
   else if (chunks <= 1024)
-    hipLaunchKernelGGL((k_sampler_merge<4>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<4>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
   else if (chunks <= 2048)
-    hipLaunchKernelGGL((k_sampler_merge<8>), grid, block, 0, s, part, chunks, n, active, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<8>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, hipStream_t s) {
+hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s) {
   const size_t nq = (size_t)M * d / 4;      // d is a multiple of 256
   if (nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, part, M, d, splits, S);
+  hipLaunchKernelGGL(k_selfcond_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, part, M, d, splits, S,
+                     g, n);
   return hipGetLastError();
 }
 
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas, int32_t* prev_am,
                          uint8_t* mask, int32_t* n_committed, uint8_t* done, const SeedArg& seeds, int B, int n,
-                         int vocab, int step, int max_steps, float bound, int stop_mode, float tau,
-                         int canvas_index, hipStream_t s) {
+                         int vocab, const StepInfo& si, int max_steps, float bound, int stop_mode, float tau,
+                         hipStream_t s) {
   hipLaunchKernelGGL(k_commit, dim3(B), dim3(256), 0, s, H, y, am, canvas, prev_am, mask, n_committed, done, seeds,
-                     n, vocab, step, max_steps, bound, stop_mode, tau, canvas_index);
+                     n, vocab, si, max_steps, bound, stop_mode, tau);
   return hipGetLastError();
 }
 
-template hipError_t head_from_logits<float>(const float*, int, int, float, const SeedArg&, int, int, int,
-                                            HeadPart*, float*, hipStream_t);
-template hipError_t head_from_logits<bf16>(const float*, int, int, float, const SeedArg&, int, int, int,
-                                           HeadPart*, bf16*, hipStream_t);
+// End of a step of the device-driven loop (one wave): every request done?
+// The canvas step moves on, the completed-step count too, and the progress
+// record in mapped host memory (steps completed, all done) is written with
+// system-scope stores so the host sees it without a synchronisation.
+__global__ __launch_bounds__(64) void k_step_end(const uint8_t* done, int B, int32_t* step,
+                                                 volatile int32_t* progress) {
+  const int lane = threadIdx.x;
+  int fin = 1;
+  for (int b = lane; b < B; b += 64) fin &= done[b] != 0 ? 1 : 0;
+  fin = __all(fin) ? 1 : 0;
+  if (lane == 0) {
+    step[0] = step[0] + 1;
+    step[1] = fin;
+    const int32_t count = step[2] + 1;
+    step[2] = count;
+    if (progress != nullptr) {
+      __hip_atomic_store(const_cast<int32_t*>(progress + 1), fin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(const_cast<int32_t*>(progress), count, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+}
+
+hipError_t step_end(const uint8_t* done, int B, int32_t* step, volatile int32_t* progress, hipStream_t s) {
+  hipLaunchKernelGGL(k_step_end, dim3(1), dim3(64), 0, s, done, B, step, progress);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fixed scratch
+// Device memory of the allocation-free sampler entry point: a file-scope
+// array each GPU holds until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); its device address is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
+
+template hipError_t head_from_logits<float>(const float*, int, int, const StepInfo&, const SeedArg&, int,
+                                            HeadPart*, float*, Gate, hipStream_t);
+template hipError_t head_from_logits<bf16>(const float*, int, int, const StepInfo&, const SeedArg&, int,
+                                           HeadPart*, bf16*, Gate, hipStream_t);
 
 }  // namespace dg

@@ -206,27 +206,43 @@ class Engine:
                                           self.mask.data_ptr(), self.n_committed.data_ptr(),
                                           self.done.data_ptr(), self._stream()))
 
-    def commit_canvas_to_kv(self, canvas: Optional[torch.Tensor] = None) -> None:
+    def commit_canvas_to_kv(self, canvas: Optional[torch.Tensor] = None,
+                            which: Optional[torch.Tensor] = None) -> None:
+        """Append the canvas of the requests `which` selects (uint8 [B], None = all) to the KV cache."""
         cv = self.canvas if canvas is None else canvas
-        L.check(self.lib.dg_commit_canvas_to_kv(self._state, cv.data_ptr(), self._stream()))
+        L.check(self.lib.dg_commit_canvas_to_kv(self._state, cv.data_ptr(), _ptr(which), self._stream()))
+
+    def ctx_lens(self) -> torch.Tensor:
+        """Per-request context lengths (device view)."""
+        return self.view(L.DG_VIEW_CTX_LENS, torch.int32, (self.B,))
+
+    def canvas_indices(self) -> torch.Tensor:
+        """Per-request canvas indices (device view)."""
+        return self.view(L.DG_VIEW_CANVAS_INDEX, torch.int32, (self.B,))
+
+    def run_canvas_device(self, sp, first_step: int = 0, n_steps: Optional[int] = None, graph: bool = True,
+                          early_exit: bool = False, commit_kv: bool = False):
+        """Steps first_step .. first_step + n_steps - 1 of the canvas, driven by the library
+        (dg_run_canvas): no host read of device memory.  Returns (steps issued, canvas finished)."""
+        prm = sampler_struct(sp)
+        if n_steps is None:
+            n_steps = sp.max_steps - first_step
+        flags = ((L.DG_RUN_GRAPH if graph else 0) | (L.DG_RUN_EARLY_EXIT if early_exit else 0)
+                 | (L.DG_RUN_COMMIT_KV if commit_kv else 0))
+        res = (ctypes.c_int32 * 2)()
+        L.check(self.lib.dg_run_canvas(self._state, self.canvas.data_ptr(), ctypes.byref(prm), self._seed_ptr(),
+                                       self.H.data_ptr(), self.y.data_ptr(), self.am.data_ptr(),
+                                       self.margin.data_ptr(), self.mask.data_ptr(), self.n_committed.data_ptr(),
+                                       self.done.data_ptr(), first_step, n_steps, flags, res, self._stream()))
+        return res[0], bool(res[1])
 
     # ------------------------------------------------------------ loop
-    def run_canvas(self, sp, steps_limit: Optional[int] = None, on_step=None) -> int:
-        """Denoise one canvas for all requests; returns the number of steps run.
+    def run_canvas(self, sp, graph: bool = True, commit_kv: bool = False) -> int:
+        """Denoise one canvas for all requests on the device (dg_run_canvas).
 
-        The per-step host read of `done` is the loop's only synchronisation."""
-        self.init_canvas()
-        self.done.zero_()
-        S = sp.max_steps if steps_limit is None else min(sp.max_steps, steps_limit)
-        steps = 0
-        for t in range(S):
-            active = (self.done == 0).to(torch.uint8)
-            self.denoise_step(t, sp, active=active)
-            self.sample_commit(t, sp)
-            steps += 1
-            if on_step is not None:
-                on_step(t, self)
-            if sp.stop_mode != 0 or t == S - 1:
-                if bool((self.done != 0).all()):
-                    break
-        return steps
+        The done flags gate every step on the device, the step index and
+        temperature stay there, and with a stop rule the library ends the
+        canvas once every request is done, learning it from a progress record
+        in mapped host memory: no host read of device memory, no torch
+        kernel.  Returns the number of steps issued."""
+        return self.run_canvas_device(sp, graph=graph, early_exit=sp.stop_mode != 0, commit_kv=commit_kv)[0]

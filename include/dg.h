@@ -118,7 +118,11 @@ dg_status dg_state_init(const dg_model* model, void* d_buf, size_t bytes, int32_
                         int32_t max_ctx, dg_state** out);
 void dg_state_destroy(dg_state* state);
 
-/* Current context length N (positions held in the KV cache) and canvas index. */
+/* Largest context length N over the requests (positions held in the KV cache)
+ * and largest canvas index.  Each request keeps its own N and canvas index in
+ * device memory (DG_VIEW_CTX_LENS, DG_VIEW_CANVAS_INDEX); they differ once
+ * dg_commit_canvas_to_kv has committed only some requests ([mlqm] 四: every
+ * request stops on its own). */
 int32_t dg_state_ctx_len(const dg_state* state);
 int32_t dg_state_canvas_index(const dg_state* state);
 
@@ -135,7 +139,9 @@ int32_t dg_state_canvas_index(const dg_state* state);
  *   DG_VIEW_ROUTER_LOGITS: float [L][B * canvas_len][n_experts], router logits
  *     of each layer of the last pass (same row convention)
  *   DG_VIEW_ATTN_OUT: [rows][n_q_heads * head_dim], cfg dtype, attention output
- *     (before the output projection) of the last layer of the last pass */
+ *     (before the output projection) of the last layer of the last pass
+ *   DG_VIEW_CTX_LENS: int32 [B], context length N of each request
+ *   DG_VIEW_CANVAS_INDEX: int32 [B], canvas index of each request (Philox stream) */
 #define DG_VIEW_K_CACHE 0
 #define DG_VIEW_V_CACHE 1
 #define DG_VIEW_SELF_COND 2
@@ -144,6 +150,8 @@ int32_t dg_state_canvas_index(const dg_state* state);
 #define DG_VIEW_HIDDEN 5
 #define DG_VIEW_ROUTER_LOGITS 6
 #define DG_VIEW_ATTN_OUT 7
+#define DG_VIEW_CTX_LENS 8
+#define DG_VIEW_CANVAS_INDEX 9
 dg_status dg_state_view(dg_state* state, int32_t which, void** d_ptr, size_t* bytes);
 
 /* Initial canvas: canvas_len uniformly random tokens per request ([mlqm] 一,
@@ -165,8 +173,11 @@ dg_status dg_encode_prompt(dg_state* state, const int32_t* d_ids, int32_t P, dg_
  * d_canvas: int32 [B, canvas_len] current tokens (read).  step: 0-based round t
  * of the current canvas (self-conditioning is off at t = 0; the temperature is
  * t_start + (t_end - t_start) * t / (max_steps - 1)).  h_seeds: uint64 [B].
- * d_active: uint8 [B] or NULL (= all active); inactive requests are computed
- * but none of their outputs is written.
+ * d_active: uint8 [B] or NULL (= all active); an inactive request (0) takes
+ * no part in the pass: its rows, tiles and attention blocks are skipped, it
+ * routes no row to an expert, and none of its outputs nor its state (K/V
+ * cache, self-conditioning vector) is written ([mlqm] 四: a request that has
+ * stopped is done).
  * Outputs, all [B, canvas_len]: d_H float entropy (nats) of softmax(logits/T);
  * d_y int32 Gumbel-max sample of that distribution; d_argmax int32 argmax of
  * the logits; d_margin float best minus second-best Gumbel-perturbed score.
@@ -191,6 +202,27 @@ dg_status dg_sample_logits(dg_state* state, const float* d_logits, int32_t step,
                            const uint64_t* h_seeds, const uint8_t* d_active, float* d_H, int32_t* d_y,
                            int32_t* d_argmax, float* d_margin, dg_stream stream);
 
+/* For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the statistics of dg_sample_logits -- entropy, Gumbel-max
+ * sample, logit argmax, top-2 margin -- on caller-supplied logits, with no
+ * state.  d_logits: float [rows, vocab], rows = requests x canvas_len; request
+ * b = row / canvas_len draws with seed h_seeds[b] (host, uint64 [rows /
+ * canvas_len]) at canvas index canvas_index and step `step` (temperature from
+ * params).  Outputs d_H, d_y, d_argmax, d_margin: [rows], as dg_sample_logits
+ * writes them (bitwise: the same kernels).  No self-conditioning output.
+ * The per-(row, 128-id chunk) records live in a fixed 16 MiB device array of
+ * the library, held on each GPU until the process ends, so the call allocates
+ * nothing: rows x ceil(vocab / 128) x 32 bytes + 4 KiB must fit it, else
+ * DG_ERR_CAPACITY (for example 256 rows at vocab 262144 fit; 512 do not).
+ * Every call on one GPU shares that array and overwrites it: calls that
+ * overlap on one GPU (two streams, two threads) race and must be ordered by
+ * the caller.  Requests at most 128. */
+dg_status dg_sample_logits_static(const float* d_logits, int32_t rows, int32_t vocab, int32_t canvas_len,
+                                  int32_t canvas_index, int32_t step, const dg_sampler_params* params,
+                                  const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax,
+                                  float* d_margin, dg_stream stream);
+
 /* Entropy-bounded commit / uniform re-noise / adaptive stop ([mlqm] 四, 一).
  * Per request b with d_done[b] == 0: sort positions by (H, position), commit the
  * longest prefix whose running fp64 entropy total stays <= entropy_bound; the
@@ -208,9 +240,44 @@ dg_status dg_sample_commit(dg_state* state, const float* d_H, const int32_t* d_y
 
 /* Append the finished canvas to the KV cache by a causal encode at positions
  * N..N+canvas_len-1 ([bohu] 一, [chooseai]: block-autoregressive canvases);
- * N += canvas_len, canvas index += 1.  DG_ERR_CAPACITY if N + canvas_len >
- * max_ctx. */
-dg_status dg_commit_canvas_to_kv(dg_state* state, const int32_t* d_canvas, dg_stream stream);
+ * N += canvas_len, canvas index += 1 -- for the requests d_which selects:
+ * d_which uint8 [B] (nonzero = commit) or NULL (= every request).  The others
+ * compute nothing and keep their N, canvas index and cache.  DG_ERR_CAPACITY
+ * if the largest N + canvas_len > max_ctx. */
+dg_status dg_commit_canvas_to_kv(dg_state* state, const int32_t* d_canvas, const uint8_t* d_which,
+                                 dg_stream stream);
+
+/* Device-driven canvas loop ([mlqm] 四: up to max_steps rounds with adaptive
+ * stop; [mlqm] 五: the CPU-GPU exchange made asynchronous).  Runs steps
+ * first_step .. first_step + n_steps - 1 of the current canvas, each one
+ * dg_denoise_step over the requests not yet done followed by dg_sample_commit,
+ * with the step index and temperature kept on the device: no host read of
+ * device memory.  first_step == 0 starts a canvas: the initial canvas is drawn
+ * (dg_init_canvas), d_done and the self-conditioning vector are cleared;
+ * first_step > 0 must continue the canvas where the previous call stopped.
+ * Outputs as for those calls (the last step's values); d_done uint8 [B]
+ * holds every request's flag.
+ * flags:
+ *   DG_RUN_GRAPH      the step is captured once into a HIP graph (kept in the
+ *                     state, re-captured when buffers, parameters, seeds or
+ *                     the attention launch plan change) and replayed per step;
+ *   DG_RUN_EARLY_EXIT the host stays at most two steps ahead of the device,
+ *                     reading a progress record the device writes to mapped
+ *                     host memory, and stops issuing steps once every request
+ *                     is done (without it all n_steps steps are issued; steps
+ *                     after the last request is done compute nothing);
+ *   DG_RUN_COMMIT_KV  dg_commit_canvas_to_kv of every request once the canvas
+ *                     is finished (its last step issued, or every request seen
+ *                     done).
+ * h_result (may be NULL) receives {steps issued, canvas finished}.  Results
+ * are bitwise those of the explicit calls with the same inputs. */
+#define DG_RUN_GRAPH 1u
+#define DG_RUN_EARLY_EXIT 2u
+#define DG_RUN_COMMIT_KV 4u
+dg_status dg_run_canvas(dg_state* state, int32_t* d_canvas, const dg_sampler_params* params,
+                        const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax, float* d_margin,
+                        uint8_t* d_commit_mask, int32_t* d_n_committed, uint8_t* d_done, int32_t first_step,
+                        int32_t n_steps, uint32_t flags, int32_t* h_result, dg_stream stream);
 
 /* Stage timing ([mlqm] 五 splits a step's cost into MoE, sampling and
  * attention; these counters give the same split for this implementation).

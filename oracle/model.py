@@ -54,6 +54,10 @@ class OracleModel:
         self._raw: Dict[str, np.ndarray] = {}
         self._raw_layer = None
         self.on_layer = None      # optional callback(layer) after each layer (progress of long runs)
+        # optional callback(request, layer, router logits r, top-k ids) -> ids: lets a
+        # test impose another expert choice on rows whose own top-k is a near tie
+        # (the callback decides where; the weights stay the softmax of these logits)
+        self.route_override = None
         L, Hkv, hd = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
         self.k_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
         self.v_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
@@ -87,12 +91,14 @@ class OracleModel:
         return nm.upcast(self._stored(name)[e])
 
     # ------------------------------------------------------------ blocks
-    def _moe(self, l: int, xm: np.ndarray, trace: Optional[dict]) -> np.ndarray:
+    def _moe(self, l: int, xm: np.ndarray, trace: Optional[dict], b: int = 0) -> np.ndarray:
         cfg = self.cfg
         n, k = xm.shape[0], cfg.top_k
         r = (xm @ self.W(f"l{l}.w_router").T).astype(np.float32)          # decision in fp32
         order = np.argsort(-r, axis=1, kind="stable")                    # ties -> lower id
         idx = order[:, :k]
+        if self.route_override is not None:
+            idx = np.asarray(self.route_override(b, l, r, idx))
         rsel = np.take_along_axis(r, idx, axis=1).astype(np.float64)
         wts = nm.softmax(rsel, axis=1)
         contrib = np.zeros((n, k, cfg.d_model))
@@ -148,7 +154,7 @@ class OracleModel:
             trace.setdefault("v", []).append(v)
             trace.setdefault("attn", []).append(o)
         xm = self.rnd(nm.rmsnorm(h, self.W(f"l{l}.ffn_norm"), self.cfg.rms_eps))
-        return h + self._moe(l, xm, trace)
+        return h + self._moe(l, xm, trace, b)
 
     def _stack(self, b: int, ids: np.ndarray, pos: np.ndarray, causal: bool, store_kv: bool,
                h0_extra: Optional[np.ndarray], trace: Optional[dict]) -> np.ndarray:

@@ -76,7 +76,8 @@ def test_null_handles(lib):
     assert "null" in lib.dg_last_error().decode()
     assert lib.dg_denoise_step(None, None, 0, None, None, None, None, None, None, None, None, None) == -1
     assert lib.dg_sample_commit(None, None, None, None, None, 0, None, None, None, None, None, None) == -1
-    assert lib.dg_commit_canvas_to_kv(None, None, None) == -1
+    assert lib.dg_commit_canvas_to_kv(None, None, None, None) == -1
+    assert lib.dg_run_canvas(None, None, None, None, None, None, None, None, None, None, None, 0, 1, 0, None, None) == -1
     assert lib.dg_state_ctx_len(None) == -1
     sz = ctypes.c_size_t()
     assert lib.dg_state_bytes(None, 1, 512, ctypes.byref(sz)) == -1

@@ -2,14 +2,21 @@
 
 Integer outputs (canvas draws, sampled tokens, argmax, commit masks, routing)
 must match bit-exactly, except sampled tokens whose oracle Gumbel top-2 margin
-is below 1e-3 and rows with a router near-tie; logits and entropies must match
-within 2e-2 relative (bf16 models) or 1e-4 (fp32), relative meaning
-max|diff| / max|ref| per row.
+is below max(1e-3, twice the row's score discrepancy) and routing near-ties
+(below); logits and entropies must match within 2e-2 relative (bf16 models)
+or 1e-4 (fp32), relative meaning max|diff| / max|ref| per row.
 
-Each denoise step is compared teacher-forced: before it the GPU state gets the
-oracle's self-conditioning vector and (after their own comparison) the
-oracle's prompt K/V, so a routing flip on a near-tie row in one step cannot
-leak into the next step's inputs.
+Every pass is teacher-forced at its decisions.  The GPU runs first; the
+oracle then runs the same pass and, layer by layer, compares its router
+logits with the GPU's (within the value tolerance of the row's largest
+|logit|).  Where the two expert sets differ, the oracle's own logits must
+show that every swapped pair lies within twice the row's measured logit
+discrepancy -- two logits that close can trade places under the rounding
+noise the tolerance allows -- and the oracle then continues with the GPU's
+experts, so the next layers compare like with like on every row.  At most
+MAX_FLIP_FRAC of the rows may take such a swap in any one layer.  Before each
+denoise step the GPU state also gets the oracle's self-conditioning vector and
+(after their own comparison) the oracle's K/V.
 """
 import numpy as np
 import pytest
@@ -19,21 +26,12 @@ from oracle import numerics as nm
 from oracle import sampler as osmp
 from oracle.model import OracleModel
 
+from _forcing import RouteForcing, gpu_routing
 from _util import log, make_engine, micro, rel_err_rows, replace, tol_for
 
 pytestmark = pytest.mark.gpu
 
 MARGIN_EXEMPT = 1e-3
-# Routing may differ from the oracle only where the oracle's gap between its
-# k-th and (k+1)-th router logits is at most twice the row's measured router
-# logit discrepancy, and that discrepancy is itself held to the value
-# tolerance on logits (2e-2 of the row's largest |logit| for bf16 operands,
-# 1e-4 for fp32): both sides round the same activations to bf16, but fp32 sums
-# against fp64 ones flip a few of those roundings by one ulp, and the flips
-# carry through the residual stream to a router-logit drift the tests print.
-GAP_REL = {"bf16": 2e-2, "f32": 1e-4}
-MAX_FLIP_FRAC = 0.10     # rows of a pass with a routing flip (each one explained by the gap rule)
-MAX_KV_OFF_FRAC = 0.10   # cached K/V positions beyond the value tolerance (all at router near-ties)
 MAX_EXEMPT_TOKEN_FRAC = 0.02   # sampled tokens that differ under the margin exemption, per step
 
 
@@ -59,72 +57,7 @@ def torch_cuda():
     return torch
 
 
-def router_gap(r: np.ndarray, k: int) -> np.ndarray:
-    """Gap between the k-th and (k+1)-th largest router logits per row (inf if k = E)."""
-    if r.shape[1] <= k:
-        return np.full(r.shape[0], np.inf)
-    srt = -np.sort(-r.astype(np.float64), axis=1)
-    return srt[:, k - 1] - srt[:, k]
-
-
-def near_tie(r: np.ndarray, mc) -> np.ndarray:
-    return router_gap(r, mc.top_k) < GAP_REL[mc.dtype] * np.abs(r).max(axis=1)
-
-
-def _routing_core(mc, groute, glog, traces, tag):
-    """Routing of one pass (groute / glog: [L][requests][rows][...]) against the oracle traces.
-
-    Router logits of every row not yet flipped must match the oracle's within the
-    value tolerance (GAP_REL of the row's largest |logit|).  A row's expert set
-    may then differ from the oracle's only where the oracle's gap between its
-    k-th and (k+1)-th router logits is at most twice the row's measured logit
-    discrepancy (the largest |GPU - oracle| over its experts, itself within that
-    tolerance): an expert swap needs the two logits to move past each other,
-    and each moved by at most that much.  A row that flipped in an earlier layer
-    carries other values from then on and is not checked again.  At most
-    MAX_FLIP_FRAC of the rows may flip.  Returns the flipped rows."""
-    nreq, n = groute.shape[1], groute.shape[2]
-    flipped = np.zeros((nreq, n), bool)
-    drift_max, drift_rel_max, drift_med, n_flip = 0.0, 0.0, [], 0
-    tol = GAP_REL[mc.dtype]
-    for l in range(mc.n_layers):
-        for j in range(nreq):
-            r = traces[j]["router_logits"][l]
-            rr = traces[j]["route_idx"][l]
-            gap = router_gap(r, mc.top_k)
-            drift_row = np.abs(glog[l, j].astype(np.float64) - r).max(axis=1)
-            scale = np.maximum(np.abs(r).max(axis=1), 1e-30)
-            live = ~flipped[j]
-            rel = drift_row / scale
-            assert (rel[live] <= tol).all(), (f"{tag} layer {l}: router logits beyond {tol} of the row scale "
-                                              f"(max {rel[live].max():.3e}, rows {np.nonzero(live & (rel > tol))[0][:5]})")
-            flip = np.array([set(groute[l, j, i]) != set(rr[i]) for i in range(n)])
-            bad = flip & (gap > 2.0 * drift_row * (1 + 1e-6)) & live
-            assert not bad.any(), (f"{tag} layer {l}: routing differs where the oracle gap {gap[bad][:5]} exceeds "
-                                   f"twice the measured drift {drift_row[bad][:5]} (rows {np.nonzero(bad)[0][:5]})")
-            clean = live & ~flip
-            if clean.any():
-                drift_max = max(drift_max, float(drift_row[clean].max()))
-                drift_rel_max = max(drift_rel_max, float(rel[clean].max()))
-                drift_med.append(float(np.median(drift_row[clean])))
-            n_flip += int((flip & live).sum())
-            flipped[j] |= flip
-    log(f"[{tag}] routing flips {n_flip} (rows {int(flipped.sum())} of {flipped.size}, "
-        f"{flipped.mean():.3f}), each within twice its row's measured drift; router drift max {drift_max:.2e} "
-        f"({drift_rel_max:.2e} of the row scale) median {np.median(drift_med):.2e}")
-    assert flipped.mean() <= MAX_FLIP_FRAC, f"{tag}: {flipped.mean():.3f} of the rows flipped routing"
-    return flipped
-
-
-def check_routing(mc, eng, traces, rows_per_req, tag):
-    """Per-layer routing of the last pass against the oracle traces (see _routing_core)."""
-    B = len(traces)
-    groute = eng.route_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
-    glog = eng.router_logits_view(B * rows_per_req).cpu().numpy().reshape(mc.n_layers, B, rows_per_req, -1)
-    return _routing_core(mc, groute, glog, traces, tag)
-
-
-def _compare_step(mc, got, ref, tag, taint):
+def _compare_step(mc, got, ref, tag):
     tol = tol_for(mc)
     gl = got["logits"].reshape(-1, mc.vocab)
     rl = ref["logits"].reshape(-1, mc.vocab)
@@ -136,25 +69,23 @@ def _compare_step(mc, got, ref, tag, taint):
     inv_t = float(ref["inv_t"])
     dz = (np.abs(gl.astype(np.float64) - rl) * inv_t).max(axis=1).reshape(got["y"].shape)
     exempt = ref["margin"] < np.maximum(MARGIN_EXEMPT, 2 * dz)
-    ok = ~taint
     y_bad = (got["y"] != ref["y"]) & ~exempt
     am_bad = got["am"] != ref["am"]
-    log(f"[{tag}] logits rel err max {e_log[ok.ravel()].max():.3e} (all rows {e_log.max():.3e}) "
-        f"median {np.median(e_log):.3e}; H rel err max {e_H[ok].max():.3e}; y mismatches "
-        f"{int((got['y'] != ref['y']).sum())} (non-exempt {int((y_bad & ok).sum())}, exempt margin "
-        f"max {float(np.maximum(MARGIN_EXEMPT, 2 * dz).max()):.1e}); argmax mismatches "
-        f"{int(am_bad.sum())}; rows with a routing flip {int(taint.sum())}")
-    assert (e_log[ok.ravel()] <= tol).all(), f"{tag}: logits beyond tol {tol}"
-    assert (e_H[ok] <= tol).all(), f"{tag}: entropies beyond tol {tol}"
-    assert not (y_bad & ok).any(), f"{tag}: sampled tokens differ beyond the margin exemption"
-    n_ex = int(((got["y"] != ref["y"]) & exempt & ok).sum())
-    assert n_ex <= MAX_EXEMPT_TOKEN_FRAC * max(int(ok.sum()), 1), f"{tag}: {n_ex} exempted token differences"
+    n_ex = int(((got["y"] != ref["y"]) & exempt).sum())
+    log(f"[{tag}] logits rel err max {e_log.max():.3e} median {np.median(e_log):.3e}; H rel err max "
+        f"{e_H.max():.3e}; y mismatches {int((got['y'] != ref['y']).sum())} (non-exempt {int(y_bad.sum())}, "
+        f"exempt threshold max {float(np.maximum(MARGIN_EXEMPT, 2 * dz).max()):.1e}); argmax mismatches "
+        f"{int(am_bad.sum())}")
+    assert (e_log <= tol).all(), f"{tag}: logits beyond tol {tol} (max {e_log.max():.3e})"
+    assert (e_H <= tol).all(), f"{tag}: entropies beyond tol {tol}"
+    assert not y_bad.any(), f"{tag}: sampled tokens differ beyond the margin exemption"
+    assert n_ex <= MAX_EXEMPT_TOKEN_FRAC * got["y"].size, f"{tag}: {n_ex} exempted token differences"
     # the logit argmax is exempt only where the top two logits are within twice
     # the row's measured logit discrepancy
     rl2 = -np.sort(-rl, axis=1)[:, :2]
     dl = np.abs(gl.astype(np.float64) - rl).max(axis=1)
     am_close = ((rl2[:, 0] - rl2[:, 1]) <= 2 * dl).reshape(am_bad.shape)
-    assert not (am_bad & ok & ~am_close).any(), f"{tag}: argmax differs"
+    assert not (am_bad & ~am_close).any(), f"{tag}: argmax differs"
     return e_log
 
 
@@ -259,48 +190,58 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
                 oracle_reqs=None, sp_max_steps=None, determinism=False):
     """GPU engine over `batch` requests against the oracle on `oracle_reqs` (default: all).
 
-    Per canvas: initial canvas bit-exact, `steps` teacher-forced denoise steps,
-    then the canvas is appended to the KV cache (early if steps < budget).
-    determinism: before the canvas commit, the canvas's steps are run again
-    from the same inputs and every output compared bit for bit."""
+    The prompt is encoded in canvas-length chunks, each compared (routing) and
+    teacher-forced at its decisions; per canvas: initial canvas bit-exact,
+    `steps` teacher-forced denoise steps, then the canvas is appended to the KV
+    cache (early if steps < budget).  determinism: before the first canvas's
+    steps, two steps are run twice from the same inputs and every output
+    compared bit for bit."""
     W = di.make_weights(mc, seed, gain_std=gain_std)
     reqs = list(range(batch)) if oracle_reqs is None else list(oracle_reqs)
     nb = len(reqs)
-    max_ctx = P + mc.canvas_len * (canvases + 1)
+    n = mc.canvas_len
+    max_ctx = P + n * (canvases + 1)
     progress(f"[{tag}] weights + engine ({mc.n_layers} layers, d {mc.d_model}, V {mc.vocab})")
     eng = make_engine(mc, W, batch, max_ctx)
     om = OracleModel(mc, W, nb, max_ctx)
     if mc.n_layers >= 8:
-        om.on_layer = lambda l: progress(f"[{tag}] oracle layer {l} done") if l % 5 == 4 else None
+        om.on_layer = lambda l: progress(f"[{tag}] oracle layer {l} done") if l % 10 == 9 else None
     prompts = di.make_prompts(mc.vocab, batch, P, seed)
     seeds = di.request_seeds(seed, batch)
     oseeds = seeds[reqs]
     eng.set_seeds(seeds)
-    ptr = [dict() for _ in range(nb)]
-    progress(f"[{tag}] oracle prompt encode ({P} tokens)")
-    om.encode_prompt(prompts[reqs], ptr)
-    eng.encode_prompt(torch.from_numpy(prompts))
-    torch.cuda.synchronize()
-    assert eng.ctx_len == om.ctx == P
     tol = tol_for(mc)
     ridx = torch.tensor(reqs, device="cuda")
 
-    def check_cache(lo, hi, traces, what, teacher=True):
+    def forced(rows, what):
+        gr, gl = gpu_routing(mc, eng, batch, rows, reqs)
+        return RouteForcing(mc, gr, gl, f"{tag} {what}")
+
+    # prompt, chunk by chunk: the GPU pass, then the oracle's pass forced at its decisions
+    for p0 in range(0, P, n):
+        ln = min(n, P - p0)
+        eng.encode_prompt(torch.from_numpy(np.ascontiguousarray(prompts[:, p0:p0 + ln])))
+        torch.cuda.synchronize()
+        rf = forced(ln, f"prompt {p0}..{p0 + ln - 1}")
+        om.route_override = rf
+        progress(f"[{tag}] oracle prompt chunk {p0}..{p0 + ln - 1}")
+        om.encode_prompt(prompts[reqs, p0:p0 + ln])
+        om.route_override = None
+        rf.finish()
+    assert eng.ctx_len == om.ctx == P
+
+    def check_cache(lo, hi, what, teacher=True):
         kc, vc = eng.kv_views()
-        near = np.zeros((nb, hi - lo), bool)
         for l in range(mc.n_layers):
             gk = kc[l, ridx, :, lo:hi].float().cpu().numpy()
             rk = om.k_cache[l][:, :, lo:hi]
             gv = vc[l, ridx, :, lo:hi].float().cpu().numpy()
             rv = om.v_cache[l][:, :, lo:hi]
-            ek = np.abs(gk - rk).max(axis=(1, 3)) / np.abs(rk).max()
-            ev = np.abs(gv - rv).max(axis=(1, 3)) / np.abs(rv).max()
-            off = (ek >= tol) | (ev >= tol)
-            log(f"[{tag}] {what} layer {l} K rel {ek[~off].max():.2e} V rel {ev[~off].max():.2e}; "
-                f"positions beyond tol {int(off.sum())}")
-            assert not (off & ~near).any(), f"{tag} {what} layer {l}: K/V differ away from router near-ties"
-            assert off.mean() <= MAX_KV_OFF_FRAC
-            near |= np.stack([near_tie(traces[b]["router_logits"][l], mc) for b in range(nb)])
+            ek = np.abs(gk - rk).max() / np.abs(rk).max()
+            ev = np.abs(gv - rv).max() / np.abs(rv).max()
+            if l == 0 or l == mc.n_layers - 1 or ek > tol or ev > tol:
+                log(f"[{tag}] {what} layer {l} K rel {ek:.2e} V rel {ev:.2e}")
+            assert ek <= tol and ev <= tol, f"{tag} {what} layer {l}: K/V beyond tol ({ek:.2e}, {ev:.2e})"
             if teacher:   # later passes start from the oracle's cache
                 dt = kc.dtype
                 for j, b in enumerate(reqs):
@@ -308,12 +249,11 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
                     vc[l, b, :, lo:hi] = torch.from_numpy(rv[j]).to(dt).cuda()
 
     if check_kv and P > 0:
-        check_cache(0, P, ptr, "prompt")
+        check_cache(0, P, "prompt")
     S = sp_max_steps or steps
     sp = di.SamplerConfig(max_steps=S, entropy_bound=0.5, stop_mode=0)
     for c in range(canvases):
-        canvas = np.stack([osmp.init_canvas(int(oseeds[j]), om.canvas_index, mc.canvas_len, mc.vocab)
-                           for j in range(nb)])
+        canvas = np.stack([osmp.init_canvas(int(oseeds[j]), om.canvas_index, n, mc.vocab) for j in range(nb)])
         eng.init_canvas()
         assert np.array_equal(eng.canvas[ridx].cpu().numpy(), canvas), f"{tag}: initial canvas {c}"
         if determinism and c == 0:
@@ -321,16 +261,19 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
         for t in range(steps):
             if mc.self_cond and t > 0:
                 eng.self_cond_view()[ridx] = torch.from_numpy(om.s.astype(np.float32)).cuda()
-            ref = om.denoise_step(canvas, t, sp, oseeds, want_logits=True, trace_requests=list(range(nb)))
-            logits = torch.empty(batch, mc.canvas_len, mc.vocab, dtype=torch.float32, device="cuda")
+            logits = torch.empty(batch, n, mc.vocab, dtype=torch.float32, device="cuda")
             eng.denoise_step(t, sp, logits=logits)
             torch.cuda.synchronize()
             got = {"H": eng.H[ridx].cpu().numpy(), "y": eng.y[ridx].cpu().numpy(),
                    "am": eng.am[ridx].cpu().numpy(), "margin": eng.margin[ridx].cpu().numpy(),
                    "logits": logits[ridx].cpu().numpy()}
-            traces = [ref["traces"][j] for j in range(nb)]
-            taint = check_routing_subset(mc, eng, traces, reqs, batch, f"{tag} canvas {c} step {t}")
-            _compare_step(mc, got, ref, f"{tag} canvas {c} step {t}", taint)
+            del logits
+            rf = forced(n, f"canvas {c} step {t}")
+            om.route_override = rf
+            ref = om.denoise_step(canvas, t, sp, oseeds, want_logits=True)
+            om.route_override = None
+            rf.finish()
+            _compare_step(mc, got, ref, f"{tag} canvas {c} step {t}")
             if mc.self_cond:
                 # s = sum_v p_v E_v.  A logit discrepancy dz (max over the row, z units) perturbs the terms by
                 # relative amounts up to ~dz; summed with cancellation that moves s by about dz * sqrt(sum_v p_v^2 E_v^2)
@@ -342,9 +285,9 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
                 bound = tol * np.abs(rs).max(axis=1, keepdims=True) + 4.0 * dz.reshape(-1, 1) * ref["s_rms"].reshape(-1, mc.d_model)
                 ratio = (np.abs(gs - rs) / bound).max(axis=1)
                 es = rel_err_rows(gs, rs)
-                log(f"[{tag} canvas {c} step {t}] self-cond: max |ds| / bound {ratio[~taint.ravel()].max():.3f}; "
-                    f"rel err max {es[~taint.ravel()].max():.3e}")
-                assert ratio[~taint.ravel()].max() <= 1.0
+                log(f"[{tag} canvas {c} step {t}] self-cond: max |ds| / bound {ratio.max():.3f}; "
+                    f"rel err max {es.max():.3e}")
+                assert ratio.max() <= 1.0
             # commit on the oracle's entropies (GPU's own for requests the oracle does not run)
             Hf, yf, amf = eng.H.clone(), eng.y.clone(), eng.am.clone()
             Hf[ridx] = torch.from_numpy(ref["H"]).cuda()
@@ -359,16 +302,19 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
             canvas = new_canvas
             torch.cuda.synchronize()
             assert np.array_equal(eng.canvas[ridx].cpu().numpy(), canvas)
-        # the canvas enters the cache
+            del ref
+        # the canvas enters the cache: the GPU pass, then the oracle's forced at its decisions
         lo = om.ctx
-        ctr = [dict() for _ in range(nb)]
-        om.commit_canvas_to_kv(canvas, ctr)
         eng.commit_canvas_to_kv()
         torch.cuda.synchronize()
+        rf = forced(n, f"canvas {c} commit")
+        om.route_override = rf
+        om.commit_canvas_to_kv(canvas)
+        om.route_override = None
+        rf.finish()
         assert eng.ctx_len == om.ctx and eng.canvas_index == om.canvas_index == c + 1
         if check_kv:
-            check_routing_subset(mc, eng, ctr, reqs, batch, f"{tag} canvas {c} commit")
-            check_cache(lo, lo + mc.canvas_len, ctr, f"canvas {c} commit")
+            check_cache(lo, lo + n, f"canvas {c} commit")
     eng.close()
 
 
@@ -405,14 +351,6 @@ def _check_determinism(torch, eng, sp, steps, tag):
     eng.canvas.copy_(c0)
     eng.self_cond_view().copy_(s0)
     eng.done.zero_()
-
-
-def check_routing_subset(mc, eng, traces, reqs, batch, tag):
-    """check_routing for an oracle that runs a subset of the GPU's requests."""
-    n = mc.canvas_len
-    groute = eng.route_view(batch * n).cpu().numpy().reshape(mc.n_layers, batch, n, -1)[:, reqs]
-    glog = eng.router_logits_view(batch * n).cpu().numpy().reshape(mc.n_layers, batch, n, -1)[:, reqs]
-    return _routing_core(mc, groute, glog, traces, tag)
 
 
 def _scaled(arr, mc, s):
