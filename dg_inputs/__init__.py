@@ -51,6 +51,7 @@ class ModelConfig:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     canvas_len: int = 256
+    expert_dtype: str = ""   # "" = dtype; "fp8": experts served as OCP FP8 E4M3 with per-channel scales
 
     def n_params(self) -> int:
         d, L = self.d_model, self.n_layers
@@ -108,6 +109,12 @@ WORKLOADS: Dict[str, Workload] = {
     # 32 concurrent requests with 4096-token prompts, small model.
     "batched": Workload("batched", _SMALL, SamplerConfig(48, 0.1, STOP_MEAN, 0.05),
                         prompt_len=4096, batch=32, canvases=1, seed=1),
+    # The proxy and small workloads with their experts served in FP8 (the same
+    # seeded bf16 weights, quantised per output channel by the model).
+    "proxy-fp8": Workload("proxy-fp8", dataclasses.replace(_PROXY, expert_dtype="fp8"),
+                          SamplerConfig(48, 0.1, STOP_MEAN, 0.05), prompt_len=2048, batch=1, canvases=1, seed=2),
+    "small-fp8": Workload("small-fp8", dataclasses.replace(_SMALL, expert_dtype="fp8"), SamplerConfig(24, 0.1),
+                          prompt_len=512, batch=1, canvases=1, seed=1),
 }
 
 

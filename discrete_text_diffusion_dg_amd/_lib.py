@@ -22,6 +22,9 @@ DG_ERR_HIP = -3
 DG_ERR_UNSUPPORTED = -4
 DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
+DG_DTYPE_FP8_E4M3 = 2
+(DG_MODEL_VIEW_EXPERT_GATEUP, DG_MODEL_VIEW_EXPERT_DOWN, DG_MODEL_VIEW_EXPERT_SCALES_GATEUP,
+ DG_MODEL_VIEW_EXPERT_SCALES_DOWN) = range(4)
 (DG_VIEW_K_CACHE, DG_VIEW_V_CACHE, DG_VIEW_SELF_COND, DG_VIEW_PREV_ARGMAX, DG_VIEW_ROUTE,
  DG_VIEW_HIDDEN, DG_VIEW_ROUTER_LOGITS, DG_VIEW_ATTN_OUT, DG_VIEW_CTX_LENS, DG_VIEW_CANVAS_INDEX) = range(10)
 DG_RUN_GRAPH, DG_RUN_EARLY_EXIT, DG_RUN_COMMIT_KV = 1, 2, 4
@@ -29,7 +32,7 @@ STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "exper
           "lm_head", "sampler", "selfcond", "commit"]
 
 EXPORTS = [
-    "dg_last_error", "dg_weight_count", "dg_model_create", "dg_model_destroy", "dg_state_bytes",
+    "dg_last_error", "dg_weight_count", "dg_model_create", "dg_model_destroy", "dg_model_view", "dg_state_bytes",
     "dg_state_init", "dg_state_destroy", "dg_state_ctx_len", "dg_state_canvas_index", "dg_state_view",
     "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
     "dg_sample_commit",
@@ -41,7 +44,7 @@ class DgConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "ffn_hidden",
         "top_k", "vocab", "canvas_len", "dtype", "self_cond")] + [
-        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("expert_dtype", ctypes.c_int32)]
 
 
 class DgSamplerParams(ctypes.Structure):
@@ -74,6 +77,7 @@ def load() -> ctypes.CDLL:
     lib.dg_weight_count.restype = i32
     lib.dg_model_create.argtypes = [ctypes.POINTER(DgConfig), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]
     lib.dg_model_destroy.argtypes = [vp]
+    lib.dg_model_view.argtypes = [vp, i32, i32, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_size_t)]
     lib.dg_model_destroy.restype = None
     lib.dg_state_bytes.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.dg_state_init.argtypes = [vp, vp, ctypes.c_size_t, i32, i32, ctypes.POINTER(vp)]
@@ -98,7 +102,7 @@ def load() -> ctypes.CDLL:
                                   i32, i32, ctypes.c_uint32, ctypes.POINTER(i32), vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_uint32]
     lib.dg_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("dg_model_create", "dg_state_bytes", "dg_state_init", "dg_state_view", "dg_init_canvas",
+    for name in ("dg_model_create", "dg_model_view", "dg_state_bytes", "dg_state_init", "dg_state_view", "dg_init_canvas",
                  "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
                  "dg_sample_commit",
                  "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_profile_enable", "dg_profile_read"):

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <string>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "dg_kernels.h"
@@ -54,10 +55,13 @@ struct LayerW {
   void* wqkv;   // owned slice of dg_model::qkv_buf: [(Hq + 2 Hkv) hd, d]
   void* pgu;    // owned slice of dg_model::pack_buf: fragment-packed gate/up (or null)
   void* pd;     // owned slice of dg_model::pack_buf: fragment-packed down (or null)
+  float* sgu;   // FP8 experts: gate/up channel scales [E][2][F] (slice of pack_buf)
+  float* sd;    // FP8 experts: down channel scales [E][d]
 };
 
 struct dg_model {
   dg_config cfg;
+  bool fp8;              // expert weights in FP8 E4M3 (packed codes and scales only)
   size_t esz;            // bytes per weight element
   const void* emb;
   const void* w_sc;
@@ -151,6 +155,10 @@ static dg_status check_config(const dg_config* c) {
   if (c->canvas_len < 1 || c->canvas_len > 256) return fail(DG_ERR_UNSUPPORTED, "canvas_len must be in 1..256");
   if (c->dtype != DG_DTYPE_F32 && c->dtype != DG_DTYPE_BF16) return fail(DG_ERR_ARG, "dtype must be F32 or BF16");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(DG_ERR_ARG, "rope_theta > 0 and rms_eps >= 0 required");
+  if (c->expert_dtype != 0 && c->expert_dtype != DG_DTYPE_FP8_E4M3)
+    return fail(DG_ERR_ARG, "expert_dtype must be 0 or DG_DTYPE_FP8_E4M3");
+  if (c->expert_dtype == DG_DTYPE_FP8_E4M3 && (c->dtype != DG_DTYPE_BF16 || !expert_stream_fp8_ok(c->d_model, c->ffn_hidden)))
+    return fail(DG_ERR_UNSUPPORTED, "FP8 experts need a bf16 model with d_model %% 512 == 0 and ffn_hidden %% 256 == 0");
   return DG_OK;
 }
 
@@ -187,6 +195,8 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     LayerW L;
     L.pgu = nullptr;
     L.pd = nullptr;
+    L.sgu = nullptr;
+    L.sd = nullptr;
     L.attn_norm = static_cast<const float*>(w[i++]);
     L.wq = w[i++]; L.wk = w[i++]; L.wv = w[i++]; L.wo = w[i++];
     L.ffn_norm = static_cast<const float*>(w[i++]);
@@ -202,8 +212,31 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     }
     m->layers.push_back(L);
   }
-  // expert weights repacked in MFMA-fragment order for the weight-streaming path
-  if (expert_stream_ok(d, cfg->ffn_hidden, (int)m->esz)) {
+  m->fp8 = cfg->expert_dtype == DG_DTYPE_FP8_E4M3;
+  if (m->fp8) {
+    // FP8 E4M3 codes (one byte per weight) and fp32 channel scales, packed per layer
+    const int E = cfg->n_experts, F = cfg->ffn_hidden;
+    const size_t codes = (size_t)3 * E * F * d, scales = (size_t)E * (2 * F + d) * 4;
+    const size_t per_layer = (codes + scales + 255) / 256 * 256;
+    e = hipMalloc(&m->pack_buf, per_layer * cfg->n_layers);
+    for (int l = 0; e == hipSuccess && l < cfg->n_layers; ++l) {
+      LayerW& L = m->layers[l];
+      char* base = static_cast<char*>(m->pack_buf) + per_layer * l;
+      L.pgu = base;
+      L.pd = base + (size_t)2 * E * F * d;
+      L.sgu = reinterpret_cast<float*>(base + codes);
+      L.sd = L.sgu + (size_t)2 * E * F;
+      e = pack_expert_weights_fp8(static_cast<const bf16*>(L.w_gate), static_cast<const bf16*>(L.w_up),
+                                  static_cast<const bf16*>(L.w_down), static_cast<fp8e4m3*>(L.pgu),
+                                  static_cast<fp8e4m3*>(L.pd), L.sgu, L.sd, E, d, F, 0);
+    }
+    if (e != hipSuccess) {
+      if (m->pack_buf) hipFree(m->pack_buf);
+      hipFree(m->qkv_buf); delete m;
+      return fail(DG_ERR_HIP, "quantising expert weights: %s", hipGetErrorString(e));
+    }
+  } else if (expert_stream_ok(d, cfg->ffn_hidden, (int)m->esz)) {
+    // expert weights repacked in MFMA-fragment order for the weight-streaming path
     const size_t per_layer = (size_t)3 * cfg->n_experts * cfg->ffn_hidden * d * m->esz;
     e = hipMalloc(&m->pack_buf, per_layer * cfg->n_layers);
     for (int l = 0; e == hipSuccess && l < cfg->n_layers; ++l) {
@@ -247,6 +280,23 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     return fail(DG_ERR_HIP, "model create: %s", hipGetErrorString(e));
   }
   *out = m;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_model_view(const dg_model* m, int32_t which, int32_t layer, void** ptr, size_t* bytes) {
+  if (!m || !ptr || !bytes) return fail(DG_ERR_ARG, "null argument");
+  const dg_config& c = m->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(DG_ERR_ARG, "layer %d outside 0..%d", layer, c.n_layers - 1);
+  const LayerW& L = m->layers[layer];
+  const size_t E = c.n_experts, F = c.ffn_hidden, d = c.d_model, es = m->fp8 ? 1 : m->esz;
+  switch (which) {
+    case DG_MODEL_VIEW_EXPERT_GATEUP: *ptr = L.pgu; *bytes = 2 * E * F * d * es; break;
+    case DG_MODEL_VIEW_EXPERT_DOWN: *ptr = L.pd; *bytes = E * F * d * es; break;
+    case DG_MODEL_VIEW_EXPERT_SCALES_GATEUP: *ptr = L.sgu; *bytes = 2 * E * F * 4; break;
+    case DG_MODEL_VIEW_EXPERT_SCALES_DOWN: *ptr = L.sd; *bytes = E * d * 4; break;
+    default: return fail(DG_ERR_ARG, "unknown model view %d", which);
+  }
+  if (*ptr == nullptr) return fail(DG_ERR_ARG, "the model holds no such copy");
   return DG_OK;
 }
 
@@ -547,7 +597,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   const int splits = attn_splits_for(st, nq, keys);
   const int cap = expert_tile_capacity(M, k, E);
   const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd);
-  const bool stream_ok = m->pack_buf != nullptr;
+  const bool stream_ok = m->pack_buf != nullptr && !m->fp8;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     T* kc = static_cast<T*>(st->kc) + st->kv_layer_elems * l;
@@ -581,8 +631,9 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     float* rlog = st->rlog + (size_t)l * st->R * E;
     int* ridx = st->ridx + (size_t)l * st->R * k;
     // weight streaming while experts see at most ~64 routed rows on average
-    // (the batch-1 shapes); the LDS-tiled engine once they see many
-    const bool stream = stream_ok && (size_t)M * k <= (size_t)64 * E;
+    // (the batch-1 shapes); the LDS-tiled engine once they see many; FP8
+    // experts always stream (their codes feed the bf16 MFMA from registers)
+    const bool stream = m->fp8 || (stream_ok && (size_t)M * k <= (size_t)64 * E);
     const int tile_rows = stream ? 64 : expert_group_tile_rows(d, F, m->esz);
     if (router_fused_ok(M, d, E, k)) {
       // few routed entries: the norm's workgroups form the router logits, top-k
@@ -611,18 +662,26 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
     }
     {
       StageTimer tm(st, DG_STAGE_EXPERT_UP, s);
-      if (stream)
-        DG_HIP(expert_stream_gateup<T>(xn, st->perm, static_cast<const T*>(L.pgu), static_cast<T*>(st->act),
-                                       st->tiles, st->n_tiles, cap, d, F, s));
+      if (m->fp8) {
+        if constexpr (std::is_same<T, bf16>::value)
+          DG_HIP((expert_stream_gateup<T, fp8e4m3>(xn, st->perm, static_cast<const fp8e4m3*>(L.pgu), L.sgu,
+                                                  static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s)));
+      } else if (stream)
+        DG_HIP((expert_stream_gateup<T, T>(xn, st->perm, static_cast<const T*>(L.pgu), nullptr,
+                                          static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s)));
       else
         DG_HIP(gemm_expert_gateup<T>(xn, st->perm, static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up),
                                      static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s));
     }
     {
       StageTimer tm(st, DG_STAGE_EXPERT_DOWN, s);
-      if (stream)
-        DG_HIP(expert_stream_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.pd), st->y,
-                                     st->tiles, st->n_tiles, cap, d, F, s));
+      if (m->fp8) {
+        if constexpr (std::is_same<T, bf16>::value)
+          DG_HIP((expert_stream_down<T, fp8e4m3>(static_cast<const T*>(st->act), static_cast<const fp8e4m3*>(L.pd),
+                                                L.sd, st->y, st->tiles, st->n_tiles, cap, d, F, s)));
+      } else if (stream)
+        DG_HIP((expert_stream_down<T, T>(static_cast<const T*>(st->act), static_cast<const T*>(L.pd), nullptr, st->y,
+                                        st->tiles, st->n_tiles, cap, d, F, s)));
       else
         DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), st->y,
                                    st->tiles, st->n_tiles, cap, d, F, s));

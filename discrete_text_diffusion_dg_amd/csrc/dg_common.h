@@ -12,6 +12,12 @@ struct bf16 {
   uint16_t bits;
 };
 
+// OCP FP8 E4M3 storage (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// no infinities, largest finite 448): expert weights of FP8 models.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -26,6 +32,38 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.f); }
+
+// Eight E4M3 values (bytes of w0, then w1) -> eight bf16 (an MFMA fragment):
+// the gfx950 converter takes two bytes to two fp32 values, which bf16 holds
+// exactly (every E4M3 value has at most 4 significant bits).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  return make_uint4(f32x2_to_bf16x2(a[0], a[1]), f32x2_to_bf16x2(b[0], b[1]), f32x2_to_bf16x2(c[0], c[1]),
+                    f32x2_to_bf16x2(d[0], d[1]));
+}
+
+// fp32 -> E4M3 code, round to nearest even, saturating at +-448 (the OCP
+// specification's saturating conversion; inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (!(a <= 448.f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {                     // below 2^-6: subnormal steps of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.f);  // exact scaling, ties to even; 8 is the smallest normal
+  } else {
+    const uint32_t au = __float_as_uint(a);
+    int e = (int)(au >> 23) - 127;                // -6 .. 8
+    uint32_t m3 = (au >> 20) & 7u;
+    const uint32_t rest = au & 0xFFFFFu;          // the 20 bits rounded away
+    if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) { m3 = 0; ++e; }
+    code = e > 8 ? 0x7Eu : ((uint32_t)(e + 7) << 3) | m3;
+  }
+  return sign | code;
+}
 
 template <typename T> struct Num;
 template <> struct Num<float> {

@@ -134,12 +134,21 @@ bool expert_stream_ok(int d, int F, int elem_bytes);
 template <typename T>
 hipError_t pack_expert_weights(const T* gate, const T* up, const T* down, T* pgu, T* pd, int E, int d, int F,
                                hipStream_t s);
-template <typename T>
-hipError_t expert_stream_gateup(const T* X, const int* perm, const T* pgu, T* act, const int4* tiles,
-                                const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
-template <typename T>
-hipError_t expert_stream_down(const T* act, const T* pd, float* Y, const int4* tiles, const int* n_tiles,
-                              int cap_tiles, int d, int F, hipStream_t s);
+// FP8 (OCP E4M3) experts: per output channel scales sgu [E][2][F] (gate, up)
+// and sd [E][d], fl32(fl64(max |w|) / 448); codes E4M3(w / scale) packed as
+// P8GU[E][F/16][d/64][2][64][16 B] and P8D[E][d/16][F/64][64][16 B] (two
+// 32-wide K steps per lane piece).  WT = fp8e4m3 selects them in the streaming
+// products (the scales multiply the sums); WT = T the plain packed weights
+// (scale unused).
+bool expert_stream_fp8_ok(int d, int F);
+hipError_t pack_expert_weights_fp8(const bf16* gate, const bf16* up, const bf16* down, fp8e4m3* pgu, fp8e4m3* pd,
+                                   float* sgu, float* sd, int E, int d, int F, hipStream_t s);
+template <typename T, typename WT>
+hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, const float* scale, T* act,
+                                const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
+template <typename T, typename WT>
+hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, float* Y, const int4* tiles,
+                              const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
 // part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of
 // rnd(P[r][k] * scale[r][k / 128]) * Bt[c][k]   (P: [M][K], scale: [M][nchunk], Bt: [N][K])
 template <typename T>

@@ -22,11 +22,25 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _copy_to_host(ptr: int, nbytes: int) -> np.ndarray:
+    """Bytes of device memory the library owns, copied to the host (hipMemcpy of the HIP runtime torch loaded)."""
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    out = np.empty(nbytes, np.uint8)
+    torch.cuda.synchronize()
+    rc = hip.hipMemcpy(out.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(ptr), nbytes, 2)   # device to host
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed with {rc}")
+    return out
+
+
 def config_struct(mc) -> L.DgConfig:
     return L.DgConfig(mc.n_layers, mc.d_model, mc.n_q_heads, mc.n_kv_heads, mc.head_dim, mc.n_experts,
                       mc.ffn_hidden, mc.top_k, mc.vocab, mc.canvas_len,
                       L.DG_DTYPE_BF16 if mc.dtype == "bf16" else L.DG_DTYPE_F32,
-                      1 if mc.self_cond else 0, mc.rope_theta, mc.rms_eps)
+                      1 if mc.self_cond else 0, mc.rope_theta, mc.rms_eps,
+                      L.DG_DTYPE_FP8_E4M3 if getattr(mc, "expert_dtype", "") == "fp8" else 0)
 
 
 def sampler_struct(sp) -> L.DgSamplerParams:
@@ -156,6 +170,13 @@ class Engine:
         c = self.cfg
         t = self.view(L.DG_VIEW_ROUTE, torch.int32, (c.n_layers, self.B * self.n, c.top_k))
         return t[:, :rows]
+
+    def model_view(self, which: int, layer: int) -> np.ndarray:
+        """Host copy (raw bytes) of one of the model's derived weight copies (dg_model_view)."""
+        p = ctypes.c_void_p()
+        nb = ctypes.c_size_t()
+        L.check(self.lib.dg_model_view(self._model, which, layer, ctypes.byref(p), ctypes.byref(nb)))
+        return _copy_to_host(p.value, nb.value)
 
     # ------------------------------------------------------------ stage timing
     def profile(self, stages) -> None:

@@ -52,6 +52,7 @@ typedef int32_t dg_status;
 
 #define DG_DTYPE_F32 0
 #define DG_DTYPE_BF16 1
+#define DG_DTYPE_FP8_E4M3 2   /* expert weights only: OCP FP8 E4M3 with one fp32 scale per output channel */
 
 #define DG_STOP_NONE 0    /* run the whole step budget */
 #define DG_STOP_MEAN 1    /* stop once the mean canvas entropy < stop_tau */
@@ -72,6 +73,16 @@ typedef struct dg_config {
   int32_t self_cond;    /* 1: add (softmax of the previous step) @ E @ W_sc^T to the embeddings */
   float rope_theta;
   float rms_eps;
+  /* Storage of the expert weights: 0 = dtype; DG_DTYPE_FP8_E4M3 (bf16 models
+   * with d_model % 512 == 0 and ffn_hidden % 256 == 0): dg_model_create
+   * quantises the caller's bf16 experts to OCP FP8 E4M3 (chooseai.io speed
+   * paragraph and bohuyeshan.top 一: the model is served in FP8), one fp32
+   * scale per output channel, scale = fl32(fl64(max |w_row|) / 448) (1 for a
+   * zero row), code = E4M3(fl32(w / scale)) rounded to nearest even and
+   * saturating; the expert products then use code * scale.  The model keeps
+   * only the packed codes and scales (3 E F d bytes + (2 F + d) E 4 bytes per
+   * layer); every batch runs the weight-streaming expert products. */
+  int32_t expert_dtype;
 } dg_config;
 
 typedef struct dg_sampler_params {
@@ -89,6 +100,22 @@ typedef struct ihipStream_t* dg_stream;   /* a hipStream_t; NULL = default strea
 
 /* Thread-local text of the last failure in this thread ("" if none). */
 const char* dg_last_error(void);
+
+/* Device views into a model's derived weights, for inspection:
+ *   DG_MODEL_VIEW_EXPERT_GATEUP: layer `layer`'s packed gate/up expert weights
+ *   DG_MODEL_VIEW_EXPERT_DOWN:   its packed down weights
+ *     (FP8: codes P8GU[E][F/16][d/64][2][64][16], P8D[E][d/16][F/64][64][16],
+ *     lane (c, g) of block (n/16, k/64) holding W[n][k0 + g*8 .. +8] then
+ *     W[n][k0 + 32 + g*8 .. +8]; else the dtype's fragments
+ *     [E][F/16][d/32][2][64][8] and [E][d/16][F/32][64][8])
+ *   DG_MODEL_VIEW_EXPERT_SCALES_GATEUP: FP8 only, float [E][2][F] (gate, up)
+ *   DG_MODEL_VIEW_EXPERT_SCALES_DOWN:   FP8 only, float [E][d]
+ * DG_ERR_ARG if the model holds no such copy. */
+#define DG_MODEL_VIEW_EXPERT_GATEUP 0
+#define DG_MODEL_VIEW_EXPERT_DOWN 1
+#define DG_MODEL_VIEW_EXPERT_SCALES_GATEUP 2
+#define DG_MODEL_VIEW_EXPERT_SCALES_DOWN 3
+dg_status dg_model_view(const dg_model* model, int32_t which, int32_t layer, void** d_ptr, size_t* bytes);
 
 /* Number of weight pointers dg_model_create expects for a config:
  * 2 + self_cond + 10 * n_layers. */

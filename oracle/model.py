@@ -31,6 +31,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
+from . import fp8
 from . import numerics as nm
 from . import sampler as smp
 
@@ -53,6 +54,8 @@ class OracleModel:
         # is asked for each tensor once per pass
         self._raw: Dict[str, np.ndarray] = {}
         self._raw_layer = None
+        self._fp8: Dict[tuple, np.ndarray] = {}      # dequantised FP8 experts of the layer in use
+        self._fp8_layer = None
         self.on_layer = None      # optional callback(layer) after each layer (progress of long runs)
         # optional callback(request, layer, router logits r, top-k ids) -> ids: lets a
         # test impose another expert choice on rows whose own top-k is a near tie
@@ -86,6 +89,18 @@ class OracleModel:
 
     def expert(self, layer: int, kind: str, e: int) -> np.ndarray:
         name = f"l{layer}.{kind}"
+        if getattr(self.cfg, "expert_dtype", "") == "fp8":
+            # FP8 experts: the E4M3 codes of each output channel times its scale
+            # (oracle/fp8.py), from the stored bf16 weights
+            key = (name, int(e))
+            if key not in self._fp8:
+                if self._fp8_layer != layer:
+                    self._fp8 = {}
+                    self._fp8_layer = layer
+                w = nm.upcast(self._stored(name)[e] if not self._cache_f64 else self.w.get(name)[e])
+                q, s = fp8.quantize_rows(w.astype(np.float32))
+                self._fp8[key] = fp8.dequantize_rows(q, s)
+            return self._fp8[key]
         if self._cache_f64:
             return self.W(name)[e]
         return nm.upcast(self._stored(name)[e])

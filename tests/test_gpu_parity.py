@@ -554,3 +554,52 @@ def test_commit_and_stop_from_peaked_logits(torch_cuda):
     assert done[0] == 1 and n_com[0] == n          # stopped: every position takes y
     assert 0 < n_com[1] < n and done[1] == 0       # partial commit under the 0.1 nat bound
     assert n_com[2] == 0 and done[2] == 0
+
+
+# ------------------------------------------------------------------ FP8 experts
+def _unpack_fp8(raw, E, N, K, nf):
+    """Codes [E][nf][N][K] from the packed layout [E][N/16][K/64][nf][64 lanes][16 bytes]."""
+    a = raw.reshape(E, N // 16, K // 64, nf, 4, 16, 2, 8)       # lane = g * 16 + c; bytes = half * 8 + j
+    # -> [E][nf][N/16][c][K/64][half][g][j]: row n = nb * 16 + c, k = ks * 64 + half * 32 + g * 8 + j
+    a = a.transpose(0, 3, 1, 5, 2, 6, 4, 7)
+    return a.reshape(E, nf, N, K)
+
+
+def test_fp8_expert_quantisation_bit_exact(torch_cuda):
+    # the model's E4M3 codes and channel scales equal the oracle's quantisation of the same bf16 weights
+    from discrete_text_diffusion_dg_amd import _lib as L
+    from oracle import fp8
+    mc = micro(n_layers=2, d_model=512, ffn_hidden=256, n_experts=8, top_k=2, vocab=2048, expert_dtype="fp8")
+    W = di.make_weights(mc, 51, gain_std=0.1)
+    eng = make_engine(mc, W, 1, 512)
+    E, F, d = mc.n_experts, mc.ffn_hidden, mc.d_model
+    for l in range(mc.n_layers):
+        gu = _unpack_fp8(eng.model_view(L.DG_MODEL_VIEW_EXPERT_GATEUP, l), E, F, d, 2)
+        dn = _unpack_fp8(eng.model_view(L.DG_MODEL_VIEW_EXPERT_DOWN, l), E, d, F, 1)[:, 0]
+        sgu = eng.model_view(L.DG_MODEL_VIEW_EXPERT_SCALES_GATEUP, l).view(np.float32).reshape(E, 2, F)
+        sd = eng.model_view(L.DG_MODEL_VIEW_EXPERT_SCALES_DOWN, l).view(np.float32).reshape(E, d)
+        for j, name in enumerate(("w_gate", "w_up")):
+            q, s = fp8.quantize_rows(nm.upcast(W.get(f"l{l}.{name}")).astype(np.float32))
+            assert np.array_equal(sgu[:, j].view(np.uint32), s.view(np.uint32)), f"layer {l} {name} scales"
+            assert np.array_equal(gu[:, j], q), f"layer {l} {name} codes ({int((gu[:, j] != q).sum())} differ)"
+        q, s = fp8.quantize_rows(nm.upcast(W.get(f"l{l}.w_down")).astype(np.float32))
+        assert np.array_equal(sd.view(np.uint32), s.view(np.uint32)), f"layer {l} down scales"
+        assert np.array_equal(dn, q), f"layer {l} down codes"
+    log(f"[fp8] codes and scales of {mc.n_layers} layers x {E} experts bit-identical to the oracle's quantisation")
+    eng.close()
+
+
+def test_fp8_micro_experts_parity(torch_cuda):
+    mc = micro(n_layers=2, d_model=512, ffn_hidden=256, n_experts=8, top_k=2, vocab=2048, expert_dtype="fp8")
+    _run_parity(torch_cuda, mc, 52, 300, 2, 2, "fp8-micro", gain_std=0.1, determinism=True)
+
+
+def test_fp8_small_workload(torch_cuda):
+    wl = di.workload("small-fp8")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 2, "fp8-small")
+
+
+def test_fp8_proxy_shapes_two_layers(torch_cuda):
+    # the proxy's expert shapes (128 experts top-8, d 2048, F 768) in FP8, 2 of its 30 layers
+    mc = replace(di.workload("proxy-fp8").model, n_layers=2)
+    _run_parity(torch_cuda, mc, 2, 256, 1, 1, "fp8-proxy-2L", sp_max_steps=48)

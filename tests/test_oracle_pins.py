@@ -591,3 +591,65 @@ def test_random_weights_never_commit_or_stop():
     sp = di.SamplerConfig(max_steps=3, entropy_bound=0.5, stop_mode=1, stop_tau=0.05)
     res = run_canvas(m, sp, seeds)
     assert [int(s["n_committed"][0]) for s in res["steps"]] == [0, 0, 256]
+
+
+# ------------------------------------------------------------------ FP8 (OCP E4M3)
+def test_e4m3_hand_listed_codes():
+    from oracle import fp8
+    # (value, code) pairs written out from the format: bias 7, 3 mantissa bits
+    cases = [(0.0, 0x00), (1.0, 0x38), (-1.0, 0xB8), (0.5, 0x30), (1.125, 0x39), (1.75, 0x3E), (2.0, 0x40),
+             (448.0, 0x7E), (-448.0, 0xFE), (256.0, 0x78), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01),
+             (7 * 2.0 ** -9, 0x07), (1.75 * 2.0 ** -6, 0x0E), (1.875 * 2.0 ** -6, 0x0F), (240.0, 0x77)]
+    for v, c in cases:
+        assert int(fp8.encode(np.array([v]))[0]) == c, (v, hex(c))
+        assert fp8.decode(np.array([c], np.uint8))[0] == v, (v, hex(c))
+    # NaN codes; -0
+    assert np.isnan(fp8.decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    assert int(fp8.encode(np.array([-0.0]))[0]) == 0x80
+
+
+def test_e4m3_round_to_nearest_even_and_saturation():
+    from oracle import fp8
+    cases = [(1.0625, 0x38),          # halfway 1.0 / 1.125 -> even mantissa 0
+             (1.1875, 0x3A),          # halfway 1.125 / 1.25 -> even mantissa 2
+             (1.06, 0x38), (1.07, 0x39), (1.1, 0x39),
+             (2.0 ** -10, 0x00),      # halfway 0 / 2^-9 -> 0
+             (3 * 2.0 ** -10, 0x02),  # halfway 2^-9 / 2^-8 -> even mantissa 2
+             (15.5 * 2.0 ** -10, 0x08),  # halfway 7 * 2^-9 / 2^-6 -> even: the smallest normal
+             (464.0, 0x7E), (500.0, 0x7E), (1e9, 0x7E), (-1e9, 0xFE),   # saturate, never NaN
+             (0.9999999, 0x38), (447.9, 0x7E), (432.0, 0x7E), (431.0, 0x7D)]
+    for v, c in cases:
+        assert int(fp8.encode(np.array([v]))[0]) == c, (v, hex(int(fp8.encode(np.array([v]))[0])), hex(c))
+
+
+def test_e4m3_round_trip_and_nearest():
+    from oracle import fp8
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = fp8.decode(codes)
+    # every finite code survives decode -> encode (the zero pair aside, -0 keeps its sign bit)
+    assert np.array_equal(fp8.encode(vals), codes)
+    # brute force: random values map to the nearest representable value (ties to even code)
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(20000) * 50
+    pos = np.sort(np.unique(np.abs(vals)))
+    got = np.abs(fp8.decode(fp8.encode(x)))
+    a = np.minimum(np.abs(x), 448.0)
+    best = pos[np.argmin(np.abs(pos[None, :] - a[:, None]), axis=1)]
+    assert np.array_equal(got, best)
+
+
+def test_e4m3_row_quantisation():
+    from oracle import fp8
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((6, 40)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    q, s = fp8.quantize_rows(w)
+    # the largest magnitude of a row maps to 448 (or just below it by the fp32 division)
+    assert s[3] == 1.0 and (q[3] == 0).all()
+    for r in (0, 1, 2, 4, 5):
+        assert s[r] == np.float32(np.abs(w[r]).max() / 448.0)
+        assert np.abs(fp8.decode(q[r])).max() == 448.0
+    deq = fp8.dequantize_rows(q, s)
+    # relative error of a quantised weight: at most half an ulp of 3 mantissa bits (1/16) above the subnormals
+    big = np.abs(w) >= 2.0 ** -6 * s[:, None]
+    assert (np.abs(deq - w)[big] <= np.abs(w)[big] / 16 + 1e-12).all()
