@@ -25,6 +25,7 @@ The CPU baseline is the oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -65,11 +66,14 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
     d, F, k, V = mc.d_model, mc.ffn_hidden, mc.top_k, mc.vocab
     hd, Hq, Hkv = mc.head_dim, mc.n_q_heads, mc.n_kv_heads
     keys = ctx + n
+    # expert weight bytes per element: 1 for FP8 codes (plus one fp32 scale per output channel)
+    fp8 = getattr(mc, "expert_dtype", "") == "fp8"
+    wes = 1 if fp8 else es
     if stage == "expert_up":
-        by = n_experts_active * 2 * F * d * es + R * d * es + R * k * F * es
+        by = n_experts_active * (2 * F * d * wes + (2 * F * 4 if fp8 else 0)) + R * d * es + R * k * F * es
         fl = 2 * R * k * d * F * 2
     elif stage == "expert_down":
-        by = n_experts_active * d * F * es + R * k * F * es + R * k * d * 4
+        by = n_experts_active * (d * F * wes + (d * 4 if fp8 else 0)) + R * k * F * es + R * k * d * 4
         fl = 2 * R * k * F * d
     elif stage == "lm_head":     # with the head statistics in its epilogue: writes P~ and the chunk records
         by = V * d * es + R * d * es + (R * V * es if mc.self_cond else 0) + R * ((V + 127) // 128) * 32
@@ -228,7 +232,7 @@ class Runner:
     committed to the KV cache by the same call, and the next call starts a new
     canvas."""
 
-    def __init__(self, wl, steps: int, warmup: int):
+    def __init__(self, wl, steps: int, warmup: int, device_weights=None):
         import torch
         from discrete_text_diffusion_dg_amd.runtime import Engine, upload_weights
         self.torch = torch
@@ -241,15 +245,19 @@ class Runner:
         t0 = time.perf_counter()
         W = di.make_weights(mc, wl.seed, cache=False)       # streamed: generated, uploaded, dropped
         names = W.names()
-        dw, done_b, next_log = {}, 0, 4e9
-        for nm_ in names:
-            dw.update(upload_weights(W, [nm_], "cuda"))
-            done_b += dw[nm_].numel() * dw[nm_].element_size()
-            if done_b >= next_log:
-                log(f"[bench] {wl.name}: {done_b / 1e9:.1f} of {W.nbytes() / 1e9:.1f} GB of weights on the device")
-                next_log += 4e9
-        log(f"[bench] {wl.name}: weights {W.nbytes() / 1e9:.2f} GB generated+uploaded in "
-            f"{time.perf_counter() - t0:.1f} s")
+        if device_weights is not None:                      # the same seeded weights, already on the device
+            dw = device_weights
+        else:
+            dw, done_b, next_log = {}, 0, 4e9
+            for nm_ in names:
+                dw.update(upload_weights(W, [nm_], "cuda"))
+                done_b += dw[nm_].numel() * dw[nm_].element_size()
+                if done_b >= next_log:
+                    log(f"[bench] {wl.name}: {done_b / 1e9:.1f} of {W.nbytes() / 1e9:.1f} GB of weights on the device")
+                    next_log += 4e9
+            log(f"[bench] {wl.name}: weights {W.nbytes() / 1e9:.2f} GB generated+uploaded in "
+                f"{time.perf_counter() - t0:.1f} s")
+        self.weights = dw
         self.eng = Engine(mc, dw, names, self.B, max_ctx)
         self.eng.set_seeds(di.request_seeds(wl.seed, self.B))
         prompts = torch.from_numpy(di.make_prompts(mc.vocab, self.B, wl.prompt_len, wl.seed)).cuda()
@@ -282,10 +290,10 @@ class Runner:
         self.torch.cuda.empty_cache()
 
 
-def measure(wl, steps: int, warmup: int, stage_detail: bool, graph: bool = True):
+def measure(wl, steps: int, warmup: int, stage_detail: bool, graph: bool = True, device_weights=None):
     """Timed run of one workload; returns the bench fields (and the Runner, still open)."""
     import torch
-    r = Runner(wl, steps, warmup)
+    r = Runner(wl, steps, warmup, device_weights)
     eng, mc = r.eng, wl.model
     B, n, S = r.B, r.n, r.S
     # warm-up: the first step without timers (one-off costs), then every stage's event
@@ -385,7 +393,7 @@ def measure(wl, steps: int, warmup: int, stage_detail: bool, graph: bool = True)
 
 STAGES = ["embed", "norm", "qkv", "attn", "oproj", "router", "expert_up", "expert_down", "combine",
           "lm_head", "sampler", "selfcond", "commit"]
-EXTRA_WORKLOADS = ("small", "multicanvas", "batched")
+EXTRA_WORKLOADS = ("small", "multicanvas", "batched", "batched-topk")
 
 
 def main():
@@ -424,20 +432,50 @@ def main():
     wl = di.workload(a.workload)
     mc, sp = wl.model, wl.sampler
     res, runner = measure(wl, a.steps, a.warmup, stage_detail=True, graph=not a.no_graph)
+    dw = {wl.name: runner.weights}
     runner.close()
     extras = {}
-    if not a.no_extras:
-        for name in EXTRA_WORKLOADS:
-            if name == wl.name:
-                continue
-            try:
-                x, r = measure(di.workload(name), 24, 3, stage_detail=False, graph=not a.no_graph)
-                r.close()
-                extras[name] = {k: x[k] for k in ("value", "ms_per_step", "ms_per_step_median", "ms_per_step_p90",
-                                                  "steps_per_s", "encode_ms")}
-                extras[name]["steps"] = 24
-            except Exception as ex:   # reported, never fatal for the headline
-                extras[name] = {"error": repr(ex)}
+
+    def same_model(name):
+        """Workloads on the same seeded weights share the device copy."""
+        x = di.workload(name)
+        base = dataclasses.replace(x.model, expert_dtype="")
+        for k in list(dw):
+            w0 = di.workload(k)
+            if dataclasses.replace(w0.model, expert_dtype="") == base and w0.seed == x.seed:
+                return dw[k]
+        return None
+
+    # the headline model with its experts in FP8 and with top-k sampling, then the
+    # other workloads (the batched shape also with top-k sampling)
+    names = [n_ for n_ in (wl.name + "-fp8", wl.name + "-topk") if n_ in di.WORKLOADS]
+    names += [n_ for n_ in EXTRA_WORKLOADS if n_ != wl.name]
+    if a.no_extras:
+        names = []
+    for name in names:
+        try:
+            xw = di.workload(name)
+            detail = name.startswith(wl.name)
+            x, r = measure(xw, a.steps if detail else 24, a.warmup if detail else 3, stage_detail=detail,
+                           graph=not a.no_graph, device_weights=same_model(name))
+            if name not in dw and same_model(name) is None:
+                dw[name] = r.weights
+            r.close()
+            keys = ["value", "ms_per_step", "ms_per_step_median", "ms_per_step_p90", "steps_per_s", "encode_ms"]
+            if detail:
+                keys += ["stage_ms_warmup", "roofline"]
+            extras[name] = {k: x[k] for k in keys if k in x}
+            extras[name]["steps"] = a.steps if detail else 24
+            if xw.model.expert_dtype == "fp8":
+                extras[name]["dtype"] = "bf16 activations, fp8 e4m3 expert weights"
+            if xw.sampler.top_k:
+                extras[name]["sampler"] = f"top-{xw.sampler.top_k} truncated"
+        except Exception as ex:   # reported, never fatal for the headline
+            extras[name] = {"error": repr(ex)}
+    dw.clear()
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
     cpu = None
     if not a.no_cpu_baseline:
         try:

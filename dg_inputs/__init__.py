@@ -70,6 +70,7 @@ class SamplerConfig:
     stop_tau: float = 0.0
     t_start: float = 0.8
     t_end: float = 0.4
+    top_k: int = 0           # 0: the full vocabulary; k: top-k truncated sampling
 
 
 @dataclasses.dataclass(frozen=True)
@@ -115,6 +116,11 @@ WORKLOADS: Dict[str, Workload] = {
                           SamplerConfig(48, 0.1, STOP_MEAN, 0.05), prompt_len=2048, batch=1, canvases=1, seed=2),
     "small-fp8": Workload("small-fp8", dataclasses.replace(_SMALL, expert_dtype="fp8"), SamplerConfig(24, 0.1),
                           prompt_len=512, batch=1, canvases=1, seed=1),
+    # Top-k truncated sampling (k = 8) on the proxy and on the batched shape.
+    "proxy-topk": Workload("proxy-topk", _PROXY, SamplerConfig(48, 0.1, STOP_MEAN, 0.05, top_k=8),
+                           prompt_len=2048, batch=1, canvases=1, seed=2),
+    "batched-topk": Workload("batched-topk", _SMALL, SamplerConfig(48, 0.1, STOP_MEAN, 0.05, top_k=8),
+                             prompt_len=4096, batch=32, canvases=1, seed=1),
 }
 
 

@@ -36,7 +36,7 @@ EXPORTS = [
     "dg_state_init", "dg_state_destroy", "dg_state_ctx_len", "dg_state_canvas_index", "dg_state_view",
     "dg_init_canvas", "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
     "dg_sample_commit",
-    "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_profile_enable", "dg_profile_read",
+    "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_corrupt_forward_loss", "dg_profile_enable", "dg_profile_read",
 ]
 
 
@@ -50,7 +50,7 @@ class DgConfig(ctypes.Structure):
 class DgSamplerParams(ctypes.Structure):
     _fields_ = [("t_start", ctypes.c_float), ("t_end", ctypes.c_float),
                 ("entropy_bound", ctypes.c_float), ("stop_tau", ctypes.c_float),
-                ("max_steps", ctypes.c_int32), ("stop_mode", ctypes.c_int32)]
+                ("max_steps", ctypes.c_int32), ("stop_mode", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
 
 class DgError(RuntimeError):
@@ -98,6 +98,7 @@ def load() -> ctypes.CDLL:
     lib.dg_sample_commit.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.POINTER(DgSamplerParams), vp, vp, vp,
                                      vp, vp]
     lib.dg_commit_canvas_to_kv.argtypes = [vp, vp, vp, vp]
+    lib.dg_corrupt_forward_loss.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dg_run_canvas.argtypes = [vp, vp, ctypes.POINTER(DgSamplerParams), vp, vp, vp, vp, vp, vp, vp, vp,
                                   i32, i32, ctypes.c_uint32, ctypes.POINTER(i32), vp]
     lib.dg_profile_enable.argtypes = [vp, ctypes.c_uint32]
@@ -105,7 +106,7 @@ def load() -> ctypes.CDLL:
     for name in ("dg_model_create", "dg_model_view", "dg_state_bytes", "dg_state_init", "dg_state_view", "dg_init_canvas",
                  "dg_encode_prompt", "dg_denoise_step", "dg_sample_logits", "dg_sample_logits_static",
                  "dg_sample_commit",
-                 "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_profile_enable", "dg_profile_read"):
+                 "dg_commit_canvas_to_kv", "dg_run_canvas", "dg_corrupt_forward_loss", "dg_profile_enable", "dg_profile_read"):
         getattr(lib, name).restype = i32
     _check_single_hip_runtime()
     _lib = lib

@@ -90,7 +90,8 @@ struct dg_state {
   // checks, launch plans) and whether all requests still agree
   int ctx = 0, canvas_index = 0;
   bool uniform = true;
-  int32_t* ctx_dev; int32_t* cidx_dev; float* inv_tab;
+  int32_t* ctx_dev; int32_t* cidx_dev; float* inv_tab; float* lse;
+  TopkPart* topk; int topk_seg;   // top-k truncated sampler: per (row, vocabulary segment) records
   int32_t* step_dev;     // [0] step of the canvas, [1] every request done, [2] loop steps completed
   volatile int32_t* progress = nullptr;      // mapped host memory: (steps completed, all done)
   int32_t* progress_dev = nullptr;           // its device address
@@ -323,7 +324,7 @@ constexpr int kMaxLoopSteps = 4096;   // longest step budget of the device-drive
 
 struct Offsets {
   size_t kc, vc, rope, s, prev_am, h, xn, part, q, attn, attn_po, attn_pml, rlog, ridx, rw, perm, pos, rcnt,
-      tiles, n_tiles, act, y, hp, chunk_scale, ptilde, sc_part, tok, ctxv, cidx, stepv, inv_tab, total;
+      tiles, n_tiles, act, y, hp, chunk_scale, ptilde, sc_part, tok, ctxv, cidx, stepv, inv_tab, lse, topk, total;
   size_t part_floats;
   int chunks, splits, cap_tiles, sc_splits, sc_kchunk;
 };
@@ -393,6 +394,8 @@ Offsets layout(const dg_model* m, int B, int max_ctx) {
   o.cidx = L.take((size_t)B * 4);
   o.stepv = L.take(4 * 4);                          // step counter, all-done flag, steps completed
   o.inv_tab = L.take((size_t)kMaxLoopSteps * 4);
+  o.lse = L.take((size_t)R * 4);
+  o.topk = L.take((size_t)R * topk_segments(R, V) * sizeof(TopkPart));
   o.total = L.off;
   return o;
 }
@@ -443,6 +446,9 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->cidx_dev = reinterpret_cast<int32_t*>(b + o.cidx);
   s->step_dev = reinterpret_cast<int32_t*>(b + o.stepv);
   s->inv_tab = reinterpret_cast<float*>(b + o.inv_tab);
+  s->lse = reinterpret_cast<float*>(b + o.lse);
+  s->topk = reinterpret_cast<TopkPart*>(b + o.topk);
+  s->topk_seg = topk_segments(s->R, m->cfg.vocab);
   s->total_bytes = o.total;
   // progress record of the device-driven loop in mapped host memory
   void* hp = nullptr;
@@ -756,9 +762,26 @@ dg_status run_merge(dg_state* st, Gate gate, float* H, int32_t* y, int32_t* am, 
 
 // Sampler stage on supplied logits [R][V].
 template <typename T>
-dg_status run_head(dg_state* st, const float* logits, const StepInfo& si, const uint64_t* seeds, Gate gate,
-                   float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
+dg_status run_topk_merge(dg_state* st, int top_k, const StepInfo& si, const uint64_t* seeds, Gate gate, float* H,
+                         int32_t* y, int32_t* am, float* margin, hipStream_t s) {
   const dg_config& c = st->m->cfg;
+  StageTimer tm(st, DG_STAGE_SAMPLER, s);
+  DG_HIP(topk_merge<T>(st->topk, st->R, st->topk_seg, top_k, si, make_seeds(seeds, st->B), st->n, gate, H, y, am,
+                       margin, static_cast<const T*>(st->m->emb), c.d_model, c.self_cond ? st->s : nullptr, s));
+  return DG_OK;
+}
+
+template <typename T>
+dg_status run_head(dg_state* st, const float* logits, const StepInfo& si, int top_k, const uint64_t* seeds,
+                   Gate gate, float* H, int32_t* y, int32_t* am, float* margin, hipStream_t s) {
+  const dg_config& c = st->m->cfg;
+  if (top_k > 0) {
+    {
+      StageTimer tm(st, DG_STAGE_LM_HEAD, s);
+      DG_HIP(topk_from_logits(logits, st->R, c.vocab, st->topk_seg, st->topk, gate, st->n, s));
+    }
+    return run_topk_merge<T>(st, top_k, si, seeds, gate, H, y, am, margin, s);
+  }
   {
     StageTimer tm(st, DG_STAGE_SAMPLER, s);
     DG_HIP(head_from_logits<T>(logits, st->R, c.vocab, si, make_seeds(seeds, st->B), st->n, st->hp,
@@ -771,14 +794,29 @@ dg_status run_head(dg_state* st, const float* logits, const StepInfo& si, const 
 // (s of the previous step), as the explicit calls decide from the step; the
 // loop always adds it, with s cleared at the start of each canvas.
 template <typename T>
-dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, bool sc, const uint64_t* seeds,
-                      Gate gate, float* H, int32_t* y, int32_t* am, float* margin, float* logits_out, hipStream_t s) {
+dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, bool sc, int top_k,
+                      const uint64_t* seeds, Gate gate, float* H, int32_t* y, int32_t* am, float* margin,
+                      float* logits_out, hipStream_t s) {
   const dg_model* m = st->m;
   const dg_config& c = m->cfg;
   const int d = c.d_model, V = c.vocab, R = st->R;
   dg_status r = run_stack<T>(st, canvas, st->n, false, sc, gate, 0, s);
   if (r) return r;
   T* xn = static_cast<T*>(st->xn);   // rnd(final RMSNorm(h)), written by the last combine
+  if (top_k > 0) {
+    {
+      // the LM head keeping each row's top logits per vocabulary segment
+      StageTimer tm(st, DG_STAGE_LM_HEAD, s);
+      DG_HIP(gemm_lm_head_topk<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, st->topk_seg, st->topk, gate,
+                                  st->n, s));
+    }
+    if (logits_out != nullptr) {
+      // the raw logits, only when a caller asks for them (the plain head writes them)
+      const HeadArgs<T> h{si, make_seeds(seeds, st->B), st->n, st->hp, nullptr, logits_out, gate};
+      DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
+    }
+    return run_topk_merge<T>(st, top_k, si, seeds, gate, H, y, am, margin, s);
+  }
   {
     // the LM head with the head statistics in its epilogue (logits stored only when asked for)
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
@@ -791,6 +829,7 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, b
 
 dg_status check_params(const dg_sampler_params* p) {
   if (!p) return fail(DG_ERR_ARG, "sampler params are null");
+  if (p->top_k < 0 || p->top_k > kTopkList) return fail(DG_ERR_UNSUPPORTED, "top_k must be in 0..%d", kTopkList);
   if (p->max_steps < 1) return fail(DG_ERR_ARG, "max_steps must be >= 1");
   if (p->stop_mode < 0 || p->stop_mode > 2) return fail(DG_ERR_ARG, "stop_mode must be 0, 1 or 2");
   if (!(p->t_start > 0.f) || !(p->t_end > 0.f)) return fail(DG_ERR_ARG, "temperatures must be > 0");
@@ -838,9 +877,12 @@ extern "C" dg_status dg_denoise_step(dg_state* st, const int32_t* d_canvas, int3
   const StepInfo si = explicit_step(st, params, step);
   const bool sc = st->m->cfg.self_cond && step > 0;
   const Gate g{d_active, 0};
+  if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
   return st->m->cfg.dtype == DG_DTYPE_BF16
-             ? run_denoise<bf16>(st, d_canvas, si, sc, h_seeds, g, d_H, d_y, d_argmax, d_margin, d_logits, s)
-             : run_denoise<float>(st, d_canvas, si, sc, h_seeds, g, d_H, d_y, d_argmax, d_margin, d_logits, s);
+             ? run_denoise<bf16>(st, d_canvas, si, sc, params->top_k, h_seeds, g, d_H, d_y, d_argmax, d_margin,
+                                 d_logits, s)
+             : run_denoise<float>(st, d_canvas, si, sc, 0, h_seeds, g, d_H, d_y, d_argmax, d_margin, d_logits, s);
 }
 
 extern "C" dg_status dg_sample_logits(dg_state* st, const float* d_logits, int32_t step,
@@ -855,8 +897,8 @@ extern "C" dg_status dg_sample_logits(dg_state* st, const float* d_logits, int32
   const StepInfo si = explicit_step(st, params, step);
   const Gate g{d_active, 0};
   return st->m->cfg.dtype == DG_DTYPE_BF16
-             ? run_head<bf16>(st, d_logits, si, h_seeds, g, d_H, d_y, d_argmax, d_margin, s)
-             : run_head<float>(st, d_logits, si, h_seeds, g, d_H, d_y, d_argmax, d_margin, s);
+             ? run_head<bf16>(st, d_logits, si, params->top_k, h_seeds, g, d_H, d_y, d_argmax, d_margin, s)
+             : run_head<float>(st, d_logits, si, params->top_k, h_seeds, g, d_H, d_y, d_argmax, d_margin, s);
 }
 
 extern "C" dg_status dg_sample_logits_static(const float* d_logits, int32_t rows, int32_t vocab, int32_t canvas_len,
@@ -909,6 +951,54 @@ extern "C" dg_status dg_sample_commit(dg_state* st, const float* d_H, const int3
   return DG_OK;
 }
 
+// ------------------------------------------------------------------ training-side forward pass
+namespace {
+template <typename T>
+dg_status run_corrupt_loss(dg_state* st, const int32_t* clean, const RateArg& rates, const uint64_t* seeds,
+                           int32_t* corrupted, float* ce, float* loss, hipStream_t s) {
+  const dg_model* m = st->m;
+  const dg_config& c = m->cfg;
+  const int d = c.d_model, V = c.vocab, R = st->R;
+  const SeedArg sa = make_seeds(seeds, st->B);
+  const Gate all{nullptr, 0};
+  DG_HIP(corrupt_canvas(clean, corrupted, sa, rates, st->B, st->n, V, st->cidx_dev, s));
+  dg_status r = run_stack<T>(st, corrupted, st->n, false, false, all, 0, s);
+  if (r) return r;
+  T* xn = static_cast<T*>(st->xn);
+  {
+    // the LM head at temperature 1: the chunk statistics give each row's log-sum-exp
+    StageTimer tm(st, DG_STAGE_LM_HEAD, s);
+    const HeadArgs<T> h{StepInfo{0, 1.0f, nullptr, nullptr, st->cidx_dev}, sa, st->n, st->hp, nullptr, nullptr, all};
+    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
+  }
+  {
+    StageTimer tm(st, DG_STAGE_SAMPLER, s);
+    DG_HIP(sampler_merge(st->hp, R, st->chunks, st->n, all, nullptr, nullptr, nullptr, nullptr, nullptr, s, st->lse));
+    DG_HIP(clean_token_loss<T>(xn, static_cast<const T*>(m->emb), clean, st->lse, st->B, st->n, d, ce, loss, s));
+  }
+  return DG_OK;
+}
+}  // namespace
+
+extern "C" dg_status dg_corrupt_forward_loss(dg_state* st, const int32_t* d_clean, const float* h_rates,
+                                             const uint64_t* h_seeds, int32_t* d_corrupted, float* d_ce,
+                                             float* d_loss, dg_stream stream) {
+  if (!st || !d_clean || !h_rates || !h_seeds || !d_corrupted || !d_ce || !d_loss)
+    return fail(DG_ERR_ARG, "null argument");
+  RateArg ra;
+  memset(&ra, 0, sizeof(ra));
+  for (int b = 0; b < st->B; ++b) {
+    if (!(h_rates[b] >= 0.f && h_rates[b] <= 1.f)) return fail(DG_ERR_ARG, "rate of request %d outside [0, 1]", b);
+    ra.v[b] = h_rates[b];
+  }
+  dg_status r = check_capacity(st);
+  if (r) return r;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return st->m->cfg.dtype == DG_DTYPE_BF16
+             ? run_corrupt_loss<bf16>(st, d_clean, ra, h_seeds, d_corrupted, d_ce, d_loss, s)
+             : run_corrupt_loss<float>(st, d_clean, ra, h_seeds, d_corrupted, d_ce, d_loss, s);
+}
+
 extern "C" dg_status dg_commit_canvas_to_kv(dg_state* st, const int32_t* d_canvas, const uint8_t* d_which,
                                             dg_stream stream) {
   if (!st || !d_canvas) return fail(DG_ERR_ARG, "null argument");
@@ -937,7 +1027,8 @@ dg_status enqueue_loop_step(dg_state* st, int32_t* canvas, const dg_sampler_para
                             uint8_t* done, hipStream_t s) {
   const Gate g{done, 1};
   const StepInfo si = loop_step(st);
-  dg_status r = run_denoise<T>(st, canvas, si, st->m->cfg.self_cond != 0, seeds, g, H, y, am, margin, nullptr, s);
+  dg_status r = run_denoise<T>(st, canvas, si, st->m->cfg.self_cond != 0, p->top_k, seeds, g, H, y, am, margin,
+                               nullptr, s);
   if (r) return r;
   {
     StageTimer tm(st, DG_STAGE_COMMIT, s);
@@ -950,7 +1041,7 @@ dg_status enqueue_loop_step(dg_state* st, int32_t* canvas, const dg_sampler_para
 
 bool same_params(const dg_sampler_params& a, const dg_sampler_params& b) {
   return a.t_start == b.t_start && a.t_end == b.t_end && a.entropy_bound == b.entropy_bound &&
-         a.stop_tau == b.stop_tau && a.max_steps == b.max_steps && a.stop_mode == b.stop_mode;
+         a.stop_tau == b.stop_tau && a.max_steps == b.max_steps && a.stop_mode == b.stop_mode && a.top_k == b.top_k;
 }
 
 }  // namespace
@@ -966,6 +1057,8 @@ extern "C" dg_status dg_run_canvas(dg_state* st, int32_t* d_canvas, const dg_sam
   dg_status r = check_params(params);
   if (r) return r;
   if (params->max_steps > kMaxLoopSteps) return fail(DG_ERR_UNSUPPORTED, "max_steps above %d", kMaxLoopSteps);
+  if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
   if (first_step < 0 || first_step >= params->max_steps)
     return fail(DG_ERR_ARG, "first_step %d outside 0..max_steps-1", first_step);
   if (n_steps < 1 || n_steps > params->max_steps - first_step)

@@ -214,7 +214,7 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-enum : uint32_t { kTagInit = 2, kTagGumbel = 3, kTagRenoise = 4 };
+enum : uint32_t { kTagInit = 2, kTagGumbel = 3, kTagRenoise = 4, kTagCorrupt = 5 };
 
 // Counter layout: (j >> 2, position, step, tag << 24 | canvas), output word j & 3.
 __device__ __forceinline__ uint4 philox_block(uint64_t seed, uint32_t tag, uint32_t canvas,

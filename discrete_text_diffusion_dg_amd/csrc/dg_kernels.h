@@ -235,6 +235,35 @@ hipError_t fill_u8(void* p, uint8_t v, size_t count, hipStream_t s);
 // (step[2], step[1]).
 hipError_t step_end(const uint8_t* done, int B, int32_t* step, volatile int32_t* progress, hipStream_t s);
 
+// ---- top-k truncated sampler ([mlqm] 九: top-k truncation of the vocabulary)
+// A vocabulary segment's top kTopkList logits of one row, descending (ties:
+// lower id first); written per (row, segment) by the LM head's top-k variant
+// (or from supplied logits) and combined per row by topk_merge.
+constexpr int kTopkList = 8;
+struct TopkPart {
+  float v[kTopkList];
+  int id[kTopkList];
+};
+// Segments of the vocabulary for M rows (one workgroup per 128-row block and
+// segment, about 256 workgroups).
+int topk_segments(int M, int vocab);
+// logits = A . B^T tile by tile over each (row block, segment); per row and
+// segment its top kTopkList logits.  Rows of requests the gate leaves out are
+// skipped (whole row blocks).
+template <typename T>
+hipError_t gemm_lm_head_topk(const T* A, int lda, const T* B, int ldb, int M, int V, int K, int nseg, TopkPart* out,
+                             Gate g, int n, hipStream_t s);
+// the same records from supplied fp32 logits [M][V]
+hipError_t topk_from_logits(const float* logits, int M, int V, int nseg, TopkPart* out, Gate g, int n, hipStream_t s);
+// Per row: the top_k (1..kTopkList) largest logits of all segments; the
+// truncated tempered distribution's entropy, its Gumbel-max sample and top-2
+// margin, the logit argmax, and (emb non-null) the self-conditioning vector
+// s = sum p_v E_v over the k ids.
+template <typename T>
+hipError_t topk_merge(const TopkPart* part, int M, int nseg, int top_k, const StepInfo& si, const SeedArg& seeds, int n,
+                      Gate g, float* H, int32_t* y, int32_t* am, float* margin, const T* emb, int d, float* s_out,
+                      hipStream_t s);
+
 // ---- sampler (k_sampler.hip)
 // Fixed device scratch of the allocation-free sampler entry point
 // (dg_sample_logits_static): its device address on the current device, looked
@@ -249,9 +278,23 @@ int head_chunks(int vocab);     // 128-id chunks of the vocabulary
 template <typename T>
 hipError_t head_from_logits(const float* logits, int M, int V, const StepInfo& si, const SeedArg& seeds, int n,
                             HeadPart* part, T* ptilde, Gate g, hipStream_t s);
+// H, y, am, margin may be null (not written); lse (may be null) receives each
+// row's log sum exp(z).
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, Gate g,
                          float* H, int32_t* y, int32_t* am, float* margin, float* chunk_scale,
-                         hipStream_t s);
+                         hipStream_t s, float* lse = nullptr);
+// Training-side forward pass: corruption of clean canvases (per-request
+// rates), then the cross-entropy of the clean tokens (ce [B*n]) and its mean
+// per request (loss [B]) from the final normed rows, the embedding and the
+// rows' log-sum-exp.
+struct RateArg {
+  float v[kMaxBatch];
+};
+hipError_t corrupt_canvas(const int32_t* clean, int32_t* out, const SeedArg& seeds, const RateArg& rates, int B,
+                          int n, int vocab, const int32_t* cidx, hipStream_t s);
+template <typename T>
+hipError_t clean_token_loss(const T* xn, const T* emb, const int32_t* clean, const float* lse, int B, int n, int d,
+                            float* ce, float* loss, hipStream_t s);
 // S[r][c] = sum over splits (in order) of part[split][r][c], rows of active requests
 hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s);
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,

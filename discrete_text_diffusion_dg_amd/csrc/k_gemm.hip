@@ -306,6 +306,111 @@ hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, 
   return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, ep, s);
 }
 
+// ------------------------------------------------------------------ top-k LM head
+// Tied LM head for the top-k truncated sampler: a workgroup owns a 128-row
+// block and a vocabulary segment and walks the segment's 128-id tiles in
+// order.  Each tile's logits go through LDS as for the head statistics; lane
+// (row, half) of the four waves keeps the 8 largest logits of its 64-id halves
+// (a branch-free insertion, ids arriving in increasing order so an equal
+// value never displaces the held one), and at the end the two halves of a row
+// are merged and written: 64 bytes per (row, segment) instead of the logits or
+// exp(z - m).
+__device__ __forceinline__ void topk_insert(float (&tv)[kTopkList], int (&ti)[kTopkList], float v, int id, bool ties) {
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) {
+    const bool c = v > tv[j] || (ties && v == tv[j] && id < ti[j]);
+    const float nv = c ? v : tv[j];
+    const int ni = c ? id : ti[j];
+    v = c ? tv[j] : v;
+    id = c ? ti[j] : id;
+    tv[j] = nv;
+    ti[j] = ni;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void k_lm_head_topk(ALPlain<T> al, BLPlain<T> bl, int M, int V, int K, int nseg,
+                                                         int cps, TopkPart* out, Gate gate, int n) {
+  using C = TileCfgD<kHeadChunk, kHeadChunk, 2>;
+  constexpr int kBytes = C::kSmemBytes > kHeadTileBytes ? C::kSmemBytes : kHeadTileBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kBytes];
+  const int nmb = (M + kHeadChunk - 1) / kHeadChunk, nchunk = (V + kHeadChunk - 1) / kHeadChunk;
+  const int total = nmb * nseg;
+  if ((int)blockIdx.x >= total) return;
+  // the row blocks of a segment are adjacent on one XCD: they share the segment's rows of E
+  const int idx = xcd_run(blockIdx.x, total), mb = idx % nmb, sg = idx / nmb;
+  const int m0 = mb * kHeadChunk, rows = min(kHeadChunk, M - m0);
+  if (!gate.any_active(m0, rows, n)) return;
+  const int c_begin = sg * cps, c_end = min(nchunk, c_begin + cps);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rl = w * 32 + (lane & 31), half = lane >> 5, c0 = half * 64;
+  float tv[kTopkList];
+  int ti[kTopkList];
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
+  float* tile = reinterpret_cast<float*>(smem);
+  for (int c = c_begin; c < c_end; ++c) {
+    TileCtx t;
+    t.m0 = m0; t.n0 = c * kHeadChunk; t.rows = rows; t.cols = min(kHeadChunk, V - t.n0);
+    t.k0 = 0; t.k1 = K; t.group = 0; t.row_base = m0;
+    f32x4_t acc[C::FM][C::FN];
+    tile_mma_dma<C>(t, al, bl, smem, acc);
+    for_each_acc<C>(acc, [&](int r, int cc, float v) { tile[r * kHeadLd + cc] = v; });
+    __syncthreads();
+    if (rl < rows && c0 < t.cols) {
+      const float* tr = tile + rl * kHeadLd + c0;
+#pragma unroll 4
+      for (int q = 0; q < 16; ++q) {
+        const float4 x = reinterpret_cast<const float4*>(tr)[q];
+        const int id = t.n0 + c0 + 4 * q;
+        topk_insert(tv, ti, x.x, id, false);
+        topk_insert(tv, ti, x.y, id + 1, false);
+        topk_insert(tv, ti, x.z, id + 2, false);
+        topk_insert(tv, ti, x.w, id + 3, false);
+      }
+    }
+    __syncthreads();          // the next tile's K loop reuses the LDS
+  }
+  // the row's two halves (lanes l and l ^ 32): ids interleave, so ties compare ids
+  float pv[kTopkList];
+  int pi[kTopkList];
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) { pv[j] = lane_partner<5>(tv[j]); pi[j] = lane_partner<5>(ti[j]); }
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) topk_insert(tv, ti, pv[j], pi[j], true);
+  if (half == 0 && rl < rows) {
+    TopkPart rec;
+#pragma unroll
+    for (int j = 0; j < kTopkList; ++j) { rec.v[j] = tv[j]; rec.id[j] = ti[j]; }
+    out[(size_t)(m0 + rl) * nseg + sg] = rec;
+  }
+}
+
+int topk_segments(int M, int vocab) {
+  const int nmb = cdiv(M, kHeadChunk), nchunk = cdiv(vocab, kHeadChunk);
+  int nseg = cdiv(256, nmb);
+  return nseg < 1 ? 1 : (nseg > nchunk ? nchunk : nseg);
+}
+
+template <typename T>
+hipError_t gemm_lm_head_topk(const T* A, int lda, const T* B, int ldb, int M, int V, int K, int nseg, TopkPart* out,
+                             Gate g, int n, hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    if (V % 64 || K % 64 || M <= 0) return hipErrorInvalidValue;
+    const int nmb = cdiv(M, kHeadChunk), nchunk = cdiv(V, kHeadChunk);
+    const int cps = cdiv(nchunk, nseg);
+    hipLaunchKernelGGL((k_lm_head_topk<T>), dim3(nmb * nseg), dim3(256), 0, s, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
+                       M, V, K, nseg, cps, out, g, n);
+    return hipGetLastError();
+  }
+}
+template hipError_t gemm_lm_head_topk<float>(const float*, int, const float*, int, int, int, int, int, TopkPart*, Gate,
+                                             int, hipStream_t);
+template hipError_t gemm_lm_head_topk<bf16>(const bf16*, int, const bf16*, int, int, int, int, int, TopkPart*, Gate,
+                                            int, hipStream_t);
+
 // Grouped products on the DMA tile loop take 128-row tiles: each 128 x 128
 // tile reads 32 KB of operands per 64-wide K step for 2 MFLOP, against 24 KB
 // for 1 MFLOP with 64-row tiles.

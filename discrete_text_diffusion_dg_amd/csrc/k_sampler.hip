@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_head_logits(const float* logits, int M,
 template <int CPT>
 __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int chunks, int n, Gate g,
                                                        float* H, int32_t* y, int32_t* am, float* margin,
-                                                       float* chunk_scale) {
+                                                       float* chunk_scale, float* lse) {
   __shared__ float sm_m[4], sm_l[4], sm_g1[4], sm_g2[4];
   __shared__ int sm_li[4], sm_gi[4];
   __shared__ double sm_S[4], sm_W[4];
@@ -116,6 +116,8 @@ __global__ __launch_bounds__(256) void k_sampler_merge(const HeadPart* part, int
     argmax_merge(lmax, lidx, sm_l[q], sm_li[q]);
     top2_merge(t2, Top2{sm_g1[q], sm_gi[q], sm_g2[q]});
   }
+  if (lse != nullptr) lse[r] = (float)(m + log(S));     // log sum exp(z) of the row
+  if (H == nullptr) return;
   H[r] = (float)(log(S) - W / S);
   y[r] = t2.i1;
   am[r] = lidx;
@@ -283,21 +285,262 @@ hipError_t head_from_logits(const float* logits, int M, int V, const StepInfo& s
 }
 
 hipError_t sampler_merge(const HeadPart* part, int M, int chunks, int n, Gate g, float* H,
-                         int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s) {
+                         int32_t* y, int32_t* am, float* margin, float* chunk_scale, hipStream_t s, float* lse) {
   if (M <= 0) return hipSuccess;
   const dim3 grid(M), block(256);
   if (chunks <= 256)
-    hipLaunchKernelGGL((k_sampler_merge<1>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<1>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale, lse);
   else if (chunks <= 512)
-    hipLaunchKernelGGL((k_sampler_merge<2>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<2>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale, lse);
   else if (chunks <= 1024)
-    hipLaunchKernelGGL((k_sampler_merge<4>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<4>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale, lse);
   else if (chunks <= 2048)
-    hipLaunchKernelGGL((k_sampler_merge<8>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale);
+    hipLaunchKernelGGL((k_sampler_merge<8>), grid, block, 0, s, part, chunks, n, g, H, y, am, margin, chunk_scale, lse);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
+
+// ------------------------------------------------------------------ top-k truncated sampler
+// Branch-free insertion into a descending list of (value, id); `ties`: an
+// equal value with a lower id goes first (else ids arrive in increasing order
+// and an equal value never displaces the held one).
+__device__ __forceinline__ void topk_push(float (&tv)[kTopkList], int (&ti)[kTopkList], float v, int id, bool ties) {
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) {
+    const bool c = v > tv[j] || (ties && v == tv[j] && id < ti[j]);
+    const float nv = c ? v : tv[j];
+    const int ni = c ? id : ti[j];
+    v = c ? tv[j] : v;
+    id = c ? ti[j] : id;
+    tv[j] = nv;
+    ti[j] = ni;
+  }
+}
+// Order-preserving 64-bit key of (value descending, id ascending).
+__device__ __forceinline__ uint64_t topk_key(float v, int id) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  butterfly_steps([&](auto st) {
+    constexpr int S = decltype(st)::value;
+    const uint64_t o = ((uint64_t)lane_partner<S>((uint32_t)(k >> 32)) << 32) | lane_partner<S>((uint32_t)k);
+    k = o > k ? o : k;
+  });
+  return k;
+}
+// k rounds: every lane offers the head of its sorted list, the wave's largest
+// key wins and its lane moves on; out lists the winners in order (every lane).
+__device__ __forceinline__ void topk_wave_select(float (&tv)[kTopkList], int (&ti)[kTopkList], int k,
+                                                 float (&ov)[kTopkList], int (&oi)[kTopkList]) {
+#pragma unroll
+  for (int r = 0; r < kTopkList; ++r) {
+    if (r >= k) { ov[r] = -INFINITY; oi[r] = 0x7fffffff; continue; }
+    const uint64_t mine = topk_key(tv[0], ti[0]);
+    const uint64_t best = wave_max_u64(mine);
+    const uint32_t id = 0xFFFFFFFFu - (uint32_t)best;
+    const uint32_t o = (uint32_t)(best >> 32);
+    ov[r] = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+    oi[r] = (int)id;
+    if (mine == best) {                 // this lane's head was taken: shift its list
+#pragma unroll
+      for (int j = 0; j + 1 < kTopkList; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
+      tv[kTopkList - 1] = -INFINITY;
+      ti[kTopkList - 1] = 0x7fffffff;
+    }
+  }
+}
+
+// Supplied logits: one wave per (row, segment); lane l scans ids l, l + 64, ...
+__global__ __launch_bounds__(256) void k_topk_logits(const float* logits, int M, int V, int nseg, int cps,
+                                                     TopkPart* out, Gate g, int n) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= M * nseg) return;
+  const int r = item / nseg, sg = item % nseg;
+  if (!g.active(r / n)) return;
+  const int v0 = sg * cps * kHeadChunk, v1 = min(V, v0 + cps * kHeadChunk);
+  float tv[kTopkList];
+  int ti[kTopkList];
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
+  const float* row = logits + (size_t)r * V;
+  for (int v = v0 + lane; v < v1; v += 64) topk_push(tv, ti, row[v], v, false);
+  float ov[kTopkList];
+  int oi[kTopkList];
+  topk_wave_select(tv, ti, kTopkList, ov, oi);
+  if (lane == 0) {
+    TopkPart rec;
+#pragma unroll
+    for (int j = 0; j < kTopkList; ++j) { rec.v[j] = ov[j]; rec.id[j] = oi[j]; }
+    out[(size_t)r * nseg + sg] = rec;
+  }
+}
+
+// One wave per row: the row's top k over its segments' lists, then the
+// truncated tempered distribution (fp64 sums), the Gumbel-max sample over the
+// k ids (each its own word of the GUMBEL stream), the top-2 margin, the
+// argmax, and s = sum_j p_j E[id_j] (fp32, j in order; lanes over columns).
+template <typename T>
+__global__ __launch_bounds__(256) void k_topk_merge(const TopkPart* part, int M, int nseg, int k, StepInfo si,
+                                                    SeedArg seeds, int n, Gate g, float* H, int32_t* y, int32_t* am,
+                                                    float* margin, const T* emb, int d, float* s_out) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= M) return;
+  const int b = r / n, pos = r % n;
+  if (!g.active(b)) return;
+  float tv[kTopkList];
+  int ti[kTopkList];
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) { tv[j] = -INFINITY; ti[j] = 0x7fffffff; }
+  const TopkPart* pr = part + (size_t)r * nseg;
+  for (int sg = lane; sg < nseg; sg += 64) {
+    const TopkPart rec = pr[sg];
+#pragma unroll
+    for (int j = 0; j < kTopkList; ++j) topk_push(tv, ti, rec.v[j], rec.id[j], true);
+  }
+  float lv[kTopkList];
+  int li[kTopkList];
+  topk_wave_select(tv, ti, k, lv, li);
+  // the distribution over the k (every lane the same values)
+  const int step = si.get_step();
+  const float inv_t = si.get_inv_t(step);
+  const double m = (double)(lv[0] * inv_t);
+  double S = 0.0, W = 0.0;
+  double e[kTopkList];
+#pragma unroll
+  for (int j = 0; j < kTopkList; ++j) {
+    const double z = (double)(lv[j] * inv_t);
+    e[j] = j < k ? exp(z - m) : 0.0;
+    S += e[j];
+    W += j < k ? e[j] * (z - m) : 0.0;
+  }
+  // Gumbel scores: lane j draws for the j-th id
+  float score = -INFINITY;
+  int sid = 0x7fffffff;
+  if (lane < k) {
+    float lvj = lv[0];
+    int lij = li[0];
+#pragma unroll
+    for (int j = 1; j < kTopkList; ++j) if (lane == j) { lvj = lv[j]; lij = li[j]; }
+    const uint4 x = philox_block(seeds.v[b], kTagGumbel, (uint32_t)si.cidx[b], (uint32_t)step, (uint32_t)pos,
+                                 ((uint32_t)(lij >> 6) << 4) | (uint32_t)(lij & 15));
+    const int word = (lij >> 4) & 3;
+    const uint32_t xw = word == 0 ? x.x : word == 1 ? x.y : word == 2 ? x.z : x.w;
+    score = lvj * inv_t + gumbel_of(xw);
+    sid = lij;
+  }
+  const uint64_t k1 = wave_max_u64(topk_key(score, sid));
+  const uint64_t mine = topk_key(score, sid);
+  const uint64_t k2 = wave_max_u64(mine == k1 ? topk_key(-INFINITY, 0x7fffffff) : mine);
+  auto val = [](uint64_t key) {
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+  };
+  if (lane == 0) {
+    H[r] = (float)(log(S) - W / S);
+    y[r] = (int)(0xFFFFFFFFu - (uint32_t)k1);
+    am[r] = li[0];
+    margin[r] = k > 1 ? val(k1) - val(k2) : INFINITY;
+  }
+  if (s_out != nullptr) {
+    float p[kTopkList];
+#pragma unroll
+    for (int j = 0; j < kTopkList; ++j) p[j] = (float)(e[j] / S);
+    for (int c = lane; c < d; c += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTopkList; ++j)
+        if (j < k) acc += p[j] * Num<T>::load(emb + (size_t)li[j] * d + c);
+      s_out[(size_t)r * d + c] = acc;
+    }
+  }
+}
+
+hipError_t topk_from_logits(const float* logits, int M, int V, int nseg, TopkPart* out, Gate g, int n, hipStream_t s) {
+  const int nchunk = (V + kHeadChunk - 1) / kHeadChunk, cps = (nchunk + nseg - 1) / nseg;
+  const int items = M * nseg;
+  hipLaunchKernelGGL(k_topk_logits, dim3((items + 3) / 4), dim3(256), 0, s, logits, M, V, nseg, cps, out, g, n);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t topk_merge(const TopkPart* part, int M, int nseg, int top_k, const StepInfo& si, const SeedArg& seeds,
+                      int n, Gate g, float* H, int32_t* y, int32_t* am, float* margin, const T* emb, int d,
+                      float* s_out, hipStream_t s) {
+  if (top_k < 1 || top_k > kTopkList) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_topk_merge<T>), dim3((M + 3) / 4), dim3(256), 0, s, part, M, nseg, top_k, si, seeds, n, g, H,
+                     y, am, margin, emb, d, s_out);
+  return hipGetLastError();
+}
+template hipError_t topk_merge<float>(const TopkPart*, int, int, int, const StepInfo&, const SeedArg&, int, Gate,
+                                      float*, int32_t*, int32_t*, float*, const float*, int, float*, hipStream_t);
+template hipError_t topk_merge<bf16>(const TopkPart*, int, int, int, const StepInfo&, const SeedArg&, int, Gate,
+                                     float*, int32_t*, int32_t*, float*, const bf16*, int, float*, hipStream_t);
+
+// ------------------------------------------------------------------ training-side corruption and loss
+// Corruption of a clean canvas ([mlqm] 一: a share of the tokens, 0 to 100%,
+// replaced by random vocabulary tokens): one Philox call per position (tag
+// CORRUPT, counter (0, position, 0, CORRUPT << 24 | canvas index)); word 0
+// decides (u < rate of the request, fp32), word 1 is the replacement.
+__global__ void k_corrupt(const int32_t* clean, int32_t* out, SeedArg seeds, RateArg rates, int n, int vocab,
+                          const int32_t* cidx) {
+  const int b = blockIdx.x;
+  const uint32_t c = (uint32_t)cidx[b];
+  const float rate = rates.v[b];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint4 x = philox_block(seeds.v[b], kTagCorrupt, c, 0u, (uint32_t)i, 0u);
+    const int32_t t = clean[(size_t)b * n + i];
+    out[(size_t)b * n + i] = u01(x.x) < rate ? token_of(x.y, vocab) : t;
+  }
+}
+
+// Cross-entropy of the clean token per row (one wave per row): the clean
+// token's logit rnd(final norm(h)) . E[x0] (operands as the LM head takes
+// them, fp32 sums in a fixed order), subtracted from the row's log-sum-exp.
+template <typename T>
+__global__ __launch_bounds__(256) void k_clean_ce(const T* xn, const T* emb, const int32_t* clean, const float* lse,
+                                                  int M, int d, float* ce) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= M) return;
+  const T* a = xn + (size_t)r * d;
+  const T* e = emb + (size_t)clean[r] * d;
+  float acc = 0.f;
+  for (int k = lane; k < d; k += 64) acc += Num<T>::load(a + k) * Num<T>::load(e + k);
+  acc = wave_sum(acc);
+  if (lane == 0) ce[r] = lse[r] - acc;
+}
+
+// Mean cross-entropy per request: fp64, positions in order.
+__global__ void k_loss_mean(const float* ce, int B, int n, float* loss) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += (double)ce[(size_t)b * n + i];
+  loss[b] = (float)(s / (double)n);
+}
+
+hipError_t corrupt_canvas(const int32_t* clean, int32_t* out, const SeedArg& seeds, const RateArg& rates, int B,
+                          int n, int vocab, const int32_t* cidx, hipStream_t s) {
+  hipLaunchKernelGGL(k_corrupt, dim3(B), dim3(256), 0, s, clean, out, seeds, rates, n, vocab, cidx);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t clean_token_loss(const T* xn, const T* emb, const int32_t* clean, const float* lse, int B, int n, int d,
+                            float* ce, float* loss, hipStream_t s) {
+  const int M = B * n;
+  hipLaunchKernelGGL((k_clean_ce<T>), dim3((M + 3) / 4), dim3(256), 0, s, xn, emb, clean, lse, M, d, ce);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_loss_mean, dim3((B + 63) / 64), dim3(64), 0, s, ce, B, n, loss);
+  return hipGetLastError();
+}
+template hipError_t clean_token_loss<float>(const float*, const float*, const int32_t*, const float*, int, int, int,
+                                            float*, float*, hipStream_t);
+template hipError_t clean_token_loss<bf16>(const bf16*, const bf16*, const int32_t*, const float*, int, int, int,
+                                           float*, float*, hipStream_t);
 
 hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s) {
   const size_t nq = (size_t)M * d / 4;      // d is a multiple of 256

@@ -45,7 +45,7 @@ def config_struct(mc) -> L.DgConfig:
 
 def sampler_struct(sp) -> L.DgSamplerParams:
     return L.DgSamplerParams(sp.t_start, sp.t_end, sp.entropy_bound, sp.stop_tau, sp.max_steps,
-                             sp.stop_mode)
+                             sp.stop_mode, getattr(sp, "top_k", 0))
 
 
 def upload_weights(weights, names: Sequence[str], device) -> Dict[str, torch.Tensor]:
@@ -232,6 +232,19 @@ class Engine:
         """Append the canvas of the requests `which` selects (uint8 [B], None = all) to the KV cache."""
         cv = self.canvas if canvas is None else canvas
         L.check(self.lib.dg_commit_canvas_to_kv(self._state, cv.data_ptr(), _ptr(which), self._stream()))
+
+    def corrupt_forward_loss(self, clean: torch.Tensor, rates) -> tuple:
+        """Training-side forward pass (dg_corrupt_forward_loss): (corrupted, ce [B, n], loss [B])."""
+        clean = clean.to(device=self.device, dtype=torch.int32).contiguous()
+        r = np.ascontiguousarray(rates, dtype=np.float32)
+        assert clean.shape == (self.B, self.n) and r.size == self.B
+        corrupted = torch.empty_like(clean)
+        ce = torch.empty(self.B, self.n, dtype=torch.float32, device=self.device)
+        loss = torch.empty(self.B, dtype=torch.float32, device=self.device)
+        L.check(self.lib.dg_corrupt_forward_loss(self._state, clean.data_ptr(), r.ctypes.data_as(ctypes.c_void_p),
+                                                 self._seed_ptr(), corrupted.data_ptr(), ce.data_ptr(),
+                                                 loss.data_ptr(), self._stream()))
+        return corrupted, ce, loss
 
     def ctx_lens(self) -> torch.Tensor:
         """Per-request context lengths (device view)."""

@@ -92,6 +92,16 @@ typedef struct dg_sampler_params {
   float stop_tau;       /* adaptive-stop threshold on the mean entropy, nats */
   int32_t max_steps;    /* step budget S of the canvas (48 on the pages) */
   int32_t stop_mode;    /* DG_STOP_* */
+  /* 0: the full vocabulary.  1..8: top-k truncation ([mlqm] 九: truncating
+   * the vocabulary to the top k raises throughput at high batch): the
+   * distribution of a position is the softmax of its k largest logits (ties:
+   * lower id) renormalised over them, all others 0; entropy, Gumbel-max
+   * sample (over the k ids, each with its own draw of the Gumbel stream),
+   * margin and the self-conditioning vector (sum over the k rows of E) use
+   * it.  The LM head then keeps only each row's k best per vocabulary segment:
+   * no exp(z - m) rows, no vocabulary-long softmax @ E product.  bf16 models
+   * (any model in dg_sample_logits). */
+  int32_t top_k;
 } dg_sampler_params;
 
 typedef struct dg_model dg_model;
@@ -305,6 +315,26 @@ dg_status dg_run_canvas(dg_state* state, int32_t* d_canvas, const dg_sampler_par
                         const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax, float* d_margin,
                         uint8_t* d_commit_mask, int32_t* d_n_committed, uint8_t* d_done, int32_t first_step,
                         int32_t n_steps, uint32_t flags, int32_t* h_result, dg_stream stream);
+
+/* Training-side forward pass ([mlqm] 一: in training a share of a sequence's
+ * tokens, from 0% to 100%, is replaced by random vocabulary tokens and the
+ * model learns to restore the original).  Per request b, every position of
+ * the clean canvas d_clean (int32 [B, canvas_len]) is replaced independently
+ * with probability h_rates[b] (host float [B], each in [0, 1]) by a uniform
+ * vocabulary token: one Philox4x32-10 call per position under the request's
+ * seed, counter (0, position, 0, 5 << 24 | canvas index), word 0 deciding
+ * (u < rate in fp32, u as for every draw of this library) and word 1 giving
+ * the token.  The corrupted canvas (d_corrupted, int32 [B, canvas_len],
+ * written) goes through the model exactly as a denoising round's canvas does
+ * (after the request's context, bidirectional attention over the canvas, no
+ * self-conditioning term), and the cross-entropy of the clean token,
+ * logsumexp(logits) - logits[clean] (temperature 1, nats), is written per
+ * position (d_ce, float [B, canvas_len]) and as its mean per request (d_loss,
+ * float [B]).  Like a denoising round it uses the cache positions
+ * N..N+canvas_len-1 as scratch.  Forward only: no gradients. */
+dg_status dg_corrupt_forward_loss(dg_state* state, const int32_t* d_clean, const float* h_rates,
+                                  const uint64_t* h_seeds, int32_t* d_corrupted, float* d_ce, float* d_loss,
+                                  dg_stream stream);
 
 /* Stage timing ([mlqm] 五 splits a step's cost into MoE, sampling and
  * attention; these counters give the same split for this implementation).

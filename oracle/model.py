@@ -61,6 +61,9 @@ class OracleModel:
         # test impose another expert choice on rows whose own top-k is a near tie
         # (the callback decides where; the weights stay the softmax of these logits)
         self.route_override = None
+        # optional callback(request, logits [n, V]) -> per-row id sets (None for a row to
+        # keep its own): the same for the top-k truncated sampler's vocabulary selection
+        self.topk_override = None
         L, Hkv, hd = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
         self.k_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
         self.v_cache = [np.zeros((batch, Hkv, max_ctx, hd)) for _ in range(L)]
@@ -234,21 +237,35 @@ class OracleModel:
             h = self._stack(b, canvas[b], pos, False, False, extra, trace)
             xf = self.rnd(nm.rmsnorm(h, self.W("final_norm"), cfg.rms_eps))
             logits = (xf @ self.W("emb").T).astype(np.float32)
-            st = smp.head_stats(logits, inv_t, int(seeds[b]), self.canvas_index, step,
-                                np.arange(n), want_probs=cfg.self_cond)
+            top_k = getattr(sp, "top_k", 0)
+            if top_k:
+                # the distribution truncated to each position's top_k logits ([mlqm] 九)
+                forced = self.topk_override(b, logits) if self.topk_override is not None else None
+                st = smp.head_stats_topk(logits, inv_t, top_k, int(seeds[b]), self.canvas_index, step,
+                                         np.arange(n), want_probs=cfg.self_cond, forced_ids=forced)
+            else:
+                st = smp.head_stats(logits, inv_t, int(seeds[b]), self.canvas_index, step,
+                                    np.arange(n), want_probs=cfg.self_cond)
             for key in ("H", "y", "am", "margin"):
                 out[key][b] = st[key]
             if want_logits:
                 out["logits"][b] = logits
             if cfg.self_cond:
-                s_next[b] = st["p"] @ self.W("emb")
+                E = self.W("emb")
+                if top_k:
+                    Ek = E[st["ids"]]                                   # [n, k, d]
+                    s_next[b] = np.einsum("nk,nkd->nd", st["p"], Ek)
+                else:
+                    s_next[b] = st["p"] @ E
                 if want_logits:
                     # spread of that sum under independent relative perturbations of its terms (tests):
                     # sqrt(sum_v p_v^2 E_v^2)
-                    E = self.W("emb")
-                    out.setdefault("s_rms", np.zeros((self.B, n, cfg.d_model)))[b] = np.sqrt((st["p"] ** 2) @ (E * E))
-            if trace is not None:
+                    rms = (np.sqrt(np.einsum("nk,nkd->nd", st["p"] ** 2, Ek * Ek)) if top_k
+                           else np.sqrt((st["p"] ** 2) @ (E * E)))
+                    out.setdefault("s_rms", np.zeros((self.B, n, cfg.d_model)))[b] = rms
+            if trace is not None and not top_k:
                 trace["m"], trace["logS"] = st["m"], st["logS"]
+            if trace is not None:
                 out["traces"][b] = trace
         self.s = s_next
         return out

@@ -115,6 +115,68 @@ def head_stats(logits: np.ndarray, inv_t: np.float32, seed: int, canvas: int, st
     return out
 
 
+def gumbel_of_ids(seed: int, canvas: int, step: int, pos: int, ids: np.ndarray) -> np.ndarray:
+    """Gumbel noise (fp32) of the given vocabulary ids at one position, from the GUMBEL stream."""
+    ids = np.asarray(ids, np.int64)
+    call, word = gumbel_call_of(ids)
+    ctr = np.empty((ids.size, 4), np.uint32)
+    ctr[:, 0] = call.astype(np.uint32)
+    ctr[:, 1] = np.uint32(pos)
+    ctr[:, 2] = np.uint32(step)
+    ctr[:, 3] = np.uint32((philox.TAG_GUMBEL << 24) | (canvas & 0xFFFFFF))
+    out = philox.philox4x32_10(ctr, philox.seed_key(seed))
+    return philox.gumbel(out[np.arange(ids.size), word])
+
+
+def head_stats_topk(logits: np.ndarray, inv_t: np.float32, top_k: int, seed: int, canvas: int, step: int,
+                    pos: np.ndarray, want_probs: bool = False, forced_ids=None) -> Dict[str, np.ndarray]:
+    """Head statistics of the distribution truncated to the top_k largest logits of each row.
+
+    [mlqm] 九: top-k truncation of the vocabulary at high batch (named as an
+    optimisation not yet built).  Reading: the usual top-k sampling -- the k
+    largest logits of a position (ties to the lower id) keep their softmax
+    weights renormalised over the k, every other id has probability 0.  The
+    entropy, the Gumbel-max draw (over the k ids, each with its own Gumbel
+    word of the GUMBEL stream), the top-2 margin and the self-conditioning
+    vector all use that distribution; the argmax is the largest logit as
+    before.  Returns H, am, y, margin like head_stats, the selected ids (in
+    descending logit order) and, if asked, their probabilities (fp64).
+
+    forced_ids [n, top_k] (tests only): where a row's entry is given, that id
+    set replaces the row's own selection (a caller that has shown the two sets
+    to be a near-tie at the k-th logit); it is ordered by descending logit,
+    ties to the lower id, and everything else follows as above.
+    """
+    logits = np.asarray(logits, np.float32)
+    n, V = logits.shape
+    out = {k: np.empty(n, t) for k, t in
+           (("H", np.float32), ("am", np.int32), ("y", np.int32), ("margin", np.float32))}
+    out["ids"] = np.empty((n, top_k), np.int64)
+    if want_probs:
+        out["p"] = np.empty((n, top_k))
+    for r in range(n):
+        order = np.argsort(-logits[r], kind="stable")[:top_k]       # descending, ties -> lower id
+        if forced_ids is not None and forced_ids[r] is not None:
+            ids = np.asarray(forced_ids[r], np.int64)
+            order = ids[np.lexsort((ids, -logits[r, ids]))]
+        z = logits[r, order] * np.float32(inv_t)                        # fp32
+        z64 = z.astype(np.float64)
+        m = z64.max()
+        e = np.exp(z64 - m)
+        S = e.sum()
+        out["H"][r] = np.float32(np.log(S) - (e * (z64 - m)).sum() / S)
+        out["am"][r] = order[0]
+        score = z + gumbel_of_ids(seed, canvas, step, int(pos[r]), order)   # fp32
+        best = max(range(top_k), key=lambda j: (score[j], -order[j]))   # ties -> lower id
+        out["y"][r] = order[best]
+        rest = [score[j] for j in range(top_k) if j != best]
+        out["margin"][r] = np.float32(score[best] - max(rest)) if rest else np.float32(np.inf)
+        out["ids"][r] = order
+        if want_probs:
+            out["p"][r] = e / S
+    return out
+
+
 def commit(H: np.ndarray, y: np.ndarray, am: np.ndarray, prev_am: Optional[np.ndarray],
            canvas: np.ndarray, step: int, max_steps: int, entropy_bound: float,
            stop_mode: int, stop_tau: float, seed: int, canvas_index: int, vocab: int):

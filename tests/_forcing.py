@@ -9,6 +9,13 @@ logits that close can trade places under the rounding noise that tolerance
 allows -- and the oracle then continues with the GPU's experts, so later
 layers compare like with like on every row.  At most MAX_FLIP_FRAC of the
 rows may take such a swap in any one layer of a pass.
+
+The top-k truncated sampler's vocabulary selection is forced the same way
+(TopkForcing): the GPU's selection is the top k of the logits it wrote (the
+fused head computes the same values; the test checks that by re-running the
+GPU sampler on those logits), and where it differs from the oracle's, the
+swapped ids must be within twice the row's measured logit discrepancy in the
+oracle's logits.
 """
 import numpy as np
 
@@ -16,6 +23,7 @@ from _util import log
 
 ROUTER_TOL = {"bf16": 2e-2, "f32": 1e-4}
 MAX_FLIP_FRAC = 0.10
+MAX_TOPK_SWAP_FRAC = 0.10
 
 
 class RouteForcing:
@@ -70,6 +78,42 @@ class RouteForcing:
         log(f"[{self.tag}] near-tie expert swaps per layer {self.flips.tolist()} (max {frac.max():.3f} of the rows); "
             f"router drift max {self.drift_max:.2e} ({self.drift_rel_max:.2e} of the row scale)")
         assert frac.max() <= MAX_FLIP_FRAC, f"{self.tag}: {frac.max():.3f} of a layer's rows took expert swaps"
+
+
+class TopkForcing:
+    """The top-k sampler's selection, forced from the GPU's logits gl [requests][n][V]."""
+
+    def __init__(self, gl, k, tag):
+        self.gl, self.k, self.tag = gl, k, tag
+        self.swaps = 0
+        self.rows = 0
+
+    def __call__(self, b, logits):
+        k = self.k
+        g = self.gl[b].astype(np.float32)
+        r = np.asarray(logits, np.float32)
+        dl = np.abs(g.astype(np.float64) - r).max(axis=1)
+        out = [None] * r.shape[0]
+        for i in range(r.shape[0]):
+            gs = np.sort(np.argsort(-g[i], kind="stable")[:k])
+            os_ = np.sort(np.argsort(-r[i], kind="stable")[:k])
+            if np.array_equal(gs, os_):
+                continue
+            gin = np.setdiff1d(gs, os_)          # taken by the GPU only
+            oin = np.setdiff1d(os_, gs)          # taken by the oracle only
+            gap = float(r[i, oin].astype(np.float64).max() - r[i, gin].astype(np.float64).min())
+            assert gap <= 2.0 * dl[i] * (1 + 1e-6), (
+                f"{self.tag} row {i}: GPU top-{k} ids {gs.tolist()} vs oracle {os_.tolist()}: the swapped ids "
+                f"are {gap:.3e} apart in the oracle's logits, beyond twice the row's discrepancy {dl[i]:.3e}")
+            out[i] = gs
+            self.swaps += 1
+        self.rows += r.shape[0]
+        return out
+
+    def finish(self):
+        frac = self.swaps / max(self.rows, 1)
+        log(f"[{self.tag}] near-tie top-{self.k} selection swaps {self.swaps} of {self.rows} rows ({frac:.3f})")
+        assert frac <= MAX_TOPK_SWAP_FRAC, f"{self.tag}: {frac:.3f} of the rows took top-k selection swaps"
 
 
 def gpu_routing(mc, eng, batch, rows, reqs):

@@ -77,6 +77,8 @@ def test_null_handles(lib):
     assert lib.dg_denoise_step(None, None, 0, None, None, None, None, None, None, None, None, None) == -1
     assert lib.dg_sample_commit(None, None, None, None, None, 0, None, None, None, None, None, None) == -1
     assert lib.dg_commit_canvas_to_kv(None, None, None, None) == -1
+    assert lib.dg_corrupt_forward_loss(None, None, None, None, None, None, None, None) == -1
+    assert lib.dg_model_view(None, 0, 0, None, None) == -1
     assert lib.dg_run_canvas(None, None, None, None, None, None, None, None, None, None, None, 0, 1, 0, None, None) == -1
     assert lib.dg_state_ctx_len(None) == -1
     sz = ctypes.c_size_t()

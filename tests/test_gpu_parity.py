@@ -26,7 +26,7 @@ from oracle import numerics as nm
 from oracle import sampler as osmp
 from oracle.model import OracleModel
 
-from _forcing import RouteForcing, gpu_routing
+from _forcing import RouteForcing, TopkForcing, gpu_routing
 from _util import log, make_engine, micro, rel_err_rows, replace, tol_for
 
 pytestmark = pytest.mark.gpu
@@ -187,7 +187,7 @@ def test_commit_bit_exact_on_identical_inputs(torch_cuda):
 
 
 def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=True, canvases=1,
-                oracle_reqs=None, sp_max_steps=None, determinism=False):
+                oracle_reqs=None, sp_max_steps=None, determinism=False, top_k=0):
     """GPU engine over `batch` requests against the oracle on `oracle_reqs` (default: all).
 
     The prompt is encoded in canvas-length chunks, each compared (routing) and
@@ -251,7 +251,7 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
     if check_kv and P > 0:
         check_cache(0, P, "prompt")
     S = sp_max_steps or steps
-    sp = di.SamplerConfig(max_steps=S, entropy_bound=0.5, stop_mode=0)
+    sp = di.SamplerConfig(max_steps=S, entropy_bound=0.5, stop_mode=0, top_k=top_k)
     for c in range(canvases):
         canvas = np.stack([osmp.init_canvas(int(oseeds[j]), om.canvas_index, n, mc.vocab) for j in range(nb)])
         eng.init_canvas()
@@ -267,12 +267,31 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
             got = {"H": eng.H[ridx].cpu().numpy(), "y": eng.y[ridx].cpu().numpy(),
                    "am": eng.am[ridx].cpu().numpy(), "margin": eng.margin[ridx].cpu().numpy(),
                    "logits": logits[ridx].cpu().numpy()}
+            tf = None
+            if top_k:
+                # the fused head's selection is the top k of the logits it wrote: the GPU sampler
+                # run on those logits repeats the step's outputs bit for bit
+                fused = {k_: eng_v.clone() for k_, eng_v in (("H", eng.H), ("y", eng.y), ("am", eng.am),
+                                                             ("margin", eng.margin))}
+                s_fused = eng.self_cond_view().clone() if mc.self_cond else None
+                eng.sample_logits(t, sp, logits)
+                torch.cuda.synchronize()
+                for k_, v_ in fused.items():
+                    assert torch.equal(getattr(eng, k_), v_), \
+                        f"{tag} canvas {c} step {t}: fused top-k head {k_} differs from the sampler on its logits"
+                if s_fused is not None:
+                    assert torch.equal(eng.self_cond_view(), s_fused), f"{tag}: fused top-k self-conditioning"
+                tf = TopkForcing(got["logits"], top_k, f"{tag} canvas {c} step {t}")
             del logits
             rf = forced(n, f"canvas {c} step {t}")
             om.route_override = rf
+            om.topk_override = tf
             ref = om.denoise_step(canvas, t, sp, oseeds, want_logits=True)
             om.route_override = None
+            om.topk_override = None
             rf.finish()
+            if tf is not None:
+                tf.finish()
             _compare_step(mc, got, ref, f"{tag} canvas {c} step {t}")
             if mc.self_cond:
                 # s = sum_v p_v E_v.  A logit discrepancy dz (max over the row, z units) perturbs the terms by
@@ -603,3 +622,54 @@ def test_fp8_proxy_shapes_two_layers(torch_cuda):
     # the proxy's expert shapes (128 experts top-8, d 2048, F 768) in FP8, 2 of its 30 layers
     mc = replace(di.workload("proxy-fp8").model, n_layers=2)
     _run_parity(torch_cuda, mc, 2, 256, 1, 1, "fp8-proxy-2L", sp_max_steps=48)
+
+
+# ------------------------------------------------------------------ top-k truncated sampler
+@pytest.mark.parametrize("kind", ["random", "peaked", "ties", "uniform"])
+def test_topk_sampler_on_identical_logits(torch_cuda, kind):
+    torch = torch_cuda
+    mc = micro(n_layers=1, vocab=4160)          # 32.5 chunks: a ragged last segment
+    W = di.make_weights(mc, 23)
+    B, n = 2, mc.canvas_len
+    eng = make_engine(mc, W, B, 512)
+    seeds = di.request_seeds(23, B)
+    eng.set_seeds(seeds)
+    rng = np.random.default_rng(hash(kind) % 2**32 + 1)
+    lg = _crafted_logits(rng, B, n, mc.vocab, kind)
+    E = nm.upcast(W.get("emb"))
+    for k, (t, S) in ((8, (0, 12)), (3, (11, 12)), (1, (5, 12))):
+        sp = di.SamplerConfig(max_steps=S, entropy_bound=0.1, top_k=k)
+        eng.sample_logits(t, sp, torch.from_numpy(lg).cuda())
+        torch.cuda.synchronize()
+        inv_t = osmp.inv_temperature(osmp.temperature(t, S))
+        for b in range(B):
+            st = osmp.head_stats_topk(lg[b], inv_t, k, int(seeds[b]), 0, t, np.arange(n), want_probs=True)
+            gy, gam = eng.y[b].cpu().numpy(), eng.am[b].cpu().numpy()
+            gH, gm = eng.H[b].cpu().numpy(), eng.margin[b].cpu().numpy()
+            assert np.array_equal(gam, st["am"]), f"{kind} k={k}: argmax differs"
+            tie = st["margin"] < 1e-4
+            assert np.array_equal(gy[~tie], st["y"][~tie]), f"{kind} k={k}: sampled tokens differ"
+            assert np.abs(gH.astype(np.float64) - st["H"]).max() < 1e-5, f"{kind} k={k}: entropy"
+            fin = np.isfinite(st["margin"]) & ~tie
+            assert np.abs(gm[fin] - st["margin"][fin]).max(initial=0) < 1e-4
+            s_ref = np.einsum("nk,nkd->nd", st["p"], E[st["ids"]])
+            es = rel_err_rows(eng.self_cond_view()[b].cpu().numpy(), s_ref)
+            assert es.max() < tol_for(mc), f"{kind} k={k}: self-conditioning rel err {es.max()}"
+            log(f"[top-k sampler {kind} k={k} b={b}] ties {int(tie.sum())}, s rel {es.max():.1e}")
+
+
+def test_topk_denoise_steps_micro(torch_cuda):
+    mc = micro(n_layers=2, vocab=4096)
+    _run_parity(torch_cuda, mc, 24, 300, 2, 3, "topk-micro", gain_std=0.1, top_k=8, determinism=True)
+
+
+def test_topk_small_workload(torch_cuda):
+    wl = di.workload("small")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 2, "topk-small", top_k=8)
+
+
+def test_topk_batched_workload_sampled(torch_cuda):
+    # the high-batch shape the truncation is for: 32 requests x 4096-token prompts, requests 0 and 31 checked
+    wl = di.workload("batched")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, wl.batch, 2, "topk-batched", oracle_reqs=[0, 31],
+                sp_max_steps=wl.sampler.max_steps, top_k=8)

@@ -653,3 +653,137 @@ def test_e4m3_row_quantisation():
     # relative error of a quantised weight: at most half an ulp of 3 mantissa bits (1/16) above the subnormals
     big = np.abs(w) >= 2.0 ** -6 * s[:, None]
     assert (np.abs(deq - w)[big] <= np.abs(w)[big] / 16 + 1e-12).all()
+
+
+# ------------------------------------------------------------------ training-side corruption and loss
+def test_corruption_rates_and_uniform_replacement():
+    from oracle import training as tr
+    V, n = 64, 256
+    clean = np.arange(n, dtype=np.int32) % V
+    # rate 0: nothing changes; rate 1: every position redrawn (a redraw may hit the clean token)
+    x0, r0 = tr.corrupt(clean, 0.0, 5, 0, V)
+    assert np.array_equal(x0, clean) and not r0.any()
+    x1, r1 = tr.corrupt(clean, 1.0, 5, 0, V)
+    assert r1.all()
+    # the replaced fraction follows the rate (binomial, 5 sigma over 200 canvases)
+    hits, toks = 0, []
+    for s in range(200):
+        x, r = tr.corrupt(clean, 0.3, s, 0, V)
+        hits += int(r.sum())
+        toks.append(x[r])
+        assert np.array_equal(x[~r], clean[~r])
+    N = 200 * n
+    assert abs(hits - 0.3 * N) < 5 * np.sqrt(N * 0.3 * 0.7)
+    c = np.bincount(np.concatenate(toks), minlength=V).astype(np.float64)
+    e = c.sum() / V
+    assert ((c - e) ** 2 / e).sum() < 140                     # df = 63
+    # the draws are the counter layout's: word 0 of the call decides, word 1 is the token
+    w = philox.philox4x32_10(np.array([0, 7, 0, (tr.TAG_CORRUPT << 24) | 3], np.uint32),
+                             philox.seed_key(11))
+    x, r = tr.corrupt(np.zeros(8, np.int32), 0.5, 11, 3, V)
+    assert r[7] == (philox.uniform01(w[0:1])[0] < np.float32(0.5))
+    assert x[7] == (philox.uniform_token(w[1:2], V)[0] if r[7] else 0)
+
+
+def test_denoising_cross_entropy_closed_forms():
+    from oracle import training as tr
+    V = 512
+    # uniform logits: CE = log V for any target
+    assert np.allclose(tr.logsumexp(np.zeros((3, V))) - 0.0, math.log(V), rtol=0, atol=1e-12)
+    # a dominant logit at the target: CE -> 0; at another id: CE ~ the gap
+    lg = np.zeros(V)
+    lg[7] = 50.0
+    assert tr.logsumexp(lg) - lg[7] < 1e-19
+    assert abs((tr.logsumexp(lg) - lg[8]) - 50.0) < 1e-12
+    # the explicit formula -log softmax(l)[t] by a per-element loop on a small vocabulary
+    rng = np.random.default_rng(14)
+    l = rng.standard_normal(9) * 3
+    for t in range(9):
+        p = math.exp(l[t]) / sum(math.exp(v) for v in l)
+        assert abs((tr.logsumexp(l) - l[t]) - (-math.log(p))) < 1e-12
+
+
+def test_forward_loss_scores_the_clean_tokens():
+    from oracle import training as tr
+    cfg = _micro_cfg(dtype="f32", E=4, k=2, L=1)
+    W = di.make_weights(cfg, 15)
+    m = OracleModel(cfg, W, 2, 32)
+    m.encode_prompt(np.array([[1, 2, 3], [4, 5, 6]]))
+    clean = np.array([[3, 9, 1, 15, 0], [2, 2, 7, 0, 11]], np.int32)
+    out = tr.forward_loss(m, clean, [0.0, 1.0], np.array([3, 4], np.uint64), want_logits=True)
+    assert np.array_equal(out["corrupted"][0], clean[0])            # rate 0 keeps the canvas
+    assert out["replaced"][1].all()
+    for b in range(2):
+        lg = out["logits"][b]
+        for i in range(5):
+            ce = -math.log(math.exp(lg[i, clean[b, i]]) / sum(math.exp(v) for v in lg[i]))
+            assert abs(out["ce"][b, i] - ce) < 1e-12
+        assert abs(out["loss"][b] - out["ce"][b].mean()) < 1e-15
+    # the rate-0 request's logits are the denoising round's on the same canvas
+    sp = di.SamplerConfig(max_steps=4, entropy_bound=0.1)
+    ref = m.denoise_step(clean, 0, sp, np.array([3, 4], np.uint64), want_logits=True)
+    assert np.allclose(out["logits"][0], ref["logits"][0], rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ top-k truncated sampler
+def test_topk_truncation_special_cases():
+    V = 4096
+    rng = np.random.default_rng(16)
+    lg = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    full = smp.head_stats(lg, np.float32(1.25), 3, 1, 2, np.arange(6))
+    # k = V: the truncated distribution is the full one (same draws, same statistics)
+    allk = smp.head_stats_topk(lg, np.float32(1.25), V, 3, 1, 2, np.arange(6))
+    assert np.array_equal(allk["y"], full["y"]) and np.array_equal(allk["am"], full["am"])
+    assert np.allclose(allk["H"], full["H"], rtol=1e-6)
+    assert np.allclose(allk["margin"], full["margin"], atol=1e-6)
+    # k = 1: the argmax with probability 1, entropy 0
+    one = smp.head_stats_topk(lg, np.float32(1.25), 1, 3, 1, 2, np.arange(6))
+    assert np.array_equal(one["y"], full["am"]) and np.all(one["H"] == 0)
+    # k = 8: entropy at most log 8, the sample among the 8 largest logits, ids in descending order
+    k8 = smp.head_stats_topk(lg, np.float32(1.25), 8, 3, 1, 2, np.arange(6), want_probs=True)
+    for r in range(6):
+        top = np.argsort(-lg[r], kind="stable")[:8]
+        assert list(k8["ids"][r]) == list(top)
+        assert k8["y"][r] in top and 0 <= k8["H"][r] <= math.log(8) + 1e-6
+        z = lg[r, top].astype(np.float64) * np.float64(np.float32(1.25))
+        p = np.exp(z - z.max()); p /= p.sum()
+        assert np.allclose(k8["p"][r], p) and abs(k8["H"][r] + (p * np.log(p)).sum()) < 1e-5
+    # uniform logits: the lowest k ids, entropy exactly log k
+    u = smp.head_stats_topk(np.zeros((1, V), np.float32), np.float32(1.0), 8, 3, 1, 2, np.arange(1))
+    assert list(u["ids"][0]) == list(range(8)) and u["H"][0] == np.float32(math.log(8))
+
+
+def test_topk_gumbel_max_frequencies():
+    # over many positions the truncated sample follows the renormalised top-k softmax (chi-square)
+    z = np.log(np.array([0.3, 0.25, 0.2, 0.1, 0.05, 0.04, 0.03, 0.03]))
+    n = 20000
+    lg = np.tile(z.astype(np.float32), (n, 1))
+    st = smp.head_stats_topk(lg, np.float32(1.0), 4, 11, 0, 0, np.arange(n))
+    c = np.bincount(st["y"], minlength=8).astype(np.float64)
+    assert c[4:].sum() == 0
+    p = np.exp(z[:4]) / np.exp(z[:4]).sum()
+    chi2 = ((c[:4] - n * p) ** 2 / (n * p)).sum()
+    assert chi2 < 25                                             # df = 3
+
+
+def test_topk_forced_selection():
+    # a forced id set equal to the row's own selection changes nothing; another set is
+    # reordered by logit and the statistics are those of its renormalised softmax
+    V = 512
+    rng = np.random.default_rng(17)
+    lg = (rng.standard_normal((3, V)) * 2).astype(np.float32)
+    own = smp.head_stats_topk(lg, np.float32(1.0), 4, 5, 0, 1, np.arange(3), want_probs=True)
+    same = smp.head_stats_topk(lg, np.float32(1.0), 4, 5, 0, 1, np.arange(3), want_probs=True,
+                               forced_ids=[own["ids"][0][::-1].copy(), None, None])
+    for key in ("H", "y", "am", "margin", "ids", "p"):
+        assert np.array_equal(own[key], same[key])
+    alt = np.argsort(-lg[1], kind="stable")[[0, 1, 2, 4]]          # the 4th largest swapped for the 5th
+    f = smp.head_stats_topk(lg, np.float32(1.0), 4, 5, 0, 1, np.arange(3), want_probs=True,
+                            forced_ids=[None, alt[::-1].copy(), None])
+    assert list(f["ids"][1]) == list(alt)
+    z = lg[1, alt].astype(np.float64)
+    p = np.exp(z - z.max()); p /= p.sum()
+    assert np.allclose(f["p"][1], p) and abs(f["H"][1] + (p * np.log(p)).sum()) < 1e-5
+    assert f["y"][1] in alt
+    for key in ("H", "y", "am", "margin"):
+        assert f[key][0] == own[key][0] and f[key][2] == own[key][2]
