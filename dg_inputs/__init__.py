@@ -249,6 +249,14 @@ class WeightSet:
             self._store[name] = arr
         return arr
 
+    def scale_by_power_of_two(self, name: str, exponent: int) -> None:
+        """Multiply one cached tensor by 2^exponent (exact in fp32 and bf16 while in range)."""
+        assert self.cache, "scaling needs the cached weights"
+        arr = self.get(name)
+        f = bf16_bits_to_f32(arr) if arr.dtype == np.uint16 else arr
+        f = np.ldexp(f, exponent).astype(np.float32)
+        self._store[name] = f32_to_bf16_bits(f) if arr.dtype == np.uint16 else f
+
     def items(self) -> Iterator[Tuple[str, np.ndarray]]:
         for n in self.names():
             yield n, self.get(n)

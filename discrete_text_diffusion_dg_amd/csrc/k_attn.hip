@@ -90,9 +90,16 @@ __device__ __forceinline__ void store4(T* dst, const float* v) {
 }
 
 // ---- wide: 16 * NWQ query rows per workgroup sharing LDS-staged K / V^T tiles
-// bf16 V^T pieces are staged as fp16 (exact for |v| in [2^-14, 65504]) so that
-// the probabilities enter O^T += V^T P as one fp16 operand (11 significant
-// bits) instead of a two-term bf16 split.
+// bf16 V^T pieces are staged as fp16 so that the probabilities enter
+// O^T += V^T P as one fp16 operand (11 significant bits) instead of a two-term
+// bf16 split.  The conversion is exact for bf16 values with 2^-17 <= |v| <
+// 2^16 (fp16's largest finite value is 65504; every bf16 value below 2^16 is
+// at most 65280); smaller ones are rounded to fp16's 2^-24 grid.  A tile whose
+// largest |v| is 2^16 or more, or below 2^-14, is staged instead as
+// fp16(v * 2^-s), s chosen so that its largest |v| lands in [2^14, 2^15), and
+// its products are taken as O = 2^s (2^-s O + V'^T P): exact power-of-two
+// scalings around the same fp16 products.  Either way each staged value is
+// within 2^-11 of its tile's largest |v| of the exact one.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
@@ -105,6 +112,30 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) r[j] = f32x2_to_f16x2(__uint_as_float(w[j] << 16), __uint_as_float(w[j] & 0xFFFF0000u));
   return make_uint4(r[0], r[1], r[2], r[3]);
+}
+// Largest biased exponent (the 8-bit field) among eight bf16 values.
+__device__ __forceinline__ uint32_t bf16x8_max_exp(uint4 x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7F80u, (w[j] >> 16) & 0x7F80u));
+  return m >> 7;
+}
+// fp16(v * 2^-s) of eight bf16 values (the scaling is exact in fp32).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_scaled(uint4 x, int s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = f32x2_to_f16x2(__builtin_amdgcn_ldexpf(__uint_as_float(w[j] << 16), -s),
+                          __builtin_amdgcn_ldexpf(__uint_as_float(w[j] & 0xFFFF0000u), -s));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+constexpr uint32_t kF16ExpHi = 127 + 16;   // |v| >= 2^16: beyond fp16
+constexpr uint32_t kF16ExpLo = 127 - 14;   // |v| >= 2^-14: fp16 normal
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  butterfly_steps([&](auto st) { v = max(v, lane_partner<decltype(st)::value>(v)); });
+  return v;
 }
 __device__ __forceinline__ void mma16x16x32_f16(f32x4_t& acc, uint4 a, uint4 b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc, 0,
@@ -134,6 +165,9 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   static_assert(KCH >= 1 && VCH >= 1 && KT * CH_PER_KEY % NTH == 0 && HD * (KT / EPC) % NTH == 0, "tile shape");
   static_assert(QBW == 1 || sizeof(T) == 2, "several query blocks per wave: bf16 path only");
   __shared__ __attribute__((aligned(16))) T smem[2 * (KBUF + VBUF)];
+  // per stage and wave: bit 0 some |v| >= 2^16, bit 1 some |v| >= 2^-14 (bf16)
+  __shared__ uint32_t s_vflag[2][NWQ];
+  __shared__ uint32_t s_vexp[NWQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4, q16 = lane & 15;
   const int G = a.Hq / a.Hkv, rows_total = G * a.nq;
@@ -233,6 +267,49 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
       if constexpr (sizeof(T) == 2) v = bf16x8_to_f16x8(v);
       *reinterpret_cast<uint4*>(sV + (c / (KT / EPC)) * LDV + (c % (KT / EPC)) * EPC) = v;
     }
+    if constexpr (sizeof(T) == 2) {
+      uint32_t em = 0;
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) em = max(em, bf16x8_max_exp(SL == 0 ? vr0[i] : vr1[i]));
+      const bool hi = __ballot(em >= kF16ExpHi) != 0, nrm = __ballot(em >= kF16ExpLo) != 0;
+      if (lane == 0) s_vflag[buf][w] = (hi ? 1u : 0u) | (nrm ? 2u : 0u);
+    }
+  };
+  // After the barrier that publishes stage `buf`: a tile outside fp16's range
+  // is staged again, scaled by 2^-s (workgroup-uniform branch), and s kept for
+  // its products; 0 for a tile staged as is.
+  int vsc0 = 0, vsc1 = 0;
+  auto vrange = [&](auto slot, int buf) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2) {
+      constexpr int SL = decltype(slot)::value;
+      uint32_t f = 0;
+#pragma unroll
+      for (int j = 0; j < NWQ; ++j) f |= s_vflag[buf][j];
+      f = __builtin_amdgcn_readfirstlane(f);
+      int sc = 0;
+      if ((f & 1u) || !(f & 2u)) {
+        uint32_t em = 0;
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) em = max(em, bf16x8_max_exp(SL == 0 ? vr0[i] : vr1[i]));
+        em = wave_max_u32(em);
+        if (lane == 0) s_vexp[w] = em;
+        lds_barrier();
+        uint32_t e = 0;
+#pragma unroll
+        for (int j = 0; j < NWQ; ++j) e = max(e, s_vexp[j]);
+        e = __builtin_amdgcn_readfirstlane(e);
+        sc = min(max((int)e - 127 - 14, -100), 113);   // never 0 here: e >= 143 or e < 113
+        T* sV = smem + buf * (KBUF + VBUF) + KBUF;
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int c = tid + NTH * i;
+          *reinterpret_cast<uint4*>(sV + (c / (KT / EPC)) * LDV + (c % (KT / EPC)) * EPC) =
+              bf16x8_to_f16x8_scaled(SL == 0 ? vr0[i] : vr1[i], sc);
+        }
+        lds_barrier();
+      }
+      if (buf == 0) vsc0 = sc; else vsc1 = sc;
+    }
   };
   auto compute = [&](int buf, int t) __attribute__((always_inline)) {
     const T* sK = smem + buf * (KBUF + VBUF);
@@ -296,6 +373,14 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
         pf[qb][1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
       }
       // O^T[d][q] += V^T[d][keys] P[keys][q]; each V^T fragment serves every query block
+      const int vs = buf == 0 ? vsc0 : vsc1;
+      if (vs != 0) {                       // the tile was staged as V * 2^-vs
+        const float f = __builtin_amdgcn_ldexpf(1.f, -vs);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[qb][db] *= f;
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -306,6 +391,13 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
         }
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) mma16x16x32_f16(osum[qb], ones16, pf[qb][ks]);
+      }
+      if (vs != 0) {
+        const float f = __builtin_amdgcn_ldexpf(1.f, vs);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[qb][db] *= f;
       }
     } else {
       float p[16];
@@ -362,11 +454,14 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   // tile t: its data came through register slot t % 2 into LDS stage t % 2.
   // Tile t + 2 is loaded into slot t % 2 while tile t is computed; tile t + 1
   // (slot (t + 1) % 2, loaded during tile t - 1) is staged at the end.
+  // vrange(slot, stage) follows each barrier that publishes a staged tile,
+  // while its register slot still holds the tile.
   if (ntiles > 0) {
     gload(S0{}, 0);
     gload(S1{}, min(1, ntiles - 1));
     sstore(S0{}, 0);
     lds_barrier();
+    vrange(S0{}, 0);
   }
   int t = 0;
   for (; t + 3 < ntiles; t += 2) {          // every load here exists
@@ -374,10 +469,12 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
     compute(0, t);
     sstore(S1{}, 1);
     lds_barrier();
+    vrange(S1{}, 1);
     gload(S1{}, t + 3);
     compute(1, t + 1);
     sstore(S0{}, 0);
     lds_barrier();
+    vrange(S0{}, 0);
   }
   // at most three tiles left (t even): loads only for tiles that exist
   if (t < ntiles) {
@@ -385,11 +482,13 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
     compute(0, t);
     if (t + 1 < ntiles) sstore(S1{}, 1);
     lds_barrier();
+    if (t + 1 < ntiles) vrange(S1{}, 1);
   }
   if (t + 1 < ntiles) {
     compute(1, t + 1);
     if (t + 2 < ntiles) sstore(S0{}, 0);
     lds_barrier();
+    if (t + 2 < ntiles) vrange(S0{}, 0);
   }
   if (t + 2 < ntiles) compute(0, t + 2);
 

@@ -187,7 +187,7 @@ def test_commit_bit_exact_on_identical_inputs(torch_cuda):
 
 
 def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=True, canvases=1,
-                oracle_reqs=None, sp_max_steps=None, determinism=False, top_k=0):
+                oracle_reqs=None, sp_max_steps=None, determinism=False, top_k=0, v_scale_exp=0):
     """GPU engine over `batch` requests against the oracle on `oracle_reqs` (default: all).
 
     The prompt is encoded in canvas-length chunks, each compared (routing) and
@@ -197,6 +197,12 @@ def _run_parity(torch, mc, seed, P, batch, steps, tag, gain_std=0.0, check_kv=Tr
     steps, two steps are run twice from the same inputs and every output
     compared bit for bit."""
     W = di.make_weights(mc, seed, gain_std=gain_std)
+    if v_scale_exp:
+        # V (the cache and the attention output) scaled by 2^e, the output projection by 2^-e:
+        # the residual stream keeps its scale while attention sees values outside fp16's range
+        for l in range(mc.n_layers):
+            W.scale_by_power_of_two(f"l{l}.wv", v_scale_exp)
+            W.scale_by_power_of_two(f"l{l}.wo", -v_scale_exp)
     reqs = list(range(batch)) if oracle_reqs is None else list(oracle_reqs)
     nb = len(reqs)
     n = mc.canvas_len
@@ -428,6 +434,17 @@ def test_micro_many_requests_wide_attention_f32(torch_cuda):
     mc = micro(n_layers=1, dtype="f32", n_q_heads=16, n_kv_heads=8, head_dim=64, n_experts=8, top_k=2,
                vocab=2048)
     _run_parity(torch_cuda, mc, 18, 40, 16, 2, "micro-wide-f32", oracle_reqs=[0, 15])
+
+
+@pytest.mark.parametrize("e", [20, -24])
+def test_attention_values_beyond_fp16_range(torch_cuda, e):
+    # V ~ 0.3 * 2^e: 2^20 puts |v| near 3e5, past fp16's 65504; 2^-24 puts it near 2e-8, under fp16's
+    # smallest subnormal.  One request takes the spread kernel (bf16 V in its products), sixteen take
+    # the wide kernel (V staged as fp16, rescaled tile by tile when out of range); both on the oracle.
+    mc = micro(n_layers=1, vocab=2048)
+    _run_parity(torch_cuda, mc, 31, 300, 1, 2, f"v-2^{e}-spread", v_scale_exp=e)
+    mcw = micro(n_layers=1, n_q_heads=16, n_kv_heads=8, head_dim=64, n_experts=8, top_k=2, vocab=2048)
+    _run_parity(torch_cuda, mcw, 32, 300, 16, 2, f"v-2^{e}-wide", oracle_reqs=[0, 15], v_scale_exp=e)
 
 
 def test_micro_ragged_vocabulary_full_step(torch_cuda):
