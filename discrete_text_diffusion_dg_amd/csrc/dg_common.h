@@ -186,6 +186,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup bid runs on XCD
+// bid % 8), each with its own L2; xcd_run gives XCD x a contiguous run of the
+// `total` logical tiles (bid < total), so neighbouring tiles meet in one L2.
+__device__ __forceinline__ int xcd_run(int bid, int total) {
+  const int q = total >> 3, r = total & 7, x = bid & 7;
+  return x * q + min(x, r) + (bid >> 3);
+}
+
 // Workgroup barrier for LDS hand-overs: orders this wave's LDS writes before
 // the barrier and the other waves' LDS reads after it (s_waitcnt lgkmcnt(0);
 // s_barrier), without waiting for the wave's outstanding global loads, which

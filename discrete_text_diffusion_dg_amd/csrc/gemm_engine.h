@@ -56,12 +56,7 @@ struct TileCfg {
 };
 
 // ------------------------------------------------------------------ schedulers
-// Workgroups are dealt round-robin over the 8 XCDs (workgroup bid runs on XCD
-// bid % 8); xcd_run gives XCD x a contiguous run of the `total` logical tiles.
-__device__ __forceinline__ int xcd_run(int bid, int total) {
-  const int q = total >> 3, r = total & 7, x = bid & 7;
-  return x * q + min(x, r) + (bid >> 3);
-}
+// (xcd_run, in dg_common.h, gives each XCD a contiguous run of logical tiles)
 
 // Dense tiles in bands of kBandRows row tiles: within a band the row tiles
 // vary fastest, then the column tiles, so the workgroups resident on one XCD

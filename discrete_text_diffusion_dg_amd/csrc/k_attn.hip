@@ -743,6 +743,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
 }
 
 // One thread per (row, 4 dims): combine the split partials in split order.
+constexpr int kMaxAttnSplits = 16;   // key splits of one launch (the merge unrolls over them)
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const size_t nrows = (size_t)a.B * a.nq * a.Hq;
@@ -750,16 +752,28 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const size_t rowid = gid / (HD / 4);
   const int d0 = (int)(gid % (HD / 4)) * 4;
   if (rowid >= nrows || !a.gate.active((int)(rowid / a.Hq / a.nq))) return;
+  // every split's (max, sum) and output piece are loaded before the first
+  // use (at most kMaxAttnSplits), so the loads are one round trip, not one per split
+  float2 ml[kMaxAttnSplits];
+  float4 po[kMaxAttnSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s) {
+    if (s < a.splits) {
+      ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * nrows + rowid) * 2);
+      po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * nrows + rowid) * HD + d0);
+    }
+  }
   float m = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, a.part_ml[(s * nrows + rowid) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s)
+    if (s < a.splits) m = fmaxf(m, ml[s].x);
   float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = a.part_ml[(s * nrows + rowid) * 2];
-    if (ms == -INFINITY) continue;
-    const float f = expf(ms - m);
-    l += a.part_ml[(s * nrows + rowid) * 2 + 1] * f;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_o + (s * nrows + rowid) * HD + d0);
-    acc[0] += v.x * f; acc[1] += v.y * f; acc[2] += v.z * f; acc[3] += v.w * f;
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s) {
+    if (s >= a.splits || ml[s].x == -INFINITY) continue;
+    const float f = expf(ml[s].x - m);
+    l += ml[s].y * f;
+    acc[0] += po[s].x * f; acc[1] += po[s].y * f; acc[2] += po[s].z * f; acc[3] += po[s].w * f;
   }
   const float inv = 1.f / l;
   const int head = (int)(rowid % a.Hq);
@@ -836,7 +850,7 @@ int attention_splits(int B, int nq, int Hq, int Hkv, int hd, int keys, int elem_
     const int max_by_keys = tiles / 4;
     if (splits > max_by_keys) splits = max_by_keys;
   }
-  if (splits > 16) splits = 16;
+  if (splits > kMaxAttnSplits) splits = kMaxAttnSplits;
   if (splits < 1) splits = 1;
   return splits;
 }

@@ -358,18 +358,23 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const W
     }
 }
 
-// Grid: x = N / (16 * NW) feature-block groups (exact), y = tile capacity
-// (tiles past n_tiles exit; the exit is uniform over the workgroup, so every
-// wave reaches the same barriers).
+// Grid: groups = N / (16 * NW) feature-block groups (exact) times the tile
+// capacity, one dimension.  The first groups * n_tiles workgroups take
+// (tile, group) pairs, tile-major, in contiguous runs per XCD: the groups of a
+// tile and the neighbouring tiles (an expert's row tiles are adjacent in the
+// list) run together on one XCD, so an expert's weight slices streamed for
+// several row tiles are fetched from HBM once into that XCD's L2.  The rest
+// exit (uniformly over the workgroup, so every wave reaches the same barriers).
 template <typename T, typename WT, bool GATEUP, int NW, int PD, int KC>
 __global__ __launch_bounds__(64 * NW, 2) void k_expert_stream(const T* X, const int* perm, const WT* Wp,
                                                               const float* scale, void* out, const int4* tiles,
                                                               const int* n_tiles, int K, int N) {
   __shared__ __attribute__((aligned(16))) T lds[2 * 64 * (KC * SubSteps<WT>::value * 32 + 16 / sizeof(T))];
-  const int ti = blockIdx.y;
-  if (ti >= *n_tiles) return;
+  const int groups = N / (16 * NW), total = groups * *n_tiles;
+  if ((int)blockIdx.x >= total) return;
+  const int lg = xcd_run(blockIdx.x, total), ti = lg / groups;
   const int4 td = tiles[ti];
-  const int nb = blockIdx.x * NW + (int)(threadIdx.x >> 6);
+  const int nb = (lg % groups) * NW + (int)(threadIdx.x >> 6);
   switch ((td.z + 15) >> 4) {
     case 1: stream_body<T, WT, GATEUP, 1, NW, PD, KC>(X, perm, Wp, scale, out, td.x, td.y, td.z, K, N, nb, lds); break;
     case 2: stream_body<T, WT, GATEUP, 2, NW, PD, KC>(X, perm, Wp, scale, out, td.x, td.y, td.z, K, N, nb, lds); break;
@@ -433,7 +438,7 @@ hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, cons
                                 const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
   constexpr int NW = kStreamWaves;
   using C = StreamCfg<WT, true>;
-  hipLaunchKernelGGL((k_expert_stream<T, WT, true, NW, C::PD, C::KC>), dim3(F / (16 * NW), cap_tiles),
+  hipLaunchKernelGGL((k_expert_stream<T, WT, true, NW, C::PD, C::KC>), dim3(F / (16 * NW) * cap_tiles),
                      dim3(64 * NW), 0, s, X, perm, pgu, scale, (void*)act, tiles, n_tiles, d, F);
   return hipGetLastError();
 }
@@ -443,7 +448,7 @@ hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, fl
                               const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
   constexpr int NW = kStreamWaves;
   using C = StreamCfg<WT, false>;
-  hipLaunchKernelGGL((k_expert_stream<T, WT, false, NW, C::PD, C::KC>), dim3(d / (16 * NW), cap_tiles),
+  hipLaunchKernelGGL((k_expert_stream<T, WT, false, NW, C::PD, C::KC>), dim3(d / (16 * NW) * cap_tiles),
                      dim3(64 * NW), 0, s, act, (const int*)nullptr, pd, scale, (void*)Y, tiles, n_tiles, F, d);
   return hipGetLastError();
 }
