@@ -142,8 +142,10 @@ struct StageTimer {
 static dg_status check_config(const dg_config* c) {
   if (!c) return fail(DG_ERR_ARG, "config is null");
   if (c->n_layers < 1) return fail(DG_ERR_ARG, "n_layers must be >= 1");
-  if (c->d_model < 256 || c->d_model % 256 || c->d_model > kMaxModel)
-    return fail(DG_ERR_UNSUPPORTED, "d_model must be a multiple of 256 in 256..%d", kMaxModel);
+  // the row kernels give each thread whole 4-element chunks of a row: 256..1024
+  // in steps of 256 (one chunk, d / 4 threads), then multiples of 1024 (256 threads)
+  if (c->d_model < 256 || c->d_model % 256 || c->d_model > kMaxModel || (c->d_model > 1024 && c->d_model % 1024))
+    return fail(DG_ERR_UNSUPPORTED, "d_model must be 256, 512, 768, 1024 or a multiple of 1024 up to %d", kMaxModel);
   if (c->head_dim != 64 && c->head_dim != 128) return fail(DG_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
     return fail(DG_ERR_ARG, "n_kv_heads must divide n_q_heads");

@@ -156,10 +156,16 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
   constexpr int NT = sizeof(T) == 2 ? 2 : 1;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int LDK = HD + EPC, LDV = KT + EPC;
+  // bf16 K rows are unpadded, their 16-byte pieces XOR-swizzled by kswz(key):
+  // the 16 keys a fragment read takes (tile_key over 16 lanes) then fall on 16
+  // distinct piece slots, where a padded row put rows r and r + 16 on the same
+  // banks.  fp32 rows keep one piece of padding.
+  constexpr bool KSWZ = sizeof(T) == 2;
+  constexpr int LDK = KSWZ ? HD : HD + EPC, LDV = KT + EPC;
   constexpr int KBUF = KT * LDK, VBUF = HD * LDV;     // elements per stage
   constexpr int NTH = 64 * NWQ;
   constexpr int CH_PER_KEY = HD / EPC;
+  auto kswz = [](int key) { return KSWZ ? ((key & 3) | (((key >> 3) & 3) << 2)) & (CH_PER_KEY - 1) : 0; };
   constexpr int KCH = KT * CH_PER_KEY / NTH, VCH = HD * (KT / EPC) / NTH;
   constexpr int RPW = 16 * NWQ;                        // query rows per query block of the workgroup
   static_assert(KCH >= 1 && VCH >= 1 && KT * CH_PER_KEY % NTH == 0 && HD * (KT / EPC) % NTH == 0, "tile shape");
@@ -258,7 +264,8 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + NTH * i;
-      *reinterpret_cast<uint4*>(sK + (c / CH_PER_KEY) * LDK + (c % CH_PER_KEY) * EPC) = SL == 0 ? kr0[i] : kr1[i];
+      const int kr = c / CH_PER_KEY;
+      *reinterpret_cast<uint4*>(sK + kr * LDK + ((c % CH_PER_KEY) ^ kswz(kr)) * EPC) = SL == 0 ? kr0[i] : kr1[i];
     }
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
@@ -325,7 +332,11 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         Frag<T> kf;
-        lds_frag(kf, sK + tile_key(kb, q16) * LDK + s * 32 + g4 * 8);
+        const int key = tile_key(kb, q16);
+        if constexpr (KSWZ)
+          lds_frag(kf, sK + key * LDK + ((s * 4 + g4) ^ kswz(key)) * EPC);
+        else
+          lds_frag(kf, sK + key * LDK + s * 32 + g4 * 8);
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) mma16x16x32(sc[qb][kb], kf, qf[qb][s]);
       }

@@ -117,55 +117,94 @@ __global__ __launch_bounds__(256) void k_embed_norm(const T* emb, const int32_t*
   norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
 }
 
-// h += sum_s part[s]; xn = rnd(rmsnorm(h) * g)
-template <typename T>
+// h += sum_s part[s]; xn = rnd(rmsnorm(h) * g).  NJ = d / (4 * threads)
+// chunks per thread; every chunk's partials (up to 8 splits at a time) and h
+// are loaded before the first sum, so the row costs one load round trip.
+template <typename T, int NJ>
 __global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int M, int d, const float* g, float eps,
                                                   float* H, T* xn, Gate gt, int n) {
-  const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  const int r = blockIdx.x;
   if (!gt.active(r / n)) return;
+  const size_t stride = (size_t)M * d;
   float4 v[kRowChunks];
+  float4 p[NJ];
 #pragma unroll
-  for (int j = 0; j < kRowChunks; ++j)
-    if (j < nj) {
-      const int c = (j * blockDim.x + threadIdx.x) * 4;
-      const float4 p = sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c);
-      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
-      add4(x, p);
-      v[j] = x;
-    }
-  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
+  for (int j = 0; j < NJ; ++j) p[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 pv[NJ][8];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        pv[j][u] = *reinterpret_cast<const float4*>(part + (size_t)min(s0 + u, S - 1) * stride + (size_t)r * d +
+                                                    (j * blockDim.x + threadIdx.x) * 4);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < S) add4(p[j], pv[j][u]);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + (j * blockDim.x + threadIdx.x) * 4);
+    add4(x, p[j]);
+    v[j] = x;
+  }
+  norm_store<T>(v, NJ, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
 }
 
-// h += sum_j w[j] * Y[pos[j]] (slots in selection order); xn = rnd(rmsnorm(h) * g)
-template <typename T>
+// h += sum_j w[j] * Y[pos[j]] (slots in selection order); xn = rnd(rmsnorm(h) * g).
+// Every slot's expert output (slot indices clamped to the k selected, so the
+// loads are unconditional) and h are loaded before the first sum: one load
+// round trip after the slot indices, where conditional loads went one by one.
+template <typename T, int NJ>
 __global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int* pos, const float* w, int k, int M,
                                                       int d, const float* g, float eps, float* H, T* xn, Gate gt,
                                                       int n) {
-  const int r = blockIdx.x, nj = d / (4 * blockDim.x);
+  const int r = blockIdx.x;
   if (!gt.active(r / n)) return;
   int ps[8];
   float ws[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (s < k) { ps[s] = pos[(size_t)r * k + s]; ws[s] = w[(size_t)r * k + s]; }
+  for (int s = 0; s < 8; ++s) {
+    const int sc = min(s, k - 1);
+    ps[s] = pos[(size_t)r * k + sc];
+    ws[s] = w[(size_t)r * k + sc];
+  }
+  float4 y[NJ][8], hx[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = (j * blockDim.x + threadIdx.x) * 4;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) y[j][s] = *reinterpret_cast<const float4*>(Y + (size_t)ps[s] * d + c);
+    hx[j] = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
+  }
   float4 v[kRowChunks];
 #pragma unroll
-  for (int j = 0; j < kRowChunks; ++j)
-    if (j < nj) {
-      const int c = (j * blockDim.x + threadIdx.x) * 4;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < NJ; ++j) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        if (s < k) {
-          const float4 y = *reinterpret_cast<const float4*>(Y + (size_t)ps[s] * d + c);
-          acc.x += ws[s] * y.x; acc.y += ws[s] * y.y; acc.z += ws[s] * y.z; acc.w += ws[s] * y.w;
-        }
-      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
-      add4(x, acc);
-      v[j] = x;
-    }
-  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
+    for (int s = 0; s < 8; ++s)
+      if (s < k) {
+        acc.x += ws[s] * y[j][s].x; acc.y += ws[s] * y[j][s].y; acc.z += ws[s] * y[j][s].z; acc.w += ws[s] * y[j][s].w;
+      }
+    float4 x = hx[j];
+    add4(x, acc);
+    v[j] = x;
+  }
+  norm_store<T>(v, NJ, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
 }
+
+// Chunks per thread of a row kernel: d / (4 * row_threads(d)), exactly 1..4
+// for the widths the model accepts (256..1024 in steps of 256, then 2048,
+// 3072, 4096).
+#define DG_ROW_NJ(d, LAUNCH)                    \
+  switch ((d) / (4 * row_threads(d))) {         \
+    case 1: LAUNCH(1); break;                    \
+    case 2: LAUNCH(2); break;                    \
+    case 3: LAUNCH(3); break;                    \
+    default: LAUNCH(4); break;                   \
+  }
 
 template <typename T>
 hipError_t embed_norm(const T* emb, const int32_t* tok, const float* part, int S, int M, int d, int vocab,
@@ -179,15 +218,21 @@ template <typename T>
 hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
                     Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_add_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, gt, n);
+#define DG_L(NJ) \
+  hipLaunchKernelGGL((k_add_norm<T, NJ>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, gt, n)
+  DG_ROW_NJ(d, DG_L)
+#undef DG_L
   return hipGetLastError();
 }
 template <typename T>
 hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
                         float eps, float* H, T* xn, Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_combine_norm<T>), dim3(M), dim3(row_threads(d)), 0, s, Y, pos, w, k, M, d, g, eps, H, xn,
-                     gt, n);
+#define DG_L(NJ)                                                                                              \
+  hipLaunchKernelGGL((k_combine_norm<T, NJ>), dim3(M), dim3(row_threads(d)), 0, s, Y, pos, w, k, M, d, g, eps, H, \
+                     xn, gt, n)
+  DG_ROW_NJ(d, DG_L)
+#undef DG_L
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ typedef int32_t dg_status;
 
 typedef struct dg_config {
   int32_t n_layers;
-  int32_t d_model;      /* multiple of 256, at most 4096 */
+  int32_t d_model;      /* 256, 512, 768, 1024, 2048, 3072 or 4096 */
   int32_t n_q_heads;
   int32_t n_kv_heads;   /* divides n_q_heads */
   int32_t head_dim;     /* 64 or 128 */

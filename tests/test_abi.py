@@ -57,7 +57,8 @@ def _create(lib, **kw):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("head_dim", 96, -4), ("d_model", 100, -4), ("n_kv_heads", 3, -1), ("n_experts", 200, -4),
+    ("head_dim", 96, -4), ("d_model", 100, -4), ("d_model", 1280, -4), ("d_model", 1536, -4),
+    ("n_kv_heads", 3, -1), ("n_experts", 200, -4),
     ("top_k", 9, -4), ("vocab", 1000, -4), ("vocab", 262208, -4), ("canvas_len", 300, -4), ("dtype", 5, -1),
     ("ffn_hidden", 100, -4), ("n_layers", 0, -1),
 ])
