@@ -556,8 +556,10 @@ SeedArg make_seeds(const uint64_t* h, int B) {
 }
 
 // Split plan of a small-M product, reduced if the partial buffer is too small.
-SplitPlan plan(const dg_state* st, int M, int N, int K) {
-  SplitPlan p = plan_splits(M, N, K, 64, 64, (int)st->m->esz, 512);
+// bf16 products with whole 64-element slices take the DMA loop's two K groups
+// per workgroup: half as many workgroups (and split partials) as the register loop.
+SplitPlan plan(const dg_state* st, int M, int N, int K, bool dma_groups = false) {
+  SplitPlan p = plan_splits(M, N, K, 64, 64, (int)st->m->esz, dma_groups && st->m->esz == 2 && K % 64 == 0 ? 256 : 512);
   const int bk = 128 / (int)st->m->esz;
   while (p.splits > 1 && (size_t)p.splits * M * N > st->part_floats) {
     const int s = p.splits - 1;
@@ -604,7 +606,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
   const int keys = st->ctx + pos_off + nq;    // the largest key count over the requests
   const int splits = attn_splits_for(st, nq, keys);
   const int cap = expert_tile_capacity(M, k, E);
-  const SplitPlan p_qkv = plan(st, M, nqkv, d), p_o = plan(st, M, d, Hq * hd);
+  const SplitPlan p_qkv = plan(st, M, nqkv, d, true), p_o = plan(st, M, d, Hq * hd, true);
   const bool stream_ok = m->pack_buf != nullptr && !m->fp8;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];

@@ -44,7 +44,7 @@ struct TileCtx {
 
 template <typename T, int BM_, int BN_, int STAGES_ = 3>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, KG = 1;
   static constexpr int EPC = 16 / (int)sizeof(T);      // elements per 16-byte chunk
   static constexpr int BK = 128 / (int)sizeof(T);      // K elements per slice
   static constexpr int LDK = BK + EPC;                 // padded LDS row stride (elements)
@@ -314,17 +314,22 @@ __device__ __forceinline__ void tile_mma(const TileCtx& t, const AL& al, const B
 
 // ------------------------------------------------------------------ the DMA tile loop (bf16)
 // Same tile and accumulator layout as TileCfg<bf16, BM, BN> (4 waves, 2 x 2),
-// S slices of 64 K-elements in LDS.
-template <int BM_, int BN_, int S_>
+// S slices of 64 K-elements in LDS.  KG > 1: KG groups of 4 waves split the
+// tile's K range (each with its own slice ring) and add their sums in LDS in
+// group order before the epilogue -- more loads in flight per workgroup
+// without split-K partials in global memory.
+template <int BM_, int BN_, int S_, int KG_ = 1>
 struct TileCfgD {
-  static constexpr int BM = BM_, BN = BN_, STAGES = S_;
+  static constexpr int BM = BM_, BN = BN_, STAGES = S_, KG = KG_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int ROWB = 128;                          // bytes of a slice row (64 bf16)
   static constexpr int STAGE = (BM + BN) * ROWB;            // bytes of one slice of the tile
   static constexpr int NI = (BM + BN) / 8 / 4;              // 8-row load groups per wave per slice
   static_assert((BM + BN) % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
-  static constexpr int kSmemBytes = S_ * STAGE + S_ * BM * 4;   // slices, then per-slice row scales (scaled loaders)
+  static constexpr int RING = S_ * STAGE + S_ * BM * 4;   // a group's slices, then per-slice row scales (scaled loaders)
+  static constexpr int RED = (KG_ - 1) * BM * BN * 4;       // groups 1..KG-1's sums for the reduction
+  static constexpr int kSmemBytes = KG_ * RING > RED ? KG_ * RING : RED;
 };
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
@@ -370,14 +375,20 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
                                              f32x4_t (&acc)[C::FM][C::FN]) {
   static_assert(std::is_same<typename AL::Row, const void*>::value && std::is_same<typename BL::Row, const void*>::value,
                 "row-locating loaders only");
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // K group kg (4 waves) takes slices [kg * per, kg * per + nk) of the tile's
+  // K range and its own slice ring; every group runs `per` slice steps so the
+  // workgroup's barriers pair up
+  const int tid = threadIdx.x & 255, kg = threadIdx.x >> 8, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int a = 0; a < C::FM; ++a)
 #pragma unroll
     for (int b = 0; b < C::FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nk = (t.k1 - t.k0) / 64;
-  if (nk <= 0) return;
+  const int nk_all = (t.k1 - t.k0) / 64;
+  if (nk_all <= 0) return;      // uniform over the workgroup
+  const int per = (nk_all + C::KG - 1) / C::KG;
+  const int nk = max(0, min(per, nk_all - kg * per));
+  smem += kg * C::RING;
   // load group j of this wave: tile rows 8 * (w + 4 j) .. + 7 (A rows, then B
   // rows); lane (row rr = lane >> 3, position p = lane & 7) fetches piece
   // p ^ ((r >> 1) & 7) of its row.  Rows past the tile repeat a valid row;
@@ -393,12 +404,12 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     bool valid;
     const void* rp = isA ? al.row(t, r, valid) : bl.row(t, r, valid);
     const int q = (lane & 7) ^ ((r >> 1) & 7);
-    src[j] = static_cast<const char*>(rp) + (size_t)t.k0 * 2 + q * 16;
+    src[j] = static_cast<const char*>(rp) + ((size_t)t.k0 + (size_t)kg * per * 64) * 2 + q * 16;
     dst[j] = (uint32_t)(gi * 8 * C::ROWB);
   }
   const uint32_t lbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   constexpr bool SCALED = chunk_scaled<AL>::value;
-  static_assert(!SCALED || (C::STAGES == 2 && C::BM == 128), "chunk scales: two stages, 128 rows");
+  static_assert(!SCALED || (C::STAGES == 2 && C::BM == 128 && C::KG == 1), "chunk scales: two stages, 128 rows");
   // chunk scales: wave 0 brings the 128 rows' scales of a slice's chunk with the slice
   const char* ssrc[2] = {nullptr, nullptr};
   if constexpr (SCALED) {
@@ -484,13 +495,41 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     }
   } else {
     for (int kt = 0; kt < nk; ++kt) slice(kt, Cont{});
+    if constexpr (C::KG > 1)
+      for (int kt = nk; kt < per; ++kt) lds_barrier();   // a short (or empty) group keeps the barriers paired
   }
   __syncthreads();   // the epilogue may reuse the shared memory
+  if constexpr (C::KG > 1) {
+    // groups 1..KG-1 hand their sums to group 0, which adds them in group order
+    float* red = reinterpret_cast<float*>(smem - kg * C::RING);
+    constexpr int PT = C::FM * C::FN * 4;          // accumulator elements per thread
+    if (kg > 0) {
+#pragma unroll
+      for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((size_t)(kg - 1) * PT + (a * C::FN + b) * 4 + i) * 256 + tid] = acc[a][b][i];
+    }
+    __syncthreads();
+    if (kg == 0) {
+      for (int g = 1; g < C::KG; ++g)
+#pragma unroll
+        for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+          for (int b = 0; b < C::FN; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] += red[((size_t)(g - 1) * PT + (a * C::FN + b) * 4 + i) * 256 + tid];
+    }
+    __syncthreads();
+  }
 }
 
-// Visit every accumulator element with its tile-relative (row, col) and block indices.
+// Visit every accumulator element with its tile-relative (row, col) and block
+// indices (the first 4 waves: with K groups, group 0 holds the sums).
 template <class C, class F>
 __device__ __forceinline__ void for_each_acc(const f32x4_t (&acc)[C::FM][C::FN], F&& f) {
+  if (threadIdx.x >= 256) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
 #pragma unroll
@@ -515,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(SCHED sc, AL al, BL bl, EP ep) 
 
 // LDS: the slice ring, or what the epilogue needs if that is more
 template <class C, class SCHED, class AL, class BL, class EP>
-__global__ __launch_bounds__(256, 2) void k_gemm_dma(SCHED sc, AL al, BL bl, EP ep) {
+__global__ __launch_bounds__(256 * C::KG, C::KG == 1 ? 2 : 1) void k_gemm_dma(SCHED sc, AL al, BL bl, EP ep) {
   constexpr int kBytes = C::kSmemBytes > EP::kSmemBytes ? C::kSmemBytes : EP::kSmemBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kBytes];
   TileCtx t;

@@ -29,6 +29,7 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
   T* act; int F;
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
+    static_assert(C::KG == 1, "one wave group");
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
     for (int a = 0; a < C::FM; ++a)
@@ -57,6 +58,7 @@ struct EpHead {
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
     static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk, "head tiles");
+    static_assert(C::KG == 1, "the head statistics map 256 threads onto the tile");
     float* tile = reinterpret_cast<float*>(smem);
     for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kHeadLd + c] = v; });
     if (logits != nullptr)
@@ -172,7 +174,7 @@ static hipError_t launch(int grid, const SCHED& sc, const AL& al, const BL& bl, 
 template <class C, class SCHED, class AL, class BL, class EP>
 static hipError_t launch_dma(int grid, const SCHED& sc, const AL& al, const BL& bl, const EP& ep, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dma<C, SCHED, AL, BL, EP>), dim3(grid), dim3(256), 0, s, sc, al, bl, ep);
+  hipLaunchKernelGGL((k_gemm_dma<C, SCHED, AL, BL, EP>), dim3(grid), dim3(256 * C::KG), 0, s, sc, al, bl, ep);
   return hipGetLastError();
 }
 
@@ -228,9 +230,11 @@ hipError_t gemm_partials(const T* A, int lda, const T* B, int ldb, float* part, 
       SchedDense<128, 128> sc{M, N, K, cdiv(M, 128), cdiv(N, 128), 1, K, g, n};
       return launch_dma<C>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, EpStoreF32{part, N, 0}, s);
     }
-    // few rows, split along K: 64 x 64 tiles, a split's slices all in flight at once
+    // few rows, split along K: 64 x 64 tiles, two K groups of 4 waves per
+    // workgroup (the split plan targets half as many workgroups as for the
+    // register loop), each group's slices in flight at once
     if (sp.kchunk % 64 == 0 && K % 64 == 0) {
-      using C = TileCfgD<64, 64, kSplitStages - 1>;
+      using C = TileCfgD<64, 64, kSplitStages - 1, 2>;
       SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), cdiv(N, 64), sp.splits, sp.kchunk, g, n};
       return launch_dma<C>(sc.mt * sc.nt * sp.splits, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
                            EpStoreF32{part, N, (size_t)M * N}, s);
@@ -251,9 +255,13 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
                       EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
-// few rows: 32-row tiles, one per CU, four slices in flight (eight measured
-// no faster on the small shape: 8.55 against 8.45 us)
-template <int HD> constexpr int kQkvStages = 4;
+// few rows: 32-row tiles, one per CU, two K groups of 4 waves each with its
+// own slice ring (the 30-layer proxy's QKV, 256 x 4096 x 2048: 18.5 -> 13.8 us
+// against one group of four slices; eight slices of one group measured no
+// faster on the small shape: 8.55 against 8.45 us).  Three slices per group
+// for 128-dim heads, where four would not fit the LDS.
+template <int HD> constexpr int kQkvStages = HD == 128 ? 3 : 4;
+constexpr int kQkvGroups = 2;
 
 template <typename T, int HD>
 static hipError_t qkv_rope_hd(const T* xn, const T* wqkv, int M, int K, const float2* rope, T* q, T* kc, T* vc, int n,
@@ -263,7 +271,8 @@ static hipError_t qkv_rope_hd(const T* xn, const T* wqkv, int M, int K, const fl
   if constexpr (sizeof(T) == 2) {
     if (M <= 512) {
       SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K, g, n};
-      return launch_dma<TileCfgD<32, HD, kQkvStages<HD>>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
+      return launch_dma<TileCfgD<32, HD, kQkvStages<HD>, kQkvGroups>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K},
+                                                                      BLPlain<T>{wqkv, K}, ep, s);
     }
     SchedDense<128, HD> sc{M, N, K, cdiv(M, 128), N / HD, 1, K, g, n};
     return launch_dma<TileCfgD<128, HD, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
