@@ -681,7 +681,8 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
                                           static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s)));
       else
         DG_HIP(gemm_expert_gateup<T>(xn, st->perm, static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up),
-                                     static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s));
+                                     static_cast<T*>(st->act), st->tiles, st->n_tiles, cap, d, F, s,
+                                     static_cast<const T*>(L.pgu)));
     }
     {
       StageTimer tm(st, DG_STAGE_EXPERT_DOWN, s);
@@ -694,7 +695,7 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
                                         st->tiles, st->n_tiles, cap, d, F, s)));
       else
         DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), st->y,
-                                   st->tiles, st->n_tiles, cap, d, F, s));
+                                   st->tiles, st->n_tiles, cap, d, F, s, static_cast<const T*>(L.pd)));
     }
     {
       StageTimer tm(st, DG_STAGE_COMBINE, s);

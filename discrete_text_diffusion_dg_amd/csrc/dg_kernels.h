@@ -118,15 +118,17 @@ hipError_t gemm_qkv_rope(const T* xn, const T* wqkv, int M, int d, int hd, const
 // list with this many rows per tile for them): 128 on the bf16 LDS-DMA tile
 // loop, else 64.
 int expert_group_tile_rows(int d, int F, size_t elem_bytes);
-// act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T
+// act[g][f] = silu(x[perm[g]] . gate_e[f]) * (x[perm[g]] . up_e[f]), rounded to T.
+// pgu (optional): the fragment-packed gate/up weights (pack_expert_weights),
+// read instead of gate / up by the bf16 DMA tile loop.
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
                               const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F,
-                              hipStream_t s);
-// Y[g][c] = act[g] . down_e[c]
+                              hipStream_t s, const T* pgu = nullptr);
+// Y[g][c] = act[g] . down_e[c]; pd (optional): the packed down weights
 template <typename T>
 hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
-                            const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
+                            const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s, const T* pd = nullptr);
 // Weight-streaming expert products for thin routed tiles (k_expert.hip) over
 // fragment-packed weights: PGU[e][F/16][d/32][2][64][8] (gate/up) and
 // PD[e][d/16][F/32][64][8] (down), built by pack_expert_weights.

@@ -222,6 +222,48 @@ struct BLGateUp {
   __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
 };
 
+// B operands already in MFMA fragment order (the fragment-packed expert
+// weights the streaming products read): for 16 B rows and a 32-wide K step,
+// 64 lanes x 16 bytes, lane l holding row (l & 15), K elements (l >> 4) * 8.. .
+// The DMA tile loop copies each such kilobyte as is into LDS and reads it back
+// one 16-byte piece per lane.
+//   BLPackedGateUp: PGU[e][F/16][K/32][gate, up][1 KB]; tile rows [32j, 32j+16)
+//     are the gate rows of features n0 + 16j.., [32j+16, 32j+32) their up rows.
+//   BLPackedRows:   PD[e][N/16][K/32][1 KB]; tile rows n0 + ...
+template <typename T>
+struct BLPackedGateUp {
+  using Row = const void*;
+  static constexpr bool kPacked = true;
+  const T* p; int F, K;
+  // the kilobyte of 16-row block rb (of the tile) at K step ks; blocks past the
+  // matrix repeat its last one (their products are never stored)
+  __device__ const char* frag(const TileCtx& t, int rb, int ks) const {
+    int fb = t.n0 / 16 + (rb >> 1);
+    if (fb >= F / 16) fb = F / 16 - 1;
+    const size_t ksn = (size_t)K / 32;
+    return reinterpret_cast<const char*>(p) +
+           ((((size_t)t.group * (F / 16) + fb) * ksn + ks) * 2 + (rb & 1)) * 1024;
+  }
+  static constexpr int kStepBytes = 2048;     // from one K step to the next
+};
+template <typename T>
+struct BLPackedRows {
+  using Row = const void*;
+  static constexpr bool kPacked = true;
+  const T* p; int N, K;
+  __device__ const char* frag(const TileCtx& t, int rb, int ks) const {
+    int fb = t.n0 / 16 + rb;
+    if (fb >= N / 16) fb = N / 16 - 1;
+    const size_t ksn = (size_t)K / 32;
+    return reinterpret_cast<const char*>(p) + (((size_t)t.group * (N / 16) + fb) * ksn + ks) * 1024;
+  }
+  static constexpr int kStepBytes = 1024;
+};
+template <class BL, class = void>
+struct b_packed : std::false_type {};
+template <class BL>
+struct b_packed<BL, std::void_t<decltype(BL::kPacked)>> : std::integral_constant<bool, BL::kPacked> {};
+
 // ------------------------------------------------------------------ the tile loop
 // acc[a][b][i] holds C[wm*WM + a*16 + (lane>>4)*4 + i][wn*WN + b*16 + (lane&15)].
 template <class C, typename T, class AL, class BL>
@@ -373,7 +415,9 @@ struct chunk_scaled<AL, std::void_t<decltype(AL::kChunkScale)>> : std::integral_
 template <class C, class AL, class BL>
 __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, const BL& bl, char* smem,
                                              f32x4_t (&acc)[C::FM][C::FN]) {
-  static_assert(std::is_same<typename AL::Row, const void*>::value && std::is_same<typename BL::Row, const void*>::value,
+  constexpr bool BPACK = b_packed<BL>::value;
+  static_assert(std::is_same<typename AL::Row, const void*>::value &&
+                    (BPACK || std::is_same<typename BL::Row, const void*>::value),
                 "row-locating loaders only");
   // K group kg (4 waves) takes slices [kg * per, kg * per + nk) of the tile's
   // K range and its own slice ring; every group runs `per` slice steps so the
@@ -393,19 +437,34 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
   // rows); lane (row rr = lane >> 3, position p = lane & 7) fetches piece
   // p ^ ((r >> 1) & 7) of its row.  Rows past the tile repeat a valid row;
   // their products are never stored.
+  // packed B: its kilobytes follow the A rows in LDS, (16-row block, K step of
+  // the slice) in order -- load group gi >= BM / 8 copies kilobyte gi - BM / 8
   const char* src[C::NI];
   uint32_t dst[C::NI];
+  size_t adv[C::NI];          // bytes from one slice to the next
+  const size_t kbase = (size_t)t.k0 + (size_t)kg * per * 64;
 #pragma unroll
   for (int j = 0; j < C::NI; ++j) {
     const int gi = w + 4 * j;
     const int row = gi * 8 + (lane >> 3);
     const bool isA = row < C::BM;
+    dst[j] = (uint32_t)(gi * 8 * C::ROWB);
+    if constexpr (BPACK) {
+      if (!isA) {
+        const int gb = gi - C::BM / 8;
+        src[j] = bl.frag(t, gb >> 1, (int)(kbase / 32) + (gb & 1)) + lane * 16;
+        adv[j] = 2 * (size_t)BL::kStepBytes;
+        continue;
+      }
+    }
     const int r = isA ? row : row - C::BM;
     bool valid;
-    const void* rp = isA ? al.row(t, r, valid) : bl.row(t, r, valid);
+    const void* rp;
+    if constexpr (BPACK) rp = al.row(t, r, valid);
+    else rp = isA ? al.row(t, r, valid) : bl.row(t, r, valid);
     const int q = (lane & 7) ^ ((r >> 1) & 7);
-    src[j] = static_cast<const char*>(rp) + ((size_t)t.k0 + (size_t)kg * per * 64) * 2 + q * 16;
-    dst[j] = (uint32_t)(gi * 8 * C::ROWB);
+    src[j] = static_cast<const char*>(rp) + kbase * 2 + q * 16;
+    adv[j] = 128;
   }
   const uint32_t lbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
   constexpr bool SCALED = chunk_scaled<AL>::value;
@@ -422,7 +481,7 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const uint32_t sb = lbase + (uint32_t)((kt % C::STAGES) * C::STAGE);
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) lds_dma16(src[j] + (size_t)kt * 128, sb + dst[j]);
+    for (int j = 0; j < C::NI; ++j) lds_dma16(src[j] + (size_t)kt * adv[j], sb + dst[j]);
     if constexpr (SCALED) {
       if (w == 0) {
         const uint32_t slot = lbase + (uint32_t)(C::STAGES * C::STAGE + (kt % C::STAGES) * C::BM * 4);
@@ -443,7 +502,13 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
 #pragma unroll
     for (int a = 0; a < C::FM; ++a) fa[a].v = *reinterpret_cast<const uint4*>(sb + aoff + a * 16 * C::ROWB + ch);
 #pragma unroll
-    for (int b = 0; b < C::FN; ++b) fb[b].v = *reinterpret_cast<const uint4*>(sb + boff + b * 16 * C::ROWB + ch);
+    for (int b = 0; b < C::FN; ++b) {
+      if constexpr (BPACK)
+        fb[b].v = *reinterpret_cast<const uint4*>(sb + C::BM * C::ROWB + ((wn * C::WN / 16 + b) * 2 + kk) * 1024 +
+                                                  lane * 16);
+      else
+        fb[b].v = *reinterpret_cast<const uint4*>(sb + boff + b * 16 * C::ROWB + ch);
+    }
 #pragma unroll
     for (int a = 0; a < C::FM; ++a)
 #pragma unroll

@@ -429,11 +429,15 @@ int expert_group_tile_rows(int d, int F, size_t es) { return expert_group_dma(d,
 template <typename T>
 hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const T* up, T* act,
                               const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F,
-                              hipStream_t s) {
+                              hipStream_t s, const T* pgu) {
   if constexpr (sizeof(T) == 2) {
     if (expert_group_dma(d, F, sizeof(T))) {
-      // 128 rows x 64 features (gate and up interleaved: 128 B rows) per tile
+      // 128 rows x 64 features (gate and up interleaved) per tile; the
+      // fragment-packed weights when the model holds them, else the caller's rows
       SchedGroup<128, 128> sc{tiles, n_tiles, cdiv(F, 64), F, d, 64};
+      if (pgu != nullptr)
+        return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALGather<T>{X, d, perm},
+                                                            BLPackedGateUp<T>{pgu, F, d}, EpSwiGLU<T>{act, F}, s);
       return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALGather<T>{X, d, perm},
                                                           BLGateUp<T>{gate, up, (size_t)F * d, d},
                                                           EpSwiGLU<T>{act, F}, s);
@@ -447,10 +451,13 @@ hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const 
 
 template <typename T>
 hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
-                            const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
+                            const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s, const T* pd) {
   if constexpr (sizeof(T) == 2) {
     if (expert_group_dma(d, F, sizeof(T))) {
       SchedGroup<128, 128> sc{tiles, n_tiles, cdiv(d, 128), d, F, 128};
+      if (pd != nullptr)
+        return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALRows<T>{act, F},
+                                                            BLPackedRows<T>{pd, d, F}, EpStoreF32{Y, d, 0}, s);
       return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALRows<T>{act, F},
                                                           BLExpert<T>{down, (size_t)d * F, F}, EpStoreF32{Y, d, 0},
                                                           s);
@@ -493,9 +500,9 @@ hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt
   template hipError_t gemm_qkv_rope<T>(const T*, const T*, int, int, int, const float2*, T*, T*, T*, int, int, \
                                        int, int, PosArg, Gate, hipStream_t);                            \
   template hipError_t gemm_expert_gateup<T>(const T*, const int*, const T*, const T*, T*, const int4*,    \
-                                            const int*, int, int, int, hipStream_t);                    \
+                                            const int*, int, int, int, hipStream_t, const T*);          \
   template hipError_t gemm_expert_down<T>(const T*, const T*, float*, const int4*, const int*, int, int,  \
-                                          int, hipStream_t);                                            \
+                                          int, hipStream_t, const T*);                                  \
   template hipError_t gemm_selfcond<T>(const T*, const float*, int, const T*, float*, int, int, int, int, \
                                        int, Gate, int, hipStream_t);
 DG_INST(float)

@@ -23,8 +23,15 @@
  *     and freed by dg_model_destroy: the fused QKV matrices ((Hq + 2 Hkv) hd d
  *     elements per layer), the transposed embedding for the self-conditioning
  *     contraction (V d elements, self-conditioning models), and the expert
- *     weights in MFMA-fragment order for the weight-streaming expert kernels
- *     (3 E F d elements per layer: as large as the caller's expert tensors).
+ *     weights in MFMA-fragment order (3 E F d elements per layer, or bytes in
+ *     FP8), which every expert product of a bf16 model reads -- the weight
+ *     streaming for few routed rows and the grouped 128 x 128 products for
+ *     many -- whenever ffn_hidden is a multiple of 128 (fp32 models pack for
+ *     the streaming products only and keep reading the caller's tensors in
+ *     the grouped ones).  A bf16 model so packed, and every FP8 model, reads
+ *     the caller's w_gate / w_up / w_down only inside dg_model_create: the
+ *     caller may release them afterwards (the borrowed-weights rule below
+ *     covers every other tensor).
  *   - The four step calls allocate nothing and never synchronise the device,
  *     except dg_encode_prompt / dg_commit_canvas_to_kv which only enqueue work.
  *   - Errors: a negative status is returned and a thread-local message is set
@@ -138,8 +145,9 @@ int32_t dg_weight_count(const dg_config* cfg);
  *   then per layer: attn_norm [d], wq [Hq*hd, d], wk [Hkv*hd, d], wv [Hkv*hd, d],
  *   wo [d, Hq*hd], ffn_norm [d], w_router [E, d], w_gate [E, F, d],
  *   w_up [E, F, d], w_down [E, d, F].
- * The weights are borrowed (must outlive the model); the call synchronises the
- * device once after building the derived copies.  The LM head is tied to emb. */
+ * The weights are borrowed (must outlive the model; for the expert tensors see
+ * the conventions above); the call synchronises the device once after building
+ * the derived copies.  The LM head is tied to emb. */
 dg_status dg_model_create(const dg_config* cfg, const void* const* d_weights, int32_t n_weights,
                           dg_model** out);
 void dg_model_destroy(dg_model* model);
