@@ -156,11 +156,13 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
   constexpr int KT = 64, NS = HD / 32, NDB = HD / 16;
   constexpr int NT = sizeof(T) == 2 ? 2 : 1;
   constexpr int EPC = 16 / (int)sizeof(T);
-  // bf16 K rows are unpadded, their 16-byte pieces XOR-swizzled by kswz(key):
-  // the 16 keys a fragment read takes (tile_key over 16 lanes) then fall on 16
-  // distinct piece slots, where a padded row put rows r and r + 16 on the same
-  // banks.  fp32 rows keep one piece of padding.
-  constexpr bool KSWZ = sizeof(T) == 2;
+  // bf16 128-dim K rows are unpadded, their 16-byte pieces XOR-swizzled by
+  // kswz(key): the 16 keys a fragment read takes (tile_key over 16 lanes) then
+  // fall on 16 distinct piece slots, where a padded row put rows r and r + 16
+  // on the same banks (proxy shape, no key splits: 63.7 -> 61.7 us).  64-dim
+  // rows keep one piece of padding (the swizzle measured 1-2% slower at the
+  // batched shape), as do fp32 rows.
+  constexpr bool KSWZ = sizeof(T) == 2 && HD == 128;
   constexpr int LDK = KSWZ ? HD : HD + EPC, LDV = KT + EPC;
   constexpr int KBUF = KT * LDK, VBUF = HD * LDV;     // elements per stage
   constexpr int NTH = 64 * NWQ;
