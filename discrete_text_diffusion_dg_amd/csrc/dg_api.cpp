@@ -920,6 +920,8 @@ extern "C" dg_status dg_sample_logits_static(const float* d_logits, int32_t rows
   if (vocab < 64 || vocab % 64 || vocab > 262144)
     return fail(DG_ERR_UNSUPPORTED, "vocab must be a multiple of 64 in 64..262144");
   if (canvas_index < 0) return fail(DG_ERR_ARG, "canvas_index must be >= 0");
+  if (params->top_k != 0)
+    return fail(DG_ERR_UNSUPPORTED, "the static sampler takes the full vocabulary (top_k 0), not top_k %d", params->top_k);
   const size_t need = kStaticHeadOffset + (size_t)rows * head_chunks(vocab) * sizeof(HeadPart);
   if (need > kStaticScratchBytes)
     return fail(DG_ERR_CAPACITY, "rows x 128-id chunks need %zu scratch bytes, the fixed scratch holds %zu", need,

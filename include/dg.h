@@ -262,7 +262,8 @@ dg_status dg_sample_logits(dg_state* state, const float* d_logits, int32_t step,
  * DG_ERR_CAPACITY (for example 256 rows at vocab 262144 fit; 512 do not).
  * Every call on one GPU shares that array and overwrites it: calls that
  * overlap on one GPU (two streams, two threads) race and must be ordered by
- * the caller.  Requests at most 128. */
+ * the caller.  Requests at most 128; params->top_k must be 0 (the full
+ * vocabulary; DG_ERR_UNSUPPORTED otherwise). */
 dg_status dg_sample_logits_static(const float* d_logits, int32_t rows, int32_t vocab, int32_t canvas_len,
                                   int32_t canvas_index, int32_t step, const dg_sampler_params* params,
                                   const uint64_t* h_seeds, float* d_H, int32_t* d_y, int32_t* d_argmax,

@@ -101,3 +101,23 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_static_sampler_argument_checks(lib):
+    # the checks run before any device work, so they hold on a host without a GPU
+    from discrete_text_diffusion_dg_amd import _lib as L
+    fake = ctypes.c_void_p(16)                 # never dereferenced: every case fails its checks first
+    seeds = (ctypes.c_uint64 * 1)(1)
+
+    def call(rows=256, vocab=4096, canvas=256, cidx=0, step=0, **kw):
+        sp = L.DgSamplerParams(0.8, 0.4, 0.1, 0.05, kw.get("max_steps", 12), 0, kw.get("top_k", 0))
+        return lib.dg_sample_logits_static(fake, rows, vocab, canvas, cidx, step, ctypes.byref(sp), seeds, fake,
+                                           fake, fake, fake, None)
+    assert call(top_k=8) == -4 and "top_k" in lib.dg_last_error().decode()
+    assert call(step=12) == -1
+    assert call(rows=100) == -1                # not a multiple of the canvas length
+    assert call(vocab=1000) == -4
+    assert call(rows=256 * 129) == -4          # more than 128 requests
+    assert call(rows=512, vocab=262144) == -2  # the records would not fit the fixed scratch
+    assert call(cidx=-1) == -1
+    assert lib.dg_sample_logits_static(None, 256, 4096, 256, 0, 0, None, None, None, None, None, None, None) == -1
