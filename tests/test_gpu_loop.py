@@ -88,6 +88,40 @@ def test_device_loop_matches_explicit_calls(torch_cuda, graph):
     eb.close()
 
 
+@pytest.mark.parametrize("variant", ["topk", "fp8", "fp8-topk"])
+def test_device_loop_variants_match_explicit_calls(torch_cuda, variant):
+    # the captured step with the top-k sampler and / or FP8 experts: one canvas
+    # through the graph, bit-identical to the explicit calls
+    torch = torch_cuda
+    fp8 = variant.startswith("fp8")
+    mc = micro(n_layers=2, vocab=4096, d_model=512, ffn_hidden=256, expert_dtype="fp8" if fp8 else "")
+    W = di.make_weights(mc, 33, gain_std=0.1)
+    B, P, S = 2, 200, 4
+    prompts = torch.from_numpy(di.make_prompts(mc.vocab, B, P, 33))
+    seeds = di.request_seeds(33, B)
+    sp = di.SamplerConfig(max_steps=S, entropy_bound=0.5, stop_mode=0, top_k=8 if "topk" in variant else 0)
+    ea = make_engine(mc, W, B, P + 2 * mc.canvas_len)
+    ea.set_seeds(seeds)
+    ea.encode_prompt(prompts)
+    ea.init_canvas()
+    for t in range(S):
+        ea.denoise_step(t, sp)
+        ea.sample_commit(t, sp)
+    ea.commit_canvas_to_kv()
+    torch.cuda.synchronize()
+    ref = _snapshot(ea)
+    ea.close()
+    eb = make_engine(mc, W, B, P + 2 * mc.canvas_len)
+    eb.set_seeds(seeds)
+    eb.encode_prompt(prompts)
+    n, f = eb.run_canvas_device(sp, graph=True, commit_kv=True)
+    torch.cuda.synchronize()
+    assert (n, f) == (S, True)
+    _assert_same(ref, _snapshot(eb), f"device loop ({variant})")
+    log(f"[device loop {variant}] one canvas of {S} steps and its commit bit-identical to the explicit calls")
+    eb.close()
+
+
 def test_device_loop_early_exit(torch_cuda):
     # a stop threshold above log V stops every request at its first step: the
     # host learns it from the mapped progress record and issues no more steps

@@ -85,3 +85,9 @@ def test_corrupt_forward_loss_fp32_no_prompt(torch_cuda):
 def test_corrupt_forward_loss_small_workload(torch_cuda):
     wl = di.workload("small")
     _case(torch_cuda, wl.model, wl.seed, 1, wl.prompt_len, [0.5], "train-small", gain_std=0.0)
+
+
+def test_corrupt_forward_loss_fp8_experts(torch_cuda):
+    # the pass through the FP8 expert products (grouped: 256 canvas positions per request)
+    mc = micro(n_layers=2, d_model=512, ffn_hidden=256, vocab=2048, expert_dtype="fp8")
+    _case(torch_cuda, mc, 63, 2, 130, [0.3, 0.9], "train-fp8")
