@@ -55,6 +55,7 @@ struct EpHead {
   static constexpr int kSmemBytes = kHeadTileBytes;
   StepInfo si; SeedArg seeds; int n, V, nchunk;
   HeadPart* part; T* ptilde; float* logits;
+  Gate gate;      // a tile may hold rows of a request left out: their logits are not stored
   template <class C>
   __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
     static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk, "head tiles");
@@ -63,7 +64,7 @@ struct EpHead {
     for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kHeadLd + c] = v; });
     if (logits != nullptr)
       for_each_acc<C>(acc, [&](int r, int c, float v) {
-        if (r < t.rows && c < t.cols) logits[(size_t)(t.m0 + r) * V + t.n0 + c] = v;
+        if (r < t.rows && c < t.cols && gate.active((t.m0 + r) / n)) logits[(size_t)(t.m0 + r) * V + t.n0 + c] = v;
       });
     __syncthreads();
     head_tile_stats<T>(tile, t.m0, t.rows, t.n0, t.cols, V, si, seeds, n, part, nchunk, ptilde);
@@ -305,7 +306,7 @@ hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, 
                         hipStream_t s) {
   if (V % 64) return hipErrorInvalidValue;
   SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K, h.gate, h.n};
-  EpHead<T> ep{h.si, h.seeds, h.n, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits};
+  EpHead<T> ep{h.si, h.seeds, h.n, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits, h.gate};
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0)
       return launch_dma<TileCfgD<kHeadChunk, kHeadChunk, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},

@@ -60,7 +60,7 @@ __device__ __forceinline__ void store_row4(float* p, float a, float b, float c, 
 template <typename T>
 __device__ __forceinline__ void norm_store(float4 (&v)[kRowChunks], int nj, int d, const float* g, float eps,
                                            float* hrow, T* xrow, float* xs = nullptr) {
-  __shared__ float red[4];
+  __shared__ float red[8];             // up to 512 threads
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = (blockDim.x + 63) >> 6;
   float ss = 0.f;
 #pragma unroll
@@ -679,11 +679,21 @@ template hipError_t router<bf16>(const bf16*, const bf16*, int, int, int, int, f
 constexpr int kSortThreads = 1024, kSortMaxEntries = 4096, kSortBlocks = kSortMaxEntries / kSortThreads;
 constexpr int kRouterPieces = 16;
 
-bool router_fused_ok(int M, int d, int E, int k) {
+// at most kRouterPieces 8-element pieces of W_r per thread, all loaded at once
+static bool router_pieces_ok(int d, int E) {
   const int nt = row_threads(d);
-  // at most kRouterPieces 8-element pieces of W_r per thread, all loaded at once
-  return M * k <= kSortMaxEntries && E <= 128 && k <= 8 && (E & (E - 1)) == 0 && nt >= 64 && E <= nt && nt / E <= 64 &&
-         d % (8 * (nt / E)) == 0 && d <= kMaxModel && d / (8 * (nt / E)) <= kRouterPieces;
+  return (E & (E - 1)) == 0 && nt >= 64 && E <= nt && nt / E <= 64 && d % (8 * (nt / E)) == 0 &&
+         d / (8 * (nt / E)) <= kRouterPieces;
+}
+// W_r streamed by whole waves in kilobyte pieces
+static bool router_stream_ok(int d) {
+  const int it = d / 512;
+  return d % 512 == 0 && (it == 1 || it == 2 || it == 4 || it == 6 || it == 8);
+}
+
+bool router_fused_ok(int M, int d, int E, int k) {
+  return M * k <= kSortMaxEntries && E <= 128 && k >= 1 && k <= 8 && k <= E && d <= kMaxModel &&
+         (router_pieces_ok(d, E) || router_stream_ok(d));
 }
 
 // One 8-element piece of a router-matrix row, held as loaded (load) and
@@ -711,14 +721,41 @@ struct WrPiece<float> {
   }
 };
 
+// Top k of one row's E logits (lg, in LDS) by one wave -- ties to the lower
+// expert id -- and the softmax over the selected, slots summed in order.
+__device__ __forceinline__ void row_topk_softmax(const float* lg, int E, int k, int r, int* idx, float* w, int* sel_e,
+                                                 float* sel_v) {
+  const int lane = threadIdx.x & 63;
+  if (E > 32) {
+    topk_rounds(lg, E, k, lane, sel_e, sel_v);
+  } else if (lane < E) {
+    // rank of expert lane: the logits that beat it (greater, or equal with a lower id)
+    const float x = lg[lane];
+    int rank = 0;
+    for (int q = 0; q < E; ++q) {
+      const float o = lg[q];
+      rank += (o > x) || (o == x && q < lane);
+    }
+    if (rank < k) { sel_e[rank] = lane; sel_v[rank] = x; }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");   // one wave: LDS writes before reads
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  if (lane < k) {
+    const float mx = sel_v[0];
+    float sum = 0.f;
+    for (int u = 0; u < k; ++u) sum += expf(sel_v[u] - mx);
+    idx[(size_t)r * k + lane] = sel_e[lane];
+    w[(size_t)r * k + lane] = expf(sel_v[lane] - mx) / sum;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int S, int M, int d, const float* g,
                                                          float eps, float* H, T* xn, const T* wr, int E, int k,
                                                          float* rlog, int* idx, float* w, Gate gt, int n) {
   __shared__ float xs[kMaxModel];
   __shared__ float lg[128];
-  __shared__ int sel_e[8];
-  __shared__ float sel_v[8];
   const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
   if (!gt.active(r / n)) {            // a row of a request left out: no expert, no place in the order
     if (tid < k) { idx[(size_t)r * k + tid] = -1; w[(size_t)r * k + tid] = 0.f; }
@@ -766,29 +803,166 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
     rlog[(size_t)r * E + e] = acc;
   }
   __syncthreads();
-  if (tid >= 64) return;
-  if (E > 32) {
-    topk_rounds(lg, E, k, lane, sel_e, sel_v);
-  } else if (lane < E) {
-    // rank of expert lane: the logits that beat it (greater, or equal with a lower id)
-    const float x = lg[lane];
-    int rank = 0;
-    for (int q = 0; q < E; ++q) {
-      const float o = lg[q];
-      rank += (o > x) || (o == x && q < lane);
+  __shared__ int sel_e[8];
+  __shared__ float sel_v[8];
+  if (tid < 64) row_topk_softmax(lg, E, k, r, idx, w, sel_e, sel_v);
+}
+
+// Sums over a wave's 64 lanes of C values at once: each step over lane bit S
+// (high bits first) pairs every lane with its partner across that bit; while
+// more than one value is left, a lane keeps one half of its values (the upper
+// half where the bit is set), adds the partner's copy of that half and sends
+// the other half.  After log2 C halving steps lane l holds value
+// idx = (the top log2 C bits of l), and the remaining steps sum it over the
+// lanes that share idx, in a fixed order.
+template <int S, int C>
+__device__ __forceinline__ void halving_sum(float* v, int& idx) {
+  if constexpr (C > 1) {
+    const bool hi = (threadIdx.x >> S) & 1;
+#pragma unroll
+    for (int u = 0; u < C / 2; ++u) {
+      const float send = hi ? v[u] : v[u + C / 2];
+      const float keep = hi ? v[u + C / 2] : v[u];
+      v[u] = keep + lane_partner<S>(send);
     }
-    if (rank < k) { sel_e[rank] = lane; sel_v[rank] = x; }
+    if (hi) idx += C / 2;
+  } else {
+    v[0] += lane_partner<S>(v[0]);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");   // one wave: LDS writes before reads
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  if (lane < k) {
-    const float mx = sel_v[0];
-    float sum = 0.f;
-    for (int u = 0; u < k; ++u) sum += expf(sel_v[u] - mx);
-    idx[(size_t)r * k + lane] = sel_e[lane];
-    w[(size_t)r * k + lane] = expf(sel_v[lane] - mx) / sum;
+  if constexpr (S > 0) halving_sum<S - 1, (C > 1 ? C / 2 : 1)>(v, idx);
+}
+
+// Dot product of a kilobyte-piece run of a router-matrix row with the row's
+// matching pieces: bf16 pairs on the packed dot instruction (fp32 sums, the
+// pairs in element order), fp32 by fused multiply-adds.
+template <typename T, int IT> struct RouterDot;
+template <int IT>
+struct RouterDot<bf16, IT> {
+  uint32_t x[IT][4];                  // the normalised row, bf16 pairs
+  __device__ __forceinline__ void set(const float* xs, int lane) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* p = xs + (lane + 64 * i) * 8 + 2 * q;   // bf16 values: their upper halves are exact
+        x[i][q] = (__float_as_uint(p[0]) >> 16) | (__float_as_uint(p[1]) & 0xFFFF0000u);
+      }
   }
+  __device__ __forceinline__ float dot(const WrPiece<bf16> (&w)[IT]) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint32_t wq[4] = {w[i].u.x, w[i].u.y, w[i].u.z, w[i].u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[i][q]),
+                                              __builtin_bit_cast(bf16x2_t, wq[q]), acc, false);
+    }
+    return acc;
+  }
+};
+template <int IT>
+struct RouterDot<float, IT> {
+  float x[IT][8];
+  __device__ __forceinline__ void set(const float* xs, int lane) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[i][q] = xs[(lane + 64 * i) * 8 + q];
+  }
+  __device__ __forceinline__ float dot(const WrPiece<float> (&w)[IT]) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float wq[8];
+      w[i].get(wq);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += x[i][q] * wq[q];
+    }
+    return acc;
+  }
+};
+
+// Large router matrices (d a multiple of 512): the row's workgroup streams
+// W_r in batches of EB rows, each row read by a whole wave as IT = d / 512
+// contiguous kilobyte pieces (lane l takes 8-element pieces l, l + 64, ...);
+// a lane's products go through its pieces in order, and the batch's EB sums
+// over the wave are formed together (halving_sum).  Waves take expert batches
+// round-robin, two batches in flight; the first is requested before the row
+// is added and normalised.  Row r visits the experts from expert r mod E on,
+// so that the rows' workgroups, which all read the same matrix at once,
+// spread their requests over the L2 channels.
+template <typename T, int IT>
+__global__ __launch_bounds__(512) void k_add_norm_router_stream(const float* part, int S, int M, int d,
+                                                                const float* g, float eps, float* H, T* xn,
+                                                                const T* wr, int E, int k, float* rlog, int* idx,
+                                                                float* w, Gate gt, int n) {
+  // router rows per batch: 16 bf16 (8 fp32) pieces in flight per lane
+  constexpr int PIF = sizeof(T) == 2 ? 16 : 8, EB = IT >= PIF ? 1 : PIF / IT;
+  static_assert((EB & (EB - 1)) == 0 && EB <= 64, "a power-of-two batch");
+  __shared__ float xs[kMaxModel];
+  __shared__ float lg[128];
+  __shared__ int sel_e[8];
+  __shared__ float sel_v[8];
+  const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: scalar loop control
+  const int step = (blockDim.x >> 6) * EB;
+  if (!gt.active(r / n)) {            // a row of a request left out: no expert, no place in the order
+    if (tid < k) { idx[(size_t)r * k + tid] = -1; w[(size_t)r * k + tid] = 0.f; }
+    return;
+  }
+  const int rot = r % E;
+  WrPiece<T> wa[EB][IT], wb[EB][IT];
+  auto load = [&](WrPiece<T>(&buf)[EB][IT], int e0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      // visit index past E: a repeat of the last one, not stored
+      const int e = min(e0 + j, E - 1) + rot;
+      const T* row = wr + (size_t)(e < E ? e : e - E) * d;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) buf[j][i].load(row + (lane + 64 * i) * 8);
+    }
+  };
+  int e0 = wv * EB;
+  load(wa, e0);
+  float4 v[kRowChunks];
+#pragma unroll
+  for (int j = 0; j < kRowChunks; ++j)
+    if (j < nj) {
+      const int c = (j * blockDim.x + tid) * 4;
+      const float4 p = sum_splits4(part, S, (size_t)M * d, (size_t)r * d + c);
+      float4 x = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
+      add4(x, p);
+      v[j] = x;
+    }
+  norm_store<T>(v, nj, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d, xs);
+  __syncthreads();
+  RouterDot<T, IT> xd;
+  xd.set(xs, lane);
+  auto consume = [&](const WrPiece<T>(&buf)[EB][IT], int b0) __attribute__((always_inline)) {
+    float acc[EB];
+#pragma unroll
+    for (int j = 0; j < EB; ++j) acc[j] = xd.dot(buf[j]);
+    int q = 0;
+    halving_sum<5, EB>(acc, q);
+    const int e = b0 + q + rot < E ? b0 + q + rot : b0 + q + rot - E;
+    if ((lane & (64 / EB - 1)) == 0 && b0 + q < E) {
+      lg[e] = acc[0];
+      rlog[(size_t)r * E + e] = acc[0];
+    }
+  };
+  // the next batch is requested unconditionally (visit indices past E repeat
+  // the last row): a load under a branch would make the wait before the
+  // batch in hand cover the loads just issued
+  for (; e0 < E; e0 += 2 * step) {
+    load(wb, e0 + step);
+    consume(wa, e0);
+    if (e0 + step >= E) break;
+    load(wa, e0 + 2 * step);
+    consume(wb, e0 + step);
+  }
+  __syncthreads();
+  if (tid < 64) row_topk_softmax(lg, E, k, r, idx, w, sel_e, sel_v);
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_route_sort(const int* idx, int MK, int k, int E, int tr, int* perm,
@@ -872,8 +1046,30 @@ hipError_t add_norm_router(const float* part, int S, int M, int d, const float* 
                            hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (!router_fused_ok(M, d, E, k)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_add_norm_router<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, wr, E,
-                     k, rlog, idx, w, gt, n);
+  if (router_pieces_ok(d, E)) {
+    hipLaunchKernelGGL((k_add_norm_router<T>), dim3(M), dim3(row_threads(d)), 0, s, part, S, M, d, g, eps, H, xn, wr, E,
+                       k, rlog, idx, w, gt, n);
+    return hipGetLastError();
+  }
+  // up to eight waves, each thread the same whole number of float4 chunks of the row
+  int nt = d / 4, nj = 1;
+  while (nt > 512 || 4 * nt * nj != d) nt = d / (4 * ++nj);
+  const dim3 block(nt);
+  switch (d / 512) {
+#define DG_ROUTER_IT(IT)                                                                                         \
+  case IT:                                                                                                       \
+    hipLaunchKernelGGL((k_add_norm_router_stream<T, IT>), dim3(M), block, 0, s, part, S, M, d, g, eps, H, xn, wr, E, \
+                       k, rlog, idx, w, gt, n);                                                                  \
+    break;
+    DG_ROUTER_IT(1)
+    DG_ROUTER_IT(2)
+    DG_ROUTER_IT(4)
+    DG_ROUTER_IT(6)
+    DG_ROUTER_IT(8)
+#undef DG_ROUTER_IT
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -144,13 +144,18 @@ def test_device_loop_early_exit(torch_cuda):
     eng.close()
 
 
-def test_requests_stop_independently(torch_cuda):
+@pytest.mark.parametrize("router", ["pieces", "streamed"])
+def test_requests_stop_independently(torch_cuda, router):
     # four requests; request b is driven to stop at step b (crafted entropies into
     # dg_sample_commit), the others continue with the model's own
     torch = torch_cuda
-    mc = micro(n_layers=2, vocab=4096)
+    if router == "pieces":
+        mc = micro(n_layers=2, vocab=4096)
+    else:
+        # the streamed norm + router: 75-row canvases put row pairs across requests
+        mc = micro(n_layers=2, d_model=1024, n_experts=24, top_k=3, ffn_hidden=128, vocab=4096, canvas_len=75)
     W = di.make_weights(mc, 33, gain_std=0.1)
-    B, P, S = 4, 100, 6
+    B, P, S = 4, min(100, mc.canvas_len), 6       # the prompt in one pass
     eng = make_engine(mc, W, B, P + 2 * mc.canvas_len)
     seeds = di.request_seeds(33, B)
     eng.set_seeds(seeds)

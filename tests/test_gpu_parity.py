@@ -408,6 +408,21 @@ def test_micro_many_experts_top8(torch_cuda):
     _run_parity(torch_cuda, mc, 14, 200, 2, 2, "micro-e128", gain_std=0.1)
 
 
+def test_micro_streamed_router_rank_select(torch_cuda):
+    # d 1024 with 24 experts (not a power of two): the fused norm + router streams W_r by whole
+    # waves (two kilobyte pieces per row) for two rows a workgroup, ranks the 24 logits, and its
+    # last wave has no rows; three 75-row canvases: 225 rows, row pairs across requests, a
+    # workgroup of one row at the end
+    mc = micro(n_layers=2, d_model=1024, n_experts=24, top_k=3, ffn_hidden=128, vocab=2048, canvas_len=75)
+    _run_parity(torch_cuda, mc, 18, 100, 3, 2, "micro-stream-e24", gain_std=0.1)
+
+
+def test_micro_streamed_router_two_waves(torch_cuda):
+    # d 512, 128 experts top-8: two waves per row stream W_r sixteen rows a batch, top-8 by rounds
+    mc = micro(n_layers=2, d_model=512, n_experts=128, top_k=8, ffn_hidden=128, vocab=2048)
+    _run_parity(torch_cuda, mc, 19, 100, 1, 2, "micro-stream-e128", gain_std=0.1, determinism=True)
+
+
 def test_micro_grouped_experts_fused_router(torch_cuda):
     # 4 experts top-2: 512 routed entries over 4 experts take the grouped 128-row tile products
     # (ragged last tiles per expert), routed by the fused norm + router and the one-workgroup sort
