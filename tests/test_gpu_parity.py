@@ -423,6 +423,16 @@ def test_micro_streamed_router_two_waves(torch_cuda):
     _run_parity(torch_cuda, mc, 19, 100, 1, 2, "micro-stream-e128", gain_std=0.1, determinism=True)
 
 
+@pytest.mark.parametrize("d,E,k,dtype", [(3072, 64, 4, "bf16"), (4096, 128, 8, "bf16"), (1024, 64, 4, "f32")])
+def test_micro_streamed_router_wide_rows(torch_cuda, d, E, k, dtype):
+    # the streamed norm + router at its other row widths: 3072 (six waves, six pieces
+    # per router row, two rows a batch), 4096 (eight waves, two float4 chunks per thread),
+    # and fp32 weights (FMAs, four rows a batch)
+    mc = micro(n_layers=1, d_model=d, n_experts=E, top_k=k, ffn_hidden=128, vocab=2048, canvas_len=100,
+               dtype=dtype)
+    _run_parity(torch_cuda, mc, 20 + d // 1024, 60, 1, 2, f"micro-stream-d{d}-{dtype}", gain_std=0.1)
+
+
 def test_micro_grouped_experts_fused_router(torch_cuda):
     # 4 experts top-2: 512 routed entries over 4 experts take the grouped 128-row tile products
     # (ragged last tiles per expert), routed by the fused norm + router and the one-workgroup sort
