@@ -756,6 +756,8 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
                                                          float* rlog, int* idx, float* w, Gate gt, int n) {
   __shared__ float xs[kMaxModel];
   __shared__ float lg[128];
+  __shared__ int sel_e[8];
+  __shared__ float sel_v[8];
   const int r = blockIdx.x, nj = d / (4 * blockDim.x), tid = threadIdx.x, lane = tid & 63;
   if (!gt.active(r / n)) {            // a row of a request left out: no expert, no place in the order
     if (tid < k) { idx[(size_t)r * k + tid] = -1; w[(size_t)r * k + tid] = 0.f; }
@@ -803,8 +805,6 @@ __global__ __launch_bounds__(256) void k_add_norm_router(const float* part, int 
     rlog[(size_t)r * E + e] = acc;
   }
   __syncthreads();
-  __shared__ int sel_e[8];
-  __shared__ float sel_v[8];
   if (tid < 64) row_topk_softmax(lg, E, k, r, idx, w, sel_e, sel_v);
 }
 
