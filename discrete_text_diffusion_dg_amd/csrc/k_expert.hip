@@ -69,7 +69,13 @@ template <bool G> struct StreamCfg<float, G> { static constexpr int PD = 2, KC =
 // stage at 128 activation columns
 template <> struct StreamCfg<fp8e4m3, true> { static constexpr int PD = 8, KC = 2; };
 template <> struct StreamCfg<fp8e4m3, false> { static constexpr int PD = 4, KC = 2; };
+// Waves (16-feature blocks) per workgroup: 4 for gate/up; 8 for the bf16 and
+// fp32 down products, whose short K range (F) leaves a 4-wave workgroup too
+// little streaming to cover its fixed cost (proxy: 0.80 -> 0.78 ms per
+// step); FP8 down weights stream half the bytes per step and keep 4 (8 was
+// 0.72 -> 0.73 ms).
 constexpr int kStreamWaves = 4;
+template <typename WT> constexpr int kStreamDownWaves = std::is_same<WT, fp8e4m3>::value ? 4 : 8;
 
 // ---- packing
 // Gate/up of expert e: PGU[e][F/16][d/32][2][64][8] from gate/up [e][F][d].
@@ -395,12 +401,12 @@ bool expert_stream_ok(int d, int F, int elem_bytes) {
   const int ssg = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, true>>() : stream_ss<StreamCfg<float, true>>();
   const int ssd = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, false>>() : stream_ss<StreamCfg<float, false>>();
   // whole super steps along K, whole workgroups of feature blocks along N
-  return d % (32 * ssg) == 0 && F % (32 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamWaves) == 0;
+  return d % (32 * ssg) == 0 && F % (32 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamDownWaves<bf16>) == 0;
 }
 
 bool expert_stream_fp8_ok(int d, int F) {
   const int ssg = stream_ss<StreamCfg<fp8e4m3, true>>(), ssd = stream_ss<StreamCfg<fp8e4m3, false>>();
-  return d % (64 * ssg) == 0 && F % (64 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamWaves) == 0;
+  return d % (64 * ssg) == 0 && F % (64 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamDownWaves<fp8e4m3>) == 0;
 }
 
 template <typename T>
@@ -446,7 +452,7 @@ hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, cons
 template <typename T, typename WT>
 hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, float* Y, const int4* tiles,
                               const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
-  constexpr int NW = kStreamWaves;
+  constexpr int NW = kStreamDownWaves<WT>;
   using C = StreamCfg<WT, false>;
   hipLaunchKernelGGL((k_expert_stream<T, WT, false, NW, C::PD, C::KC>), dim3(d / (16 * NW) * cap_tiles),
                      dim3(64 * NW), 0, s, act, (const int*)nullptr, pd, scale, (void*)Y, tiles, n_tiles, F, d);
