@@ -50,8 +50,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # gate/up expert streaming, small workload: FETCH 43067.6 KiB x2.0 + WRITE 2048.1 KiB x1.0
     ("small", "expert_up"): {"bytes_per_launch": 90290784, "sha1": "bd5783d754f0351abad89e32efe0de52f165e312"},
-    # gate/up expert streaming, 30-layer proxy (one step's 30 launches): FETCH 85099.6 KiB x2.0 + WRITE 3072.1 KiB x1.0
-    ("proxy", "expert_up"): {"bytes_per_launch": 177412387, "sha1": "7a4d1eb6166f91969074a677b2d498460fb2bd4f"},
+    # gate/up expert streaming, 30-layer proxy (one step's 30 launches): FETCH 85430.0 KiB x2.0 + WRITE 3072.1 KiB x1.0
+    ("proxy", "expert_up"): {"bytes_per_launch": 178089143, "sha1": "dd970025203bccaceea42d9f20b2bfa2b24d74cd"},
 }
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
