@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and its
 Python binding) may import, call or link anything in this package; only the
-tests, the graft smoke check and the CPU baseline leg of the benchmark do.
+tests, ``__graft_entry__.smoke()`` and the CPU baseline leg of the benchmark do.
 
 The oracle is a plain, slow numpy implementation of what one denoising step
 computes, written from the pages that describe the method and shares no code

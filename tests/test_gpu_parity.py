@@ -36,14 +36,17 @@ MAX_EXEMPT_TOKEN_FRAC = 0.02   # sampled tokens that differ under the margin exe
 
 
 def progress(msg: str) -> None:
-    """A progress line on stdout and in gpurun_out/test_progress.log (long cases)."""
+    """A progress line on stdout and, when DG_PROGRESS_LOG names a file, appended
+    there too (long cases: pytest holds a test's stdout until it ends)."""
     import os
     import time
     log(msg)
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    path = os.environ.get("DG_PROGRESS_LOG")
+    if not path:
+        return
     try:
-        os.makedirs(d, exist_ok=True)
-        with open(os.path.join(d, "test_progress.log"), "a") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
             f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
     except OSError:
         pass
