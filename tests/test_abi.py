@@ -121,3 +121,14 @@ def test_static_sampler_argument_checks(lib):
     assert call(rows=512, vocab=262144) == -2  # the records would not fit the fixed scratch
     assert call(cidx=-1) == -1
     assert lib.dg_sample_logits_static(None, 256, 4096, 256, 0, 0, None, None, None, None, None, None, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: N > 1 ends at once with the reason, before any device work
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
