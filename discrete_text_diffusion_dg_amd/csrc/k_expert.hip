@@ -401,14 +401,12 @@ bool expert_stream_ok(int d, int F, int elem_bytes) {
   const int ssg = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, true>>() : stream_ss<StreamCfg<float, true>>();
   const int ssd = elem_bytes == 2 ? stream_ss<StreamCfg<bf16, false>>() : stream_ss<StreamCfg<float, false>>();
   // whole super steps along K, whole workgroups of feature blocks along N
-  return d % (32 * ssg) == 0 && F % (32 * ssd) == 0 && F % (16 * kStreamWaves) == 0 &&
-         d % (16 * kStreamDownWaves<bf16>) == 0;   // fp32 down products take as many waves
+  return d % (32 * ssg) == 0 && F % (32 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamDownWaves<bf16>) == 0;
 }
 
 bool expert_stream_fp8_ok(int d, int F) {
   const int ssg = stream_ss<StreamCfg<fp8e4m3, true>>(), ssd = stream_ss<StreamCfg<fp8e4m3, false>>();
-  return d % (64 * ssg) == 0 && F % (64 * ssd) == 0 && F % (16 * kStreamWaves) == 0 &&
-         d % (16 * kStreamDownWaves<fp8e4m3>) == 0;
+  return d % (64 * ssg) == 0 && F % (64 * ssd) == 0 && F % (16 * kStreamWaves) == 0 && d % (16 * kStreamDownWaves<fp8e4m3>) == 0;
 }
 
 template <typename T>
