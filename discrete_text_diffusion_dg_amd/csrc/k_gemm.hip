@@ -131,6 +131,81 @@ struct EpQKV {
   }
 };
 
+// Half-head QKV tiles (128-dim heads, few rows): a 64-column tile of head h
+// holds features [j0, j0 + hd/4) and [hd/2 + j0, hd/2 + j0 + hd/4), j0 = 0 or
+// hd/4, so both halves of every rotate-half pair meet in the tile.  The B
+// loader fetches those weight rows; the epilogue is EpQKV's on half the
+// columns.
+template <int HD>
+__device__ __forceinline__ int pair_feature(int n0, int c) {
+  const int j0 = (n0 % HD) / 2;
+  return c < HD / 4 ? j0 + c : HD / 2 + j0 + (c - HD / 4);
+}
+template <typename T, int HD>
+struct BLHeadPairs {
+  using Row = const void*;
+  const T* p; int ldb;
+  __device__ const void* row(const TileCtx& t, int n, bool& valid) const {
+    valid = n < t.cols;
+    const int head = t.n0 / HD;
+    return p + (size_t)(head * HD + pair_feature<HD>(t.n0, valid ? n : 0)) * ldb;
+  }
+  __device__ uint4 ld(const void* rp, int k) const { return ld16<T>(rp, k); }
+};
+template <typename T, int HD>
+struct EpQKVPairs {
+  static constexpr int BN = HD / 2, Q = HD / 4;
+  static constexpr int kLd = BN + 4;
+  static constexpr int kSmemBytes = 128 * kLd * 4;
+  const float2* rope; T* q; T* kc; T* vc;
+  int n, Hq, Hkv, stride;
+  PosArg pa; Gate gate;
+  template <class C>
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
+    static_assert(C::BN == BN && C::BM <= 128, "half a head per tile");
+    float* tile = reinterpret_cast<float*>(smem);
+    for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kLd + c] = v; });
+    __syncthreads();
+    constexpr int half = HD / 2;
+    const int head = t.n0 / HD, j0 = (t.n0 % HD) / 2;
+    const bool pow2 = (n & (n - 1)) == 0;
+    const int nsh = __ffs(n) - 1;
+    auto split_row = [&](int row, int& b, int& pos) __attribute__((always_inline)) {
+      if (pow2) { b = row >> nsh; pos = pa.base(b) + (row & (n - 1)); }
+      else { b = row / n; pos = pa.base(b) + row % n; }
+    };
+    if (head < Hq + Hkv) {
+      for (int u = threadIdx.x; u < C::BM * Q; u += blockDim.x) {
+        const int r = u / Q, j = u % Q;
+        if (r >= t.rows) continue;
+        const int row = t.m0 + r;
+        int b, pos;
+        split_row(row, b, pos);
+        if (!gate.active(b)) continue;
+        const int f = j0 + j;
+        const float a = tile[r * kLd + j], bb = tile[r * kLd + j + Q];
+        const float2 cs = rope[(size_t)pos * half + f];
+        const float o1 = a * cs.x - bb * cs.y, o2 = bb * cs.x + a * cs.y;
+        T* dst = head < Hq ? q + (size_t)row * Hq * HD + head * HD
+                           : kc + (((size_t)b * Hkv + (head - Hq)) * stride + pos) * HD;
+        Num<T>::store(dst + f, o1);
+        Num<T>::store(dst + f + half, o2);
+      }
+    } else {
+      const int kh = head - Hq - Hkv;
+      for (int u = threadIdx.x; u < C::BM * BN; u += blockDim.x) {
+        const int c = u / C::BM, r = u % C::BM;
+        if (r >= t.rows) continue;
+        const int row = t.m0 + r;
+        int b, pos;
+        split_row(row, b, pos);
+        if (!gate.active(b)) continue;
+        Num<T>::store(vc + (((size_t)b * Hkv + kh) * HD + pair_feature<HD>(t.n0, c)) * stride + pos, tile[r * kLd + c]);
+      }
+    }
+  }
+};
+
 // A rows of exp(z - m_c) (128-id chunks c) times the chunk's probability scale
 // scale[row][c], in fp32, rounded to the operand type: the softmax @ E operand.
 template <typename T>
@@ -256,12 +331,15 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
                       EpStoreF32{part, N, (size_t)M * N}, s);
 }
 
-// few rows: 32-row tiles, one per CU, two K groups of 4 waves each with its
-// own slice ring (the 30-layer proxy's QKV, 256 x 4096 x 2048: 18.5 -> 13.8 us
+// few rows: one workgroup per CU, two K groups of 4 waves each with its own
+// slice ring (the 30-layer proxy's QKV, 256 x 4096 x 2048: 18.5 -> 13.8 us
 // against one group of four slices; eight slices of one group measured no
-// faster on the small shape: 8.55 against 8.45 us).  Three slices per group
-// for 128-dim heads, where four would not fit the LDS.
-template <int HD> constexpr int kQkvStages = HD == 128 ? 3 : 4;
+// faster on the small shape: 8.55 against 8.45 us).  64-dim heads take
+// 32-row tiles of a whole head; 128-dim heads take 64 x 64 half-head tiles
+// with four slices per group: at 256 rows each workgroup reads (64 + 64)
+// instead of (32 + 128) operand rows per slice, and the QKV stage of the
+// proxy step went 19.7 -> 17.7 us per layer (two or three slices, or 32 x 64
+// tiles at two workgroups per CU, were slower).
 constexpr int kQkvGroups = 2;
 
 template <typename T, int HD>
@@ -271,9 +349,16 @@ static hipError_t qkv_rope_hd(const T* xn, const T* wqkv, int M, int K, const fl
   const EpQKV<T, HD> ep{rope, q, kc, vc, n, Hq, Hkv, stride, pa, g};
   if constexpr (sizeof(T) == 2) {
     if (M <= 512) {
-      SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K, g, n};
-      return launch_dma<TileCfgD<32, HD, kQkvStages<HD>, kQkvGroups>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K},
-                                                                      BLPlain<T>{wqkv, K}, ep, s);
+      if constexpr (HD == 128) {
+        const EpQKVPairs<T, HD> eph{rope, q, kc, vc, n, Hq, Hkv, stride, pa, g};
+        SchedDense<64, 64> sc{M, N, K, cdiv(M, 64), N / 64, 1, K, g, n};
+        return launch_dma<TileCfgD<64, 64, 4, kQkvGroups>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K},
+                                                           BLHeadPairs<T, HD>{wqkv, K}, eph, s);
+      } else {
+        SchedDense<32, HD> sc{M, N, K, cdiv(M, 32), N / HD, 1, K, g, n};
+        return launch_dma<TileCfgD<32, HD, 4, kQkvGroups>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K},
+                                                           BLPlain<T>{wqkv, K}, ep, s);
+      }
     }
     SchedDense<128, HD> sc{M, N, K, cdiv(M, 128), N / HD, 1, K, g, n};
     return launch_dma<TileCfgD<128, HD, 2>>(sc.mt * sc.nt, sc, ALPlain<T>{xn, K}, BLPlain<T>{wqkv, K}, ep, s);
