@@ -148,13 +148,17 @@ def test_device_loop_early_exit(torch_cuda):
     eng.close()
 
 
-@pytest.mark.parametrize("router", ["pieces", "streamed"])
+@pytest.mark.parametrize("router", ["pieces", "streamed", "hd128"])
 def test_requests_stop_independently(torch_cuda, router):
     # four requests; request b is driven to stop at step b (crafted entropies into
     # dg_sample_commit), the others continue with the model's own
     torch = torch_cuda
     if router == "pieces":
         mc = micro(n_layers=2, vocab=4096)
+    elif router == "hd128":
+        # 128-dim heads on the half-head QKV tiles: 75-row canvases put tile
+        # rows across requests, and a finished request's rows are left out
+        mc = micro(n_layers=2, d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128, vocab=4096, canvas_len=75)
     else:
         # the streamed norm + router: 75-row canvases put row pairs across requests
         mc = micro(n_layers=2, d_model=1024, n_experts=24, top_k=3, ffn_hidden=128, vocab=4096, canvas_len=75)
