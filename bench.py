@@ -78,7 +78,9 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
         by = n_experts_active * (d * F * wes + (d * 4 if fp8 else 0)) + R * k * F * es + R * k * d * 4
         fl = 2 * R * k * F * d
     elif stage == "lm_head":     # with the head statistics in its epilogue: writes P~ and the chunk records
-        by = V * d * es + R * d * es + (R * V * es if mc.self_cond else 0) + R * ((V + 127) // 128) * 32
+        # head rows: bf16 E, or (FP8 head) one E4M3 code per weight plus one fp32 scale per id
+        hb = V * d + V * 4 if getattr(mc, "head_dtype", "") == "fp8" else V * d * es
+        by = hb + R * d * es + (R * V * es if mc.self_cond else 0) + R * ((V + 127) // 128) * 32
         fl = 2 * R * d * V
     elif stage == "attn":
         by = 2 * B * Hkv * keys * hd * es + 2 * R * Hq * hd * es
@@ -441,16 +443,17 @@ def main():
     def same_model(name):
         """Workloads on the same seeded weights share the device copy."""
         x = di.workload(name)
-        base = dataclasses.replace(x.model, expert_dtype="")
+        base = dataclasses.replace(x.model, expert_dtype="", head_dtype="")
         for k in list(dw):
             w0 = di.workload(k)
-            if dataclasses.replace(w0.model, expert_dtype="") == base and w0.seed == x.seed:
+            if dataclasses.replace(w0.model, expert_dtype="", head_dtype="") == base and w0.seed == x.seed:
                 return dw[k]
         return None
 
-    # the headline model with its experts in FP8 and with top-k sampling, then the
-    # other workloads (the batched shape also with top-k sampling)
-    names = [n_ for n_ in (wl.name + "-fp8", wl.name + "-topk") if n_ in di.WORKLOADS]
+    # the headline model with its experts in FP8, with experts and LM head in FP8,
+    # and with top-k sampling, then the other workloads (the batched shape also
+    # with top-k sampling)
+    names = [n_ for n_ in (wl.name + "-fp8", wl.name + "-fp8-head", wl.name + "-topk") if n_ in di.WORKLOADS]
     names += [n_ for n_ in EXTRA_WORKLOADS if n_ != wl.name]
     if a.no_extras:
         names = []
@@ -469,7 +472,8 @@ def main():
             extras[name] = {k: x[k] for k in keys if k in x}
             extras[name]["steps"] = a.steps if detail else 24
             if xw.model.expert_dtype == "fp8":
-                extras[name]["dtype"] = "bf16 activations, fp8 e4m3 expert weights"
+                extras[name]["dtype"] = ("bf16 activations, fp8 e4m3 expert and LM-head weights"
+                                         if xw.model.head_dtype == "fp8" else "bf16 activations, fp8 e4m3 expert weights")
             if xw.sampler.top_k:
                 extras[name]["sampler"] = f"top-{xw.sampler.top_k} truncated"
         except Exception as ex:   # reported, never fatal for the headline

@@ -52,6 +52,7 @@ class ModelConfig:
     rms_eps: float = 1e-6
     canvas_len: int = 256
     expert_dtype: str = ""   # "" = dtype; "fp8": experts served as OCP FP8 E4M3 with per-channel scales
+    head_dtype: str = ""     # "" = dtype; "fp8": the LM head reads E as OCP FP8 E4M3 with one scale per id
 
     def n_params(self) -> int:
         d, L = self.d_model, self.n_layers
@@ -116,6 +117,11 @@ WORKLOADS: Dict[str, Workload] = {
                           SamplerConfig(48, 0.1, STOP_MEAN, 0.05), prompt_len=2048, batch=1, canvases=1, seed=2),
     "small-fp8": Workload("small-fp8", dataclasses.replace(_SMALL, expert_dtype="fp8"), SamplerConfig(24, 0.1),
                           prompt_len=512, batch=1, canvases=1, seed=1),
+    # The same with the LM head's rows of E in FP8 as well (the model served in FP8).
+    "proxy-fp8-head": Workload("proxy-fp8-head", dataclasses.replace(_PROXY, expert_dtype="fp8", head_dtype="fp8"),
+                               SamplerConfig(48, 0.1, STOP_MEAN, 0.05), prompt_len=2048, batch=1, canvases=1, seed=2),
+    "small-fp8-head": Workload("small-fp8-head", dataclasses.replace(_SMALL, expert_dtype="fp8", head_dtype="fp8"),
+                               SamplerConfig(24, 0.1), prompt_len=512, batch=1, canvases=1, seed=1),
     # Top-k truncated sampling (k = 8) on the proxy and on the batched shape.
     "proxy-topk": Workload("proxy-topk", _PROXY, SamplerConfig(48, 0.1, STOP_MEAN, 0.05, top_k=8),
                            prompt_len=2048, batch=1, canvases=1, seed=2),

@@ -24,7 +24,7 @@ DG_DTYPE_F32 = 0
 DG_DTYPE_BF16 = 1
 DG_DTYPE_FP8_E4M3 = 2
 (DG_MODEL_VIEW_EXPERT_GATEUP, DG_MODEL_VIEW_EXPERT_DOWN, DG_MODEL_VIEW_EXPERT_SCALES_GATEUP,
- DG_MODEL_VIEW_EXPERT_SCALES_DOWN) = range(4)
+ DG_MODEL_VIEW_EXPERT_SCALES_DOWN, DG_MODEL_VIEW_HEAD_CODES, DG_MODEL_VIEW_HEAD_SCALES) = range(6)
 (DG_VIEW_K_CACHE, DG_VIEW_V_CACHE, DG_VIEW_SELF_COND, DG_VIEW_PREV_ARGMAX, DG_VIEW_ROUTE,
  DG_VIEW_HIDDEN, DG_VIEW_ROUTER_LOGITS, DG_VIEW_ATTN_OUT, DG_VIEW_CTX_LENS, DG_VIEW_CANVAS_INDEX) = range(10)
 DG_RUN_GRAPH, DG_RUN_EARLY_EXIT, DG_RUN_COMMIT_KV = 1, 2, 4
@@ -44,7 +44,8 @@ class DgConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "ffn_hidden",
         "top_k", "vocab", "canvas_len", "dtype", "self_cond")] + [
-        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("expert_dtype", ctypes.c_int32)]
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("expert_dtype", ctypes.c_int32),
+        ("head_dtype", ctypes.c_int32)]
 
 
 class DgSamplerParams(ctypes.Structure):

@@ -64,6 +64,8 @@ struct dg_model {
   bool fp8;              // expert weights in FP8 E4M3 (packed codes and scales only)
   size_t esz;            // bytes per weight element
   const void* emb;
+  fp8e4m3* head8 = nullptr;     // owned (FP8 LM head): E4M3 codes of the embedding rows, P8 order
+  float* head_scale = nullptr;  // owned (FP8 LM head): one scale per vocabulary id
   const void* w_sc;
   const float* final_norm;
   std::vector<LayerW> layers;
@@ -162,6 +164,10 @@ static dg_status check_config(const dg_config* c) {
     return fail(DG_ERR_ARG, "expert_dtype must be 0 or DG_DTYPE_FP8_E4M3");
   if (c->expert_dtype == DG_DTYPE_FP8_E4M3 && (c->dtype != DG_DTYPE_BF16 || !expert_stream_fp8_ok(c->d_model, c->ffn_hidden)))
     return fail(DG_ERR_UNSUPPORTED, "FP8 experts need a bf16 model with d_model %% 512 == 0 and ffn_hidden %% 256 == 0");
+  if (c->head_dtype != 0 && c->head_dtype != DG_DTYPE_FP8_E4M3)
+    return fail(DG_ERR_ARG, "head_dtype must be 0 or DG_DTYPE_FP8_E4M3");
+  if (c->head_dtype == DG_DTYPE_FP8_E4M3 && c->dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_UNSUPPORTED, "an FP8 LM head needs a bf16 model");
   return DG_OK;
 }
 
@@ -261,6 +267,23 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
       return fail(DG_ERR_HIP, "packing expert weights: %s", hipGetErrorString(e));
     }
   }
+  if (cfg->head_dtype == DG_DTYPE_FP8_E4M3) {
+    // the LM head's copy of the embedding in E4M3 with one scale per vocabulary id
+    const size_t codes = ((size_t)cfg->vocab * d + 255) / 256 * 256;
+    void* buf = nullptr;
+    e = hipMalloc(&buf, codes + (size_t)cfg->vocab * 4);
+    if (e == hipSuccess) {
+      m->head8 = static_cast<fp8e4m3*>(buf);
+      m->head_scale = reinterpret_cast<float*>(static_cast<char*>(buf) + codes);
+      e = pack_head_fp8(static_cast<const bf16*>(m->emb), m->head8, m->head_scale, cfg->vocab, d, 0);
+    }
+    if (e != hipSuccess) {
+      if (buf) hipFree(buf);
+      if (m->pack_buf) hipFree(m->pack_buf);
+      hipFree(m->qkv_buf); delete m;
+      return fail(DG_ERR_HIP, "quantising the LM head: %s", hipGetErrorString(e));
+    }
+  }
   if (cfg->self_cond) {
     e = hipMalloc(&m->emb_t, (size_t)cfg->vocab * d * m->esz);
     if (e == hipSuccess) {
@@ -270,6 +293,7 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
     }
     if (e != hipSuccess) {
       if (m->emb_t) hipFree(m->emb_t);
+      if (m->head8) hipFree(m->head8);
       if (m->pack_buf) hipFree(m->pack_buf);
       hipFree(m->qkv_buf); delete m;
       return fail(DG_ERR_HIP, "building transposed embedding: %s", hipGetErrorString(e));
@@ -278,6 +302,7 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
   e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     if (m->emb_t) hipFree(m->emb_t);
+    if (m->head8) hipFree(m->head8);
     if (m->pack_buf) hipFree(m->pack_buf);
     hipFree(m->qkv_buf); delete m;
     return fail(DG_ERR_HIP, "model create: %s", hipGetErrorString(e));
@@ -289,6 +314,12 @@ extern "C" dg_status dg_model_create(const dg_config* cfg, const void* const* w,
 extern "C" dg_status dg_model_view(const dg_model* m, int32_t which, int32_t layer, void** ptr, size_t* bytes) {
   if (!m || !ptr || !bytes) return fail(DG_ERR_ARG, "null argument");
   const dg_config& c = m->cfg;
+  if (which == DG_MODEL_VIEW_HEAD_CODES || which == DG_MODEL_VIEW_HEAD_SCALES) {
+    if (!m->head8) return fail(DG_ERR_ARG, "the model holds no such copy");
+    *ptr = which == DG_MODEL_VIEW_HEAD_CODES ? static_cast<void*>(m->head8) : static_cast<void*>(m->head_scale);
+    *bytes = which == DG_MODEL_VIEW_HEAD_CODES ? (size_t)c.vocab * c.d_model : (size_t)c.vocab * 4;
+    return DG_OK;
+  }
   if (layer < 0 || layer >= c.n_layers) return fail(DG_ERR_ARG, "layer %d outside 0..%d", layer, c.n_layers - 1);
   const LayerW& L = m->layers[layer];
   const size_t E = c.n_experts, F = c.ffn_hidden, d = c.d_model, es = m->fp8 ? 1 : m->esz;
@@ -306,6 +337,7 @@ extern "C" dg_status dg_model_view(const dg_model* m, int32_t which, int32_t lay
 extern "C" void dg_model_destroy(dg_model* m) {
   if (!m) return;
   if (m->emb_t) hipFree(m->emb_t);
+  if (m->head8) hipFree(m->head8);
   if (m->pack_buf) hipFree(m->pack_buf);
   if (m->qkv_buf) hipFree(m->qkv_buf);
   delete m;
@@ -798,6 +830,17 @@ dg_status run_head(dg_state* st, const float* logits, const StepInfo& si, int to
 // One denoising round.  sc_mode: 0 no self-conditioning term, 1 the term
 // (s of the previous step), as the explicit calls decide from the step; the
 // loop always adds it, with s cleared at the start of each canvas.
+// The LM head with the statistics epilogue over the model's head weights: the
+// embedding, or its E4M3 copy with per-id scales (FP8 head).
+template <typename T>
+hipError_t lm_head(const dg_model* m, const T* xn, int R, const HeadArgs<T>& h, hipStream_t s) {
+  const int d = m->cfg.d_model, V = m->cfg.vocab;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (m->head8 != nullptr) return gemm_lm_head_fp8(xn, d, m->head8, m->head_scale, R, V, d, h, s);
+  }
+  return gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s);
+}
+
 template <typename T>
 dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, bool sc, int top_k,
                       const uint64_t* seeds, Gate gate, float* H, int32_t* y, int32_t* am, float* margin,
@@ -818,7 +861,7 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, b
     if (logits_out != nullptr) {
       // the raw logits, only when a caller asks for them (the plain head writes them)
       const HeadArgs<T> h{si, make_seeds(seeds, st->B), st->n, st->hp, nullptr, logits_out, gate};
-      DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
+      DG_HIP(lm_head<T>(m, xn, R, h, s));
     }
     return run_topk_merge<T>(st, top_k, si, seeds, gate, H, y, am, margin, s);
   }
@@ -827,7 +870,7 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, b
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
     const HeadArgs<T> h{si, make_seeds(seeds, st->B), st->n, st->hp,
                         c.self_cond ? static_cast<T*>(st->ptilde) : nullptr, logits_out, gate};
-    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
+    DG_HIP(lm_head<T>(m, xn, R, h, s));
   }
   return run_merge<T>(st, gate, H, y, am, margin, s);
 }
@@ -884,6 +927,8 @@ extern "C" dg_status dg_denoise_step(dg_state* st, const int32_t* d_canvas, int3
   const Gate g{d_active, 0};
   if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
     return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
+  if (params->top_k > 0 && st->m->head8 != nullptr)
+    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step reads the bf16 LM head, not an FP8 one");
   return st->m->cfg.dtype == DG_DTYPE_BF16
              ? run_denoise<bf16>(st, d_canvas, si, sc, params->top_k, h_seeds, g, d_H, d_y, d_argmax, d_margin,
                                  d_logits, s)
@@ -998,6 +1043,8 @@ extern "C" dg_status dg_corrupt_forward_loss(dg_state* st, const int32_t* d_clea
     if (!(h_rates[b] >= 0.f && h_rates[b] <= 1.f)) return fail(DG_ERR_ARG, "rate of request %d outside [0, 1]", b);
     ra.v[b] = h_rates[b];
   }
+  if (st->m->head8 != nullptr)
+    return fail(DG_ERR_UNSUPPORTED, "the training-side pass takes the bf16 LM head, not an FP8 one");
   dg_status r = check_capacity(st);
   if (r) return r;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1066,6 +1113,8 @@ extern "C" dg_status dg_run_canvas(dg_state* st, int32_t* d_canvas, const dg_sam
   if (params->max_steps > kMaxLoopSteps) return fail(DG_ERR_UNSUPPORTED, "max_steps above %d", kMaxLoopSteps);
   if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
     return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
+  if (params->top_k > 0 && st->m->head8 != nullptr)
+    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step reads the bf16 LM head, not an FP8 one");
   if (first_step < 0 || first_step >= params->max_steps)
     return fail(DG_ERR_ARG, "first_step %d outside 0..max_steps-1", first_step);
   if (n_steps < 1 || n_steps > params->max_steps - first_step)

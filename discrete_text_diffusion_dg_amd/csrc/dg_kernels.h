@@ -106,6 +106,15 @@ hipError_t gemm_partials_f32a(const float* A, int lda, const T* B, int ldb, floa
 template <typename T>
 hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, int K, const HeadArgs<T>& h,
                         hipStream_t s);
+// The same over FP8 (E4M3) rows: B8 holds the codes of B [V, K] in the P8
+// fragment order (pack_head_fp8), bscale[v] the scale of row v; logits[r][v] =
+// bscale[v] * (A[r] . codes of row v).  V and K multiples of 64.
+hipError_t gemm_lm_head_fp8(const bf16* A, int lda, const fp8e4m3* B8, const float* bscale, int M, int V, int K,
+                            const HeadArgs<bf16>& h, hipStream_t s);
+// Quantise the rows of a bf16 [V, K] matrix to E4M3 with one fp32 scale per
+// row (scale = fl32(fl64(max |row|) / 448), 1 for a zero row; code =
+// E4M3(fl32(w / scale)), nearest even, saturating) into the P8 order above.
+hipError_t pack_head_fp8(const bf16* w, fp8e4m3* codes, float* scales, int V, int K, hipStream_t s);
 // The fused QKV projection of rows r = b * n + i with RoPE at position
 // pos.base(b) + i applied to q and k in its epilogue: q -> q [M][Hq * hd],
 // k -> K cache rows, v -> V^T cache columns (the layouts rope_scatter writes).

@@ -259,10 +259,34 @@ struct BLPackedRows {
   }
   static constexpr int kStepBytes = 1024;
 };
+// FP8 (OCP E4M3) B rows in the order the FP8 expert products stream:
+// P8[N/16][K/64][64 lanes][16 B], lane (c, g) of block (n/16, k/64) holding
+// row n0 + c, K elements g*8 .. +8 then 32 + g*8 .. +8 -- one kilobyte per 16
+// rows and 64-wide K step, copied as is into LDS by the DMA tile loop, whose
+// fragment reads widen a lane's 8 codes of a 32-wide K step to bf16.  The
+// per-row scales are left to the epilogue.
+struct BLPackedFp8Rows {
+  using Row = const void*;
+  static constexpr bool kPacked = true;
+  static constexpr bool kFp8 = true;
+  const fp8e4m3* p; int N, K;
+  // the kilobyte of 16-row block rb (of the tile) at 64-wide K step ks; blocks
+  // past the matrix repeat its last one (their products are never stored)
+  __device__ const char* frag(const TileCtx& t, int rb, int ks) const {
+    int fb = t.n0 / 16 + rb;
+    if (fb >= N / 16) fb = N / 16 - 1;
+    return reinterpret_cast<const char*>(p) + ((size_t)fb * (size_t)(K / 64) + ks) * 1024;
+  }
+  static constexpr int kStepBytes = 1024;
+};
 template <class BL, class = void>
 struct b_packed : std::false_type {};
 template <class BL>
 struct b_packed<BL, std::void_t<decltype(BL::kPacked)>> : std::integral_constant<bool, BL::kPacked> {};
+template <class BL, class = void>
+struct b_fp8 : std::false_type {};
+template <class BL>
+struct b_fp8<BL, std::void_t<decltype(BL::kFp8)>> : std::integral_constant<bool, BL::kFp8> {};
 
 // ------------------------------------------------------------------ the tile loop
 // acc[a][b][i] holds C[wm*WM + a*16 + (lane>>4)*4 + i][wn*WN + b*16 + (lane&15)].
@@ -360,15 +384,17 @@ __device__ __forceinline__ void tile_mma(const TileCtx& t, const AL& al, const B
 // tile's K range (each with its own slice ring) and add their sums in LDS in
 // group order before the epilogue -- more loads in flight per workgroup
 // without split-K partials in global memory.
-template <int BM_, int BN_, int S_, int KG_ = 1>
+template <int BM_, int BN_, int S_, int KG_ = 1, bool B8_ = false>
 struct TileCfgD {
   static constexpr int BM = BM_, BN = BN_, STAGES = S_, KG = KG_;
+  static constexpr bool B8 = B8_;                           // B rows in FP8 (BLPackedFp8Rows)
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int ROWB = 128;                          // bytes of a slice row (64 bf16)
-  static constexpr int STAGE = (BM + BN) * ROWB;            // bytes of one slice of the tile
-  static constexpr int NI = (BM + BN) / 8 / 4;              // 8-row load groups per wave per slice
-  static_assert((BM + BN) % 32 == 0 && FM >= 1 && FN >= 1, "tile shape");
+  static constexpr int BROWB = B8_ ? 64 : ROWB;             // bytes of a B slice row
+  static constexpr int STAGE = BM * ROWB + BN * BROWB;      // bytes of one slice of the tile
+  static constexpr int NI = STAGE / 1024 / 4;               // 1 KB load groups per wave per slice
+  static_assert(STAGE % 4096 == 0 && FM >= 1 && FN >= 1, "tile shape");
   static constexpr int RING = S_ * STAGE + S_ * BM * 4;   // a group's slices, then per-slice row scales (scaled loaders)
   static constexpr int RED = (KG_ - 1) * BM * BN * 4;       // groups 1..KG-1's sums for the reduction
   static constexpr int kSmemBytes = KG_ * RING > RED ? KG_ * RING : RED;
@@ -416,6 +442,8 @@ template <class C, class AL, class BL>
 __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, const BL& bl, char* smem,
                                              f32x4_t (&acc)[C::FM][C::FN]) {
   constexpr bool BPACK = b_packed<BL>::value;
+  constexpr bool B8 = b_fp8<BL>::value;
+  static_assert(B8 == C::B8, "FP8 B rows need a tile configuration laid out for them");
   static_assert(std::is_same<typename AL::Row, const void*>::value &&
                     (BPACK || std::is_same<typename BL::Row, const void*>::value),
                 "row-locating loaders only");
@@ -439,6 +467,7 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
   // their products are never stored.
   // packed B: its kilobytes follow the A rows in LDS, (16-row block, K step of
   // the slice) in order -- load group gi >= BM / 8 copies kilobyte gi - BM / 8
+  // (FP8 rows: one kilobyte per 16-row block covers the slice's 64 K elements)
   const char* src[C::NI];
   uint32_t dst[C::NI];
   size_t adv[C::NI];          // bytes from one slice to the next
@@ -452,8 +481,13 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     if constexpr (BPACK) {
       if (!isA) {
         const int gb = gi - C::BM / 8;
-        src[j] = bl.frag(t, gb >> 1, (int)(kbase / 32) + (gb & 1)) + lane * 16;
-        adv[j] = 2 * (size_t)BL::kStepBytes;
+        if constexpr (B8) {
+          src[j] = bl.frag(t, gb, (int)(kbase / 64)) + lane * 16;
+          adv[j] = (size_t)BL::kStepBytes;
+        } else {
+          src[j] = bl.frag(t, gb >> 1, (int)(kbase / 32) + (gb & 1)) + lane * 16;
+          adv[j] = 2 * (size_t)BL::kStepBytes;
+        }
         continue;
       }
     }
@@ -503,7 +537,10 @@ __device__ __forceinline__ void tile_mma_dma(const TileCtx& t, const AL& al, con
     for (int a = 0; a < C::FM; ++a) fa[a].v = *reinterpret_cast<const uint4*>(sb + aoff + a * 16 * C::ROWB + ch);
 #pragma unroll
     for (int b = 0; b < C::FN; ++b) {
-      if constexpr (BPACK)
+      if constexpr (B8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(sb + C::BM * C::ROWB + (wn * C::WN / 16 + b) * 1024 + lane * 16);
+        fb[b].v = kk == 0 ? fp8x8_to_bf16x8(u.x, u.y) : fp8x8_to_bf16x8(u.z, u.w);
+      } else if constexpr (BPACK)
         fb[b].v = *reinterpret_cast<const uint4*>(sb + C::BM * C::ROWB + ((wn * C::WN / 16 + b) * 2 + kk) * 1024 +
                                                   lane * 16);
       else

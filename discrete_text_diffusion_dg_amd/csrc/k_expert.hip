@@ -439,6 +439,18 @@ hipError_t pack_expert_weights_fp8(const bf16* gate, const bf16* up, const bf16*
   return hipGetLastError();
 }
 
+hipError_t pack_head_fp8(const bf16* w, fp8e4m3* codes, float* scales, int V, int K, hipStream_t s) {
+  if (V % 16 || K % 64) return hipErrorInvalidValue;
+  // the down projection's P8 order with one "expert": rows V, K elements per row K
+  hipLaunchKernelGGL(k_row_scales, dim3((unsigned)((V + 3) / 4)), dim3(256), 0, s, w, K, (size_t)V, V, 0, 0, scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t pieces = (size_t)V * K / 16;
+  hipLaunchKernelGGL(k_pack_down_fp8, dim3((unsigned)((pieces + 255) / 256), 1), dim3(256), 0, s, w, scales,
+                     reinterpret_cast<uint4*>(codes), V, K);
+  return hipGetLastError();
+}
+
 template <typename T, typename WT>
 hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, const float* scale, T* act,
                                 const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {

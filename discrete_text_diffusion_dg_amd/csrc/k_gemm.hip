@@ -50,16 +50,35 @@ struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the s
 // LM-head tile -> head statistics of its 128 rows x 128 vocabulary ids (and,
 // when asked for, the fp32 logits).  The accumulators go through the tile's
 // shared memory, free once the K loop has ended.
-template <typename T>
+// kScaled (FP8 head rows): logit = bscale[v] * (the product with the E4M3
+// codes of row v), the scale applied in fp32 before anything reads the tile.
+template <typename T, bool kScaled = false>
 struct EpHead {
   static constexpr int kSmemBytes = kHeadTileBytes;
   StepInfo si; SeedArg seeds; int n, V, nchunk;
   HeadPart* part; T* ptilde; float* logits;
   Gate gate;      // a tile may hold rows of a request left out: their logits are not stored
+  const float* bscale;   // kScaled: one fp32 scale per vocabulary id
   template <class C>
-  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char* smem) const {
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc_in)[C::FM][C::FN], char* smem) const {
     static_assert(C::BM == kHeadChunk && C::BN == kHeadChunk, "head tiles");
     static_assert(C::KG == 1, "the head statistics map 256 threads onto the tile");
+    f32x4_t acc[C::FM][C::FN];
+    {
+      const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+      for (int b = 0; b < C::FN; ++b) {
+        float sc = 1.f;
+        if constexpr (kScaled) {
+          const int c = wn * C::WN + b * 16 + (lane & 15);
+          sc = bscale[t.n0 + (c < t.cols ? c : 0)];
+        }
+#pragma unroll
+        for (int a = 0; a < C::FM; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[a][b][i] = kScaled ? acc_in[a][b][i] * sc : acc_in[a][b][i];
+      }
+    }
     float* tile = reinterpret_cast<float*>(smem);
     for_each_acc<C>(acc, [&](int r, int c, float v) { tile[r * kHeadLd + c] = v; });
     if (logits != nullptr)
@@ -399,6 +418,18 @@ hipError_t gemm_lm_head(const T* A, int lda, const T* B, int ldb, int M, int V, 
   }
   using C = TileCfg<T, kHeadChunk, kHeadChunk>;
   return launch<C, T>(sc.mt * sc.nt, sc, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, ep, s);
+}
+
+// The LM head over FP8 (E4M3) rows of the embedding in the P8 fragment order,
+// one fp32 scale per vocabulary id: the same 128 x 128 tiles and statistics
+// epilogue, B slices at half the bytes.
+hipError_t gemm_lm_head_fp8(const bf16* A, int lda, const fp8e4m3* B8, const float* bscale, int M, int V, int K,
+                            const HeadArgs<bf16>& h, hipStream_t s) {
+  if (V % 64 || K % 64) return hipErrorInvalidValue;
+  SchedDense<kHeadChunk, kHeadChunk> sc{M, V, K, cdiv(M, kHeadChunk), cdiv(V, kHeadChunk), 1, K, h.gate, h.n};
+  EpHead<bf16, true> ep{h.si, h.seeds, h.n, V, cdiv(V, kHeadChunk), h.part, h.ptilde, h.logits, h.gate, bscale};
+  return launch_dma<TileCfgD<kHeadChunk, kHeadChunk, 2, 1, true>>(sc.mt * sc.nt, sc, ALPlain<bf16>{A, lda},
+                                                                  BLPackedFp8Rows{B8, V, K}, ep, s);
 }
 
 // ------------------------------------------------------------------ top-k LM head

@@ -40,7 +40,8 @@ def config_struct(mc) -> L.DgConfig:
                       mc.ffn_hidden, mc.top_k, mc.vocab, mc.canvas_len,
                       L.DG_DTYPE_BF16 if mc.dtype == "bf16" else L.DG_DTYPE_F32,
                       1 if mc.self_cond else 0, mc.rope_theta, mc.rms_eps,
-                      L.DG_DTYPE_FP8_E4M3 if getattr(mc, "expert_dtype", "") == "fp8" else 0)
+                      L.DG_DTYPE_FP8_E4M3 if getattr(mc, "expert_dtype", "") == "fp8" else 0,
+                      L.DG_DTYPE_FP8_E4M3 if getattr(mc, "head_dtype", "") == "fp8" else 0)
 
 
 def sampler_struct(sp) -> L.DgSamplerParams:

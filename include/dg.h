@@ -28,10 +28,11 @@
  *     streaming for few routed rows and the grouped 128 x 128 products for
  *     many -- whenever ffn_hidden is a multiple of 128 (fp32 models pack for
  *     the streaming products only and keep reading the caller's tensors in
- *     the grouped ones).  A bf16 model so packed, and every FP8 model, reads
- *     the caller's w_gate / w_up / w_down only inside dg_model_create: the
- *     caller may release them afterwards (the borrowed-weights rule below
- *     covers every other tensor).
+ *     the grouped ones), and (FP8 LM head) the E4M3 codes and scales of the
+ *     embedding's rows (V d bytes + 4 V).  A bf16 model so packed, and every
+ *     FP8 model, reads the caller's w_gate / w_up / w_down only inside
+ *     dg_model_create: the caller may release them afterwards (the
+ *     borrowed-weights rule below covers every other tensor).
  *   - The four step calls allocate nothing and never synchronise the device,
  *     except dg_encode_prompt / dg_commit_canvas_to_kv which only enqueue work.
  *   - Errors: a negative status is returned and a thread-local message is set
@@ -59,7 +60,7 @@ typedef int32_t dg_status;
 
 #define DG_DTYPE_F32 0
 #define DG_DTYPE_BF16 1
-#define DG_DTYPE_FP8_E4M3 2   /* expert weights only: OCP FP8 E4M3 with one fp32 scale per output channel */
+#define DG_DTYPE_FP8_E4M3 2   /* expert and LM-head weights only: OCP FP8 E4M3 with one fp32 scale per output channel */
 
 #define DG_STOP_NONE 0    /* run the whole step budget */
 #define DG_STOP_MEAN 1    /* stop once the mean canvas entropy < stop_tau */
@@ -90,6 +91,16 @@ typedef struct dg_config {
    * only the packed codes and scales (3 E F d bytes + (2 F + d) E 4 bytes per
    * layer); every batch runs the weight-streaming expert products. */
   int32_t expert_dtype;
+  /* Storage of the LM head's weights (the tied embedding E [V, d]): 0 = dtype;
+   * DG_DTYPE_FP8_E4M3 (bf16 models): dg_model_create quantises each row of E
+   * (one vocabulary id, one output channel of the head) to E4M3 by the rule
+   * above, and the LM head computes logit[r][v] = scale[v] * (x_r . codes of
+   * row v), fp32 sums of bf16 products, before the temperature and the head
+   * statistics.  The embedding lookup and the self-conditioning contraction
+   * keep reading the bf16 E.  The model holds V d bytes of codes and V fp32
+   * scales in addition.  Not taken by top-k truncated sampling (top_k > 0) or
+   * by dg_corrupt_forward_loss (DG_ERR_UNSUPPORTED). */
+  int32_t head_dtype;
 } dg_config;
 
 typedef struct dg_sampler_params {
@@ -132,6 +143,12 @@ const char* dg_last_error(void);
 #define DG_MODEL_VIEW_EXPERT_DOWN 1
 #define DG_MODEL_VIEW_EXPERT_SCALES_GATEUP 2
 #define DG_MODEL_VIEW_EXPERT_SCALES_DOWN 3
+/*   DG_MODEL_VIEW_HEAD_CODES:  FP8 LM head only (layer ignored): E4M3 codes
+ *     of E in the order P8H[V/16][d/64][64][16], lane (c, g) of block
+ *     (v/16, k/64) holding E[v][k0 + g*8 .. +8] then E[v][k0 + 32 + g*8 .. +8]
+ *   DG_MODEL_VIEW_HEAD_SCALES: FP8 LM head only, float [V] */
+#define DG_MODEL_VIEW_HEAD_CODES 4
+#define DG_MODEL_VIEW_HEAD_SCALES 5
 dg_status dg_model_view(const dg_model* model, int32_t which, int32_t layer, void** d_ptr, size_t* bytes);
 
 /* Number of weight pointers dg_model_create expects for a config:

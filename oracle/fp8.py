@@ -1,4 +1,4 @@
-"""OCP 8-bit floating point E4M3 for the expert weights (oracle side).
+"""OCP 8-bit floating point E4M3 for the expert and LM-head weights (oracle side).
 
 The pages give the deployed model's weights in FP8 (chooseai.io speed
 paragraph: the vLLM FP8 figures; bohuyeshan.top 一: the quantised model runs
@@ -11,7 +11,8 @@ Conversion rounds to nearest, ties to even, and saturates to +-448 (the
 specification's saturating mode).
 
 Scaling (a reading; the pages name none): one fp32 scale per output channel
-of each expert matrix (a row of the [out, in] layout),
+of each expert matrix (a row of the [out, in] layout) and of the LM head (a
+row of E, one vocabulary id),
     scale = fl32(fl64(max |w_row|) / 448)     (1.0 for an all-zero row),
     q     = E4M3(fl32(w / scale))             (an fp32 division, then the conversion),
 and the weight the model uses is q * scale (exact in fp64).

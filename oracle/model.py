@@ -19,6 +19,10 @@ Readings where the pages are silent (no layer formula is printed):
     expert id, weights softmax over the k selected logits, no capacity limit;
   * self-conditioning: s = softmax(z) E (the previous step's tempered
     distribution times the embedding), added as s W_sc^T; s = 0 at step 0;
+  * FP8 serving (chooseai.io speed paragraph, bohuyeshan.top 一: the model is
+    served in FP8): experts, and optionally the LM head's rows of E, use the
+    E4M3 codes of each output channel times its scale (oracle/fp8.py); the
+    embedding lookup and the self-conditioning product keep the stored E;
   * canvas queries sit at positions N..N+255 after an N-token context and see
     every cached key and every canvas key; the canvas's own K/V are not kept;
     committing a canvas re-encodes it causally and appends its K/V.
@@ -107,6 +111,20 @@ class OracleModel:
         if self._cache_f64:
             return self.W(name)[e]
         return nm.upcast(self._stored(name)[e])
+
+    def head_weight(self) -> np.ndarray:
+        """Rows of the LM head: E, or (FP8 head) each row's E4M3 codes times its scale."""
+        if getattr(self.cfg, "head_dtype", "") != "fp8":
+            return self.W("emb")
+        if "emb.fp8" not in self._f64:
+            E = self.W("emb")
+            out = np.empty_like(E)
+            # row by row is the definition; blocks of rows only bound the temporaries
+            for r0 in range(0, E.shape[0], 8192):
+                q, s = fp8.quantize_rows(E[r0:r0 + 8192].astype(np.float32))
+                out[r0:r0 + 8192] = fp8.dequantize_rows(q, s)
+            self._f64["emb.fp8"] = out
+        return self._f64["emb.fp8"]
 
     # ------------------------------------------------------------ blocks
     def _moe(self, l: int, xm: np.ndarray, trace: Optional[dict], b: int = 0) -> np.ndarray:
@@ -236,7 +254,7 @@ class OracleModel:
                 extra = self.rnd(self.s[b]) @ self.W("w_sc").T
             h = self._stack(b, canvas[b], pos, False, False, extra, trace)
             xf = self.rnd(nm.rmsnorm(h, self.W("final_norm"), cfg.rms_eps))
-            logits = (xf @ self.W("emb").T).astype(np.float32)
+            logits = (xf @ self.head_weight().T).astype(np.float32)
             top_k = getattr(sp, "top_k", 0)
             if top_k:
                 # the distribution truncated to each position's top_k logits ([mlqm] 九)

@@ -65,7 +65,7 @@ def forward_loss(model, clean: np.ndarray, rates, seeds, want_logits: bool = Fal
         out["corrupted"][b], out["replaced"][b] = x, rep
         h = model._stack(b, x, pos, False, False, None, None)
         xf = model.rnd(nm.rmsnorm(h, model.W("final_norm"), cfg.rms_eps))
-        logits = xf @ model.W("emb").T
+        logits = xf @ model.head_weight().T
         ce = logsumexp(logits) - logits[np.arange(n), np.asarray(clean[b])]
         out["ce"][b] = ce
         out["loss"][b] = ce.mean()

@@ -61,6 +61,8 @@ def _create(lib, **kw):
     ("n_kv_heads", 3, -1), ("n_experts", 200, -4),
     ("top_k", 9, -4), ("vocab", 1000, -4), ("vocab", 262208, -4), ("canvas_len", 300, -4), ("dtype", 5, -1),
     ("ffn_hidden", 100, -4), ("n_layers", 0, -1),
+    ("expert_dtype", 5, -1), ("head_dtype", 5, -1),
+    ("head_dtype", 2, -4),          # an FP8 LM head needs a bf16 model (this one is fp32)
 ])
 def test_model_create_rejects_bad_config(lib, field, value, code):
     st, msg, out = _create(lib, **{field: value})

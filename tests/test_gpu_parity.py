@@ -669,6 +669,41 @@ def test_fp8_proxy_shapes_two_layers(torch_cuda):
     _run_parity(torch_cuda, mc, 2, 256, 1, 1, "fp8-proxy-2L", sp_max_steps=48)
 
 
+# ------------------------------------------------------------------ FP8 LM head
+def test_fp8_head_quantisation_bit_exact(torch_cuda):
+    # the LM head's E4M3 codes and per-id scales equal the oracle's quantisation of the bf16 E
+    from discrete_text_diffusion_dg_amd import _lib as L
+    from oracle import fp8
+    mc = micro(n_layers=1, d_model=512, vocab=4160, head_dtype="fp8")
+    W = di.make_weights(mc, 53)
+    eng = make_engine(mc, W, 1, 512)
+    V, d = mc.vocab, mc.d_model
+    codes = _unpack_fp8(eng.model_view(L.DG_MODEL_VIEW_HEAD_CODES, 0), 1, V, d, 1)[0, 0]
+    sc = eng.model_view(L.DG_MODEL_VIEW_HEAD_SCALES, 0).view(np.float32)
+    q, s = fp8.quantize_rows(nm.upcast(W.get("emb")).astype(np.float32))
+    assert np.array_equal(sc.view(np.uint32), s.view(np.uint32)), "head scales"
+    assert np.array_equal(codes, q), f"head codes ({int((codes != q).sum())} differ)"
+    log(f"[fp8 head] codes and scales of {V} rows bit-identical to the oracle's quantisation")
+    eng.close()
+
+
+def test_fp8_head_micro_parity(torch_cuda):
+    # 4160 ids: 32.5 head tiles, the last one 64 wide (the per-id scales of a ragged tile)
+    mc = micro(n_layers=2, d_model=512, ffn_hidden=256, n_experts=8, top_k=2, vocab=4160, head_dtype="fp8")
+    _run_parity(torch_cuda, mc, 54, 300, 2, 2, "fp8-head-micro", gain_std=0.1, determinism=True)
+
+
+def test_fp8_head_small_workload(torch_cuda):
+    wl = di.workload("small-fp8-head")
+    _run_parity(torch_cuda, wl.model, wl.seed, wl.prompt_len, 1, 2, "fp8-head-small")
+
+
+def test_fp8_head_proxy_shapes_one_layer(torch_cuda):
+    # the proxy's head (262144 ids, d 2048) and experts in FP8, 1 of its 30 layers
+    mc = replace(di.workload("proxy-fp8-head").model, n_layers=1)
+    _run_parity(torch_cuda, mc, 2, 256, 1, 1, "fp8-head-proxy-1L", sp_max_steps=48)
+
+
 # ------------------------------------------------------------------ top-k truncated sampler
 @pytest.mark.parametrize("kind", ["random", "peaked", "ties", "uniform"])
 def test_topk_sampler_on_identical_logits(torch_cuda, kind):

@@ -655,6 +655,58 @@ def test_e4m3_row_quantisation():
     assert (np.abs(deq - w)[big] <= np.abs(w)[big] / 16 + 1e-12).all()
 
 
+class _Replaced:
+    """A weight set with some tensors replaced (the rest from the base set)."""
+
+    def __init__(self, base, **tensors):
+        self.base, self.tensors = base, tensors
+
+    def get(self, name):
+        return self.tensors[name] if name in self.tensors else self.base.get(name)
+
+
+def test_fp8_head_rounds_only_off_grid_entries():
+    """The FP8 LM head reads each row of E as its E4M3 codes times the row's scale.
+
+    Rows of E here are exact E4M3 values times 2^-8 with a 448 * 2^-8 entry, so
+    each row's scale is exactly 2^-8 and the codes hold those rows exactly,
+    except two hand-placed entries off the E4M3 grid in column 5: 1.0625 in row
+    3 (a tie between 1.0 and 1.125: to the even mantissa, 1.0) and 1.1875 in
+    row 7 (a tie between 1.125 and 1.25: to 1.25), both times 2^-8.  The FP8
+    head's logits then equal the stored-E head's on every other row, and on rows
+    3 and 7 differ by x[5] * (-1/16) * 2^-8 and x[5] * (+1/16) * 2^-8: equal
+    and opposite.  The embedding lookup keeps the stored E."""
+    import dataclasses
+    from oracle import fp8
+    cfg = _micro_cfg(sc=True)
+    cfg8 = dataclasses.replace(cfg, head_dtype="fp8")
+    V, d = cfg.vocab, cfg.d_model
+    rng = np.random.default_rng(22)
+    codes = rng.integers(0, 0x7F, size=(V, d)).astype(np.uint8) | (rng.integers(0, 2, size=(V, d)) << 7).astype(np.uint8)
+    codes[:, 0] = np.where(rng.integers(0, 2, size=V) == 1, 0xFE, 0x7E)      # -448 or +448
+    E = (fp8.decode(codes) * 2.0 ** -8).astype(np.float32)
+    E[3, 5] = 1.0625 * 2.0 ** -8
+    E[7, 5] = 1.1875 * 2.0 ** -8
+    W = _Replaced(di.make_weights(cfg, 5, gain_std=0.3), emb=E)
+    sp = di.SamplerConfig(4, 0.1)
+    seeds = di.request_seeds(5, 1)
+    canvas = rng.integers(0, V, size=(1, cfg.canvas_len)).astype(np.int32)
+    prompt = rng.integers(0, V, size=(1, 3))
+    res = []
+    for c in (cfg, cfg8):
+        m = OracleModel(c, W, 1, 16)
+        m.encode_prompt(prompt)
+        res.append(m.denoise_step(canvas, 0, sp, seeds, want_logits=True, trace_requests=[0]))
+    a, b = res[0]["logits"][0].astype(np.float64), res[1]["logits"][0].astype(np.float64)
+    others = [v for v in range(V) if v not in (3, 7)]
+    assert np.array_equal(a[:, others], b[:, others])
+    d3, d7 = b[:, 3] - a[:, 3], b[:, 7] - a[:, 7]
+    assert np.abs(d3).min() > 0
+    scale = np.abs(a).max()
+    assert np.allclose(d3, -d7, rtol=0, atol=4 * 2.0 ** -24 * scale)
+    assert np.array_equal(res[0]["traces"][0]["h0"], res[1]["traces"][0]["h0"])
+
+
 # ------------------------------------------------------------------ training-side corruption and loss
 def test_corruption_rates_and_uniform_replacement():
     from oracle import training as tr
