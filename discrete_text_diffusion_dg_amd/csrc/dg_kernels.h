@@ -172,7 +172,7 @@ struct AttnArgs {
   const void* kc;       // K cache of this layer: [B][Hkv][kv_stride][hd]
   const void* vc;       // V cache of this layer, transposed: [B][Hkv][hd][kv_stride]
   void* out;            // [B*nq, Hq*hd] operand type
-  float* part_o;        // split partials [splits][B*nq*Hq][hd] (fp32, unnormalised)
+  void* part_o;         // split partials [splits][B*nq*Hq][hd] (operand type, unnormalised)
   float* part_ml;       // split partials [splits][B*nq*Hq][2] (running max, sum)
   int B, nq, Hq, Hkv, hd, kv_stride;   // kv_stride: context capacity rounded up to 64
   PosArg pos;           // request b: keys 0..pos.base(b)+nq-1 (the new rows sit at pos.base(b)..+nq-1)

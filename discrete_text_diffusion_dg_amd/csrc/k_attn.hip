@@ -88,6 +88,16 @@ __device__ __forceinline__ void store4(T* dst, const float* v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* src) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(src);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xFFFF0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(src);
+  }
+}
 
 // ---- wide: 16 * NWQ query rows per workgroup sharing LDS-staged K / V^T tiles
 // bf16 V^T pieces are staged as fp16 so that the probabilities enter
@@ -527,11 +537,14 @@ __global__ __launch_bounds__(64 * NWQ) void k_attn_wide(AttnArgs a) {
         store4(out + db * 16 + g4 * 4, v);
       }
     } else {
-      float* po = a.part_o + ((size_t)split * a.B * a.nq * a.Hq + rowid) * HD;
+      // unnormalised partial output in the operand type (rounded once more
+      // before the merge, which rounds its result to the operand type too)
+      T* po = reinterpret_cast<T*>(a.part_o) + ((size_t)split * a.B * a.nq * a.Hq + rowid) * HD;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<float4*>(po + db * 16 + g4 * 4) =
-            make_float4(o[qb][db][0], o[qb][db][1], o[qb][db][2], o[qb][db][3]);
+      for (int db = 0; db < NDB; ++db) {
+        const float v[4] = {o[qb][db][0], o[qb][db][1], o[qb][db][2], o[qb][db][3]};
+        store4(po + db * 16 + g4 * 4, v);
+      }
       if (g4 == 0) {
         float* pm = a.part_ml + ((size_t)split * a.B * a.nq * a.Hq + rowid) * 2;
         pm[0] = sizeof(T) == 2 ? m_run[qb] * 0.6931471805599453f : m_run[qb];   // the merge takes natural units
@@ -746,7 +759,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
     if (a.splits == 1) {
       Num<T>::store(reinterpret_cast<T*>(a.out) + rowid * HD + d, O / L);
     } else {
-      a.part_o[((size_t)split * nrows + rowid) * HD + d] = O;
+      Num<T>::store(reinterpret_cast<T*>(a.part_o) + ((size_t)split * nrows + rowid) * HD + d, O);
       if (d == 0) {
         a.part_ml[((size_t)split * nrows + rowid) * 2] = M;
         a.part_ml[((size_t)split * nrows + rowid) * 2 + 1] = L;
@@ -773,7 +786,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   for (int s = 0; s < kMaxAttnSplits; ++s) {
     if (s < a.splits) {
       ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * nrows + rowid) * 2);
-      po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * nrows + rowid) * HD + d0);
+      po[s] = load4(reinterpret_cast<const T*>(a.part_o) + (s * nrows + rowid) * HD + d0);
     }
   }
   float m = -INFINITY;
