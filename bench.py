@@ -50,8 +50,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # gate/up expert streaming, small workload: FETCH 43067.6 KiB x2.0 + WRITE 2048.1 KiB x1.0
     ("small", "expert_up"): {"bytes_per_launch": 90290784, "sha1": "bd5783d754f0351abad89e32efe0de52f165e312"},
-    # gate/up expert streaming, 30-layer proxy (one step's 30 launches): FETCH 85430.0 KiB x2.0 + WRITE 3072.1 KiB x1.0
-    ("proxy", "expert_up"): {"bytes_per_launch": 178089143, "sha1": "dd970025203bccaceea42d9f20b2bfa2b24d74cd"},
+    # gate/up expert streaming, 30-layer proxy (one step's 30 launches): FETCH 84028.6 KiB x2.0 + WRITE 3072.1 KiB x1.0
+    ("proxy", "expert_up"): {"bytes_per_launch": 175236422, "sha1": "6238650c9184f54eb8bb54b9e7f012bf021065fe"},
 }
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
@@ -75,7 +75,7 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
         by = n_experts_active * (2 * F * d * wes + (2 * F * 4 if fp8 else 0)) + R * d * es + R * k * F * es
         fl = 2 * R * k * d * F * 2
     elif stage == "expert_down":
-        by = n_experts_active * (d * F * wes + (d * 4 if fp8 else 0)) + R * k * F * es + R * k * d * 4
+        by = n_experts_active * (d * F * wes + (d * 4 if fp8 else 0)) + R * k * F * es + R * k * d * es
         fl = 2 * R * k * F * d
     elif stage == "lm_head":     # with the head statistics in its epilogue: writes P~ and the chunk records
         # head rows: bf16 E, or (FP8 head) one E4M3 code per weight plus one fp32 scale per id
@@ -107,8 +107,8 @@ def stage_work(stage: str, mc, B: int, ctx: int, n_experts_active: int):
     elif stage == "norm":
         by = R * d * 4 + R * d * es
         fl = 0
-    elif stage == "combine":
-        by = R * k * d * 4 + 2 * R * d * 4
+    elif stage == "combine":     # expert outputs in the operand type, residual h in fp32
+        by = R * k * d * es + 2 * R * d * 4
         fl = 2 * R * k * d
     elif stage == "commit":
         by = R * 16

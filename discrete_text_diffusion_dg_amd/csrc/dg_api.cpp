@@ -112,7 +112,7 @@ struct dg_state {
   // workspace
   float* h; void* xn; float* part; size_t part_floats; void* q; void* attn; float* attn_po; float* attn_pml;
   float* rlog; int* ridx; float* rw; int* perm; int* pos; int4* tiles; int* rcnt;
-  int* n_tiles; void* act; float* y; HeadPart* hp; float* chunk_scale;
+  int* n_tiles; void* act; void* y; HeadPart* hp; float* chunk_scale;
   void* ptilde; float* sc_part; int sc_splits, sc_kchunk; int32_t* tok;
   size_t total_bytes;
   // stage timing (dg_profile_enable): event pairs from a fixed pool
@@ -471,7 +471,7 @@ extern "C" dg_status dg_state_init(const dg_model* m, void* buf, size_t bytes, i
   s->perm = reinterpret_cast<int*>(b + o.perm); s->pos = reinterpret_cast<int*>(b + o.pos);
   s->tiles = reinterpret_cast<int4*>(b + o.tiles); s->n_tiles = reinterpret_cast<int*>(b + o.n_tiles);
   s->rcnt = reinterpret_cast<int*>(b + o.rcnt);
-  s->act = b + o.act; s->y = reinterpret_cast<float*>(b + o.y);
+  s->act = b + o.act; s->y = b + o.y;
   s->hp = reinterpret_cast<HeadPart*>(b + o.hp); s->chunk_scale = reinterpret_cast<float*>(b + o.chunk_scale);
   s->ptilde = m->cfg.self_cond ? b + o.ptilde : nullptr;
   s->sc_part = m->cfg.self_cond ? reinterpret_cast<float*>(b + o.sc_part) : nullptr;
@@ -721,18 +721,20 @@ dg_status run_stack(dg_state* st, const int32_t* tok, int nq, bool causal, bool 
       if (m->fp8) {
         if constexpr (std::is_same<T, bf16>::value)
           DG_HIP((expert_stream_down<T, fp8e4m3>(static_cast<const T*>(st->act), static_cast<const fp8e4m3*>(L.pd),
-                                                L.sd, st->y, st->tiles, st->n_tiles, cap, d, F, s)));
+                                                L.sd, static_cast<T*>(st->y), st->tiles, st->n_tiles, cap, d, F,
+                                                s)));
       } else if (stream)
-        DG_HIP((expert_stream_down<T, T>(static_cast<const T*>(st->act), static_cast<const T*>(L.pd), nullptr, st->y,
-                                        st->tiles, st->n_tiles, cap, d, F, s)));
+        DG_HIP((expert_stream_down<T, T>(static_cast<const T*>(st->act), static_cast<const T*>(L.pd), nullptr,
+                                        static_cast<T*>(st->y), st->tiles, st->n_tiles, cap, d, F, s)));
       else
-        DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), st->y,
+        DG_HIP(gemm_expert_down<T>(static_cast<const T*>(st->act), static_cast<const T*>(L.w_down), static_cast<T*>(st->y),
                                    st->tiles, st->n_tiles, cap, d, F, s, static_cast<const T*>(L.pd)));
     }
     {
       StageTimer tm(st, DG_STAGE_COMBINE, s);
       const float* g_next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
-      DG_HIP(combine_norm<T>(st->y, st->pos, st->rw, k, M, d, g_next, c.rms_eps, st->h, xn, gate, nq, s));
+      DG_HIP(combine_norm<T>(static_cast<const T*>(st->y), st->pos, st->rw, k, M, d, g_next, c.rms_eps, st->h, xn,
+                             gate, nq, s));
     }
   }
   return DG_OK;

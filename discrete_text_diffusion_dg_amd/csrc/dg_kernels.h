@@ -136,7 +136,7 @@ hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const 
                               hipStream_t s, const T* pgu = nullptr);
 // Y[g][c] = act[g] . down_e[c]; pd (optional): the packed down weights
 template <typename T>
-hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
+hipError_t gemm_expert_down(const T* act, const T* down, T* Y, const int4* tiles,
                             const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s, const T* pd = nullptr);
 // Weight-streaming expert products for thin routed tiles (k_expert.hip) over
 // fragment-packed weights: PGU[e][F/16][d/32][2][64][8] (gate/up) and
@@ -158,7 +158,7 @@ template <typename T, typename WT>
 hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, const float* scale, T* act,
                                 const int4* tiles, const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
 template <typename T, typename WT>
-hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, float* Y, const int4* tiles,
+hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, T* Y, const int4* tiles,
                               const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s);
 // part[split][r][c] = sum over k in [split*kchunk, (split+1)*kchunk) of
 // rnd(P[r][k] * scale[r][k / 128]) * Bt[c][k]   (P: [M][K], scale: [M][nchunk], Bt: [N][K])
@@ -198,7 +198,7 @@ template <typename T>
 hipError_t add_norm(const float* part, int S, int M, int d, const float* g, float eps, float* H, T* xn,
                     Gate gt, int n, hipStream_t s);
 template <typename T>
-hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
+hipError_t combine_norm(const T* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
                         float eps, float* H, T* xn, Gate gt, int n, hipStream_t s);
 // RoPE on q and k of the fused projection (sum of S partials), q -> Q buffer, k and v -> cache at
 // pos.base(b) + i (K rows [B][Hkv][stride][hd], V transposed [B][Hkv][hd][stride])

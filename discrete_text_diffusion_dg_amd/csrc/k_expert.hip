@@ -359,7 +359,7 @@ __device__ __forceinline__ void stream_body(const T* X, const int* perm, const W
       } else {
         float y = acc[rb][0][i];
         if constexpr (std::is_same<WT, fp8e4m3>::value) y *= sc[0];
-        static_cast<float*>(out)[(size_t)(row_base + r) * N + col] = y;
+        Num<T>::store(static_cast<T*>(out) + (size_t)(row_base + r) * N + col, y);
       }
     }
 }
@@ -462,7 +462,7 @@ hipError_t expert_stream_gateup(const T* X, const int* perm, const WT* pgu, cons
 }
 
 template <typename T, typename WT>
-hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, float* Y, const int4* tiles,
+hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, T* Y, const int4* tiles,
                               const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s) {
   constexpr int NW = kStreamDownWaves<WT>;
   using C = StreamCfg<WT, false>;
@@ -474,7 +474,7 @@ hipError_t expert_stream_down(const T* act, const WT* pd, const float* scale, fl
 #define DG_INST(T, WT)                                                                                            \
   template hipError_t expert_stream_gateup<T, WT>(const T*, const int*, const WT*, const float*, T*, const int4*,  \
                                                   const int*, int, int, int, hipStream_t);                      \
-  template hipError_t expert_stream_down<T, WT>(const T*, const WT*, const float*, float*, const int4*, const int*, \
+  template hipError_t expert_stream_down<T, WT>(const T*, const WT*, const float*, T*, const int4*, const int*,     \
                                                 int, int, int, hipStream_t);
 DG_INST(float, float)
 DG_INST(bf16, bf16)

@@ -24,6 +24,18 @@ struct EpStoreF32 {        // out[group * split_stride + (row_base + r) * ldo + 
 };
 
 template <typename T>
+struct EpStore {           // out[(row_base + r) * ldo + n0 + c] = v in the operand type
+  static constexpr int kSmemBytes = 0;
+  T* out; int ldo;
+  template <class C>
+  __device__ void apply(const TileCtx& t, const f32x4_t (&acc)[C::FM][C::FN], char*) const {
+    for_each_acc<C>(acc, [&](int r, int c, float v) {
+      if (r < t.rows && c < t.cols) Num<T>::store(out + (size_t)(t.row_base + r) * ldo + t.n0 + c, v);
+    });
+  }
+};
+
+template <typename T>
 struct EpSwiGLU {          // blocks 2j / 2j+1 of a wave hold gate / up of the same 16 features
   static constexpr int kSmemBytes = 0;
   T* act; int F;
@@ -567,23 +579,22 @@ hipError_t gemm_expert_gateup(const T* X, const int* perm, const T* gate, const 
 }
 
 template <typename T>
-hipError_t gemm_expert_down(const T* act, const T* down, float* Y, const int4* tiles,
+hipError_t gemm_expert_down(const T* act, const T* down, T* Y, const int4* tiles,
                             const int* n_tiles, int cap_tiles, int d, int F, hipStream_t s, const T* pd) {
   if constexpr (sizeof(T) == 2) {
     if (expert_group_dma(d, F, sizeof(T))) {
       SchedGroup<128, 128> sc{tiles, n_tiles, cdiv(d, 128), d, F, 128};
       if (pd != nullptr)
         return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALRows<T>{act, F},
-                                                            BLPackedRows<T>{pd, d, F}, EpStoreF32{Y, d, 0}, s);
+                                                            BLPackedRows<T>{pd, d, F}, EpStore<T>{Y, d}, s);
       return launch_dma<TileCfgD<128, 128, kGroupStages>>(cap_tiles * sc.nt, sc, ALRows<T>{act, F},
-                                                          BLExpert<T>{down, (size_t)d * F, F}, EpStoreF32{Y, d, 0},
-                                                          s);
+                                                          BLExpert<T>{down, (size_t)d * F, F}, EpStore<T>{Y, d}, s);
     }
   }
   using C = TileCfg<T, 64, 64>;
   SchedGroup<64, 64> sc{tiles, n_tiles, cdiv(d, 64), d, F, 64};
   return launch<C, T>(cap_tiles * sc.nt, sc, ALRows<T>{act, F}, BLExpert<T>{down, (size_t)d * F, F},
-                      EpStoreF32{Y, d, 0}, s);
+                      EpStore<T>{Y, d}, s);
 }
 
 template <typename T>
@@ -618,7 +629,7 @@ hipError_t gemm_selfcond(const T* P, const float* scale, int nchunk, const T* Bt
                                        int, int, PosArg, Gate, hipStream_t);                            \
   template hipError_t gemm_expert_gateup<T>(const T*, const int*, const T*, const T*, T*, const int4*,    \
                                             const int*, int, int, int, hipStream_t, const T*);          \
-  template hipError_t gemm_expert_down<T>(const T*, const T*, float*, const int4*, const int*, int, int,  \
+  template hipError_t gemm_expert_down<T>(const T*, const T*, T*, const int4*, const int*, int, int,      \
                                           int, hipStream_t, const T*);                                  \
   template hipError_t gemm_selfcond<T>(const T*, const float*, int, const T*, float*, int, int, int, int, \
                                        int, Gate, int, hipStream_t);

@@ -21,6 +21,14 @@ __device__ __forceinline__ void add4(float4& a, const float4 b) {
   a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
 }
 
+// Four consecutive values of an fp32 or bf16 array (4-element aligned) as fp32.
+__device__ __forceinline__ float4 load4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4f(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
+
 // Sum over the S split partials of one float4 (part + s * stride + off), in
 // split order; the loads of up to 8 splits are issued together (indices past S
 // re-read the last split and are not added).
@@ -153,12 +161,13 @@ __global__ __launch_bounds__(256) void k_add_norm(const float* part, int S, int 
   norm_store<T>(v, NJ, d, g, eps, H + (size_t)r * d, xn + (size_t)r * d);
 }
 
-// h += sum_j w[j] * Y[pos[j]] (slots in selection order); xn = rnd(rmsnorm(h) * g).
+// h += sum_j w[j] * Y[pos[j]] (slots in selection order, expert outputs in the
+// operand type); xn = rnd(rmsnorm(h) * g).
 // Every slot's expert output (slot indices clamped to the k selected, so the
 // loads are unconditional) and h are loaded before the first sum: one load
 // round trip after the slot indices, where conditional loads went one by one.
 template <typename T, int NJ>
-__global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int* pos, const float* w, int k, int M,
+__global__ __launch_bounds__(256) void k_combine_norm(const T* Y, const int* pos, const float* w, int k, int M,
                                                       int d, const float* g, float eps, float* H, T* xn, Gate gt,
                                                       int n) {
   const int r = blockIdx.x;
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256) void k_combine_norm(const float* Y, const int*
   for (int j = 0; j < NJ; ++j) {
     const int c = (j * blockDim.x + threadIdx.x) * 4;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) y[j][s] = *reinterpret_cast<const float4*>(Y + (size_t)ps[s] * d + c);
+    for (int s = 0; s < 8; ++s) y[j][s] = load4f(Y + (size_t)ps[s] * d + c);
     hx[j] = *reinterpret_cast<const float4*>(H + (size_t)r * d + c);
   }
   float4 v[kRowChunks];
@@ -225,7 +234,7 @@ hipError_t add_norm(const float* part, int S, int M, int d, const float* g, floa
   return hipGetLastError();
 }
 template <typename T>
-hipError_t combine_norm(const float* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
+hipError_t combine_norm(const T* Y, const int* pos, const float* w, int k, int M, int d, const float* g,
                         float eps, float* H, T* xn, Gate gt, int n, hipStream_t s) {
   if (M <= 0) return hipSuccess;
 #define DG_L(NJ)                                                                                              \
@@ -1159,7 +1168,7 @@ hipError_t fill_u32(void* p, uint32_t v, size_t count, hipStream_t s) {
                                     float, float*, T*, Gate, int, hipStream_t);                                 \
   template hipError_t add_norm<T>(const float*, int, int, int, const float*, float, float*, T*, Gate, int,      \
                                   hipStream_t);                                                                 \
-  template hipError_t combine_norm<T>(const float*, const int*, const float*, int, int, int, const float*, float, \
+  template hipError_t combine_norm<T>(const T*, const int*, const float*, int, int, int, const float*, float,     \
                                       float*, T*, Gate, int, hipStream_t);                                      \
   template hipError_t rope_scatter<T>(const float*, int, const float2*, T*, T*, T*, int, int, int, int, int, int, \
                                       PosArg, Gate, hipStream_t);                                               \
