@@ -768,45 +768,59 @@ __global__ __launch_bounds__(64 * NW) void k_attn_spread(AttnArgs a) {
   }
 }
 
-// One thread per (row, 4 dims): combine the split partials in split order.
+// One thread per (row, kMergeDims<T> dims -- 16 bytes of partial output per
+// split): combine the split partials in split order.
 constexpr int kMaxAttnSplits = 16;   // key splits of one launch (the merge unrolls over them)
+template <typename T> constexpr int kMergeDims = 16 / (int)sizeof(T);
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int V = kMergeDims<T>;
   const size_t nrows = (size_t)a.B * a.nq * a.Hq;
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t rowid = gid / (HD / 4);
-  const int d0 = (int)(gid % (HD / 4)) * 4;
+  const size_t rowid = gid / (HD / V);
+  const int d0 = (int)(gid % (HD / V)) * V;
   if (rowid >= nrows || !a.gate.active((int)(rowid / a.Hq / a.nq))) return;
   // every split's (max, sum) and output piece are loaded before the first
   // use (at most kMaxAttnSplits), so the loads are one round trip, not one per split
   float2 ml[kMaxAttnSplits];
-  float4 po[kMaxAttnSplits];
+  float4 po[kMaxAttnSplits][V / 4];
+  const T* part = reinterpret_cast<const T*>(a.part_o);
 #pragma unroll
   for (int s = 0; s < kMaxAttnSplits; ++s) {
     if (s < a.splits) {
       ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * nrows + rowid) * 2);
-      po[s] = load4(reinterpret_cast<const T*>(a.part_o) + (s * nrows + rowid) * HD + d0);
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) po[s][h] = load4(part + (s * nrows + rowid) * HD + d0 + 4 * h);
     }
   }
   float m = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxAttnSplits; ++s)
     if (s < a.splits) m = fmaxf(m, ml[s].x);
-  float l = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f, acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
   for (int s = 0; s < kMaxAttnSplits; ++s) {
     if (s >= a.splits || ml[s].x == -INFINITY) continue;
     const float f = expf(ml[s].x - m);
     l += ml[s].y * f;
-    acc[0] += po[s].x * f; acc[1] += po[s].y * f; acc[2] += po[s].z * f; acc[3] += po[s].w * f;
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+      acc[4 * h] += po[s][h].x * f; acc[4 * h + 1] += po[s][h].y * f;
+      acc[4 * h + 2] += po[s][h].z * f; acc[4 * h + 3] += po[s][h].w * f;
+    }
   }
   const float inv = 1.f / l;
   const int head = (int)(rowid % a.Hq);
   const size_t tok = rowid / a.Hq;
   T* out = reinterpret_cast<T*>(a.out) + tok * (size_t)a.Hq * HD + (size_t)head * HD + d0;
-  float v[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-  store4(out, v);
+#pragma unroll
+  for (int h = 0; h < V / 4; ++h) {
+    float v[4] = {acc[4 * h] * inv, acc[4 * h + 1] * inv, acc[4 * h + 2] * inv, acc[4 * h + 3] * inv};
+    store4(out + 4 * h, v);
+  }
 }
 
 // Launch shape.  Spread while the K/V bytes its 16-row query blocks re-read
@@ -854,7 +868,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const size_t threads = (size_t)a.B * a.nq * a.Hq * (HD / 4);
+  const size_t threads = (size_t)a.B * a.nq * a.Hq * (HD / kMergeDims<T>);
   hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
