@@ -857,8 +857,16 @@ dg_status run_denoise(dg_state* st, const int32_t* canvas, const StepInfo& si, b
     {
       // the LM head keeping each row's top logits per vocabulary segment
       StageTimer tm(st, DG_STAGE_LM_HEAD, s);
-      DG_HIP(gemm_lm_head_topk<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, st->topk_seg, st->topk, gate,
-                                  st->n, s));
+      if constexpr (std::is_same<T, bf16>::value) {
+        if (m->head8 != nullptr)
+          DG_HIP(gemm_lm_head_topk_fp8(xn, d, m->head8, m->head_scale, R, V, d, st->topk_seg, st->topk, gate, st->n, s));
+        else
+          DG_HIP(gemm_lm_head_topk<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, st->topk_seg, st->topk, gate,
+                                      st->n, s));
+      } else {
+        DG_HIP(gemm_lm_head_topk<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, st->topk_seg, st->topk, gate,
+                                    st->n, s));
+      }
     }
     if (logits_out != nullptr) {
       // the raw logits, only when a caller asks for them (the plain head writes them)
@@ -929,8 +937,6 @@ extern "C" dg_status dg_denoise_step(dg_state* st, const int32_t* d_canvas, int3
   const Gate g{d_active, 0};
   if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
     return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
-  if (params->top_k > 0 && st->m->head8 != nullptr)
-    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step reads the bf16 LM head, not an FP8 one");
   return st->m->cfg.dtype == DG_DTYPE_BF16
              ? run_denoise<bf16>(st, d_canvas, si, sc, params->top_k, h_seeds, g, d_H, d_y, d_argmax, d_margin,
                                  d_logits, s)
@@ -1115,8 +1121,6 @@ extern "C" dg_status dg_run_canvas(dg_state* st, int32_t* d_canvas, const dg_sam
   if (params->max_steps > kMaxLoopSteps) return fail(DG_ERR_UNSUPPORTED, "max_steps above %d", kMaxLoopSteps);
   if (params->top_k > 0 && st->m->cfg.dtype != DG_DTYPE_BF16)
     return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step needs a bf16 model");
-  if (params->top_k > 0 && st->m->head8 != nullptr)
-    return fail(DG_ERR_UNSUPPORTED, "top-k truncation in the denoising step reads the bf16 LM head, not an FP8 one");
   if (first_step < 0 || first_step >= params->max_steps)
     return fail(DG_ERR_ARG, "first_step %d outside 0..max_steps-1", first_step);
   if (n_steps < 1 || n_steps > params->max_steps - first_step)

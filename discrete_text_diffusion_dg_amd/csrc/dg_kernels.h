@@ -261,6 +261,9 @@ int topk_segments(int M, int vocab);
 // logits = A . B^T tile by tile over each (row block, segment); per row and
 // segment its top kTopkList logits.  Rows of requests the gate leaves out are
 // skipped (whole row blocks).
+// (gemm_lm_head_topk_fp8: the same over the E4M3 rows and per-id scales of an FP8 head)
+hipError_t gemm_lm_head_topk_fp8(const bf16* A, int lda, const fp8e4m3* B8, const float* bscale, int M, int V, int K,
+                                 int nseg, TopkPart* out, Gate g, int n, hipStream_t s);
 template <typename T>
 hipError_t gemm_lm_head_topk(const T* A, int lda, const T* B, int ldb, int M, int V, int K, int nseg, TopkPart* out,
                              Gate g, int n, hipStream_t s);

@@ -466,10 +466,11 @@ __device__ __forceinline__ void topk_insert(float (&tv)[kTopkList], int (&ti)[kT
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void k_lm_head_topk(ALPlain<T> al, BLPlain<T> bl, int M, int V, int K, int nseg,
-                                                         int cps, TopkPart* out, Gate gate, int n) {
-  using C = TileCfgD<kHeadChunk, kHeadChunk, 2>;
+// C: the tile configuration for the B loader (bf16 rows of E, or their E4M3
+// codes); bscale (FP8 rows): each id's scale, applied as the tile is staged.
+template <typename T, class C, class BL>
+__global__ __launch_bounds__(256, 2) void k_lm_head_topk(ALPlain<T> al, BL bl, const float* bscale, int M, int V,
+                                                         int K, int nseg, int cps, TopkPart* out, Gate gate, int n) {
   constexpr int kBytes = C::kSmemBytes > kHeadTileBytes ? C::kSmemBytes : kHeadTileBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kBytes];
   const int nmb = (M + kHeadChunk - 1) / kHeadChunk, nchunk = (V + kHeadChunk - 1) / kHeadChunk;
@@ -493,7 +494,10 @@ __global__ __launch_bounds__(256, 2) void k_lm_head_topk(ALPlain<T> al, BLPlain<
     t.k0 = 0; t.k1 = K; t.group = 0; t.row_base = m0;
     f32x4_t acc[C::FM][C::FN];
     tile_mma_dma<C>(t, al, bl, smem, acc);
-    for_each_acc<C>(acc, [&](int r, int cc, float v) { tile[r * kHeadLd + cc] = v; });
+    for_each_acc<C>(acc, [&](int r, int cc, float v) {
+      if constexpr (C::B8) v *= bscale[t.n0 + (cc < t.cols ? cc : 0)];
+      tile[r * kHeadLd + cc] = v;
+    });
     __syncthreads();
     if (rl < rows && c0 < t.cols) {
       const float* tr = tile + rl * kHeadLd + c0;
@@ -539,10 +543,22 @@ hipError_t gemm_lm_head_topk(const T* A, int lda, const T* B, int ldb, int M, in
     if (V % 64 || K % 64 || M <= 0) return hipErrorInvalidValue;
     const int nmb = cdiv(M, kHeadChunk), nchunk = cdiv(V, kHeadChunk);
     const int cps = cdiv(nchunk, nseg);
-    hipLaunchKernelGGL((k_lm_head_topk<T>), dim3(nmb * nseg), dim3(256), 0, s, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb},
-                       M, V, K, nseg, cps, out, g, n);
+    hipLaunchKernelGGL((k_lm_head_topk<T, TileCfgD<kHeadChunk, kHeadChunk, 2>, BLPlain<T>>), dim3(nmb * nseg),
+                       dim3(256), 0, s, ALPlain<T>{A, lda}, BLPlain<T>{B, ldb}, (const float*)nullptr, M, V, K, nseg,
+                       cps, out, g, n);
     return hipGetLastError();
   }
+}
+
+hipError_t gemm_lm_head_topk_fp8(const bf16* A, int lda, const fp8e4m3* B8, const float* bscale, int M, int V, int K,
+                                 int nseg, TopkPart* out, Gate g, int n, hipStream_t s) {
+  if (V % 64 || K % 64 || M <= 0) return hipErrorInvalidValue;
+  const int nmb = cdiv(M, kHeadChunk), nchunk = cdiv(V, kHeadChunk);
+  const int cps = cdiv(nchunk, nseg);
+  hipLaunchKernelGGL((k_lm_head_topk<bf16, TileCfgD<kHeadChunk, kHeadChunk, 2, 1, true>, BLPackedFp8Rows>),
+                     dim3(nmb * nseg), dim3(256), 0, s, ALPlain<bf16>{A, lda}, BLPackedFp8Rows{B8, V, K}, bscale, M, V,
+                     K, nseg, cps, out, g, n);
+  return hipGetLastError();
 }
 template hipError_t gemm_lm_head_topk<float>(const float*, int, const float*, int, int, int, int, int, TopkPart*, Gate,
                                              int, hipStream_t);

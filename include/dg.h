@@ -98,8 +98,9 @@ typedef struct dg_config {
    * row v), fp32 sums of bf16 products, before the temperature and the head
    * statistics.  The embedding lookup and the self-conditioning contraction
    * keep reading the bf16 E.  The model holds V d bytes of codes and V fp32
-   * scales in addition.  Not taken by top-k truncated sampling (top_k > 0) or
-   * by dg_corrupt_forward_loss (DG_ERR_UNSUPPORTED). */
+   * scales in addition.  Full-vocabulary and top-k truncated sampling both
+   * read it; dg_corrupt_forward_loss does not take an FP8 head
+   * (DG_ERR_UNSUPPORTED). */
   int32_t head_dtype;
 } dg_config;
 

@@ -88,7 +88,7 @@ def test_device_loop_matches_explicit_calls(torch_cuda, graph):
     eb.close()
 
 
-@pytest.mark.parametrize("variant", ["topk", "fp8", "fp8-topk", "fp8-head", "streamed-router"])
+@pytest.mark.parametrize("variant", ["topk", "fp8", "fp8-topk", "fp8-head", "fp8-head-topk", "streamed-router"])
 def test_device_loop_variants_match_explicit_calls(torch_cuda, variant):
     # the captured step with the top-k sampler and / or FP8 experts (and the FP8
     # LM head), or with the streamed norm + router (d 1024, 24 experts): one
@@ -99,7 +99,7 @@ def test_device_loop_variants_match_explicit_calls(torch_cuda, variant):
         mc = micro(n_layers=2, vocab=4096, d_model=1024, n_experts=24, top_k=3, ffn_hidden=128)
     else:
         mc = micro(n_layers=2, vocab=4096, d_model=512, ffn_hidden=256, expert_dtype="fp8" if fp8 else "",
-                   head_dtype="fp8" if variant == "fp8-head" else "")
+                   head_dtype="fp8" if variant.startswith("fp8-head") else "")
     W = di.make_weights(mc, 33, gain_std=0.1)
     B, P, S = 2, 200, 4
     prompts = torch.from_numpy(di.make_prompts(mc.vocab, B, P, 33))
