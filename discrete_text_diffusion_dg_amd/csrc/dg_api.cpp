@@ -1029,12 +1029,19 @@ dg_status run_corrupt_loss(dg_state* st, const int32_t* clean, const RateArg& ra
     // the LM head at temperature 1: the chunk statistics give each row's log-sum-exp
     StageTimer tm(st, DG_STAGE_LM_HEAD, s);
     const HeadArgs<T> h{StepInfo{0, 1.0f, nullptr, nullptr, st->cidx_dev}, sa, st->n, st->hp, nullptr, nullptr, all};
-    DG_HIP(gemm_lm_head<T>(xn, d, static_cast<const T*>(m->emb), d, R, V, d, h, s));
+    DG_HIP(lm_head<T>(m, xn, R, h, s));
   }
   {
     StageTimer tm(st, DG_STAGE_SAMPLER, s);
     DG_HIP(sampler_merge(st->hp, R, st->chunks, st->n, all, nullptr, nullptr, nullptr, nullptr, nullptr, s, st->lse));
-    DG_HIP(clean_token_loss<T>(xn, static_cast<const T*>(m->emb), clean, st->lse, st->B, st->n, d, ce, loss, s));
+    if constexpr (std::is_same<T, bf16>::value) {
+      if (m->head8 != nullptr)
+        DG_HIP(clean_token_loss_fp8(xn, m->head8, m->head_scale, clean, st->lse, st->B, st->n, d, V, ce, loss, s));
+      else
+        DG_HIP(clean_token_loss<T>(xn, static_cast<const T*>(m->emb), clean, st->lse, st->B, st->n, d, V, ce, loss, s));
+    } else {
+      DG_HIP(clean_token_loss<T>(xn, static_cast<const T*>(m->emb), clean, st->lse, st->B, st->n, d, V, ce, loss, s));
+    }
   }
   return DG_OK;
 }
@@ -1051,8 +1058,6 @@ extern "C" dg_status dg_corrupt_forward_loss(dg_state* st, const int32_t* d_clea
     if (!(h_rates[b] >= 0.f && h_rates[b] <= 1.f)) return fail(DG_ERR_ARG, "rate of request %d outside [0, 1]", b);
     ra.v[b] = h_rates[b];
   }
-  if (st->m->head8 != nullptr)
-    return fail(DG_ERR_UNSUPPORTED, "the training-side pass takes the bf16 LM head, not an FP8 one");
   dg_status r = check_capacity(st);
   if (r) return r;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

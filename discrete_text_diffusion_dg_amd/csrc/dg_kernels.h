@@ -308,7 +308,12 @@ hipError_t corrupt_canvas(const int32_t* clean, int32_t* out, const SeedArg& see
                           int n, int vocab, const int32_t* cidx, hipStream_t s);
 template <typename T>
 hipError_t clean_token_loss(const T* xn, const T* emb, const int32_t* clean, const float* lse, int B, int n, int d,
-                            float* ce, float* loss, hipStream_t s);
+                            int vocab, float* ce, float* loss, hipStream_t s);
+// The same with the clean token's logit from an FP8 head (E4M3 codes in the P8
+// order of gemm_lm_head_fp8 and per-id scales).
+hipError_t clean_token_loss_fp8(const bf16* xn, const fp8e4m3* codes, const float* scale, const int32_t* clean,
+                                const float* lse, int B, int n, int d, int vocab, float* ce, float* loss,
+                                hipStream_t s);
 // S[r][c] = sum over splits (in order) of part[split][r][c], rows of active requests
 hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s);
 hipError_t commit_kernel(const float* H, const int32_t* y, const int32_t* am, int32_t* canvas,

@@ -501,15 +501,35 @@ __global__ void k_corrupt(const int32_t* clean, int32_t* out, SeedArg seeds, Rat
 // them, fp32 sums in a fixed order), subtracted from the row's log-sum-exp.
 template <typename T>
 __global__ __launch_bounds__(256) void k_clean_ce(const T* xn, const T* emb, const int32_t* clean, const float* lse,
-                                                  int M, int d, float* ce) {
+                                                  int M, int d, int vocab, float* ce) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= M) return;
   const T* a = xn + (size_t)r * d;
-  const T* e = emb + (size_t)clean[r] * d;
+  const T* e = emb + (size_t)min(max(clean[r], 0), vocab - 1) * d;   // ids outside [0, V) are clamped
   float acc = 0.f;
   for (int k = lane; k < d; k += 64) acc += Num<T>::load(a + k) * Num<T>::load(e + k);
   acc = wave_sum(acc);
   if (lane == 0) ce[r] = lse[r] - acc;
+}
+
+// The same for an FP8 head: the clean token's logit is scale[x0] times the
+// product with the E4M3 codes of row x0, read from the P8 fragment order
+// (block (x0/16, k/64), lane (k%32)/8 * 16 + x0%16, byte (k%64)/32 * 8 + k%8).
+__global__ __launch_bounds__(256) void k_clean_ce_fp8(const bf16* xn, const fp8e4m3* codes, const float* scale,
+                                                      const int32_t* clean, const float* lse, int M, int d,
+                                                      int vocab, float* ce) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= M) return;
+  const bf16* a = xn + (size_t)r * d;
+  const int v = min(max(clean[r], 0), vocab - 1);
+  const uint8_t* rowblk = reinterpret_cast<const uint8_t*>(codes) + (size_t)(v / 16) * (d / 64) * 1024;
+  float acc = 0.f;
+  for (int k = lane; k < d; k += 64) {
+    const uint8_t c = rowblk[(size_t)(k / 64) * 1024 + (((k % 32) / 8) * 16 + v % 16) * 16 + ((k % 64) / 32) * 8 + k % 8];
+    acc += Num<bf16>::load(a + k) * __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false)[0];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) ce[r] = lse[r] - scale[v] * acc;
 }
 
 // Mean cross-entropy per request: fp64, positions in order.
@@ -529,18 +549,30 @@ hipError_t corrupt_canvas(const int32_t* clean, int32_t* out, const SeedArg& see
 
 template <typename T>
 hipError_t clean_token_loss(const T* xn, const T* emb, const int32_t* clean, const float* lse, int B, int n, int d,
-                            float* ce, float* loss, hipStream_t s) {
+                            int vocab, float* ce, float* loss, hipStream_t s) {
   const int M = B * n;
-  hipLaunchKernelGGL((k_clean_ce<T>), dim3((M + 3) / 4), dim3(256), 0, s, xn, emb, clean, lse, M, d, ce);
+  hipLaunchKernelGGL((k_clean_ce<T>), dim3((M + 3) / 4), dim3(256), 0, s, xn, emb, clean, lse, M, d, vocab, ce);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_loss_mean, dim3((B + 63) / 64), dim3(64), 0, s, ce, B, n, loss);
+  return hipGetLastError();
+}
+hipError_t clean_token_loss_fp8(const bf16* xn, const fp8e4m3* codes, const float* scale, const int32_t* clean,
+                                const float* lse, int B, int n, int d, int vocab, float* ce, float* loss,
+                                hipStream_t s) {
+  const int M = B * n;
+  if (d % 64 || vocab % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_clean_ce_fp8, dim3((M + 3) / 4), dim3(256), 0, s, xn, codes, scale, clean, lse, M, d, vocab,
+                     ce);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_loss_mean, dim3((B + 63) / 64), dim3(64), 0, s, ce, B, n, loss);
   return hipGetLastError();
 }
 template hipError_t clean_token_loss<float>(const float*, const float*, const int32_t*, const float*, int, int, int,
-                                            float*, float*, hipStream_t);
+                                            int, float*, float*, hipStream_t);
 template hipError_t clean_token_loss<bf16>(const bf16*, const bf16*, const int32_t*, const float*, int, int, int,
-                                           float*, float*, hipStream_t);
+                                           int, float*, float*, hipStream_t);
 
 hipError_t selfcond_reduce(const float* part, int M, int d, int splits, float* S, Gate g, int n, hipStream_t s) {
   const size_t nq = (size_t)M * d / 4;      // d is a multiple of 256

@@ -98,9 +98,8 @@ typedef struct dg_config {
    * row v), fp32 sums of bf16 products, before the temperature and the head
    * statistics.  The embedding lookup and the self-conditioning contraction
    * keep reading the bf16 E.  The model holds V d bytes of codes and V fp32
-   * scales in addition.  Full-vocabulary and top-k truncated sampling both
-   * read it; dg_corrupt_forward_loss does not take an FP8 head
-   * (DG_ERR_UNSUPPORTED). */
+   * scales in addition.  Full-vocabulary and top-k truncated sampling and
+   * the training-side pass (dg_corrupt_forward_loss) all read it. */
   int32_t head_dtype;
 } dg_config;
 
@@ -346,7 +345,8 @@ dg_status dg_run_canvas(dg_state* state, int32_t* d_canvas, const dg_sampler_par
 /* Training-side forward pass ([mlqm] 一: in training a share of a sequence's
  * tokens, from 0% to 100%, is replaced by random vocabulary tokens and the
  * model learns to restore the original).  Per request b, every position of
- * the clean canvas d_clean (int32 [B, canvas_len]) is replaced independently
+ * the clean canvas d_clean (int32 [B, canvas_len], ids in [0, V); an id
+ * outside is clamped to that range) is replaced independently
  * with probability h_rates[b] (host float [B], each in [0, 1]) by a uniform
  * vocabulary token: one Philox4x32-10 call per position under the request's
  * seed, counter (0, position, 0, 5 << 24 | canvas index), word 0 deciding

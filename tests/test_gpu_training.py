@@ -91,3 +91,9 @@ def test_corrupt_forward_loss_fp8_experts(torch_cuda):
     # the pass through the FP8 expert products (grouped: 256 canvas positions per request)
     mc = micro(n_layers=2, d_model=512, ffn_hidden=256, vocab=2048, expert_dtype="fp8")
     _case(torch_cuda, mc, 63, 2, 130, [0.3, 0.9], "train-fp8")
+
+
+def test_corrupt_forward_loss_fp8_head(torch_cuda):
+    # experts and LM head in FP8: the log-sum-exp and the clean token's logit from the E4M3 rows
+    mc = micro(n_layers=2, d_model=512, ffn_hidden=256, vocab=4160, expert_dtype="fp8", head_dtype="fp8")
+    _case(torch_cuda, mc, 64, 2, 130, [0.3, 0.9], "train-fp8-head")
